@@ -1,0 +1,167 @@
+/*
+ * idx_topk.h -- DSA Lightning Indexer scoring fused with exact per-row top-K
+ * on AMD Instinct MI355X (gfx950).
+ *
+ * The operation (Fused Indexer Top-k page, "1.1 The problem" equation and
+ * "2.3 Problem definition"):
+ *
+ *     I[t,s] = sum_{j<64} w[t,j] * ReLU( q[t,j] . k[s] )
+ *
+ * for every query row t and every key s in the row's half-open valid range
+ * [row_start[t], row_end[t]), with q[t,j] = e4m3(q8[t,j,:]) * q_scale[t,j] and
+ * k[s] = e4m3(k8[s,:]) * k_scale[s] (FP8 operands "each with scales"), and the
+ * output is, per row, the K ids with the largest I, in no particular order.
+ * Among equal scores any valid id may be returned (same section: ties may
+ * resolve to any valid index).  The result is exact: a sampled threshold only
+ * decides whether the fast path's candidate set certifies the answer
+ * ("3.2 Sampled threshold: turn maintenance into filtering"); rows where it
+ * does not are recomputed by an exact repair path.
+ *
+ * The paged decode variant follows the contest report page, "DSA TopK
+ * Indexer": one FP8 query per sequence, a paged FP8 key cache with per-token
+ * FP32 scales, per-head weights and sequence lengths; sequences no longer
+ * than K reduce to an index remap.
+ *
+ * Conventions for every entry point below:
+ *   - All array pointers are DEVICE pointers owned by the caller; the library
+ *     keeps none of them after returning and allocates no device memory.
+ *   - Scratch memory is the caller's `workspace` of at least the size
+ *     returned by the matching *_workspace() query (256-byte aligned).
+ *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL means
+ *     the default stream).  There is no host synchronisation.
+ *   - Geometry is fixed: 64 heads, head dimension 128, 1 <= K <= 2048.
+ *   - FP8 codes are OCP e4m3fn (max 448, no infinities); NaN codes are not
+ *     allowed in the inputs.  Scales must be finite and > 0.
+ *   - Argument errors detectable on the host return a negative IDX_E* code
+ *     and enqueue nothing.  Ranges that can only be seen on the device
+ *     (start > end, end > N, a page id outside the cache) make that row's
+ *     output all -1 and count it in idx_topk_stats.bad_rows.
+ *   - Output rows hold min(K, L) valid ids (L = the row's range length)
+ *     followed by K - min(K, L) entries of -1.
+ *   - Calls that share one workspace must not overlap in time.
+ */
+#ifndef IDX_TOPK_H
+#define IDX_TOPK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define IDX_TOPK_HEADS 64
+#define IDX_TOPK_DIM 128
+#define IDX_TOPK_KMAX 2048
+#define IDX_TOPK_PAGE 64
+
+/* Threshold sampler: keys row_start + OFFSET + STRIDE*i inside the row are
+ * scored exactly; the threshold is the r-th largest sample score with
+ * r = ceil(n_samples * TARGET / L), aiming at TARGET = 2K candidates
+ * ("3.2 Sampled threshold": about 0.5% of the row, about twice K). */
+#define IDX_TOPK_SAMPLE_STRIDE 200
+#define IDX_TOPK_SAMPLE_OFFSET 100
+#define IDX_TOPK_SAMPLE_TARGET 4096
+
+enum {
+  IDX_OK = 0,
+  IDX_EINVAL = -1,       /* null pointer, negative size, bad alignment, K out of range */
+  IDX_EUNSUPPORTED = -2, /* geometry the kernels do not implement (page_size != 64) */
+  IDX_EWORKSPACE = -3,   /* workspace missing or smaller than the query returned */
+  IDX_EHIP = -4          /* a HIP launch or copy failed */
+};
+
+/* Per-call counters kept in the workspace (read with idx_topk_read_stats). */
+typedef struct {
+  uint32_t rows;       /* rows (or sequences) processed                         */
+  uint32_t fast_ok;    /* rows certified by the sampled-threshold fast path     */
+  uint32_t underflow;  /* fast path failed: fewer than K candidates             */
+  uint32_t overflow;   /* fast path failed: candidates exceeded capacity        */
+  uint32_t spilled;    /* fast-path rows whose candidates overflowed on-chip
+                          storage into the workspace spill area                 */
+  uint32_t repaired;   /* rows recomputed by the exact repair path              */
+  uint32_t trivial;    /* rows (sequences) with L <= K: no scoring needed       */
+  uint32_t bad_rows;   /* rows with an invalid range or page id (output all -1) */
+} idx_topk_stats;
+
+/* Test and diagnosis knobs for idx_topk_prefill_debug (zero = default). */
+typedef struct {
+  int32_t force_tau;   /* 1: use tau_value as every row's threshold             */
+  float tau_value;
+  int32_t lds_cap;     /* >0: on-chip candidate capacity per row (<= default)   */
+  int32_t spill_cap;   /* >0: spill capacity per row (<= default); -1: none     */
+} idx_topk_opts;
+
+/* Bytes of workspace idx_topk_prefill needs for Q rows over N keys. */
+size_t idx_topk_prefill_workspace(int32_t Q, int32_t N, int32_t K);
+
+/*
+ * Prefill: top-K ids per query row (Fused Indexer Top-k page, "2.3 Problem
+ * definition").
+ *   q         [Q][64][128] uint8 e4m3fn codes, 16-byte aligned
+ *   q_scale   [Q][64] float > 0, or NULL for all-ones
+ *   k         [N][128] uint8 e4m3fn codes, 16-byte aligned
+ *   k_scale   [N] float > 0
+ *   w         [Q][64] float head weights
+ *   row_start [Q] int32, row_end [Q] int32: valid range [start, end), 0 <= start <= end <= N
+ *   K         1..2048
+ *   out_idx   [Q][K] int32: absolute key ids in [start, end), unsorted, -1 padded
+ * Returns IDX_OK or a negative IDX_E* code.
+ */
+int idx_topk_prefill(const uint8_t *q, const float *q_scale, const uint8_t *k,
+                     const float *k_scale, const float *w, const int32_t *row_start,
+                     const int32_t *row_end, int32_t K, int32_t *out_idx, int32_t Q,
+                     int32_t N, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Same as idx_topk_prefill, plus diagnostics for tests:
+ *   scores_out [Q][N] float or NULL: the FP32 score of every valid (t, s), as
+ *              used by the selection (entries outside a row's range are not
+ *              written);
+ *   tau_out    [Q] float or NULL: the threshold each row was filtered with;
+ *   opts       NULL or knobs that force the threshold or shrink capacities so
+ *              that the repair path runs.
+ */
+int idx_topk_prefill_debug(const uint8_t *q, const float *q_scale, const uint8_t *k,
+                           const float *k_scale, const float *w, const int32_t *row_start,
+                           const int32_t *row_end, int32_t K, int32_t *out_idx, int32_t Q,
+                           int32_t N, void *workspace, size_t workspace_bytes, void *stream,
+                           float *scores_out, float *tau_out, const idx_topk_opts *opts);
+
+/* Bytes of workspace idx_topk_decode_paged needs. */
+size_t idx_topk_decode_workspace(int32_t B, int32_t max_pages, int32_t page_size, int32_t K);
+
+/*
+ * Paged decode (contest report page, "DSA TopK Indexer"): one query per
+ * sequence b, keys at logical positions i in [0, seq_lens[b]) stored in page
+ * page_table[b][i / page_size], slot i % page_size.
+ *   q          [B][64][128] uint8 e4m3fn, 16-byte aligned
+ *   q_scale    [B][64] float > 0, or NULL for all-ones
+ *   k_cache    [num_pages][page_size][128] uint8 e4m3fn, 16-byte aligned
+ *   k_scale    [num_pages][page_size] float > 0
+ *   w          [B][64] float
+ *   page_table [B][max_pages] int32 physical page ids
+ *   seq_lens   [B] int32 (device), 0 <= seq_len <= max_pages * page_size
+ *   page_size  must be 64
+ *   out_idx    [B][K] int32: physical cache slots page*page_size + slot of the
+ *              selected keys, unsorted, -1 padded.  Sequences with
+ *              seq_len <= K take the remap path: all their slots, no scoring.
+ */
+int idx_topk_decode_paged(const uint8_t *q, const float *q_scale, const uint8_t *k_cache,
+                          const float *k_scale, const float *w, const int32_t *page_table,
+                          const int32_t *seq_lens, int32_t B, int32_t max_pages,
+                          int32_t page_size, int32_t num_pages, int32_t K, int32_t *out_idx,
+                          void *workspace, size_t workspace_bytes, void *stream);
+
+/* Copy the counters of the last call that used `workspace` into *out.
+ * Synchronises `stream`.  For tests and diagnosis, not for hot loops. */
+int idx_topk_read_stats(const void *workspace, idx_topk_stats *out, void *stream);
+
+/* Static description of an error code. */
+const char *idx_topk_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* IDX_TOPK_H */

@@ -1,0 +1,194 @@
+"""DSA Lightning Indexer scoring fused with exact top-K on MI355X (gfx950).
+
+Thin ctypes binding of libidxtopk.so (C ABI in include/idx_topk.h).  This
+module only marshals arguments: torch supplies device memory and the current
+stream; every step of the computation runs in the library's HIP kernels.
+Importing raises if the library has not been built (run
+``python -m scoring_exact_top_amd.build`` or ``__graft_entry__.build()``).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libidxtopk.so")
+
+HEADS = 64
+DIM = 128
+KMAX = 2048
+PAGE = 64
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError("libidxtopk.so is not built at %s; run python -m scoring_exact_top_amd.build"
+                      % LIB_PATH)
+
+_lib = ctypes.CDLL(LIB_PATH)
+_vp = ctypes.c_void_p
+_i32 = ctypes.c_int32
+_sz = ctypes.c_size_t
+
+
+class Opts(ctypes.Structure):
+    _fields_ = [("force_tau", ctypes.c_int32), ("tau_value", ctypes.c_float),
+                ("lds_cap", ctypes.c_int32), ("spill_cap", ctypes.c_int32)]
+
+
+class Stats(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_uint32) for n in
+                ("rows", "fast_ok", "underflow", "overflow", "spilled", "repaired", "trivial",
+                 "bad_rows")]
+
+    def asdict(self):
+        return {n: int(getattr(self, n)) for n, _ in self._fields_}
+
+
+_lib.idx_topk_prefill_workspace.restype = _sz
+_lib.idx_topk_prefill_workspace.argtypes = [_i32, _i32, _i32]
+_lib.idx_topk_prefill.restype = ctypes.c_int
+_lib.idx_topk_prefill.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _vp, _sz,
+                                  _vp]
+_lib.idx_topk_prefill_debug.restype = ctypes.c_int
+_lib.idx_topk_prefill_debug.argtypes = _lib.idx_topk_prefill.argtypes + [_vp, _vp,
+                                                                          ctypes.POINTER(Opts)]
+_lib.idx_topk_decode_workspace.restype = _sz
+_lib.idx_topk_decode_workspace.argtypes = [_i32, _i32, _i32, _i32]
+_lib.idx_topk_decode_paged.restype = ctypes.c_int
+_lib.idx_topk_decode_paged.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
+                                       _i32, _vp, _vp, _sz, _vp]
+_lib.idx_topk_read_stats.restype = ctypes.c_int
+_lib.idx_topk_read_stats.argtypes = [_vp, ctypes.POINTER(Stats), _vp]
+_lib.idx_topk_strerror.restype = ctypes.c_char_p
+_lib.idx_topk_strerror.argtypes = [ctypes.c_int]
+
+
+class IdxTopkError(RuntimeError):
+    def __init__(self, code: int):
+        super().__init__("idx_topk error %d: %s" % (code, _lib.idx_topk_strerror(code).decode()))
+        self.code = code
+
+
+def _check(rc: int):
+    if rc != 0:
+        raise IdxTopkError(rc)
+
+
+def _ptr(t: Optional[torch.Tensor], dtype=None):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("expected a device tensor")
+    if not t.is_contiguous():
+        raise ValueError("expected a contiguous tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError("expected dtype %s, got %s" % (dtype, t.dtype))
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def prefill_workspace_bytes(Q: int, N: int, K: int) -> int:
+    return int(_lib.idx_topk_prefill_workspace(Q, N, K))
+
+
+def decode_workspace_bytes(B: int, max_pages: int, page_size: int, K: int) -> int:
+    return int(_lib.idx_topk_decode_workspace(B, max_pages, page_size, K))
+
+
+def alloc_workspace(nbytes: int, device) -> torch.Tensor:
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+def _q_k(q8, k8):
+    if q8.dtype == torch.float8_e4m3fn:
+        q8 = q8.view(torch.uint8)
+    if k8.dtype == torch.float8_e4m3fn:
+        k8 = k8.view(torch.uint8)
+    return q8, k8
+
+
+def prefill(q8, q_scale, k8, k_scale, w, row_start, row_end, K: int, out=None, workspace=None,
+            stream=None):
+    """Top-K key ids per query row; see idx_topk_prefill in include/idx_topk.h.
+
+    q8 [Q,64,128] uint8 (or float8_e4m3fn), q_scale [Q,64] f32 or None,
+    k8 [N,128], k_scale [N] f32, w [Q,64] f32, row_start/row_end [Q] int32.
+    Returns out [Q,K] int32 (absolute ids, unsorted, -1 padded).
+    """
+    return _prefill(q8, q_scale, k8, k_scale, w, row_start, row_end, K, out, workspace, stream,
+                    debug=False)
+
+
+def prefill_debug(q8, q_scale, k8, k_scale, w, row_start, row_end, K: int, out=None,
+                  workspace=None, stream=None, scores_out=None, tau_out=None,
+                  force_tau: Optional[float] = None, lds_cap: int = 0, spill_cap: int = 0):
+    """idx_topk_prefill_debug: also emits FP32 scores [Q,N] and thresholds [Q]."""
+    opts = Opts(1 if force_tau is not None else 0, float(force_tau or 0.0), int(lds_cap),
+                int(spill_cap))
+    return _prefill(q8, q_scale, k8, k_scale, w, row_start, row_end, K, out, workspace, stream,
+                    debug=True, scores_out=scores_out, tau_out=tau_out, opts=opts)
+
+
+def _prefill(q8, q_scale, k8, k_scale, w, row_start, row_end, K, out, workspace, stream, debug,
+             scores_out=None, tau_out=None, opts=None):
+    q8, k8 = _q_k(q8, k8)
+    Q, N = int(q8.shape[0]), int(k8.shape[0])
+    if q8.shape[1:] != (HEADS, DIM) or k8.shape[1:] != (DIM,):
+        raise ValueError("q8 must be [Q,64,128] and k8 [N,128]")
+    dev = q8.device
+    if out is None:
+        out = torch.empty((Q, K), dtype=torch.int32, device=dev)
+    if workspace is None:
+        workspace = alloc_workspace(prefill_workspace_bytes(Q, N, K), dev)
+    args = [_ptr(q8, torch.uint8), _ptr(q_scale, torch.float32), _ptr(k8, torch.uint8),
+            _ptr(k_scale, torch.float32), _ptr(w, torch.float32), _ptr(row_start, torch.int32),
+            _ptr(row_end, torch.int32), int(K), _ptr(out, torch.int32), Q, N, _ptr(workspace),
+            int(workspace.numel()), _stream(stream)]
+    if debug:
+        _check(_lib.idx_topk_prefill_debug(*args, _ptr(scores_out, torch.float32),
+                                           _ptr(tau_out, torch.float32), ctypes.byref(opts)))
+    else:
+        _check(_lib.idx_topk_prefill(*args))
+    return out
+
+
+def decode_paged(q8, q_scale, k_cache, k_scale, w, page_table, seq_lens, K: int, out=None,
+                 workspace=None, stream=None):
+    """Top-K physical cache slots per sequence; see idx_topk_decode_paged.
+
+    q8 [B,64,128], q_scale [B,64] or None, k_cache [P,64,128], k_scale [P,64],
+    w [B,64], page_table [B,max_pages] int32, seq_lens [B] int32 (device).
+    """
+    q8, k_cache = _q_k(q8, k_cache)
+    B = int(q8.shape[0])
+    P, page = int(k_cache.shape[0]), int(k_cache.shape[1])
+    max_pages = int(page_table.shape[1])
+    dev = q8.device
+    if out is None:
+        out = torch.empty((B, K), dtype=torch.int32, device=dev)
+    if workspace is None:
+        workspace = alloc_workspace(decode_workspace_bytes(B, max_pages, page, K), dev)
+    _check(_lib.idx_topk_decode_paged(
+        _ptr(q8, torch.uint8), _ptr(q_scale, torch.float32), _ptr(k_cache, torch.uint8),
+        _ptr(k_scale, torch.float32), _ptr(w, torch.float32), _ptr(page_table, torch.int32),
+        _ptr(seq_lens, torch.int32), B, max_pages, page, P, int(K), _ptr(out, torch.int32),
+        _ptr(workspace), int(workspace.numel()), _stream(stream)))
+    return out
+
+
+def read_stats(workspace: torch.Tensor, stream=None) -> dict:
+    st = Stats()
+    _check(_lib.idx_topk_read_stats(_ptr(workspace), ctypes.byref(st), _stream(stream)))
+    return st.asdict()
+
+
+def raw_library():
+    """The loaded ctypes library (for ABI-level tests)."""
+    return _lib

@@ -1,0 +1,137 @@
+// Host side of the C ABI declared in include/idx_topk.h: argument checks,
+// workspace carving and kernel launches on the caller's stream.
+#include <string.h>
+
+#include "idx_internal.hpp"
+#include "idx_decode.hpp"
+
+namespace idxk {
+
+static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+static inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+struct PrefillLayout {
+  size_t ctrl, tau, fail, skey, sidx, scratch, total;
+};
+
+static PrefillLayout prefill_layout(int32_t Q, int32_t N) {
+  PrefillLayout L;
+  size_t o = 0;
+  L.ctrl = o; o = align256(o + sizeof(uint32_t) * kCtrlWords);
+  L.tau = o; o = align256(o + sizeof(float) * (size_t)Q);
+  L.fail = o; o = align256(o + sizeof(int32_t) * (size_t)Q);
+  L.skey = o; o = align256(o + sizeof(uint32_t) * (size_t)Q * kSpillCap);
+  L.sidx = o; o = align256(o + sizeof(int32_t) * (size_t)Q * kSpillCap);
+  L.scratch = o; o = align256(o + sizeof(uint32_t) * (size_t)repair_grid(Q) * (size_t)N);
+  L.total = o;
+  return L;
+}
+
+static int prefill_common(const uint8_t* q, const float* q_scale, const uint8_t* k,
+                          const float* k_scale, const float* w, const int32_t* row_start,
+                          const int32_t* row_end, int32_t K, int32_t* out_idx, int32_t Q, int32_t N,
+                          void* workspace, size_t workspace_bytes, void* stream, float* scores_out,
+                          float* tau_out, const idx_topk_opts* opts) {
+  if (Q < 0 || N < 0 || K < 1 || K > kKmax) return IDX_EINVAL;
+  if (Q == 0) return IDX_OK;
+  if (!q || !w || !row_start || !row_end || !out_idx) return IDX_EINVAL;
+  if (N > 0 && (!k || !k_scale)) return IDX_EINVAL;
+  if (!aligned16(q) || (k && !aligned16(k))) return IDX_EINVAL;
+  const PrefillLayout L = prefill_layout(Q, N);
+  if (!workspace || workspace_bytes < L.total) return IDX_EWORKSPACE;
+  if (((uintptr_t)workspace & 255u) != 0) return IDX_EINVAL;
+  char* ws = static_cast<char*>(workspace);
+
+  PrefillArgs A;
+  memset(&A, 0, sizeof(A));
+  A.q = q; A.q_scale = q_scale; A.k = k; A.k_scale = k_scale; A.w = w;
+  A.row_start = row_start; A.row_end = row_end;
+  A.Q = Q; A.N = N; A.K = K;
+  A.ctrl = reinterpret_cast<uint32_t*>(ws + L.ctrl);
+  A.tau = reinterpret_cast<float*>(ws + L.tau);
+  A.fail_list = reinterpret_cast<int32_t*>(ws + L.fail);
+  A.spill_key = reinterpret_cast<uint32_t*>(ws + L.skey);
+  A.spill_idx = reinterpret_cast<int32_t*>(ws + L.sidx);
+  A.scratch = reinterpret_cast<uint32_t*>(ws + L.scratch);
+  A.out = out_idx;
+  A.dbg_scores = scores_out;
+  A.lds_cap = kLdsCap;
+  A.spill_cap = kSpillCap;
+  if (opts) {
+    if (opts->lds_cap < 0 || opts->lds_cap > kLdsCap || opts->spill_cap < -1 || opts->spill_cap > kSpillCap)
+      return IDX_EINVAL;
+    if (opts->lds_cap > 0) A.lds_cap = opts->lds_cap;
+    if (opts->spill_cap > 0) A.spill_cap = opts->spill_cap;
+    if (opts->spill_cap == -1) A.spill_cap = 0;
+    A.force_tau = opts->force_tau ? 1 : 0;
+    A.tau_value = opts->tau_value;
+  }
+  A.cap_total = A.lds_cap + A.spill_cap;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int rc = launch_prefill(A, s);
+  if (rc == IDX_OK && tau_out) {
+    if (hipMemcpyAsync(tau_out, A.tau, sizeof(float) * (size_t)Q, hipMemcpyDeviceToDevice, s) != hipSuccess)
+      rc = IDX_EHIP;
+  }
+  return rc;
+}
+
+}  // namespace idxk
+
+using namespace idxk;
+
+extern "C" size_t idx_topk_prefill_workspace(int32_t Q, int32_t N, int32_t K) {
+  if (Q < 0 || N < 0 || K < 1 || K > kKmax) return 0;
+  return prefill_layout(Q, N).total;
+}
+
+extern "C" int idx_topk_prefill(const uint8_t* q, const float* q_scale, const uint8_t* k,
+                                const float* k_scale, const float* w, const int32_t* row_start,
+                                const int32_t* row_end, int32_t K, int32_t* out_idx, int32_t Q,
+                                int32_t N, void* workspace, size_t workspace_bytes, void* stream) {
+  return prefill_common(q, q_scale, k, k_scale, w, row_start, row_end, K, out_idx, Q, N, workspace,
+                        workspace_bytes, stream, nullptr, nullptr, nullptr);
+}
+
+extern "C" int idx_topk_prefill_debug(const uint8_t* q, const float* q_scale, const uint8_t* k,
+                                      const float* k_scale, const float* w,
+                                      const int32_t* row_start, const int32_t* row_end, int32_t K,
+                                      int32_t* out_idx, int32_t Q, int32_t N, void* workspace,
+                                      size_t workspace_bytes, void* stream, float* scores_out,
+                                      float* tau_out, const idx_topk_opts* opts) {
+  return prefill_common(q, q_scale, k, k_scale, w, row_start, row_end, K, out_idx, Q, N, workspace,
+                        workspace_bytes, stream, scores_out, tau_out, opts);
+}
+
+extern "C" size_t idx_topk_decode_workspace(int32_t B, int32_t max_pages, int32_t page_size, int32_t K) {
+  return decode_workspace_bytes(B, max_pages, page_size, K);
+}
+
+extern "C" int idx_topk_decode_paged(const uint8_t* q, const float* q_scale, const uint8_t* k_cache,
+                                     const float* k_scale, const float* w, const int32_t* page_table,
+                                     const int32_t* seq_lens, int32_t B, int32_t max_pages,
+                                     int32_t page_size, int32_t num_pages, int32_t K, int32_t* out_idx,
+                                     void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_paged(q, q_scale, k_cache, k_scale, w, page_table, seq_lens, B, max_pages, page_size,
+                      num_pages, K, out_idx, workspace, workspace_bytes, static_cast<hipStream_t>(stream));
+}
+
+extern "C" int idx_topk_read_stats(const void* workspace, idx_topk_stats* out, void* stream) {
+  if (!workspace || !out) return IDX_EINVAL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const char* src = static_cast<const char*>(workspace) + sizeof(uint32_t) * kStatsOff;
+  if (hipMemcpyAsync(out, src, sizeof(idx_topk_stats), hipMemcpyDeviceToHost, s) != hipSuccess) return IDX_EHIP;
+  if (hipStreamSynchronize(s) != hipSuccess) return IDX_EHIP;
+  return IDX_OK;
+}
+
+extern "C" const char* idx_topk_strerror(int code) {
+  switch (code) {
+    case IDX_OK: return "ok";
+    case IDX_EINVAL: return "invalid argument";
+    case IDX_EUNSUPPORTED: return "unsupported geometry";
+    case IDX_EWORKSPACE: return "workspace missing or too small";
+    case IDX_EHIP: return "HIP launch or copy failed";
+    default: return "unknown error";
+  }
+}

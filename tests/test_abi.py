@@ -1,0 +1,93 @@
+"""The C-ABI library loads and exports every entry point include/*.h declares;
+host-side argument checks return the documented codes (no GPU needed: these
+calls return before any HIP call)."""
+import ctypes
+import glob
+import os
+import re
+
+import pytest
+
+import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+LIB = os.path.join(ROOT, "scoring_exact_top_amd", "libidxtopk.so")
+
+
+def _declared():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        src = open(h).read()
+        src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+        for m in re.finditer(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_\s\*]*?\b(idx_topk_[a-z_]+)\s*\(",
+                             src, flags=re.M):
+            names.add(m.group(1))
+    return names
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        pytest.fail("libidxtopk.so not built (run __graft_entry__.build())")
+    return ctypes.CDLL(LIB)
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _declared()
+    assert {"idx_topk_prefill", "idx_topk_decode_paged", "idx_topk_prefill_workspace",
+            "idx_topk_decode_workspace", "idx_topk_prefill_debug", "idx_topk_read_stats",
+            "idx_topk_strerror"} <= names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_header_constants_match_generators():
+    src = open(os.path.join(ROOT, "include", "idx_topk.h")).read()
+    stride = int(re.search(r"#define IDX_TOPK_SAMPLE_STRIDE (\d+)", src).group(1))
+    off = int(re.search(r"#define IDX_TOPK_SAMPLE_OFFSET (\d+)", src).group(1))
+    assert (stride, off) == (synth.SAMPLE_STRIDE, synth.SAMPLE_OFFSET)
+
+
+def test_workspace_queries(lib):
+    lib.idx_topk_prefill_workspace.restype = ctypes.c_size_t
+    lib.idx_topk_decode_workspace.restype = ctypes.c_size_t
+    a = lib.idx_topk_prefill_workspace(64, 8192, 2048)
+    b = lib.idx_topk_prefill_workspace(4096, 131072, 2048)
+    assert 0 < a < b < (1 << 31)
+    assert lib.idx_topk_prefill_workspace(64, 8192, 0) == 0
+    assert lib.idx_topk_prefill_workspace(64, 8192, 2049) == 0
+    assert lib.idx_topk_decode_workspace(16, 1024, 64, 2048) > 0
+    assert lib.idx_topk_decode_workspace(16, 1024, 32, 2048) == 0
+
+
+def test_host_argument_errors(lib):
+    vp = ctypes.c_void_p
+    f = lib.idx_topk_prefill
+    f.restype = ctypes.c_int
+    f.argtypes = [vp] * 7 + [ctypes.c_int32, vp, ctypes.c_int32, ctypes.c_int32, vp, ctypes.c_size_t, vp]
+    good = vp(1 << 20)          # never dereferenced: every case fails before any launch
+    bad_align = vp((1 << 20) + 8)
+    ws = vp(1 << 30)
+    big = 1 << 40
+    args = lambda **kw: [kw.get("q", good), None, kw.get("k", good), good, good, good, good,
+                         kw.get("K", 2048), good, kw.get("Q", 4), kw.get("N", 100),
+                         kw.get("ws", ws), kw.get("wsb", big), None]
+    assert f(*args(K=0)) == -1
+    assert f(*args(K=2049)) == -1
+    assert f(*args(Q=-1)) == -1
+    assert f(*args(q=None)) == -1
+    assert f(*args(q=bad_align)) == -1
+    assert f(*args(k=bad_align)) == -1
+    assert f(*args(ws=None)) == -3
+    assert f(*args(wsb=16)) == -3
+    assert f(*args(ws=vp((1 << 30) + 64))) == -1     # workspace not 256-byte aligned
+    assert f(*args(Q=0)) == 0                         # empty batch: nothing to do
+    d = lib.idx_topk_decode_paged
+    d.restype = ctypes.c_int
+    d.argtypes = [vp] * 7 + [ctypes.c_int32] * 5 + [vp, vp, ctypes.c_size_t, vp]
+    dargs = lambda ps=64, K=2048, B=2: [good] * 7 + [B, 8, ps, 16, K, good, ws, big, None]
+    assert d(*dargs(ps=32)) == -2
+    assert d(*dargs(K=0)) == -1
+    assert d(*dargs(B=0)) == 0
+    lib.idx_topk_strerror.restype = ctypes.c_char_p
+    assert lib.idx_topk_strerror(-3) == b"workspace missing or too small"

@@ -1,0 +1,139 @@
+"""Prefill parity on MI355X: the HIP path through the C ABI against the CPU
+oracle, element by element on seeded inputs."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from oracle import check
+
+pytestmark = pytest.mark.gpu
+
+from gpu_util import check_prefill_rows, log, run_prefill, sample_rows  # noqa: E402
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a GPU")
+    import scoring_exact_top_amd  # noqa: F401  (fails loudly if the library is missing)
+
+
+@pytest.fixture(scope="module")
+def e4m3():
+    return oracle.e4m3_table()
+
+
+def test_small_ragged_all_rows_debug(e4m3):
+    """Ragged random ranges (including empty and shorter-than-K rows) over
+    several tiles with a tail; every row, plus scores and bit-exact check."""
+    case = synth.random_case("ragged", 37, 5000, seed=21, K=1000, min_len=0)
+    case.row_end[3] = case.row_start[3]          # an empty row
+    log("case", case.name, case.Q, case.N)
+    r = run_prefill(case, scores=True)
+    rep = check_prefill_rows(case, r["out"], np.arange(case.Q), gpu_scores=r["scores"], e4m3=e4m3)
+    log("ragged", rep, r["stats"])
+    assert r["stats"]["rows"] == case.Q and r["stats"]["bad_rows"] == 0
+
+
+@pytest.mark.parametrize("K", [1, 7, 64, 2048])
+def test_k_values(K):
+    case = synth.random_case("kvals", 9, 3000, seed=22 + K, K=K, min_len=0)
+    log("K", K)
+    r = run_prefill(case)
+    check_prefill_rows(case, r["out"], np.arange(case.Q))
+
+
+def test_prefill_smoke_workload_full(e4m3):
+    """64 rows at positions 8128..8191 of 8192 keys: every row, scores too."""
+    case = synth.prefill_smoke(0)
+    log("case", case.name)
+    r = run_prefill(case, scores=True)
+    rep = check_prefill_rows(case, r["out"], np.arange(case.Q), gpu_scores=r["scores"], e4m3=e4m3)
+    log("smoke", rep, r["stats"])
+    r2 = run_prefill(case)
+    assert np.array_equal(np.sort(r2["out"], axis=1), np.sort(r["out"], axis=1))
+
+
+def test_forced_underflow_goes_to_repair():
+    case = synth.random_case("under", 12, 9000, seed=23, K=512, min_len=3000)
+    log("case", case.name)
+    r = run_prefill(case, force_tau=float("inf"))
+    assert r["stats"]["underflow"] == case.Q and r["stats"]["repaired"] == case.Q
+    check_prefill_rows(case, r["out"], np.arange(case.Q))
+
+
+def test_forced_overflow_goes_to_repair():
+    case = synth.random_case("over", 12, 9000, seed=24, K=512, min_len=3000)
+    log("case", case.name)
+    r = run_prefill(case, force_tau=float("-inf"), lds_cap=1024, spill_cap=-1)
+    assert r["stats"]["overflow"] == case.Q and r["stats"]["repaired"] == case.Q
+    check_prefill_rows(case, r["out"], np.arange(case.Q))
+
+
+def test_spill_area_is_merged():
+    """A small on-chip capacity pushes candidates into the spill area; the
+    certificate still holds, and the selection merges both sources."""
+    case = synth.random_case("spill", 10, 6000, seed=25, K=700, min_len=2500, max_len=4500)
+    log("case", case.name)
+    r = run_prefill(case, force_tau=float("-inf"), lds_cap=512, spill_cap=4096, scores=True)
+    st = r["stats"]
+    assert st["spilled"] > 0 and st["repaired"] == 0, st
+    check_prefill_rows(case, r["out"], np.arange(case.Q))
+
+
+def test_invalid_ranges_give_minus_one():
+    case = synth.random_case("badrange", 6, 1000, seed=26, K=64, min_len=10)
+    case.row_start[1], case.row_end[1] = 50, 40        # start > end
+    case.row_end[4] = case.N + 5                        # end > N
+    log("case", case.name)
+    r = run_prefill(case)
+    assert np.all(r["out"][1] == -1) and np.all(r["out"][4] == -1)
+    assert r["stats"]["bad_rows"] == 2
+    check_prefill_rows(case, r["out"], [0, 2, 3, 5])
+
+
+def test_identical_keys_get_identical_scores():
+    case = synth.causal_case("ties_small", 8, 6000, seed=27, key_mode="ties16", K=300)
+    log("case", case.name)
+    r = run_prefill(case, scores=True)
+    keys = np.concatenate([case.k8, case.k_scale.view(np.uint8).reshape(-1, 4)], axis=1)
+    _, group = np.unique(keys, axis=0, return_inverse=True)
+    group = group.reshape(-1)
+    for t in range(case.Q):
+        s1 = case.row_end[t]
+        S = r["scores"][t, :s1]
+        for g in range(16):
+            v = S[group[:s1] == g]
+            assert v.size == 0 or np.all(v.view(np.uint32) == v[0].view(np.uint32))
+    check_prefill_rows(case, r["out"], np.arange(case.Q))
+
+
+@pytest.mark.parametrize("name", ["prefill_chunk", "long_prefill"])
+def test_full_size_sampled_rows(name):
+    """Full-size workloads in the benchmark's launch configuration; the oracle
+    checks a sample of rows (first, middle, last and random)."""
+    case = synth.WORKLOADS[name](0)
+    log("case", case.name, case.Q, case.N)
+    r = run_prefill(case)
+    log("stats", r["stats"])
+    assert r["stats"]["rows"] == case.Q
+    rows = sample_rows(case.Q, 12, seed=1)
+    rep = check_prefill_rows(case, r["out"], rows)
+    log(name, rep)
+    # structure of every row
+    for t in range(case.Q):
+        check.check_structure(r["out"][t], int(case.row_start[t]), int(case.row_end[t]), case.K)
+
+
+def test_adversarial_subcalls_sampled_rows():
+    for case in synth.adversarial(0) + [synth.adversarial_decoy(0, Q=64)]:
+        log("case", case.name, case.Q, case.N)
+        r = run_prefill(case)
+        log("stats", r["stats"])
+        rows = sample_rows(case.Q, 6, seed=2)
+        rep = check_prefill_rows(case, r["out"], rows)
+        log(case.name, rep)
+        if case.name == "adversarial_decoy":
+            assert r["stats"]["underflow"] > 0 and r["stats"]["repaired"] > 0
