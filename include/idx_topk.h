@@ -90,6 +90,8 @@ typedef struct {
   float tau_value;
   int32_t lds_cap;     /* >0: on-chip candidate capacity per row (<= default)   */
   int32_t spill_cap;   /* >0: spill capacity per row (<= default); -1: none     */
+  void *ev_main_start; /* hipEvent_t or NULL: recorded on `stream` right before */
+  void *ev_main_stop;  /*   and right after the fused main kernel (timing only) */
 } idx_topk_opts;
 
 /* Bytes of workspace idx_topk_prefill needs for Q rows over N keys. */

@@ -34,7 +34,8 @@ _sz = ctypes.c_size_t
 
 class Opts(ctypes.Structure):
     _fields_ = [("force_tau", ctypes.c_int32), ("tau_value", ctypes.c_float),
-                ("lds_cap", ctypes.c_int32), ("spill_cap", ctypes.c_int32)]
+                ("lds_cap", ctypes.c_int32), ("spill_cap", ctypes.c_int32),
+                ("ev_main_start", ctypes.c_void_p), ("ev_main_stop", ctypes.c_void_p)]
 
 
 class Stats(ctypes.Structure):
@@ -128,10 +129,17 @@ def prefill(q8, q_scale, k8, k_scale, w, row_start, row_end, K: int, out=None, w
 
 def prefill_debug(q8, q_scale, k8, k_scale, w, row_start, row_end, K: int, out=None,
                   workspace=None, stream=None, scores_out=None, tau_out=None,
-                  force_tau: Optional[float] = None, lds_cap: int = 0, spill_cap: int = 0):
-    """idx_topk_prefill_debug: also emits FP32 scores [Q,N] and thresholds [Q]."""
+                  force_tau: Optional[float] = None, lds_cap: int = 0, spill_cap: int = 0,
+                  main_events=None):
+    """idx_topk_prefill_debug: also emits FP32 scores [Q,N] and thresholds [Q].
+
+    main_events: optional (start, stop) pair of torch.cuda.Event(enable_timing=True)
+    recorded around the fused main kernel."""
+    ev0 = ev1 = None
+    if main_events is not None:
+        ev0, ev1 = (ctypes.c_void_p(e.cuda_event) for e in main_events)
     opts = Opts(1 if force_tau is not None else 0, float(force_tau or 0.0), int(lds_cap),
-                int(spill_cap))
+                int(spill_cap), ev0, ev1)
     return _prefill(q8, q_scale, k8, k_scale, w, row_start, row_end, K, out, workspace, stream,
                     debug=True, scores_out=scores_out, tau_out=tau_out, opts=opts)
 

@@ -65,6 +65,8 @@ static int prefill_common(const uint8_t* q, const float* q_scale, const uint8_t*
     if (opts->spill_cap == -1) A.spill_cap = 0;
     A.force_tau = opts->force_tau ? 1 : 0;
     A.tau_value = opts->tau_value;
+    A.ev_main_start = static_cast<hipEvent_t>(opts->ev_main_start);
+    A.ev_main_stop = static_cast<hipEvent_t>(opts->ev_main_stop);
   }
   A.cap_total = A.lds_cap + A.spill_cap;
   hipStream_t s = static_cast<hipStream_t>(stream);

@@ -52,6 +52,7 @@ struct PrefillArgs {
   float* dbg_scores;    // [Q][N] or null
   int32_t force_tau;
   float tau_value;
+  hipEvent_t ev_main_start, ev_main_stop;  // host-side only: timing hooks
 };
 
 struct SampleGeom {

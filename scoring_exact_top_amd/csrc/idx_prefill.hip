@@ -183,7 +183,9 @@ __global__ __launch_bounds__(kWG) void k_prefill_repair(PrefillArgs A) {
 int launch_prefill(const PrefillArgs& A, hipStream_t stream) {
   if (A.Q == 0) return IDX_OK;
   hipLaunchKernelGGL(k_prefill_tau, dim3(A.Q), dim3(kWG), 0, stream, A);
+  if (A.ev_main_start && hipEventRecord(A.ev_main_start, stream) != hipSuccess) return IDX_EHIP;
   hipLaunchKernelGGL(k_prefill_fused<kBQ>, dim3((A.Q + kBQ - 1) / kBQ), dim3(kWG), 0, stream, A);
+  if (A.ev_main_stop && hipEventRecord(A.ev_main_stop, stream) != hipSuccess) return IDX_EHIP;
   hipLaunchKernelGGL(k_prefill_repair, dim3(repair_grid(A.Q)), dim3(kWG), 0, stream, A);
   return hipGetLastError() == hipSuccess ? IDX_OK : IDX_EHIP;
 }
