@@ -11,7 +11,7 @@ static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 static inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 struct PrefillLayout {
-  size_t ctrl, tau, fail, skey, sidx, scratch, total;
+  size_t ctrl, tau, fail, skey, cidx, scratch, kt, total;
 };
 
 static PrefillLayout prefill_layout(int32_t Q, int32_t N) {
@@ -20,9 +20,10 @@ static PrefillLayout prefill_layout(int32_t Q, int32_t N) {
   L.ctrl = o; o = align256(o + sizeof(uint32_t) * kCtrlWords);
   L.tau = o; o = align256(o + sizeof(float) * (size_t)Q);
   L.fail = o; o = align256(o + sizeof(int32_t) * (size_t)Q);
-  L.skey = o; o = align256(o + sizeof(uint32_t) * (size_t)Q * kSpillCap);
-  L.sidx = o; o = align256(o + sizeof(int32_t) * (size_t)Q * kSpillCap);
+  L.skey = o; o = align256(o + sizeof(uint32_t) * (size_t)Q * kCandCap);
+  L.cidx = o; o = align256(o + sizeof(int32_t) * (size_t)Q * kCandCap);
   L.scratch = o; o = align256(o + sizeof(uint32_t) * (size_t)repair_grid(Q) * (size_t)N);
+  L.kt = o; o = align256(o + (size_t)((N + 63) / 64) * 64 * 128);
   L.total = o;
   return L;
 }
@@ -50,9 +51,10 @@ static int prefill_common(const uint8_t* q, const float* q_scale, const uint8_t*
   A.ctrl = reinterpret_cast<uint32_t*>(ws + L.ctrl);
   A.tau = reinterpret_cast<float*>(ws + L.tau);
   A.fail_list = reinterpret_cast<int32_t*>(ws + L.fail);
-  A.spill_key = reinterpret_cast<uint32_t*>(ws + L.skey);
-  A.spill_idx = reinterpret_cast<int32_t*>(ws + L.sidx);
+  A.cand_key = reinterpret_cast<uint32_t*>(ws + L.skey);
+  A.cand_idx = reinterpret_cast<int32_t*>(ws + L.cidx);
   A.scratch = reinterpret_cast<uint32_t*>(ws + L.scratch);
+  A.kt = reinterpret_cast<uint8_t*>(ws + L.kt);
   A.out = out_idx;
   A.dbg_scores = scores_out;
   A.lds_cap = kLdsCap;

@@ -1,24 +1,34 @@
 // Device building blocks shared by the prefill and decode kernels (gfx950).
 //
-// Scoring (Fused Indexer Top-k page, "1.1 The problem" equation):
-//   I[t,s] = k_scale[s] * sum_j w'[t,j] * max(dot8(q8[t,j], k8[s]), 0),
-//   w'[t,j] = w[t,j] * q_scale[t,j]
-// Positive scales commute with ReLU, so both scales leave the dot product and
-// the 128-deep FP8 contraction is one v_mfma_f32_16x16x128_f8f6f4 per 16 heads
-// x 16 keys.  A (16 heads x 128) lives in registers for the whole key loop;
-// B (128 x 16 keys) comes straight from global memory, each lane holding the
-// 32 contiguous bytes [32*(lane/16), +32) of key lane%16.  Operand lane maps
-// for A and B are the same, so any consistent split of the 128-byte vectors
-// gives the same dot product.
+// Score of query row t against key s (Fused Indexer Top-k page, "1.1 The
+// problem" equation, with the FP8 operands dequantised by their scales as in
+// "2.3 Problem definition"):
 //
-// The 16x16 f32 result puts head 4*(lane/16)+r of a 16-head block in register
-// r of the lane that owns key lane%16.  Each lane therefore ReLUs and weights
-// its 16 heads of a key, and four partial sums of the same key sit in lanes
-// that differ in bits 4 and 5.  Four 16-key sub-tiles are combined by a
-// reduce-scatter built on v_permlane32_swap / v_permlane16_swap so that after
-// three adds lane l owns the complete score of key l of the 64-key tile, with
-// the same addition tree (g0+g2)+(g1+g3) for every key: identical keys give
-// bit-identical scores wherever they sit.
+//   I[t,s] = k_scale[s] * sum_j w'_j * max(c_j, 0),   w'_j = w[t,j] * q_scale[t,j],
+//   c_j    = dot(e4m3(q8[t,j,:]), e4m3(k8[s,:]))      (both scales are > 0)
+//
+// The ReLU is evaluated as max(c,0) = (c + |c|)/2, so that
+//
+//   sum_j w'_j max(c_j,0) = sum_j (w'_j/2)|c_j|  +  (1/2) u.k,   u = sum_j w'_j q_j.
+//
+// The first sum costs one VALU op per head (an FMA with an |x| source
+// modifier); the linear term u.k goes to the matrix core: u is split into
+// eight e4m3 vectors with FP32 scales, u ~= sum_m sigma_m e4m3(u8_m), residual
+// below 16^-8 |u|_max, and these eight rows form a fifth 16-row A block.
+//
+// Every 128-deep FP8 contraction is one v_mfma_f32_16x16x128_f8f6f4 per 16
+// rows x 16 keys.  A (rows x 128) lives in registers for the whole key loop;
+// B (128 x 16 keys) comes from global memory through a buffer resource, lane l
+// holding the 32 contiguous bytes [32*(l/16), +32) of key l%16 (A uses the
+// same lane map, so any consistent split of the 128 bytes gives the same dot
+// product).  The 16x16 f32 result puts row 4*(l/16)+r of a block in register r
+// of the lane that owns key l%16: each lane weights its 16 heads and its 4
+// rows of the u block, and the four partial sums of a key sit in lanes that
+// differ in bits 4 and 5.  Four 16-key sub-tiles are combined by a
+// reduce-scatter on v_permlane32_swap / v_permlane16_swap so that lane l ends
+// with key l of the 64-key tile, through the same addition tree
+// (g0+g2)+(g1+g3) for every key: identical keys give bit-identical scores
+// wherever they sit.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -26,16 +36,20 @@
 namespace idxk {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
 constexpr int kH = 64;
 constexpr int kD = 128;
 constexpr int kKmax = 2048;
-constexpr int kWG = 256;     // threads per workgroup
-constexpr int kWaves = 4;    // waves per workgroup (one per SIMD)
-constexpr int kTile = 64;    // keys per wave-iteration (4 MFMA sub-tiles of 16)
+constexpr int kWG = 256;     // threads per workgroup of the 4-wave kernels
+constexpr int kWaves = 4;
+constexpr int kTile = 64;    // keys per tile (4 MFMA sub-tiles of 16)
+constexpr int kUTerms = 8;   // e4m3 terms of the linear vector u
+constexpr int kBlocks = 5;   // A blocks per tile: 4 head blocks + the u block
 
-// Sub-tile c of a 64-key tile covers keys [kSubOff[c], +16).  This order makes
+// Sub-tile c of a 64-key tile covers keys [sub_off(c), +16).  This order makes
 // the reduce-scatter below land key l in lane l.
 __device__ __forceinline__ int sub_off(int c) { return c == 0 ? 0 : c == 1 ? 32 : c == 2 ? 16 : 48; }
 
@@ -58,6 +72,13 @@ __device__ __forceinline__ uint32_t rank_in(uint64_t ball) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(ball >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)ball, 0u));
 }
 
+// Make this wave's LDS writes visible to all its lanes before they read.
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 __device__ __forceinline__ v8i ld32(const uint8_t* p) {
   const uint4* v = reinterpret_cast<const uint4*>(p);
   uint4 x = v[0], y = v[1];
@@ -67,51 +88,241 @@ __device__ __forceinline__ v8i ld32(const uint8_t* p) {
   return r;
 }
 
+__device__ __forceinline__ v8i cat8(v4i x, v4i y) {
+  v8i r;
+  r[0] = x[0]; r[1] = x[1]; r[2] = x[2]; r[3] = x[3];
+  r[4] = y[0]; r[5] = y[1]; r[6] = y[2]; r[7] = y[3];
+  return r;
+}
+
+// OCP e4m3fn decode from the bit fields (S.EEEE.MMM, bias 7, subnormal
+// m * 2^-9).  Codes are never NaN here.
+__device__ __forceinline__ float e4m3_dec(uint32_t c) {
+  const uint32_t e = (c >> 3) & 15u, m = c & 7u;
+  const float mag = e == 0 ? (float)m * 0.001953125f : __uint_as_float(((e + 120u) << 23) | (m << 20));
+  return (c & 0x80u) ? -mag : mag;
+}
+
+// Nearest e4m3fn code (ties to even) of v, |v| clamped to 448.
+__device__ __forceinline__ uint32_t e4m3_enc(float v) {
+  const uint32_t s = v < 0.f ? 0x80u : 0u;
+  const float a = fminf(fabsf(v), 448.f);
+  if (a < 0.015625f) return s | (uint32_t)rintf(a * 512.f);   // 8 -> 0x08, the smallest normal
+  int e = (int)((__float_as_uint(a) >> 23) & 255u) - 127;       // -6 .. 8
+  const float mant = __uint_as_float((__float_as_uint(a) & 0x007fffffu) | 0x3f800000u);  // [1,2)
+  uint32_t m3 = (uint32_t)rintf((mant - 1.f) * 8.f);
+  if (m3 == 8u) { m3 = 0u; ++e; }
+  return s | ((uint32_t)(e + 7) << 3) | m3;
+}
+
 // One query row as held by a lane: A operands of the four 16-head blocks and
-// the folded weights w' of the 16 heads whose results land in this lane.
+// of the u block, the halved weights w'/2 of the 16 heads whose results land in
+// this lane, and the halved scales sigma/2 of the 4 u-block rows it holds.
 struct QOp {
   v8i a[4];
-  float wq[16];
+  v8i au;
+  float wh[16];
+  float sh[4];
 };
 
-__device__ __forceinline__ void load_q(QOp& o, const uint8_t* q, const float* q_scale, const float* w,
-                                       int64_t t, uint32_t lane) {
+// Prepare query row t.  All 64 lanes of the wave call this; `scratch` is
+// 8*128 bytes of this wave's LDS.  u is accumulated over heads in order
+// j = 0..63 in FP32; term m takes sigma_m = max|r_m| / 448 and the nearest
+// e4m3 codes of r_m / sigma_m, then r_{m+1} = r_m - sigma_m * dec(code).
+// Two query rows as held by a lane, sharing one u block: rows 0..7 carry the
+// first row's terms, rows 8..15 the second's.  sh[x] is zero in the lanes
+// that hold the other row's u rows, so each row picks up only its own terms.
+struct QOp2 {
+  v8i a[2][4];
+  v8i au;
+  float wh[2][16];
+  float sh[2][4];
+};
+
+// Linear vector u of row t at dims lane and lane+64, split into kUTerms
+// e4m3 terms written to codes[m*128 + d]; returns the scales in sig.
+__device__ __forceinline__ void split_u(const uint8_t* q, const float* q_scale, const float* w, int64_t t,
+                                        uint32_t lane, uint8_t* codes, float (&sig)[kUTerms]) {
+  const uint8_t* base = q + t * (kH * kD);
+  float u0 = 0.f, u1 = 0.f;
+  for (int j = 0; j < kH; ++j) {
+    const float qs = q_scale ? q_scale[t * kH + j] : 1.0f;
+    const float wj = w[t * kH + j] * qs;
+    u0 = fmaf(wj, e4m3_dec(base[j * kD + lane]), u0);
+    u1 = fmaf(wj, e4m3_dec(base[j * kD + 64 + lane]), u1);
+  }
+#pragma unroll
+  for (int m = 0; m < kUTerms; ++m) {
+    float amax = fmaxf(fabsf(u0), fabsf(u1));
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
+    const float s = amax / 448.f;
+    const uint32_t c0 = s > 0.f ? e4m3_enc(u0 / s) : 0u;
+    const uint32_t c1 = s > 0.f ? e4m3_enc(u1 / s) : 0u;
+    codes[m * kD + lane] = (uint8_t)c0;
+    codes[m * kD + 64 + lane] = (uint8_t)c1;
+    u0 = fmaf(-s, e4m3_dec(c0), u0);
+    u1 = fmaf(-s, e4m3_dec(c1), u1);
+    sig[m] = s;
+  }
+}
+
+__device__ __forceinline__ void head_ops(v8i (&a)[4], float (&wh)[16], const uint8_t* q, const float* q_scale,
+                                         const float* w, int64_t t, uint32_t lane) {
   const uint8_t* base = q + t * (kH * kD);
   const uint32_t g = lane >> 4, i = lane & 15;
 #pragma unroll
   for (int b = 0; b < 4; ++b) {
-    o.a[b] = ld32(base + (16 * b + i) * kD + 32 * g);
+    a[b] = ld32(base + (16 * b + i) * kD + 32 * g);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int j = 16 * b + 4 * g + r;
       const float qs = q_scale ? q_scale[t * kH + j] : 1.0f;
-      o.wq[4 * b + r] = w[t * kH + j] * qs;
+      wh[4 * b + r] = 0.5f * (w[t * kH + j] * qs);
     }
   }
 }
 
-// Partial weighted-ReLU sum over this lane's 16 heads for key lane%16 of the
-// sub-tile whose B operand is kb.
-__device__ __forceinline__ float partial16(const QOp& o, const v8i& kb) {
+// Prepare rows t0 and t1 (all 64 lanes; scratch = 16*128 bytes of LDS).
+__device__ __forceinline__ void prepare_q2(QOp2& o, const uint8_t* q, const float* q_scale, const float* w,
+                                           int64_t t0, int64_t t1, uint32_t lane, uint8_t* scratch) {
+  head_ops(o.a[0], o.wh[0], q, q_scale, w, t0, lane);
+  head_ops(o.a[1], o.wh[1], q, q_scale, w, t1, lane);
+  float s0[kUTerms], s1[kUTerms];
+  split_u(q, q_scale, w, t0, lane, scratch, s0);
+  split_u(q, q_scale, w, t1, lane, scratch + kUTerms * kD, s1);
+  wave_sync();
+  const uint32_t g = lane >> 4, i = lane & 15;
+  const uint32_t* src = reinterpret_cast<const uint32_t*>(scratch + i * kD + 32 * g);
+#pragma unroll
+  for (int k = 0; k < 8; ++k) o.au[k] = (int)src[k];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int row = 4 * (int)g + r;  // 0..15
+    float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+    for (int m = 0; m < kUTerms; ++m) {
+      a0 = row == m ? s0[m] : a0;
+      a1 = row == m + kUTerms ? s1[m] : a1;
+    }
+    o.sh[0][r] = 0.5f * a0;
+    o.sh[1][r] = 0.5f * a1;
+  }
+  wave_sync();
+}
+
+// Prepare query row t (all 64 lanes; scratch = 8*128 bytes of LDS).  u is
+// accumulated over heads in order j = 0..63 in FP32; term m takes
+// sigma_m = max|r_m| / 448 and the nearest e4m3 codes of r_m / sigma_m, then
+// r_{m+1} = r_m - sigma_m * dec(code).
+__device__ __forceinline__ void prepare_q(QOp& o, const uint8_t* q, const float* q_scale, const float* w,
+                                          int64_t t, uint32_t lane, uint8_t* scratch) {
+  head_ops(o.a, o.wh, q, q_scale, w, t, lane);
+  float sig[kUTerms];
+  split_u(q, q_scale, w, t, lane, scratch, sig);
+  wave_sync();
+  const uint32_t g = lane >> 4, i = lane & 15;
+  if (i < (uint32_t)kUTerms) {
+    const uint32_t* src = reinterpret_cast<const uint32_t*>(scratch + i * kD + 32 * g);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) o.au[k] = (int)src[k];
+  } else {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) o.au[k] = 0;
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int row = 4 * (int)g + r;
+    float sr = 0.f;
+#pragma unroll
+    for (int m = 0; m < kUTerms; ++m) sr = row == m ? sig[m] : sr;
+    o.sh[r] = 0.5f * sr;
+  }
+  wave_sync();
+}
+
+// Keys of one 64-key tile as B operands plus the scale of this lane's key.
+struct KeyTile {
+  v8i kb[4];
+  float ks;
+};
+
+// Buffer resources over the key codes and key scales of `nkeys` keys.  Reads
+// past the end return 0 (and are masked by the callers).
+struct KeyBuf {
+  rsrc_t k, ks;
+};
+__device__ __forceinline__ KeyBuf make_keybuf(const uint8_t* k, const float* k_scale, int64_t nkeys) {
+  const int64_t nk = nkeys < 0 ? 0 : nkeys;
+  const int kb = (int)(nk * kD > 0x7fffffffLL ? 0x7fffffffLL : nk * kD);
+  const int sb = (int)(nk * 4 > 0x7fffffffLL ? 0x7fffffffLL : nk * 4);
+  return KeyBuf{__builtin_amdgcn_make_buffer_rsrc((void*)k, (short)0, kb, 0x00020000),
+                __builtin_amdgcn_make_buffer_rsrc((void*)k_scale, (short)0, sb, 0x00020000)};
+}
+
+// Tile of 64 consecutive keys starting at key index `base` (wave-uniform).
+// Lane offsets are loop invariant; the tile offset is a scalar.
+__device__ __forceinline__ void load_tile(KeyTile& t, const KeyBuf& kbuf, int base, uint32_t lane) {
+  const int voff = (int)(lane & 15) * kD + 32 * (int)(lane >> 4);
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int soff = (base + sub_off(c)) * kD;
+    const v4i x = __builtin_amdgcn_raw_buffer_load_b128(kbuf.k, voff, soff, 0);
+    const v4i y = __builtin_amdgcn_raw_buffer_load_b128(kbuf.k, voff + 16, soff, 0);
+    t.kb[c] = cat8(x, y);
+  }
+  t.ks = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(kbuf.ks, (int)lane * 4, base * 4, 0));
+}
+
+// Relaid keys: tile j occupies bytes [8192 j, 8192 (j+1)) as eight 1 KiB
+// blocks, block 2c+h holding, for lane l = 0..63, the 16 bytes that lane l
+// loads as the h-th half of its B operand of sub-tile c (key sub_off(c) +
+// l%16, bytes 32*(l/16) + 16h .. +16).  A load instruction then reads one
+// contiguous KiB instead of 64 lanes striding 128 bytes apart.
+__device__ __forceinline__ int relaid_src_offset(int tile, int blk, int l) {
+  const int c = blk >> 1, h = blk & 1;
+  return ((tile << 6) + sub_off(c) + (l & 15)) * kD + 32 * (l >> 4) + 16 * h;
+}
+
+// Load relaid tile `tile` (wave-uniform); scales from the original array.
+__device__ __forceinline__ void load_tile_relaid(KeyTile& t, rsrc_t kt, rsrc_t ks, int tile, uint32_t lane) {
+  const int soff = tile * (kTile * kD);
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const v4i x = __builtin_amdgcn_raw_buffer_load_b128(kt, (int)lane * 16, soff + (2 * c) * 1024, 0);
+    const v4i y = __builtin_amdgcn_raw_buffer_load_b128(kt, (int)lane * 16, soff + (2 * c + 1) * 1024, 0);
+    t.kb[c] = cat8(x, y);
+  }
+  t.ks = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(ks, (int)lane * 4, tile * 256, 0));
+}
+
+// Tile of 64 arbitrary keys: key_of(i) gives the key index of tile slot i.
+template <class F>
+__device__ __forceinline__ void load_tile_gather(KeyTile& t, const KeyBuf& kbuf, const F& key_of, uint32_t lane) {
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int voff = key_of(sub_off(c) + (int)(lane & 15)) * kD + 32 * (int)(lane >> 4);
+    const v4i x = __builtin_amdgcn_raw_buffer_load_b128(kbuf.k, voff, 0, 0);
+    const v4i y = __builtin_amdgcn_raw_buffer_load_b128(kbuf.k, voff + 16, 0, 0);
+    t.kb[c] = cat8(x, y);
+  }
+  t.ks = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(kbuf.ks, key_of((int)lane) * 4, 0, 0));
+}
+
+// MFMA part of a tile: 4 sub-tiles x 5 blocks into separate accumulators.
+__device__ __forceinline__ void tile_mfma(const QOp& o, const v8i (&kb)[4], v4f (&acc)[20]) {
   const v4f z = {0.f, 0.f, 0.f, 0.f};
-  v4f c0 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(o.a[0], kb, z, 0, 0, 0, 0, 0, 0);
-  v4f c1 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(o.a[1], kb, z, 0, 0, 0, 0, 0, 0);
-  v4f c2 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(o.a[2], kb, z, 0, 0, 0, 0, 0, 0);
-  v4f c3 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(o.a[3], kb, z, 0, 0, 0, 0, 0, 0);
-  float p = 0.f;
 #pragma unroll
-  for (int r = 0; r < 4; ++r) p = fmaf(o.wq[r], fmaxf(c0[r], 0.f), p);
+  for (int c = 0; c < 4; ++c) {
 #pragma unroll
-  for (int r = 0; r < 4; ++r) p = fmaf(o.wq[4 + r], fmaxf(c1[r], 0.f), p);
-#pragma unroll
-  for (int r = 0; r < 4; ++r) p = fmaf(o.wq[8 + r], fmaxf(c2[r], 0.f), p);
-#pragma unroll
-  for (int r = 0; r < 4; ++r) p = fmaf(o.wq[12 + r], fmaxf(c3[r], 0.f), p);
-  return p;
+    for (int b = 0; b < 4; ++b)
+      acc[5 * c + b] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(o.a[b], kb[c], z, 0, 0, 0, 0, 0, 0);
+    acc[5 * c + 4] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(o.au, kb[c], z, 0, 0, 0, 0, 0, 0);
+  }
 }
 
 // p0..p3: partials of sub-tiles 0..3 (keys 0-15, 32-47, 16-31, 48-63).
-// Returns the full head sum of key `lane` of the 64-key tile.
+// Returns the full sum of key `lane` of the 64-key tile.
 __device__ __forceinline__ float reduce_scatter4(float p0, float p1, float p2, float p3) {
   auto x = __builtin_amdgcn_permlane32_swap(__float_as_uint(p0), __float_as_uint(p1), false, false);
   const float A = __uint_as_float(x[0]) + __uint_as_float(x[1]);
@@ -121,14 +332,30 @@ __device__ __forceinline__ float reduce_scatter4(float p0, float p1, float p2, f
   return __uint_as_float(z[0]) + __uint_as_float(z[1]);
 }
 
-// Scores (before k_scale) of the 64 keys whose B operands are kb[0..3]; lane
-// l receives key l.
-__device__ __forceinline__ float tile_sum(const QOp& o, const v8i (&kb)[4]) {
-  const float p0 = partial16(o, kb[0]);
-  const float p1 = partial16(o, kb[1]);
-  const float p2 = partial16(o, kb[2]);
-  const float p3 = partial16(o, kb[3]);
-  return reduce_scatter4(p0, p1, p2, p3);
+// Epilogue of tile_mfma: per lane and sub-tile, sum over its 16 heads of
+// (w'/2)|c| then over its 4 u-block rows of (sigma/2) d, in this fixed order;
+// then the reduce-scatter.  Lane l returns key l's sum (before k_scale).
+__device__ __forceinline__ float tile_epilogue(const QOp& o, const v4f (&acc)[20]) {
+  float p[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    float x = 0.f;
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) x = fmaf(o.wh[4 * b + r], fabsf(acc[5 * c + b][r]), x);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) x = fmaf(o.sh[r], acc[5 * c + 4][r], x);
+    p[c] = x;
+  }
+  return reduce_scatter4(p[0], p[1], p[2], p[3]);
+}
+
+// Score of the tile (lane l: key l), k_scale applied.
+__device__ __forceinline__ float tile_score(const QOp& o, const KeyTile& t) {
+  v4f acc[20];
+  tile_mfma(o, t.kb, acc);
+  return tile_epilogue(o, acc) * t.ks;
 }
 
 // ------------------------------------------------------------- histograms
@@ -263,6 +490,82 @@ __device__ void emit_selection(const Src& src, int n, const SelResult& sel, int 
     if (eq && (int)pe < sel.rem) out[eq_base + pe] = src.id(i);
   }
   for (int i = kr + tid; i < K; i += kWG) out[i] = -1;
+}
+
+// ------------------------------------------------- wave-level selection
+
+
+// Radix select run by ONE wave over its own 256-bin LDS histogram, so that
+// several rows of a workgroup are selected concurrently without workgroup
+// barriers.  Same contract as radix_select (1 <= rem <= n).
+template <typename Src>
+__device__ SelResult wave_radix_select(const Src& src, int n, int rem, uint32_t* hist, uint32_t lane,
+                                       bool allow_early) {
+  uint32_t prefix = 0, mask = 0;
+#pragma unroll 1
+  for (int shift = 24; shift >= 0; shift -= 8) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) hist[lane + 64 * i] = 0u;
+    wave_sync();
+    for (int base = 0; base < n; base += 64) {
+      const int i = base + (int)lane;
+      const bool v = i < n;
+      const uint32_t key = v ? src.key(i) : 0u;
+      hist_add(hist, (key >> shift) & 255u, v && ((key & mask) == prefix));
+    }
+    wave_sync();
+    const uint32_t h0 = hist[4 * lane + 0], h1 = hist[4 * lane + 1];
+    const uint32_t h2 = hist[4 * lane + 2], h3 = hist[4 * lane + 3];
+    const uint32_t s = h0 + h1 + h2 + h3;
+    uint32_t suf = s;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const uint32_t o = __shfl_down(suf, off, 64);
+      if (lane + off < 64) suf += o;
+    }
+    const uint32_t above_lane = suf - s;
+    const uint32_t r = (uint32_t)rem;
+    const bool owner = above_lane < r && r <= suf;
+    uint32_t acc = above_lane, b = 4 * lane, hb = h0;
+    if (acc + h3 >= r) { b = 4 * lane + 3; hb = h3; }
+    else if ((acc += h3) + h2 >= r) { b = 4 * lane + 2; hb = h2; }
+    else if ((acc += h2) + h1 >= r) { b = 4 * lane + 1; hb = h1; }
+    else { acc += h1; }
+    const int ol = __ffsll((unsigned long long)__ballot(owner)) - 1;
+    const uint32_t bb = (uint32_t)__builtin_amdgcn_readlane((int)b, ol);
+    const uint32_t above = (uint32_t)__builtin_amdgcn_readlane((int)acc, ol);
+    const uint32_t inb = (uint32_t)__builtin_amdgcn_readlane((int)hb, ol);
+    prefix |= bb << shift;
+    mask |= 0xFFu << shift;
+    rem -= (int)above;
+    wave_sync();  // histogram reads done before the next pass clears it
+    if (allow_early && (int)inb == rem) break;
+  }
+  return SelResult{prefix, mask, rem};
+}
+
+// Wave-level emit: same output layout as emit_selection.
+template <typename Src>
+__device__ void wave_emit(const Src& src, int n, const SelResult& sel, int kr, int K, int32_t* out,
+                          uint32_t lane) {
+  uint32_t gt_cnt = 0, eq_cnt = 0;
+  const int eq_base = kr - sel.rem;
+  for (int base = 0; base < n; base += 64) {
+    const int i = base + (int)lane;
+    const bool v = i < n;
+    const uint32_t key = v ? src.key(i) : 0u;
+    const uint32_t mk = key & sel.mask;
+    const bool gt = v && mk > sel.prefix;
+    const bool eq = v && mk == sel.prefix;
+    const uint64_t bg = __ballot(gt);
+    if (gt) out[gt_cnt + rank_in(bg)] = src.id(i);
+    gt_cnt += (uint32_t)__popcll(bg);
+    const uint64_t be = __ballot(eq);
+    const uint32_t pe = eq_cnt + rank_in(be);
+    if (eq && (int)pe < sel.rem) out[eq_base + pe] = src.id(i);
+    eq_cnt += (uint32_t)__popcll(be);
+  }
+  for (int i = kr + (int)lane; i < K; i += 64) out[i] = -1;
 }
 
 }  // namespace idxk

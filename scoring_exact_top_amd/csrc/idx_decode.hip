@@ -53,6 +53,7 @@ struct SrcGlobal {
 __global__ __launch_bounds__(kWG) void k_decode_prep(DecodeArgs A) {
   __shared__ uint32_t s_samp[kMaxSamples];
   __shared__ SelShared sh;
+  __shared__ uint8_t s_qprep[kWaves][kUTerms * kD];
   __shared__ int s_bad;
   const int tid = threadIdx.x;
   const uint32_t lane = tid & 63;
@@ -91,8 +92,9 @@ __global__ __launch_bounds__(kWG) void k_decode_prep(DecodeArgs A) {
   float tau = -INFINITY;
   if (sg.n > 0) {
     QOp qo;
-    load_q(qo, A.q, A.q_scale, A.w, b, lane);
-    tau = sample_tau(qo, A.k, A.k_scale, MapPaged{pt}, 0, sg, s_samp, sh, tid);
+    prepare_q(qo, A.q, A.q_scale, A.w, b, lane, s_qprep[tid >> 6]);
+    tau = sample_tau(qo, make_keybuf(A.k, A.k_scale, (int64_t)A.num_pages * 64), TilePaged{pt}, 0, sg,
+                     s_samp, sh, tid);
   }
   if (tid == 0) {
     A.tau[b] = tau;
@@ -102,10 +104,11 @@ __global__ __launch_bounds__(kWG) void k_decode_prep(DecodeArgs A) {
 
 __global__ __launch_bounds__(kWG) void k_decode_split(DecodeArgs A) {
   __shared__ SelShared sh;
+  __shared__ uint8_t s_qprep[kWaves][kUTerms * kD];
   __shared__ uint32_t s_last;
   const int tid = threadIdx.x;
   const uint32_t lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = blockIdx.x, b = blockIdx.y;
   uint32_t* stats = A.ctrl + kStatsOff;
   const int st = A.status[b];
@@ -125,19 +128,21 @@ __global__ __launch_bounds__(kWG) void k_decode_split(DecodeArgs A) {
   uint32_t* ckey = A.cand_key + (int64_t)b * kDecCap;
   int32_t* cidx = A.cand_idx + (int64_t)b * kDecCap;
   if (k0 < k1) {
-    QOp qo[1];
-    load_q(qo[0], A.q, A.q_scale, A.w, b, lane);
-    const MapPaged map{pt};
+    QOp qo;
+    prepare_q(qo, A.q, A.q_scale, A.w, b, lane, s_qprep[wave]);
+    const KeyBuf kbuf = make_keybuf(A.k, A.k_scale, (int64_t)A.num_pages * 64);
+    const TilePaged tm{pt};
     for (int tile = (k0 >> 6) + wave; tile < ((k1 + 63) >> 6); tile += kWaves) {
-      const int key0 = tile << 6;
-      const int my = key0 + (int)lane;
-      float sc[1];
-      score_tile<1>(qo, A.k, A.k_scale, map, key0, k0, k1, lane, sc);
-      const bool take = my < k1 && sc[0] >= tau;
+      KeyTile kt;
+      const int base = tm(tile);
+      load_tile(kt, kbuf, base, lane);
+      const float sc = tile_score(qo, kt);
+      const int my = (tile << 6) + (int)lane;
+      const bool take = my < k1 && sc >= tau;
       const uint32_t pos = reserve(cnt, take);
       if (take && pos < (uint32_t)kDecCap) {
-        ckey[pos] = f2key(sc[0]);
-        cidx[pos] = (int32_t)map(my);
+        ckey[pos] = f2key(sc);
+        cidx[pos] = base + (int)lane;
       }
     }
   }
@@ -165,6 +170,7 @@ __global__ __launch_bounds__(kWG) void k_decode_split(DecodeArgs A) {
 
 __global__ __launch_bounds__(kWG) void k_decode_repair(DecodeArgs A) {
   __shared__ SelShared sh;
+  __shared__ uint8_t s_qprep[kWaves][kUTerms * kD];
   const int tid = threadIdx.x;
   const uint32_t lane = tid & 63;
   const uint32_t n_fail = __atomic_load_n(&A.ctrl[kCtrlFail], __ATOMIC_RELAXED);
@@ -176,9 +182,9 @@ __global__ __launch_bounds__(kWG) void k_decode_repair(DecodeArgs A) {
     const int L = A.seq_lens[b];
     const int32_t* pt = A.table + (int64_t)b * A.max_pages;
     QOp qo;
-    load_q(qo, A.q, A.q_scale, A.w, b, lane);
-    repair_row(qo, A.k, A.k_scale, MapPaged{pt}, IdPaged{pt}, 0, L, A.K, A.out + (int64_t)b * A.K,
-               scratch, sh, tid);
+    prepare_q(qo, A.q, A.q_scale, A.w, b, lane, s_qprep[tid >> 6]);
+    repair_row(qo, make_keybuf(A.k, A.k_scale, (int64_t)A.num_pages * 64), TilePaged{pt}, IdPaged{pt}, 0, L,
+               A.K, A.out + (int64_t)b * A.K, scratch, sh, tid);
     if (tid == 0) atomicAdd(&stats[kStRepaired], 1u);
     __syncthreads();
   }

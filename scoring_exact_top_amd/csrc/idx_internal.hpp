@@ -15,13 +15,24 @@ constexpr int kSampleOffset = IDX_TOPK_SAMPLE_OFFSET;
 constexpr int kSampleTarget = IDX_TOPK_SAMPLE_TARGET;
 constexpr int kMaxSamples = 2048;  // longer rows widen the stride instead
 
-// Candidate capacities per row.  Two rows per workgroup keep 2 x 4096
-// candidates (64 KiB) on chip so that two workgroups fit one CU's 160 KiB of
-// LDS; the spill area in the workspace doubles the capacity ("4.5 Overflow
-// spill area").
-constexpr int kBQ = 2;
-constexpr int kLdsCap = 4096;
-constexpr int kSpillCap = 4096;
+// Main kernel geometry: 8 waves (two per SIMD), one query row per wave.
+constexpr int kMainWaves = 8;
+constexpr int kMainThreads = 64 * kMainWaves;
+// Candidates per row: (key, id) pairs are staged in a 2048-entry LDS area per
+// wave (8 x 16 KiB of the CU's 160 KiB) and flushed to the row's candidate
+// list in the workspace whenever the stage is nearly full ("4.5 Overflow
+// spill area": on-chip first, device memory beyond).  The certificate's
+// capacity is the list length kCandCap.
+constexpr int kStage = 2048;
+constexpr int kLdsCap = 4096;    // default on-chip share of the capacity
+constexpr int kSpillCap = 4096;  // default device-memory share
+constexpr int kCandCap = kLdsCap + kSpillCap;
+// Paired-row kernel: each (row, wave) owns a private segment of the row's
+// candidate list ("4.3 Candidate layout: warp-private segments"): an LDS
+// stage of kSegStage entries flushed in bulk to kSegCap entries of the
+// workspace, so slot positions come from a scalar count with no atomics.
+constexpr int kSegStage = 1024;
+constexpr int kSegCap = kCandCap / 4;
 
 // Control words at the start of every workspace.
 constexpr int kCtrlWords = 16;
@@ -43,8 +54,9 @@ struct PrefillArgs {
   int32_t Q, N, K;
   float* tau;           // [Q]
   int32_t* out;         // [Q][K]
-  uint32_t* spill_key;  // [Q][spill_cap]
-  int32_t* spill_idx;   // [Q][spill_cap]
+  uint8_t* kt;          // [ntiles][8][64][16] keys relaid in MFMA lane order
+  uint32_t* cand_key;   // [Q][kCandCap] flushed candidate keys
+  int32_t* cand_idx;    // [Q][kCandCap] flushed candidate ids
   int32_t lds_cap, spill_cap, cap_total;
   int32_t* fail_list;   // [Q]
   uint32_t* ctrl;       // kCtrlWords
@@ -82,6 +94,23 @@ struct SrcLds {
   __device__ int32_t id(int i) const { return i; }
 };
 
+// Candidates of the paired-row kernel: four wave segments of one row in the
+// workspace, o[s] = first element of segment s, raw FP32 score bits.
+struct SrcSeg4 {
+  const uint32_t* gk;  // [4][kSegCap]
+  const int32_t* gi;
+  int o1, o2, o3;
+  __device__ int at(int i) const {
+    const int s = (i >= o1) + (i >= o2) + (i >= o3);
+    const int base = s == 0 ? 0 : s == 1 ? o1 : s == 2 ? o2 : o3;
+    return s * kSegCap + (i - base);
+  }
+  __device__ uint32_t key(int i) const { return f2key(__uint_as_float(gk[at(i)])); }
+  __device__ int32_t id(int i) const { return gi[at(i)]; }
+};
+
+// Candidates of the paired-row kernel: [0, nl) in LDS, the rest in the
+// row's spill area of the workspace.
 struct SrcLdsSpill {
   const uint32_t* lk;
   const int32_t* li;
@@ -92,64 +121,65 @@ struct SrcLdsSpill {
   __device__ int32_t id(int i) const { return i < nl ? li[i] : gi[i - nl]; }
 };
 
+// Main-kernel candidates: [0, nflushed) in the workspace list, the rest
+// still in the wave's LDS stage.
+struct SrcMain {
+  const uint32_t* gk;
+  const int32_t* gi;
+  int nflushed;
+  const uint2* stage;
+  __device__ uint32_t key(int i) const { return i < nflushed ? gk[i] : stage[i - nflushed].x; }
+  __device__ int32_t id(int i) const { return i < nflushed ? gi[i] : (int32_t)stage[i - nflushed].y; }
+};
+
 // ------------------------------------------------ key addressing
 
-// Logical key position -> row of the [*, 128] key array (and of the scale
-// array, which is indexed the same way).
-struct MapIdentity {
-  __device__ int64_t operator()(int i) const { return i; }
+// Tile j of a row covers logical positions [64j, 64j+64).  A tile map gives
+// the key index of the tile's first key (wave-uniform); the tile's keys are
+// consecutive from there.
+struct TileContig {
+  __device__ int operator()(int tile) const { return tile << 6; }
 };
-
-// Paged cache with 64-token pages: position i of a sequence lives in page
-// table[i / 64], slot i % 64 ("DSA TopK Indexer", contest report page).
-struct MapPaged {
+// Paged cache with 64-token pages: tile j is page table[j] ("DSA TopK
+// Indexer", contest report page: a page holds 64 tokens).
+struct TilePaged {
   const int32_t* table;
-  __device__ int64_t operator()(int i) const { return (int64_t)table[i >> 6] * 64 + (i & 63); }
+  __device__ int operator()(int tile) const { return table[tile] << 6; }
 };
 
-// Sample i of a row starting at s0 sits at position s0 + OFFSET + stride * i.
-template <class M>
-struct MapLattice {
-  M inner;
-  int s0, stride;
-  __device__ int64_t operator()(int i) const { return inner(s0 + kSampleOffset + stride * i); }
+// Id emitted for logical position i.
+struct IdIdentity {
+  __device__ int32_t operator()(int i) const { return i; }
+};
+struct IdPaged {
+  const int32_t* table;
+  __device__ int32_t operator()(int i) const { return table[i >> 6] * 64 + (i & 63); }
 };
 
-__device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
+// Key index of logical position i under a tile map.
+template <class TM>
+__device__ __forceinline__ int key_index(const TM& tm, int i) { return tm(i >> 6) + (i & 63); }
 
-// Scores of the 64 positions key0 .. key0+63 for BQ query rows; lane l gets
-// position key0 + l.  Positions are clamped into [lo, hi-1] for the loads
-// (callers mask by range), so every access stays inside the key arrays.
-template <int BQ, class M>
-__device__ __forceinline__ void score_tile(const QOp (&qo)[BQ], const uint8_t* k, const float* k_scale,
-                                           const M& map, int key0, int lo, int hi, uint32_t lane,
-                                           float (&sc)[BQ]) {
-  v8i kb[4];
-#pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    const int i = clampi(key0 + sub_off(c) + (int)(lane & 15), lo, hi - 1);
-    kb[c] = ld32(k + map(i) * kD + 32 * (lane >> 4));
-  }
-  const float ks = k_scale[map(clampi(key0 + (int)lane, lo, hi - 1))];
-#pragma unroll
-  for (int r = 0; r < BQ; ++r) sc[r] = tile_sum(qo[r], kb) * ks;
-}
-
-// Threshold of one row from its sample lattice: score the samples exactly
-// like the main pass (so the sampled keys reproduce bit-identical scores
-// there) and return the r-th largest.  Whole workgroup calls.
-template <class M>
-__device__ float sample_tau(const QOp& qo, const uint8_t* k, const float* k_scale, const M& map, int s0,
-                            const SampleGeom& sg, uint32_t* s_samp, SelShared& sh, int tid) {
+// Threshold of one row from its sample lattice: positions s0 + OFFSET +
+// stride*i, scored exactly like the main pass (same operations, so a
+// sampled key reproduces its score bit for bit there); returns the r-th
+// largest.  Whole workgroup calls; q is prepared by every wave.
+template <class TM>
+__device__ float sample_tau(const QOp& qo, const KeyBuf& kbuf, const TM& tm, int s0, const SampleGeom& sg,
+                            uint32_t* s_samp, SelShared& sh, int tid) {
   const uint32_t lane = tid & 63;
   const int wave = tid >> 6;
-  const MapLattice<M> lm{map, s0, sg.stride};
-  const QOp qa[1] = {qo};
   for (int tile = wave; tile * kTile < sg.n; tile += kWaves) {
-    float sc[1];
-    score_tile<1>(qa, k, k_scale, lm, tile * kTile, 0, sg.n, lane, sc);
-    const int i = tile * kTile + (int)lane;
-    if (i < sg.n) s_samp[i] = f2key(sc[0]);
+    const int i0 = tile * kTile;
+    const auto key_of = [&](int i) {
+      const int smp = min(i0 + i, sg.n - 1);
+      return key_index(tm, s0 + kSampleOffset + sg.stride * smp);
+    };
+    KeyTile kt;
+    load_tile_gather(kt, kbuf, key_of, lane);
+    const float sc = tile_score(qo, kt);
+    const int i = i0 + (int)lane;
+    if (i < sg.n) s_samp[i] = f2key(sc);
   }
   __syncthreads();
   const SrcLds src{s_samp};
@@ -167,36 +197,26 @@ struct SrcScratchT {
   __device__ int32_t id(int i) const { return ids(s0 + i); }
 };
 
-struct IdIdentity {
-  __device__ int32_t operator()(int i) const { return i; }
-};
-struct IdPaged {
-  const int32_t* table;
-  __device__ int32_t operator()(int i) const { return table[i >> 6] * 64 + (i & 63); }
-};
-
 // Exact selection for one row without a threshold: rescore positions
 // [s0, s1) into scratch (order-preserving keys), build the top-byte
 // histogram on the way, finish the radix select over scratch and emit
 // ids(i) of the winners into out[0..K).  Whole workgroup calls.
-template <class M, class IdMap>
-__device__ void repair_row(const QOp& qo, const uint8_t* k, const float* k_scale, const M& map,
-                           const IdMap& ids, int s0, int s1, int K, int32_t* out, uint32_t* scratch,
-                           SelShared& sh, int tid) {
+template <class TM, class IdMap>
+__device__ void repair_row(const QOp& qo, const KeyBuf& kbuf, const TM& tm, const IdMap& ids, int s0, int s1,
+                           int K, int32_t* out, uint32_t* scratch, SelShared& sh, int tid) {
   const uint32_t lane = tid & 63;
   const int wave = tid >> 6;
   const int L = s1 - s0, kr = L < K ? L : K;
   for (int i = tid; i < 256; i += kWG) sh.hist[i] = 0u;
   __syncthreads();
-  const QOp qa[1] = {qo};
   const int tile_lo = s0 >> 6, tile_hi = (s1 + 63) >> 6;
   for (int tile = tile_lo + wave; tile < tile_hi; tile += kWaves) {
-    const int key0 = tile << 6;
-    float sc[1];
-    score_tile<1>(qa, k, k_scale, map, key0, s0, s1, lane, sc);
-    const int my = key0 + (int)lane;
+    KeyTile kt;
+    load_tile(kt, kbuf, tm(tile), lane);
+    const float sc = tile_score(qo, kt);
+    const int my = (tile << 6) + (int)lane;
     const bool valid = my >= s0 && my < s1;
-    const uint32_t key = f2key(sc[0]);
+    const uint32_t key = f2key(sc);
     if (valid) scratch[my - s0] = key;
     hist_add(sh.hist, key >> 24, valid);
   }
