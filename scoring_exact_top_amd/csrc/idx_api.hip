@@ -11,7 +11,7 @@ static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 static inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 struct PrefillLayout {
-  size_t ctrl, tau, fail, skey, cidx, scratch, kt, total;
+  size_t ctrl, tau, fail, skey, cidx, scratch, rhist, rcnt, kt, total;
 };
 
 static PrefillLayout prefill_layout(int32_t Q, int32_t N) {
@@ -22,7 +22,9 @@ static PrefillLayout prefill_layout(int32_t Q, int32_t N) {
   L.fail = o; o = align256(o + sizeof(int32_t) * (size_t)Q);
   L.skey = o; o = align256(o + sizeof(uint32_t) * (size_t)Q * kCandCap);
   L.cidx = o; o = align256(o + sizeof(int32_t) * (size_t)Q * kCandCap);
-  L.scratch = o; o = align256(o + sizeof(uint32_t) * (size_t)repair_grid(Q) * (size_t)N);
+  L.scratch = o; o = align256(o + sizeof(uint32_t) * (size_t)repair_rows(Q, N) * (size_t)repair_stride(N));
+  L.rhist = o; o = align256(o + sizeof(uint32_t) * (size_t)repair_slots(Q, N) * 4 * 256);
+  L.rcnt = o; o = align256(o + sizeof(uint32_t) * (size_t)repair_slots(Q, N) * 2);
   L.kt = o; o = align256(o + (size_t)((N + 63) / 64) * 64 * 128);
   L.total = o;
   return L;
@@ -54,6 +56,10 @@ static int prefill_common(const uint8_t* q, const float* q_scale, const uint8_t*
   A.cand_key = reinterpret_cast<uint32_t*>(ws + L.skey);
   A.cand_idx = reinterpret_cast<int32_t*>(ws + L.cidx);
   A.scratch = reinterpret_cast<uint32_t*>(ws + L.scratch);
+  A.rhist = reinterpret_cast<uint32_t*>(ws + L.rhist);
+  A.rcnt = reinterpret_cast<uint32_t*>(ws + L.rcnt);
+  A.rslots = repair_slots(Q, N);
+  A.rstride = repair_stride(N);
   A.kt = reinterpret_cast<uint8_t*>(ws + L.kt);
   A.out = out_idx;
   A.dbg_scores = scores_out;

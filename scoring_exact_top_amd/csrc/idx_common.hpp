@@ -98,9 +98,14 @@ __device__ __forceinline__ v8i cat8(v4i x, v4i y) {
 // OCP e4m3fn decode from the bit fields (S.EEEE.MMM, bias 7, subnormal
 // m * 2^-9).  Codes are never NaN here.
 __device__ __forceinline__ float e4m3_dec(uint32_t c) {
-  const uint32_t e = (c >> 3) & 15u, m = c & 7u;
-  const float mag = e == 0 ? (float)m * 0.001953125f : __uint_as_float(((e + 120u) << 23) | (m << 20));
-  return (c & 0x80u) ? -mag : mag;
+  // exponent and mantissa bits moved under an FP32 exponent rebiased by
+  // 127 - 7 give 2^(e-7) * (1 + m/8); for e = 0 the same bits read
+  // 2^-7 * (1 + m/8), and twice the excess over 2^-7 is the subnormal m/512.
+  // Both forms are computed and one selected, so the decode has no branch.
+  const float nrm = __uint_as_float(((c & 0x7Fu) << 20) + (120u << 23));
+  const float sub = (nrm - 0.0078125f) * 2.0f;
+  const float mag = (c & 0x78u) ? nrm : sub;
+  return __uint_as_float(__float_as_uint(mag) | ((c & 0x80u) << 24));
 }
 
 // Nearest e4m3fn code (ties to even) of v, |v| clamped to 448.
@@ -125,10 +130,6 @@ struct QOp {
   float sh[4];
 };
 
-// Prepare query row t.  All 64 lanes of the wave call this; `scratch` is
-// 8*128 bytes of this wave's LDS.  u is accumulated over heads in order
-// j = 0..63 in FP32; term m takes sigma_m = max|r_m| / 448 and the nearest
-// e4m3 codes of r_m / sigma_m, then r_{m+1} = r_m - sigma_m * dec(code).
 // Two query rows as held by a lane, sharing one u block: rows 0..7 carry the
 // first row's terms, rows 8..15 the second's.  sh[x] is zero in the lanes
 // that hold the other row's u rows, so each row picks up only its own terms.
@@ -139,18 +140,60 @@ struct QOp2 {
   float sh[2][4];
 };
 
-// Linear vector u of row t at dims lane and lane+64, split into kUTerms
-// e4m3 terms written to codes[m*128 + d]; returns the scales in sig.
+// Per-head query scales, all ones, for calls without q_scale.
+__constant__ float kOnes[kH] = {
+    1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f,
+    1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f,
+    1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f,
+    1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f};
+
+__device__ __forceinline__ const float* row_qscale(const float* q_scale, int64_t t) {
+  return q_scale ? q_scale + t * kH : kOnes;
+}
+
+// Linear vector u[d] = sum_j w_j q_scale_j dec(q[t,j,d]) of row t, split
+// into kUTerms e4m3 terms written to codes[m*128 + d]; the scales go to sig.
+// Lane l reads dims 16*(l&7) .. +15 of heads j = (l>>3) + 8i, i < 8, all
+// eight 16-byte loads in flight together; the eight lanes that share a dim
+// slice then add their partials with shuffles (tree xor 8, 16, 32).  The
+// sum u goes through `codes` (512 bytes of FP32) to lanes d and d+64.
+// Term m takes sigma_m = max|r_m| / 448 and the nearest e4m3 codes of
+// r_m / sigma_m, then r_{m+1} = r_m - sigma_m * dec(code).
 __device__ __forceinline__ void split_u(const uint8_t* q, const float* q_scale, const float* w, int64_t t,
                                         uint32_t lane, uint8_t* codes, float (&sig)[kUTerms]) {
-  const uint8_t* base = q + t * (kH * kD);
-  float u0 = 0.f, u1 = 0.f;
-  for (int j = 0; j < kH; ++j) {
-    const float qs = q_scale ? q_scale[t * kH + j] : 1.0f;
-    const float wj = w[t * kH + j] * qs;
-    u0 = fmaf(wj, e4m3_dec(base[j * kD + lane]), u0);
-    u1 = fmaf(wj, e4m3_dec(base[j * kD + 64 + lane]), u1);
+  const uint8_t* base = q + t * (kH * kD) + 16 * (lane & 7u);
+  const float* qs = row_qscale(q_scale, t);
+  const uint32_t h0 = lane >> 3;
+  uint4 x[8];
+  float wj[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) x[i] = *reinterpret_cast<const uint4*>(base + (h0 + 8 * i) * kD);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) wj[i] = w[t * kH + h0 + 8 * i] * qs[h0 + 8 * i];
+  float acc[16];
+#pragma unroll
+  for (int d = 0; d < 16; ++d) acc[d] = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t wd[4] = {x[i].x, x[i].y, x[i].z, x[i].w};
+#pragma unroll
+    for (int d = 0; d < 16; ++d) acc[d] = fmaf(wj[i], e4m3_dec((wd[d >> 2] >> (8 * (d & 3))) & 255u), acc[d]);
   }
+#pragma unroll
+  for (int d = 0; d < 16; ++d) {
+    acc[d] += __shfl_xor(acc[d], 8, 64);
+    acc[d] += __shfl_xor(acc[d], 16, 64);
+    acc[d] += __shfl_xor(acc[d], 32, 64);
+  }
+  float* uf = reinterpret_cast<float*>(codes);
+  if (lane < 8u) {
+#pragma unroll
+    for (int d = 0; d < 16; d += 4)
+      *reinterpret_cast<float4*>(uf + 16 * lane + d) = make_float4(acc[d], acc[d + 1], acc[d + 2], acc[d + 3]);
+  }
+  wave_sync();
+  float u0 = uf[lane], u1 = uf[64 + lane];
+  wave_sync();
 #pragma unroll
   for (int m = 0; m < kUTerms; ++m) {
     float amax = fmaxf(fabsf(u0), fabsf(u1));
@@ -170,6 +213,7 @@ __device__ __forceinline__ void split_u(const uint8_t* q, const float* q_scale, 
 __device__ __forceinline__ void head_ops(v8i (&a)[4], float (&wh)[16], const uint8_t* q, const float* q_scale,
                                          const float* w, int64_t t, uint32_t lane) {
   const uint8_t* base = q + t * (kH * kD);
+  const float* qs = row_qscale(q_scale, t);
   const uint32_t g = lane >> 4, i = lane & 15;
 #pragma unroll
   for (int b = 0; b < 4; ++b) {
@@ -177,8 +221,7 @@ __device__ __forceinline__ void head_ops(v8i (&a)[4], float (&wh)[16], const uin
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int j = 16 * b + 4 * g + r;
-      const float qs = q_scale ? q_scale[t * kH + j] : 1.0f;
-      wh[4 * b + r] = 0.5f * (w[t * kH + j] * qs);
+      wh[4 * b + r] = 0.5f * (w[t * kH + j] * qs[j]);
     }
   }
 }
@@ -211,10 +254,7 @@ __device__ __forceinline__ void prepare_q2(QOp2& o, const uint8_t* q, const floa
   wave_sync();
 }
 
-// Prepare query row t (all 64 lanes; scratch = 8*128 bytes of LDS).  u is
-// accumulated over heads in order j = 0..63 in FP32; term m takes
-// sigma_m = max|r_m| / 448 and the nearest e4m3 codes of r_m / sigma_m, then
-// r_{m+1} = r_m - sigma_m * dec(code).
+// Prepare query row t (all 64 lanes; scratch = 8*128 bytes of LDS).
 __device__ __forceinline__ void prepare_q(QOp& o, const uint8_t* q, const float* q_scale, const float* w,
                                           int64_t t, uint32_t lane, uint8_t* scratch) {
   head_ops(o.a, o.wh, q, q_scale, w, t, lane);
@@ -488,6 +528,67 @@ __device__ void emit_selection(const Src& src, int n, const SelResult& sel, int 
     if (gt) out[gt_base + pg] = src.id(i);
     const uint32_t pe = reserve(&sh.eq_count, eq);
     if (eq && (int)pe < sel.rem) out[eq_base + pe] = src.id(i);
+  }
+  for (int i = kr + tid; i < K; i += kWG) out[i] = -1;
+}
+
+// ------------------------------------------ register-resident selection
+
+// Radix select over keys held in registers: thread (wave w, lane l) holds
+// key[j] = element j*64 + l of wave w's list, valid for j*64 + l < nw (the
+// wave's own count).  Same passes and result as radix_select over the union
+// of the four waves' lists; no memory traffic besides the LDS histogram.
+template <int M>
+__device__ SelResult radix_select_regs(const uint32_t (&key)[M], uint32_t nw, int rem, SelShared& sh,
+                                       int tid, bool allow_early) {
+  const uint32_t lane = tid & 63;
+  const uint32_t jmax = (nw + 63) >> 6;  // wave-uniform
+  uint32_t prefix = 0, mask = 0;
+#pragma unroll 1
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    sh.hist[tid] = 0u;  // kWG == 256 bins
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < M; ++j) {
+      if ((uint32_t)j >= jmax) break;
+      const bool v = (uint32_t)j * 64u + lane < nw;
+      hist_add(sh.hist, (key[j] >> shift) & 255u, v && ((key[j] & mask) == prefix));
+    }
+    __syncthreads();
+    find_bucket(sh, rem, tid);
+    __syncthreads();
+    const uint32_t b = sh.bucket, above = sh.above, inb = sh.inbucket;
+    __syncthreads();
+    prefix |= b << shift;
+    mask |= 0xFFu << shift;
+    rem -= (int)above;
+    if (allow_early && (int)inb == rem) break;
+  }
+  return SelResult{prefix, mask, rem};
+}
+
+// Emit for radix_select_regs: ids[j*64 + lane] is the id of key[j].
+template <int M>
+__device__ void emit_selection_regs(const uint32_t (&key)[M], uint32_t nw, const int32_t* ids,
+                                    const SelResult& sel, int kr, int K, int32_t* out, SelShared& sh,
+                                    int tid) {
+  const uint32_t lane = tid & 63;
+  const uint32_t jmax = (nw + 63) >> 6;
+  if (tid == 0) { sh.gt_count = 0; sh.eq_count = 0; }
+  __syncthreads();
+  const int eq_base = kr - sel.rem;
+#pragma unroll
+  for (int j = 0; j < M; ++j) {
+    if ((uint32_t)j >= jmax) break;
+    const uint32_t i = (uint32_t)j * 64u + lane;
+    const bool v = i < nw;
+    const uint32_t mk = key[j] & sel.mask;
+    const bool gt = v && mk > sel.prefix;
+    const bool eq = v && mk == sel.prefix;
+    const uint32_t pg = reserve(&sh.gt_count, gt);
+    if (gt) out[pg] = ids[i];
+    const uint32_t pe = reserve(&sh.eq_count, eq);
+    if (eq && (int)pe < sel.rem) out[eq_base + pe] = ids[i];
   }
   for (int i = kr + tid; i < K; i += kWG) out[i] = -1;
 }

@@ -15,24 +15,27 @@ constexpr int kSampleOffset = IDX_TOPK_SAMPLE_OFFSET;
 constexpr int kSampleTarget = IDX_TOPK_SAMPLE_TARGET;
 constexpr int kMaxSamples = 2048;  // longer rows widen the stride instead
 
-// Main kernel geometry: 8 waves (two per SIMD), one query row per wave.
-constexpr int kMainWaves = 8;
-constexpr int kMainThreads = 64 * kMainWaves;
-// Candidates per row: (key, id) pairs are staged in a 2048-entry LDS area per
-// wave (8 x 16 KiB of the CU's 160 KiB) and flushed to the row's candidate
-// list in the workspace whenever the stage is nearly full ("4.5 Overflow
-// spill area": on-chip first, device memory beyond).  The certificate's
-// capacity is the list length kCandCap.
-constexpr int kStage = 2048;
-constexpr int kLdsCap = 4096;    // default on-chip share of the capacity
-constexpr int kSpillCap = 4096;  // default device-memory share
+// Candidates per row ("4.3 Candidate layout: warp-private segments" and "4.5
+// Overflow spill area"): each (row, wave) pair of the main kernel stages
+// (score, id) pairs in an on-chip area of kSegStage entries and copies a full
+// stage in bulk to its private workspace segment of kSegCap entries.  The
+// certificate's capacity per row is kCandCap, the four segments together;
+// a row also fails it when one segment alone overflows.
+constexpr int kLdsCap = 4096;    // on-chip stage entries per row (all waves)
+constexpr int kSpillCap = 4096;  // capacity beyond one stage fill
 constexpr int kCandCap = kLdsCap + kSpillCap;
-// Paired-row kernel: each (row, wave) owns a private segment of the row's
-// candidate list ("4.3 Candidate layout: warp-private segments"): an LDS
-// stage of kSegStage entries flushed in bulk to kSegCap entries of the
-// workspace, so slot positions come from a scalar count with no atomics.
-constexpr int kSegStage = 1024;
-constexpr int kSegCap = kCandCap / 4;
+constexpr int kSegStage = kLdsCap / kWaves;
+constexpr int kSegCap = kCandCap / kWaves;
+
+// Exact repair, split over the chip: one work item covers kRepairChunk
+// positions of one failed row; scratch holds the scores of up to
+// repair_slots() failed rows at once, and kRepairFallback more slots serve
+// workgroups that repair whole rows alone once the slots run out.
+constexpr int kRepairChunk = 4096;
+constexpr int kRepairChunkTiles = kRepairChunk / 64;
+constexpr int kRepairGrid = 1024;
+constexpr int kRepairFallback = 256;
+constexpr int64_t kRepairScratchKeys = (int64_t)1 << 28;  // 1 GiB of scores
 
 // Control words at the start of every workspace.
 constexpr int kCtrlWords = 16;
@@ -42,6 +45,26 @@ constexpr int kStRows = 0, kStFast = 1, kStUnder = 2, kStOver = 3, kStSpilled = 
               kStRepaired = 5, kStTrivial = 6, kStBad = 7;
 
 __host__ __device__ inline int repair_grid(int rows) { return rows < 256 ? (rows > 0 ? rows : 1) : 256; }
+
+// Scratch row stride (keys): N rounded up to 64, so rows are 256-byte aligned.
+__host__ __device__ inline int64_t repair_stride(int nkeys) { return ((int64_t)nkeys + 63) & ~(int64_t)63; }
+
+// Failed rows whose scores fit the repair scratch together: at most
+// kRepairScratchKeys scores, at least kRepairFallback rows, at most Q.
+__host__ __device__ inline int repair_slots(int rows, int nkeys) {
+  const int64_t ns = repair_stride(nkeys);
+  int64_t s = ns > 0 ? kRepairScratchKeys / ns : (int64_t)rows;
+  if (s < kRepairFallback) s = kRepairFallback;
+  if (s > rows) s = rows;
+  return s > 0 ? (int)s : 1;
+}
+
+// Scratch rows in all: the slots plus, when some rows may not get a slot,
+// the fallback workgroups' own rows.
+__host__ __device__ inline int repair_rows(int rows, int nkeys) {
+  const int s = repair_slots(rows, nkeys);
+  return s + (rows > s ? kRepairFallback : 0);
+}
 
 struct PrefillArgs {
   const uint8_t* q;
@@ -55,12 +78,16 @@ struct PrefillArgs {
   float* tau;           // [Q]
   int32_t* out;         // [Q][K]
   uint8_t* kt;          // [ntiles][8][64][16] keys relaid in MFMA lane order
-  uint32_t* cand_key;   // [Q][kCandCap] flushed candidate keys
-  int32_t* cand_idx;    // [Q][kCandCap] flushed candidate ids
+  uint32_t* cand_key;   // [Q][kWaves][kSegCap] candidate scores (FP32 bits)
+  int32_t* cand_idx;    // [Q][kWaves][kSegCap] candidate key ids
   int32_t lds_cap, spill_cap, cap_total;
   int32_t* fail_list;   // [Q]
   uint32_t* ctrl;       // kCtrlWords
-  uint32_t* scratch;    // [repair_grid(Q)][N]
+  uint32_t* scratch;    // [repair_rows][repair_stride(N)] repair scores (order-preserving keys)
+  uint32_t* rhist;      // [rslots][4][256] digit histograms of each slotted repair row
+  uint32_t* rcnt;       // [rslots][2] output counters of each slotted repair row
+  int32_t rslots;
+  int64_t rstride;
   float* dbg_scores;    // [Q][N] or null
   int32_t force_tau;
   float tau_value;
@@ -92,44 +119,6 @@ struct SrcLds {
   const uint32_t* k;
   __device__ uint32_t key(int i) const { return k[i]; }
   __device__ int32_t id(int i) const { return i; }
-};
-
-// Candidates of the paired-row kernel: four wave segments of one row in the
-// workspace, o[s] = first element of segment s, raw FP32 score bits.
-struct SrcSeg4 {
-  const uint32_t* gk;  // [4][kSegCap]
-  const int32_t* gi;
-  int o1, o2, o3;
-  __device__ int at(int i) const {
-    const int s = (i >= o1) + (i >= o2) + (i >= o3);
-    const int base = s == 0 ? 0 : s == 1 ? o1 : s == 2 ? o2 : o3;
-    return s * kSegCap + (i - base);
-  }
-  __device__ uint32_t key(int i) const { return f2key(__uint_as_float(gk[at(i)])); }
-  __device__ int32_t id(int i) const { return gi[at(i)]; }
-};
-
-// Candidates of the paired-row kernel: [0, nl) in LDS, the rest in the
-// row's spill area of the workspace.
-struct SrcLdsSpill {
-  const uint32_t* lk;
-  const int32_t* li;
-  int nl;
-  const uint32_t* gk;
-  const int32_t* gi;
-  __device__ uint32_t key(int i) const { return i < nl ? lk[i] : gk[i - nl]; }
-  __device__ int32_t id(int i) const { return i < nl ? li[i] : gi[i - nl]; }
-};
-
-// Main-kernel candidates: [0, nflushed) in the workspace list, the rest
-// still in the wave's LDS stage.
-struct SrcMain {
-  const uint32_t* gk;
-  const int32_t* gi;
-  int nflushed;
-  const uint2* stage;
-  __device__ uint32_t key(int i) const { return i < nflushed ? gk[i] : stage[i - nflushed].x; }
-  __device__ int32_t id(int i) const { return i < nflushed ? gi[i] : (int32_t)stage[i - nflushed].y; }
 };
 
 // ------------------------------------------------ key addressing

@@ -31,233 +31,53 @@ __global__ __launch_bounds__(kWG) void k_relayout_keys(PrefillArgs A) {
 // One workgroup per row: score the sampled keys exactly as the main pass
 // does, then take the r-th largest as tau.
 __global__ __launch_bounds__(kWG) void k_prefill_tau(PrefillArgs A) {
-  __shared__ uint32_t s_samp[kMaxSamples];
-  __shared__ SelShared sh;
+  __shared__ uint32_t s_samp[kWaves][kMaxSamples];
+  __shared__ uint32_t s_hist[kWaves][256];
   __shared__ uint8_t s_qprep[kWaves][kUTerms * kD];
   const int tid = threadIdx.x;
   const uint32_t lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   if (blockIdx.x == 0 && tid < kCtrlWords) A.ctrl[tid] = 0u;
-  const int t = blockIdx.x;
+  const int t = kWaves * blockIdx.x + wave;  // one row per wave
+  if (t >= A.Q) return;
+  if (t < A.rslots) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) A.rhist[(int64_t)t * 1024 + 64 * i + lane] = 0u;
+    if (lane < 2) A.rcnt[2 * t + lane] = 0u;
+  }
   const int s0 = A.row_start[t], s1 = A.row_end[t];
   if (s0 < 0 || s0 > s1 || s1 > A.N) {
-    if (tid == 0) A.tau[t] = INFINITY;
+    if (lane == 0) A.tau[t] = INFINITY;
     return;
   }
   const int L = s1 - s0;
   if (A.force_tau) {
-    if (tid == 0) A.tau[t] = A.tau_value;
+    if (lane == 0) A.tau[t] = A.tau_value;
     return;
   }
   const SampleGeom sg = sample_geom(L, A.cap_total);
   if (sg.n == 0) {
-    if (tid == 0) A.tau[t] = -INFINITY;
+    if (lane == 0) A.tau[t] = -INFINITY;
     return;
   }
   QOp qo;
-  prepare_q(qo, A.q, A.q_scale, A.w, t, lane, s_qprep[tid >> 6]);
+  prepare_q(qo, A.q, A.q_scale, A.w, t, lane, s_qprep[wave]);
   const KeyBuf kbuf = make_keybuf(A.k, A.k_scale, A.N);
-  const float tau = sample_tau(qo, kbuf, TileContig{}, s0, sg, s_samp, sh, tid);
-  if (tid == 0) A.tau[t] = tau;
-}
-
-// ------------------------------------------------------------- fused main
-
-// Per-wave candidate bookkeeping of the main kernel.
-struct CandState {
-  uint32_t cnt;      // candidates seen (may exceed the capacity)
-  uint32_t staged;   // entries in the LDS stage
-  uint32_t flushed;  // entries already in the workspace list
-};
-
-// Copy the wave's LDS stage to its workspace list (as far as capacity
-// allows) and empty it.  Rare: once per ~kStage candidates.
-__device__ __forceinline__ void flush_stage(CandState& cs, uint2* stage, uint32_t* gk, int32_t* gi,
-                                            uint32_t cap, uint32_t lane) {
+  // Score the samples 64 at a time, the next tile's gather in flight.
+  const auto key_of = [&](int i) { return s0 + kSampleOffset + sg.stride * min(i, sg.n - 1); };
+  KeyTile cur;
+  load_tile_gather(cur, kbuf, [&](int i) { return key_of(i); }, lane);
+#pragma unroll 1
+  for (int i0 = 0; i0 < sg.n; i0 += kTile) {
+    KeyTile nxt;
+    load_tile_gather(nxt, kbuf, [&](int i) { return key_of(i0 + kTile + i); }, lane);
+    const float sc = tile_score(qo, cur);
+    if (i0 + (int)lane < sg.n) s_samp[wave][i0 + lane] = f2key(sc);
+    cur = nxt;
+  }
   wave_sync();
-  for (uint32_t i = lane; i < cs.staged; i += 64) {
-    const uint32_t o = cs.flushed + i;
-    if (o < cap) {
-      const uint2 e = stage[i];
-      gk[o] = e.x;
-      gi[o] = (int32_t)e.y;
-    }
-  }
-  cs.flushed = min(cs.flushed + cs.staged, cap);
-  cs.staged = 0;
-  wave_sync();
-  // Drain the stores here (vmcnt(0), other counters untouched) so that the
-  // common no-flush path never has to assume stores in flight.
-  __builtin_amdgcn_s_waitcnt(0x0F70);
-}
-
-// Epilogue phase for one tile: scores of keys key0..key0+63 (lane l: key0+l)
-// from the accumulators, range mask, threshold filter and staging.
-template <bool DBG>
-__device__ __forceinline__ void main_epilogue(const QOp& qo, const v4f (&acc)[20], float ks, int key0,
-                                              int rs, int re, float tau, float* dbg, CandState& cs,
-                                              uint2* stage, uint32_t stage_cap, uint32_t* gk,
-                                              int32_t* gi, uint32_t cap, uint32_t lane) {
-  const int my = key0 + (int)lane;
-  const float sc = tile_epilogue(qo, acc) * ks;
-  const bool valid = my >= rs && my < re;
-  if (DBG && valid) dbg[my] = sc;
-  const bool take = valid && sc >= tau;
-  const uint64_t ball = __ballot(take);
-  if (ball) {
-    const uint32_t n = (uint32_t)__popcll(ball);
-    if (cs.staged + n > stage_cap) flush_stage(cs, stage, gk, gi, cap, lane);
-    if (take) stage[cs.staged + rank_in(ball)] = make_uint2(f2key(sc), (uint32_t)my);
-    cs.staged += n;
-    cs.cnt += n;
-  }
-}
-
-// Eight waves, one query row each, walk the same 64-key tiles of the rows'
-// union range.  Waves w and w+4 share a SIMD and run in opposite phases:
-// while one issues the 16 MFMAs of a tile, the other runs the VALU epilogue
-// of its previous tile, so the matrix core and the vector ALU work at the same
-// time.  Execution barriers swap the phases.  Key tiles are prefetched into
-// registers two phases ahead; the epilogue touches only LDS.  After the walk
-// every wave certifies and selects its own row.
-// DBG: also write every valid score to A.dbg_scores (test/diagnosis build of
-// the same arithmetic; the production instantiation has no store in its
-// epilogue).
-template <bool DBG>
-__global__ __launch_bounds__(kMainThreads, 1) void k_prefill_main(PrefillArgs A) {
-  __shared__ uint2 s_stage[kMainWaves][kStage];
-  __shared__ uint32_t s_hist[kMainWaves][256];
-  const int tid = threadIdx.x;
-  const uint32_t lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int group = wave >> 2;
-  const int t0 = blockIdx.x * kMainWaves;
-  const int t = t0 + wave;
-  const bool row_ok = t < A.Q;
-  const int tc = min(t, A.Q - 1);
-
-  // union of the workgroup's valid ranges (every wave computes it alike)
-  int lo = 0x7fffffff, hi = -1;
-  for (int r = 0; r < kMainWaves && t0 + r < A.Q; ++r) {
-    const int s = A.row_start[t0 + r], e = A.row_end[t0 + r];
-    if (s >= 0 && s < e && e <= A.N) { lo = min(lo, s); hi = max(hi, e); }
-  }
-  int rs = 0, re = 0;
-  bool bad = false;
-  float tau = INFINITY;
-  if (row_ok) {
-    rs = A.row_start[t]; re = A.row_end[t];
-    bad = rs < 0 || rs > re || re > A.N;
-    if (bad) { rs = 0; re = 0; } else tau = A.tau[t];
-  }
-  QOp qo;
-  prepare_q(qo, A.q, A.q_scale, A.w, tc, lane, reinterpret_cast<uint8_t*>(s_hist[wave]));
-  const KeyBuf kbuf = make_keybuf(A.k, A.k_scale, A.N);
-
-  const int tile_lo = lo >> 6;
-  const int nt = lo < hi ? ((hi + 63) >> 6) - tile_lo : 0;
-  const uint32_t cap = (uint32_t)min(A.cap_total, kCandCap);
-  const uint32_t stage_cap = (uint32_t)max(64, min(A.lds_cap, kStage));
-  uint2* stage = s_stage[wave];
-  uint32_t* gk = A.cand_key + (int64_t)tc * kCandCap;
-  int32_t* gi = A.cand_idx + (int64_t)tc * kCandCap;
-  float* dbg = A.dbg_scores ? A.dbg_scores + (int64_t)tc * A.N : nullptr;
-  CandState cs{0u, 0u, 0u};
-  KeyTile b0, b1;
-  v4f acc[20];
-
-#define IDX_PHASE_BARRIER()            \
-  do {                                 \
-    __builtin_amdgcn_sched_barrier(0); \
-    __builtin_amdgcn_s_barrier();      \
-    __builtin_amdgcn_sched_barrier(0); \
-  } while (0)
-  // MFMA phase on tile j held in CUR, then prefetch tile j+1 into NXT.
-#define IDX_M(j, CUR, NXT)                                                                     \
-  do {                                                                                         \
-    tile_mfma(qo, CUR.kb, acc);                                                                \
-    __builtin_amdgcn_sched_barrier(0);                                                         \
-    /* unconditional: past the end the buffer reads return 0, and a fixed   \
-       load count lets the epilogue wait only for the older loads it needs */ \
-    load_tile(NXT, kbuf, (tile_lo + (j) + 1) << 6, lane);                                       \
-  } while (0)
-#define IDX_V(j, CUR)                                                                          \
-  main_epilogue<DBG>(qo, acc, CUR.ks, (tile_lo + (j)) << 6, rs, re, tau, dbg, cs, stage, stage_cap, gk, gi, \
-                cap, lane)
-
-  if (nt > 0) load_tile(b0, kbuf, tile_lo << 6, lane);
-  // One full drain before the loop: the loop's own wait analysis then only
-  // sees its in-loop prefetches and waits for exactly the tile it needs.
-  __builtin_amdgcn_s_waitcnt(0x0F70);
-  // Each loop iteration handles two tiles with fixed register roles; an odd
-  // last tile leaves through `break`, so the loop back-edge always carries
-  // the same set of loads in flight.
-  if (group == 0) {
-    for (int j = 0; j < nt; j += 2) {
-      IDX_M(j, b0, b1);
-      IDX_PHASE_BARRIER();
-      IDX_V(j, b0);
-      IDX_PHASE_BARRIER();
-      if (j + 1 >= nt) break;
-      IDX_M(j + 1, b1, b0);
-      IDX_PHASE_BARRIER();
-      IDX_V(j + 1, b1);
-      IDX_PHASE_BARRIER();
-    }
-  } else {
-    int j = 0;
-    if (nt > 0) {
-      IDX_PHASE_BARRIER();
-      IDX_M(0, b0, b1);
-      IDX_PHASE_BARRIER();
-      for (j = 1; j < nt; j += 2) {
-        IDX_V(j - 1, b0);
-        IDX_PHASE_BARRIER();
-        IDX_M(j, b1, b0);
-        IDX_PHASE_BARRIER();
-        if (j + 1 >= nt) break;
-        IDX_V(j, b1);
-        IDX_PHASE_BARRIER();
-        IDX_M(j + 1, b0, b1);
-        IDX_PHASE_BARRIER();
-      }
-      // the last tile nt-1 sits in b0 when nt is odd, in b1 when even
-      if (nt & 1) IDX_V(nt - 1, b0);
-      else IDX_V(nt - 1, b1);
-    }
-  }
-#undef IDX_V
-#undef IDX_M
-#undef IDX_PHASE_BARRIER
-
-  // certificate + selection, one row per wave, no workgroup barrier
-  if (!row_ok) return;
-  wave_sync();
-  uint32_t* stats = A.ctrl + kStatsOff;
-  int32_t* out = A.out + (int64_t)t * A.K;
-  if (lane == 0) atomicAdd(&stats[kStRows], 1u);
-  if (bad) {
-    for (int i = (int)lane; i < A.K; i += 64) out[i] = -1;
-    if (lane == 0) atomicAdd(&stats[kStBad], 1u);
-    return;
-  }
-  const int L = re - rs;
-  const int kr = min(A.K, L);
-  if (cs.cnt >= (uint32_t)kr && cs.cnt <= cap) {
-    const SrcMain src{gk, gi, (int)cs.flushed, stage};
-    const SelResult sel = (cs.cnt > (uint32_t)kr)
-                              ? wave_radix_select(src, (int)cs.cnt, kr, s_hist[wave], lane, true)
-                              : SelResult{0u, 0u, kr};
-    wave_emit(src, (int)cs.cnt, sel, kr, A.K, out, lane);
-    if (lane == 0) {
-      atomicAdd(&stats[kStFast], 1u);
-      if (cs.flushed > 0) atomicAdd(&stats[kStSpilled], 1u);
-      if (L <= A.K) atomicAdd(&stats[kStTrivial], 1u);
-    }
-  } else if (lane == 0) {
-    const uint32_t f = atomicAdd(&A.ctrl[kCtrlFail], 1u);
-    A.fail_list[f] = t;
-    atomicAdd(&stats[cs.cnt < (uint32_t)kr ? kStUnder : kStOver], 1u);
-  }
+  const SelResult sel = wave_radix_select(SrcLds{s_samp[wave]}, sg.n, sg.r, s_hist[wave], lane, false);
+  if (lane == 0) A.tau[t] = key2f(sel.prefix);
 }
 
 // ------------------------------------------------------ paired-row main
@@ -278,7 +98,7 @@ template <bool DBG>
 __global__ __launch_bounds__(kWG, 2) void k_prefill_pair(PrefillArgs A) {
   __shared__ uint2 s_stage[2][kWaves][kSegStage];
   __shared__ uint32_t s_segn[2][kWaves];   // entries in each segment (capped)
-  __shared__ uint32_t s_segover[2];        // some segment of the row overflowed
+  __shared__ uint32_t s_segover[2];        // bit 0: a segment overflowed; bit 1: a stage was flushed early
   __shared__ SelShared sh;
   __shared__ uint8_t s_qprep[kWaves][2 * kUTerms * kD];
   const int tid = threadIdx.x;
@@ -420,10 +240,12 @@ __global__ __launch_bounds__(kWG, 2) void k_prefill_pair(PrefillArgs A) {
   }
 #pragma unroll
   for (int r = 0; r < 2; ++r) {
+    const bool spilled = flushed[r] > 0u;  // a stage filled up during the walk
     if (staged[r]) flush(r);
     if (lane == 0) {
       s_segn[r][wave] = flushed[r];
-      if (cnt[r] > seg_cap) s_segover[r] = 1u;
+      if (cnt[r] > seg_cap) atomicOr(&s_segover[r], 1u);
+      if (spilled) atomicOr(&s_segover[r], 2u);
     }
   }
   __syncthreads();
@@ -443,18 +265,25 @@ __global__ __launch_bounds__(kWG, 2) void k_prefill_pair(PrefillArgs A) {
     }
     const int L = re_t - rs_t;
     const int kr = min(A.K, L);
-    const uint32_t n0 = s_segn[r][0], n1 = s_segn[r][1], n2 = s_segn[r][2], n3 = s_segn[r][3];
-    const uint32_t n = n0 + n1 + n2 + n3;
-    const bool complete = s_segover[r] == 0u;
+    const uint32_t n = s_segn[r][0] + s_segn[r][1] + s_segn[r][2] + s_segn[r][3];
+    const bool complete = (s_segover[r] & 1u) == 0u;
     if (complete && n >= (uint32_t)kr) {
-      const int64_t o = (int64_t)t * kWaves * kSegCap;
-      const SrcSeg4 src{A.cand_key + o, A.cand_idx + o, (int)n0, (int)(n0 + n1), (int)(n0 + n1 + n2)};
-      const SelResult sel = (n > (uint32_t)kr) ? radix_select(src, (int)n, kr, sh, tid, false, true)
+      // each wave takes its own segment (written by itself) into registers
+      const uint32_t nw = s_segn[r][wave];
+      const int64_t o = ((int64_t)t * kWaves + wave) * kSegCap;
+      const uint32_t* gk = A.cand_key + o;
+      uint32_t key[kSegCap / 64];
+#pragma unroll
+      for (int j = 0; j < kSegCap / 64; ++j) {
+        const uint32_t i = (uint32_t)j * 64u + lane;
+        key[j] = i < nw ? f2key(__uint_as_float(gk[i])) : 0u;
+      }
+      const SelResult sel = (n > (uint32_t)kr) ? radix_select_regs(key, nw, kr, sh, tid, true)
                                               : SelResult{0u, 0u, kr};
-      emit_selection(src, (int)n, sel, kr, A.K, out, sh, tid);
+      emit_selection_regs(key, nw, A.cand_idx + o, sel, kr, A.K, out, sh, tid);
       if (tid == 0) {
         atomicAdd(&stats[kStFast], 1u);
-        if (n > (uint32_t)(kWaves * min(kSegStage, max(64, A.lds_cap / kWaves)))) atomicAdd(&stats[kStSpilled], 1u);
+        if (s_segover[r] & 2u) atomicAdd(&stats[kStSpilled], 1u);
         if (L <= A.K) atomicAdd(&stats[kStTrivial], 1u);
       }
     } else if (tid == 0) {
@@ -466,206 +295,217 @@ __global__ __launch_bounds__(kWG, 2) void k_prefill_pair(PrefillArgs A) {
   }
 }
 
-// ---------------------------------------------- 12-wave main (3 per SIMD)
+// ------------------------------------------------------------------ repair
+//
+// Exact repair of rows the certificate rejected, split over the whole chip:
+// the first rslots failed rows each get a scratch slot, and every kernel
+// below walks work items (f, c) = (failed row, chunk of kRepairChunk
+// positions).  The radix select runs one 8-bit digit per launch: the digit
+// histogram of a row is summed in device memory over its chunks, and each
+// work item replays the finished digits (find_bucket over the stored
+// histograms) to know the prefix it filters by.
 
-constexpr int kTripRows = 4;    // query rows per workgroup
-constexpr int kTripParts = 2;   // waves per row (interleaved tiles)
-constexpr int kTripWaves = kTripRows * kTripParts;
-constexpr int kTripThreads = 64 * kTripWaves;
+// Selection state after the first `npass` digits of slot f.  done: the
+// boundary bucket is taken whole, or the row has no more than kr keys.
+struct RepairSel {
+  uint32_t prefix, mask;
+  int rem;
+  bool done;
+};
 
-// Twelve waves, three per SIMD: four query rows per workgroup, each row's
-// tiles dealt round-robin to three waves.  One row per wave keeps the
-// register footprint within a third of the SIMD's register file, so that
-// while one wave issues MFMAs two others can issue epilogue VALU.  4096 rows
-// fill 1024 workgroups = four full rounds of the 256 CUs.  Per 16-key
-// sub-tile a wave issues the 5 MFMAs (4 head blocks + u block), refills
-// those operand registers with the same sub-tile one tile ahead, then folds
-// the results into the key's partial sum.  Candidates of a row go to its LDS
-// area (then its spill area), slots reserved with one LDS atomic per wave;
-// after the walk one wave per row selects it.
-template <bool DBG>
-__global__ __launch_bounds__(kTripThreads, 1) void k_prefill_trip(PrefillArgs A) {
-  __shared__ uint32_t s_key[kTripRows][kLdsCap];
-  __shared__ int32_t s_idx[kTripRows][kLdsCap];
-  __shared__ uint32_t s_cnt[kTripRows];
-  __shared__ uint8_t s_qprep[kTripWaves][kUTerms * kD];
-  const int tid = threadIdx.x;
-  const uint32_t lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int row = wave / kTripParts, part = wave % kTripParts;
-  const int t0 = blockIdx.x * kTripRows;
-  const int t = t0 + row;
-  const bool row_ok = t < A.Q;
-
-  int lo = 0x7fffffff, hi = -1;
-  for (int r = 0; r < kTripRows && t0 + r < A.Q; ++r) {
-    const int s = A.row_start[t0 + r], e = A.row_end[t0 + r];
-    if (s >= 0 && s < e && e <= A.N) { lo = min(lo, s); hi = max(hi, e); }
+__device__ RepairSel repair_replay(const uint32_t* rh, int L, int kr, int npass, SelShared& sh, int tid) {
+  RepairSel r{0u, 0u, kr, L <= kr};
+#pragma unroll 1
+  for (int p = 0; p < npass && !r.done; ++p) {
+    sh.hist[tid] = rh[p * 256 + tid];
+    __syncthreads();
+    find_bucket(sh, r.rem, tid);
+    __syncthreads();
+    const uint32_t b = sh.bucket, above = sh.above, inb = sh.inbucket;
+    __syncthreads();
+    const int shift = 24 - 8 * p;
+    r.prefix |= b << shift;
+    r.mask |= 0xFFu << shift;
+    r.rem -= (int)above;
+    r.done = (int)inb == r.rem;
   }
-  int rs = 0, re = 0;
-  float tau = INFINITY;
-  if (row_ok) {
-    const int s = A.row_start[t], e = A.row_end[t];
-    if (s >= 0 && s <= e && e <= A.N) { rs = s; re = e; tau = A.tau[t]; }
-  }
-  if (tid < kTripRows) s_cnt[tid] = 0u;
-  QOp qo;
-  prepare_q(qo, A.q, A.q_scale, A.w, min(t, A.Q - 1), lane, s_qprep[wave]);
-  __syncthreads();
-
-  const KeyBuf kbuf = make_keybuf(A.k, A.k_scale, A.N);
-  const uint32_t lcap = (uint32_t)A.lds_cap, scap = (uint32_t)A.spill_cap;
-  const int tile_hi = (hi + 63) >> 6;
-  const int voff = (int)(lane & 15) * kD + 32 * (int)(lane >> 4);
-  const v4f z = {0.f, 0.f, 0.f, 0.f};
-  if (lo < hi) {
-    int T = (lo >> 6) + part;
-    v8i kb[4];
-    float ks_cur, ks_nxt;
-    {
-      KeyTile kt;
-      load_tile(kt, kbuf, T << 6, lane);
-#pragma unroll
-      for (int c = 0; c < 4; ++c) kb[c] = kt.kb[c];
-      ks_cur = kt.ks;
-    }
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // drain once so the loop's waits stay exact
-    // Software pipeline over 16-key sub-tiles: stage c issues the MFMAs of
-    // the next sub-tile (one by one, between the VALU ops of this sub-tile's
-    // epilogue) into the other accumulator set, then refills that sub-tile's
-    // operand registers one tile ahead.  issue(c) always writes acc[c & 1].
-    v4f acc[2][5];
-    auto issue = [&](v4f (&a)[5], const v8i& b) {
-#pragma unroll
-      for (int h = 0; h < 4; ++h)
-        a[h] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qo.a[h], b, z, 0, 0, 0, 0, 0, 0);
-      a[4] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qo.au, b, z, 0, 0, 0, 0, 0, 0);
-    };
-    auto refill = [&](v8i& b, int base_key, int c) {
-      const int soff = (base_key + sub_off(c)) * kD;
-      b = cat8(__builtin_amdgcn_raw_buffer_load_b128(kbuf.k, voff, soff, 0),
-               __builtin_amdgcn_raw_buffer_load_b128(kbuf.k, voff + 16, soff, 0));
-    };
-    auto epi = [&](const v4f (&a)[5]) {
-      float x = 0.f;
-#pragma unroll
-      for (int h = 0; h < 4; ++h)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) x = fmaf(qo.wh[4 * h + r], fabsf(a[h][r]), x);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) x = fmaf(qo.sh[r], a[4][r], x);
-      return x;
-    };
-    issue(acc[0], kb[0]);
-    refill(kb[0], (T + kTripParts) << 6, 0);
-    for (;;) {
-      const int nbase = (T + kTripParts) << 6;  // this wave's next tile (reads past the end return 0)
-      const bool more = T + kTripParts < tile_hi;
-      float p[4];
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        if (c < 3) {
-          issue(acc[(c + 1) & 1], kb[c + 1]);
-        } else if (more) {
-          issue(acc[0], kb[0]);
-        }
-        p[c] = epi(acc[c & 1]);
-        // interleave: one MFMA then four epilogue VALU ops, five times
-#pragma unroll
-        for (int i = 0; i < 5; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
-        }
-        if (c < 3) {
-          refill(kb[c + 1], nbase, c + 1);
-          if (c == 0)
-            ks_nxt = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(kbuf.ks, (int)lane * 4, nbase * 4, 0));
-        } else {
-          refill(kb[0], nbase + (kTripParts << 6), 0);
-        }
-      }
-      const float sc = reduce_scatter4(p[0], p[1], p[2], p[3]) * ks_cur;
-      ks_cur = ks_nxt;
-      const int my = (T << 6) + (int)lane;
-      const bool valid = my >= rs && my < re;
-      if (DBG && valid) A.dbg_scores[(int64_t)t * A.N + my] = sc;
-      const bool take = valid && sc >= tau;
-      const uint32_t pos = reserve(&s_cnt[row], take);
-      if (take) {
-        const uint32_t key = f2key(sc);
-        if (pos < lcap) {
-          s_key[row][pos] = key;
-          s_idx[row][pos] = my;
-        } else if (pos - lcap < scap) {
-          const int64_t o = (int64_t)t * kCandCap + (pos - lcap);
-          A.cand_key[o] = key;
-          A.cand_idx[o] = my;
-          __builtin_amdgcn_s_waitcnt(0x0F70);  // rare: keep the common path's waits exact
-        }
-      }
-      if (!more) break;
-      T += kTripParts;
-    }
-  }
-  __syncthreads();
-  if (!row_ok || part != 0) return;
-
-  // one wave per row: certificate and selection
-  uint32_t* stats = A.ctrl + kStatsOff;
-  int32_t* out = A.out + (int64_t)t * A.K;
-  if (lane == 0) atomicAdd(&stats[kStRows], 1u);
-  const int rs_t = A.row_start[t], re_t = A.row_end[t];
-  if (rs_t < 0 || rs_t > re_t || re_t > A.N) {
-    for (int i = (int)lane; i < A.K; i += 64) out[i] = -1;
-    if (lane == 0) atomicAdd(&stats[kStBad], 1u);
-    return;
-  }
-  const int L = re_t - rs_t;
-  const int kr = min(A.K, L);
-  const uint32_t n = s_cnt[row];
-  if (n >= (uint32_t)kr && n <= lcap + scap) {
-    const SrcLdsSpill src{s_key[row], s_idx[row], (int)min(n, lcap), A.cand_key + (int64_t)t * kCandCap,
-                          A.cand_idx + (int64_t)t * kCandCap};
-    // the wave's 1 KiB of prepare scratch is free now: use it as the histogram
-    uint32_t* hist = reinterpret_cast<uint32_t*>(s_qprep[wave]);
-    const SelResult sel = (n > (uint32_t)kr) ? wave_radix_select(src, (int)n, kr, hist, lane, true)
-                                            : SelResult{0u, 0u, kr};
-    wave_emit(src, (int)n, sel, kr, A.K, out, lane);
-    if (lane == 0) {
-      atomicAdd(&stats[kStFast], 1u);
-      if (n > lcap) atomicAdd(&stats[kStSpilled], 1u);
-      if (L <= A.K) atomicAdd(&stats[kStTrivial], 1u);
-    }
-  } else if (lane == 0) {
-    const uint32_t f = atomicAdd(&A.ctrl[kCtrlFail], 1u);
-    A.fail_list[f] = t;
-    atomicAdd(&stats[n < (uint32_t)kr ? kStUnder : kStOver], 1u);
-  }
+  return r;
 }
 
-// ------------------------------------------------------------------ repair
-
-// Exact repair of rows the certificate rejected: rescore the whole row into
-// this workgroup's scratch slice as order-preserving keys, building the
-// top-byte histogram on the way, then finish the radix select over the
-// scratch.  Persistent: workgroup g handles failures g, g+G, ...
-__global__ __launch_bounds__(kWG) void k_prefill_repair(PrefillArgs A) {
+// Rescore chunk c of slotted failed row f into its scratch row and add the
+// chunk's top-byte histogram to the row's first histogram.  Failures beyond
+// the slots are then repaired whole, one per fallback workgroup.
+__global__ __launch_bounds__(kWG) void k_prefill_repair_score(PrefillArgs A) {
   __shared__ SelShared sh;
   __shared__ uint8_t s_qprep[kWaves][kUTerms * kD];
   const int tid = threadIdx.x;
   const uint32_t lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const uint32_t n_fail = __atomic_load_n(&A.ctrl[kCtrlFail], __ATOMIC_RELAXED);
-  uint32_t* scratch = A.scratch + (int64_t)blockIdx.x * A.N;
+  const uint32_t n_slot = min(n_fail, (uint32_t)A.rslots);
+  const int ntiles = (A.N + 63) >> 6;
+  const int cmax = (ntiles + kRepairChunkTiles - 1) / kRepairChunkTiles;
+  const KeyBuf kbuf = make_keybuf(A.k, A.k_scale, A.N);
+  const rsrc_t ktb = __builtin_amdgcn_make_buffer_rsrc((void*)A.kt, (short)0, ntiles * kTile * kD, 0x00020000);
+  const int64_t items = (int64_t)n_slot * cmax;
+#pragma unroll 1
+  for (int64_t i = blockIdx.x; i < items; i += gridDim.x) {
+    const int f = (int)(i / cmax), c = (int)(i % cmax);
+    const int t = A.fail_list[f];
+    const int s0 = A.row_start[t], s1 = A.row_end[t];
+    const int tile_lo = (s0 >> 6) + c * kRepairChunkTiles;
+    const int tile_hi = min((s1 + 63) >> 6, tile_lo + kRepairChunkTiles);
+    if (tile_lo >= tile_hi) continue;
+    sh.hist[tid] = 0u;
+    QOp qo;
+    prepare_q(qo, A.q, A.q_scale, A.w, t, lane, s_qprep[wave]);
+    __syncthreads();
+    uint32_t* scratch = A.scratch + (int64_t)f * A.rstride;
+#pragma unroll 1
+    for (int tile = tile_lo + wave; tile < tile_hi; tile += kWaves) {
+      KeyTile kt;
+      load_tile_relaid(kt, ktb, kbuf.ks, tile, lane);
+      const float sc = tile_score(qo, kt);
+      const int my = (tile << 6) + (int)lane;
+      const bool valid = my >= s0 && my < s1;
+      const uint32_t key = f2key(sc);
+      if (valid) scratch[my - s0] = key;
+      hist_add(sh.hist, key >> 24, valid);
+    }
+    __syncthreads();
+    const uint32_t h = sh.hist[tid];
+    if (h) atomicAdd(&A.rhist[(int64_t)f * 4 * 256 + tid], h);
+    __syncthreads();
+  }
+  if (blockIdx.x >= kRepairFallback) return;
+  uint32_t* own = A.scratch + ((int64_t)A.rslots + blockIdx.x) * A.rstride;
   uint32_t* stats = A.ctrl + kStatsOff;
 #pragma unroll 1
-  for (uint32_t f = blockIdx.x; f < n_fail; f += gridDim.x) {
+  for (uint32_t f = (uint32_t)A.rslots + blockIdx.x; f < n_fail; f += kRepairFallback) {
     const int t = A.fail_list[f];
     const int s0 = A.row_start[t], s1 = A.row_end[t];
     QOp qo;
-    prepare_q(qo, A.q, A.q_scale, A.w, t, lane, s_qprep[tid >> 6]);
+    prepare_q(qo, A.q, A.q_scale, A.w, t, lane, s_qprep[wave]);
     repair_row(qo, make_keybuf(A.k, A.k_scale, A.N), TileContig{}, IdIdentity{}, s0, s1, A.K,
-               A.out + (int64_t)t * A.K, scratch, sh, tid);
+               A.out + (int64_t)t * A.K, own, sh, tid);
     if (tid == 0) atomicAdd(&stats[kStRepaired], 1u);
+    __syncthreads();
+  }
+}
+
+// Keys of chunk c of a scratch row, four per 16-byte load: thread tid holds
+// positions c*kRepairChunk + 4*(k*kWG + tid) + e for k < 4, e < 4.
+struct ChunkKeys {
+  uint32_t v[16];
+  int base;  // position of v[0] relative to the row start
+};
+
+__device__ __forceinline__ void load_chunk(ChunkKeys& ck, const uint32_t* row, int c, int L, int tid) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int e0 = c * kRepairChunk + 4 * (k * kWG + tid);
+    uint4 x = make_uint4(0u, 0u, 0u, 0u);
+    if (e0 < L) x = *reinterpret_cast<const uint4*>(row + e0);
+    ck.v[4 * k + 0] = x.x; ck.v[4 * k + 1] = x.y; ck.v[4 * k + 2] = x.z; ck.v[4 * k + 3] = x.w;
+  }
+  ck.base = c * kRepairChunk + 4 * tid;
+}
+
+__device__ __forceinline__ int chunk_pos(const ChunkKeys& ck, int j) { return ck.base + (j >> 2) * 4 * kWG + (j & 3); }
+
+// Digit pass P (1..3) over the slotted failed rows that are still open.
+template <int P>
+__global__ __launch_bounds__(kWG) void k_prefill_repair_pass(PrefillArgs A) {
+  __shared__ SelShared sh;
+  const int tid = threadIdx.x;
+  const uint32_t n_slot = min(__atomic_load_n(&A.ctrl[kCtrlFail], __ATOMIC_RELAXED), (uint32_t)A.rslots);
+  const int cmax = (A.N + kRepairChunk - 1) / kRepairChunk;
+  const int64_t items = (int64_t)n_slot * cmax;
+#pragma unroll 1
+  for (int64_t i = blockIdx.x; i < items; i += gridDim.x) {
+    const int f = (int)(i / cmax), c = (int)(i % cmax);
+    const int t = A.fail_list[f];
+    const int L = A.row_end[t] - A.row_start[t];
+    if (c * kRepairChunk >= L) continue;
+    const uint32_t* rh = A.rhist + (int64_t)f * 4 * 256;
+    const RepairSel rs = repair_replay(rh, L, min(A.K, L), P, sh, tid);
+    if (rs.done) continue;
+    ChunkKeys ck;
+    load_chunk(ck, A.scratch + (int64_t)f * A.rstride, c, L, tid);
+    sh.hist[tid] = 0u;
+    __syncthreads();
+    constexpr int shift = 24 - 8 * P;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const bool v = chunk_pos(ck, j) < L && (ck.v[j] & rs.mask) == rs.prefix;
+      hist_add(sh.hist, (ck.v[j] >> shift) & 255u, v);
+    }
+    __syncthreads();
+    const uint32_t h = sh.hist[tid];
+    if (h) atomicAdd(&A.rhist[((int64_t)f * 4 + P) * 256 + tid], h);
+    __syncthreads();
+  }
+}
+
+// Write each slotted failed row's selection: keys above the boundary prefix
+// and the first `rem` keys equal to it, positions from the row's counters.
+__global__ __launch_bounds__(kWG) void k_prefill_repair_emit(PrefillArgs A) {
+  __shared__ SelShared sh;
+  const int tid = threadIdx.x;
+  const uint32_t n_slot = min(__atomic_load_n(&A.ctrl[kCtrlFail], __ATOMIC_RELAXED), (uint32_t)A.rslots);
+  const int cmax = (A.N + kRepairChunk - 1) / kRepairChunk;
+  const int64_t items = (int64_t)n_slot * cmax;
+  uint32_t* stats = A.ctrl + kStatsOff;
+#pragma unroll 1
+  for (int64_t i = blockIdx.x; i < items; i += gridDim.x) {
+    const int f = (int)(i / cmax), c = (int)(i % cmax);
+    const int t = A.fail_list[f];
+    const int s0 = A.row_start[t];
+    const int L = A.row_end[t] - s0;
+    const int kr = min(A.K, L);
+    int32_t* out = A.out + (int64_t)t * A.K;
+    if (c == 0) {
+      for (int j = kr + tid; j < A.K; j += kWG) out[j] = -1;
+      if (tid == 0) atomicAdd(&stats[kStRepaired], 1u);
+    }
+    if (c * kRepairChunk >= L) continue;
+    const RepairSel rs = repair_replay(A.rhist + (int64_t)f * 4 * 256, L, kr, 4, sh, tid);
+    ChunkKeys ck;
+    load_chunk(ck, A.scratch + (int64_t)f * A.rstride, c, L, tid);
+    // count this chunk's winners in LDS, then reserve their output range
+    // with one device-memory atomic per class
+    uint32_t gmask = 0u, emask = 0u;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const bool v = chunk_pos(ck, j) < L;
+      const uint32_t mk = ck.v[j] & rs.mask;
+      gmask |= (uint32_t)(v && mk > rs.prefix) << j;
+      emask |= (uint32_t)(v && mk == rs.prefix) << j;
+    }
+    if (tid == 0) { sh.gt_count = 0u; sh.eq_count = 0u; }
+    __syncthreads();
+    const uint32_t ng = (uint32_t)__popc(gmask), ne = (uint32_t)__popc(emask);
+    uint32_t pg = 0u, pe = 0u;
+    if (ng) pg = atomicAdd(&sh.gt_count, ng);
+    if (ne) pe = atomicAdd(&sh.eq_count, ne);
+    __syncthreads();
+    if (tid == 0) {
+      sh.pad0 = sh.gt_count ? atomicAdd(&A.rcnt[2 * f + 0], sh.gt_count) : 0u;
+      sh.pad1 = sh.eq_count ? atomicAdd(&A.rcnt[2 * f + 1], sh.eq_count) : 0u;
+    }
+    __syncthreads();
+    pg += sh.pad0;
+    pe += sh.pad1;
+    const int eq_base = kr - rs.rem;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int pos = chunk_pos(ck, j);
+      if (gmask >> j & 1u) out[pg++] = s0 + pos;
+      if (emask >> j & 1u) {
+        if ((int)pe < rs.rem) out[eq_base + pe] = s0 + pos;
+        ++pe;
+      }
+    }
     __syncthreads();
   }
 }
@@ -676,14 +516,18 @@ int launch_prefill(const PrefillArgs& A, hipStream_t stream) {
   if (A.Q == 0) return IDX_OK;
   const int64_t nchunks = (int64_t)((A.N + 63) >> 6) * 512;
   if (nchunks > 0) hipLaunchKernelGGL(k_relayout_keys, dim3((unsigned)(nchunks / kWG)), dim3(kWG), 0, stream, A);
-  hipLaunchKernelGGL(k_prefill_tau, dim3(A.Q), dim3(kWG), 0, stream, A);
+  hipLaunchKernelGGL(k_prefill_tau, dim3((A.Q + kWaves - 1) / kWaves), dim3(kWG), 0, stream, A);
   if (A.ev_main_start && hipEventRecord(A.ev_main_start, stream) != hipSuccess) return IDX_EHIP;
   if (A.dbg_scores)
     hipLaunchKernelGGL(k_prefill_pair<true>, dim3((A.Q + 1) / 2), dim3(kWG), 0, stream, A);
   else
     hipLaunchKernelGGL(k_prefill_pair<false>, dim3((A.Q + 1) / 2), dim3(kWG), 0, stream, A);
   if (A.ev_main_stop && hipEventRecord(A.ev_main_stop, stream) != hipSuccess) return IDX_EHIP;
-  hipLaunchKernelGGL(k_prefill_repair, dim3(repair_grid(A.Q)), dim3(kWG), 0, stream, A);
+  hipLaunchKernelGGL(k_prefill_repair_score, dim3(kRepairGrid), dim3(kWG), 0, stream, A);
+  hipLaunchKernelGGL(k_prefill_repair_pass<1>, dim3(kRepairGrid), dim3(kWG), 0, stream, A);
+  hipLaunchKernelGGL(k_prefill_repair_pass<2>, dim3(kRepairGrid), dim3(kWG), 0, stream, A);
+  hipLaunchKernelGGL(k_prefill_repair_pass<3>, dim3(kRepairGrid), dim3(kWG), 0, stream, A);
+  hipLaunchKernelGGL(k_prefill_repair_emit, dim3(kRepairGrid), dim3(kWG), 0, stream, A);
   return hipGetLastError() == hipSuccess ? IDX_OK : IDX_EHIP;
 }
 
