@@ -1,20 +1,29 @@
 """Benchmark: fused indexer scoring + exact top-2048 on one MI355X.
 
-One step = one complete operator call (threshold sampler, fused main kernel,
-exact repair) over one batch of seeded synthetic input already resident in
-HBM.  Throughput counts the scoring the causal ranges require
-(Fused Indexer Top-k page, "5.1 Version trajectory" equation): pairs =
-sum_t (row_end - row_start), FLOP = 2*64*128 per pair.
+One step = one complete operator call over one batch of seeded synthetic
+input already resident in HBM: for prefill the threshold sampler, the fused
+main kernel and the exact repair (idx_topk_prefill); for paged decode the
+prep, split and repair kernels (idx_topk_decode_paged).  Throughput counts
+the scoring the valid ranges require (Fusing Indexer Scoring and Exact Top-k
+page, "5.1 Version trajectory" equation): pairs = sum over rows of the range
+length, 2*64*128 FLOP per pair.
 
-Prints ONE JSON line.  The roofline object is for the fused main kernel:
-its duration comes from HIP events recorded on the call's stream right
-around that kernel in every timed step.
+The timed calls go through the *_debug entry points with nothing set but a
+pair of HIP events recorded on the call's stream right around the dominant
+kernel; kernels and arguments are otherwise those of the plain entry points.
+
+Prints ONE JSON line.  The roofline object is for the dominant kernel:
+k_prefill_pair (bound by FP8 MFMA) for prefill, k_decode_split (bound by
+HBM) for decode.
 """
 from __future__ import annotations
 
 import argparse
+import glob
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -29,32 +38,215 @@ import synth  # noqa: E402
 
 FLOP_PER_PAIR = 2 * 64 * 128
 FP8_DENSE_PEAK_TFLOPS = 5000.0  # MI355X dense FP8 MFMA
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E
+METRIC = "fused score+top-2048 Gqk-pairs/s and % FP8 MFMA peak at 128K ctx, 1 MI355X"
+PREFILL = ["long_prefill", "prefill_chunk", "prefill_smoke", "adversarial"]
+DECODE = ["paged_decode"]
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def to_dev(case):
-    t = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a)).cuda()
-    return dict(q8=t(case.q8), q_scale=t(case.q_scale), k8=t(case.k8), k_scale=t(case.k_scale),
-                w=t(case.w), row_start=t(case.row_start), row_end=t(case.row_end))
+def tensor(a):
+    return None if a is None else torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
 
-def cpu_baseline(case, n_rows: int):
-    """The oracle as it stands, on an evenly spaced sample of full rows."""
-    import oracle
-    rows = np.linspace(0, case.Q - 1, n_rows).round().astype(np.int32)
-    pairs = int((case.row_end[rows].astype(np.int64) - case.row_start[rows]).sum())
+def oracle_threads() -> int:
     threads = len(os.sched_getaffinity(0))
     if os.environ.get("OMP_NUM_THREADS"):
         threads = min(threads, int(os.environ["OMP_NUM_THREADS"]))
-    t0 = time.perf_counter()
-    oracle.prefill_case(case, rows=rows, want_scores=False, nthreads=threads)
-    dt = time.perf_counter() - t0
+    return threads
+
+
+def cpu_baseline_prefill(case, seconds: float, chunk: int = 64):
+    """The oracle as it stands, on a bounded sample of full rows: chunks of
+    rows from a seeded permutation until `seconds` of work have been done."""
+    import oracle
+    order = np.random.default_rng(0).permutation(case.Q).astype(np.int32)
+    threads = oracle_threads()
+    done, pairs, dt = 0, 0, 0.0
+    while done < case.Q and dt < seconds:
+        rows = np.sort(order[done:done + chunk])
+        t0 = time.perf_counter()
+        oracle.prefill_case(case, rows=rows, want_scores=False, nthreads=threads)
+        dt += time.perf_counter() - t0
+        pairs += int((case.row_end[rows].astype(np.int64) - case.row_start[rows]).sum())
+        done += len(rows)
     return {"value": pairs / dt / 1e9, "unit": "Gqk-pairs/s", "cores": threads, "kind": "oracle",
-            "sample": "%d of %d rows of %s (evenly spaced, full rows: fp64 exact scoring + full "
-                      "sort), %.1f s" % (n_rows, case.Q, case.name, dt)}
+            "sample": "%d of %d rows of %s (seeded random full rows, fp64 exact scoring + full "
+                      "sort per row), %.1f s" % (done, case.Q, case.name, dt)}
+
+
+def cpu_baseline_decode(case, seconds: float):
+    """The oracle on the whole decode batch, repeated until `seconds`."""
+    import oracle
+    threads = oracle_threads()
+    reps, dt = 0, 0.0
+    while reps == 0 or dt < seconds:
+        t0 = time.perf_counter()
+        oracle.decode_case(case, want_scores=False, nthreads=threads)
+        dt += time.perf_counter() - t0
+        reps += 1
+    return {"value": case.pairs * reps / dt / 1e9, "unit": "Gqk-pairs/s", "cores": threads,
+            "kind": "oracle",
+            "sample": "the whole %s batch (%d sequences, %d keys) x %d, fp64 exact scoring + full "
+                      "sort per sequence, %.1f s" % (case.name, case.B, case.pairs, reps, dt)}
+
+
+def source_digest() -> str:
+    """sha256 over the HIP sources, the public header and the build flags."""
+    h = hashlib.sha256()
+    pkg = os.path.join(ROOT, "scoring_exact_top_amd")
+    files = sorted(glob.glob(os.path.join(pkg, "csrc", "*"))) + [
+        os.path.join(ROOT, "include", "idx_topk.h"), os.path.join(pkg, "build.py")]
+    for f in files:
+        h.update(os.path.relpath(f, ROOT).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def stored_traffic(kernel: str, workload: str):
+    """HBM bytes per launch of `kernel` from the committed counter summary,
+    or None when there is none for this workload or it covers other sources."""
+    path = os.path.join(ROOT, "profiles", "%s_%s_hbm_traffic.md" % (kernel, workload))
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_b = re.search(r"^traffic_bytes_per_launch\s*=\s*(\d+)", text, re.M)
+    m_h = re.search(r"^source_sha256\s*=\s*([0-9a-f]{64})", text, re.M)
+    if not (m_b and m_h) or m_h.group(1) != source_digest():
+        return None
+    return int(m_b.group(1))
+
+
+def calibrate_copy(mib: int):
+    """A plain device-to-device copy of `mib` MiB, the reference for scaling
+    the FETCH_SIZE / WRITE_SIZE counters."""
+    x = torch.ones(mib << 18, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    torch.cuda.synchronize()
+    y.copy_(x)
+    torch.cuda.synchronize()
+    log("copied %d MiB" % mib)
+
+
+def timed(step, n_calls: int, steps: int, warmup: int):
+    """Run `warmup` untimed steps, then `steps` timed ones bracketed by
+    synchronisation; step(evs) records evs[j] around call j's dominant
+    kernel.  Returns (ms per step, mean dominant-kernel ms per launch, min)."""
+    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in range(n_calls)] for _ in range(steps)]
+    for step_evs in evs:  # torch creates the HIP events on first record
+        for e0, e1 in step_evs:
+            e0.record()
+            e1.record()
+    for _ in range(warmup):
+        step(None)
+    torch.cuda.synchronize()
+    t_begin = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    t_begin.record()
+    for s in range(steps):
+        step(evs[s])
+    t_end.record()
+    torch.cuda.synchronize()
+    ms_per_step = t_begin.elapsed_time(t_end) / steps
+    per_step = [sum(e0.elapsed_time(e1) for e0, e1 in step_evs) for step_evs in evs]
+    return ms_per_step, float(np.mean(per_step)) / n_calls, min(per_step) / n_calls
+
+
+def result(args, value, ms_per_step, config, roofline, dtype):
+    return {"metric": METRIC, "value": value, "unit": "Gqk-pairs/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dtype,
+            "data": "synthetic (seeded Gaussian, e4m3 with amax/448 scales)", "config": config,
+            "roofline": roofline}
+
+
+def bench_prefill(args, lib):
+    made = synth.WORKLOADS[args.workload](0)
+    cases = made if isinstance(made, list) else [made]
+    pairs = sum(c.pairs for c in cases)
+    devs = [{k: tensor(getattr(c, k)) for k in
+             ("q8", "q_scale", "k8", "k_scale", "w", "row_start", "row_end")} for c in cases]
+    outs = [torch.empty((c.Q, c.K), dtype=torch.int32, device="cuda") for c in cases]
+    wss = [lib.alloc_workspace(lib.prefill_workspace_bytes(c.Q, c.N, c.K), "cuda") for c in cases]
+    n_calls = len(cases)
+
+    def step(step_evs):
+        for j, (c, d) in enumerate(zip(cases, devs)):
+            lib.prefill_debug(d["q8"], d["q_scale"], d["k8"], d["k_scale"], d["w"], d["row_start"],
+                              d["row_end"], c.K, out=outs[j], workspace=wss[j],
+                              main_events=None if step_evs is None else step_evs[j])
+
+    ms_per_step, main_avg, main_min = timed(step, n_calls, args.steps, args.warmup)
+    log("workload", args.workload, "pairs", pairs, "ms/step %.4f" % ms_per_step,
+        "main kernel ms/launch %.4f (min %.4f)" % (main_avg, main_min))
+    for c, ws in zip(cases, wss):
+        log("  ", c.name, lib.read_stats(ws))
+    achieved = FLOP_PER_PAIR * (pairs / n_calls) / (main_avg * 1e-3) / 1e12
+    config = {"workload": cases[0].name if n_calls == 1 else args.workload,
+              "rows": sum(c.Q for c in cases), "keys": max(c.N for c in cases), "heads": 64,
+              "dim": 128, "K": cases[0].K, "pairs": pairs, "calls_per_step": n_calls}
+    roofline = {"bound": "mfma", "achieved": achieved, "peak": FP8_DENSE_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": achieved / FP8_DENSE_PEAK_TFLOPS,
+                "traffic": stored_traffic("k_prefill_pair", args.workload) if n_calls == 1 else None,
+                "kernel": "k_prefill_pair", "ms_per_launch": main_avg}
+    res = result(args, pairs / (ms_per_step * 1e-3) / 1e9, ms_per_step, config, roofline,
+                 "fp8_e4m3 x fp8_e4m3 -> f32")
+    res["pct_fp8_peak"] = (100.0 * pairs * FLOP_PER_PAIR / (ms_per_step * 1e-3) / 1e12
+                           / FP8_DENSE_PEAK_TFLOPS)
+    if args.cpu_seconds > 0:
+        res["cpu_baseline"] = cpu_baseline_prefill(cases[0], args.cpu_seconds)
+    return res
+
+
+def decode_split_bytes(case) -> int:
+    """Algorithmic bytes of k_decode_split: every scored sequence (L > K)
+    reads its keys (128 B codes + 4 B scale each), its page-table entries,
+    its query (64x128 B), weights and q scales (2 x 64 x 4 B), and writes K
+    output ids; shorter sequences take the remap path outside this kernel."""
+    n = 0
+    for L in case.seq_lens.astype(np.int64):
+        if L > case.K:
+            n += L * 132 + ((L + 63) // 64) * 4 + 64 * 128 + 2 * 64 * 4 + case.K * 4
+    return int(n)
+
+
+def bench_decode(args, lib):
+    case = synth.WORKLOADS[args.workload](0)
+    d = {k: tensor(getattr(case, k)) for k in
+         ("q8", "q_scale", "k_cache", "k_scale", "w", "page_table", "seq_lens")}
+    out = torch.empty((case.B, case.K), dtype=torch.int32, device="cuda")
+    ws = lib.alloc_workspace(lib.decode_workspace_bytes(case.B, case.max_pages, case.page_size,
+                                                        case.K), "cuda")
+
+    def step(step_evs):
+        lib.decode_paged(d["q8"], d["q_scale"], d["k_cache"], d["k_scale"], d["w"], d["page_table"],
+                         d["seq_lens"], case.K, out=out, workspace=ws,
+                         main_events=None if step_evs is None else step_evs[0])
+
+    ms_per_step, main_avg, main_min = timed(step, 1, args.steps, args.warmup)
+    log("workload", args.workload, "keys", case.pairs, "ms/step %.4f" % ms_per_step,
+        "split kernel ms/launch %.4f (min %.4f)" % (main_avg, main_min))
+    log("  ", case.name, lib.read_stats(ws))
+    nbytes = decode_split_bytes(case)
+    achieved = nbytes / (main_avg * 1e-3) / 1e9
+    config = {"workload": case.name, "batch": case.B, "keys": case.pairs,
+              "max_seq_len": int(case.seq_lens.max()), "page_size": case.page_size, "heads": 64,
+              "dim": 128, "K": case.K, "pairs": case.pairs, "calls_per_step": 1}
+    roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS,
+                "traffic": stored_traffic("k_decode_split", args.workload),
+                "kernel": "k_decode_split", "ms_per_launch": main_avg,
+                "algorithmic_bytes": nbytes}
+    res = result(args, case.pairs / (ms_per_step * 1e-3) / 1e9, ms_per_step, config, roofline,
+                 "fp8_e4m3 x fp8_e4m3 -> f32")
+    if args.cpu_seconds > 0:
+        res["cpu_baseline"] = cpu_baseline_decode(case, args.cpu_seconds)
+    return res
 
 
 def main():
@@ -62,83 +254,22 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="long_prefill",
-                    choices=["long_prefill", "prefill_chunk", "prefill_smoke", "adversarial"])
-    ap.add_argument("--cpu-rows", type=int, default=128, help="oracle sample size (0: skip)")
+    ap.add_argument("--workload", default="long_prefill", choices=PREFILL + DECODE)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="oracle sample budget in seconds (0: skip the CPU baseline)")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain copy of MIB MiB (counter calibration) and exit")
     args = ap.parse_args()
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
         sys.exit(2)
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     import scoring_exact_top_amd as lib
-
-    made = synth.WORKLOADS[args.workload](0)
-    cases = made if isinstance(made, list) else [made]
-    pairs = sum(c.pairs for c in cases)
-    devs = [to_dev(c) for c in cases]
-    outs = [torch.empty((c.Q, c.K), dtype=torch.int32, device="cuda") for c in cases]
-    wss = [lib.alloc_workspace(lib.prefill_workspace_bytes(c.Q, c.N, c.K), "cuda") for c in cases]
-    n_calls = len(cases)
-    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-            for _ in range(n_calls)] for _ in range(args.steps)]
-    for step_evs in evs:  # create the events so their handles exist
-        for e0, e1 in step_evs:
-            e0.record(); e1.record()
-
-    def step(step_evs=None):
-        for j, (c, d) in enumerate(zip(cases, devs)):
-            lib.prefill_debug(d["q8"], d["q_scale"], d["k8"], d["k_scale"], d["w"], d["row_start"],
-                              d["row_end"], c.K, out=outs[j], workspace=wss[j],
-                              main_events=None if step_evs is None else step_evs[j])
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    t_begin = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    t_begin.record()
-    for s in range(args.steps):
-        step(evs[s])
-    t_end.record()
-    torch.cuda.synchronize()
-    total_ms = t_begin.elapsed_time(t_end)
-    ms_per_step = total_ms / args.steps
-    main_ms = [sum(e0.elapsed_time(e1) for e0, e1 in step_evs) for step_evs in evs]
-    main_avg = float(np.mean(main_ms)) / n_calls  # per launch
-    stats = [lib.read_stats(ws) for ws in wss]
-    log("workload", args.workload, "pairs", pairs, "ms/step %.4f" % ms_per_step,
-        "main kernel ms/launch %.4f (min %.4f)" % (main_avg, min(main_ms) / n_calls))
-    for c, st in zip(cases, stats):
-        log("  ", c.name, st)
-
-    pairs_per_launch = pairs / n_calls
-    achieved = FLOP_PER_PAIR * pairs_per_launch / (main_avg * 1e-3) / 1e12
-    res = {
-        "metric": "fused score+top-2048 Gqk-pairs/s and % FP8 MFMA peak at 128K ctx, 1 MI355X",
-        "value": pairs / (ms_per_step * 1e-3) / 1e9,
-        "unit": "Gqk-pairs/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": ms_per_step,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "fp8_e4m3 x fp8_e4m3 -> f32",
-        "data": "synthetic (seeded Gaussian, e4m3 with amax/448 scales)",
-        "config": {"workload": cases[0].name if n_calls == 1 else args.workload,
-                   "rows": sum(c.Q for c in cases), "keys": max(c.N for c in cases),
-                   "heads": 64, "dim": 128, "K": cases[0].K, "pairs": pairs,
-                   "calls_per_step": n_calls},
-        "roofline": {"bound": "mfma", "achieved": achieved, "peak": FP8_DENSE_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": achieved / FP8_DENSE_PEAK_TFLOPS, "traffic": None,
-                     "kernel": "k_prefill_fused", "ms_per_launch": main_avg},
-        "pct_fp8_peak": 100.0 * pairs * FLOP_PER_PAIR / (ms_per_step * 1e-3) / 1e12
-                        / FP8_DENSE_PEAK_TFLOPS,
-    }
-    if args.cpu_rows > 0:
-        res["cpu_baseline"] = cpu_baseline(cases[0], min(args.cpu_rows, cases[0].Q))
+    res = (bench_decode if args.workload in DECODE else bench_prefill)(args, lib)
     print(json.dumps(res), flush=True)
 
 

@@ -2,7 +2,7 @@
  * idx_topk.h -- DSA Lightning Indexer scoring fused with exact per-row top-K
  * on AMD Instinct MI355X (gfx950).
  *
- * The operation (Fused Indexer Top-k page, "1.1 The problem" equation and
+ * The operation (Fusing Indexer Scoring and Exact Top-k page, "1.1 The problem" equation and
  * "2.3 Problem definition"):
  *
  *     I[t,s] = sum_{j<64} w[t,j] * ReLU( q[t,j] . k[s] )
@@ -17,7 +17,7 @@
  * ("3.2 Sampled threshold: turn maintenance into filtering"); rows where it
  * does not are recomputed by an exact repair path.
  *
- * The paged decode variant follows the contest report page, "DSA TopK
+ * The paged decode variant follows the contest report page (arXiv 2608.14560), "DSA TopK
  * Indexer": one FP8 query per sequence, a paged FP8 key cache with per-token
  * FP32 scales, per-head weights and sequence lengths; sequences no longer
  * than K reduce to an index remap.
@@ -91,14 +91,14 @@ typedef struct {
   int32_t lds_cap;     /* >0: on-chip candidate capacity per row (<= default)   */
   int32_t spill_cap;   /* >0: spill capacity per row (<= default); -1: none     */
   void *ev_main_start; /* hipEvent_t or NULL: recorded on `stream` right before */
-  void *ev_main_stop;  /*   and right after the fused main kernel (timing only) */
+  void *ev_main_stop;  /*   and right after the main scoring kernel (timing only) */
 } idx_topk_opts;
 
 /* Bytes of workspace idx_topk_prefill needs for Q rows over N keys. */
 size_t idx_topk_prefill_workspace(int32_t Q, int32_t N, int32_t K);
 
 /*
- * Prefill: top-K ids per query row (Fused Indexer Top-k page, "2.3 Problem
+ * Prefill: top-K ids per query row (Fusing Indexer Scoring and Exact Top-k page, "2.3 Problem
  * definition").
  *   q         [Q][64][128] uint8 e4m3fn codes, 16-byte aligned
  *   q_scale   [Q][64] float > 0, or NULL for all-ones
@@ -134,7 +134,7 @@ int idx_topk_prefill_debug(const uint8_t *q, const float *q_scale, const uint8_t
 size_t idx_topk_decode_workspace(int32_t B, int32_t max_pages, int32_t page_size, int32_t K);
 
 /*
- * Paged decode (contest report page, "DSA TopK Indexer"): one query per
+ * Paged decode (contest report page (arXiv 2608.14560), "DSA TopK Indexer"): one query per
  * sequence b, keys at logical positions i in [0, seq_lens[b]) stored in page
  * page_table[b][i / page_size], slot i % page_size.
  *   q          [B][64][128] uint8 e4m3fn, 16-byte aligned
@@ -154,6 +154,20 @@ int idx_topk_decode_paged(const uint8_t *q, const float *q_scale, const uint8_t 
                           const int32_t *seq_lens, int32_t B, int32_t max_pages,
                           int32_t page_size, int32_t num_pages, int32_t K, int32_t *out_idx,
                           void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Same as idx_topk_decode_paged, plus diagnostics for tests and timing.
+ * opts (NULL = none) is read as follows: force_tau/tau_value replace every
+ * scored sequence's sampled threshold (so that tests can force the repair
+ * path); ev_main_start/ev_main_stop are recorded right before and right
+ * after the split scoring kernel; lds_cap and spill_cap are ignored.
+ */
+int idx_topk_decode_paged_debug(const uint8_t *q, const float *q_scale, const uint8_t *k_cache,
+                                const float *k_scale, const float *w, const int32_t *page_table,
+                                const int32_t *seq_lens, int32_t B, int32_t max_pages,
+                                int32_t page_size, int32_t num_pages, int32_t K, int32_t *out_idx,
+                                void *workspace, size_t workspace_bytes, void *stream,
+                                const idx_topk_opts *opts);
 
 /* Copy the counters of the last call that used `workspace` into *out.
  * Synchronises `stream`.  For tests and diagnosis, not for hot loops. */

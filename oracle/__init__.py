@@ -5,11 +5,11 @@ leg are the only users.  The product path (scoring_exact_top_amd) never imports
 this package.  The arithmetic lives in idx_oracle.c (plain C, fp64, OpenMP over
 rows); this module only builds it with gcc and marshals numpy arrays.
 
-Definitions followed (Fused Indexer Top-k page): the score equation of "1.1
+Definitions followed (Fusing Indexer Scoring and Exact Top-k page): the score equation of "1.1
 The problem", the inputs/outputs of "2.3 Problem definition" (FP8 Q and KV
 "each with scales", head weights, half-open valid range, K int32 indices,
 unsorted), and the exactness criterion of the same section.  The paged decode
-variant follows the contest report page, "DSA TopK Indexer".
+variant follows the contest report page (arXiv 2608.14560), "DSA TopK Indexer".
 """
 from __future__ import annotations
 

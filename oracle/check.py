@@ -1,6 +1,6 @@
 """Exactness checks against the oracle -- TEST INFRASTRUCTURE ONLY.
 
-The criterion is the one of the Fused Indexer Top-k page, "2.3 Problem
+The criterion is the one of the Fusing Indexer Scoring and Exact Top-k page, "2.3 Problem
 definition": indices lie in the valid range and are distinct, the K selected
 scores sorted equal the true top-K scores, and ties may resolve to any valid
 index.  Because the GPU computes scores in FP32 while the oracle is fp64, the

@@ -7,7 +7,7 @@
  * with the GPU library (scoring_exact_top_amd/csrc) and neither includes the
  * other.
  *
- * What it computes (Fused Indexer Top-k page, "1.1 The problem" equation and
+ * What it computes (Fusing Indexer Scoring and Exact Top-k page, "1.1 The problem" equation and
  * "2.3 Problem definition"):
  *
  *   I[t,s] = sum_{j<64} w[t,j] * ReLU( q[t,j] . k[s] ),     s in [start_t, end_t)
@@ -195,7 +195,7 @@ int oracle_prefill_rows(const uint8_t *q, const float *q_scale, const uint8_t *k
 }
 
 /*
- * Paged decode oracle (contest report page, "DSA TopK Indexer"): one query per
+ * Paged decode oracle (contest report page (arXiv 2608.14560), "DSA TopK Indexer"): one query per
  * sequence b, logical positions i in [0, seq_lens[b]), key i lives in page
  * page_table[b][i / page_size] at slot i % page_size.  Output ids are physical
  * cache slots page * page_size + slot, -1 padded.

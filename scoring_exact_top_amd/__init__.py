@@ -4,7 +4,7 @@ Thin ctypes binding of libidxtopk.so (C ABI in include/idx_topk.h).  This
 module only marshals arguments: torch supplies device memory and the current
 stream; every step of the computation runs in the library's HIP kernels.
 Importing raises if the library has not been built (run
-``python -m scoring_exact_top_amd.build`` or ``__graft_entry__.build()``).
+``python scoring_exact_top_amd/build.py`` or ``__graft_entry__.build()``).
 """
 from __future__ import annotations
 
@@ -23,7 +23,7 @@ KMAX = 2048
 PAGE = 64
 
 if not os.path.exists(LIB_PATH):
-    raise ImportError("libidxtopk.so is not built at %s; run python -m scoring_exact_top_amd.build"
+    raise ImportError("libidxtopk.so is not built at %s; run python scoring_exact_top_amd/build.py"
                       % LIB_PATH)
 
 _lib = ctypes.CDLL(LIB_PATH)
@@ -60,6 +60,8 @@ _lib.idx_topk_decode_workspace.argtypes = [_i32, _i32, _i32, _i32]
 _lib.idx_topk_decode_paged.restype = ctypes.c_int
 _lib.idx_topk_decode_paged.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
                                        _i32, _vp, _vp, _sz, _vp]
+_lib.idx_topk_decode_paged_debug.restype = ctypes.c_int
+_lib.idx_topk_decode_paged_debug.argtypes = _lib.idx_topk_decode_paged.argtypes + [ctypes.POINTER(Opts)]
 _lib.idx_topk_read_stats.restype = ctypes.c_int
 _lib.idx_topk_read_stats.argtypes = [_vp, ctypes.POINTER(Stats), _vp]
 _lib.idx_topk_strerror.restype = ctypes.c_char_p
@@ -168,11 +170,13 @@ def _prefill(q8, q_scale, k8, k_scale, w, row_start, row_end, K, out, workspace,
 
 
 def decode_paged(q8, q_scale, k_cache, k_scale, w, page_table, seq_lens, K: int, out=None,
-                 workspace=None, stream=None):
+                 workspace=None, stream=None, force_tau: Optional[float] = None, main_events=None):
     """Top-K physical cache slots per sequence; see idx_topk_decode_paged.
 
     q8 [B,64,128], q_scale [B,64] or None, k_cache [P,64,128], k_scale [P,64],
     w [B,64], page_table [B,max_pages] int32, seq_lens [B] int32 (device).
+    force_tau / main_events select idx_topk_decode_paged_debug (a forced
+    threshold; a (start, stop) torch.cuda.Event pair around the split kernel).
     """
     q8, k_cache = _q_k(q8, k_cache)
     B = int(q8.shape[0])
@@ -183,11 +187,18 @@ def decode_paged(q8, q_scale, k_cache, k_scale, w, page_table, seq_lens, K: int,
         out = torch.empty((B, K), dtype=torch.int32, device=dev)
     if workspace is None:
         workspace = alloc_workspace(decode_workspace_bytes(B, max_pages, page, K), dev)
-    _check(_lib.idx_topk_decode_paged(
-        _ptr(q8, torch.uint8), _ptr(q_scale, torch.float32), _ptr(k_cache, torch.uint8),
-        _ptr(k_scale, torch.float32), _ptr(w, torch.float32), _ptr(page_table, torch.int32),
-        _ptr(seq_lens, torch.int32), B, max_pages, page, P, int(K), _ptr(out, torch.int32),
-        _ptr(workspace), int(workspace.numel()), _stream(stream)))
+    args = [_ptr(q8, torch.uint8), _ptr(q_scale, torch.float32), _ptr(k_cache, torch.uint8),
+            _ptr(k_scale, torch.float32), _ptr(w, torch.float32), _ptr(page_table, torch.int32),
+            _ptr(seq_lens, torch.int32), B, max_pages, page, P, int(K), _ptr(out, torch.int32),
+            _ptr(workspace), int(workspace.numel()), _stream(stream)]
+    if force_tau is None and main_events is None:
+        _check(_lib.idx_topk_decode_paged(*args))
+    else:
+        ev0 = ev1 = None
+        if main_events is not None:
+            ev0, ev1 = (ctypes.c_void_p(e.cuda_event) for e in main_events)
+        opts = Opts(1 if force_tau is not None else 0, float(force_tau or 0.0), 0, 0, ev0, ev1)
+        _check(_lib.idx_topk_decode_paged_debug(*args, ctypes.byref(opts)))
     return out
 
 

@@ -123,7 +123,17 @@ extern "C" int idx_topk_decode_paged(const uint8_t* q, const float* q_scale, con
                                      int32_t page_size, int32_t num_pages, int32_t K, int32_t* out_idx,
                                      void* workspace, size_t workspace_bytes, void* stream) {
   return decode_paged(q, q_scale, k_cache, k_scale, w, page_table, seq_lens, B, max_pages, page_size,
-                      num_pages, K, out_idx, workspace, workspace_bytes, static_cast<hipStream_t>(stream));
+                      num_pages, K, out_idx, workspace, workspace_bytes, static_cast<hipStream_t>(stream), nullptr);
+}
+
+extern "C" int idx_topk_decode_paged_debug(const uint8_t* q, const float* q_scale, const uint8_t* k_cache,
+                                           const float* k_scale, const float* w, const int32_t* page_table,
+                                           const int32_t* seq_lens, int32_t B, int32_t max_pages,
+                                           int32_t page_size, int32_t num_pages, int32_t K, int32_t* out_idx,
+                                           void* workspace, size_t workspace_bytes, void* stream,
+                                           const idx_topk_opts* opts) {
+  return decode_paged(q, q_scale, k_cache, k_scale, w, page_table, seq_lens, B, max_pages, page_size,
+                      num_pages, K, out_idx, workspace, workspace_bytes, static_cast<hipStream_t>(stream), opts);
 }
 
 extern "C" int idx_topk_read_stats(const void* workspace, idx_topk_stats* out, void* stream) {

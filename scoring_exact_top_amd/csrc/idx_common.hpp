@@ -1,6 +1,6 @@
 // Device building blocks shared by the prefill and decode kernels (gfx950).
 //
-// Score of query row t against key s (Fused Indexer Top-k page, "1.1 The
+// Score of query row t against key s (Fusing Indexer Scoring and Exact Top-k page, "1.1 The
 // problem" equation, with the FP8 operands dequantised by their scales as in
 // "2.3 Problem definition"):
 //
@@ -550,9 +550,10 @@ __device__ SelResult radix_select_regs(const uint32_t (&key)[M], uint32_t nw, in
     __syncthreads();
 #pragma unroll
     for (int j = 0; j < M; ++j) {
-      if ((uint32_t)j >= jmax) break;
-      const bool v = (uint32_t)j * 64u + lane < nw;
-      hist_add(sh.hist, (key[j] >> shift) & 255u, v && ((key[j] & mask) == prefix));
+      if ((uint32_t)j < jmax) {  // wave-uniform guard; keeps key[] in registers
+        const bool v = (uint32_t)j * 64u + lane < nw;
+        hist_add(sh.hist, (key[j] >> shift) & 255u, v && ((key[j] & mask) == prefix));
+      }
     }
     __syncthreads();
     find_bucket(sh, rem, tid);
@@ -579,7 +580,7 @@ __device__ void emit_selection_regs(const uint32_t (&key)[M], uint32_t nw, const
   const int eq_base = kr - sel.rem;
 #pragma unroll
   for (int j = 0; j < M; ++j) {
-    if ((uint32_t)j >= jmax) break;
+    if ((uint32_t)j >= jmax) continue;  // wave-uniform
     const uint32_t i = (uint32_t)j * 64u + lane;
     const bool v = i < nw;
     const uint32_t mk = key[j] & sel.mask;

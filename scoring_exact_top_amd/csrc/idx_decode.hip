@@ -1,4 +1,4 @@
-// Paged decode path (contest report page, "DSA TopK Indexer"): one FP8 query
+// Paged decode path (contest report page (arXiv 2608.14560), "DSA TopK Indexer"): one FP8 query
 // per sequence against its keys in a paged FP8 cache with per-token scales.
 //
 //   k_decode_prep   one workgroup per sequence: validate the sequence's page
@@ -6,7 +6,7 @@
 //                   (every slot is selected, no scoring); longer ones get a
 //                   sampled threshold.
 //   k_decode_split  G workgroups per sequence split its keys (KV-dimension
-//                   parallelism, Fused Indexer Top-k page, "10. The
+//                   parallelism, Fusing Indexer Scoring and Exact Top-k page, "10. The
 //                   optimization target after fusion"); each scores its
 //                   chunk and appends keys >= tau to the sequence's candidate
 //                   list in the workspace.  The last workgroup to finish
@@ -41,6 +41,8 @@ struct DecodeArgs {
   uint32_t* cand_key;    // [B][kDecCap]
   int32_t* cand_idx;     // [B][kDecCap]
   uint32_t* scratch;     // [repair_grid(B)][max_pages*64]
+  int32_t force_tau;     // debug: every scored sequence uses tau_value
+  float tau_value;
 };
 
 struct SrcGlobal {
@@ -89,8 +91,8 @@ __global__ __launch_bounds__(kWG) void k_decode_prep(DecodeArgs A) {
     return;
   }
   const SampleGeom sg = sample_geom(L, kDecCap);
-  float tau = -INFINITY;
-  if (sg.n > 0) {
+  float tau = A.force_tau ? A.tau_value : -INFINITY;
+  if (!A.force_tau && sg.n > 0) {
     QOp qo;
     prepare_q(qo, A.q, A.q_scale, A.w, b, lane, s_qprep[tid >> 6]);
     tau = sample_tau(qo, make_keybuf(A.k, A.k_scale, (int64_t)A.num_pages * 64), TilePaged{pt}, 0, sg,
@@ -233,7 +235,7 @@ size_t decode_workspace_bytes(int32_t B, int32_t max_pages, int32_t page_size, i
 int decode_paged(const uint8_t* q, const float* q_scale, const uint8_t* k_cache, const float* k_scale,
                  const float* w, const int32_t* page_table, const int32_t* seq_lens, int32_t B,
                  int32_t max_pages, int32_t page_size, int32_t num_pages, int32_t K, int32_t* out_idx,
-                 void* workspace, size_t workspace_bytes, hipStream_t stream) {
+                 void* workspace, size_t workspace_bytes, hipStream_t stream, const idx_topk_opts* opts) {
   if (B < 0 || max_pages < 0 || num_pages < 0 || K < 1 || K > kKmax) return IDX_EINVAL;
   if (page_size != 64) return IDX_EUNSUPPORTED;
   if ((int64_t)max_pages * 64 > 0x7fffffffLL || (int64_t)num_pages * 64 > 0x7fffffffLL) return IDX_EINVAL;
@@ -261,8 +263,17 @@ int decode_paged(const uint8_t* q, const float* q_scale, const uint8_t* k_cache,
   A.cand_key = reinterpret_cast<uint32_t*>(ws + L.ckey);
   A.cand_idx = reinterpret_cast<int32_t*>(ws + L.cidx);
   A.scratch = reinterpret_cast<uint32_t*>(ws + L.scratch);
+  hipEvent_t ev0 = nullptr, ev1 = nullptr;
+  if (opts) {
+    A.force_tau = opts->force_tau ? 1 : 0;
+    A.tau_value = opts->tau_value;
+    ev0 = static_cast<hipEvent_t>(opts->ev_main_start);
+    ev1 = static_cast<hipEvent_t>(opts->ev_main_stop);
+  }
   hipLaunchKernelGGL(k_decode_prep, dim3(B), dim3(kWG), 0, stream, A);
+  if (ev0 && hipEventRecord(ev0, stream) != hipSuccess) return IDX_EHIP;
   hipLaunchKernelGGL(k_decode_split, dim3(A.G, B), dim3(kWG), 0, stream, A);
+  if (ev1 && hipEventRecord(ev1, stream) != hipSuccess) return IDX_EHIP;
   hipLaunchKernelGGL(k_decode_repair, dim3(repair_grid(B)), dim3(kWG), 0, stream, A);
   return hipGetLastError() == hipSuccess ? IDX_OK : IDX_EHIP;
 }

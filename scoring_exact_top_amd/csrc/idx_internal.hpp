@@ -130,7 +130,7 @@ struct TileContig {
   __device__ int operator()(int tile) const { return tile << 6; }
 };
 // Paged cache with 64-token pages: tile j is page table[j] ("DSA TopK
-// Indexer", contest report page: a page holds 64 tokens).
+// Indexer", contest report page (arXiv 2608.14560): a page holds 64 tokens).
 struct TilePaged {
   const int32_t* table;
   __device__ int operator()(int tile) const { return table[tile] << 6; }

@@ -1,6 +1,6 @@
 // Prefill path: sampled threshold -> fused score/filter/select -> exact repair.
 //
-// Fused Indexer Top-k page, "3.2 Sampled threshold: turn maintenance into
+// Fusing Indexer Scoring and Exact Top-k page, "3.2 Sampled threshold: turn maintenance into
 // filtering": each row gets a threshold tau from a sparse sample of its keys;
 // the main pass keeps every key with score >= tau as a candidate (compare and
 // append only), then an exact radix select over the candidates finds the

@@ -14,7 +14,7 @@ Recipe (fixed draw order per case, CPU ``torch.Generator`` seeded per case):
 
 Shapes follow the five workloads of the pages' operating points (Fused Indexer
 Top-k page, "2.3 Problem definition" and "6.1 Setup": B=1, 64 heads, d=128,
-K=2048, N from 8K to 160K; contest report page, "DSA TopK Indexer": paged
+K=2048, N from 8K to 160K; contest report page (arXiv 2608.14560), "DSA TopK Indexer": paged
 decode with 64-token pages).  Real DeepSeek-V3.2 activations are not available;
 these Gaussian inputs stand in for them.
 """

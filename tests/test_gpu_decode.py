@@ -11,13 +11,13 @@ from gpu_util import log
 pytestmark = pytest.mark.gpu
 
 
-def _run(case):
+def _run(case, **opts):
     import scoring_exact_top_amd as lib
     t = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a)).cuda()
     ws = lib.alloc_workspace(lib.decode_workspace_bytes(case.B, case.max_pages, case.page_size, case.K),
                              "cuda")
     out = lib.decode_paged(t(case.q8), t(case.q_scale), t(case.k_cache), t(case.k_scale), t(case.w),
-                           t(case.page_table), t(case.seq_lens), case.K, workspace=ws)
+                           t(case.page_table), t(case.seq_lens), case.K, workspace=ws, **opts)
     torch.cuda.synchronize()
     return out.cpu().numpy(), lib.read_stats(ws)
 
@@ -62,3 +62,40 @@ def test_decode_bad_page_id():
     case.page_table[1, 3] = case.k_cache.shape[0] + 7
     out, st = _run(case)
     assert np.all(out[1] == -1) and st["bad_rows"] == 1
+
+
+def test_decode_forced_underflow_repairs():
+    """A threshold above every score leaves no candidates: every scored
+    sequence fails the certificate (underflow) and is repaired exactly."""
+    lens = [1500, 3000, 9000, 20000, 65536]
+    case = synth.decode_case("dec_under", lens, seed=33, max_pages=1024)
+    log("case", case.name, lens)
+    out, st = _run(case, force_tau=float("inf"))
+    log("stats", st)
+    scored = int(np.sum(case.seq_lens > case.K))
+    assert st["underflow"] == scored and st["repaired"] == scored and st["trivial"] == len(lens) - scored
+    _check(case, out)
+
+
+def test_decode_forced_overflow_repairs():
+    """A threshold below every score takes every key: sequences longer than
+    the candidate list capacity (16384) overflow and are repaired; shorter
+    ones are selected on the fast path from all of their keys."""
+    lens = [5000, 16384, 16385, 40000]
+    case = synth.decode_case("dec_over", lens, seed=34, max_pages=700)
+    log("case", case.name, lens)
+    out, st = _run(case, force_tau=float("-inf"))
+    log("stats", st)
+    assert st["overflow"] == 2 and st["repaired"] == 2 and st["fast_ok"] == 2
+    _check(case, out)
+
+
+def test_decode_main_events_time_the_split_kernel():
+    import scoring_exact_top_amd as lib
+    case = synth.decode_case("dec_ev", [3000, 70000 // 2], seed=35, max_pages=600)
+    ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    for e in ev:  # torch creates the HIP event on first record
+        e.record()
+    out, st = _run(case, main_events=ev)
+    assert ev[0].elapsed_time(ev[1]) > 0.0
+    _check(case, out)
