@@ -14,7 +14,8 @@
 // The first sum costs one VALU op per head (an FMA with an |x| source
 // modifier); the linear term u.k goes to the matrix core: u is split into
 // eight e4m3 vectors with FP32 scales, u ~= sum_m sigma_m e4m3(u8_m), residual
-// below 16^-8 |u|_max, and these eight rows form a fifth 16-row A block.
+// below 27^-7 * 16/448 |u|_max, and these eight rows form a fifth 16-row A
+// block.
 //
 // Every 128-deep FP8 contraction is one v_mfma_f32_16x16x128_f8f6f4 per 16
 // rows x 16 keys.  A (rows x 128) lives in registers for the whole key loop;
@@ -95,29 +96,21 @@ __device__ __forceinline__ v8i cat8(v4i x, v4i y) {
   return r;
 }
 
-// OCP e4m3fn decode from the bit fields (S.EEEE.MMM, bias 7, subnormal
-// m * 2^-9).  Codes are never NaN here.
-__device__ __forceinline__ float e4m3_dec(uint32_t c) {
-  // exponent and mantissa bits moved under an FP32 exponent rebiased by
-  // 127 - 7 give 2^(e-7) * (1 + m/8); for e = 0 the same bits read
-  // 2^-7 * (1 + m/8), and twice the excess over 2^-7 is the subnormal m/512.
-  // Both forms are computed and one selected, so the decode has no branch.
-  const float nrm = __uint_as_float(((c & 0x7Fu) << 20) + (120u << 23));
-  const float sub = (nrm - 0.0078125f) * 2.0f;
-  const float mag = (c & 0x78u) ? nrm : sub;
-  return __uint_as_float(__float_as_uint(mag) | ((c & 0x80u) << 24));
+// OCP e4m3fn conversions on gfx950's own FP8 converters (OCP formats on
+// this architecture; checked against a bit-field codec over every non-NaN
+// code, all rounding midpoints and the subnormal range).
+// Bytes 2H and 2H+1 of w as floats:
+template <bool H>
+__device__ __forceinline__ float2 e4m3x2_dec(uint32_t w) {
+  const auto f = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, H);
+  return make_float2(f[0], f[1]);
 }
-
-// Nearest e4m3fn code (ties to even) of v, |v| clamped to 448.
-__device__ __forceinline__ uint32_t e4m3_enc(float v) {
-  const uint32_t s = v < 0.f ? 0x80u : 0u;
-  const float a = fminf(fabsf(v), 448.f);
-  if (a < 0.015625f) return s | (uint32_t)rintf(a * 512.f);   // 8 -> 0x08, the smallest normal
-  int e = (int)((__float_as_uint(a) >> 23) & 255u) - 127;       // -6 .. 8
-  const float mant = __uint_as_float((__float_as_uint(a) & 0x007fffffu) | 0x3f800000u);  // [1,2)
-  uint32_t m3 = (uint32_t)rintf((mant - 1.f) * 8.f);
-  if (m3 == 8u) { m3 = 0u; ++e; }
-  return s | ((uint32_t)(e + 7) << 3) | m3;
+// Nearest codes (ties to even) of a and b in bytes 0 and 1; the inputs are
+// clamped to [-448, 448] because the converter does not saturate.
+__device__ __forceinline__ uint32_t e4m3x2_enc(float a, float b) {
+  a = __builtin_amdgcn_fmed3f(a, -448.f, 448.f);
+  b = __builtin_amdgcn_fmed3f(b, -448.f, 448.f);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xFFFFu;
 }
 
 // One query row as held by a lane: A operands of the four 16-head blocks and
@@ -157,8 +150,12 @@ __device__ __forceinline__ const float* row_qscale(const float* q_scale, int64_t
 // eight 16-byte loads in flight together; the eight lanes that share a dim
 // slice then add their partials with shuffles (tree xor 8, 16, 32).  The
 // sum u goes through `codes` (512 bytes of FP32) to lanes d and d+64.
-// Term m takes sigma_m = max|r_m| / 448 and the nearest e4m3 codes of
-// r_m / sigma_m, then r_{m+1} = r_m - sigma_m * dec(code).
+// Term m takes the nearest e4m3 codes of r_m / sigma_m, then
+// r_{m+1} = r_m - sigma_m * dec(code), with sigma_0 = max|u| / 448 and
+// sigma_{m+1} = sigma_m / 27.  That ratio needs no further max-reduction:
+// a code within [-448, 448] is within 16 units of its value (half the
+// largest e4m3 spacing, 32), so |r_{m+1}| <= 16 sigma_m = (16*27/448)
+// sigma_{m+1} <= 448 sigma_{m+1}, and the next quotient needs no clamp.
 __device__ __forceinline__ void split_u(const uint8_t* q, const float* q_scale, const float* w, int64_t t,
                                         uint32_t lane, uint8_t* codes, float (&sig)[kUTerms]) {
   const uint8_t* base = q + t * (kH * kD) + 16 * (lane & 7u);
@@ -177,7 +174,13 @@ __device__ __forceinline__ void split_u(const uint8_t* q, const float* q_scale, 
   for (int i = 0; i < 8; ++i) {
     const uint32_t wd[4] = {x[i].x, x[i].y, x[i].z, x[i].w};
 #pragma unroll
-    for (int d = 0; d < 16; ++d) acc[d] = fmaf(wj[i], e4m3_dec((wd[d >> 2] >> (8 * (d & 3))) & 255u), acc[d]);
+    for (int k = 0; k < 4; ++k) {
+      const float2 lo = e4m3x2_dec<false>(wd[k]), hi = e4m3x2_dec<true>(wd[k]);
+      acc[4 * k] = fmaf(wj[i], lo.x, acc[4 * k]);
+      acc[4 * k + 1] = fmaf(wj[i], lo.y, acc[4 * k + 1]);
+      acc[4 * k + 2] = fmaf(wj[i], hi.x, acc[4 * k + 2]);
+      acc[4 * k + 3] = fmaf(wj[i], hi.y, acc[4 * k + 3]);
+    }
   }
 #pragma unroll
   for (int d = 0; d < 16; ++d) {
@@ -194,19 +197,21 @@ __device__ __forceinline__ void split_u(const uint8_t* q, const float* q_scale, 
   wave_sync();
   float u0 = uf[lane], u1 = uf[64 + lane];
   wave_sync();
+  float amax = fmaxf(fabsf(u0), fabsf(u1));
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
+  float s = amax / 448.f;
 #pragma unroll
   for (int m = 0; m < kUTerms; ++m) {
-    float amax = fmaxf(fabsf(u0), fabsf(u1));
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
-    const float s = amax / 448.f;
-    const uint32_t c0 = s > 0.f ? e4m3_enc(u0 / s) : 0u;
-    const uint32_t c1 = s > 0.f ? e4m3_enc(u1 / s) : 0u;
-    codes[m * kD + lane] = (uint8_t)c0;
-    codes[m * kD + 64 + lane] = (uint8_t)c1;
-    u0 = fmaf(-s, e4m3_dec(c0), u0);
-    u1 = fmaf(-s, e4m3_dec(c1), u1);
+    const float inv = 1.0f / s;
+    const uint32_t c = s > 0.f ? e4m3x2_enc(u0 * inv, u1 * inv) : 0u;
+    codes[m * kD + lane] = (uint8_t)c;
+    codes[m * kD + 64 + lane] = (uint8_t)(c >> 8);
+    const float2 d = e4m3x2_dec<false>(c);
+    u0 = fmaf(-s, d.x, u0);
+    u1 = fmaf(-s, d.y, u1);
     sig[m] = s;
+    s *= (1.0f / 27.0f);
   }
 }
 
@@ -279,6 +284,38 @@ __device__ __forceinline__ void prepare_q(QOp& o, const uint8_t* q, const float*
     o.sh[r] = 0.5f * sr;
   }
   wave_sync();
+}
+
+// A prepared query row in device memory: kQOpWords dwords per lane, stored
+// field-major ([word][lane]) so that a wave's stores and loads are coalesced.
+constexpr int kQOpWords = 4 * 8 + 8 + 16 + 4;
+
+__device__ __forceinline__ void store_qop(const QOp& o, uint32_t* dst, uint32_t lane) {
+  int f = 0;
+#pragma unroll
+  for (int b = 0; b < 4; ++b)
+#pragma unroll
+    for (int k = 0; k < 8; ++k) dst[(f++) * 64 + lane] = (uint32_t)o.a[b][k];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) dst[(f++) * 64 + lane] = (uint32_t)o.au[k];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) dst[(f++) * 64 + lane] = __float_as_uint(o.wh[i]);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) dst[(f++) * 64 + lane] = __float_as_uint(o.sh[r]);
+}
+
+__device__ __forceinline__ void load_qop(QOp& o, const uint32_t* src, uint32_t lane) {
+  int f = 0;
+#pragma unroll
+  for (int b = 0; b < 4; ++b)
+#pragma unroll
+    for (int k = 0; k < 8; ++k) o.a[b][k] = (int)src[(f++) * 64 + lane];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) o.au[k] = (int)src[(f++) * 64 + lane];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) o.wh[i] = __uint_as_float(src[(f++) * 64 + lane]);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) o.sh[r] = __uint_as_float(src[(f++) * 64 + lane]);
 }
 
 // Keys of one 64-key tile as B operands plus the scale of this lane's key.
@@ -435,6 +472,7 @@ struct SelShared {
   uint32_t hist[256];
   uint32_t bucket, above, inbucket, pad0;
   uint32_t gt_count, eq_count, pad1, pad2;
+  uint32_t wsum[2][kWaves];  // per-wave totals of block_exclusive_scan2
 };
 
 // Result of the digit passes: every key with (key & mask) > prefix is in the
@@ -534,15 +572,50 @@ __device__ void emit_selection(const Src& src, int n, const SelResult& sel, int 
 
 // ------------------------------------------ register-resident selection
 
-// Radix select over keys held in registers: thread (wave w, lane l) holds
-// key[j] = element j*64 + l of wave w's list, valid for j*64 + l < nw (the
-// wave's own count).  Same passes and result as radix_select over the union
-// of the four waves' lists; no memory traffic besides the LDS histogram.
+// Where a thread's register keys come from: key[j] is list element
+// base + j*step, valid when that is below n.  jmax is wave-uniform: no lane
+// of the wave holds a valid key[j] for j >= jmax.
+struct RegLayout {
+  uint32_t base, step, n, jmax;
+  __device__ uint32_t at(int j) const { return base + (uint32_t)j * step; }
+  __device__ bool valid(int j) const { return at(j) < n; }
+};
+
+// Each wave holds its own list of nw elements, element j*64 + lane in key[j].
+__device__ __forceinline__ RegLayout wave_list_layout(uint32_t nw, uint32_t lane) {
+  return RegLayout{lane, 64u, nw, (nw + 63u) >> 6};
+}
+
+// The workgroup holds one list of n elements, element j*256 + tid in key[j].
+__device__ __forceinline__ RegLayout block_list_layout(uint32_t n, uint32_t tid) {
+  return RegLayout{tid, (uint32_t)kWG, n, (n + kWG - 1u) / kWG};
+}
+
+// Loads of one list into registers, key[j] and id[j] = element lay.at(j):
+// buffer loads whose out-of-range reads return 0, so all of them are issued
+// back to back without a branch per element; invalid slots get key 0.
+template <int M, class Dec>
+__device__ __forceinline__ void load_list_regs(uint32_t (&key)[M], int32_t (&id)[M], const uint32_t* keys,
+                                               const int32_t* ids, uint32_t n, const RegLayout& lay,
+                                               const Dec& dec) {
+  const rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)keys, (short)0, (int)(n * 4u), 0x00020000);
+  const rsrc_t ri = __builtin_amdgcn_make_buffer_rsrc((void*)ids, (short)0, (int)(n * 4u), 0x00020000);
+  uint32_t raw[M];
+#pragma unroll
+  for (int j = 0; j < M; ++j) {
+    raw[j] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rk, (int)(lay.at(j) * 4u), 0, 0);
+    id[j] = __builtin_amdgcn_raw_buffer_load_b32(ri, (int)(lay.at(j) * 4u), 0, 0);
+  }
+#pragma unroll
+  for (int j = 0; j < M; ++j) key[j] = lay.valid(j) ? dec(raw[j]) : 0u;
+}
+
+// Radix select over keys held in registers (layout `lay`).  Same passes and
+// result as radix_select over the whole list; no memory traffic besides the
+// LDS histogram.  All threads of the workgroup call this.
 template <int M>
-__device__ SelResult radix_select_regs(const uint32_t (&key)[M], uint32_t nw, int rem, SelShared& sh,
-                                       int tid, bool allow_early) {
-  const uint32_t lane = tid & 63;
-  const uint32_t jmax = (nw + 63) >> 6;  // wave-uniform
+__device__ SelResult radix_select_regs(const uint32_t (&key)[M], const RegLayout& lay, int rem,
+                                       SelShared& sh, int tid, bool allow_early) {
   uint32_t prefix = 0, mask = 0;
 #pragma unroll 1
   for (int shift = 24; shift >= 0; shift -= 8) {
@@ -550,10 +623,8 @@ __device__ SelResult radix_select_regs(const uint32_t (&key)[M], uint32_t nw, in
     __syncthreads();
 #pragma unroll
     for (int j = 0; j < M; ++j) {
-      if ((uint32_t)j < jmax) {  // wave-uniform guard; keeps key[] in registers
-        const bool v = (uint32_t)j * 64u + lane < nw;
-        hist_add(sh.hist, (key[j] >> shift) & 255u, v && ((key[j] & mask) == prefix));
-      }
+      if ((uint32_t)j < lay.jmax)  // wave-uniform guard; keeps key[] in registers
+        hist_add(sh.hist, (key[j] >> shift) & 255u, lay.valid(j) && ((key[j] & mask) == prefix));
     }
     __syncthreads();
     find_bucket(sh, rem, tid);
@@ -568,28 +639,63 @@ __device__ SelResult radix_select_regs(const uint32_t (&key)[M], uint32_t nw, in
   return SelResult{prefix, mask, rem};
 }
 
-// Emit for radix_select_regs: ids[j*64 + lane] is the id of key[j].
+// Exclusive prefix sums over the workgroup of two per-thread counts, in
+// thread order; also returns the totals.  All threads call this.
+__device__ __forceinline__ void block_exclusive_scan2(uint32_t a, uint32_t b, SelShared& sh, int tid,
+                                                      uint32_t& a_ex, uint32_t& b_ex, uint32_t& a_tot,
+                                                      uint32_t& b_tot) {
+  const uint32_t lane = tid & 63;
+  const int wave = tid >> 6;
+  uint32_t ia = a, ib = b;  // inclusive scans within the wave
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t xa = __shfl_up(ia, off, 64), xb = __shfl_up(ib, off, 64);
+    if (lane >= (uint32_t)off) { ia += xa; ib += xb; }
+  }
+  if (lane == 63) { sh.wsum[0][wave] = ia; sh.wsum[1][wave] = ib; }
+  __syncthreads();
+  uint32_t pa = 0, pb = 0;
+  a_tot = 0;
+  b_tot = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    const uint32_t wa = sh.wsum[0][w], wb = sh.wsum[1][w];
+    if (w < wave) { pa += wa; pb += wb; }
+    a_tot += wa;
+    b_tot += wb;
+  }
+  a_ex = pa + ia - a;
+  b_ex = pb + ib - b;
+  __syncthreads();
+}
+
+// Emit for radix_select_regs: id[j] is the id of key[j] (loaded together with
+// the keys).  Output positions come from prefix sums of per-thread winner
+// counts, so the order is deterministic (thread order, then j) and no
+// atomics are needed: keys above the boundary prefix fill out[0, kr - rem),
+// the first `rem` keys equal to it fill out[kr - rem, kr), -1 up to K.
 template <int M>
-__device__ void emit_selection_regs(const uint32_t (&key)[M], uint32_t nw, const int32_t* ids,
+__device__ void emit_selection_regs(const uint32_t (&key)[M], const int32_t (&id)[M], const RegLayout& lay,
                                     const SelResult& sel, int kr, int K, int32_t* out, SelShared& sh,
                                     int tid) {
-  const uint32_t lane = tid & 63;
-  const uint32_t jmax = (nw + 63) >> 6;
-  if (tid == 0) { sh.gt_count = 0; sh.eq_count = 0; }
-  __syncthreads();
-  const int eq_base = kr - sel.rem;
+  uint32_t gmask = 0u, emask = 0u;
 #pragma unroll
   for (int j = 0; j < M; ++j) {
-    if ((uint32_t)j >= jmax) continue;  // wave-uniform
-    const uint32_t i = (uint32_t)j * 64u + lane;
-    const bool v = i < nw;
+    const bool v = lay.valid(j);
     const uint32_t mk = key[j] & sel.mask;
-    const bool gt = v && mk > sel.prefix;
-    const bool eq = v && mk == sel.prefix;
-    const uint32_t pg = reserve(&sh.gt_count, gt);
-    if (gt) out[pg] = ids[i];
-    const uint32_t pe = reserve(&sh.eq_count, eq);
-    if (eq && (int)pe < sel.rem) out[eq_base + pe] = ids[i];
+    gmask |= (uint32_t)(v && mk > sel.prefix) << j;
+    emask |= (uint32_t)(v && mk == sel.prefix) << j;
+  }
+  uint32_t gpos, epos, gtot, etot;
+  block_exclusive_scan2((uint32_t)__popc(gmask), (uint32_t)__popc(emask), sh, tid, gpos, epos, gtot, etot);
+  const uint32_t eq_base = (uint32_t)(kr - sel.rem);
+#pragma unroll
+  for (int j = 0; j < M; ++j) {
+    if (gmask >> j & 1u) out[gpos++] = id[j];
+    if (emask >> j & 1u) {
+      if (epos < (uint32_t)sel.rem) out[eq_base + epos] = id[j];
+      ++epos;
+    }
   }
   for (int i = kr + tid; i < K; i += kWG) out[i] = -1;
 }

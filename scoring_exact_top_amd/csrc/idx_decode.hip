@@ -1,17 +1,21 @@
 // Paged decode path (contest report page (arXiv 2608.14560), "DSA TopK Indexer"): one FP8 query
 // per sequence against its keys in a paged FP8 cache with per-token scales.
 //
-//   k_decode_prep   one workgroup per sequence: validate the sequence's page
+//   k_decode_prep   one sequence per wave: validate the sequence's page
 //                   ids; sequences with seq_len <= K take the remap path
 //                   (every slot is selected, no scoring); longer ones get a
 //                   sampled threshold.
 //   k_decode_split  G workgroups per sequence split its keys (KV-dimension
-//                   parallelism, Fusing Indexer Scoring and Exact Top-k page, "10. The
-//                   optimization target after fusion"); each scores its
-//                   chunk and appends keys >= tau to the sequence's candidate
-//                   list in the workspace.  The last workgroup to finish
-//                   (atomic ticket) checks the certificate, selects and
-//                   emits.  No host synchronisation anywhere.
+//                   parallelism, Fusing Indexer Scoring and Exact Top-k
+//                   page, "10. The optimization target after fusion"); each
+//                   scores its chunk and appends keys >= tau to the
+//                   sequence's candidate list in the workspace.
+//   k_decode_select one workgroup per sequence: certificate, register-
+//                   resident radix select, emit.  A kernel boundary rather
+//                   than an in-kernel last-arriver handoff: on this chip the
+//                   device-scope fence such a handoff needs writes back and
+//                   invalidates the L2 of the XCD, once per workgroup.
+//                   No host synchronisation anywhere.
 //   k_decode_repair exact repair of sequences the certificate rejected.
 #include <string.h>
 
@@ -20,7 +24,8 @@
 
 namespace idxk {
 
-constexpr int kDecCap = 16384;  // candidate list capacity per sequence
+constexpr int kDecCap = 8192;    // candidate list capacity per sequence
+constexpr int kDecStage = 512;   // per-wave LDS stage of the split kernel
 
 struct DecodeArgs {
   const uint8_t* q;
@@ -36,132 +41,204 @@ struct DecodeArgs {
   float* tau;            // [B]
   int32_t* status;       // [B]: 0 score, 1 remapped, 2 invalid
   uint32_t* cnt;         // [B]
-  uint32_t* ticket;      // [B]
   int32_t* fail_list;    // [B]
-  uint32_t* cand_key;    // [B][kDecCap]
-  int32_t* cand_idx;     // [B][kDecCap]
+  uint32_t* cand_key;    // [B][kDecCap] candidate scores (FP32 bits)
+  int32_t* cand_idx;     // [B][kDecCap] candidate physical slots
   uint32_t* scratch;     // [repair_grid(B)][max_pages*64]
+  uint32_t* qop;         // [B][kQOpWords][64] prepared query operands
   int32_t force_tau;     // debug: every scored sequence uses tau_value
   float tau_value;
 };
 
-struct SrcGlobal {
-  const uint32_t* k;
-  const int32_t* ids;
-  __device__ uint32_t key(int i) const { return k[i]; }
-  __device__ int32_t id(int i) const { return ids[i]; }
-};
-
+// One sequence per wave: validate its page ids, remap when L <= K, else
+// draw its sampled threshold (the prefill sampler's lattice and estimator).
 __global__ __launch_bounds__(kWG) void k_decode_prep(DecodeArgs A) {
-  __shared__ uint32_t s_samp[kMaxSamples];
-  __shared__ SelShared sh;
+  __shared__ uint32_t s_samp[kWaves][kMaxSamples];
+  __shared__ uint32_t s_hist[kWaves][256];
   __shared__ uint8_t s_qprep[kWaves][kUTerms * kD];
-  __shared__ int s_bad;
   const int tid = threadIdx.x;
   const uint32_t lane = tid & 63;
-  const int b = blockIdx.x;
-  if (b == 0 && tid < kCtrlWords) A.ctrl[tid] = 0u;
-  if (tid == 0) {
-    A.cnt[b] = 0u;
-    A.ticket[b] = 0u;
-    s_bad = 0;
-  }
-  __syncthreads();
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  if (blockIdx.x == 0 && tid < kCtrlWords) A.ctrl[tid] = 0u;
+  const int b = kWaves * blockIdx.x + wave;
+  if (b >= A.B) return;
+  if (lane == 0) A.cnt[b] = 0u;
   const int L = A.seq_lens[b];
   const int32_t* pt = A.table + (int64_t)b * A.max_pages;
   int32_t* out = A.out + (int64_t)b * A.K;
-  if (L < 0 || L > A.max_pages * 64) {
-    s_bad = 1;
-  } else {
-    for (int p = tid; p < ((L + 63) >> 6); p += kWG) {
+  bool bad = L < 0 || L > A.max_pages * 64;
+  if (!bad) {
+    for (int p = (int)lane; p < ((L + 63) >> 6); p += 64) {
       const int pg = pt[p];
-      if (pg < 0 || pg >= A.num_pages) s_bad = 1;
+      bad |= pg < 0 || pg >= A.num_pages;
     }
   }
-  __syncthreads();
-  if (s_bad) {
-    for (int i = tid; i < A.K; i += kWG) out[i] = -1;
-    if (tid == 0) A.status[b] = 2;
+  if (__ballot(bad)) {
+    for (int i = (int)lane; i < A.K; i += 64) out[i] = -1;
+    if (lane == 0) A.status[b] = 2;
     return;
   }
   if (L <= A.K) {
     // every position is in the top-K: remap to physical slots
-    for (int i = tid; i < A.K; i += kWG) out[i] = i < L ? pt[i >> 6] * 64 + (i & 63) : -1;
-    if (tid == 0) A.status[b] = 1;
+    for (int i = (int)lane; i < A.K; i += 64) out[i] = i < L ? pt[i >> 6] * 64 + (i & 63) : -1;
+    if (lane == 0) A.status[b] = 1;
     return;
   }
+  // the query operands, prepared once here for every workgroup of the split
+  QOp qo;
+  prepare_q(qo, A.q, A.q_scale, A.w, b, lane, s_qprep[wave]);
+  store_qop(qo, A.qop + (int64_t)b * kQOpWords * 64, lane);
   const SampleGeom sg = sample_geom(L, kDecCap);
   float tau = A.force_tau ? A.tau_value : -INFINITY;
   if (!A.force_tau && sg.n > 0) {
-    QOp qo;
-    prepare_q(qo, A.q, A.q_scale, A.w, b, lane, s_qprep[tid >> 6]);
-    tau = sample_tau(qo, make_keybuf(A.k, A.k_scale, (int64_t)A.num_pages * 64), TilePaged{pt}, 0, sg,
-                     s_samp, sh, tid);
+    const KeyBuf kbuf = make_keybuf(A.k, A.k_scale, (int64_t)A.num_pages * 64);
+    const TilePaged tm{pt};
+    const auto key_of = [&](int i) { return key_index(tm, kSampleOffset + sg.stride * min(i, sg.n - 1)); };
+    KeyTile cur;
+    load_tile_gather(cur, kbuf, [&](int i) { return key_of(i); }, lane);
+#pragma unroll 1
+    for (int i0 = 0; i0 < sg.n; i0 += kTile) {
+      KeyTile nxt;
+      load_tile_gather(nxt, kbuf, [&](int i) { return key_of(i0 + kTile + i); }, lane);
+      const float sc = tile_score(qo, cur);
+      if (i0 + (int)lane < sg.n) s_samp[wave][i0 + lane] = f2key(sc);
+      cur = nxt;
+    }
+    wave_sync();
+    const SelResult sel = wave_radix_select(SrcLds{s_samp[wave]}, sg.n, sg.r, s_hist[wave], lane, false);
+    tau = key2f(sel.prefix);
   }
-  if (tid == 0) {
+  if (lane == 0) {
     A.tau[b] = tau;
     A.status[b] = 0;
   }
 }
 
+// Workgroup (g, b) scores chunk g of sequence b; wave w takes the chunk's
+// tiles w, w+4, ...  Its page ids are loaded once (lane i holds the page of
+// its i-th tile, 64 tiles per reload) and key tiles are loaded two ahead.
+// Keys >= tau go to the wave's LDS stage (slots from ballot + popcount); a
+// stage that fills up mid-walk reserves a range of the sequence's
+// candidate list with one device atomic and is copied there; at the end
+// the workgroup reserves one range for all four stages.
 __global__ __launch_bounds__(kWG) void k_decode_split(DecodeArgs A) {
-  __shared__ SelShared sh;
-  __shared__ uint8_t s_qprep[kWaves][kUTerms * kD];
-  __shared__ uint32_t s_last;
+  __shared__ uint2 s_stage[kWaves][kDecStage];
+  __shared__ uint32_t s_cnt[kWaves], s_base[kWaves];
   const int tid = threadIdx.x;
   const uint32_t lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = blockIdx.x, b = blockIdx.y;
-  uint32_t* stats = A.ctrl + kStatsOff;
-  const int st = A.status[b];
-  if (st != 0) {
-    if (g == 0 && tid == 0) {
-      atomicAdd(&stats[kStRows], 1u);
-      atomicAdd(&stats[st == 1 ? kStTrivial : kStBad], 1u);
-    }
-    return;
-  }
+  if (A.status[b] != 0) return;
   const int L = A.seq_lens[b];
   const int32_t* pt = A.table + (int64_t)b * A.max_pages;
   const int chunk = (((L + A.G - 1) / A.G) + 63) & ~63;
   const int k0 = g * chunk, k1 = min(L, k0 + chunk);
+  if (k0 >= k1) return;
   const float tau = A.tau[b];
-  uint32_t* cnt = A.cnt + b;
   uint32_t* ckey = A.cand_key + (int64_t)b * kDecCap;
   int32_t* cidx = A.cand_idx + (int64_t)b * kDecCap;
-  if (k0 < k1) {
-    QOp qo;
-    prepare_q(qo, A.q, A.q_scale, A.w, b, lane, s_qprep[wave]);
-    const KeyBuf kbuf = make_keybuf(A.k, A.k_scale, (int64_t)A.num_pages * 64);
-    const TilePaged tm{pt};
-    for (int tile = (k0 >> 6) + wave; tile < ((k1 + 63) >> 6); tile += kWaves) {
-      KeyTile kt;
-      const int base = tm(tile);
-      load_tile(kt, kbuf, base, lane);
-      const float sc = tile_score(qo, kt);
-      const int my = (tile << 6) + (int)lane;
-      const bool take = my < k1 && sc >= tau;
-      const uint32_t pos = reserve(cnt, take);
-      if (take && pos < (uint32_t)kDecCap) {
-        ckey[pos] = f2key(sc);
-        cidx[pos] = base + (int)lane;
+  uint32_t staged = 0u;
+  // copy this wave's stage to [base, base + staged) of the list
+  const auto copy_out = [&](uint32_t base) {
+    for (uint32_t i = lane; i < staged; i += 64) {
+      if (base + i < (uint32_t)kDecCap) {
+        const uint2 e = s_stage[wave][i];
+        ckey[base + i] = e.x;
+        cidx[base + i] = (int32_t)e.y;
       }
     }
+  };
+  const KeyBuf kbuf = make_keybuf(A.k, A.k_scale, (int64_t)A.num_pages * 64);
+  const int tile0 = (k0 >> 6) + wave;
+  const int nt = tile0 < ((k1 + 63) >> 6) ? (((k1 + 63) >> 6) - tile0 + kWaves - 1) / kWaves : 0;
+  if (nt > 0) {
+    // page of the wave's i-th tile (clamped to its last tile past the end)
+    int pg_lane = 0, pg_group = -1;
+    const auto page_of = [&](int i) {
+      i = min(i, nt - 1);
+      if ((i >> 6) != pg_group) {
+        pg_group = i >> 6;
+        const int ti = (pg_group << 6) + (int)lane;
+        pg_lane = pt[tile0 + kWaves * min(ti, nt - 1)];
+      }
+      return __builtin_amdgcn_readlane(pg_lane, i & 63);
+    };
+    int base0 = page_of(0) << 6, base1 = page_of(1) << 6;
+    KeyTile t0, t1;
+    load_tile(t0, kbuf, base0, lane);
+    load_tile(t1, kbuf, base1, lane);
+    QOp qo;
+    load_qop(qo, A.qop + (int64_t)b * kQOpWords * 64, lane);
+#pragma unroll 1
+    for (int i = 0; i < nt; ++i) {
+      const int base2 = page_of(i + 2) << 6;
+      KeyTile t2;
+      load_tile(t2, kbuf, base2, lane);
+      const float sc = tile_score(qo, t0);
+      const int my = ((tile0 + kWaves * i) << 6) + (int)lane;
+      const bool take = my < k1 && sc >= tau;
+      const uint64_t ball = __ballot(take);
+      if (ball) {
+        const uint32_t n = (uint32_t)__popcll(ball);
+        if (staged + n > (uint32_t)kDecStage) {
+          wave_sync();
+          uint32_t base = 0u;
+          if (lane == 0) base = atomicAdd(&A.cnt[b], staged);
+          copy_out((uint32_t)__builtin_amdgcn_readfirstlane((int)base));
+          staged = 0u;
+          wave_sync();
+        }
+        if (take) s_stage[wave][staged + rank_in(ball)] = make_uint2(__float_as_uint(sc), (uint32_t)(base0 + lane));
+        staged += n;
+      }
+      t0 = t1;
+      t1 = t2;
+      base0 = base1;
+      base1 = base2;
+    }
   }
-  __threadfence();
+  if (lane == 0) s_cnt[wave] = staged;
   __syncthreads();
-  if (tid == 0) s_last = (atomicAdd(&A.ticket[b], 1u) == (uint32_t)(A.G - 1)) ? 1u : 0u;
+  if (tid == 0) {
+    const uint32_t total = s_cnt[0] + s_cnt[1] + s_cnt[2] + s_cnt[3];
+    uint32_t base = total ? atomicAdd(&A.cnt[b], total) : 0u;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      s_base[w] = base;
+      base += s_cnt[w];
+    }
+  }
   __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-  const uint32_t n = __atomic_load_n(cnt, __ATOMIC_RELAXED);
-  const int kr = A.K;  // L > K on this path
+  copy_out(s_base[wave]);
+}
+
+// One workgroup per sequence, after every chunk is in: certify the candidate
+// list, load it into registers (32 keys per thread), select and emit, or put
+// the sequence on the failure list.  Also counts the remapped and invalid
+// sequences.
+__global__ __launch_bounds__(kWG) void k_decode_select(DecodeArgs A) {
+  __shared__ SelShared sh;
+  const int tid = threadIdx.x;
+  const int b = blockIdx.x;
+  uint32_t* stats = A.ctrl + kStatsOff;
+  const int st = A.status[b];
   if (tid == 0) atomicAdd(&stats[kStRows], 1u);
+  if (st != 0) {
+    if (tid == 0) atomicAdd(&stats[st == 1 ? kStTrivial : kStBad], 1u);
+    return;
+  }
+  const uint32_t n = A.cnt[b];
+  const int kr = A.K;  // L > K on this path
   if (n >= (uint32_t)kr && n <= (uint32_t)kDecCap) {
-    const SrcGlobal src{ckey, cidx};
-    const SelResult sel = (n > (uint32_t)kr) ? radix_select(src, (int)n, kr, sh, tid, false, true)
+    const uint32_t* ckey = A.cand_key + (int64_t)b * kDecCap;
+    const int32_t* cidx = A.cand_idx + (int64_t)b * kDecCap;
+    const RegLayout lay = block_list_layout(n, (uint32_t)tid);
+    uint32_t key[kDecCap / kWG];
+    int32_t id[kDecCap / kWG];
+    load_list_regs(key, id, ckey, cidx, n, lay, [](uint32_t x) { return f2key(__uint_as_float(x)); });
+    const SelResult sel = (n > (uint32_t)kr) ? radix_select_regs(key, lay, kr, sh, tid, true)
                                             : SelResult{0u, 0u, kr};
-    emit_selection(src, (int)n, sel, kr, A.K, A.out + (int64_t)b * A.K, sh, tid);
+    emit_selection_regs(key, id, lay, sel, kr, A.K, A.out + (int64_t)b * A.K, sh, tid);
     if (tid == 0) atomicAdd(&stats[kStFast], 1u);
   } else if (tid == 0) {
     const uint32_t f = atomicAdd(&A.ctrl[kCtrlFail], 1u);
@@ -197,7 +274,7 @@ __global__ __launch_bounds__(kWG) void k_decode_repair(DecodeArgs A) {
 static inline size_t a256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct DecodeLayout {
-  size_t ctrl, tau, status, cnt, ticket, fail, ckey, cidx, scratch, total;
+  size_t ctrl, tau, status, cnt, fail, ckey, cidx, scratch, qop, total;
 };
 
 static DecodeLayout decode_layout(int32_t B, int32_t max_pages) {
@@ -208,11 +285,11 @@ static DecodeLayout decode_layout(int32_t B, int32_t max_pages) {
   L.tau = o; o = a256(o + 4 * b);
   L.status = o; o = a256(o + 4 * b);
   L.cnt = o; o = a256(o + 4 * b);
-  L.ticket = o; o = a256(o + 4 * b);
   L.fail = o; o = a256(o + 4 * b);
   L.ckey = o; o = a256(o + 4 * b * kDecCap);
   L.cidx = o; o = a256(o + 4 * b * kDecCap);
   L.scratch = o; o = a256(o + 4 * (size_t)repair_grid(B) * (size_t)max_pages * 64);
+  L.qop = o; o = a256(o + 4 * b * kQOpWords * 64);
   L.total = o;
   return L;
 }
@@ -258,11 +335,11 @@ int decode_paged(const uint8_t* q, const float* q_scale, const uint8_t* k_cache,
   A.tau = reinterpret_cast<float*>(ws + L.tau);
   A.status = reinterpret_cast<int32_t*>(ws + L.status);
   A.cnt = reinterpret_cast<uint32_t*>(ws + L.cnt);
-  A.ticket = reinterpret_cast<uint32_t*>(ws + L.ticket);
   A.fail_list = reinterpret_cast<int32_t*>(ws + L.fail);
   A.cand_key = reinterpret_cast<uint32_t*>(ws + L.ckey);
   A.cand_idx = reinterpret_cast<int32_t*>(ws + L.cidx);
   A.scratch = reinterpret_cast<uint32_t*>(ws + L.scratch);
+  A.qop = reinterpret_cast<uint32_t*>(ws + L.qop);
   hipEvent_t ev0 = nullptr, ev1 = nullptr;
   if (opts) {
     A.force_tau = opts->force_tau ? 1 : 0;
@@ -270,10 +347,11 @@ int decode_paged(const uint8_t* q, const float* q_scale, const uint8_t* k_cache,
     ev0 = static_cast<hipEvent_t>(opts->ev_main_start);
     ev1 = static_cast<hipEvent_t>(opts->ev_main_stop);
   }
-  hipLaunchKernelGGL(k_decode_prep, dim3(B), dim3(kWG), 0, stream, A);
+  hipLaunchKernelGGL(k_decode_prep, dim3((B + kWaves - 1) / kWaves), dim3(kWG), 0, stream, A);
   if (ev0 && hipEventRecord(ev0, stream) != hipSuccess) return IDX_EHIP;
   hipLaunchKernelGGL(k_decode_split, dim3(A.G, B), dim3(kWG), 0, stream, A);
   if (ev1 && hipEventRecord(ev1, stream) != hipSuccess) return IDX_EHIP;
+  hipLaunchKernelGGL(k_decode_select, dim3(B), dim3(kWG), 0, stream, A);
   hipLaunchKernelGGL(k_decode_repair, dim3(repair_grid(B)), dim3(kWG), 0, stream, A);
   return hipGetLastError() == hipSuccess ? IDX_OK : IDX_EHIP;
 }

@@ -272,15 +272,14 @@ __global__ __launch_bounds__(kWG, 2) void k_prefill_pair(PrefillArgs A) {
       const uint32_t nw = s_segn[r][wave];
       const int64_t o = ((int64_t)t * kWaves + wave) * kSegCap;
       const uint32_t* gk = A.cand_key + o;
+      const RegLayout lay = wave_list_layout(nw, lane);
       uint32_t key[kSegCap / 64];
-#pragma unroll
-      for (int j = 0; j < kSegCap / 64; ++j) {
-        const uint32_t i = (uint32_t)j * 64u + lane;
-        key[j] = i < nw ? f2key(__uint_as_float(gk[i])) : 0u;
-      }
-      const SelResult sel = (n > (uint32_t)kr) ? radix_select_regs(key, nw, kr, sh, tid, true)
+      int32_t id[kSegCap / 64];
+      load_list_regs(key, id, gk, A.cand_idx + o, nw, lay,
+                     [](uint32_t x) { return f2key(__uint_as_float(x)); });
+      const SelResult sel = (n > (uint32_t)kr) ? radix_select_regs(key, lay, kr, sh, tid, true)
                                               : SelResult{0u, 0u, kr};
-      emit_selection_regs(key, nw, A.cand_idx + o, sel, kr, A.K, out, sh, tid);
+      emit_selection_regs(key, id, lay, sel, kr, A.K, out, sh, tid);
       if (tid == 0) {
         atomicAdd(&stats[kStFast], 1u);
         if (s_segover[r] & 2u) atomicAdd(&stats[kStSpilled], 1u);

@@ -48,7 +48,7 @@ def test_paged_decode_workload():
 
 
 def test_decode_edges_and_q_scale():
-    lens = [0, 1, 2047, 2048, 2049, 4095, 16384, 16385, 20000]
+    lens = [0, 1, 2047, 2048, 2049, 4095, 8192, 8193, 16384, 16385, 20000]
     case = synth.decode_case("edges", lens, seed=31, max_pages=400, with_q_scale=True)
     log("case", case.name, lens)
     out, st = _run(case)
@@ -79,9 +79,9 @@ def test_decode_forced_underflow_repairs():
 
 def test_decode_forced_overflow_repairs():
     """A threshold below every score takes every key: sequences longer than
-    the candidate list capacity (16384) overflow and are repaired; shorter
+    the candidate list capacity (8192) overflow and are repaired; shorter
     ones are selected on the fast path from all of their keys."""
-    lens = [5000, 16384, 16385, 40000]
+    lens = [5000, 8192, 8193, 40000]
     case = synth.decode_case("dec_over", lens, seed=34, max_pages=700)
     log("case", case.name, lens)
     out, st = _run(case, force_tau=float("-inf"))
