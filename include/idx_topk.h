@@ -77,8 +77,9 @@ typedef struct {
   uint32_t fast_ok;    /* rows certified by the sampled-threshold fast path     */
   uint32_t underflow;  /* fast path failed: fewer than K candidates             */
   uint32_t overflow;   /* fast path failed: candidates exceeded capacity        */
-  uint32_t spilled;    /* fast-path rows whose candidates overflowed on-chip
-                          storage into the workspace spill area                 */
+  uint32_t spilled;    /* fast-path rows with more candidates than the on-chip
+                          share lds_cap (informational: the prefill main kernel
+                          writes candidates straight to the workspace)          */
   uint32_t repaired;   /* rows recomputed by the exact repair path              */
   uint32_t trivial;    /* rows (sequences) with L <= K: no scoring needed       */
   uint32_t bad_rows;   /* rows with an invalid range or page id (output all -1) */

@@ -83,22 +83,20 @@ __global__ __launch_bounds__(kWG) void k_prefill_tau(PrefillArgs A) {
 // ------------------------------------------------------ paired-row main
 
 // Two query rows per workgroup of four waves; two workgroups per CU.  Each
-// wave walks every fourth 64-key tile of the rows' union range and, per
-// 16-key sub-tile, issues the 9 MFMAs of both rows (4 head blocks each plus
-// the shared u block), refills that sub-tile's registers with the same
-// sub-tile of its next tile (a rolling prefetch one tile ahead), and folds
-// the results into the rows' partial sums; the compiler interleaves the next
-// MFMAs with this epilogue.  Keys >= tau are appended, as raw score bits
-// and key id, to a per-(row, wave) LDS stage whose fill level is a scalar
-// count (ballot + popcount, no atomics); a full stage is copied in bulk to
-// the wave's private segment of the row's workspace candidate area.  After
-// the walk the workgroup certifies and selects each row in turn, reading the
-// row's four segments as one list.
+// wave walks every fourth 64-key tile of the rows' union range.  Per 16-key
+// sub-tile it issues the 9 MFMAs of both rows (4 head blocks each plus the
+// shared u block), software-pipelined by row so that each row's epilogue
+// runs under the other row's MFMAs, and refills the sub-tile's registers
+// with the same sub-tile of its next tile (one tile of lead).  Keys >= tau
+// are stored, as raw score bits and key id, straight into the wave's
+// private segment of the row's workspace candidate area; the slot comes
+// from a scalar count plus the lane's rank in the ballot, so no atomics
+// are involved.  After the walk the workgroup certifies and selects each
+// row in turn, every wave holding its own segment in registers.
 template <bool DBG>
 __global__ __launch_bounds__(kWG, 2) void k_prefill_pair(PrefillArgs A) {
-  __shared__ uint2 s_stage[2][kWaves][kSegStage];
   __shared__ uint32_t s_segn[2][kWaves];   // entries in each segment (capped)
-  __shared__ uint32_t s_segover[2];        // bit 0: a segment overflowed; bit 1: a stage was flushed early
+  __shared__ uint32_t s_segover[2];        // some segment of the row overflowed
   __shared__ SelShared sh;
   __shared__ uint8_t s_qprep[kWaves][2 * kUTerms * kD];
   const int tid = threadIdx.x;
@@ -131,76 +129,42 @@ __global__ __launch_bounds__(kWG, 2) void k_prefill_pair(PrefillArgs A) {
   const rsrc_t ktb = __builtin_amdgcn_make_buffer_rsrc((void*)A.kt, (short)0, ntiles * kTile * kD, 0x00020000);
   // per-segment capacities (the debug knobs scale them down)
   const uint32_t seg_cap = (uint32_t)min(kSegCap, A.cap_total / kWaves);
-  const uint32_t stage_cap = (uint32_t)max(64, min(kSegStage, A.lds_cap / kWaves));
   const int tile_hi = (hi + 63) >> 6;
   const int voff = (int)lane * 16;
-  uint32_t cnt[2] = {0u, 0u}, staged[2] = {0u, 0u}, flushed[2] = {0u, 0u};
-  uint32_t* segk[2];
-  int32_t* segi[2];
+  uint32_t cnt[2] = {0u, 0u};  // candidates of each row found by this wave
+  // the (row, wave) workspace segments as buffer resources: a store past
+  // seg_cap is dropped by the bounds check
+  rsrc_t segk[2], segi[2];
 #pragma unroll
   for (int r = 0; r < 2; ++r) {
     const int64_t o = ((int64_t)min(t0 + r, A.Q - 1) * kWaves + wave) * kSegCap;
-    segk[r] = A.cand_key + o;
-    segi[r] = A.cand_idx + o;
+    segk[r] = __builtin_amdgcn_make_buffer_rsrc((void*)(A.cand_key + o), (short)0, (int)(seg_cap * 4u), 0x00020000);
+    segi[r] = __builtin_amdgcn_make_buffer_rsrc((void*)(A.cand_idx + o), (short)0, (int)(seg_cap * 4u), 0x00020000);
   }
-  // Copy row r's LDS stage to its workspace segment (as far as capacity
-  // allows) and empty it; drain the stores so the loop's waits stay exact.
-  auto flush = [&](int r) {
-    wave_sync();
-    for (uint32_t i = lane; i < staged[r]; i += 64) {
-      const uint32_t o = flushed[r] + i;
-      if (o < seg_cap) {
-        const uint2 e = s_stage[r][wave][i];
-        segk[r][o] = e.x;
-        segi[r][o] = (int32_t)e.y;
-      }
-    }
-    flushed[r] = min(flushed[r] + staged[r], seg_cap);
-    staged[r] = 0u;
-    wave_sync();
-    __builtin_amdgcn_s_waitcnt(0x0F70);
-  };
   const v4f z = {0.f, 0.f, 0.f, 0.f};
-  // One tile: 9 MFMAs per 16-key sub-tile on CUR (both rows' head blocks and
-  // the shared u block), then that sub-tile's slice of tile T+4 is loaded
-  // into NXT (the other buffer: a whole tile of lead, no register copies),
-  // then the sub-tile's epilogue.  Reads past the end return 0.
-  auto tile_body = [&](int T, const v8i (&cur)[4], v8i (&nxt)[4], float ks_cur, float& ks_nxt) {
-    const int ntoff = (T + kWaves) * (kTile * kD);
-    float p0[4], p1[4];
+  // Head-weighted sum of one row's 16 heads held by this lane plus its 4
+  // u-block rows, in a fixed order (20 FMAs).
+  const auto epi = [](const float (&wh)[16], const float (&shr)[4], const v4f (&a)[4], const v4f& au) {
+    float x = 0.f;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      v4f a0[4], a1[4];
+    for (int b = 0; b < 4; ++b)
 #pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        a0[b] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qo.a[0][b], cur[c], z, 0, 0, 0, 0, 0, 0);
-        a1[b] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qo.a[1][b], cur[c], z, 0, 0, 0, 0, 0, 0);
-      }
-      const v4f au = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qo.au, cur[c], z, 0, 0, 0, 0, 0, 0);
-      nxt[c] = cat8(__builtin_amdgcn_raw_buffer_load_b128(ktb, voff, ntoff + (2 * c) * 1024, 0),
-                    __builtin_amdgcn_raw_buffer_load_b128(ktb, voff, ntoff + (2 * c + 1) * 1024, 0));
-      __builtin_amdgcn_sched_group_barrier(0x008, 9, 0);
-      __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);
-      float x0 = 0.f, x1 = 0.f;
+      for (int r = 0; r < 4; ++r) x = fmaf(wh[4 * b + r], fabsf(a[b][r]), x);
 #pragma unroll
-      for (int b = 0; b < 4; ++b)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          x0 = fmaf(qo.wh[0][4 * b + r], fabsf(a0[b][r]), x0);
-          x1 = fmaf(qo.wh[1][4 * b + r], fabsf(a1[b][r]), x1);
-        }
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        x0 = fmaf(qo.sh[0][r], au[r], x0);
-        x1 = fmaf(qo.sh[1][r], au[r], x1);
-      }
-      p0[c] = x0;
-      p1[c] = x1;
-      __builtin_amdgcn_sched_group_barrier(0x002, 40, 0);
-    }
-    ks_nxt = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(kbuf.ks, (int)lane * 4, ntoff / kD * 4, 0));
-    const float sc[2] = {reduce_scatter4(p0[0], p0[1], p0[2], p0[3]) * ks_cur,
-                         reduce_scatter4(p1[0], p1[1], p1[2], p1[3]) * ks_cur};
+    for (int r = 0; r < 4; ++r) x = fmaf(shr[r], au[r], x);
+    return x;
+  };
+  // Per-tile state: row B's accumulators of the last sub-tile (its epilogue
+  // runs under the next sub-tile's MFMAs) and the tile's partial sums.
+  v4f aB[4] = {z, z, z, z}, auB = z;
+  float q0[4], q1[4];
+  // Tail of tile T: reduce-scatter, key scale, range and threshold tests,
+  // append.  Branch-free: every lane stores, a taking lane at its slot in
+  // the wave's segment (count + rank in the ballot), the others out of
+  // range, where the buffer bounds check drops the store.
+  const auto tail = [&](int T, float ks) {
+    const float sc[2] = {reduce_scatter4(q0[0], q0[1], q0[2], q0[3]) * ks,
+                         reduce_scatter4(q1[0], q1[1], q1[2], q1[3]) * ks};
     const int my = (T << 6) + (int)lane;
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
@@ -208,46 +172,83 @@ __global__ __launch_bounds__(kWG, 2) void k_prefill_pair(PrefillArgs A) {
       if (DBG && valid) A.dbg_scores[(int64_t)(t0 + r) * A.N + my] = sc[r];
       const bool take = valid && sc[r] >= tr[r];
       const uint64_t ball = __ballot(take);
-      if (ball) {
-        const uint32_t n = (uint32_t)__popcll(ball);
-        if (staged[r] + n > stage_cap) flush(r);
-        if (take) s_stage[r][wave][staged[r] + rank_in(ball)] = make_uint2(__float_as_uint(sc[r]), (uint32_t)my);
-        staged[r] += n;
-        cnt[r] += n;
-      }
+      const uint32_t n = (uint32_t)__popcll(ball);
+      const int off = take ? (int)((cnt[r] + rank_in(ball)) * 4u) : 0x7FFFFFF0;
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sc[r]), segk[r], off, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b32((uint32_t)my, segi[r], off, 0, 0);
+      cnt[r] += n;
     }
+  };
+  // One tile, software-pipelined by row across its sub-tiles.  Per 16-key
+  // sub-tile c: row A's 4 MFMAs and the shared u MFMA, interleaved with row
+  // B's epilogue of sub-tile c-1; then row B's 4 MFMAs, interleaved with row
+  // A's epilogue of sub-tile c.  Row B's epilogue of the last sub-tile and
+  // the tile's tail follow under row B's last MFMAs.  Once both rows' MFMAs
+  // on sub-tile c are issued, its registers are refilled with the same
+  // sub-tile of tile T+4 (a whole tile of lead from a single buffer); reads
+  // past the end return 0.  (Carrying this pipeline across tiles measured
+  // faster in isolation but does not fit the register budget of two
+  // workgroups per CU.)
+  v8i kb[4];
+  float ks_cur = 0.f;
+  auto tile_body = [&](int T) {
+    const int ntoff = (T + kWaves) * (kTile * kD);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      v4f aA[4];
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+        aA[b] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qo.a[0][b], kb[c], z, 0, 0, 0, 0, 0, 0);
+      const v4f au = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qo.au, kb[c], z, 0, 0, 0, 0, 0, 0);
+      if (c > 0) q1[c - 1] = epi(qo.wh[1], qo.sh[1], aB, auB);
+#pragma unroll
+      for (int i = 0; i < 5; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+        aB[b] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qo.a[1][b], kb[c], z, 0, 0, 0, 0, 0, 0);
+      kb[c] = cat8(__builtin_amdgcn_raw_buffer_load_b128(ktb, voff, ntoff + (2 * c) * 1024, 0),
+                   __builtin_amdgcn_raw_buffer_load_b128(ktb, voff, ntoff + (2 * c + 1) * 1024, 0));
+      q0[c] = epi(qo.wh[0], qo.sh[0], aA, au);
+      auB = au;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    q1[3] = epi(qo.wh[1], qo.sh[1], aB, auB);
+    const float ks = ks_cur;
+    ks_cur = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(kbuf.ks, (int)lane * 4, ntoff / kD * 4, 0));
+    tail(T, ks);
   };
   if (lo < hi) {
     int T = (lo >> 6) + wave;
-    v8i kA[4], kB[4];
-    float sA, sB;
     {
       KeyTile t;
       load_tile_relaid(t, ktb, kbuf.ks, T, lane);
 #pragma unroll
-      for (int c = 0; c < 4; ++c) kA[c] = t.kb[c];
-      sA = t.ks;
+      for (int c = 0; c < 4; ++c) kb[c] = t.kb[c];
+      ks_cur = t.ks;
     }
     __builtin_amdgcn_s_waitcnt(0x0F70);  // drain once so the loop's waits stay exact
-    for (;;) {
-      if (T >= tile_hi) break;
-      tile_body(T, kA, kB, sA, sB);
-      T += kWaves;
-      if (T >= tile_hi) break;
-      tile_body(T, kB, kA, sB, sA);
-      T += kWaves;
-    }
+#pragma unroll 1
+    for (; T < tile_hi; T += kWaves) tile_body(T);
   }
+
 #pragma unroll
   for (int r = 0; r < 2; ++r) {
-    const bool spilled = flushed[r] > 0u;  // a stage filled up during the walk
-    if (staged[r]) flush(r);
     if (lane == 0) {
-      s_segn[r][wave] = flushed[r];
+      s_segn[r][wave] = min(cnt[r], seg_cap);
       if (cnt[r] > seg_cap) atomicOr(&s_segover[r], 1u);
-      if (spilled) atomicOr(&s_segover[r], 2u);
     }
   }
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // this wave's segment stores are done before it reads them back
   __syncthreads();
 
   uint32_t* stats = A.ctrl + kStatsOff;
@@ -266,7 +267,7 @@ __global__ __launch_bounds__(kWG, 2) void k_prefill_pair(PrefillArgs A) {
     const int L = re_t - rs_t;
     const int kr = min(A.K, L);
     const uint32_t n = s_segn[r][0] + s_segn[r][1] + s_segn[r][2] + s_segn[r][3];
-    const bool complete = (s_segover[r] & 1u) == 0u;
+    const bool complete = s_segover[r] == 0u;
     if (complete && n >= (uint32_t)kr) {
       // each wave takes its own segment (written by itself) into registers
       const uint32_t nw = s_segn[r][wave];
@@ -282,7 +283,7 @@ __global__ __launch_bounds__(kWG, 2) void k_prefill_pair(PrefillArgs A) {
       emit_selection_regs(key, id, lay, sel, kr, A.K, out, sh, tid);
       if (tid == 0) {
         atomicAdd(&stats[kStFast], 1u);
-        if (s_segover[r] & 2u) atomicAdd(&stats[kStSpilled], 1u);
+        if (n > (uint32_t)A.lds_cap) atomicAdd(&stats[kStSpilled], 1u);
         if (L <= A.K) atomicAdd(&stats[kStTrivial], 1u);
       }
     } else if (tid == 0) {
