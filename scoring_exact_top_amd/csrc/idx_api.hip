@@ -11,7 +11,7 @@ static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 static inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 struct PrefillLayout {
-  size_t ctrl, tau, fail, skey, cidx, scratch, rhist, rcnt, kt, total;
+  size_t ctrl, tau, fail, skey, cidx, segn, scratch, rhist, rcnt, kt, total;
 };
 
 static PrefillLayout prefill_layout(int32_t Q, int32_t N) {
@@ -20,8 +20,11 @@ static PrefillLayout prefill_layout(int32_t Q, int32_t N) {
   L.ctrl = o; o = align256(o + sizeof(uint32_t) * kCtrlWords);
   L.tau = o; o = align256(o + sizeof(float) * (size_t)Q);
   L.fail = o; o = align256(o + sizeof(int32_t) * (size_t)Q);
-  L.skey = o; o = align256(o + sizeof(uint32_t) * (size_t)Q * kCandCap);
-  L.cidx = o; o = align256(o + sizeof(int32_t) * (size_t)Q * kCandCap);
+  const size_t nseg = (size_t)kWaves * prefill_split(Q);
+  const size_t cand = (size_t)Q * nseg * (size_t)prefill_seg_cap(prefill_split(Q));
+  L.skey = o; o = align256(o + sizeof(uint32_t) * cand);
+  L.cidx = o; o = align256(o + sizeof(int32_t) * cand);
+  L.segn = o; o = align256(o + sizeof(uint32_t) * (size_t)Q * nseg);
   L.scratch = o; o = align256(o + sizeof(uint32_t) * (size_t)repair_rows(Q, N) * (size_t)repair_stride(N));
   L.rhist = o; o = align256(o + sizeof(uint32_t) * (size_t)repair_slots(Q, N) * 4 * 256);
   L.rcnt = o; o = align256(o + sizeof(uint32_t) * (size_t)repair_slots(Q, N) * 2);
@@ -55,6 +58,9 @@ static int prefill_common(const uint8_t* q, const float* q_scale, const uint8_t*
   A.fail_list = reinterpret_cast<int32_t*>(ws + L.fail);
   A.cand_key = reinterpret_cast<uint32_t*>(ws + L.skey);
   A.cand_idx = reinterpret_cast<int32_t*>(ws + L.cidx);
+  A.segn = reinterpret_cast<uint32_t*>(ws + L.segn);
+  A.S = prefill_split(Q);
+  A.seg_cap = prefill_seg_cap(A.S);
   A.scratch = reinterpret_cast<uint32_t*>(ws + L.scratch);
   A.rhist = reinterpret_cast<uint32_t*>(ws + L.rhist);
   A.rcnt = reinterpret_cast<uint32_t*>(ws + L.rcnt);
@@ -77,6 +83,10 @@ static int prefill_common(const uint8_t* q, const float* q_scale, const uint8_t*
     A.ev_main_stop = static_cast<hipEvent_t>(opts->ev_main_stop);
   }
   A.cap_total = A.lds_cap + A.spill_cap;
+  // usable entries per segment: the full segment unless a test knob shrank
+  // the capacity, then an even share of it
+  const int share = A.cap_total / (kWaves * A.S);
+  A.seg_eff = (A.cap_total >= kCandCap || share > A.seg_cap) ? A.seg_cap : share;
   hipStream_t s = static_cast<hipStream_t>(stream);
   int rc = launch_prefill(A, s);
   if (rc == IDX_OK && tau_out) {

@@ -594,12 +594,13 @@ __device__ __forceinline__ RegLayout block_list_layout(uint32_t n, uint32_t tid)
 // Loads of one list into registers, key[j] and id[j] = element lay.at(j):
 // buffer loads whose out-of-range reads return 0, so all of them are issued
 // back to back without a branch per element; invalid slots get key 0.
+// `extent` (uniform) bounds the buffers; lay.valid masks the entries.
 template <int M, class Dec>
 __device__ __forceinline__ void load_list_regs(uint32_t (&key)[M], int32_t (&id)[M], const uint32_t* keys,
-                                               const int32_t* ids, uint32_t n, const RegLayout& lay,
+                                               const int32_t* ids, uint32_t extent, const RegLayout& lay,
                                                const Dec& dec) {
-  const rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)keys, (short)0, (int)(n * 4u), 0x00020000);
-  const rsrc_t ri = __builtin_amdgcn_make_buffer_rsrc((void*)ids, (short)0, (int)(n * 4u), 0x00020000);
+  const rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)keys, (short)0, (int)(extent * 4u), 0x00020000);
+  const rsrc_t ri = __builtin_amdgcn_make_buffer_rsrc((void*)ids, (short)0, (int)(extent * 4u), 0x00020000);
   uint32_t raw[M];
 #pragma unroll
   for (int j = 0; j < M; ++j) {
@@ -678,16 +679,17 @@ template <int M>
 __device__ void emit_selection_regs(const uint32_t (&key)[M], const int32_t (&id)[M], const RegLayout& lay,
                                     const SelResult& sel, int kr, int K, int32_t* out, SelShared& sh,
                                     int tid) {
-  uint32_t gmask = 0u, emask = 0u;
+  static_assert(M <= 64, "winner masks hold one bit per register slot");
+  uint64_t gmask = 0u, emask = 0u;
 #pragma unroll
   for (int j = 0; j < M; ++j) {
     const bool v = lay.valid(j);
     const uint32_t mk = key[j] & sel.mask;
-    gmask |= (uint32_t)(v && mk > sel.prefix) << j;
-    emask |= (uint32_t)(v && mk == sel.prefix) << j;
+    gmask |= (uint64_t)(v && mk > sel.prefix) << j;
+    emask |= (uint64_t)(v && mk == sel.prefix) << j;
   }
   uint32_t gpos, epos, gtot, etot;
-  block_exclusive_scan2((uint32_t)__popc(gmask), (uint32_t)__popc(emask), sh, tid, gpos, epos, gtot, etot);
+  block_exclusive_scan2((uint32_t)__popcll(gmask), (uint32_t)__popcll(emask), sh, tid, gpos, epos, gtot, etot);
   const uint32_t eq_base = (uint32_t)(kr - sel.rem);
 #pragma unroll
   for (int j = 0; j < M; ++j) {

@@ -16,16 +16,39 @@ constexpr int kSampleTarget = IDX_TOPK_SAMPLE_TARGET;
 constexpr int kMaxSamples = 2048;  // longer rows widen the stride instead
 
 // Candidates per row ("4.3 Candidate layout: warp-private segments" and "4.5
-// Overflow spill area"): each (row, wave) pair of the main kernel stages
-// (score, id) pairs in an on-chip area of kSegStage entries and copies a full
-// stage in bulk to its private workspace segment of kSegCap entries.  The
-// certificate's capacity per row is kCandCap, the four segments together;
-// a row also fails it when one segment alone overflows.
-constexpr int kLdsCap = 4096;    // on-chip stage entries per row (all waves)
-constexpr int kSpillCap = 4096;  // capacity beyond one stage fill
+// Overflow spill area"): the main kernel splits each row pair's key tiles
+// over S workgroups (S = 1 when there are rows enough to fill the chip, up
+// to kMaxSplit for few rows: parallelism along the keys, "10. The
+// optimization target after fusion"), and each (split, wave) stores its
+// candidates into a private workspace segment.  The certificate's capacity
+// per row is kCandCap (kLdsCap + kSpillCap, the default of the test knobs);
+// a segment is sized so that a row short enough to keep all its keys
+// (L <= kCandCap, threshold -inf) never overflows it, and a row also fails
+// the certificate when one segment alone overflows.
+constexpr int kLdsCap = 4096;
+constexpr int kSpillCap = 4096;
 constexpr int kCandCap = kLdsCap + kSpillCap;
-constexpr int kSegStage = kLdsCap / kWaves;
-constexpr int kSegCap = kCandCap / kWaves;
+constexpr int kMaxSplit = 8;
+constexpr int kSelRegs = 40;  // keys per thread of the select kernel, all S <= kMaxSplit
+
+// Splits of the main kernel for Q rows: at least 512 workgroups (two per
+// CU) when possible.
+__host__ __device__ inline int prefill_split(int rows) {
+  const int pairs = (rows + 1) / 2;
+  int s = 1;
+  while (s < kMaxSplit && pairs * s < 512) s *= 2;
+  return s;
+}
+
+// Entries of one (split, wave) segment for S splits: the larger of an even
+// share of kCandCap and the tiles an unaligned kCandCap-key row puts on one
+// segment (such a row spans kCandCap/64 + 1 tiles).
+__host__ __device__ inline int prefill_seg_cap(int S) {
+  const int nseg = kWaves * S;
+  const int share = kCandCap / nseg;
+  const int tiles = (kCandCap / 64 + 1 + nseg - 1) / nseg;
+  return share > tiles * 64 ? share : tiles * 64;
+}
 
 // Exact repair, split over the chip: one work item covers kRepairChunk
 // positions of one failed row; scratch holds the scores of up to
@@ -78,8 +101,10 @@ struct PrefillArgs {
   float* tau;           // [Q]
   int32_t* out;         // [Q][K]
   uint8_t* kt;          // [ntiles][8][64][16] keys relaid in MFMA lane order
-  uint32_t* cand_key;   // [Q][kWaves][kSegCap] candidate scores (FP32 bits)
-  int32_t* cand_idx;    // [Q][kWaves][kSegCap] candidate key ids
+  uint32_t* cand_key;   // [Q][kWaves*S][seg_cap] candidate scores (FP32 bits)
+  int32_t* cand_idx;    // [Q][kWaves*S][seg_cap] candidate key ids
+  uint32_t* segn;       // [Q][kWaves*S] entries per segment; bit 31: it overflowed
+  int32_t S, seg_cap, seg_eff;  // splits, segment stride, usable entries per segment
   int32_t lds_cap, spill_cap, cap_total;
   int32_t* fail_list;   // [Q]
   uint32_t* ctrl;       // kCtrlWords

@@ -82,8 +82,10 @@ __global__ __launch_bounds__(kWG) void k_prefill_tau(PrefillArgs A) {
 
 // ------------------------------------------------------ paired-row main
 
-// Two query rows per workgroup of four waves; two workgroups per CU.  Each
-// wave walks every fourth 64-key tile of the rows' union range.  Per 16-key
+// Two query rows per workgroup of four waves; two workgroups per CU.  With
+// few rows the pair's tiles are split over S workgroups (S*kWaves waves in
+// all), and each wave walks every (S*kWaves)-th 64-key tile of the rows'
+// union range.  Per 16-key
 // sub-tile it issues the 9 MFMAs of both rows (4 head blocks each plus the
 // shared u block), software-pipelined by row so that each row's epilogue
 // runs under the other row's MFMAs, and refills the sub-tile's registers
@@ -91,18 +93,18 @@ __global__ __launch_bounds__(kWG) void k_prefill_tau(PrefillArgs A) {
 // are stored, as raw score bits and key id, straight into the wave's
 // private segment of the row's workspace candidate area; the slot comes
 // from a scalar count plus the lane's rank in the ballot, so no atomics
-// are involved.  After the walk the workgroup certifies and selects each
-// row in turn, every wave holding its own segment in registers.
+// are involved.  After the walk each wave publishes its segment counts;
+// certification and selection follow in their own kernel.
 template <bool DBG>
 __global__ __launch_bounds__(kWG, 2) void k_prefill_pair(PrefillArgs A) {
-  __shared__ uint32_t s_segn[2][kWaves];   // entries in each segment (capped)
-  __shared__ uint32_t s_segover[2];        // some segment of the row overflowed
-  __shared__ SelShared sh;
   __shared__ uint8_t s_qprep[kWaves][2 * kUTerms * kD];
   const int tid = threadIdx.x;
   const uint32_t lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int t0 = 2 * blockIdx.x;
+  const int split = blockIdx.x % A.S;           // which share of the pair's tiles
+  const int t0 = 2 * (blockIdx.x / A.S);
+  const int seg = split * kWaves + wave;        // this wave's segment of each row
+  const int nseg = kWaves * A.S;
 
   int rs[2], re[2];
   float tr[2];
@@ -119,7 +121,6 @@ __global__ __launch_bounds__(kWG, 2) void k_prefill_pair(PrefillArgs A) {
       }
     }
   }
-  if (tid < 2) s_segover[tid] = 0u;
   QOp2 qo;
   prepare_q2(qo, A.q, A.q_scale, A.w, min(t0, A.Q - 1), min(t0 + 1, A.Q - 1), lane, s_qprep[wave]);
   __syncthreads();
@@ -127,8 +128,7 @@ __global__ __launch_bounds__(kWG, 2) void k_prefill_pair(PrefillArgs A) {
   const KeyBuf kbuf = make_keybuf(A.k, A.k_scale, A.N);
   const int ntiles = (A.N + 63) >> 6;
   const rsrc_t ktb = __builtin_amdgcn_make_buffer_rsrc((void*)A.kt, (short)0, ntiles * kTile * kD, 0x00020000);
-  // per-segment capacities (the debug knobs scale them down)
-  const uint32_t seg_cap = (uint32_t)min(kSegCap, A.cap_total / kWaves);
+  const uint32_t seg_cap = (uint32_t)A.seg_eff;
   const int tile_hi = (hi + 63) >> 6;
   const int voff = (int)lane * 16;
   uint32_t cnt[2] = {0u, 0u};  // candidates of each row found by this wave
@@ -137,7 +137,7 @@ __global__ __launch_bounds__(kWG, 2) void k_prefill_pair(PrefillArgs A) {
   rsrc_t segk[2], segi[2];
 #pragma unroll
   for (int r = 0; r < 2; ++r) {
-    const int64_t o = ((int64_t)min(t0 + r, A.Q - 1) * kWaves + wave) * kSegCap;
+    const int64_t o = ((int64_t)min(t0 + r, A.Q - 1) * nseg + seg) * A.seg_cap;
     segk[r] = __builtin_amdgcn_make_buffer_rsrc((void*)(A.cand_key + o), (short)0, (int)(seg_cap * 4u), 0x00020000);
     segi[r] = __builtin_amdgcn_make_buffer_rsrc((void*)(A.cand_idx + o), (short)0, (int)(seg_cap * 4u), 0x00020000);
   }
@@ -192,7 +192,7 @@ __global__ __launch_bounds__(kWG, 2) void k_prefill_pair(PrefillArgs A) {
   v8i kb[4];
   float ks_cur = 0.f;
   auto tile_body = [&](int T) {
-    const int ntoff = (T + kWaves) * (kTile * kD);
+    const int ntoff = (T + nseg) * (kTile * kD);
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       v4f aA[4];
@@ -228,7 +228,7 @@ __global__ __launch_bounds__(kWG, 2) void k_prefill_pair(PrefillArgs A) {
     tail(T, ks);
   };
   if (lo < hi) {
-    int T = (lo >> 6) + wave;
+    int T = (lo >> 6) + seg;
     {
       KeyTile t;
       load_tile_relaid(t, ktb, kbuf.ks, T, lane);
@@ -238,60 +238,70 @@ __global__ __launch_bounds__(kWG, 2) void k_prefill_pair(PrefillArgs A) {
     }
     __builtin_amdgcn_s_waitcnt(0x0F70);  // drain once so the loop's waits stay exact
 #pragma unroll 1
-    for (; T < tile_hi; T += kWaves) tile_body(T);
+    for (; T < tile_hi; T += nseg) tile_body(T);
   }
 
+  // publish this wave's segment counts (bit 31: the segment overflowed)
 #pragma unroll
   for (int r = 0; r < 2; ++r) {
-    if (lane == 0) {
-      s_segn[r][wave] = min(cnt[r], seg_cap);
-      if (cnt[r] > seg_cap) atomicOr(&s_segover[r], 1u);
-    }
+    if (lane == 0 && t0 + r < A.Q)
+      A.segn[(int64_t)(t0 + r) * nseg + seg] = min(cnt[r], seg_cap) | (cnt[r] > seg_cap ? 0x80000000u : 0u);
   }
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // this wave's segment stores are done before it reads them back
-  __syncthreads();
+}
 
+// ------------------------------------------------------------------ select
+
+// One workgroup per row, after the main kernel: certify the row's candidate
+// list (its kWaves*S segments: at least K entries, none overflowed), load
+// it into registers (segment g of the row in threads [g*tps, (g+1)*tps),
+// tps = 256/nseg, each thread every tps-th entry), radix-select the K
+// largest and emit them; rows that fail go to the failure list.
+__global__ __launch_bounds__(kWG) void k_prefill_select(PrefillArgs A) {
+  __shared__ SelShared sh;
+  __shared__ uint32_t s_segn[kWaves * kMaxSplit];
+  const int tid = threadIdx.x;
+  const int t = blockIdx.x;
   uint32_t* stats = A.ctrl + kStatsOff;
-#pragma unroll 1
-  for (int r = 0; r < 2; ++r) {
-    const int t = t0 + r;
-    if (t >= A.Q) break;
-    int32_t* out = A.out + (int64_t)t * A.K;
-    if (tid == 0) atomicAdd(&stats[kStRows], 1u);
-    const int rs_t = A.row_start[t], re_t = A.row_end[t];
-    if (rs_t < 0 || rs_t > re_t || re_t > A.N) {
-      for (int i = tid; i < A.K; i += kWG) out[i] = -1;
-      if (tid == 0) atomicAdd(&stats[kStBad], 1u);
-      continue;
+  int32_t* out = A.out + (int64_t)t * A.K;
+  if (tid == 0) atomicAdd(&stats[kStRows], 1u);
+  const int rs_t = A.row_start[t], re_t = A.row_end[t];
+  if (rs_t < 0 || rs_t > re_t || re_t > A.N) {
+    for (int i = tid; i < A.K; i += kWG) out[i] = -1;
+    if (tid == 0) atomicAdd(&stats[kStBad], 1u);
+    return;
+  }
+  const int nseg = kWaves * A.S;
+  if (tid < nseg) s_segn[tid] = A.segn[(int64_t)t * nseg + tid];
+  __syncthreads();
+  uint32_t n = 0u, over = 0u;
+  for (int g = 0; g < nseg; ++g) {
+    n += s_segn[g] & 0x7FFFFFFFu;
+    over |= s_segn[g] >> 31;
+  }
+  const int L = re_t - rs_t;
+  const int kr = min(A.K, L);
+  if (!over && n >= (uint32_t)kr) {
+    const uint32_t tps = (uint32_t)(kWG / nseg);
+    const uint32_t g = (uint32_t)tid / tps;
+    const uint32_t first = g * (uint32_t)A.seg_cap;
+    const RegLayout lay{first + (uint32_t)tid % tps, tps, first + (s_segn[g] & 0x7FFFFFFFu), kSelRegs};
+    const int64_t row = (int64_t)t * nseg * A.seg_cap;
+    uint32_t key[kSelRegs];
+    int32_t id[kSelRegs];
+    load_list_regs(key, id, A.cand_key + row, A.cand_idx + row, (uint32_t)(nseg * A.seg_cap), lay,
+                   [](uint32_t x) { return f2key(__uint_as_float(x)); });
+    const SelResult sel = (n > (uint32_t)kr) ? radix_select_regs(key, lay, kr, sh, tid, true)
+                                            : SelResult{0u, 0u, kr};
+    emit_selection_regs(key, id, lay, sel, kr, A.K, out, sh, tid);
+    if (tid == 0) {
+      atomicAdd(&stats[kStFast], 1u);
+      if (n > (uint32_t)A.lds_cap) atomicAdd(&stats[kStSpilled], 1u);
+      if (L <= A.K) atomicAdd(&stats[kStTrivial], 1u);
     }
-    const int L = re_t - rs_t;
-    const int kr = min(A.K, L);
-    const uint32_t n = s_segn[r][0] + s_segn[r][1] + s_segn[r][2] + s_segn[r][3];
-    const bool complete = s_segover[r] == 0u;
-    if (complete && n >= (uint32_t)kr) {
-      // each wave takes its own segment (written by itself) into registers
-      const uint32_t nw = s_segn[r][wave];
-      const int64_t o = ((int64_t)t * kWaves + wave) * kSegCap;
-      const uint32_t* gk = A.cand_key + o;
-      const RegLayout lay = wave_list_layout(nw, lane);
-      uint32_t key[kSegCap / 64];
-      int32_t id[kSegCap / 64];
-      load_list_regs(key, id, gk, A.cand_idx + o, nw, lay,
-                     [](uint32_t x) { return f2key(__uint_as_float(x)); });
-      const SelResult sel = (n > (uint32_t)kr) ? radix_select_regs(key, lay, kr, sh, tid, true)
-                                              : SelResult{0u, 0u, kr};
-      emit_selection_regs(key, id, lay, sel, kr, A.K, out, sh, tid);
-      if (tid == 0) {
-        atomicAdd(&stats[kStFast], 1u);
-        if (n > (uint32_t)A.lds_cap) atomicAdd(&stats[kStSpilled], 1u);
-        if (L <= A.K) atomicAdd(&stats[kStTrivial], 1u);
-      }
-    } else if (tid == 0) {
-      const uint32_t f = atomicAdd(&A.ctrl[kCtrlFail], 1u);
-      A.fail_list[f] = t;
-      atomicAdd(&stats[complete ? kStUnder : kStOver], 1u);
-    }
-    __syncthreads();
+  } else if (tid == 0) {
+    const uint32_t f = atomicAdd(&A.ctrl[kCtrlFail], 1u);
+    A.fail_list[f] = t;
+    atomicAdd(&stats[over ? kStOver : kStUnder], 1u);
   }
 }
 
@@ -518,11 +528,13 @@ int launch_prefill(const PrefillArgs& A, hipStream_t stream) {
   if (nchunks > 0) hipLaunchKernelGGL(k_relayout_keys, dim3((unsigned)(nchunks / kWG)), dim3(kWG), 0, stream, A);
   hipLaunchKernelGGL(k_prefill_tau, dim3((A.Q + kWaves - 1) / kWaves), dim3(kWG), 0, stream, A);
   if (A.ev_main_start && hipEventRecord(A.ev_main_start, stream) != hipSuccess) return IDX_EHIP;
+  const unsigned grid = (unsigned)((A.Q + 1) / 2 * A.S);
   if (A.dbg_scores)
-    hipLaunchKernelGGL(k_prefill_pair<true>, dim3((A.Q + 1) / 2), dim3(kWG), 0, stream, A);
+    hipLaunchKernelGGL(k_prefill_pair<true>, dim3(grid), dim3(kWG), 0, stream, A);
   else
-    hipLaunchKernelGGL(k_prefill_pair<false>, dim3((A.Q + 1) / 2), dim3(kWG), 0, stream, A);
+    hipLaunchKernelGGL(k_prefill_pair<false>, dim3(grid), dim3(kWG), 0, stream, A);
   if (A.ev_main_stop && hipEventRecord(A.ev_main_stop, stream) != hipSuccess) return IDX_EHIP;
+  hipLaunchKernelGGL(k_prefill_select, dim3(A.Q), dim3(kWG), 0, stream, A);
   hipLaunchKernelGGL(k_prefill_repair_score, dim3(kRepairGrid), dim3(kWG), 0, stream, A);
   hipLaunchKernelGGL(k_prefill_repair_pass<1>, dim3(kRepairGrid), dim3(kWG), 0, stream, A);
   hipLaunchKernelGGL(k_prefill_repair_pass<2>, dim3(kRepairGrid), dim3(kWG), 0, stream, A);

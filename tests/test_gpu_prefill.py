@@ -73,13 +73,18 @@ def test_forced_overflow_goes_to_repair():
 
 
 def test_spill_area_is_merged():
-    """A small on-chip capacity pushes candidates into the spill area; the
-    certificate still holds, and the selection merges both sources."""
-    case = synth.random_case("spill", 10, 6000, seed=25, K=700, min_len=2500, max_len=4500)
+    """Rows that keep every key (threshold -inf, L <= 8192, the default
+    capacity) hold more candidates than the on-chip share (4096): the
+    certificate still holds for every row and the selection merges all of
+    the row's segments.  Row 0 spans 8192 keys from an unaligned start, the
+    most tiles one row can put on a segment."""
+    case = synth.random_case("spill", 10, 9000, seed=25, K=700, min_len=4200, max_len=8192)
+    case.row_start[0], case.row_end[0] = 1, 8193
     log("case", case.name)
-    r = run_prefill(case, force_tau=float("-inf"), lds_cap=512, spill_cap=4096, scores=True)
+    r = run_prefill(case, force_tau=float("-inf"), scores=True)
     st = r["stats"]
-    assert st["spilled"] > 0 and st["repaired"] == 0, st
+    log("stats", st)
+    assert st["spilled"] == case.Q and st["fast_ok"] == case.Q and st["repaired"] == 0, st
     check_prefill_rows(case, r["out"], np.arange(case.Q))
 
 
