@@ -149,9 +149,15 @@ extern "C" int idx_topk_decode_paged_debug(const uint8_t* q, const float* q_scal
 extern "C" int idx_topk_read_stats(const void* workspace, idx_topk_stats* out, void* stream) {
   if (!workspace || !out) return IDX_EINVAL;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  static_assert(sizeof(idx_topk_stats) == sizeof(uint32_t) * kStatCount, "stats layout");
   const char* src = static_cast<const char*>(workspace) + sizeof(uint32_t) * kStatsOff;
-  if (hipMemcpyAsync(out, src, sizeof(idx_topk_stats), hipMemcpyDeviceToHost, s) != hipSuccess) return IDX_EHIP;
+  uint32_t copies[kStatLanes * kStatStride];
+  if (hipMemcpyAsync(copies, src, sizeof(copies), hipMemcpyDeviceToHost, s) != hipSuccess) return IDX_EHIP;
   if (hipStreamSynchronize(s) != hipSuccess) return IDX_EHIP;
+  uint32_t sum[kStatCount] = {};
+  for (int l = 0; l < kStatLanes; ++l)
+    for (int c = 0; c < kStatCount; ++c) sum[c] += copies[l * kStatStride + c];
+  memcpy(out, sum, sizeof(sum));
   return IDX_OK;
 }
 

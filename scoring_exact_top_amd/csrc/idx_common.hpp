@@ -472,7 +472,7 @@ struct SelShared {
   uint32_t hist[256];
   uint32_t bucket, above, inbucket, pad0;
   uint32_t gt_count, eq_count, pad1, pad2;
-  uint32_t wsum[2][kWaves];  // per-wave totals of block_exclusive_scan2
+  uint32_t wsum[2][kWaves];  // per-wave minima and maxima of range_select_regs
 };
 
 // Result of the digit passes: every key with (key & mask) > prefix is in the
@@ -581,11 +581,6 @@ struct RegLayout {
   __device__ bool valid(int j) const { return at(j) < n; }
 };
 
-// Each wave holds its own list of nw elements, element j*64 + lane in key[j].
-__device__ __forceinline__ RegLayout wave_list_layout(uint32_t nw, uint32_t lane) {
-  return RegLayout{lane, 64u, nw, (nw + 63u) >> 6};
-}
-
 // The workgroup holds one list of n elements, element j*256 + tid in key[j].
 __device__ __forceinline__ RegLayout block_list_layout(uint32_t n, uint32_t tid) {
   return RegLayout{tid, (uint32_t)kWG, n, (n + kWG - 1u) / kWG};
@@ -611,95 +606,136 @@ __device__ __forceinline__ void load_list_regs(uint32_t (&key)[M], int32_t (&id)
   for (int j = 0; j < M; ++j) key[j] = lay.valid(j) ? dec(raw[j]) : 0u;
 }
 
-// Radix select over keys held in registers (layout `lay`).  Same passes and
-// result as radix_select over the whole list; no memory traffic besides the
-// LDS histogram.  All threads of the workgroup call this.
+// Selection over keys held in registers: every key above `last` is in the
+// top-K, and the first `rem` keys in [lo, last] complete it (any of them are
+// correct where they all share one value).
+struct RangeSel {
+  uint32_t lo, last;
+  int rem;
+};
+
+// Register lists for range_select_regs / emit_range_regs hold nonzero keys,
+// with 0 in unused slots (load_list_regs stores 0 there).  Candidate keys
+// qualify: a candidate passed score >= tau, which no NaN does, and only a
+// NaN maps to key 0.  So no per-slot validity mask is kept.
+
+// The K-th-largest search ("3.2 Sampled threshold", select step) with digits
+// taken relative to the list's own range: the first pass cuts [min, max]
+// into 256 equal power-of-two bins, so a candidate list (scores between tau
+// and the row maximum) spreads over the bins and the search usually ends
+// after two passes, when the bin that holds the K-th key is taken whole.
+// Each further pass splits the chosen bin 256 ways; a bin of width one ends
+// the search.  Requires 1 <= rem < number of keys.  All threads of the
+// workgroup call this.
 template <int M>
-__device__ SelResult radix_select_regs(const uint32_t (&key)[M], const RegLayout& lay, int rem,
-                                       SelShared& sh, int tid, bool allow_early) {
-  uint32_t prefix = 0, mask = 0;
+__device__ RangeSel range_select_regs(const uint32_t (&key)[M], const RegLayout& lay, int rem, SelShared& sh,
+                                      int tid) {
+  const uint32_t lane = tid & 63;
+  const int wave = tid >> 6;
+  uint32_t mn = 0xFFFFFFFFu, mx = 0u;
+#pragma unroll
+  for (int j = 0; j < M; ++j) {
+    if ((uint32_t)j < lay.jmax) {
+      mn = min(mn, key[j] ? key[j] : 0xFFFFFFFFu);
+      mx = max(mx, key[j]);
+    }
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    mn = min(mn, (uint32_t)__shfl_xor((int)mn, off, 64));
+    mx = max(mx, (uint32_t)__shfl_xor((int)mx, off, 64));
+  }
+  if (lane == 0) { sh.wsum[0][wave] = mn; sh.wsum[1][wave] = mx; }
+  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    mn = min(mn, sh.wsum[0][w]);
+    mx = max(mx, sh.wsum[1][w]);
+  }
+  const uint32_t span = mx - mn;
+  const int bits = span ? 32 - __clz((int)span) : 0;
+  int s = bits > 8 ? bits - 8 : 0;
+  uint32_t lo = mn, width = span;  // the range is [lo, lo + width]
 #pragma unroll 1
-  for (int shift = 24; shift >= 0; shift -= 8) {
+  while (true) {
     sh.hist[tid] = 0u;  // kWG == 256 bins
     __syncthreads();
 #pragma unroll
     for (int j = 0; j < M; ++j) {
-      if ((uint32_t)j < lay.jmax)  // wave-uniform guard; keeps key[] in registers
-        hist_add(sh.hist, (key[j] >> shift) & 255u, lay.valid(j) && ((key[j] & mask) == prefix));
+      if ((uint32_t)j < lay.jmax) {  // wave-uniform guard; keeps key[] in registers
+        const uint32_t d = key[j] - lo;  // key 0 wraps above any width (lo >= 1)
+        if (d <= width) atomicAdd(&sh.hist[d >> s], 1u);
+      }
     }
     __syncthreads();
     find_bucket(sh, rem, tid);
     __syncthreads();
     const uint32_t b = sh.bucket, above = sh.above, inb = sh.inbucket;
     __syncthreads();
-    prefix |= b << shift;
-    mask |= 0xFFu << shift;
     rem -= (int)above;
-    if (allow_early && (int)inb == rem) break;
+    const uint32_t off = b << s;
+    lo += off;
+    width = min(width - off, (1u << s) - 1u);  // s <= 24
+    if ((int)inb == rem || s == 0) break;
+    s = s > 8 ? s - 8 : 0;
   }
-  return SelResult{prefix, mask, rem};
+  return RangeSel{lo, lo + width, rem};
 }
 
-// Exclusive prefix sums over the workgroup of two per-thread counts, in
-// thread order; also returns the totals.  All threads call this.
-__device__ __forceinline__ void block_exclusive_scan2(uint32_t a, uint32_t b, SelShared& sh, int tid,
-                                                      uint32_t& a_ex, uint32_t& b_ex, uint32_t& a_tot,
-                                                      uint32_t& b_tot) {
+// Emit for range_select_regs: id[j] is the id of key[j].  Keys above `last`
+// fill out[0, kr - rem), the first `rem` keys in [lo, last] fill
+// out[kr - rem, kr), -1 up to K.  Positions run over (slot j, wave, lane) in
+// that order, so a wave's winners in one slot are stored to consecutive
+// addresses and the result does not depend on timing.  At most 64 slots
+// per thread and 65535 keys per list (two 16-bit counts share a word).
+// Same key convention as range_select_regs (lo >= 1).
+template <int M>
+__device__ void emit_range_regs(const uint32_t (&key)[M], const int32_t (&id)[M], const RegLayout& lay,
+                                const RangeSel& sel, int kr, int K, int32_t* out, SelShared& sh, int tid) {
+  static_assert(M <= 64, "one lane per register slot");
   const uint32_t lane = tid & 63;
   const int wave = tid >> 6;
-  uint32_t ia = a, ib = b;  // inclusive scans within the wave
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint32_t xa = __shfl_up(ia, off, 64), xb = __shfl_up(ib, off, 64);
-    if (lane >= (uint32_t)off) { ia += xa; ib += xb; }
-  }
-  if (lane == 63) { sh.wsum[0][wave] = ia; sh.wsum[1][wave] = ib; }
-  __syncthreads();
-  uint32_t pa = 0, pb = 0;
-  a_tot = 0;
-  b_tot = 0;
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w) {
-    const uint32_t wa = sh.wsum[0][w], wb = sh.wsum[1][w];
-    if (w < wave) { pa += wa; pb += wb; }
-    a_tot += wa;
-    b_tot += wb;
-  }
-  a_ex = pa + ia - a;
-  b_ex = pb + ib - b;
-  __syncthreads();
-}
-
-// Emit for radix_select_regs: id[j] is the id of key[j] (loaded together with
-// the keys).  Output positions come from prefix sums of per-thread winner
-// counts, so the order is deterministic (thread order, then j) and no
-// atomics are needed: keys above the boundary prefix fill out[0, kr - rem),
-// the first `rem` keys equal to it fill out[kr - rem, kr), -1 up to K.
-template <int M>
-__device__ void emit_selection_regs(const uint32_t (&key)[M], const int32_t (&id)[M], const RegLayout& lay,
-                                    const SelResult& sel, int kr, int K, int32_t* out, SelShared& sh,
-                                    int tid) {
-  static_assert(M <= 64, "winner masks hold one bit per register slot");
-  uint64_t gmask = 0u, emask = 0u;
+  const uint32_t width = sel.last - sel.lo;
+  // lane j: this wave's winners in slot j (above | boundary << 16)
+  uint32_t mine = 0u;
 #pragma unroll
   for (int j = 0; j < M; ++j) {
-    const bool v = lay.valid(j);
-    const uint32_t mk = key[j] & sel.mask;
-    gmask |= (uint64_t)(v && mk > sel.prefix) << j;
-    emask |= (uint64_t)(v && mk == sel.prefix) << j;
+    if ((uint32_t)j < lay.jmax) {
+      const uint32_t c = (uint32_t)__popcll(__ballot(key[j] > sel.last)) |
+                         (uint32_t)__popcll(__ballot(key[j] - sel.lo <= width)) << 16;
+      mine = lane == (uint32_t)j ? c : mine;
+    }
   }
-  uint32_t gpos, epos, gtot, etot;
-  block_exclusive_scan2((uint32_t)__popcll(gmask), (uint32_t)__popcll(emask), sh, tid, gpos, epos, gtot, etot);
+  sh.hist[wave * 64 + lane] = mine;
+  __syncthreads();
+  uint32_t col = 0u, before = 0u;  // slot `lane` over all waves, over the waves before this one
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    const uint32_t c = sh.hist[w * 64 + lane];
+    col += c;
+    before += w < wave ? c : 0u;
+  }
+  uint32_t inc = col;  // inclusive scan over the slots
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t x = (uint32_t)__shfl_up((int)inc, off, 64);
+    if (lane >= (uint32_t)off) inc += x;
+  }
+  const uint32_t base = inc - col + before;
   const uint32_t eq_base = (uint32_t)(kr - sel.rem);
 #pragma unroll
   for (int j = 0; j < M; ++j) {
-    if (gmask >> j & 1u) out[gpos++] = id[j];
-    if (emask >> j & 1u) {
-      if (epos < (uint32_t)sel.rem) out[eq_base + epos] = id[j];
-      ++epos;
+    if ((uint32_t)j < lay.jmax) {
+      const uint32_t bj = (uint32_t)__builtin_amdgcn_readlane((int)base, j);
+      const bool g = key[j] > sel.last, e = key[j] - sel.lo <= width;
+      const uint64_t bg = __ballot(g), be = __ballot(e);
+      if (g) out[(bj & 0xFFFFu) + rank_in(bg)] = id[j];
+      const uint32_t pe = (bj >> 16) + rank_in(be);
+      if (e && pe < (uint32_t)sel.rem) out[eq_base + pe] = id[j];
     }
   }
   for (int i = kr + tid; i < K; i += kWG) out[i] = -1;
+  __syncthreads();
 }
 
 // ------------------------------------------------- wave-level selection

@@ -59,7 +59,7 @@ __global__ __launch_bounds__(kWG) void k_decode_prep(DecodeArgs A) {
   const int tid = threadIdx.x;
   const uint32_t lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  if (blockIdx.x == 0 && tid < kCtrlWords) A.ctrl[tid] = 0u;
+  if (blockIdx.x == 0) clear_ctrl(A.ctrl, tid);
   const int b = kWaves * blockIdx.x + wave;
   if (b >= A.B) return;
   if (lane == 0) A.cnt[b] = 0u;
@@ -220,7 +220,7 @@ __global__ __launch_bounds__(kWG) void k_decode_select(DecodeArgs A) {
   __shared__ SelShared sh;
   const int tid = threadIdx.x;
   const int b = blockIdx.x;
-  uint32_t* stats = A.ctrl + kStatsOff;
+  uint32_t* stats = stat_copy(A.ctrl, blockIdx.x);
   const int st = A.status[b];
   if (tid == 0) atomicAdd(&stats[kStRows], 1u);
   if (st != 0) {
@@ -236,9 +236,9 @@ __global__ __launch_bounds__(kWG) void k_decode_select(DecodeArgs A) {
     uint32_t key[kDecCap / kWG];
     int32_t id[kDecCap / kWG];
     load_list_regs(key, id, ckey, cidx, n, lay, [](uint32_t x) { return f2key(__uint_as_float(x)); });
-    const SelResult sel = (n > (uint32_t)kr) ? radix_select_regs(key, lay, kr, sh, tid, true)
-                                            : SelResult{0u, 0u, kr};
-    emit_selection_regs(key, id, lay, sel, kr, A.K, A.out + (int64_t)b * A.K, sh, tid);
+    const RangeSel sel = (n > (uint32_t)kr) ? range_select_regs(key, lay, kr, sh, tid)
+                                           : RangeSel{1u, 0xFFFFFFFFu, kr};
+    emit_range_regs(key, id, lay, sel, kr, A.K, A.out + (int64_t)b * A.K, sh, tid);
     if (tid == 0) atomicAdd(&stats[kStFast], 1u);
   } else if (tid == 0) {
     const uint32_t f = atomicAdd(&A.ctrl[kCtrlFail], 1u);
@@ -254,7 +254,7 @@ __global__ __launch_bounds__(kWG) void k_decode_repair(DecodeArgs A) {
   const uint32_t lane = tid & 63;
   const uint32_t n_fail = __atomic_load_n(&A.ctrl[kCtrlFail], __ATOMIC_RELAXED);
   uint32_t* scratch = A.scratch + (int64_t)blockIdx.x * A.max_pages * 64;
-  uint32_t* stats = A.ctrl + kStatsOff;
+  uint32_t* stats = stat_copy(A.ctrl, blockIdx.x);
 #pragma unroll 1
   for (uint32_t f = blockIdx.x; f < n_fail; f += gridDim.x) {
     const int b = A.fail_list[f];

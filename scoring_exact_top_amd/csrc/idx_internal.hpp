@@ -60,12 +60,27 @@ constexpr int kRepairGrid = 1024;
 constexpr int kRepairFallback = 256;
 constexpr int64_t kRepairScratchKeys = (int64_t)1 << 28;  // 1 GiB of scores
 
-// Control words at the start of every workspace.
-constexpr int kCtrlWords = 16;
+// Control words at the start of every workspace: the failure count, then
+// kStatLanes copies of the idx_topk_stats counters, one 128-byte line each
+// (workgroup b counts into copy b % kStatLanes, so that thousands of
+// per-row increments do not queue on one address; the reader sums them).
 constexpr int kCtrlFail = 0;   // number of rows on the failure list
-constexpr int kStatsOff = 8;   // idx_topk_stats, in declaration order
+constexpr int kStatsOff = 32;  // first counter copy
+constexpr int kStatLanes = 32;
+constexpr int kStatStride = 32;  // words between copies
+constexpr int kStatCount = 8;    // counters per copy, idx_topk_stats order
+constexpr int kCtrlWords = kStatsOff + kStatLanes * kStatStride;
 constexpr int kStRows = 0, kStFast = 1, kStUnder = 2, kStOver = 3, kStSpilled = 4,
               kStRepaired = 5, kStTrivial = 6, kStBad = 7;
+
+__device__ __forceinline__ uint32_t* stat_copy(uint32_t* ctrl, int block) {
+  return ctrl + kStatsOff + (block & (kStatLanes - 1)) * kStatStride;
+}
+
+// Zero the control words (first workgroup of the first kernel of a call).
+__device__ __forceinline__ void clear_ctrl(uint32_t* ctrl, int tid) {
+  for (int i = tid; i < kCtrlWords; i += kWG) ctrl[i] = 0u;
+}
 
 __host__ __device__ inline int repair_grid(int rows) { return rows < 256 ? (rows > 0 ? rows : 1) : 256; }
 

@@ -37,7 +37,7 @@ __global__ __launch_bounds__(kWG) void k_prefill_tau(PrefillArgs A) {
   const int tid = threadIdx.x;
   const uint32_t lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  if (blockIdx.x == 0 && tid < kCtrlWords) A.ctrl[tid] = 0u;
+  if (blockIdx.x == 0) clear_ctrl(A.ctrl, tid);
   const int t = kWaves * blockIdx.x + wave;  // one row per wave
   if (t >= A.Q) return;
   if (t < A.rslots) {
@@ -261,7 +261,7 @@ __global__ __launch_bounds__(kWG) void k_prefill_select(PrefillArgs A) {
   __shared__ uint32_t s_segn[kWaves * kMaxSplit];
   const int tid = threadIdx.x;
   const int t = blockIdx.x;
-  uint32_t* stats = A.ctrl + kStatsOff;
+  uint32_t* stats = stat_copy(A.ctrl, blockIdx.x);
   int32_t* out = A.out + (int64_t)t * A.K;
   if (tid == 0) atomicAdd(&stats[kStRows], 1u);
   const int rs_t = A.row_start[t], re_t = A.row_end[t];
@@ -290,9 +290,9 @@ __global__ __launch_bounds__(kWG) void k_prefill_select(PrefillArgs A) {
     int32_t id[kSelRegs];
     load_list_regs(key, id, A.cand_key + row, A.cand_idx + row, (uint32_t)(nseg * A.seg_cap), lay,
                    [](uint32_t x) { return f2key(__uint_as_float(x)); });
-    const SelResult sel = (n > (uint32_t)kr) ? radix_select_regs(key, lay, kr, sh, tid, true)
-                                            : SelResult{0u, 0u, kr};
-    emit_selection_regs(key, id, lay, sel, kr, A.K, out, sh, tid);
+    const RangeSel sel = (n > (uint32_t)kr) ? range_select_regs(key, lay, kr, sh, tid)
+                                           : RangeSel{1u, 0xFFFFFFFFu, kr};
+    emit_range_regs(key, id, lay, sel, kr, A.K, out, sh, tid);
     if (tid == 0) {
       atomicAdd(&stats[kStFast], 1u);
       if (n > (uint32_t)A.lds_cap) atomicAdd(&stats[kStSpilled], 1u);
@@ -389,7 +389,7 @@ __global__ __launch_bounds__(kWG) void k_prefill_repair_score(PrefillArgs A) {
   }
   if (blockIdx.x >= kRepairFallback) return;
   uint32_t* own = A.scratch + ((int64_t)A.rslots + blockIdx.x) * A.rstride;
-  uint32_t* stats = A.ctrl + kStatsOff;
+  uint32_t* stats = stat_copy(A.ctrl, blockIdx.x);
 #pragma unroll 1
   for (uint32_t f = (uint32_t)A.rslots + blockIdx.x; f < n_fail; f += kRepairFallback) {
     const int t = A.fail_list[f];
@@ -465,7 +465,7 @@ __global__ __launch_bounds__(kWG) void k_prefill_repair_emit(PrefillArgs A) {
   const uint32_t n_slot = min(__atomic_load_n(&A.ctrl[kCtrlFail], __ATOMIC_RELAXED), (uint32_t)A.rslots);
   const int cmax = (A.N + kRepairChunk - 1) / kRepairChunk;
   const int64_t items = (int64_t)n_slot * cmax;
-  uint32_t* stats = A.ctrl + kStatsOff;
+  uint32_t* stats = stat_copy(A.ctrl, blockIdx.x);
 #pragma unroll 1
   for (int64_t i = blockIdx.x; i < items; i += gridDim.x) {
     const int f = (int)(i / cmax), c = (int)(i % cmax);
