@@ -24,7 +24,7 @@ static PrefillLayout prefill_layout(int32_t Q, int32_t N) {
   const size_t cand = (size_t)Q * nseg * (size_t)prefill_seg_cap(prefill_split(Q));
   L.skey = o; o = align256(o + sizeof(uint32_t) * cand);
   L.cidx = o; o = align256(o + sizeof(int32_t) * cand);
-  L.segn = o; o = align256(o + sizeof(uint32_t) * (size_t)Q * nseg);
+  L.segn = o; o = align256(o + 2 * sizeof(uint32_t) * (size_t)Q * nseg);
   L.scratch = o; o = align256(o + sizeof(uint32_t) * (size_t)repair_rows(Q, N) * (size_t)repair_stride(N));
   L.rhist = o; o = align256(o + sizeof(uint32_t) * (size_t)repair_slots(Q, N) * 4 * 256);
   L.rcnt = o; o = align256(o + sizeof(uint32_t) * (size_t)repair_slots(Q, N) * 2);

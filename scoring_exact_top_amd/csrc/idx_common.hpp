@@ -259,16 +259,21 @@ __device__ __forceinline__ void prepare_q2(QOp2& o, const uint8_t* q, const floa
   wave_sync();
 }
 
-// Prepare query row t (all 64 lanes; scratch = 8*128 bytes of LDS).
+// Prepare query row t (all 64 lanes; scratch = 8*128 bytes of LDS).  slot
+// (0 or 1) places the u terms where prepare_q2 puts them for the first or
+// the second row of a pair (u-block rows 0..7 or 8..15), so that a row
+// scored alone adds exactly the same partial sums in the same lanes as in
+// its pair and gets bit-identical scores.
 __device__ __forceinline__ void prepare_q(QOp& o, const uint8_t* q, const float* q_scale, const float* w,
-                                          int64_t t, uint32_t lane, uint8_t* scratch) {
+                                          int64_t t, uint32_t lane, uint8_t* scratch, int slot) {
   head_ops(o.a, o.wh, q, q_scale, w, t, lane);
   float sig[kUTerms];
   split_u(q, q_scale, w, t, lane, scratch, sig);
   wave_sync();
   const uint32_t g = lane >> 4, i = lane & 15;
-  if (i < (uint32_t)kUTerms) {
-    const uint32_t* src = reinterpret_cast<const uint32_t*>(scratch + i * kD + 32 * g);
+  const uint32_t term = i - (uint32_t)(kUTerms * slot);  // wraps above kUTerms for the other half
+  if (term < (uint32_t)kUTerms) {
+    const uint32_t* src = reinterpret_cast<const uint32_t*>(scratch + term * kD + 32 * g);
 #pragma unroll
     for (int k = 0; k < 8; ++k) o.au[k] = (int)src[k];
   } else {
@@ -280,7 +285,7 @@ __device__ __forceinline__ void prepare_q(QOp& o, const uint8_t* q, const float*
     const int row = 4 * (int)g + r;
     float sr = 0.f;
 #pragma unroll
-    for (int m = 0; m < kUTerms; ++m) sr = row == m ? sig[m] : sr;
+    for (int m = 0; m < kUTerms; ++m) sr = row == m + kUTerms * slot ? sig[m] : sr;
     o.sh[r] = 0.5f * sr;
   }
   wave_sync();
@@ -680,6 +685,29 @@ __device__ RangeSel range_select_regs(const uint32_t (&key)[M], const RegLayout&
     s = s > 8 ? s - 8 : 0;
   }
   return RangeSel{lo, lo + width, rem};
+}
+
+// Smallest key in [sel.lo, sel.last] (the smallest key selected by `sel`
+// when the boundary range is taken whole or holds one value).  All threads
+// of the workgroup call this.
+template <int M>
+__device__ uint32_t range_min_regs(const uint32_t (&key)[M], const RegLayout& lay, const RangeSel& sel,
+                                   SelShared& sh, int tid) {
+  const uint32_t lane = tid & 63;
+  const int wave = tid >> 6;
+  const uint32_t width = sel.last - sel.lo;
+  uint32_t mn = 0xFFFFFFFFu;
+#pragma unroll
+  for (int j = 0; j < M; ++j)
+    if ((uint32_t)j < lay.jmax && key[j] - sel.lo <= width) mn = min(mn, key[j]);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) mn = min(mn, (uint32_t)__shfl_xor((int)mn, off, 64));
+  if (lane == 0) sh.wsum[0][wave] = mn;
+  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) mn = min(mn, sh.wsum[0][w]);
+  __syncthreads();
+  return mn;
 }
 
 // Emit for range_select_regs: id[j] is the id of key[j].  Keys above `last`

@@ -86,7 +86,7 @@ __global__ __launch_bounds__(kWG) void k_decode_prep(DecodeArgs A) {
   }
   // the query operands, prepared once here for every workgroup of the split
   QOp qo;
-  prepare_q(qo, A.q, A.q_scale, A.w, b, lane, s_qprep[wave]);
+  prepare_q(qo, A.q, A.q_scale, A.w, b, lane, s_qprep[wave], 0);
   store_qop(qo, A.qop + (int64_t)b * kQOpWords * 64, lane);
   const SampleGeom sg = sample_geom(L, kDecCap);
   float tau = A.force_tau ? A.tau_value : -INFINITY;
@@ -261,7 +261,7 @@ __global__ __launch_bounds__(kWG) void k_decode_repair(DecodeArgs A) {
     const int L = A.seq_lens[b];
     const int32_t* pt = A.table + (int64_t)b * A.max_pages;
     QOp qo;
-    prepare_q(qo, A.q, A.q_scale, A.w, b, lane, s_qprep[tid >> 6]);
+    prepare_q(qo, A.q, A.q_scale, A.w, b, lane, s_qprep[tid >> 6], 0);
     repair_row(qo, make_keybuf(A.k, A.k_scale, (int64_t)A.num_pages * 64), TilePaged{pt}, IdPaged{pt}, 0, L,
                A.K, A.out + (int64_t)b * A.K, scratch, sh, tid);
     if (tid == 0) atomicAdd(&stats[kStRepaired], 1u);

@@ -118,7 +118,7 @@ struct PrefillArgs {
   uint8_t* kt;          // [ntiles][8][64][16] keys relaid in MFMA lane order
   uint32_t* cand_key;   // [Q][kWaves*S][seg_cap] candidate scores (FP32 bits)
   int32_t* cand_idx;    // [Q][kWaves*S][seg_cap] candidate key ids
-  uint32_t* segn;       // [Q][kWaves*S] entries per segment; bit 31: it overflowed
+  uint32_t* segn;       // [Q][kWaves*S][2]: entries stored, key of the largest dropped candidate (0: none)
   int32_t S, seg_cap, seg_eff;  // splits, segment stride, usable entries per segment
   int32_t lds_cap, spill_cap, cap_total;
   int32_t* fail_list;   // [Q]

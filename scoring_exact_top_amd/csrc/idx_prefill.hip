@@ -61,7 +61,7 @@ __global__ __launch_bounds__(kWG) void k_prefill_tau(PrefillArgs A) {
     return;
   }
   QOp qo;
-  prepare_q(qo, A.q, A.q_scale, A.w, t, lane, s_qprep[wave]);
+  prepare_q(qo, A.q, A.q_scale, A.w, t, lane, s_qprep[wave], t & 1);
   const KeyBuf kbuf = make_keybuf(A.k, A.k_scale, A.N);
   // Score the samples 64 at a time, the next tile's gather in flight.
   const auto key_of = [&](int i) { return s0 + kSampleOffset + sg.stride * min(i, sg.n - 1); };
@@ -132,6 +132,7 @@ __global__ __launch_bounds__(kWG, 2) void k_prefill_pair(PrefillArgs A) {
   const int tile_hi = (hi + 63) >> 6;
   const int voff = (int)lane * 16;
   uint32_t cnt[2] = {0u, 0u};  // candidates of each row found by this wave
+  float dmax[2] = {-INFINITY, -INFINITY};  // per lane: largest candidate dropped for lack of room
   // the (row, wave) workspace segments as buffer resources: a store past
   // seg_cap is dropped by the bounds check
   rsrc_t segk[2], segi[2];
@@ -161,7 +162,9 @@ __global__ __launch_bounds__(kWG, 2) void k_prefill_pair(PrefillArgs A) {
   // Tail of tile T: reduce-scatter, key scale, range and threshold tests,
   // append.  Branch-free: every lane stores, a taking lane at its slot in
   // the wave's segment (count + rank in the ballot), the others out of
-  // range, where the buffer bounds check drops the store.
+  // range, where the buffer bounds check drops the store.  Candidates past
+  // the segment's end are dropped the same way; the lanes that drop one
+  // remember the largest dropped score (a rare, wave-uniform branch).
   const auto tail = [&](int T, float ks) {
     const float sc[2] = {reduce_scatter4(q0[0], q0[1], q0[2], q0[3]) * ks,
                          reduce_scatter4(q1[0], q1[1], q1[2], q1[3]) * ks};
@@ -176,6 +179,10 @@ __global__ __launch_bounds__(kWG, 2) void k_prefill_pair(PrefillArgs A) {
       const int off = take ? (int)((cnt[r] + rank_in(ball)) * 4u) : 0x7FFFFFF0;
       __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sc[r]), segk[r], off, 0, 0);
       __builtin_amdgcn_raw_buffer_store_b32((uint32_t)my, segi[r], off, 0, 0);
+      if (cnt[r] + n > seg_cap) {
+        const bool dropped = take && cnt[r] + rank_in(ball) >= seg_cap;
+        dmax[r] = dropped ? fmaxf(dmax[r], sc[r]) : dmax[r];
+      }
       cnt[r] += n;
     }
   };
@@ -241,24 +248,38 @@ __global__ __launch_bounds__(kWG, 2) void k_prefill_pair(PrefillArgs A) {
     for (; T < tile_hi; T += nseg) tile_body(T);
   }
 
-  // publish this wave's segment counts (bit 31: the segment overflowed)
+  // publish this wave's segment: entries stored, and the order-preserving
+  // key of the largest dropped candidate (0: none dropped; a candidate is
+  // never NaN, so its key is nonzero)
 #pragma unroll
   for (int r = 0; r < 2; ++r) {
+    uint32_t dk = 0u;
+    if (cnt[r] > seg_cap) {
+      float m = dmax[r];
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+      dk = f2key(m);
+    }
     if (lane == 0 && t0 + r < A.Q)
-      A.segn[(int64_t)(t0 + r) * nseg + seg] = min(cnt[r], seg_cap) | (cnt[r] > seg_cap ? 0x80000000u : 0u);
+      *reinterpret_cast<uint2*>(A.segn + 2 * ((int64_t)(t0 + r) * nseg + seg)) = make_uint2(min(cnt[r], seg_cap), dk);
   }
 }
 
 // ------------------------------------------------------------------ select
 
-// One workgroup per row, after the main kernel: certify the row's candidate
-// list (its kWaves*S segments: at least K entries, none overflowed), load
-// it into registers (segment g of the row in threads [g*tps, (g+1)*tps),
-// tps = 256/nseg, each thread every tps-th entry), radix-select the K
-// largest and emit them; rows that fail go to the failure list.
+// One workgroup per row, after the main kernel.  The row's candidates (its
+// kWaves*S segments: segment g in threads [g*tps, (g+1)*tps), tps =
+// 256/nseg, each thread every tps-th entry) are loaded into registers and
+// the K largest selected.  Certificate ("3.2 Sampled threshold", made
+// exact for capacity drops): the selection is the row's exact top-K iff
+// there were at least K candidates and no dropped candidate scores above
+// the smallest selected one (a dropped candidate equal to it is a tie, any
+// of which may be taken).  So massive ties at the boundary need no repair.
+// Rows that fail go to the failure list.
 __global__ __launch_bounds__(kWG) void k_prefill_select(PrefillArgs A) {
   __shared__ SelShared sh;
   __shared__ uint32_t s_segn[kWaves * kMaxSplit];
+  __shared__ uint32_t s_ok;
   const int tid = threadIdx.x;
   const int t = blockIdx.x;
   uint32_t* stats = stat_copy(A.ctrl, blockIdx.x);
@@ -271,20 +292,28 @@ __global__ __launch_bounds__(kWG) void k_prefill_select(PrefillArgs A) {
     return;
   }
   const int nseg = kWaves * A.S;
-  if (tid < nseg) s_segn[tid] = A.segn[(int64_t)t * nseg + tid];
-  __syncthreads();
-  uint32_t n = 0u, over = 0u;
-  for (int g = 0; g < nseg; ++g) {
-    n += s_segn[g] & 0x7FFFFFFFu;
-    over |= s_segn[g] >> 31;
+  uint32_t dk = 0u;
+  if (tid < nseg) {
+    const uint2 e = *reinterpret_cast<const uint2*>(A.segn + 2 * ((int64_t)t * nseg + tid));
+    s_segn[tid] = e.x;
+    dk = e.y;
   }
+  // largest dropped key over the segments (all in wave 0: nseg <= 32)
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) dk = max(dk, (uint32_t)__shfl_xor((int)dk, o, 64));
+  if (tid == 0) sh.pad0 = dk;
+  __syncthreads();
+  const uint32_t drop = sh.pad0;
+  uint32_t n = 0u;
+  for (int g = 0; g < nseg; ++g) n += s_segn[g];
   const int L = re_t - rs_t;
   const int kr = min(A.K, L);
-  if (!over && n >= (uint32_t)kr) {
+  bool ok = n >= (uint32_t)kr;
+  if (ok) {
     const uint32_t tps = (uint32_t)(kWG / nseg);
     const uint32_t g = (uint32_t)tid / tps;
     const uint32_t first = g * (uint32_t)A.seg_cap;
-    const RegLayout lay{first + (uint32_t)tid % tps, tps, first + (s_segn[g] & 0x7FFFFFFFu), kSelRegs};
+    const RegLayout lay{first + (uint32_t)tid % tps, tps, first + s_segn[g], kSelRegs};
     const int64_t row = (int64_t)t * nseg * A.seg_cap;
     uint32_t key[kSelRegs];
     int32_t id[kSelRegs];
@@ -292,16 +321,19 @@ __global__ __launch_bounds__(kWG) void k_prefill_select(PrefillArgs A) {
                    [](uint32_t x) { return f2key(__uint_as_float(x)); });
     const RangeSel sel = (n > (uint32_t)kr) ? range_select_regs(key, lay, kr, sh, tid)
                                            : RangeSel{1u, 0xFFFFFFFFu, kr};
-    emit_range_regs(key, id, lay, sel, kr, A.K, out, sh, tid);
-    if (tid == 0) {
+    if (drop > sel.lo) ok = drop <= range_min_regs(key, lay, sel, sh, tid);
+    if (ok) emit_range_regs(key, id, lay, sel, kr, A.K, out, sh, tid);
+  }
+  if (tid == 0) {
+    if (ok) {
       atomicAdd(&stats[kStFast], 1u);
       if (n > (uint32_t)A.lds_cap) atomicAdd(&stats[kStSpilled], 1u);
       if (L <= A.K) atomicAdd(&stats[kStTrivial], 1u);
+    } else {
+      const uint32_t f = atomicAdd(&A.ctrl[kCtrlFail], 1u);
+      A.fail_list[f] = t;
+      atomicAdd(&stats[drop ? kStOver : kStUnder], 1u);
     }
-  } else if (tid == 0) {
-    const uint32_t f = atomicAdd(&A.ctrl[kCtrlFail], 1u);
-    A.fail_list[f] = t;
-    atomicAdd(&stats[over ? kStOver : kStUnder], 1u);
   }
 }
 
@@ -368,7 +400,7 @@ __global__ __launch_bounds__(kWG) void k_prefill_repair_score(PrefillArgs A) {
     if (tile_lo >= tile_hi) continue;
     sh.hist[tid] = 0u;
     QOp qo;
-    prepare_q(qo, A.q, A.q_scale, A.w, t, lane, s_qprep[wave]);
+    prepare_q(qo, A.q, A.q_scale, A.w, t, lane, s_qprep[wave], t & 1);
     __syncthreads();
     uint32_t* scratch = A.scratch + (int64_t)f * A.rstride;
 #pragma unroll 1
@@ -395,7 +427,7 @@ __global__ __launch_bounds__(kWG) void k_prefill_repair_score(PrefillArgs A) {
     const int t = A.fail_list[f];
     const int s0 = A.row_start[t], s1 = A.row_end[t];
     QOp qo;
-    prepare_q(qo, A.q, A.q_scale, A.w, t, lane, s_qprep[wave]);
+    prepare_q(qo, A.q, A.q_scale, A.w, t, lane, s_qprep[wave], t & 1);
     repair_row(qo, make_keybuf(A.k, A.k_scale, A.N), TileContig{}, IdIdentity{}, s0, s1, A.K,
                A.out + (int64_t)t * A.K, own, sh, tid);
     if (tid == 0) atomicAdd(&stats[kStRepaired], 1u);

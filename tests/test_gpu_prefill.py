@@ -88,6 +88,49 @@ def test_spill_area_is_merged():
     check_prefill_rows(case, r["out"], np.arange(case.Q))
 
 
+def _sample_tau(S_row, s0, s1):
+    """The threshold the sampler must produce from the main kernel's own
+    scores: r-th largest score at positions s0 + OFFSET + STRIDE*i inside the
+    row (the sampling reading of the "3.2 Sampled threshold" section, as
+    documented in include/idx_topk.h, for rows of at most 2048 samples)."""
+    stride, offset, target = synth.SAMPLE_STRIDE, synth.SAMPLE_OFFSET, 4096
+    L = s1 - s0
+    n = -(-(L - offset) // stride)
+    assert n <= 2048
+    r = min(max(-(-(n * target) // L), 1), n)
+    v = np.sort(S_row[s0 + offset + stride * np.arange(n)])[::-1]
+    return v[r - 1]
+
+
+def test_sampler_matches_main_scores_bit_for_bit(e4m3):
+    """Even and odd rows (first and second row of a main-kernel pair) get the
+    same scores from the sampler as from the main kernel, bit for bit, so a
+    threshold equal to a sampled score keeps every copy of that score."""
+    case = synth.random_case("sampled", 7, 24000, seed=28, K=2048, min_len=9000, max_len=24000)
+    log("case", case.name)
+    r = run_prefill(case, scores=True)
+    for t in range(case.Q):
+        s0, s1 = int(case.row_start[t]), int(case.row_end[t])
+        want = np.float32(_sample_tau(r["scores"][t], s0, s1))
+        assert r["tau"][t].view(np.uint32) == want.view(np.uint32), (t, r["tau"][t], want)
+    check_prefill_rows(case, r["out"], np.arange(case.Q), gpu_scores=r["scores"], e4m3=e4m3)
+
+
+def test_massive_ties_take_the_fast_path(e4m3):
+    """Rows over 16 distinct keys: the threshold is the top score, held by
+    about 10K keys, far more than the segments hold (capacity cut to 4096).
+    The dropped candidates all tie with the smallest selected score, so the
+    certificate accepts every row without repair."""
+    pos = np.arange(163840 - 8, 163840, dtype=np.int64)
+    case = synth.causal_case("ties_fast", 8, 163840, seed=29, key_mode="ties16", positions=pos)
+    log("case", case.name)
+    r = run_prefill(case, scores=True, lds_cap=2048, spill_cap=2048)
+    st = r["stats"]
+    log("stats", st)
+    assert st["fast_ok"] == case.Q and st["repaired"] == 0, st
+    check_prefill_rows(case, r["out"], np.arange(case.Q), gpu_scores=r["scores"], e4m3=e4m3)
+
+
 def test_invalid_ranges_give_minus_one():
     case = synth.random_case("badrange", 6, 1000, seed=26, K=64, min_len=10)
     case.row_start[1], case.row_end[1] = 50, 40        # start > end
@@ -142,3 +185,6 @@ def test_adversarial_subcalls_sampled_rows():
         log(case.name, rep)
         if case.name == "adversarial_decoy":
             assert r["stats"]["underflow"] > 0 and r["stats"]["repaired"] > 0
+        if case.name == "adversarial_ties16":
+            # ties at the threshold are certified without repair
+            assert r["stats"]["fast_ok"] >= 0.9 * case.Q, r["stats"]
