@@ -11,11 +11,14 @@
  * [row_start[t], row_end[t]), with q[t,j] = e4m3(q8[t,j,:]) * q_scale[t,j] and
  * k[s] = e4m3(k8[s,:]) * k_scale[s] (FP8 operands "each with scales"), and the
  * output is, per row, the K ids with the largest I, in no particular order.
- * Among equal scores any valid id may be returned (same section: ties may
- * resolve to any valid index).  The result is exact: a sampled threshold only
- * decides whether the fast path's candidate set certifies the answer
- * ("3.2 Sampled threshold: turn maintenance into filtering"); rows where it
- * does not are recomputed by an exact repair path.
+ * The pages allow any valid id among equal scores (same section); this
+ * library resolves a tie at the K-th score toward the lowest key ids (decode:
+ * the lowest logical positions), on every path, so the selected set is a
+ * function of the inputs (the order inside a row is not).  The result is
+ * exact: a sampled threshold only decides whether the fast path's candidate
+ * set certifies the answer ("3.2 Sampled threshold: turn maintenance into
+ * filtering"); rows where it does not are recomputed by an exact repair
+ * path.
  *
  * The paged decode variant follows the contest report page (arXiv 2608.14560), "DSA TopK
  * Indexer": one FP8 query per sequence, a paged FP8 key cache with per-token
@@ -76,7 +79,9 @@ typedef struct {
   uint32_t rows;       /* rows (or sequences) processed                         */
   uint32_t fast_ok;    /* rows certified by the sampled-threshold fast path     */
   uint32_t underflow;  /* fast path failed: fewer than K candidates             */
-  uint32_t overflow;   /* fast path failed: candidates exceeded capacity        */
+  uint32_t overflow;   /* fast path failed: a candidate dropped for lack of
+                          capacity scores above the selection (or ties with
+                          it below a selected tied id)                          */
   uint32_t spilled;    /* fast-path rows with more candidates than the on-chip
                           share lds_cap (informational: the prefill main kernel
                           writes candidates straight to the workspace)          */

@@ -137,6 +137,27 @@ def check_debug_bitexact(out_row, S_row, start, end, K, where=""):
         _fail("%s: wrong number taken at theta_S" % where)
 
 
+def check_debug_canonical(out_row, S_row, start, end, K, where=""):
+    """The library's tie rule on its own scores: the selected set is exactly
+    {S > theta_S} plus the (K - #(S > theta_S)) lowest ids with S == theta_S,
+    theta_S the K-th largest S in the valid range (-0 and +0 equal)."""
+    check_structure(out_row, start, end, K, where)
+    kk = min(K, end - start)
+    if kk == 0:
+        return
+    S = np.asarray(S_row, dtype=np.float32).astype(np.float64) + 0.0
+    ids = np.arange(start, end)
+    valid = S[start:end]
+    theta = np.sort(valid)[::-1][kk - 1]
+    above = ids[valid > theta]
+    tied = ids[valid == theta]          # ascending ids
+    want = np.concatenate([above, tied[: kk - above.size]])
+    got = np.sort(np.asarray(out_row[:kk], dtype=np.int64))
+    if not np.array_equal(got, np.sort(want)):
+        _fail("%s: selection differs from the lowest-id tie rule (%d ids differ)"
+              % (where, int(np.setxor1d(got, want).size)))
+
+
 def score_bound(q8, q_scale, k8, k_scale, w, t, ids, e4m3_table):
     """B[t,s] for the cancellation clause (numpy, fp64)."""
     qd = np.abs(e4m3_table[q8[t]])                       # [64,128]

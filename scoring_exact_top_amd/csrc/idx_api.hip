@@ -11,7 +11,7 @@ static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 static inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 struct PrefillLayout {
-  size_t ctrl, tau, fail, skey, cidx, segn, scratch, rhist, rcnt, kt, total;
+  size_t ctrl, tau, fail, skey, cidx, segn, scratch, rhist, rcnt, reqc, kt, total;
 };
 
 static PrefillLayout prefill_layout(int32_t Q, int32_t N) {
@@ -24,10 +24,11 @@ static PrefillLayout prefill_layout(int32_t Q, int32_t N) {
   const size_t cand = (size_t)Q * nseg * (size_t)prefill_seg_cap(prefill_split(Q));
   L.skey = o; o = align256(o + sizeof(uint32_t) * cand);
   L.cidx = o; o = align256(o + sizeof(int32_t) * cand);
-  L.segn = o; o = align256(o + 2 * sizeof(uint32_t) * (size_t)Q * nseg);
+  L.segn = o; o = align256(o + 4 * sizeof(uint32_t) * (size_t)Q * nseg);
   L.scratch = o; o = align256(o + sizeof(uint32_t) * (size_t)repair_rows(Q, N) * (size_t)repair_stride(N));
   L.rhist = o; o = align256(o + sizeof(uint32_t) * (size_t)repair_slots(Q, N) * 4 * 256);
   L.rcnt = o; o = align256(o + sizeof(uint32_t) * (size_t)repair_slots(Q, N) * 2);
+  L.reqc = o; o = align256(o + sizeof(uint32_t) * (size_t)repair_slots(Q, N) * (size_t)((N + kRepairChunk - 1) / kRepairChunk));
   L.kt = o; o = align256(o + (size_t)((N + 63) / 64) * 64 * 128);
   L.total = o;
   return L;
@@ -64,6 +65,7 @@ static int prefill_common(const uint8_t* q, const float* q_scale, const uint8_t*
   A.scratch = reinterpret_cast<uint32_t*>(ws + L.scratch);
   A.rhist = reinterpret_cast<uint32_t*>(ws + L.rhist);
   A.rcnt = reinterpret_cast<uint32_t*>(ws + L.rcnt);
+  A.reqc = reinterpret_cast<uint32_t*>(ws + L.reqc);
   A.rslots = repair_slots(Q, N);
   A.rstride = repair_stride(N);
   A.kt = reinterpret_cast<uint8_t*>(ws + L.kt);

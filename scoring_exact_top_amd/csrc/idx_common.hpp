@@ -481,10 +481,12 @@ struct SelShared {
 };
 
 // Result of the digit passes: every key with (key & mask) > prefix is in the
-// top-K; `rem` more are taken among keys with (key & mask) == prefix.
+// top-K; `rem` more are taken among the `group` keys with (key & mask) ==
+// prefix.  rem < group only where the group is one value (all digits
+// fixed): a tie at the K-th score, resolved toward the lowest positions.
 struct SelResult {
   uint32_t prefix, mask;
-  int rem;
+  int rem, group;
 };
 
 // From a complete 256-bin histogram in sh.hist, find the bucket that holds
@@ -527,6 +529,7 @@ template <typename Src>
 __device__ SelResult radix_select(const Src& src, int n, int rem, SelShared& sh, int tid,
                                   bool first_hist_ready, bool allow_early) {
   uint32_t prefix = 0, mask = 0;
+  int group = n;
 #pragma unroll 1
   for (int shift = 24; shift >= 0; shift -= 8) {
     if (!(shift == 24 && first_hist_ready)) {
@@ -547,19 +550,48 @@ __device__ SelResult radix_select(const Src& src, int n, int rem, SelShared& sh,
     prefix |= b << shift;
     mask |= 0xFFu << shift;
     rem -= (int)above;
+    group = (int)inb;
     if (allow_early && (int)inb == rem) break;
   }
-  return SelResult{prefix, mask, rem};
+  return SelResult{prefix, mask, rem, group};
+}
+
+// Exclusive prefix sum over the workgroup of one per-thread count, in
+// thread order; also returns the total.  All threads call this.
+__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t a, SelShared& sh, int tid, uint32_t& total) {
+  const uint32_t lane = tid & 63;
+  const int wave = tid >> 6;
+  uint32_t inc = a;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t x = (uint32_t)__shfl_up((int)inc, off, 64);
+    if (lane >= (uint32_t)off) inc += x;
+  }
+  if (lane == 63) sh.wsum[0][wave] = inc;
+  __syncthreads();
+  uint32_t before = 0u;
+  total = 0u;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    const uint32_t c = sh.wsum[0][w];
+    before += w < wave ? c : 0u;
+    total += c;
+  }
+  __syncthreads();
+  return before + inc - a;
 }
 
 // Write the selection into out[0..kr): ids of keys above the boundary first,
-// then `rem` ids from the boundary group, then -1 up to K.
+// then `rem` ids from the boundary group (the lowest positions first where
+// the group is a tie larger than rem), then -1 up to K.
 template <typename Src>
 __device__ void emit_selection(const Src& src, int n, const SelResult& sel, int kr, int K,
                                int32_t* out, SelShared& sh, int tid) {
   if (tid == 0) { sh.gt_count = 0; sh.eq_count = 0; }
   __syncthreads();
-  const int gt_base = 0, eq_base = kr - sel.rem;
+  const int eq_base = kr - sel.rem;
+  const bool ordered = sel.rem < sel.group;  // a tie: take its lowest positions
+  uint32_t eq_done = 0u;                     // group members before this pass (ordered)
   for (int base = 0; base < n; base += kWG) {
     const int i = base + tid;
     const bool v = i < n;
@@ -568,9 +600,16 @@ __device__ void emit_selection(const Src& src, int n, const SelResult& sel, int 
     const bool gt = v && mk > sel.prefix;
     const bool eq = v && mk == sel.prefix;
     const uint32_t pg = reserve(&sh.gt_count, gt);
-    if (gt) out[gt_base + pg] = src.id(i);
-    const uint32_t pe = reserve(&sh.eq_count, eq);
-    if (eq && (int)pe < sel.rem) out[eq_base + pe] = src.id(i);
+    if (gt) out[pg] = src.id(i);
+    if (!ordered) {
+      const uint32_t pe = reserve(&sh.eq_count, eq);
+      if (eq && (int)pe < sel.rem) out[eq_base + pe] = src.id(i);
+    } else if (eq_done < (uint32_t)sel.rem) {  // workgroup-uniform
+      uint32_t tot;
+      const uint32_t pe = eq_done + block_exclusive_scan(eq ? 1u : 0u, sh, tid, tot);
+      if (eq && pe < (uint32_t)sel.rem) out[eq_base + pe] = src.id(i);
+      eq_done += tot;
+    }
   }
   for (int i = kr + tid; i < K; i += kWG) out[i] = -1;
 }
@@ -612,17 +651,19 @@ __device__ __forceinline__ void load_list_regs(uint32_t (&key)[M], int32_t (&id)
 }
 
 // Selection over keys held in registers: every key above `last` is in the
-// top-K, and the first `rem` keys in [lo, last] complete it (any of them are
-// correct where they all share one value).
+// top-K, and `rem` of the `group` keys in [lo, last] complete it.  rem <
+// group only where lo == last (a tie at the K-th score).
 struct RangeSel {
   uint32_t lo, last;
-  int rem;
+  int rem, group;
 };
 
-// Register lists for range_select_regs / emit_range_regs hold nonzero keys,
-// with 0 in unused slots (load_list_regs stores 0 there).  Candidate keys
-// qualify: a candidate passed score >= tau, which no NaN does, and only a
-// NaN maps to key 0.  So no per-slot validity mask is kept.
+// Register lists for the functions below hold nonzero keys, with 0 in
+// unused slots (load_list_regs stores 0 there).  Candidate keys qualify: a
+// candidate passed score >= tau, which no NaN does, and only a NaN maps to
+// key 0.  So no per-slot validity mask is kept.  A list is read through a
+// functor kf(j) returning slot j's key, so that derived keys (the tie-break
+// below) need no second register array.
 
 // The K-th-largest search ("3.2 Sampled threshold", select step) with digits
 // taken relative to the list's own range: the first pass cuts [min, max]
@@ -632,17 +673,17 @@ struct RangeSel {
 // Each further pass splits the chosen bin 256 ways; a bin of width one ends
 // the search.  Requires 1 <= rem < number of keys.  All threads of the
 // workgroup call this.
-template <int M>
-__device__ RangeSel range_select_regs(const uint32_t (&key)[M], const RegLayout& lay, int rem, SelShared& sh,
-                                      int tid) {
+template <int M, class KF>
+__device__ RangeSel range_select_regs(const KF& kf, const RegLayout& lay, int rem, SelShared& sh, int tid) {
   const uint32_t lane = tid & 63;
   const int wave = tid >> 6;
   uint32_t mn = 0xFFFFFFFFu, mx = 0u;
 #pragma unroll
   for (int j = 0; j < M; ++j) {
     if ((uint32_t)j < lay.jmax) {
-      mn = min(mn, key[j] ? key[j] : 0xFFFFFFFFu);
-      mx = max(mx, key[j]);
+      const uint32_t k = kf(j);
+      mn = min(mn, k ? k : 0xFFFFFFFFu);
+      mx = max(mx, k);
     }
   }
 #pragma unroll
@@ -661,14 +702,15 @@ __device__ RangeSel range_select_regs(const uint32_t (&key)[M], const RegLayout&
   const int bits = span ? 32 - __clz((int)span) : 0;
   int s = bits > 8 ? bits - 8 : 0;
   uint32_t lo = mn, width = span;  // the range is [lo, lo + width]
+  int group;
 #pragma unroll 1
   while (true) {
     sh.hist[tid] = 0u;  // kWG == 256 bins
     __syncthreads();
 #pragma unroll
     for (int j = 0; j < M; ++j) {
-      if ((uint32_t)j < lay.jmax) {  // wave-uniform guard; keeps key[] in registers
-        const uint32_t d = key[j] - lo;  // key 0 wraps above any width (lo >= 1)
+      if ((uint32_t)j < lay.jmax) {  // wave-uniform guard; keeps the keys in registers
+        const uint32_t d = kf(j) - lo;  // key 0 wraps above any width (lo >= 1)
         if (d <= width) atomicAdd(&sh.hist[d >> s], 1u);
       }
     }
@@ -678,28 +720,29 @@ __device__ RangeSel range_select_regs(const uint32_t (&key)[M], const RegLayout&
     const uint32_t b = sh.bucket, above = sh.above, inb = sh.inbucket;
     __syncthreads();
     rem -= (int)above;
+    group = (int)inb;
     const uint32_t off = b << s;
     lo += off;
     width = min(width - off, (1u << s) - 1u);  // s <= 24
     if ((int)inb == rem || s == 0) break;
     s = s > 8 ? s - 8 : 0;
   }
-  return RangeSel{lo, lo + width, rem};
+  return RangeSel{lo, lo + width, rem, group};
 }
 
-// Smallest key in [sel.lo, sel.last] (the smallest key selected by `sel`
-// when the boundary range is taken whole or holds one value).  All threads
+// Smallest key in [sel.lo, sel.last]: the smallest key selected by `sel`
+// when the boundary range is taken whole or holds one value.  All threads
 // of the workgroup call this.
-template <int M>
-__device__ uint32_t range_min_regs(const uint32_t (&key)[M], const RegLayout& lay, const RangeSel& sel,
-                                   SelShared& sh, int tid) {
+template <int M, class KF>
+__device__ uint32_t range_min_regs(const KF& kf, const RegLayout& lay, const RangeSel& sel, SelShared& sh,
+                                   int tid) {
   const uint32_t lane = tid & 63;
   const int wave = tid >> 6;
   const uint32_t width = sel.last - sel.lo;
   uint32_t mn = 0xFFFFFFFFu;
 #pragma unroll
   for (int j = 0; j < M; ++j)
-    if ((uint32_t)j < lay.jmax && key[j] - sel.lo <= width) mn = min(mn, key[j]);
+    if ((uint32_t)j < lay.jmax && kf(j) - sel.lo <= width) mn = min(mn, kf(j));
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) mn = min(mn, (uint32_t)__shfl_xor((int)mn, off, 64));
   if (lane == 0) sh.wsum[0][wave] = mn;
@@ -710,27 +753,43 @@ __device__ uint32_t range_min_regs(const uint32_t (&key)[M], const RegLayout& la
   return mn;
 }
 
-// Emit for range_select_regs: id[j] is the id of key[j].  Keys above `last`
-// fill out[0, kr - rem), the first `rem` keys in [lo, last] fill
-// out[kr - rem, kr), -1 up to K.  Positions run over (slot j, wave, lane) in
-// that order, so a wave's winners in one slot are stored to consecutive
-// addresses and the result does not depend on timing.  At most 64 slots
-// per thread and 65535 keys per list (two 16-bit counts share a word).
-// Same key convention as range_select_regs (lo >= 1).
+// Which boundary keys to take: all of [lo, last] when rem == group, else
+// (a tie at one value) the rem with the lowest ids, found by a second
+// range select over ~id of the tied keys (ids are >= 0 and distinct, so
+// ~id is nonzero and the select ends with the rem largest ~id taken whole).
+// Returns the smallest ~id taken (0: no tie-break, every boundary key).
 template <int M>
+__device__ uint32_t tie_bound_regs(const uint32_t (&key)[M], const int32_t (&id)[M], const RegLayout& lay,
+                                   const RangeSel& sel, SelShared& sh, int tid) {
+  if (sel.rem >= sel.group) return 0u;
+  const uint32_t v = sel.lo;
+  const auto tk = [&](int j) { return key[j] == v ? ~(uint32_t)id[j] : 0u; };
+  return range_select_regs<M>(tk, lay, sel.rem, sh, tid).lo;
+}
+
+// Emit for range_select_regs: keys above `last` fill out[0, kr - rem), the
+// boundary keys taken (those in [lo, last] with ~id >= idlo) fill
+// out[kr - rem, kr), -1 up to K; idmap(id[j]) is written.  Positions run
+// over (slot j, wave, lane) in that order, so a wave's winners in one slot
+// are stored to consecutive addresses and the result does not depend on
+// timing.  At most 64 slots per thread and 65535 keys per list (two 16-bit
+// counts share a word).
+template <int M, class IdMap>
 __device__ void emit_range_regs(const uint32_t (&key)[M], const int32_t (&id)[M], const RegLayout& lay,
-                                const RangeSel& sel, int kr, int K, int32_t* out, SelShared& sh, int tid) {
+                                const RangeSel& sel, uint32_t idlo, int kr, int K, int32_t* out,
+                                const IdMap& idmap, SelShared& sh, int tid) {
   static_assert(M <= 64, "one lane per register slot");
   const uint32_t lane = tid & 63;
   const int wave = tid >> 6;
   const uint32_t width = sel.last - sel.lo;
+  const auto gt = [&](int j) { return key[j] > sel.last; };
+  const auto eq = [&](int j) { return key[j] - sel.lo <= width && ~(uint32_t)id[j] >= idlo; };
   // lane j: this wave's winners in slot j (above | boundary << 16)
   uint32_t mine = 0u;
 #pragma unroll
   for (int j = 0; j < M; ++j) {
     if ((uint32_t)j < lay.jmax) {
-      const uint32_t c = (uint32_t)__popcll(__ballot(key[j] > sel.last)) |
-                         (uint32_t)__popcll(__ballot(key[j] - sel.lo <= width)) << 16;
+      const uint32_t c = (uint32_t)__popcll(__ballot(gt(j))) | (uint32_t)__popcll(__ballot(eq(j))) << 16;
       mine = lane == (uint32_t)j ? c : mine;
     }
   }
@@ -755,11 +814,11 @@ __device__ void emit_range_regs(const uint32_t (&key)[M], const int32_t (&id)[M]
   for (int j = 0; j < M; ++j) {
     if ((uint32_t)j < lay.jmax) {
       const uint32_t bj = (uint32_t)__builtin_amdgcn_readlane((int)base, j);
-      const bool g = key[j] > sel.last, e = key[j] - sel.lo <= width;
+      const bool g = gt(j), e = eq(j);
       const uint64_t bg = __ballot(g), be = __ballot(e);
-      if (g) out[(bj & 0xFFFFu) + rank_in(bg)] = id[j];
+      if (g) out[(bj & 0xFFFFu) + rank_in(bg)] = idmap(id[j]);
       const uint32_t pe = (bj >> 16) + rank_in(be);
-      if (e && pe < (uint32_t)sel.rem) out[eq_base + pe] = id[j];
+      if (e && pe < (uint32_t)sel.rem) out[eq_base + pe] = idmap(id[j]);
     }
   }
   for (int i = kr + tid; i < K; i += kWG) out[i] = -1;
@@ -776,6 +835,7 @@ template <typename Src>
 __device__ SelResult wave_radix_select(const Src& src, int n, int rem, uint32_t* hist, uint32_t lane,
                                        bool allow_early) {
   uint32_t prefix = 0, mask = 0;
+  int group = n;
 #pragma unroll 1
   for (int shift = 24; shift >= 0; shift -= 8) {
 #pragma unroll
@@ -812,34 +872,11 @@ __device__ SelResult wave_radix_select(const Src& src, int n, int rem, uint32_t*
     prefix |= bb << shift;
     mask |= 0xFFu << shift;
     rem -= (int)above;
+    group = (int)inb;
     wave_sync();  // histogram reads done before the next pass clears it
     if (allow_early && (int)inb == rem) break;
   }
-  return SelResult{prefix, mask, rem};
-}
-
-// Wave-level emit: same output layout as emit_selection.
-template <typename Src>
-__device__ void wave_emit(const Src& src, int n, const SelResult& sel, int kr, int K, int32_t* out,
-                          uint32_t lane) {
-  uint32_t gt_cnt = 0, eq_cnt = 0;
-  const int eq_base = kr - sel.rem;
-  for (int base = 0; base < n; base += 64) {
-    const int i = base + (int)lane;
-    const bool v = i < n;
-    const uint32_t key = v ? src.key(i) : 0u;
-    const uint32_t mk = key & sel.mask;
-    const bool gt = v && mk > sel.prefix;
-    const bool eq = v && mk == sel.prefix;
-    const uint64_t bg = __ballot(gt);
-    if (gt) out[gt_cnt + rank_in(bg)] = src.id(i);
-    gt_cnt += (uint32_t)__popcll(bg);
-    const uint64_t be = __ballot(eq);
-    const uint32_t pe = eq_cnt + rank_in(be);
-    if (eq && (int)pe < sel.rem) out[eq_base + pe] = src.id(i);
-    eq_cnt += (uint32_t)__popcll(be);
-  }
-  for (int i = kr + (int)lane; i < K; i += 64) out[i] = -1;
+  return SelResult{prefix, mask, rem, group};
 }
 
 }  // namespace idxk

@@ -40,10 +40,11 @@ struct DecodeArgs {
   uint32_t* ctrl;
   float* tau;            // [B]
   int32_t* status;       // [B]: 0 score, 1 remapped, 2 invalid
-  uint32_t* cnt;         // [B]
+  uint32_t* cnt;         // [B] candidates appended (may exceed kDecCap)
+  uint32_t* drop;        // [B][2]: key of the largest dropped candidate (0: none), lowest dropped position
   int32_t* fail_list;    // [B]
   uint32_t* cand_key;    // [B][kDecCap] candidate scores (FP32 bits)
-  int32_t* cand_idx;     // [B][kDecCap] candidate physical slots
+  int32_t* cand_idx;     // [B][kDecCap] candidate logical positions
   uint32_t* scratch;     // [repair_grid(B)][max_pages*64]
   uint32_t* qop;         // [B][kQOpWords][64] prepared query operands
   int32_t force_tau;     // debug: every scored sequence uses tau_value
@@ -62,7 +63,11 @@ __global__ __launch_bounds__(kWG) void k_decode_prep(DecodeArgs A) {
   if (blockIdx.x == 0) clear_ctrl(A.ctrl, tid);
   const int b = kWaves * blockIdx.x + wave;
   if (b >= A.B) return;
-  if (lane == 0) A.cnt[b] = 0u;
+  if (lane == 0) {
+    A.cnt[b] = 0u;
+    A.drop[2 * b] = 0u;
+    A.drop[2 * b + 1] = 0xFFFFFFFFu;
+  }
   const int L = A.seq_lens[b];
   const int32_t* pt = A.table + (int64_t)b * A.max_pages;
   int32_t* out = A.out + (int64_t)b * A.K;
@@ -138,14 +143,24 @@ __global__ __launch_bounds__(kWG) void k_decode_split(DecodeArgs A) {
   uint32_t* ckey = A.cand_key + (int64_t)b * kDecCap;
   int32_t* cidx = A.cand_idx + (int64_t)b * kDecCap;
   uint32_t staged = 0u;
-  // copy this wave's stage to [base, base + staged) of the list
+  // copy this wave's stage to [base, base + staged) of the list; entries
+  // past the capacity are dropped, and the sequence keeps the largest
+  // dropped key and the lowest dropped position (for the certificate)
   const auto copy_out = [&](uint32_t base) {
+    uint32_t dk = 0u, dp = 0xFFFFFFFFu;
     for (uint32_t i = lane; i < staged; i += 64) {
+      const uint2 e = s_stage[wave][i];
       if (base + i < (uint32_t)kDecCap) {
-        const uint2 e = s_stage[wave][i];
         ckey[base + i] = e.x;
         cidx[base + i] = (int32_t)e.y;
+      } else {
+        dk = max(dk, f2key(__uint_as_float(e.x)));
+        dp = min(dp, e.y);
       }
+    }
+    if (dk) {
+      atomicMax(&A.drop[2 * b], dk);
+      atomicMin(&A.drop[2 * b + 1], dp);
     }
   };
   const KeyBuf kbuf = make_keybuf(A.k, A.k_scale, (int64_t)A.num_pages * 64);
@@ -188,7 +203,7 @@ __global__ __launch_bounds__(kWG) void k_decode_split(DecodeArgs A) {
           staged = 0u;
           wave_sync();
         }
-        if (take) s_stage[wave][staged + rank_in(ball)] = make_uint2(__float_as_uint(sc), (uint32_t)(base0 + lane));
+        if (take) s_stage[wave][staged + rank_in(ball)] = make_uint2(__float_as_uint(sc), (uint32_t)my);
         staged += n;
       }
       t0 = t1;
@@ -212,13 +227,18 @@ __global__ __launch_bounds__(kWG) void k_decode_split(DecodeArgs A) {
   copy_out(s_base[wave]);
 }
 
-// One workgroup per sequence, after every chunk is in: certify the candidate
-// list, load it into registers (32 keys per thread), select and emit, or put
-// the sequence on the failure list.  Also counts the remapped and invalid
-// sequences.
+// One workgroup per sequence, after every chunk is in: load the candidate
+// list into registers (32 keys per thread), select the K largest (ties at
+// the K-th score to the lowest logical positions) and emit their physical
+// slots, or put the sequence on the failure list.  The certificate is the
+// prefill one: at least K candidates kept, no dropped candidate above the
+// smallest selected score theta, and where one equals theta, the tied
+// positions taken all below the lowest dropped position.  Also counts the
+// remapped and invalid sequences.
 __global__ __launch_bounds__(kWG) void k_decode_select(DecodeArgs A) {
   __shared__ SelShared sh;
   const int tid = threadIdx.x;
+  const uint32_t lane = tid & 63;
   const int b = blockIdx.x;
   uint32_t* stats = stat_copy(A.ctrl, blockIdx.x);
   const int st = A.status[b];
@@ -227,23 +247,51 @@ __global__ __launch_bounds__(kWG) void k_decode_select(DecodeArgs A) {
     if (tid == 0) atomicAdd(&stats[st == 1 ? kStTrivial : kStBad], 1u);
     return;
   }
-  const uint32_t n = A.cnt[b];
+  const uint32_t n = min(A.cnt[b], (uint32_t)kDecCap);
+  const uint32_t drop = A.drop[2 * b], first_drop = A.drop[2 * b + 1];
   const int kr = A.K;  // L > K on this path
-  if (n >= (uint32_t)kr && n <= (uint32_t)kDecCap) {
+  bool ok = n >= (uint32_t)kr;
+  if (ok) {
     const uint32_t* ckey = A.cand_key + (int64_t)b * kDecCap;
     const int32_t* cidx = A.cand_idx + (int64_t)b * kDecCap;
     const RegLayout lay = block_list_layout(n, (uint32_t)tid);
     uint32_t key[kDecCap / kWG];
     int32_t id[kDecCap / kWG];
+    constexpr int M = kDecCap / kWG;
     load_list_regs(key, id, ckey, cidx, n, lay, [](uint32_t x) { return f2key(__uint_as_float(x)); });
-    const RangeSel sel = (n > (uint32_t)kr) ? range_select_regs(key, lay, kr, sh, tid)
-                                           : RangeSel{1u, 0xFFFFFFFFu, kr};
-    emit_range_regs(key, id, lay, sel, kr, A.K, A.out + (int64_t)b * A.K, sh, tid);
-    if (tid == 0) atomicAdd(&stats[kStFast], 1u);
-  } else if (tid == 0) {
-    const uint32_t f = atomicAdd(&A.ctrl[kCtrlFail], 1u);
-    A.fail_list[f] = b;
-    atomicAdd(&stats[n < (uint32_t)kr ? kStUnder : kStOver], 1u);
+    const auto kf = [&](int j) { return key[j]; };
+    const RangeSel sel = (n > (uint32_t)kr) ? range_select_regs<M>(kf, lay, kr, sh, tid)
+                                           : RangeSel{1u, 0xFFFFFFFFu, kr, (int)n};
+    const uint32_t idlo = tie_bound_regs(key, id, lay, sel, sh, tid);
+    if (drop >= sel.lo) {
+      const uint32_t theta = range_min_regs<M>(kf, lay, sel, sh, tid);
+      ok = drop <= theta;
+      if (drop == theta) {  // tied keys were dropped: the taken ones must precede them
+        uint32_t mn = 0xFFFFFFFFu;  // smallest ~position taken at theta
+#pragma unroll
+        for (int j = 0; j < M; ++j)
+          if ((uint32_t)j < lay.jmax && key[j] == theta && ~(uint32_t)id[j] >= idlo) mn = min(mn, ~(uint32_t)id[j]);
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) mn = min(mn, (uint32_t)__shfl_xor((int)mn, o, 64));
+        if (lane == 0) sh.wsum[0][tid >> 6] = mn;
+        __syncthreads();
+        mn = min(min(sh.wsum[0][0], sh.wsum[0][1]), min(sh.wsum[0][2], sh.wsum[0][3]));
+        __syncthreads();
+        ok = ok && ~mn < first_drop;
+      }
+    }
+    if (ok)
+      emit_range_regs(key, id, lay, sel, idlo, kr, A.K, A.out + (int64_t)b * A.K,
+                      IdPaged{A.table + (int64_t)b * A.max_pages}, sh, tid);
+  }
+  if (tid == 0) {
+    if (ok) {
+      atomicAdd(&stats[kStFast], 1u);
+    } else {
+      const uint32_t f = atomicAdd(&A.ctrl[kCtrlFail], 1u);
+      A.fail_list[f] = b;
+      atomicAdd(&stats[drop ? kStOver : kStUnder], 1u);
+    }
   }
 }
 
@@ -274,7 +322,7 @@ __global__ __launch_bounds__(kWG) void k_decode_repair(DecodeArgs A) {
 static inline size_t a256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct DecodeLayout {
-  size_t ctrl, tau, status, cnt, fail, ckey, cidx, scratch, qop, total;
+  size_t ctrl, tau, status, cnt, drop, fail, ckey, cidx, scratch, qop, total;
 };
 
 static DecodeLayout decode_layout(int32_t B, int32_t max_pages) {
@@ -285,6 +333,7 @@ static DecodeLayout decode_layout(int32_t B, int32_t max_pages) {
   L.tau = o; o = a256(o + 4 * b);
   L.status = o; o = a256(o + 4 * b);
   L.cnt = o; o = a256(o + 4 * b);
+  L.drop = o; o = a256(o + 8 * b);
   L.fail = o; o = a256(o + 4 * b);
   L.ckey = o; o = a256(o + 4 * b * kDecCap);
   L.cidx = o; o = a256(o + 4 * b * kDecCap);
@@ -335,6 +384,7 @@ int decode_paged(const uint8_t* q, const float* q_scale, const uint8_t* k_cache,
   A.tau = reinterpret_cast<float*>(ws + L.tau);
   A.status = reinterpret_cast<int32_t*>(ws + L.status);
   A.cnt = reinterpret_cast<uint32_t*>(ws + L.cnt);
+  A.drop = reinterpret_cast<uint32_t*>(ws + L.drop);
   A.fail_list = reinterpret_cast<int32_t*>(ws + L.fail);
   A.cand_key = reinterpret_cast<uint32_t*>(ws + L.ckey);
   A.cand_idx = reinterpret_cast<int32_t*>(ws + L.cidx);

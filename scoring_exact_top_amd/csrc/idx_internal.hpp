@@ -118,7 +118,8 @@ struct PrefillArgs {
   uint8_t* kt;          // [ntiles][8][64][16] keys relaid in MFMA lane order
   uint32_t* cand_key;   // [Q][kWaves*S][seg_cap] candidate scores (FP32 bits)
   int32_t* cand_idx;    // [Q][kWaves*S][seg_cap] candidate key ids
-  uint32_t* segn;       // [Q][kWaves*S][2]: entries stored, key of the largest dropped candidate (0: none)
+  uint32_t* segn;       // [Q][kWaves*S][4]: entries stored, key of the largest dropped candidate
+                        // (0: none), position of the first dropped one, unused
   int32_t S, seg_cap, seg_eff;  // splits, segment stride, usable entries per segment
   int32_t lds_cap, spill_cap, cap_total;
   int32_t* fail_list;   // [Q]
@@ -126,6 +127,7 @@ struct PrefillArgs {
   uint32_t* scratch;    // [repair_rows][repair_stride(N)] repair scores (order-preserving keys)
   uint32_t* rhist;      // [rslots][4][256] digit histograms of each slotted repair row
   uint32_t* rcnt;       // [rslots][2] output counters of each slotted repair row
+  uint32_t* reqc;       // [rslots][ceil(N/kRepairChunk)] keys tied at the K-th score per chunk
   int32_t rslots;
   int64_t rstride;
   float* dbg_scores;    // [Q][N] or null
@@ -189,33 +191,6 @@ struct IdPaged {
 template <class TM>
 __device__ __forceinline__ int key_index(const TM& tm, int i) { return tm(i >> 6) + (i & 63); }
 
-// Threshold of one row from its sample lattice: positions s0 + OFFSET +
-// stride*i, scored exactly like the main pass (same operations, so a
-// sampled key reproduces its score bit for bit there); returns the r-th
-// largest.  Whole workgroup calls; q is prepared by every wave.
-template <class TM>
-__device__ float sample_tau(const QOp& qo, const KeyBuf& kbuf, const TM& tm, int s0, const SampleGeom& sg,
-                            uint32_t* s_samp, SelShared& sh, int tid) {
-  const uint32_t lane = tid & 63;
-  const int wave = tid >> 6;
-  for (int tile = wave; tile * kTile < sg.n; tile += kWaves) {
-    const int i0 = tile * kTile;
-    const auto key_of = [&](int i) {
-      const int smp = min(i0 + i, sg.n - 1);
-      return key_index(tm, s0 + kSampleOffset + sg.stride * smp);
-    };
-    KeyTile kt;
-    load_tile_gather(kt, kbuf, key_of, lane);
-    const float sc = tile_score(qo, kt);
-    const int i = i0 + (int)lane;
-    if (i < sg.n) s_samp[i] = f2key(sc);
-  }
-  __syncthreads();
-  const SrcLds src{s_samp};
-  const SelResult sel = radix_select(src, sg.n, sg.r, sh, tid, false, false);
-  return key2f(sel.prefix);
-}
-
 // Candidate source over a repair scratch row: element i is position s0 + i.
 template <class IdMap>
 struct SrcScratchT {
@@ -251,7 +226,7 @@ __device__ void repair_row(const QOp& qo, const KeyBuf& kbuf, const TM& tm, cons
   }
   __syncthreads();
   const SrcScratchT<IdMap> src{scratch, s0, ids};
-  const SelResult sel = (L > kr) ? radix_select(src, L, kr, sh, tid, true, true) : SelResult{0u, 0u, kr};
+  const SelResult sel = (L > kr) ? radix_select(src, L, kr, sh, tid, true, true) : SelResult{0u, 0u, kr, kr};
   emit_selection(src, L, sel, kr, K, out, sh, tid);
 }
 

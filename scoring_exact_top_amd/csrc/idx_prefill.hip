@@ -133,6 +133,7 @@ __global__ __launch_bounds__(kWG, 2) void k_prefill_pair(PrefillArgs A) {
   const int voff = (int)lane * 16;
   uint32_t cnt[2] = {0u, 0u};  // candidates of each row found by this wave
   float dmax[2] = {-INFINITY, -INFINITY};  // per lane: largest candidate dropped for lack of room
+  int fdrop[2] = {0x7FFFFFFF, 0x7FFFFFFF};  // position of the segment's first dropped candidate
   // the (row, wave) workspace segments as buffer resources: a store past
   // seg_cap is dropped by the bounds check
   rsrc_t segk[2], segi[2];
@@ -182,6 +183,12 @@ __global__ __launch_bounds__(kWG, 2) void k_prefill_pair(PrefillArgs A) {
       if (cnt[r] + n > seg_cap) {
         const bool dropped = take && cnt[r] + rank_in(ball) >= seg_cap;
         dmax[r] = dropped ? fmaxf(dmax[r], sc[r]) : dmax[r];
+        if (cnt[r] <= seg_cap) {  // the tile where the segment fills up
+          int v = dropped ? my : 0x7FFFFFFF;
+#pragma unroll
+          for (int o = 32; o > 0; o >>= 1) v = min(v, __shfl_xor(v, o, 64));
+          fdrop[r] = __builtin_amdgcn_readfirstlane(v);
+        }
       }
       cnt[r] += n;
     }
@@ -248,9 +255,10 @@ __global__ __launch_bounds__(kWG, 2) void k_prefill_pair(PrefillArgs A) {
     for (; T < tile_hi; T += nseg) tile_body(T);
   }
 
-  // publish this wave's segment: entries stored, and the order-preserving
-  // key of the largest dropped candidate (0: none dropped; a candidate is
-  // never NaN, so its key is nonzero)
+  // publish this wave's segment: entries stored, the order-preserving key of
+  // the largest dropped candidate (0: none dropped; a candidate is never
+  // NaN, so its key is nonzero) and the position of the first dropped one
+  // (candidates arrive in position order, so every later one was dropped)
 #pragma unroll
   for (int r = 0; r < 2; ++r) {
     uint32_t dk = 0u;
@@ -261,7 +269,8 @@ __global__ __launch_bounds__(kWG, 2) void k_prefill_pair(PrefillArgs A) {
       dk = f2key(m);
     }
     if (lane == 0 && t0 + r < A.Q)
-      *reinterpret_cast<uint2*>(A.segn + 2 * ((int64_t)(t0 + r) * nseg + seg)) = make_uint2(min(cnt[r], seg_cap), dk);
+      *reinterpret_cast<uint4*>(A.segn + 4 * ((int64_t)(t0 + r) * nseg + seg)) =
+          make_uint4(min(cnt[r], seg_cap), dk, (uint32_t)fdrop[r], 0u);
   }
 }
 
@@ -270,17 +279,19 @@ __global__ __launch_bounds__(kWG, 2) void k_prefill_pair(PrefillArgs A) {
 // One workgroup per row, after the main kernel.  The row's candidates (its
 // kWaves*S segments: segment g in threads [g*tps, (g+1)*tps), tps =
 // 256/nseg, each thread every tps-th entry) are loaded into registers and
-// the K largest selected.  Certificate ("3.2 Sampled threshold", made
-// exact for capacity drops): the selection is the row's exact top-K iff
-// there were at least K candidates and no dropped candidate scores above
-// the smallest selected one (a dropped candidate equal to it is a tie, any
-// of which may be taken).  So massive ties at the boundary need no repair.
-// Rows that fail go to the failure list.
+// the K largest selected, ties at the K-th score going to the lowest ids.
+// Certificate ("3.2 Sampled threshold", made exact for capacity drops):
+// this is the row's exact top-K iff there were at least K candidates and
+// no dropped candidate scores above the smallest selected score theta; if
+// a dropped one equals theta, the tied ids taken must also all lie below
+// the first dropped position (segments drop only their latest candidates),
+// so that they are the lowest tied ids of the whole row.  Massive ties at
+// the boundary thus need no repair.  Rows that fail go to the failure list.
 __global__ __launch_bounds__(kWG) void k_prefill_select(PrefillArgs A) {
   __shared__ SelShared sh;
   __shared__ uint32_t s_segn[kWaves * kMaxSplit];
-  __shared__ uint32_t s_ok;
   const int tid = threadIdx.x;
+  const uint32_t lane = tid & 63;
   const int t = blockIdx.x;
   uint32_t* stats = stat_copy(A.ctrl, blockIdx.x);
   int32_t* out = A.out + (int64_t)t * A.K;
@@ -292,18 +303,23 @@ __global__ __launch_bounds__(kWG) void k_prefill_select(PrefillArgs A) {
     return;
   }
   const int nseg = kWaves * A.S;
-  uint32_t dk = 0u;
+  uint32_t dk = 0u, fd = 0xFFFFFFFFu;
   if (tid < nseg) {
-    const uint2 e = *reinterpret_cast<const uint2*>(A.segn + 2 * ((int64_t)t * nseg + tid));
+    const uint4 e = *reinterpret_cast<const uint4*>(A.segn + 4 * ((int64_t)t * nseg + tid));
     s_segn[tid] = e.x;
     dk = e.y;
+    fd = e.y ? e.z : 0xFFFFFFFFu;
   }
-  // largest dropped key over the segments (all in wave 0: nseg <= 32)
+  // largest dropped key and first dropped position over the segments (all
+  // in wave 0: nseg <= 32)
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) dk = max(dk, (uint32_t)__shfl_xor((int)dk, o, 64));
-  if (tid == 0) sh.pad0 = dk;
+  for (int o = 32; o > 0; o >>= 1) {
+    dk = max(dk, (uint32_t)__shfl_xor((int)dk, o, 64));
+    fd = min(fd, (uint32_t)__shfl_xor((int)fd, o, 64));
+  }
+  if (tid == 0) { sh.pad0 = dk; sh.pad1 = fd; }
   __syncthreads();
-  const uint32_t drop = sh.pad0;
+  const uint32_t drop = sh.pad0, first_drop = sh.pad1;
   uint32_t n = 0u;
   for (int g = 0; g < nseg; ++g) n += s_segn[g];
   const int L = re_t - rs_t;
@@ -319,10 +335,28 @@ __global__ __launch_bounds__(kWG) void k_prefill_select(PrefillArgs A) {
     int32_t id[kSelRegs];
     load_list_regs(key, id, A.cand_key + row, A.cand_idx + row, (uint32_t)(nseg * A.seg_cap), lay,
                    [](uint32_t x) { return f2key(__uint_as_float(x)); });
-    const RangeSel sel = (n > (uint32_t)kr) ? range_select_regs(key, lay, kr, sh, tid)
-                                           : RangeSel{1u, 0xFFFFFFFFu, kr};
-    if (drop > sel.lo) ok = drop <= range_min_regs(key, lay, sel, sh, tid);
-    if (ok) emit_range_regs(key, id, lay, sel, kr, A.K, out, sh, tid);
+    const auto kf = [&](int j) { return key[j]; };
+    const RangeSel sel = (n > (uint32_t)kr) ? range_select_regs<kSelRegs>(kf, lay, kr, sh, tid)
+                                           : RangeSel{1u, 0xFFFFFFFFu, kr, (int)n};
+    const uint32_t idlo = tie_bound_regs(key, id, lay, sel, sh, tid);
+    if (drop >= sel.lo) {
+      const uint32_t theta = range_min_regs<kSelRegs>(kf, lay, sel, sh, tid);
+      ok = drop <= theta;
+      if (drop == theta) {  // tied keys were dropped: the taken ones must precede them
+        const auto tk = [&](int j) { return key[j] == theta && ~(uint32_t)id[j] >= idlo ? ~(uint32_t)id[j] : 0xFFFFFFFFu; };
+        uint32_t mn = 0xFFFFFFFFu;  // smallest ~id taken at theta = ~(largest id)
+#pragma unroll
+        for (int j = 0; j < kSelRegs; ++j) mn = min(mn, tk(j));
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) mn = min(mn, (uint32_t)__shfl_xor((int)mn, o, 64));
+        if (lane == 0) sh.wsum[0][tid >> 6] = mn;
+        __syncthreads();
+        mn = min(min(sh.wsum[0][0], sh.wsum[0][1]), min(sh.wsum[0][2], sh.wsum[0][3]));
+        __syncthreads();
+        ok = ok && ~mn < first_drop;
+      }
+    }
+    if (ok) emit_range_regs(key, id, lay, sel, idlo, kr, A.K, out, IdIdentity{}, sh, tid);
   }
   if (tid == 0) {
     if (ok) {
@@ -489,8 +523,37 @@ __global__ __launch_bounds__(kWG) void k_prefill_repair_pass(PrefillArgs A) {
   }
 }
 
+// Rows whose selection ends in a tie (after all four digits, fewer keys
+// are still needed than share the K-th score): count each chunk's keys
+// equal to that score, so that the emit can take the lowest positions.
+__global__ __launch_bounds__(kWG) void k_prefill_repair_ties(PrefillArgs A) {
+  __shared__ SelShared sh;
+  const int tid = threadIdx.x;
+  const uint32_t n_slot = min(__atomic_load_n(&A.ctrl[kCtrlFail], __ATOMIC_RELAXED), (uint32_t)A.rslots);
+  const int cmax = (A.N + kRepairChunk - 1) / kRepairChunk;
+  const int64_t items = (int64_t)n_slot * cmax;
+#pragma unroll 1
+  for (int64_t i = blockIdx.x; i < items; i += gridDim.x) {
+    const int f = (int)(i / cmax), c = (int)(i % cmax);
+    const int t = A.fail_list[f];
+    const int L = A.row_end[t] - A.row_start[t];
+    if (c * kRepairChunk >= L) continue;
+    const RepairSel rs = repair_replay(A.rhist + (int64_t)f * 4 * 256, L, min(A.K, L), 4, sh, tid);
+    if (rs.done) continue;
+    ChunkKeys ck;
+    load_chunk(ck, A.scratch + (int64_t)f * A.rstride, c, L, tid);
+    uint32_t m = 0u;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) m += (chunk_pos(ck, j) < L && ck.v[j] == rs.prefix) ? 1u : 0u;
+    uint32_t tot;
+    block_exclusive_scan(m, sh, tid, tot);
+    if (tid == 0) A.reqc[(int64_t)f * cmax + c] = tot;
+  }
+}
+
 // Write each slotted failed row's selection: keys above the boundary prefix
-// and the first `rem` keys equal to it, positions from the row's counters.
+// and `rem` keys equal to it (the lowest positions where the boundary is a
+// tie), positions from the row's counters.
 __global__ __launch_bounds__(kWG) void k_prefill_repair_emit(PrefillArgs A) {
   __shared__ SelShared sh;
   const int tid = threadIdx.x;
@@ -539,6 +602,29 @@ __global__ __launch_bounds__(kWG) void k_prefill_repair_emit(PrefillArgs A) {
     pg += sh.pad0;
     pe += sh.pad1;
     const int eq_base = kr - rs.rem;
+    if (!rs.done) {
+      // a tie: rank the chunk's tied keys in position order (k, thread, e),
+      // after the tied keys of the chunks before it
+      uint32_t before = 0u, tot;
+      for (int cc = tid; cc < c; cc += kWG) before += A.reqc[(int64_t)f * cmax + cc];
+      block_exclusive_scan(before, sh, tid, tot);
+      pe = tot;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint32_t mk = (emask >> (4 * k)) & 15u;
+        const uint32_t r = block_exclusive_scan((uint32_t)__popc(mk), sh, tid, tot);
+        uint32_t p = pe + r;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if (mk >> e & 1u) {
+            if ((int)p < rs.rem) out[eq_base + p] = s0 + chunk_pos(ck, 4 * k + e);
+            ++p;
+          }
+        }
+        pe += tot;
+      }
+      emask = 0u;
+    }
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       const int pos = chunk_pos(ck, j);
@@ -571,6 +657,7 @@ int launch_prefill(const PrefillArgs& A, hipStream_t stream) {
   hipLaunchKernelGGL(k_prefill_repair_pass<1>, dim3(kRepairGrid), dim3(kWG), 0, stream, A);
   hipLaunchKernelGGL(k_prefill_repair_pass<2>, dim3(kRepairGrid), dim3(kWG), 0, stream, A);
   hipLaunchKernelGGL(k_prefill_repair_pass<3>, dim3(kRepairGrid), dim3(kWG), 0, stream, A);
+  hipLaunchKernelGGL(k_prefill_repair_ties, dim3(kRepairGrid), dim3(kWG), 0, stream, A);
   hipLaunchKernelGGL(k_prefill_repair_emit, dim3(kRepairGrid), dim3(kWG), 0, stream, A);
   return hipGetLastError() == hipSuccess ? IDX_OK : IDX_EHIP;
 }

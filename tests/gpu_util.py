@@ -64,6 +64,7 @@ def check_prefill_rows(case, out, rows, nthreads=0, gpu_scores=None, e4m3=None):
                                       e4m3) if e4m3 is not None else None
             cancel += check.check_scores(S[s0:s1], sc[j][s0:s1], bound=bound, where=where)
             check.check_debug_bitexact(out[t], S, s0, s1, case.K, where=where)
+            check.check_debug_canonical(out[t], S, s0, s1, case.K, where=where)
     return dict(rows=len(rows), below_theta=below, cancel_only=cancel)
 
 

@@ -131,6 +131,30 @@ def test_massive_ties_take_the_fast_path(e4m3):
     check_prefill_rows(case, r["out"], np.arange(case.Q), gpu_scores=r["scores"], e4m3=e4m3)
 
 
+def test_ties_through_repair_take_the_lowest_ids(e4m3):
+    """Rows over 16 distinct keys sent to the exact repair (threshold above
+    every score): the boundary tie resolves to the lowest tied ids there too
+    (the checker applies the tie rule on the GPU's own scores)."""
+    case = synth.causal_case("ties_repair", 8, 20000, seed=30, key_mode="ties16", K=300)
+    log("case", case.name)
+    r = run_prefill(case, scores=True, force_tau=float("inf"))
+    st = r["stats"]
+    log("stats", st)
+    assert st["repaired"] == case.Q, st
+    check_prefill_rows(case, r["out"], np.arange(case.Q), gpu_scores=r["scores"], e4m3=e4m3)
+
+
+def test_output_is_deterministic():
+    """Two calls on the same inputs select the same ids (ties included)."""
+    case = synth.causal_case("determinism", 16, 12000, seed=31, key_mode="ties16", K=512)
+    log("case", case.name)
+    a = run_prefill(case)["out"]
+    b = run_prefill(case, force_tau=float("inf"))["out"]   # all rows through repair
+    c = run_prefill(case)["out"]
+    assert np.array_equal(np.sort(a, axis=1), np.sort(c, axis=1))
+    assert np.array_equal(np.sort(a, axis=1), np.sort(b, axis=1))
+
+
 def test_invalid_ranges_give_minus_one():
     case = synth.random_case("badrange", 6, 1000, seed=26, K=64, min_len=10)
     case.row_start[1], case.row_end[1] = 50, 40        # start > end

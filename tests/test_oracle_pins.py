@@ -306,6 +306,27 @@ def test_checker_score_tolerance_and_bitexact():
         check.check_debug_bitexact(m, S, s0, s1, 128)
 
 
+def test_checker_canonical_tie_rule():
+    """A 60-way tie straddling the K-th place (24 ids above it, K = 64): only
+    the 40 lowest tied ids are accepted.  Swapping in a higher tied id still
+    gives a valid top-K (the bit-exact check passes) but breaks the rule."""
+    rng = np.random.default_rng(5)
+    s0, s1, K = 10, 410, 64
+    ids = rng.permutation(np.arange(s0, s1))
+    above, tied, rest = ids[:24], np.sort(ids[24:84]), ids[84:]
+    S = np.full(500, np.nan, np.float32)
+    S[above] = 2.0 + np.arange(24, dtype=np.float32) / 64
+    S[tied] = 1.5
+    S[rest] = rng.uniform(0.0, 1.0, rest.size).astype(np.float32)
+    good = np.concatenate([above, tied[:40]]).astype(np.int32)
+    check.check_debug_canonical(good, S, s0, s1, K)
+    bad = good.copy()
+    bad[-1] = tied[-1]
+    check.check_debug_bitexact(bad, S, s0, s1, K)
+    with pytest.raises(check.CheckError):
+        check.check_debug_canonical(bad, S, s0, s1, K)
+
+
 # ------------------------------------------------------------------ decode
 
 def test_decode_trivial_path_is_a_remap():
