@@ -14,8 +14,8 @@
 // The first sum costs one VALU op per head (an FMA with an |x| source
 // modifier); the linear term u.k goes to the matrix core: u is split into
 // eight e4m3 vectors with FP32 scales, u ~= sum_m sigma_m e4m3(u8_m), residual
-// below 27^-7 * 16/448 |u|_max, and these eight rows form a fifth 16-row A
-// block.
+// below 27^-7 * 16/448 |u|_max, and these eight rows form half of a fifth
+// 16-row A block, shared by two query rows (u_slot below).
 //
 // Every 128-deep FP8 contraction is one v_mfma_f32_16x16x128_f8f6f4 per 16
 // rows x 16 keys.  A (rows x 128) lives in registers for the whole key loop;
@@ -113,9 +113,16 @@ __device__ __forceinline__ uint32_t e4m3x2_enc(float a, float b) {
   return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xFFFFu;
 }
 
+// Layout of the shared u block: row 4*(m/2) + 2p + (m%2) carries term m of
+// slot p (p = 0, 1: the first or second row of a pair).  Result rows
+// 4g..4g+3 of a block land in lane group g, so every lane holds two terms of
+// each slot (terms 2g and 2g+1, in registers 2p and 2p+1): each row of a pair
+// adds two u partials per lane, none of them zero.
+
 // One query row as held by a lane: A operands of the four 16-head blocks and
 // of the u block, the halved weights w'/2 of the 16 heads whose results land in
-// this lane, and the halved scales sigma/2 of the 4 u-block rows it holds.
+// this lane, and the halved scales sigma/2 of the 4 u-block rows it holds
+// (zero for the rows of the other slot).
 struct QOp {
   v8i a[4];
   v8i au;
@@ -123,14 +130,14 @@ struct QOp {
   float sh[4];
 };
 
-// Two query rows as held by a lane, sharing one u block: rows 0..7 carry the
-// first row's terms, rows 8..15 the second's.  sh[x] is zero in the lanes
-// that hold the other row's u rows, so each row picks up only its own terms.
+// Two query rows as held by a lane, sharing one u block in that layout:
+// sh[p][i] is sigma/2 of u-block row 4g+2p+i, whose result is register 2p+i
+// of this lane's u accumulator.
 struct QOp2 {
   v8i a[2][4];
   v8i au;
   float wh[2][16];
-  float sh[2][4];
+  float sh[2][2];
 };
 
 // Per-head query scales, all ones, for calls without q_scale.
@@ -241,29 +248,32 @@ __device__ __forceinline__ void prepare_q2(QOp2& o, const uint8_t* q, const floa
   split_u(q, q_scale, w, t1, lane, scratch + kUTerms * kD, s1);
   wave_sync();
   const uint32_t g = lane >> 4, i = lane & 15;
-  const uint32_t* src = reinterpret_cast<const uint32_t*>(scratch + i * kD + 32 * g);
+  // A row i of the u block: slot (i & 3) >> 1, term 2 (i >> 2) + (i & 1)
+  const uint32_t urow = ((i & 3u) >> 1) * kUTerms + 2u * (i >> 2) + (i & 1u);
+  const uint32_t* src = reinterpret_cast<const uint32_t*>(scratch + urow * kD + 32 * g);
 #pragma unroll
   for (int k = 0; k < 8; ++k) o.au[k] = (int)src[k];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int row = 4 * (int)g + r;  // 0..15
+  for (int x = 0; x < 2; ++x) {
+    const int m = 2 * (int)g + x;
     float a0 = 0.f, a1 = 0.f;
 #pragma unroll
-    for (int m = 0; m < kUTerms; ++m) {
-      a0 = row == m ? s0[m] : a0;
-      a1 = row == m + kUTerms ? s1[m] : a1;
+    for (int j = 0; j < kUTerms; ++j) {
+      a0 = m == j ? s0[j] : a0;
+      a1 = m == j ? s1[j] : a1;
     }
-    o.sh[0][r] = 0.5f * a0;
-    o.sh[1][r] = 0.5f * a1;
+    o.sh[0][x] = 0.5f * a0;
+    o.sh[1][x] = 0.5f * a1;
   }
   wave_sync();
 }
 
 // Prepare query row t (all 64 lanes; scratch = 8*128 bytes of LDS).  slot
 // (0 or 1) places the u terms where prepare_q2 puts them for the first or
-// the second row of a pair (u-block rows 0..7 or 8..15), so that a row
-// scored alone adds exactly the same partial sums in the same lanes as in
-// its pair and gets bit-identical scores.
+// the second row of a pair, so that a row scored alone adds exactly
+// the same nonzero partial sums in the same lanes and order as in its pair
+// and gets bit-identical scores (the other slot's rows are zero codes with
+// zero scales, and adding 0*0 leaves a sum unchanged).
 __device__ __forceinline__ void prepare_q(QOp& o, const uint8_t* q, const float* q_scale, const float* w,
                                           int64_t t, uint32_t lane, uint8_t* scratch, int slot) {
   head_ops(o.a, o.wh, q, q_scale, w, t, lane);
@@ -271,8 +281,8 @@ __device__ __forceinline__ void prepare_q(QOp& o, const uint8_t* q, const float*
   split_u(q, q_scale, w, t, lane, scratch, sig);
   wave_sync();
   const uint32_t g = lane >> 4, i = lane & 15;
-  const uint32_t term = i - (uint32_t)(kUTerms * slot);  // wraps above kUTerms for the other half
-  if (term < (uint32_t)kUTerms) {
+  if (((i & 3u) >> 1) == (uint32_t)slot) {  // A row i carries term 2 (i >> 2) + (i & 1) of slot (i & 3) >> 1
+    const uint32_t term = 2u * (i >> 2) + (i & 1u);
     const uint32_t* src = reinterpret_cast<const uint32_t*>(scratch + term * kD + 32 * g);
 #pragma unroll
     for (int k = 0; k < 8; ++k) o.au[k] = (int)src[k];
@@ -282,11 +292,11 @@ __device__ __forceinline__ void prepare_q(QOp& o, const uint8_t* q, const float*
   }
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    const int row = 4 * (int)g + r;
+    const int m = 2 * (int)g + (r & 1);  // result row 4g + r: slot r >> 1, term m
     float sr = 0.f;
 #pragma unroll
-    for (int m = 0; m < kUTerms; ++m) sr = row == m + kUTerms * slot ? sig[m] : sr;
-    o.sh[r] = 0.5f * sr;
+    for (int j = 0; j < kUTerms; ++j) sr = m == j ? sig[j] : sr;
+    o.sh[r] = (r >> 1) == slot ? 0.5f * sr : 0.f;
   }
   wave_sync();
 }

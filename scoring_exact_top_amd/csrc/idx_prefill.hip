@@ -144,17 +144,17 @@ __global__ __launch_bounds__(kWG, 2) void k_prefill_pair(PrefillArgs A) {
     segi[r] = __builtin_amdgcn_make_buffer_rsrc((void*)(A.cand_idx + o), (short)0, (int)(seg_cap * 4u), 0x00020000);
   }
   const v4f z = {0.f, 0.f, 0.f, 0.f};
-  // Head-weighted sum of one row's 16 heads held by this lane plus its 4
-  // u-block rows, in a fixed order (20 FMAs).
-  const auto epi = [](const float (&wh)[16], const float (&shr)[4], const v4f (&a)[4], const v4f& au) {
+  // Head-weighted sum of one row's 16 heads held by this lane plus its two
+  // u-block rows (registers u0, u0+1 of the u accumulator), in a fixed order
+  // (18 FMAs).
+  const auto epi = [](const float (&wh)[16], const float (&shr)[2], const v4f (&a)[4], float ua, float ub) {
     float x = 0.f;
 #pragma unroll
     for (int b = 0; b < 4; ++b)
 #pragma unroll
       for (int r = 0; r < 4; ++r) x = fmaf(wh[4 * b + r], fabsf(a[b][r]), x);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) x = fmaf(shr[r], au[r], x);
-    return x;
+    x = fmaf(shr[0], ua, x);
+    return fmaf(shr[1], ub, x);
   };
   // Per-tile state: row B's accumulators of the last sub-tile (its epilogue
   // runs under the next sub-tile's MFMAs) and the tile's partial sums.
@@ -214,7 +214,7 @@ __global__ __launch_bounds__(kWG, 2) void k_prefill_pair(PrefillArgs A) {
       for (int b = 0; b < 4; ++b)
         aA[b] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qo.a[0][b], kb[c], z, 0, 0, 0, 0, 0, 0);
       const v4f au = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qo.au, kb[c], z, 0, 0, 0, 0, 0, 0);
-      if (c > 0) q1[c - 1] = epi(qo.wh[1], qo.sh[1], aB, auB);
+      if (c > 0) q1[c - 1] = epi(qo.wh[1], qo.sh[1], aB, auB[2], auB[3]);
 #pragma unroll
       for (int i = 0; i < 5; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -226,7 +226,7 @@ __global__ __launch_bounds__(kWG, 2) void k_prefill_pair(PrefillArgs A) {
         aB[b] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qo.a[1][b], kb[c], z, 0, 0, 0, 0, 0, 0);
       kb[c] = cat8(__builtin_amdgcn_raw_buffer_load_b128(ktb, voff, ntoff + (2 * c) * 1024, 0),
                    __builtin_amdgcn_raw_buffer_load_b128(ktb, voff, ntoff + (2 * c + 1) * 1024, 0));
-      q0[c] = epi(qo.wh[0], qo.sh[0], aA, au);
+      q0[c] = epi(qo.wh[0], qo.sh[0], aA, au[0], au[1]);
       auB = au;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -236,10 +236,13 @@ __global__ __launch_bounds__(kWG, 2) void k_prefill_pair(PrefillArgs A) {
       __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
-    q1[3] = epi(qo.wh[1], qo.sh[1], aB, auB);
-    const float ks = ks_cur;
+    q1[3] = epi(qo.wh[1], qo.sh[1], aB, auB[2], auB[3]);
+    tail(T, ks_cur);
+    // The next tile's key scale is loaded only now, into the register the
+    // tail just read: a load whose result were copied at the loop's back edge
+    // would make that edge wait for every load issued before it (the memory
+    // counter retires in order), that is for the whole next tile's keys.
     ks_cur = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(kbuf.ks, (int)lane * 4, ntoff / kD * 4, 0));
-    tail(T, ks);
   };
   if (lo < hi) {
     int T = (lo >> 6) + seg;
