@@ -203,6 +203,75 @@ def bench_prefill(args, lib):
     return res
 
 
+def bench_unfused(args, lib):
+    """The unfused comparator on a prefill workload: idx_topk_prefill_unfused
+    (the same scoring writes the [Q,N] FP32 matrix, then the dense top-K), the
+    fused idx_topk_prefill timed the same way in the same process, and the
+    standalone dense top-K (idx_topk_rows) on the matrix alone."""
+    made = synth.WORKLOADS[args.workload](0)
+    cases = made if isinstance(made, list) else [made]
+    pairs = sum(c.pairs for c in cases)
+    devs = [{k: tensor(getattr(c, k)) for k in
+             ("q8", "q_scale", "k8", "k_scale", "w", "row_start", "row_end")} for c in cases]
+    outs = [torch.empty((c.Q, c.K), dtype=torch.int32, device="cuda") for c in cases]
+    n_calls = len(cases)
+    wsu = [lib.alloc_workspace(lib.prefill_unfused_workspace_bytes(c.Q, c.N, c.K), "cuda")
+           for c in cases]
+
+    def step_unfused(step_evs):
+        for j, (c, d) in enumerate(zip(cases, devs)):
+            lib.prefill_unfused(d["q8"], d["q_scale"], d["k8"], d["k_scale"], d["w"],
+                                d["row_start"], d["row_end"], c.K, out=outs[j], workspace=wsu[j],
+                                main_events=None if step_evs is None else step_evs[j])
+
+    ms_unf, score_avg, score_min = timed(step_unfused, n_calls, args.steps, args.warmup)
+    del wsu
+    wsf = [lib.alloc_workspace(lib.prefill_workspace_bytes(c.Q, c.N, c.K), "cuda") for c in cases]
+
+    def step_fused(step_evs):
+        for j, (c, d) in enumerate(zip(cases, devs)):
+            lib.prefill_debug(d["q8"], d["q_scale"], d["k8"], d["k_scale"], d["w"], d["row_start"],
+                              d["row_end"], c.K, out=outs[j], workspace=wsf[j],
+                              main_events=None if step_evs is None else step_evs[j])
+
+    ms_fused, main_avg, _ = timed(step_fused, n_calls, args.steps, args.warmup)
+    # standalone dense top-K over each call's score matrix
+    mats = []
+    for j, (c, d) in enumerate(zip(cases, devs)):
+        S = torch.empty((c.Q, c.N), dtype=torch.float32, device="cuda")
+        lib.prefill_debug(d["q8"], d["q_scale"], d["k8"], d["k_scale"], d["w"], d["row_start"],
+                          d["row_end"], c.K, out=outs[j], workspace=wsf[j], scores_out=S)
+        mats.append(S)
+    del wsf
+
+    def step_rows(step_evs):
+        for j, (c, d) in enumerate(zip(cases, devs)):
+            if step_evs is not None:
+                step_evs[j][0].record()
+            lib.topk_rows(mats[j], d["row_start"], d["row_end"], c.K, out=outs[j])
+            if step_evs is not None:
+                step_evs[j][1].record()
+
+    ms_rows, _, _ = timed(step_rows, n_calls, args.steps, args.warmup)
+    log("workload", args.workload, "unfused ms/step %.4f (scoring %.4f)" % (ms_unf, score_avg * n_calls),
+        "fused ms/step %.4f (main %.4f)" % (ms_fused, main_avg * n_calls),
+        "standalone top-K ms/step %.4f" % ms_rows)
+    achieved = FLOP_PER_PAIR * (pairs / n_calls) / (score_avg * 1e-3) / 1e12
+    config = {"workload": cases[0].name if n_calls == 1 else args.workload, "variant": "unfused",
+              "rows": sum(c.Q for c in cases), "keys": max(c.N for c in cases), "heads": 64,
+              "dim": 128, "K": cases[0].K, "pairs": pairs, "calls_per_step": n_calls}
+    roofline = {"bound": "mfma", "achieved": achieved, "peak": FP8_DENSE_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": achieved / FP8_DENSE_PEAK_TFLOPS, "traffic": None,
+                "kernel": "k_prefill_pair (dense scores)", "ms_per_launch": score_avg}
+    res = result(args, pairs / (ms_unf * 1e-3) / 1e9, ms_unf, config, roofline,
+                 "fp8_e4m3 x fp8_e4m3 -> f32")
+    res["compare"] = {"unfused_ms_per_step": ms_unf, "fused_ms_per_step": ms_fused,
+                      "fused_speedup": ms_unf / ms_fused, "standalone_topk_ms_per_step": ms_rows,
+                      "scoring_ms_per_step": score_avg * n_calls,
+                      "fused_main_ms_per_step": main_avg * n_calls}
+    return res
+
+
 def decode_split_bytes(case) -> int:
     """Algorithmic bytes of k_decode_split: every scored sequence (L > K)
     reads its keys (128 B codes + 4 B scale each), its page-table entries,
@@ -257,6 +326,9 @@ def main():
     ap.add_argument("--workload", default="long_prefill", choices=PREFILL + DECODE)
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="oracle sample budget in seconds (0: skip the CPU baseline)")
+    ap.add_argument("--unfused", action="store_true",
+                    help="time the unfused comparator (score matrix, then top-K) on a prefill "
+                         "workload, beside the fused path and the standalone top-K")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain copy of MIB MiB (counter calibration) and exit")
     args = ap.parse_args()
@@ -269,7 +341,13 @@ def main():
         sys.exit(2)
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     import scoring_exact_top_amd as lib
-    res = (bench_decode if args.workload in DECODE else bench_prefill)(args, lib)
+    if args.unfused:
+        if args.workload in DECODE:
+            print("--unfused applies to prefill workloads", file=sys.stderr)
+            sys.exit(2)
+        res = bench_unfused(args, lib)
+    else:
+        res = (bench_decode if args.workload in DECODE else bench_prefill)(args, lib)
     print(json.dumps(res), flush=True)
 
 

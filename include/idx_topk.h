@@ -136,6 +136,47 @@ int idx_topk_prefill_debug(const uint8_t *q, const float *q_scale, const uint8_t
                            int32_t N, void *workspace, size_t workspace_bytes, void *stream,
                            float *scores_out, float *tau_out, const idx_topk_opts *opts);
 
+/* Bytes of workspace idx_topk_prefill_unfused needs: that of idx_topk_prefill
+ * plus the [Q][N] FP32 score matrix (2 GiB at Q = 4096, N = 131072). */
+size_t idx_topk_prefill_unfused_workspace(int32_t Q, int32_t N, int32_t K);
+
+/*
+ * Unfused comparator of idx_topk_prefill (Fusing Indexer Scoring and Exact Top-k page,
+ * "2.1 Where the cost goes": a scoring kernel writes the full score matrix, a
+ * separate top-k reads it back).  Same arguments and output as
+ * idx_topk_prefill: the same MFMA scoring (bit-identical scores) writes all
+ * valid scores of every row into the workspace, then idx_topk_rows' kernel
+ * selects each row from that matrix.  With the lowest-id tie rule both paths
+ * return the same id set per row.  opts may be NULL or carry only the timing
+ * events (ev_main_* bracket the scoring kernel); the other knobs give
+ * IDX_EINVAL.  N * 4 must fit in 31 bits (IDX_EUNSUPPORTED otherwise).
+ */
+int idx_topk_prefill_unfused(const uint8_t *q, const float *q_scale, const uint8_t *k,
+                             const float *k_scale, const float *w, const int32_t *row_start,
+                             const int32_t *row_end, int32_t K, int32_t *out_idx, int32_t Q,
+                             int32_t N, void *workspace, size_t workspace_bytes, void *stream,
+                             const idx_topk_opts *opts);
+
+/*
+ * Exact top-K of every row of a dense FP32 matrix (the standalone selection
+ * stage of Fusing Indexer Scoring and Exact Top-k page, "2.1 Where the cost goes" and Table 2).
+ *   scores    device, 16-byte aligned; row t's value at position s is
+ *             scores[t * ld + s]; only [row_start[t], row_end[t]) is read;
+ *             NaN-free
+ *   ld        row stride in floats, >= N
+ *   row_start, row_end [Q] int32 device: 0 <= start <= end <= N (a row that
+ *             breaks this gets all -1)
+ *   K         1..2048
+ *   out_idx   [Q][K] int32 device: the positions of the K largest values,
+ *             unsorted; ties at the K-th value go to the lowest positions;
+ *             rows with L = end - start <= K get all L positions then -1.
+ * Needs no workspace (LDS only); N * 4 must fit in 31 bits.  Asynchronous on
+ * `stream`.  Returns IDX_OK or a negative IDX_E* code.
+ */
+int idx_topk_rows(const float *scores, int64_t ld, const int32_t *row_start,
+                  const int32_t *row_end, int32_t K, int32_t *out_idx, int32_t Q, int32_t N,
+                  void *stream);
+
 /* Bytes of workspace idx_topk_decode_paged needs. */
 size_t idx_topk_decode_workspace(int32_t B, int32_t max_pages, int32_t page_size, int32_t K);
 

@@ -55,6 +55,12 @@ _lib.idx_topk_prefill.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, 
 _lib.idx_topk_prefill_debug.restype = ctypes.c_int
 _lib.idx_topk_prefill_debug.argtypes = _lib.idx_topk_prefill.argtypes + [_vp, _vp,
                                                                           ctypes.POINTER(Opts)]
+_lib.idx_topk_prefill_unfused_workspace.restype = _sz
+_lib.idx_topk_prefill_unfused_workspace.argtypes = [_i32, _i32, _i32]
+_lib.idx_topk_prefill_unfused.restype = ctypes.c_int
+_lib.idx_topk_prefill_unfused.argtypes = _lib.idx_topk_prefill.argtypes + [ctypes.POINTER(Opts)]
+_lib.idx_topk_rows.restype = ctypes.c_int
+_lib.idx_topk_rows.argtypes = [_vp, ctypes.c_int64, _vp, _vp, _i32, _vp, _i32, _i32, _vp]
 _lib.idx_topk_decode_workspace.restype = _sz
 _lib.idx_topk_decode_workspace.argtypes = [_i32, _i32, _i32, _i32]
 _lib.idx_topk_decode_paged.restype = ctypes.c_int
@@ -99,6 +105,10 @@ def _stream(stream):
 
 def prefill_workspace_bytes(Q: int, N: int, K: int) -> int:
     return int(_lib.idx_topk_prefill_workspace(Q, N, K))
+
+
+def prefill_unfused_workspace_bytes(Q: int, N: int, K: int) -> int:
+    return int(_lib.idx_topk_prefill_unfused_workspace(Q, N, K))
 
 
 def decode_workspace_bytes(B: int, max_pages: int, page_size: int, K: int) -> int:
@@ -166,6 +176,48 @@ def _prefill(q8, q_scale, k8, k_scale, w, row_start, row_end, K, out, workspace,
                                            _ptr(tau_out, torch.float32), ctypes.byref(opts)))
     else:
         _check(_lib.idx_topk_prefill(*args))
+    return out
+
+
+def prefill_unfused(q8, q_scale, k8, k_scale, w, row_start, row_end, K: int, out=None,
+                    workspace=None, stream=None, main_events=None):
+    """idx_topk_prefill_unfused: the same scores written to an explicit [Q,N]
+    matrix in the workspace, then a separate top-K over it (the comparator of
+    the fused path).  main_events: optional (start, stop) event pair around
+    the scoring kernel."""
+    q8, k8 = _q_k(q8, k8)
+    Q, N = int(q8.shape[0]), int(k8.shape[0])
+    if q8.shape[1:] != (HEADS, DIM) or k8.shape[1:] != (DIM,):
+        raise ValueError("q8 must be [Q,64,128] and k8 [N,128]")
+    dev = q8.device
+    if out is None:
+        out = torch.empty((Q, K), dtype=torch.int32, device=dev)
+    if workspace is None:
+        workspace = alloc_workspace(prefill_unfused_workspace_bytes(Q, N, K), dev)
+    ev0 = ev1 = None
+    if main_events is not None:
+        ev0, ev1 = (ctypes.c_void_p(e.cuda_event) for e in main_events)
+    opts = Opts(0, 0.0, 0, 0, ev0, ev1)
+    _check(_lib.idx_topk_prefill_unfused(
+        _ptr(q8, torch.uint8), _ptr(q_scale, torch.float32), _ptr(k8, torch.uint8),
+        _ptr(k_scale, torch.float32), _ptr(w, torch.float32), _ptr(row_start, torch.int32),
+        _ptr(row_end, torch.int32), int(K), _ptr(out, torch.int32), Q, N, _ptr(workspace),
+        int(workspace.numel()), _stream(stream), ctypes.byref(opts)))
+    return out
+
+
+def topk_rows(scores, row_start, row_end, K: int, out=None, stream=None):
+    """idx_topk_rows: exact top-K positions of each row of a dense FP32
+    matrix scores [Q, ld] over [row_start, row_end) (ties to the lowest
+    positions; rows with fewer than K positions are -1 padded)."""
+    if scores.dim() != 2:
+        raise ValueError("scores must be [Q, N]")
+    Q, N = int(scores.shape[0]), int(scores.shape[1])
+    if out is None:
+        out = torch.empty((Q, K), dtype=torch.int32, device=scores.device)
+    _check(_lib.idx_topk_rows(_ptr(scores, torch.float32), N, _ptr(row_start, torch.int32),
+                              _ptr(row_end, torch.int32), int(K), _ptr(out, torch.int32), Q, N,
+                              _stream(stream)))
     return out
 
 

@@ -4,6 +4,7 @@
 
 #include "idx_internal.hpp"
 #include "idx_decode.hpp"
+#include "idx_rows.hpp"
 
 namespace idxk {
 
@@ -11,10 +12,11 @@ static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 static inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 struct PrefillLayout {
-  size_t ctrl, tau, fail, skey, cidx, segn, scratch, rhist, rcnt, reqc, kt, total;
+  size_t ctrl, tau, fail, skey, cidx, segn, scratch, rhist, rcnt, reqc, kt, dense, total;
 };
 
-static PrefillLayout prefill_layout(int32_t Q, int32_t N) {
+// unfused: also the [Q][N] FP32 score matrix of the unfused comparator.
+static PrefillLayout prefill_layout(int32_t Q, int32_t N, bool unfused = false) {
   PrefillLayout L;
   size_t o = 0;
   L.ctrl = o; o = align256(o + sizeof(uint32_t) * kCtrlWords);
@@ -30,6 +32,7 @@ static PrefillLayout prefill_layout(int32_t Q, int32_t N) {
   L.rcnt = o; o = align256(o + sizeof(uint32_t) * (size_t)repair_slots(Q, N) * 2);
   L.reqc = o; o = align256(o + sizeof(uint32_t) * (size_t)repair_slots(Q, N) * (size_t)((N + kRepairChunk - 1) / kRepairChunk));
   L.kt = o; o = align256(o + (size_t)((N + 63) / 64) * 64 * 128);
+  L.dense = o; if (unfused) o = align256(o + sizeof(float) * (size_t)Q * (size_t)N);
   L.total = o;
   return L;
 }
@@ -38,13 +41,14 @@ static int prefill_common(const uint8_t* q, const float* q_scale, const uint8_t*
                           const float* k_scale, const float* w, const int32_t* row_start,
                           const int32_t* row_end, int32_t K, int32_t* out_idx, int32_t Q, int32_t N,
                           void* workspace, size_t workspace_bytes, void* stream, float* scores_out,
-                          float* tau_out, const idx_topk_opts* opts) {
+                          float* tau_out, const idx_topk_opts* opts, bool unfused = false) {
   if (Q < 0 || N < 0 || K < 1 || K > kKmax) return IDX_EINVAL;
   if (Q == 0) return IDX_OK;
   if (!q || !w || !row_start || !row_end || !out_idx) return IDX_EINVAL;
   if (N > 0 && (!k || !k_scale)) return IDX_EINVAL;
   if (!aligned16(q) || (k && !aligned16(k))) return IDX_EINVAL;
-  const PrefillLayout L = prefill_layout(Q, N);
+  if (unfused && (int64_t)N * 4 > 0x7fffffffLL) return IDX_EUNSUPPORTED;
+  const PrefillLayout L = prefill_layout(Q, N, unfused);
   if (!workspace || workspace_bytes < L.total) return IDX_EWORKSPACE;
   if (((uintptr_t)workspace & 255u) != 0) return IDX_EINVAL;
   char* ws = static_cast<char*>(workspace);
@@ -90,6 +94,12 @@ static int prefill_common(const uint8_t* q, const float* q_scale, const uint8_t*
   const int share = A.cap_total / (kWaves * A.S);
   A.seg_eff = (A.cap_total >= kCandCap || share > A.seg_cap) ? A.seg_cap : share;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (unfused) {
+    A.dbg_scores = reinterpret_cast<float*>(ws + L.dense);
+    A.force_tau = 1;
+    A.tau_value = INFINITY;
+    return launch_prefill_unfused(A, s);
+  }
   int rc = launch_prefill(A, s);
   if (rc == IDX_OK && tau_out) {
     if (hipMemcpyAsync(tau_out, A.tau, sizeof(float) * (size_t)Q, hipMemcpyDeviceToDevice, s) != hipSuccess)
@@ -123,6 +133,33 @@ extern "C" int idx_topk_prefill_debug(const uint8_t* q, const float* q_scale, co
                                       float* tau_out, const idx_topk_opts* opts) {
   return prefill_common(q, q_scale, k, k_scale, w, row_start, row_end, K, out_idx, Q, N, workspace,
                         workspace_bytes, stream, scores_out, tau_out, opts);
+}
+
+extern "C" size_t idx_topk_prefill_unfused_workspace(int32_t Q, int32_t N, int32_t K) {
+  if (Q < 0 || N < 0 || K < 1 || K > kKmax) return 0;
+  return prefill_layout(Q, N, true).total;
+}
+
+extern "C" int idx_topk_prefill_unfused(const uint8_t* q, const float* q_scale, const uint8_t* k,
+                                        const float* k_scale, const float* w, const int32_t* row_start,
+                                        const int32_t* row_end, int32_t K, int32_t* out_idx, int32_t Q,
+                                        int32_t N, void* workspace, size_t workspace_bytes, void* stream,
+                                        const idx_topk_opts* opts) {
+  if (opts && (opts->force_tau || opts->lds_cap || opts->spill_cap)) return IDX_EINVAL;
+  return prefill_common(q, q_scale, k, k_scale, w, row_start, row_end, K, out_idx, Q, N, workspace,
+                        workspace_bytes, stream, nullptr, nullptr, opts, true);
+}
+
+extern "C" int idx_topk_rows(const float* scores, int64_t ld, const int32_t* row_start,
+                             const int32_t* row_end, int32_t K, int32_t* out_idx, int32_t Q, int32_t N,
+                             void* stream) {
+  if (Q < 0 || N < 0 || K < 1 || K > kKmax) return IDX_EINVAL;
+  if (Q == 0) return IDX_OK;
+  if (!scores || !row_start || !row_end || !out_idx) return IDX_EINVAL;
+  if (ld < N || ((uintptr_t)scores & 15u) != 0) return IDX_EINVAL;
+  if ((int64_t)N * 4 > 0x7fffffffLL) return IDX_EUNSUPPORTED;
+  RowsArgs R{scores, ld, row_start, row_end, Q, N, K, out_idx, nullptr};
+  return launch_topk_rows(R, static_cast<hipStream_t>(stream));
 }
 
 extern "C" size_t idx_topk_decode_workspace(int32_t B, int32_t max_pages, int32_t page_size, int32_t K) {

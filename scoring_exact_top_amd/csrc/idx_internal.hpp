@@ -231,5 +231,6 @@ __device__ void repair_row(const QOp& qo, const KeyBuf& kbuf, const TM& tm, cons
 }
 
 int launch_prefill(const PrefillArgs& A, hipStream_t stream);
+int launch_prefill_unfused(const PrefillArgs& A, hipStream_t stream);
 
 }  // namespace idxk

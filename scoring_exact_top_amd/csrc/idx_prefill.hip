@@ -10,6 +10,7 @@
 // workspace and selects exactly there.
 #include "idx_common.hpp"
 #include "idx_internal.hpp"
+#include "idx_rows.hpp"
 
 namespace idxk {
 
@@ -95,7 +96,12 @@ __global__ __launch_bounds__(kWG) void k_prefill_tau(PrefillArgs A) {
 // from a scalar count plus the lane's rank in the ballot, so no atomics
 // are involved.  After the walk each wave publishes its segment counts;
 // certification and selection follow in their own kernel.
-template <bool DBG>
+//
+// MODE kPairFused is that fused pass; kPairDebug also writes every valid
+// score to dbg_scores [Q][N]; kPairDense only writes the scores (no filter,
+// no candidates): the scoring stage of the unfused comparator.
+constexpr int kPairFused = 0, kPairDebug = 1, kPairDense = 2;
+template <int MODE>
 __global__ __launch_bounds__(kWG, 2) void k_prefill_pair(PrefillArgs A) {
   __shared__ uint8_t s_qprep[kWaves][2 * kUTerms * kD];
   const int tid = threadIdx.x;
@@ -173,7 +179,8 @@ __global__ __launch_bounds__(kWG, 2) void k_prefill_pair(PrefillArgs A) {
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
       const bool valid = my >= rs[r] && my < re[r];
-      if (DBG && valid) A.dbg_scores[(int64_t)(t0 + r) * A.N + my] = sc[r];
+      if (MODE != kPairFused && valid) A.dbg_scores[(int64_t)(t0 + r) * A.N + my] = sc[r];
+      if (MODE == kPairDense) continue;
       const bool take = valid && sc[r] >= tr[r];
       const uint64_t ball = __ballot(take);
       const uint32_t n = (uint32_t)__popcll(ball);
@@ -258,6 +265,7 @@ __global__ __launch_bounds__(kWG, 2) void k_prefill_pair(PrefillArgs A) {
     for (; T < tile_hi; T += nseg) tile_body(T);
   }
 
+  if (MODE == kPairDense) return;
   // publish this wave's segment: entries stored, the order-preserving key of
   // the largest dropped candidate (0: none dropped; a candidate is never
   // NaN, so its key is nonzero) and the position of the first dropped one
@@ -651,9 +659,9 @@ int launch_prefill(const PrefillArgs& A, hipStream_t stream) {
   if (A.ev_main_start && hipEventRecord(A.ev_main_start, stream) != hipSuccess) return IDX_EHIP;
   const unsigned grid = (unsigned)((A.Q + 1) / 2 * A.S);
   if (A.dbg_scores)
-    hipLaunchKernelGGL(k_prefill_pair<true>, dim3(grid), dim3(kWG), 0, stream, A);
+    hipLaunchKernelGGL(k_prefill_pair<kPairDebug>, dim3(grid), dim3(kWG), 0, stream, A);
   else
-    hipLaunchKernelGGL(k_prefill_pair<false>, dim3(grid), dim3(kWG), 0, stream, A);
+    hipLaunchKernelGGL(k_prefill_pair<kPairFused>, dim3(grid), dim3(kWG), 0, stream, A);
   if (A.ev_main_stop && hipEventRecord(A.ev_main_stop, stream) != hipSuccess) return IDX_EHIP;
   hipLaunchKernelGGL(k_prefill_select, dim3(A.Q), dim3(kWG), 0, stream, A);
   hipLaunchKernelGGL(k_prefill_repair_score, dim3(kRepairGrid), dim3(kWG), 0, stream, A);
@@ -663,6 +671,24 @@ int launch_prefill(const PrefillArgs& A, hipStream_t stream) {
   hipLaunchKernelGGL(k_prefill_repair_ties, dim3(kRepairGrid), dim3(kWG), 0, stream, A);
   hipLaunchKernelGGL(k_prefill_repair_emit, dim3(kRepairGrid), dim3(kWG), 0, stream, A);
   return hipGetLastError() == hipSuccess ? IDX_OK : IDX_EHIP;
+}
+
+// Unfused comparator ("2.1 Where the cost goes"): the same MFMA scoring
+// writes the whole [Q,N] FP32 score matrix to A.dbg_scores, then the
+// dense-matrix top-K selects each row from it.  The sampler kernel runs
+// only to clear the control words (its forced threshold is unused).
+int launch_prefill_unfused(const PrefillArgs& A, hipStream_t stream) {
+  if (A.Q == 0) return IDX_OK;
+  const int64_t nchunks = (int64_t)((A.N + 63) >> 6) * 512;
+  if (nchunks > 0) hipLaunchKernelGGL(k_relayout_keys, dim3((unsigned)(nchunks / kWG)), dim3(kWG), 0, stream, A);
+  hipLaunchKernelGGL(k_prefill_tau, dim3((A.Q + kWaves - 1) / kWaves), dim3(kWG), 0, stream, A);
+  if (A.ev_main_start && hipEventRecord(A.ev_main_start, stream) != hipSuccess) return IDX_EHIP;
+  const unsigned grid = (unsigned)((A.Q + 1) / 2 * A.S);
+  hipLaunchKernelGGL(k_prefill_pair<kPairDense>, dim3(grid), dim3(kWG), 0, stream, A);
+  if (A.ev_main_stop && hipEventRecord(A.ev_main_stop, stream) != hipSuccess) return IDX_EHIP;
+  if (hipGetLastError() != hipSuccess) return IDX_EHIP;
+  RowsArgs R{A.dbg_scores, (int64_t)A.N, A.row_start, A.row_end, A.Q, A.N, A.K, A.out, A.ctrl};
+  return launch_topk_rows(R, stream);
 }
 
 }  // namespace idxk

@@ -91,3 +91,25 @@ def test_host_argument_errors(lib):
     assert d(*dargs(B=0)) == 0
     lib.idx_topk_strerror.restype = ctypes.c_char_p
     assert lib.idx_topk_strerror(-3) == b"workspace missing or too small"
+
+
+def test_unfused_and_rows_argument_errors(lib):
+    vp = ctypes.c_void_p
+    lib.idx_topk_prefill_unfused_workspace.restype = ctypes.c_size_t
+    fused = lib.idx_topk_prefill_workspace(4096, 131072, 2048)
+    unf = lib.idx_topk_prefill_unfused_workspace(4096, 131072, 2048)
+    assert unf >= fused + 4096 * 131072 * 4        # plus the dense score matrix
+    assert lib.idx_topk_prefill_unfused_workspace(4, 100, 0) == 0
+    r = lib.idx_topk_rows
+    r.restype = ctypes.c_int
+    r.argtypes = [vp, ctypes.c_int64, vp, vp, ctypes.c_int32, vp, ctypes.c_int32, ctypes.c_int32, vp]
+    good = vp(1 << 20)
+    rargs = lambda **kw: [kw.get("s", good), kw.get("ld", 100), good, good, kw.get("K", 64), good,
+                          kw.get("Q", 4), kw.get("N", 100), None]
+    assert r(*rargs(K=0)) == -1
+    assert r(*rargs(K=2049)) == -1
+    assert r(*rargs(ld=99)) == -1                     # row stride below N
+    assert r(*rargs(s=vp((1 << 20) + 4))) == -1       # scores not 16-byte aligned
+    assert r(*rargs(s=None)) == -1
+    assert r(*rargs(N=1 << 30, ld=1 << 30)) == -2     # rows longer than a buffer resource reaches
+    assert r(*rargs(Q=0)) == 0
