@@ -3,7 +3,8 @@
 One step = one complete operator call over one batch of seeded synthetic
 input already resident in HBM: for prefill the threshold sampler, the fused
 main kernel and the exact repair (idx_topk_prefill); for paged decode the
-prep, split and repair kernels (idx_topk_decode_paged).  Throughput counts
+split scoring kernel and the per-sequence exact selection
+(idx_topk_decode_paged).  Throughput counts
 the scoring the valid ranges require (Fusing Indexer Scoring and Exact Top-k
 page, "5.1 Version trajectory" equation): pairs = sum over rows of the range
 length, 2*64*128 FLOP per pair.
@@ -13,7 +14,7 @@ pair of HIP events recorded on the call's stream right around the dominant
 kernel; kernels and arguments are otherwise those of the plain entry points.
 
 Prints ONE JSON line.  The roofline object is for the dominant kernel:
-k_prefill_pair (bound by FP8 MFMA) for prefill, k_decode_split (bound by
+k_prefill_pair (bound by FP8 MFMA) for prefill, k_decode_score (bound by
 HBM) for decode.
 """
 from __future__ import annotations
@@ -134,7 +135,8 @@ def calibrate_copy(mib: int):
 
 def timed(step, n_calls: int, steps: int, warmup: int):
     """Run `warmup` untimed steps, then `steps` timed ones bracketed by
-    synchronisation; step(evs) records evs[j] around call j's dominant
+    synchronisation, without any event inside the steps (ms per step); then
+    `steps` more in which step(evs) records evs[j] around call j's dominant
     kernel.  Returns (ms per step, mean dominant-kernel ms per launch, min)."""
     evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
             for _ in range(n_calls)] for _ in range(steps)]
@@ -149,10 +151,13 @@ def timed(step, n_calls: int, steps: int, warmup: int):
     t_end = torch.cuda.Event(enable_timing=True)
     t_begin.record()
     for s in range(steps):
-        step(evs[s])
+        step(None)
     t_end.record()
     torch.cuda.synchronize()
     ms_per_step = t_begin.elapsed_time(t_end) / steps
+    for s in range(steps):
+        step(evs[s])
+    torch.cuda.synchronize()
     per_step = [sum(e0.elapsed_time(e1) for e0, e1 in step_evs) for step_evs in evs]
     return ms_per_step, float(np.mean(per_step)) / n_calls, min(per_step) / n_calls
 
@@ -272,15 +277,18 @@ def bench_unfused(args, lib):
     return res
 
 
-def decode_split_bytes(case) -> int:
-    """Algorithmic bytes of k_decode_split: every scored sequence (L > K)
+def decode_score_bytes(case) -> int:
+    """Algorithmic bytes of k_decode_score: every scored sequence (L > K)
     reads its keys (128 B codes + 4 B scale each), its page-table entries,
-    its query (64x128 B), weights and q scales (2 x 64 x 4 B), and writes K
-    output ids; shorter sequences take the remap path outside this kernel."""
+    its query (64x128 B), weights and q scales (2 x 64 x 4 B), and writes one
+    FP32 score per key; shorter sequences only have their page ids checked
+    (4 B per page) and take the remap path in the selection kernel."""
     n = 0
     for L in case.seq_lens.astype(np.int64):
         if L > case.K:
-            n += L * 132 + ((L + 63) // 64) * 4 + 64 * 128 + 2 * 64 * 4 + case.K * 4
+            n += L * 132 + ((L + 63) // 64) * 4 + 64 * 128 + 2 * 64 * 4 + L * 4
+        else:
+            n += ((L + 63) // 64) * 4
     return int(n)
 
 
@@ -299,17 +307,17 @@ def bench_decode(args, lib):
 
     ms_per_step, main_avg, main_min = timed(step, 1, args.steps, args.warmup)
     log("workload", args.workload, "keys", case.pairs, "ms/step %.4f" % ms_per_step,
-        "split kernel ms/launch %.4f (min %.4f)" % (main_avg, main_min))
+        "scoring kernel ms/launch %.4f (min %.4f)" % (main_avg, main_min))
     log("  ", case.name, lib.read_stats(ws))
-    nbytes = decode_split_bytes(case)
+    nbytes = decode_score_bytes(case)
     achieved = nbytes / (main_avg * 1e-3) / 1e9
     config = {"workload": case.name, "batch": case.B, "keys": case.pairs,
               "max_seq_len": int(case.seq_lens.max()), "page_size": case.page_size, "heads": 64,
               "dim": 128, "K": case.K, "pairs": case.pairs, "calls_per_step": 1}
     roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": achieved / HBM_PEAK_GBS,
-                "traffic": stored_traffic("k_decode_split", args.workload),
-                "kernel": "k_decode_split", "ms_per_launch": main_avg,
+                "traffic": stored_traffic("k_decode_score", args.workload),
+                "kernel": "k_decode_score", "ms_per_launch": main_avg,
                 "algorithmic_bytes": nbytes}
     res = result(args, case.pairs / (ms_per_step * 1e-3) / 1e9, ms_per_step, config, roofline,
                  "fp8_e4m3 x fp8_e4m3 -> f32")

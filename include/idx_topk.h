@@ -193,8 +193,13 @@ size_t idx_topk_decode_workspace(int32_t B, int32_t max_pages, int32_t page_size
  *   seq_lens   [B] int32 (device), 0 <= seq_len <= max_pages * page_size
  *   page_size  must be 64
  *   out_idx    [B][K] int32: physical cache slots page*page_size + slot of the
- *              selected keys, unsorted, -1 padded.  Sequences with
+ *              selected keys, unsorted, -1 padded; ties at the K-th score go
+ *              to the lowest logical positions.  Sequences with
  *              seq_len <= K take the remap path: all their slots, no scoring.
+ *              A sequence whose length is out of range or whose used page
+ *              ids are outside [0, num_pages) gets all -1 (bad_rows count).
+ * The keys are scored into a [B][max_pages*page_size] FP32 row per sequence in
+ * the workspace, then each row is selected exactly (no threshold, no repair).
  */
 int idx_topk_decode_paged(const uint8_t *q, const float *q_scale, const uint8_t *k_cache,
                           const float *k_scale, const float *w, const int32_t *page_table,
@@ -203,11 +208,10 @@ int idx_topk_decode_paged(const uint8_t *q, const float *q_scale, const uint8_t 
                           void *workspace, size_t workspace_bytes, void *stream);
 
 /*
- * Same as idx_topk_decode_paged, plus diagnostics for tests and timing.
- * opts (NULL = none) is read as follows: force_tau/tau_value replace every
- * scored sequence's sampled threshold (so that tests can force the repair
- * path); ev_main_start/ev_main_stop are recorded right before and right
- * after the split scoring kernel; lds_cap and spill_cap are ignored.
+ * Same as idx_topk_decode_paged, plus timing: opts (NULL = none) may carry
+ * ev_main_start/ev_main_stop, recorded right before and right after the
+ * split scoring kernel.  The decode path has no threshold and no capacity
+ * knobs: opts with force_tau, lds_cap or spill_cap set gives IDX_EINVAL.
  */
 int idx_topk_decode_paged_debug(const uint8_t *q, const float *q_scale, const uint8_t *k_cache,
                                 const float *k_scale, const float *w, const int32_t *page_table,

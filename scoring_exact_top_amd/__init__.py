@@ -227,8 +227,10 @@ def decode_paged(q8, q_scale, k_cache, k_scale, w, page_table, seq_lens, K: int,
 
     q8 [B,64,128], q_scale [B,64] or None, k_cache [P,64,128], k_scale [P,64],
     w [B,64], page_table [B,max_pages] int32, seq_lens [B] int32 (device).
-    force_tau / main_events select idx_topk_decode_paged_debug (a forced
-    threshold; a (start, stop) torch.cuda.Event pair around the split kernel).
+    main_events selects idx_topk_decode_paged_debug with a (start, stop)
+    torch.cuda.Event pair around the scoring kernel; force_tau is passed
+    through so that the library's rejection of it (decode has no threshold)
+    can be tested.
     """
     q8, k_cache = _q_k(q8, k_cache)
     B = int(q8.shape[0])

@@ -443,11 +443,34 @@ __device__ __forceinline__ float tile_epilogue(const QOp& o, const v4f (&acc)[20
   return reduce_scatter4(p[0], p[1], p[2], p[3]);
 }
 
-// Score of the tile (lane l: key l), k_scale applied.
+// Score of the tile (lane l: key l), k_scale applied.  Same arithmetic as
+// tile_mfma + tile_epilogue, pipelined by sub-tile: the MFMAs of sub-tile
+// c+1 are issued before the epilogue of sub-tile c, so only two sub-tiles'
+// accumulators (40 VGPRs instead of 80) are live at once.
 __device__ __forceinline__ float tile_score(const QOp& o, const KeyTile& t) {
-  v4f acc[20];
-  tile_mfma(o, t.kb, acc);
-  return tile_epilogue(o, acc) * t.ks;
+  const v4f z = {0.f, 0.f, 0.f, 0.f};
+  v4f acc[2][5];
+  const auto issue = [&](v4f (&a)[5], const v8i& kb) {
+#pragma unroll
+    for (int b = 0; b < 4; ++b) a[b] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(o.a[b], kb, z, 0, 0, 0, 0, 0, 0);
+    a[4] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(o.au, kb, z, 0, 0, 0, 0, 0, 0);
+  };
+  float p[4];
+  issue(acc[0], t.kb[0]);
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    if (c < 3) issue(acc[(c + 1) & 1], t.kb[c + 1]);
+    const v4f (&a)[5] = acc[c & 1];
+    float x = 0.f;
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) x = fmaf(o.wh[4 * b + r], fabsf(a[b][r]), x);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) x = fmaf(o.sh[r], a[4][r], x);
+    p[c] = x;
+  }
+  return reduce_scatter4(p[0], p[1], p[2], p[3]) * t.ks;
 }
 
 // ------------------------------------------------------------- histograms
@@ -684,7 +707,7 @@ struct RangeSel {
 // the search.  Requires 1 <= rem < number of keys.  All threads of the
 // workgroup call this.
 template <int M, class KF>
-__device__ RangeSel range_select_regs(const KF& kf, const RegLayout& lay, int rem, SelShared& sh, int tid) {
+__device__ __forceinline__ RangeSel range_select_regs(const KF& kf, const RegLayout& lay, int rem, SelShared& sh, int tid) {
   const uint32_t lane = tid & 63;
   const int wave = tid >> 6;
   uint32_t mn = 0xFFFFFFFFu, mx = 0u;
@@ -744,7 +767,7 @@ __device__ RangeSel range_select_regs(const KF& kf, const RegLayout& lay, int re
 // when the boundary range is taken whole or holds one value.  All threads
 // of the workgroup call this.
 template <int M, class KF>
-__device__ uint32_t range_min_regs(const KF& kf, const RegLayout& lay, const RangeSel& sel, SelShared& sh,
+__device__ __forceinline__ uint32_t range_min_regs(const KF& kf, const RegLayout& lay, const RangeSel& sel, SelShared& sh,
                                    int tid) {
   const uint32_t lane = tid & 63;
   const int wave = tid >> 6;
@@ -769,7 +792,7 @@ __device__ uint32_t range_min_regs(const KF& kf, const RegLayout& lay, const Ran
 // ~id is nonzero and the select ends with the rem largest ~id taken whole).
 // Returns the smallest ~id taken (0: no tie-break, every boundary key).
 template <int M>
-__device__ uint32_t tie_bound_regs(const uint32_t (&key)[M], const int32_t (&id)[M], const RegLayout& lay,
+__device__ __forceinline__ uint32_t tie_bound_regs(const uint32_t (&key)[M], const int32_t (&id)[M], const RegLayout& lay,
                                    const RangeSel& sel, SelShared& sh, int tid) {
   if (sel.rem >= sel.group) return 0u;
   const uint32_t v = sel.lo;
@@ -785,7 +808,7 @@ __device__ uint32_t tie_bound_regs(const uint32_t (&key)[M], const int32_t (&id)
 // timing.  At most 64 slots per thread and 65535 keys per list (two 16-bit
 // counts share a word).
 template <int M, class IdMap>
-__device__ void emit_range_regs(const uint32_t (&key)[M], const int32_t (&id)[M], const RegLayout& lay,
+__device__ __forceinline__ void emit_range_regs(const uint32_t (&key)[M], const int32_t (&id)[M], const RegLayout& lay,
                                 const RangeSel& sel, uint32_t idlo, int kr, int K, int32_t* out,
                                 const IdMap& idmap, SelShared& sh, int tid) {
   static_assert(M <= 64, "one lane per register slot");

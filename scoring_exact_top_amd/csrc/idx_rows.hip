@@ -9,12 +9,12 @@
 //      256 scores spread over it, c = a sample key with about 2K of the
 //      row's keys expected at or above it (the page's sampled threshold,
 //      "3.2 Sampled threshold", applied to an explicit score row);
-//   1. one streaming pass gathers every key >= c into LDS; with K to
-//      kRowsCap of them, the register-resident range select over the
-//      gathered keys finishes the row (ties at the K-th score to the lowest
-//      ids): one read of the row in all.
-// Otherwise (a short row without a sample, or a cut that kept too few or
-// too many keys) two more passes: a 2048-bin histogram of the top 11 bits
+//   1. one streaming pass gathers every key >= c into LDS (a row shorter
+//      than the sample, c = key 0: all of it), each wave into a private
+//      segment with a scalar count; with K to kRowsCap of them, the
+//      register-resident range select over the gathered keys finishes the
+//      row (ties at the K-th score to the lowest ids): one read of the row.
+// Otherwise (a cut that kept too few or too many keys) two more passes: a 2048-bin histogram of the top 11 bits
 // of the order-preserving keys (>= c when c kept too many) finds the bin b
 // of the K-th largest key ("3.2": radix select on order-preserving 32-bit
 // integers); the next pass writes out every key in a bin above b and
@@ -30,26 +30,29 @@ constexpr int kRowsBins = 2048;
 constexpr int kRowsShift = 21;  // 32 - 11 bits
 constexpr int kRowsCap = 6144;  // gathered keys held in LDS
 constexpr int kRowsRegs = kRowsCap / kWG;
-constexpr int kRowsUnroll = 4;  // 16-byte loads per thread per pass step (two steps in flight)
+constexpr int kSegCap = kRowsCap / kWaves;  // one-pass gather: a private segment per wave
 constexpr int kSampleBlocks = 16;  // sample: 16 blocks of kWG scores
 constexpr int kSampleKeys = kSampleBlocks * kWG;
-constexpr int kSampleMinLen = 4 * kSampleKeys;  // shorter rows are not sampled
+constexpr int kSampleMinLen = kSampleKeys;  // shorter rows (< kRowsCap keys) are gathered whole
 
-// Dense row in memory: element i is position s0 + i.
+// Dense row in memory: element i is position s0 + i, emitted as ids(s0 + i).
+template <class IdMap>
 struct SrcDense {
   const float* row;
   int32_t s0;
+  IdMap ids;
   __device__ uint32_t key(int i) const { return f2key(row[i]); }
-  __device__ int32_t id(int i) const { return s0 + i; }
+  __device__ int32_t id(int i) const { return ids(s0 + i); }
 };
 
 // Calls f(i, valid, key) for every element i < L of the row (and for some
 // positions outside it with valid = false), reading it with 16-byte buffer
 // loads from the 16-byte-aligned address at or below the row's start (reads
-// past the end return 0); the next step's loads are issued before this
-// step's keys are processed.
-template <class F>
+// past the end return 0), U loads per thread per step; the next step's
+// loads are issued before this step's keys are processed.
+template <int U, class F>
 __device__ __forceinline__ void for_each_key(const float* row, int L, int tid, const F& f) {
+  constexpr int kRowsUnroll = U;
   const int shift = (int)(((uintptr_t)row & 15u) >> 2);  // elements before the row in its first 16 bytes
   const float* abase = row - shift;
   const int span = L + shift;
@@ -60,23 +63,90 @@ __device__ __forceinline__ void for_each_key(const float* row, int L, int tid, c
     for (int u = 0; u < kRowsUnroll; ++u)
       v[u] = __builtin_amdgcn_raw_buffer_load_b128(rr, (base + (u * kWG + tid) * 4) * 4, 0, 0);
   };
-  v4i cur[kRowsUnroll];
-  load(cur, 0);
-  for (int base = 0; base < span; base += kStep) {
-    v4i nxt[kRowsUnroll];
-    load(nxt, base + kStep);
+  const auto process = [&](const v4i (&v)[kRowsUnroll], int base) {
 #pragma unroll
     for (int u = 0; u < kRowsUnroll; ++u) {
       const int i0 = base + (u * kWG + tid) * 4 - shift;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int i = i0 + e;
-        f(i, i >= 0 && i < L, f2key(__int_as_float(cur[u][e])));
+        f(i, i >= 0 && i < L, f2key(__int_as_float(v[u][e])));
       }
     }
-#pragma unroll
-    for (int u = 0; u < kRowsUnroll; ++u) cur[u] = nxt[u];
+  };
+  // two buffers in turn, no copy between them: a register copy of a load's
+  // result would wait for that load (the memory counter retires in order)
+  v4i a[kRowsUnroll], b[kRowsUnroll];
+  load(a, 0);
+  for (int base = 0; base < span; base += 2 * kStep) {
+    load(b, base + kStep);
+    process(a, base);
+    load(a, base + 2 * kStep);
+    process(b, base + kStep);
   }
+}
+
+// Gathers the keys >= cut of the row into this wave's segment (lkey/lid
+// point at it, kSegCap entries) and returns how many there were (more than
+// kSegCap: the excess was not stored).  Same loads as for_each_key; per
+// step each thread counts its qualifying keys, a wave scan turns the counts
+// into slots after the wave's running total, and each thread stores its
+// keys there: vector instructions only, no branch or atomic per key.
+template <int U>
+__device__ __forceinline__ uint32_t gather_ge(const float* row, int L, int tid, uint32_t cut, uint32_t* lkey,
+                                              int32_t* lid, int32_t s0) {
+  const uint32_t lane = tid & 63;
+  const int shift = (int)(((uintptr_t)row & 15u) >> 2);
+  const float* abase = row - shift;
+  const int span = L + shift;
+  const rsrc_t rr = __builtin_amdgcn_make_buffer_rsrc((void*)abase, (short)0, span * 4, 0x00020000);
+  constexpr int kStep = kWG * 4 * U;
+  const auto load = [&](v4i (&v)[U], int base) {
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      v[u] = __builtin_amdgcn_raw_buffer_load_b128(rr, (base + (u * kWG + tid) * 4) * 4, 0, 0);
+  };
+  const auto take = [&](int i, int v) { return i >= 0 && i < L && f2key(__int_as_float(v)) >= cut; };
+  uint32_t wcnt = 0u;
+  const auto step = [&](const v4i (&cur)[U], int base) {
+    uint32_t cnt = 0u;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i0 = base + (u * kWG + tid) * 4 - shift;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) cnt += take(i0 + e, cur[u][e]) ? 1u : 0u;
+    }
+    uint32_t inc = cnt;  // inclusive scan over the wave's lanes
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const uint32_t x = (uint32_t)__shfl_up((int)inc, off, 64);
+      if (lane >= (uint32_t)off) inc += x;
+    }
+    uint32_t slot = wcnt + inc - cnt;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i0 = base + (u * kWG + tid) * 4 - shift;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const bool g = take(i0 + e, cur[u][e]);
+        if (g && slot < (uint32_t)kSegCap) {
+          lkey[slot] = f2key(__int_as_float(cur[u][e]));
+          lid[slot] = s0 + i0 + e;
+        }
+        slot += g ? 1u : 0u;
+      }
+    }
+    wcnt += (uint32_t)__builtin_amdgcn_readlane((int)inc, 63);
+  };
+  v4i a[U], b[U];  // in turn, no copy between them (see for_each_key)
+  load(a, 0);
+  for (int base = 0; base < span; base += 2 * kStep) {
+    load(b, base + kStep);
+    step(a, base);
+    load(a, base + 2 * kStep);
+    step(b, base + kStep);
+  }
+  return wcnt;
 }
 
 struct RowsShared {
@@ -86,146 +156,319 @@ struct RowsShared {
   };
   int32_t lid[kRowsCap];
   uint32_t n_gt, n_eq, bin, above, inbin, pad[3];
+  uint32_t segc[kWaves];  // keys each wave's gather segment received
   SelShared sh;
 };
 
-// Exact selection of the rem largest of the n gathered keys (ties to the
-// lowest ids), written to out[0, rem).  1 <= rem <= n <= kRowsCap.  All
-// threads call this.
-__device__ void select_gathered(RowsShared& S, uint32_t n, int rem, int32_t* out, int tid) {
+// Step 0: the sampled cut of a row of length L > K (key 0 keeps every key):
+// the r-th largest of kSampleKeys sampled keys, r chosen so that about 2K
+// of the row's keys are expected at or above it.  All threads call this.
+__device__ __forceinline__ uint32_t sample_cut(const float* row, int L, int K, SelShared& sh, int tid) {
+  if (L < kSampleMinLen) return 0u;
+  uint32_t sk[kSampleBlocks];
+  const int step = (L - kWG) / (kSampleBlocks - 1);  // block j starts at j*step
+#pragma unroll
+  for (int j = 0; j < kSampleBlocks; ++j) sk[j] = f2key(row[j * step + tid]);
+  // rank r in the sample <=> about r * L / kSampleKeys keys of the row
+  const int r = (int)(((int64_t)2 * K * kSampleKeys + L - 1) / L);
+  if (r >= kSampleKeys) return 0u;
+  const RegLayout lay{(uint32_t)tid, (uint32_t)kWG, (uint32_t)kSampleKeys, (uint32_t)kSampleBlocks};
+  return range_select_regs<kSampleBlocks>([&](int j) { return sk[j]; }, lay, r, sh, tid).lo;
+}
+
+// Exact selection of the rem largest of the gathered keys (ties to the
+// lowest positions), ids(position) written to out[0, rem).  The keys sit in
+// kWaves segments of lkey/lid: segment w holds c[w] keys from w*stride (the
+// histogram path passes one segment).  1 <= rem <= n = sum of c[w] <=
+// kRowsCap.  All threads call this.
+template <class IdMap>
+__device__ __forceinline__ void select_gathered(RowsShared& S, const uint32_t (&c)[kWaves], uint32_t stride,
+                                                int rem, int32_t* out, const IdMap& ids, int tid) {
+  const uint32_t n = c[0] + c[1] + c[2] + c[3];
   const RegLayout lay = block_list_layout(n, (uint32_t)tid);
   uint32_t key[kRowsRegs];
   int32_t id[kRowsRegs];
 #pragma unroll
   for (int j = 0; j < kRowsRegs; ++j) {
+    uint32_t x = lay.at(j), at = x;  // list element x -> its segment slot
+    bool later = true;               // x lies beyond the segments seen so far
+#pragma unroll
+    for (int w = 0; w < kWaves - 1; ++w) {
+      later = later && x >= c[w];
+      x = later ? x - c[w] : x;
+      at = later ? x + (uint32_t)(w + 1) * stride : at;
+    }
     const bool v = lay.valid(j);
-    key[j] = v ? S.lkey[lay.at(j)] : 0u;
-    id[j] = v ? S.lid[lay.at(j)] : 0;
+    key[j] = v ? S.lkey[at] : 0u;
+    id[j] = v ? S.lid[at] : 0;
   }
   const auto kf = [&](int j) { return key[j]; };
   const RangeSel sel = (n > (uint32_t)rem) ? range_select_regs<kRowsRegs>(kf, lay, rem, S.sh, tid)
                                             : RangeSel{1u, 0xFFFFFFFFu, rem, (int)n};
   const uint32_t idlo = tie_bound_regs(key, id, lay, sel, S.sh, tid);
-  emit_range_regs(key, id, lay, sel, idlo, rem, rem, out, IdIdentity{}, S.sh, tid);
+  emit_range_regs(key, id, lay, sel, idlo, rem, rem, out, ids, S.sh, tid);
 }
 
-__global__ __launch_bounds__(kWG, 3) void k_topk_rows(RowsArgs A) {
+// Rows of a dense matrix: row t is scores + t*ld, range [row_start[t],
+// row_end[t]), ids are positions.
+struct DenseRows {
+  static constexpr int kUnroll = 4;  // many rows: workgroups enough to cover the latency
+  static constexpr int kMinBlocks = 3;
+  RowsArgs A;
+  __device__ __forceinline__ bool range(int t, int& s0, int& s1, int) const {
+    s0 = A.row_start[t];
+    s1 = A.row_end[t];
+    return s0 >= 0 && s0 <= s1 && s1 <= A.N;
+  }
+  __device__ __forceinline__ const float* row(int t) const { return A.scores + (int64_t)t * A.ld; }
+  __device__ __forceinline__ IdIdentity ids(int) const { return IdIdentity{}; }
+};
+
+// Sequences of the paged decode: row b holds the scores of logical positions
+// [0, seq_lens[b]) at scores + b*ld; it is invalid when its length is out of
+// range or a workgroup of the scoring kernel flagged a bad page id; ids are
+// physical cache slots.
+struct PagedRows {
+  static constexpr int kUnroll = 16;  // few long rows: one workgroup must cover the latency alone
+  static constexpr int kMinBlocks = 1;
+  RowsArgs A;
+  // all threads call this (one flag per thread, then a workgroup OR)
+  __device__ __forceinline__ bool range(int b, int& s0, int& s1, int tid) const {
+    s0 = 0;
+    s1 = A.row_end[b];
+    bool bad = s1 < 0 || s1 > A.N;
+    for (int g = tid; g < A.nflags; g += kWG) bad |= A.flags[(int64_t)b * A.nflags + g] != 0u;
+    return !__syncthreads_or(bad);
+  }
+  __device__ __forceinline__ const float* row(int b) const { return A.scores + (int64_t)b * A.ld; }
+  __device__ __forceinline__ IdPaged ids(int b) const { return IdPaged{A.table + (int64_t)b * A.max_pages}; }
+};
+
+// Dense rows come by the thousand: three workgroups per CU (LDS allows
+// three) keep enough loads in flight.  Paged decode rows are few and long:
+// one workgroup per row with deeper loads and no occupancy bound, so that
+// the register select does not spill.
+template <class Rows>
+__global__ __launch_bounds__(kWG, Rows::kMinBlocks) void k_topk_rows(RowsArgs A) {
   __shared__ RowsShared S;
+  const Rows R{A};
   const int tid = threadIdx.x;
   const int t = blockIdx.x;
   int32_t* out = A.out + (int64_t)t * A.K;
   uint32_t* stats = A.ctrl ? stat_copy(A.ctrl, blockIdx.x) : nullptr;
   if (stats && tid == 0) atomicAdd(&stats[kStRows], 1u);
-  const int s0 = A.row_start[t], s1 = A.row_end[t];
-  if (s0 < 0 || s0 > s1 || s1 > A.N) {
+  int s0, s1;
+  if (!R.range(t, s0, s1, tid)) {
     for (int i = tid; i < A.K; i += kWG) out[i] = -1;
     if (stats && tid == 0) atomicAdd(&stats[kStBad], 1u);
     return;
   }
   const int L = s1 - s0;
   const int K = A.K;
+  const auto ids = R.ids(t);
   if (L <= K) {  // every key of the row, in position order
-    for (int i = tid; i < K; i += kWG) out[i] = i < L ? s0 + i : -1;
+    for (int i = tid; i < K; i += kWG) out[i] = i < L ? ids(s0 + i) : -1;
     if (stats && tid == 0) atomicAdd(&stats[kStTrivial], 1u);
     return;
   }
-  const float* row = A.scores + (int64_t)t * A.ld + s0;
+  const float* row = R.row(t) + s0;
 
-  // step 0: the sampled cut (key 0 keeps every key)
-  uint32_t cut = 0u;
-  if (L >= kSampleMinLen) {
-    uint32_t sk[kSampleBlocks];
-    const int64_t span = (int64_t)L - kWG;
+  // pre-gathered regions that hold K to kRowsCap keys in all and each fit
+  // its threads' registers: select from them.  Region g is read by the
+  // 256/G threads g*256/G .. ; thread slot j holds region element
+  // (tid mod 256/G) + j*256/G.
+  if (A.gcnt) {
+    const int G = A.gsplit;  // a power of two <= kMaxGatherSplit
+    const uint32_t tpr = (uint32_t)(kWG / G);
+    const int g = tid / (int)tpr;
+    const uint32_t gc = A.gcnt[(int64_t)t * G + g];
+    uint32_t n = 0u;
+    block_exclusive_scan(tid % (int)tpr == 0 ? gc : 0u, S.sh, tid, n);
+    const bool fits = !__syncthreads_or(gc > tpr * (uint32_t)kRowsRegs);
+    if (fits && n >= (uint32_t)K) {
+      const RegLayout lay{(uint32_t)tid % tpr, tpr, gc, (uint32_t)kRowsRegs};
+      uint32_t key[kRowsRegs];
+      int32_t id[kRowsRegs];
+      const int64_t region = ((int64_t)t * G + g) * A.gcap;
 #pragma unroll
-    for (int j = 0; j < kSampleBlocks; ++j)
-      sk[j] = f2key(row[span * j / (kSampleBlocks - 1) + tid]);
-    // rank r in the sample <=> about r * L / kSampleKeys keys of the row
-    const int r = (int)(((int64_t)2 * K * kSampleKeys + L - 1) / L);
-    if (r < kSampleKeys) {
-      const RegLayout lay{(uint32_t)tid, (uint32_t)kWG, (uint32_t)kSampleKeys, (uint32_t)kSampleBlocks};
-      cut = range_select_regs<kSampleBlocks>([&](int j) { return sk[j]; }, lay, r, S.sh, tid).lo;
-    }
-  }
-
-  // step 1: one pass gathering the keys at or above the cut
-  if (cut) {
-    if (tid == 0) S.n_eq = 0u;
-    __syncthreads();
-    for_each_key(row, L, tid, [&](int i, bool v, uint32_t key) {
-      const bool ge = v && key >= cut;
-      if (__ballot(ge)) {
-        const uint32_t pe = reserve(&S.n_eq, ge);
-        if (ge && pe < (uint32_t)kRowsCap) { S.lkey[pe] = key; S.lid[pe] = s0 + i; }
+      for (int j = 0; j < kRowsRegs; ++j) {
+        const bool v = lay.valid(j);
+        key[j] = v ? A.gkey[region + lay.at(j)] : 0u;
+        id[j] = v ? A.gid[region + lay.at(j)] : 0;
       }
-    });
-    __syncthreads();
-    const uint32_t n = S.n_eq;
-    if (n >= (uint32_t)K && n <= (uint32_t)kRowsCap) {
-      select_gathered(S, n, K, out, tid);
+      const auto kf = [&](int j) { return key[j]; };
+      const RangeSel sel = (n > (uint32_t)K) ? range_select_regs<kRowsRegs>(kf, lay, K, S.sh, tid)
+                                              : RangeSel{1u, 0xFFFFFFFFu, K, (int)n};
+      const uint32_t idlo = tie_bound_regs(key, id, lay, sel, S.sh, tid);
+      emit_range_regs(key, id, lay, sel, idlo, K, K, out, ids, S.sh, tid);
       if (stats && tid == 0) atomicAdd(&stats[kStFast], 1u);
       return;
     }
+  }
+
+  // step 0: the sampled cut (key 0 keeps every key)
+  uint32_t cut = sample_cut(row, L, K, S.sh, tid);
+
+  // step 1: one pass gathering the keys at or above the cut into the
+  // waves' private segments (slot = the wave's scalar count + rank in the
+  // ballot: no atomics)
+  uint32_t c[kWaves] = {0u, 0u, 0u, 0u};  // keys in each segment
+  uint32_t stride = (uint32_t)kSegCap;
+  int rem = K;       // how many of them to take
+  int32_t* dst = out;
+  bool gathered = false;
+  {
+    const int wave = tid >> 6;
+    const uint32_t wcnt = gather_ge<Rows::kUnroll>(row, L, tid, cut, S.lkey + wave * kSegCap,
+                                                    S.lid + wave * kSegCap, s0);
+    if ((tid & 63) == 0) S.segc[wave] = wcnt;
+    __syncthreads();
+    uint32_t n = 0u;
+    bool full = false;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      c[w] = S.segc[w];
+      n += c[w];
+      full |= c[w] > (uint32_t)kSegCap;
+    }
+    gathered = n >= (uint32_t)K && !full;
     if (n < (uint32_t)K) cut = 0u;  // the cut kept too few keys: histogram the whole row
     __syncthreads();
   }
+  static_assert(kSampleMinLen <= kRowsCap, "unsampled rows must fit the gather");
 
-  // histogram path: the bin of the K-th largest key among keys >= cut
-  for (int i = tid; i < kRowsBins; i += kWG) S.hist[i] = 0u;
-  if (tid == 0) { S.n_gt = 0u; S.n_eq = 0u; }
-  __syncthreads();
-  for_each_key(row, L, tid, [&](int, bool v, uint32_t key) {
-    hist_add(S.hist, key >> kRowsShift, v && key >= cut);  // returns at once when no lane qualifies
-  });
-  __syncthreads();
-  {
-    // thread u holds bins 8u .. 8u+7
-    uint32_t h[8], a = 0u;
+  bool generic = false;  // the boundary bin does not fit in LDS
+  if (!gathered) {
+    // histogram path: the bin of the K-th largest key among keys >= cut
+    for (int i = tid; i < kRowsBins; i += kWG) S.hist[i] = 0u;
+    if (tid == 0) { S.n_gt = 0u; S.n_eq = 0u; }
+    __syncthreads();
+    for_each_key<Rows::kUnroll>(row, L, tid, [&](int, bool v, uint32_t key) {
+      hist_add(S.hist, key >> kRowsShift, v && key >= cut);  // returns at once when no lane qualifies
+    });
+    __syncthreads();
+    {
+      // thread u holds bins 8u .. 8u+7
+      uint32_t h[8], a = 0u;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) { h[j] = S.hist[8 * tid + j]; a += h[j]; }
-    uint32_t total;
-    const uint32_t before = block_exclusive_scan(a, S.sh, tid, total);
-    uint32_t ab = total - before - a;  // keys in bins above this thread's
-    const uint32_t r = (uint32_t)K;
-    if (ab < r && r <= ab + a) {
+      for (int j = 0; j < 8; ++j) { h[j] = S.hist[8 * tid + j]; a += h[j]; }
+      uint32_t total;
+      const uint32_t before = block_exclusive_scan(a, S.sh, tid, total);
+      uint32_t ab = total - before - a;  // keys in bins above this thread's
+      const uint32_t r = (uint32_t)K;
+      if (ab < r && r <= ab + a) {
 #pragma unroll
-      for (int j = 7; j >= 0; --j) {
-        if (ab < r && r <= ab + h[j]) { S.bin = 8u * tid + j; S.above = ab; S.inbin = h[j]; }
-        ab += h[j];
+        for (int j = 7; j >= 0; --j) {
+          if (ab < r && r <= ab + h[j]) { S.bin = 8u * tid + j; S.above = ab; S.inbin = h[j]; }
+          ab += h[j];
+        }
       }
     }
+    __syncthreads();
+    const uint32_t bin = S.bin, above = S.above, inbin = S.inbin;
+
+    // keys above the bin go straight out; the bin's keys (>= cut) to LDS
+    for_each_key<Rows::kUnroll>(row, L, tid, [&](int i, bool v, uint32_t key) {
+      const uint32_t d = key >> kRowsShift;
+      const bool gt = v && d > bin, eq = v && d == bin && key >= cut;
+      if (__ballot(gt || eq)) {
+        const uint32_t pg = reserve(&S.n_gt, gt);
+        if (gt) out[pg] = ids(s0 + i);
+        const uint32_t pe = reserve(&S.n_eq, eq);
+        if (eq && pe < (uint32_t)kRowsCap) { S.lkey[pe] = key; S.lid[pe] = s0 + i; }
+      }
+    });
+    __syncthreads();
+    c[0] = inbin; c[1] = 0u; c[2] = 0u; c[3] = 0u;
+    stride = 0u;
+    rem = K - (int)above;  // 1 <= rem <= inbin
+    dst = out + above;
+    generic = inbin > (uint32_t)kRowsCap;
   }
-  __syncthreads();
-  const uint32_t bin = S.bin, above = S.above, inbin = S.inbin;
 
-  // keys above the bin go straight out; the bin's keys (>= cut) to LDS
-  for_each_key(row, L, tid, [&](int i, bool v, uint32_t key) {
-    const uint32_t d = key >> kRowsShift;
-    const bool gt = v && d > bin, eq = v && d == bin && key >= cut;
-    if (__ballot(gt || eq)) {
-      const uint32_t pg = reserve(&S.n_gt, gt);
-      if (gt) out[pg] = s0 + i;
-      const uint32_t pe = reserve(&S.n_eq, eq);
-      if (eq && pe < (uint32_t)kRowsCap) { S.lkey[pe] = key; S.lid[pe] = s0 + i; }
-    }
-  });
-  __syncthreads();
-
-  const int rem = K - (int)above;  // 1 <= rem <= inbin
-  if (inbin <= (uint32_t)kRowsCap) {
-    select_gathered(S, inbin, rem, out + above, tid);
+  if (!generic) {
+    select_gathered(S, c, stride, rem, dst, ids, tid);
     if (stats && tid == 0) atomicAdd(&stats[kStFast], 1u);
   } else {
     // the bin does not fit: exact radix select over the row in memory
-    const SrcDense src{row, s0};
+    const SrcDense<decltype(ids)> src{row, s0, ids};
     const SelResult sel = radix_select(src, L, K, S.sh, tid, false, true);
     emit_selection(src, L, sel, K, K, out, S.sh, tid);
     if (stats && tid == 0) atomicAdd(&stats[kStRepaired], 1u);
   }
 }
 
+// Pre-gather of paged rows: workgroup (g, t) computes row t's sampled cut
+// (as the per-row kernel would) and stores the keys >= cut of slice g of
+// the row into its own region of the workspace: per step each thread
+// counts its keys and a workgroup scan gives the slots, with no atomics
+// (same-address device atomics from every workgroup of a row would queue
+// at one L2 line).  Spreads over many CUs the pass that one workgroup per
+// row would make alone.
+template <class Rows>
+__global__ __launch_bounds__(kWG) void k_rows_gather(RowsArgs A) {
+  __shared__ SelShared sh;
+  const Rows R{A};
+  const int tid = threadIdx.x;
+  const uint32_t lane = tid & 63;
+  const int g = blockIdx.x, t = blockIdx.y;
+  int s0, s1;
+  if (!R.range(t, s0, s1, tid)) return;
+  const int L = s1 - s0, K = A.K;
+  if (L <= K) return;
+  const float* row = R.row(t) + s0;
+  const uint32_t cut = sample_cut(row, L, K, sh, tid);
+  const int64_t lo = (int64_t)L * g / A.gsplit, hi = (int64_t)L * (g + 1) / A.gsplit;
+  const int64_t region = ((int64_t)t * A.gsplit + g) * A.gcap;
+  uint32_t* gk = A.gkey + region;
+  int32_t* gi = A.gid + region;
+  constexpr int U = 4;
+  constexpr int kStep = kWG * U;
+  uint32_t count = 0u;  // keys found so far in the slice (uniform)
+#pragma unroll 1
+  for (int64_t base = lo; base < hi; base += kStep) {
+    uint32_t k[U];
+    bool take[U];
+    uint32_t cnt = 0u;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t i = base + u * kWG + tid;
+      const bool v = i < hi;
+      k[u] = v ? f2key(row[v ? i : 0]) : 0u;
+      take[u] = v && k[u] >= cut;
+      cnt += take[u] ? 1u : 0u;
+    }
+    uint32_t total;
+    uint32_t slot = count + block_exclusive_scan(cnt, sh, tid, total);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (take[u] && slot < (uint32_t)A.gcap) {
+        gk[slot] = k[u];
+        gi[slot] = (int32_t)(base + u * kWG + tid) + s0;
+      }
+      slot += take[u] ? 1u : 0u;
+    }
+    count += total;
+  }
+  if (tid == 0) A.gcnt[(int64_t)t * A.gsplit + g] = count;
+}
+
+int launch_topk_rows_gathered(const RowsArgs& A, hipStream_t stream) {
+  if (A.Q == 0) return IDX_OK;
+  if (!A.table || !A.gkey || A.gsplit < 1 || A.gsplit > kMaxGatherSplit || (A.gsplit & (A.gsplit - 1)) ||
+      A.gcap * A.gsplit > kRowsCap)
+    return IDX_EINVAL;
+  hipLaunchKernelGGL(k_rows_gather<PagedRows>, dim3(A.gsplit, A.Q), dim3(kWG), 0, stream, A);
+  hipLaunchKernelGGL(k_topk_rows<PagedRows>, dim3(A.Q), dim3(kWG), 0, stream, A);
+  return hipGetLastError() == hipSuccess ? IDX_OK : IDX_EHIP;
+}
+
 int launch_topk_rows(const RowsArgs& A, hipStream_t stream) {
   if (A.Q == 0) return IDX_OK;
-  hipLaunchKernelGGL(k_topk_rows, dim3(A.Q), dim3(kWG), 0, stream, A);
+  if (A.table)
+    hipLaunchKernelGGL(k_topk_rows<PagedRows>, dim3(A.Q), dim3(kWG), 0, stream, A);
+  else
+    hipLaunchKernelGGL(k_topk_rows<DenseRows>, dim3(A.Q), dim3(kWG), 0, stream, A);
   return hipGetLastError() == hipSuccess ? IDX_OK : IDX_EHIP;
 }
 

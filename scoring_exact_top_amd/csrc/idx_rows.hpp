@@ -5,15 +5,37 @@
 
 namespace idxk {
 
+// Dense rows: row t's scores at scores + t*ld, position s at [s], range
+// [row_start[t], row_end[t]).  Paged decode rows (table != null): row b
+// covers logical positions [0, row_end[b]) (the sequence lengths, row_start
+// unused), is invalid when any of its nflags flags is set, and emits
+// physical slots table[b*max_pages + i/64]*64 + i%64.
 struct RowsArgs {
-  const float* scores;  // row t's scores at scores + t*ld; position s at [s]
+  const float* scores;
   int64_t ld;
   const int32_t* row_start;
   const int32_t* row_end;
   int32_t Q, N, K;
   int32_t* out;    // [Q][K]
   uint32_t* ctrl;  // control words with the stats copies, or null
+  const int32_t* table;
+  int32_t max_pages;
+  const uint32_t* flags;  // [Q][nflags]
+  int32_t nflags;
+  // Optional pre-gathered lists (paged rows): workgroup g of k_rows_gather
+  // (gsplit a power of two <= kMaxGatherSplit per row) stores the keys at or above the
+  // row's sampled cut found in slice g of the row into its own region
+  // (gcap entries) and their number into gcnt[t*gsplit + g].
+  uint32_t* gkey;  // [Q][gsplit][gcap] order-preserving keys, or null
+  int32_t* gid;    // [Q][gsplit][gcap] logical positions
+  uint32_t* gcnt;  // [Q][gsplit]
+  int32_t gcap, gsplit;
 };
+
+constexpr int kMaxGatherSplit = 32;
+
+// Launch the pre-gather (paged rows with gkey set) and the per-row select.
+int launch_topk_rows_gathered(const RowsArgs& A, hipStream_t stream);
 
 int launch_topk_rows(const RowsArgs& A, hipStream_t stream);
 

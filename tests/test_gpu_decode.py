@@ -64,33 +64,26 @@ def test_decode_bad_page_id():
     assert np.all(out[1] == -1) and st["bad_rows"] == 1
 
 
-def test_decode_forced_underflow_repairs():
-    """A threshold above every score leaves no candidates: every scored
-    sequence fails the certificate (underflow) and is repaired exactly."""
-    lens = [1500, 3000, 9000, 20000, 65536]
-    case = synth.decode_case("dec_under", lens, seed=33, max_pages=1024)
+def test_decode_row_paths():
+    """Sequence lengths around each limit of the per-sequence selection:
+    around K, rows gathered whole (below 4096 keys), sampled rows (one-pass
+    gather); every row exact, the counters add up."""
+    lens = [1500, 2049, 3000, 4095, 4096, 9000, 16384, 20000, 65536]
+    case = synth.decode_case("dec_paths", lens, seed=33, max_pages=1024)
     log("case", case.name, lens)
-    out, st = _run(case, force_tau=float("inf"))
+    out, st = _run(case)
     log("stats", st)
     scored = int(np.sum(case.seq_lens > case.K))
-    assert st["underflow"] == scored and st["repaired"] == scored and st["trivial"] == len(lens) - scored
+    assert st["fast_ok"] + st["repaired"] == scored and st["trivial"] == len(lens) - scored
     _check(case, out)
 
 
-def test_decode_forced_overflow_repairs():
-    """A threshold below every score takes every key.  The list holds 8192
-    candidates: sequences up to that length are selected on the fast path;
-    a longer one is certified only if no dropped key beats its selection
-    (8193 drops a single key), and the 40000-key sequence, which drops most
-    of its keys, is repaired."""
-    lens = [5000, 8192, 8193, 40000]
-    case = synth.decode_case("dec_over", lens, seed=34, max_pages=700)
-    log("case", case.name, lens)
-    out, st = _run(case, force_tau=float("-inf"))
-    log("stats", st)
-    assert st["overflow"] >= 1 and st["repaired"] == st["overflow"] and st["fast_ok"] >= 2
-    assert st["fast_ok"] + st["repaired"] == len(lens)
-    _check(case, out)
+def test_decode_rejects_a_threshold():
+    """Decode has no threshold: the debug knob is refused, not ignored."""
+    import scoring_exact_top_amd as lib
+    case = synth.decode_case("dec_tau", [3000], seed=34, max_pages=100)
+    with pytest.raises(lib.IdxTopkError):
+        _run(case, force_tau=1.0)
 
 
 def _tie_keys(case, seed):
@@ -105,18 +98,15 @@ def _tie_keys(case, seed):
     return case
 
 
-@pytest.mark.parametrize("force_tau", [None, float("inf")])
-def test_decode_ties_take_the_lowest_positions(force_tau):
-    """Massive ties at the K-th score: the selected physical slots are those
-    of the lowest tied logical positions, on the fast path (ties beyond the
-    candidate capacity are certified) and through the repair alike."""
+def test_decode_ties_take_the_lowest_positions():
+    """Massive ties at the K-th score (16 distinct keys): the selected
+    physical slots are those of the lowest tied logical positions; the tie
+    group exceeds the on-chip gather, so the generic radix path runs."""
     lens = [3000, 20000, 60000]
     case = _tie_keys(synth.decode_case("dec_ties", lens, seed=36, max_pages=1000), 37)
-    log("case", case.name, lens, "force_tau", force_tau)
-    out, st = _run(case) if force_tau is None else _run(case, force_tau=force_tau)
+    log("case", case.name, lens)
+    out, st = _run(case)
     log("stats", st)
-    if force_tau is None:
-        assert st["fast_ok"] == len(lens), st
     _, theta, sc = oracle.decode_case(case)
     for b, L in enumerate(case.seq_lens):
         L = int(L)
@@ -127,7 +117,7 @@ def test_decode_ties_take_the_lowest_positions(force_tau):
         check.check_debug_canonical(logical, sc[b].astype(np.float32), 0, L, case.K, where="seq %d" % b)
 
 
-def test_decode_main_events_time_the_split_kernel():
+def test_decode_main_events_time_the_scoring_kernel():
     import scoring_exact_top_amd as lib
     case = synth.decode_case("dec_ev", [3000, 70000 // 2], seed=35, max_pages=600)
     ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))

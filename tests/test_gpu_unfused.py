@@ -77,6 +77,38 @@ def test_rows_ties_and_bins():
     _check_rows(S, starts, ends, K, out, "ties")
 
 
+def _sample_mask(L):
+    """Positions of the dense top-K's sample: 16 blocks of 256 scores, block j
+    at j * ((L - 256) // 15) (restated here to build rows that fool it)."""
+    step = (L - 256) // 15
+    m = np.zeros(L, dtype=bool)
+    for j in range(16):
+        m[j * step: j * step + 256] = True
+    return m
+
+
+def test_rows_biased_samples_take_the_fallbacks():
+    """Rows built against the sampled cut: 600 huge values inside the sample
+    blocks (the cut keeps fewer than K keys: histogram over the whole row),
+    and 9000 huge values outside them (the cut keeps more than fit: histogram
+    above the cut), each with ragged, unaligned ranges."""
+    rng = np.random.default_rng(11)
+    N, K = 30000, 2048
+    S = rng.standard_normal((4, N)).astype(np.float32)
+    starts = np.array([0, 3, 0, 5])
+    ends = np.array([N, N - 2, N, N - 1])
+    for t in (0, 1):
+        L = ends[t] - starts[t]
+        inside = np.nonzero(_sample_mask(L))[0]
+        S[t, starts[t] + rng.choice(inside, 600, replace=False)] = 50.0 + rng.random(600).astype(np.float32)
+    for t in (2, 3):
+        L = ends[t] - starts[t]
+        outside = np.nonzero(~_sample_mask(L))[0]
+        S[t, starts[t] + rng.choice(outside, 9000, replace=False)] = 50.0 + rng.random(9000).astype(np.float32)
+    out = _rows(S, starts, ends, K)
+    _check_rows(S, starts, ends, K, out, "biased")
+
+
 def test_rows_invalid_ranges():
     S = np.zeros((3, 1000), dtype=np.float32)
     out = _rows(S, np.array([-1, 10, 5]), np.array([10, 5, 1001]), 16)
