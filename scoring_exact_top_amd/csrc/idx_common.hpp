@@ -796,7 +796,15 @@ __device__ __forceinline__ uint32_t tie_bound_regs(const uint32_t (&key)[M], con
                                    const RangeSel& sel, SelShared& sh, int tid) {
   if (sel.rem >= sel.group) return 0u;
   const uint32_t v = sel.lo;
-  const auto tk = [&](int j) { return key[j] == v ? ~(uint32_t)id[j] : 0u; };
+  // recomputed at every use (the empty asm hides the value from common
+  // subexpression elimination): a precomputed copy of all M values would
+  // stay live across the whole kernel and cost M registers where ties are
+  // rare
+  const auto tk = [&](int j) {
+    uint32_t x = (uint32_t)id[j];
+    asm volatile("" : "+v"(x));
+    return key[j] == v ? ~x : 0u;
+  };
   return range_select_regs<M>(tk, lay, sel.rem, sh, tid).lo;
 }
 
@@ -816,7 +824,11 @@ __device__ __forceinline__ void emit_range_regs(const uint32_t (&key)[M], const 
   const int wave = tid >> 6;
   const uint32_t width = sel.last - sel.lo;
   const auto gt = [&](int j) { return key[j] > sel.last; };
-  const auto eq = [&](int j) { return key[j] - sel.lo <= width && ~(uint32_t)id[j] >= idlo; };
+  const auto eq = [&](int j) {  // recomputed at every use, as in tie_bound_regs
+    uint32_t x = (uint32_t)id[j];
+    asm volatile("" : "+v"(x));
+    return key[j] - sel.lo <= width && ~x >= idlo;
+  };
   // lane j: this wave's winners in slot j (above | boundary << 16)
   uint32_t mine = 0u;
 #pragma unroll

@@ -354,7 +354,11 @@ __global__ __launch_bounds__(kWG) void k_prefill_select(PrefillArgs A) {
       const uint32_t theta = range_min_regs<kSelRegs>(kf, lay, sel, sh, tid);
       ok = drop <= theta;
       if (drop == theta) {  // tied keys were dropped: the taken ones must precede them
-        const auto tk = [&](int j) { return key[j] == theta && ~(uint32_t)id[j] >= idlo ? ~(uint32_t)id[j] : 0xFFFFFFFFu; };
+        const auto tk = [&](int j) {  // recomputed per use (see tie_bound_regs)
+          uint32_t x = (uint32_t)id[j];
+          asm volatile("" : "+v"(x));
+          return key[j] == theta && ~x >= idlo ? ~x : 0xFFFFFFFFu;
+        };
         uint32_t mn = 0xFFFFFFFFu;  // smallest ~id taken at theta = ~(largest id)
 #pragma unroll
         for (int j = 0; j < kSelRegs; ++j) mn = min(mn, tk(j));
