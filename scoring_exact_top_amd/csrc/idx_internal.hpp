@@ -56,7 +56,7 @@ __host__ __device__ inline int prefill_seg_cap(int S) {
 // workgroups that repair whole rows alone once the slots run out.
 constexpr int kRepairChunk = 4096;
 constexpr int kRepairChunkTiles = kRepairChunk / 64;
-constexpr int kRepairGrid = 1024;
+constexpr int kRepairGrid = 256;  // one workgroup per CU; items are strided over the grid
 constexpr int kRepairFallback = 256;
 constexpr int64_t kRepairScratchKeys = (int64_t)1 << 28;  // 1 GiB of scores
 
