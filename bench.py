@@ -136,8 +136,11 @@ def calibrate_copy(mib: int):
 def timed(step, n_calls: int, steps: int, warmup: int):
     """Run `warmup` untimed steps, then `steps` timed ones bracketed by
     synchronisation, without any event inside the steps (ms per step); then
-    `steps` more in which step(evs) records evs[j] around call j's dominant
-    kernel.  Returns (ms per step, mean dominant-kernel ms per launch, min)."""
+    `steps` more in which step(evs, reps) has call j launch its dominant
+    kernel `reps` times back to back with evs[j] recorded by the first and
+    the last launch (reps is chosen so that these spans last about 2 ms: one
+    dispatch's latency does not then dominate a small kernel's duration).
+    Returns (ms per step, mean dominant-kernel ms per launch, min)."""
     evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
             for _ in range(n_calls)] for _ in range(steps)]
     for step_evs in evs:  # torch creates the HIP events on first record
@@ -145,20 +148,21 @@ def timed(step, n_calls: int, steps: int, warmup: int):
             e0.record()
             e1.record()
     for _ in range(warmup):
-        step(None)
+        step(None, 1)
     torch.cuda.synchronize()
     t_begin = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     t_begin.record()
     for s in range(steps):
-        step(None)
+        step(None, 1)
     t_end.record()
     torch.cuda.synchronize()
     ms_per_step = t_begin.elapsed_time(t_end) / steps
+    reps = int(min(50, max(1, round(2.0 / (ms_per_step / n_calls)))))
     for s in range(steps):
-        step(evs[s])
+        step(evs[s], reps)
     torch.cuda.synchronize()
-    per_step = [sum(e0.elapsed_time(e1) for e0, e1 in step_evs) for step_evs in evs]
+    per_step = [sum(e0.elapsed_time(e1) for e0, e1 in step_evs) / reps for step_evs in evs]
     return ms_per_step, float(np.mean(per_step)) / n_calls, min(per_step) / n_calls
 
 
@@ -180,11 +184,11 @@ def bench_prefill(args, lib):
     wss = [lib.alloc_workspace(lib.prefill_workspace_bytes(c.Q, c.N, c.K), "cuda") for c in cases]
     n_calls = len(cases)
 
-    def step(step_evs):
+    def step(step_evs, reps):
         for j, (c, d) in enumerate(zip(cases, devs)):
             lib.prefill_debug(d["q8"], d["q_scale"], d["k8"], d["k_scale"], d["w"], d["row_start"],
                               d["row_end"], c.K, out=outs[j], workspace=wss[j],
-                              main_events=None if step_evs is None else step_evs[j])
+                              main_events=None if step_evs is None else step_evs[j], main_reps=reps)
 
     ms_per_step, main_avg, main_min = timed(step, n_calls, args.steps, args.warmup)
     log("workload", args.workload, "pairs", pairs, "ms/step %.4f" % ms_per_step,
@@ -223,21 +227,21 @@ def bench_unfused(args, lib):
     wsu = [lib.alloc_workspace(lib.prefill_unfused_workspace_bytes(c.Q, c.N, c.K), "cuda")
            for c in cases]
 
-    def step_unfused(step_evs):
+    def step_unfused(step_evs, reps):
         for j, (c, d) in enumerate(zip(cases, devs)):
             lib.prefill_unfused(d["q8"], d["q_scale"], d["k8"], d["k_scale"], d["w"],
                                 d["row_start"], d["row_end"], c.K, out=outs[j], workspace=wsu[j],
-                                main_events=None if step_evs is None else step_evs[j])
+                                main_events=None if step_evs is None else step_evs[j], main_reps=reps)
 
     ms_unf, score_avg, score_min = timed(step_unfused, n_calls, args.steps, args.warmup)
     del wsu
     wsf = [lib.alloc_workspace(lib.prefill_workspace_bytes(c.Q, c.N, c.K), "cuda") for c in cases]
 
-    def step_fused(step_evs):
+    def step_fused(step_evs, reps):
         for j, (c, d) in enumerate(zip(cases, devs)):
             lib.prefill_debug(d["q8"], d["q_scale"], d["k8"], d["k_scale"], d["w"], d["row_start"],
                               d["row_end"], c.K, out=outs[j], workspace=wsf[j],
-                              main_events=None if step_evs is None else step_evs[j])
+                              main_events=None if step_evs is None else step_evs[j], main_reps=reps)
 
     ms_fused, main_avg, _ = timed(step_fused, n_calls, args.steps, args.warmup)
     # standalone dense top-K over each call's score matrix
@@ -249,11 +253,12 @@ def bench_unfused(args, lib):
         mats.append(S)
     del wsf
 
-    def step_rows(step_evs):
+    def step_rows(step_evs, reps):
         for j, (c, d) in enumerate(zip(cases, devs)):
             if step_evs is not None:
                 step_evs[j][0].record()
-            lib.topk_rows(mats[j], d["row_start"], d["row_end"], c.K, out=outs[j])
+            for _ in range(reps):
+                lib.topk_rows(mats[j], d["row_start"], d["row_end"], c.K, out=outs[j])
             if step_evs is not None:
                 step_evs[j][1].record()
 
@@ -300,10 +305,10 @@ def bench_decode(args, lib):
     ws = lib.alloc_workspace(lib.decode_workspace_bytes(case.B, case.max_pages, case.page_size,
                                                         case.K), "cuda")
 
-    def step(step_evs):
+    def step(step_evs, reps):
         lib.decode_paged(d["q8"], d["q_scale"], d["k_cache"], d["k_scale"], d["w"], d["page_table"],
                          d["seq_lens"], case.K, out=out, workspace=ws,
-                         main_events=None if step_evs is None else step_evs[0])
+                         main_events=None if step_evs is None else step_evs[0], main_reps=reps)
 
     ms_per_step, main_avg, main_min = timed(step, 1, args.steps, args.warmup)
     log("workload", args.workload, "keys", case.pairs, "ms/step %.4f" % ms_per_step,

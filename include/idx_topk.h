@@ -96,8 +96,13 @@ typedef struct {
   float tau_value;
   int32_t lds_cap;     /* >0: on-chip candidate capacity per row (<= default)   */
   int32_t spill_cap;   /* >0: spill capacity per row (<= default); -1: none     */
-  void *ev_main_start; /* hipEvent_t or NULL: recorded on `stream` right before */
-  void *ev_main_stop;  /*   and right after the main scoring kernel (timing only) */
+  void *ev_main_start; /* hipEvent_t or NULL: recorded by the launch of the main  */
+  void *ev_main_stop;  /*   scoring kernel at its start and at its end (timing only) */
+  int32_t main_reps;   /* >1: the main scoring kernel is launched this many times
+                          back to back (it is idempotent), ev_main_start with the
+                          first launch and ev_main_stop with the last, so that a
+                          small kernel's average duration is not dominated by
+                          one dispatch (timing only; at most 1000)              */
 } idx_topk_opts;
 
 /* Bytes of workspace idx_topk_prefill needs for Q rows over N keys. */
@@ -209,8 +214,8 @@ int idx_topk_decode_paged(const uint8_t *q, const float *q_scale, const uint8_t 
 
 /*
  * Same as idx_topk_decode_paged, plus timing: opts (NULL = none) may carry
- * ev_main_start/ev_main_stop, recorded right before and right after the
- * split scoring kernel.  The decode path has no threshold and no capacity
+ * ev_main_start/ev_main_stop, recorded by the launch of the split scoring
+ * kernel at its start and at its end.  The decode path has no threshold and no capacity
  * knobs: opts with force_tau, lds_cap or spill_cap set gives IDX_EINVAL.
  */
 int idx_topk_decode_paged_debug(const uint8_t *q, const float *q_scale, const uint8_t *k_cache,

@@ -35,7 +35,8 @@ _sz = ctypes.c_size_t
 class Opts(ctypes.Structure):
     _fields_ = [("force_tau", ctypes.c_int32), ("tau_value", ctypes.c_float),
                 ("lds_cap", ctypes.c_int32), ("spill_cap", ctypes.c_int32),
-                ("ev_main_start", ctypes.c_void_p), ("ev_main_stop", ctypes.c_void_p)]
+                ("ev_main_start", ctypes.c_void_p), ("ev_main_stop", ctypes.c_void_p),
+                ("main_reps", ctypes.c_int32)]
 
 
 class Stats(ctypes.Structure):
@@ -142,16 +143,17 @@ def prefill(q8, q_scale, k8, k_scale, w, row_start, row_end, K: int, out=None, w
 def prefill_debug(q8, q_scale, k8, k_scale, w, row_start, row_end, K: int, out=None,
                   workspace=None, stream=None, scores_out=None, tau_out=None,
                   force_tau: Optional[float] = None, lds_cap: int = 0, spill_cap: int = 0,
-                  main_events=None):
+                  main_events=None, main_reps: int = 1):
     """idx_topk_prefill_debug: also emits FP32 scores [Q,N] and thresholds [Q].
 
     main_events: optional (start, stop) pair of torch.cuda.Event(enable_timing=True)
-    recorded around the fused main kernel."""
+    recorded around the fused main kernel; main_reps > 1 launches that kernel
+    so many times back to back inside the pair (timing only)."""
     ev0 = ev1 = None
     if main_events is not None:
         ev0, ev1 = (ctypes.c_void_p(e.cuda_event) for e in main_events)
     opts = Opts(1 if force_tau is not None else 0, float(force_tau or 0.0), int(lds_cap),
-                int(spill_cap), ev0, ev1)
+                int(spill_cap), ev0, ev1, int(main_reps))
     return _prefill(q8, q_scale, k8, k_scale, w, row_start, row_end, K, out, workspace, stream,
                     debug=True, scores_out=scores_out, tau_out=tau_out, opts=opts)
 
@@ -180,7 +182,7 @@ def _prefill(q8, q_scale, k8, k_scale, w, row_start, row_end, K, out, workspace,
 
 
 def prefill_unfused(q8, q_scale, k8, k_scale, w, row_start, row_end, K: int, out=None,
-                    workspace=None, stream=None, main_events=None):
+                    workspace=None, stream=None, main_events=None, main_reps: int = 1):
     """idx_topk_prefill_unfused: the same scores written to an explicit [Q,N]
     matrix in the workspace, then a separate top-K over it (the comparator of
     the fused path).  main_events: optional (start, stop) event pair around
@@ -197,7 +199,7 @@ def prefill_unfused(q8, q_scale, k8, k_scale, w, row_start, row_end, K: int, out
     ev0 = ev1 = None
     if main_events is not None:
         ev0, ev1 = (ctypes.c_void_p(e.cuda_event) for e in main_events)
-    opts = Opts(0, 0.0, 0, 0, ev0, ev1)
+    opts = Opts(0, 0.0, 0, 0, ev0, ev1, int(main_reps))
     _check(_lib.idx_topk_prefill_unfused(
         _ptr(q8, torch.uint8), _ptr(q_scale, torch.float32), _ptr(k8, torch.uint8),
         _ptr(k_scale, torch.float32), _ptr(w, torch.float32), _ptr(row_start, torch.int32),
@@ -222,7 +224,8 @@ def topk_rows(scores, row_start, row_end, K: int, out=None, stream=None):
 
 
 def decode_paged(q8, q_scale, k_cache, k_scale, w, page_table, seq_lens, K: int, out=None,
-                 workspace=None, stream=None, force_tau: Optional[float] = None, main_events=None):
+                 workspace=None, stream=None, force_tau: Optional[float] = None, main_events=None,
+                 main_reps: int = 1):
     """Top-K physical cache slots per sequence; see idx_topk_decode_paged.
 
     q8 [B,64,128], q_scale [B,64] or None, k_cache [P,64,128], k_scale [P,64],
@@ -245,13 +248,14 @@ def decode_paged(q8, q_scale, k_cache, k_scale, w, page_table, seq_lens, K: int,
             _ptr(k_scale, torch.float32), _ptr(w, torch.float32), _ptr(page_table, torch.int32),
             _ptr(seq_lens, torch.int32), B, max_pages, page, P, int(K), _ptr(out, torch.int32),
             _ptr(workspace), int(workspace.numel()), _stream(stream)]
-    if force_tau is None and main_events is None:
+    if force_tau is None and main_events is None and main_reps == 1:
         _check(_lib.idx_topk_decode_paged(*args))
     else:
         ev0 = ev1 = None
         if main_events is not None:
             ev0, ev1 = (ctypes.c_void_p(e.cuda_event) for e in main_events)
-        opts = Opts(1 if force_tau is not None else 0, float(force_tau or 0.0), 0, 0, ev0, ev1)
+        opts = Opts(1 if force_tau is not None else 0, float(force_tau or 0.0), 0, 0, ev0, ev1,
+                    int(main_reps))
         _check(_lib.idx_topk_decode_paged_debug(*args, ctypes.byref(opts)))
     return out
 

@@ -87,6 +87,8 @@ static int prefill_common(const uint8_t* q, const float* q_scale, const uint8_t*
     A.tau_value = opts->tau_value;
     A.ev_main_start = static_cast<hipEvent_t>(opts->ev_main_start);
     A.ev_main_stop = static_cast<hipEvent_t>(opts->ev_main_stop);
+    if (opts->main_reps < 0 || opts->main_reps > 1000) return IDX_EINVAL;
+    A.main_reps = opts->main_reps;
   }
   A.cap_total = A.lds_cap + A.spill_cap;
   // usable entries per segment: the full segment unless a test knob shrank

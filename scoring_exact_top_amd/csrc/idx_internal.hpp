@@ -134,6 +134,7 @@ struct PrefillArgs {
   int32_t force_tau;
   float tau_value;
   hipEvent_t ev_main_start, ev_main_stop;  // host-side only: timing hooks
+  int32_t main_reps;                       // host-side only: launches of the main kernel
 };
 
 struct SampleGeom {

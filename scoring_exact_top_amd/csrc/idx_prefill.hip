@@ -8,6 +8,8 @@
 // are at least K of them, the top-K of the candidates is the top-K of the row.
 // Otherwise the row goes to the repair kernel, which rescores it into the
 // workspace and selects exactly there.
+#include <hip/hip_ext.h>
+
 #include "idx_common.hpp"
 #include "idx_internal.hpp"
 #include "idx_rows.hpp"
@@ -660,13 +662,18 @@ int launch_prefill(const PrefillArgs& A, hipStream_t stream) {
   const int64_t nchunks = (int64_t)((A.N + 63) >> 6) * 512;
   if (nchunks > 0) hipLaunchKernelGGL(k_relayout_keys, dim3((unsigned)(nchunks / kWG)), dim3(kWG), 0, stream, A);
   hipLaunchKernelGGL(k_prefill_tau, dim3((A.Q + kWaves - 1) / kWaves), dim3(kWG), 0, stream, A);
-  if (A.ev_main_start && hipEventRecord(A.ev_main_start, stream) != hipSuccess) return IDX_EHIP;
+  // the timing events, when given, are recorded by the launches themselves
+  // (the first launch's start, the last launch's end; main_reps > 1 repeats
+  // the idempotent kernel for timing)
   const unsigned grid = (unsigned)((A.Q + 1) / 2 * A.S);
-  if (A.dbg_scores)
-    hipLaunchKernelGGL(k_prefill_pair<kPairDebug>, dim3(grid), dim3(kWG), 0, stream, A);
-  else
-    hipLaunchKernelGGL(k_prefill_pair<kPairFused>, dim3(grid), dim3(kWG), 0, stream, A);
-  if (A.ev_main_stop && hipEventRecord(A.ev_main_stop, stream) != hipSuccess) return IDX_EHIP;
+  const int reps = A.main_reps > 1 ? A.main_reps : 1;
+  for (int r = 0; r < reps; ++r) {
+    hipEvent_t e0 = r == 0 ? A.ev_main_start : nullptr, e1 = r == reps - 1 ? A.ev_main_stop : nullptr;
+    if (A.dbg_scores)
+      hipExtLaunchKernelGGL(k_prefill_pair<kPairDebug>, dim3(grid), dim3(kWG), 0, stream, e0, e1, 0, A);
+    else
+      hipExtLaunchKernelGGL(k_prefill_pair<kPairFused>, dim3(grid), dim3(kWG), 0, stream, e0, e1, 0, A);
+  }
   hipLaunchKernelGGL(k_prefill_select, dim3(A.Q), dim3(kWG), 0, stream, A);
   hipLaunchKernelGGL(k_prefill_repair_score, dim3(kRepairGrid), dim3(kWG), 0, stream, A);
   hipLaunchKernelGGL(k_prefill_repair_pass<1>, dim3(kRepairGrid), dim3(kWG), 0, stream, A);
@@ -686,10 +693,11 @@ int launch_prefill_unfused(const PrefillArgs& A, hipStream_t stream) {
   const int64_t nchunks = (int64_t)((A.N + 63) >> 6) * 512;
   if (nchunks > 0) hipLaunchKernelGGL(k_relayout_keys, dim3((unsigned)(nchunks / kWG)), dim3(kWG), 0, stream, A);
   hipLaunchKernelGGL(k_prefill_tau, dim3((A.Q + kWaves - 1) / kWaves), dim3(kWG), 0, stream, A);
-  if (A.ev_main_start && hipEventRecord(A.ev_main_start, stream) != hipSuccess) return IDX_EHIP;
   const unsigned grid = (unsigned)((A.Q + 1) / 2 * A.S);
-  hipLaunchKernelGGL(k_prefill_pair<kPairDense>, dim3(grid), dim3(kWG), 0, stream, A);
-  if (A.ev_main_stop && hipEventRecord(A.ev_main_stop, stream) != hipSuccess) return IDX_EHIP;
+  const int reps = A.main_reps > 1 ? A.main_reps : 1;
+  for (int r = 0; r < reps; ++r)
+    hipExtLaunchKernelGGL(k_prefill_pair<kPairDense>, dim3(grid), dim3(kWG), 0, stream,
+                          r == 0 ? A.ev_main_start : nullptr, r == reps - 1 ? A.ev_main_stop : nullptr, 0, A);
   if (hipGetLastError() != hipSuccess) return IDX_EHIP;
   RowsArgs R{A.dbg_scores, (int64_t)A.N, A.row_start, A.row_end, A.Q, A.N, A.K, A.out, A.ctrl};
   return launch_topk_rows(R, stream);
