@@ -147,7 +147,7 @@ size_t idx_topk_prefill_unfused_workspace(int32_t Q, int32_t N, int32_t K);
 
 /*
  * Unfused comparator of idx_topk_prefill (Fusing Indexer Scoring and Exact Top-k page,
- * "2.1 Where the cost goes": a scoring kernel writes the full score matrix, a
+ * "2.2 Indexer scoring is compute-bound": a scoring kernel writes the full score matrix, a
  * separate top-k reads it back).  Same arguments and output as
  * idx_topk_prefill: the same MFMA scoring (bit-identical scores) writes all
  * valid scores of every row into the workspace, then idx_topk_rows' kernel
@@ -164,7 +164,7 @@ int idx_topk_prefill_unfused(const uint8_t *q, const float *q_scale, const uint8
 
 /*
  * Exact top-K of every row of a dense FP32 matrix (the standalone selection
- * stage of Fusing Indexer Scoring and Exact Top-k page, "2.1 Where the cost goes" and Table 2).
+ * stage of Fusing Indexer Scoring and Exact Top-k page, "3.5 Stage result", Table 2).
  *   scores    device, 16-byte aligned; row t's value at position s is
  *             scores[t * ld + s]; only [row_start[t], row_end[t]) is read;
  *             NaN-free

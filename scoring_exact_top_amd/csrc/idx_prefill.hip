@@ -684,7 +684,8 @@ int launch_prefill(const PrefillArgs& A, hipStream_t stream) {
   return hipGetLastError() == hipSuccess ? IDX_OK : IDX_EHIP;
 }
 
-// Unfused comparator ("2.1 Where the cost goes"): the same MFMA scoring
+// Unfused comparator ("2.2 Indexer scoring is compute-bound", "6.2 Operator
+// performance"): the same MFMA scoring
 // writes the whole [Q,N] FP32 score matrix to A.dbg_scores, then the
 // dense-matrix top-K selects each row from it.  The sampler kernel runs
 // only to clear the control words (its forced threshold is unused).

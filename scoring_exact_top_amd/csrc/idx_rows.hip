@@ -1,8 +1,9 @@
 // Exact top-K over a dense FP32 score matrix, one workgroup per row: the
 // standalone selection stage of an unfused pipeline (Fusing Indexer Scoring
-// and Exact Top-k page, "2.1 Where the cost goes" and Table 2: score into an
-// explicit [Q,N] matrix, then select), kept as the comparator for the fused
-// path and as a library routine of its own.
+// and Exact Top-k page, "2.2 Indexer scoring is compute-bound": score into an
+// explicit [Q,N] matrix, then select; "3.5 Stage result", Table 2: the
+// standalone top-k), kept as the comparator for the fused path, as the
+// selection stage of the paged decode, and as a library routine of its own.
 //
 // Per row of length L > K:
 //   0. a cut c from a sample of the row: kSampleBlocks contiguous blocks of
