@@ -9,7 +9,9 @@ Definitions followed (Fusing Indexer Scoring and Exact Top-k page): the score eq
 The problem", the inputs/outputs of "2.3 Problem definition" (FP8 Q and KV
 "each with scales", head weights, half-open valid range, K int32 indices,
 unsorted), and the exactness criterion of the same section.  The paged decode
-variant follows the contest report page (arXiv 2608.14560), "DSA TopK Indexer".
+variant follows the contest report page (arXiv 2608.14560), "DSA TopK Indexer".  The BF16
+stream scan follows the page "Deleting the key transpose puts the DSA indexer scan on its
+streaming floor" (unquantised BF16 keys per stream, exact top-2048).
 """
 from __future__ import annotations
 
@@ -29,6 +31,7 @@ _lib = None
 _f64p = ctypes.POINTER(ctypes.c_double)
 _i32p = ctypes.POINTER(ctypes.c_int32)
 _u8p = ctypes.POINTER(ctypes.c_uint8)
+_u16p = ctypes.POINTER(ctypes.c_uint16)
 _f32p = ctypes.POINTER(ctypes.c_float)
 
 
@@ -63,6 +66,12 @@ def _load():
             _u8p, _f32p, _u8p, _f32p, _f32p, _i32p, _i32p, ctypes.c_int32, ctypes.c_int32,
             ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _f64p, ctypes.c_int32, _i32p, _f64p,
             ctypes.c_int]
+        lib.oracle_bf16_value.restype = ctypes.c_double
+        lib.oracle_bf16_value.argtypes = [ctypes.c_int]
+        lib.oracle_scan_bf16.restype = ctypes.c_int
+        lib.oracle_scan_bf16.argtypes = [
+            _u16p, _f32p, _u16p, _i32p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _f64p, _i32p,
+            _f64p, ctypes.c_int]
         lib.oracle_topk_of_scores.restype = ctypes.c_int
         lib.oracle_topk_of_scores.argtypes = [_f64p, ctypes.c_int32, ctypes.c_int32, _i32p, _f64p]
         _lib = lib
@@ -165,3 +174,28 @@ def topk_of_scores(scores, K):
     if rc != 0:
         raise ValueError("oracle_topk_of_scores failed")
     return out, float(th[0])
+
+
+def bf16_value(bits: int) -> float:
+    return float(_load().oracle_bf16_value(int(bits)))
+
+
+def scan_bf16(q16, w, k16, lens, K, want_scores=True, nthreads=0):
+    """BF16 stream scan: q16 [B,64,128] uint16, w [B,64] f32, k16 [B,N,128]
+    uint16, lens [B] int32.  Returns (topk [B,K] positions, theta [B],
+    scores [B,N] or None)."""
+    lib = _load()
+    q16 = _c(q16, np.uint16)
+    k16 = _c(k16, np.uint16)
+    w = _c(w, np.float32)
+    lens = _c(lens, np.int32)
+    B, N = int(k16.shape[0]), int(k16.shape[1])
+    topk = np.empty((B, K), dtype=np.int32)
+    theta = np.empty(B, dtype=np.float64)
+    scores = np.empty((B, N), dtype=np.float64) if want_scores else None
+    rc = lib.oracle_scan_bf16(_p(q16, _u16p), _p(w, _f32p), _p(k16, _u16p), _p(lens, _i32p), B, N,
+                              int(K), _p(scores, _f64p) if want_scores else None, _p(topk, _i32p),
+                              _p(theta, _f64p), int(nthreads))
+    if rc != 0:
+        raise ValueError("oracle_scan_bf16 failed: %d" % rc)
+    return topk, theta, scores

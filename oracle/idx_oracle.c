@@ -279,3 +279,83 @@ int oracle_topk_of_scores(const double *scores, int32_t L, int32_t K, int32_t *o
     free(sv);
     return 0;
 }
+
+/*
+ * BF16 stream scan oracle (the page "Deleting the key transpose puts the DSA indexer scan on its
+ * streaming floor": every stream scores all of its own candidate keys, stored unquantised as
+ * BF16, and keeps an exact top-2048).  Stream b has a BF16 query q[b][64][128],
+ * head weights w[b][64] and keys k[b][i][128] for positions i in [0, lens[b]):
+ *
+ *   I[b,i] = sum_{j<64} w[b,j] * ReLU( q[b,j] . k[b,i] )
+ *
+ * BF16 is the upper half of an IEEE binary32: the value of the 16-bit pattern
+ * x is the binary32 whose bits are x << 16.  A product of two BF16 values has
+ * at most 16 significant bits, so it is exact in double; the 128-term sum and
+ * the weighted head sum round at ~1e-16 relative.
+ *   q [B][64][128], w [B][64], k [B][N][128] (16-bit patterns), lens [B].
+ *   scores_out [B][N] double or NULL (NaN past lens[b]).
+ *   topk_out [B][K]: positions, (score desc, index asc), -1 padded; theta_out [B].
+ * Returns 0, -1 on a bad argument, -2 on a NaN or infinite input value.
+ */
+static double bf16_value(uint16_t x) {
+    uint32_t u = (uint32_t)x << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+double oracle_bf16_value(int bits) { return bf16_value((uint16_t)(bits & 0xFFFF)); }
+
+int oracle_scan_bf16(const uint16_t *q, const float *w, const uint16_t *k, const int32_t *lens,
+                     int32_t B, int32_t N, int32_t K, double *scores_out, int32_t *topk_out,
+                     double *theta_out, int nthreads) {
+    if (!q || !w || !k || !lens || !topk_out || K < 1 || B < 0 || N < 0) return -1;
+    for (int b = 0; b < B; ++b)
+        if (lens[b] < 0 || lens[b] > N) return -1;
+    int err = 0;
+#ifdef _OPENMP
+    if (nthreads <= 0) nthreads = omp_get_max_threads();
+#pragma omp parallel num_threads(nthreads) reduction(| : err)
+#endif
+    {
+        double *qd = (double *)malloc(sizeof(double) * OR_H * OR_D);
+        double *kd = (double *)malloc(sizeof(double) * OR_D);
+        sv_t *sv = (sv_t *)malloc(sizeof(sv_t) * (size_t)(N > 0 ? N : 1));
+#ifdef _OPENMP
+#pragma omp for schedule(dynamic, 1)
+#endif
+        for (int b = 0; b < B; ++b) {
+            const uint16_t *qrow = q + (size_t)b * OR_H * OR_D;
+            for (int i = 0; i < OR_H * OR_D; ++i) qd[i] = bf16_value(qrow[i]);
+            for (int i = 0; i < OR_H * OR_D; ++i)
+                if (!isfinite(qd[i])) err |= 2;
+            const float *wb = w + (size_t)b * OR_H;
+            int L = lens[b];
+            for (int s = 0; s < L; ++s) {
+                const uint16_t *krow = k + ((size_t)b * N + s) * OR_D;
+                for (int d = 0; d < OR_D; ++d) {
+                    kd[d] = bf16_value(krow[d]);
+                    if (!isfinite(kd[d])) err |= 2;
+                }
+                double I = 0.0;
+                for (int j = 0; j < OR_H; ++j) {
+                    double dot = 0.0;
+                    for (int d = 0; d < OR_D; ++d) dot += qd[(size_t)j * OR_D + d] * kd[d];
+                    I += (double)wb[j] * (dot > 0.0 ? dot : 0.0);
+                }
+                sv[s].v = I + 0.0;
+                sv[s].i = s;
+            }
+            if (scores_out) {
+                double *so = scores_out + (size_t)b * N;
+                for (int s = 0; s < N; ++s) so[s] = NAN;
+                for (int s = 0; s < L; ++s) so[s] = sv[s].v;
+            }
+            select_row(sv, L, K, NULL, topk_out + (size_t)b * K, theta_out ? theta_out + b : NULL);
+        }
+        free(qd);
+        free(kd);
+        free(sv);
+    }
+    return err ? -2 : 0;
+}

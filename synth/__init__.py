@@ -12,6 +12,10 @@ Recipe (fixed draw order per case, CPU ``torch.Generator`` seeded per case):
   w ~ N(0, 1/64) [Q,64]
   ranges: causal, row at position t sees keys [0, t+1)
 
+BF16 stream scan (page "Deleting the key transpose puts the DSA indexer scan on its streaming
+floor"): per stream b (CPU generator seeded with (seed, b)): q ~ N(0,1) [64,128]
+-> BF16 (torch's RNE cast), k ~ N(0,1) [N,128] -> BF16, w ~ N(0, 1/64) [64].
+
 Shapes follow the five workloads of the pages' operating points (Fused Indexer
 Top-k page, "2.3 Problem definition" and "6.1 Setup": B=1, 64 heads, d=128,
 K=2048, N from 8K to 160K; contest report page (arXiv 2608.14560), "DSA TopK Indexer": paged
@@ -85,6 +89,28 @@ class DecodeCase:
     @property
     def pairs(self) -> int:
         return int(self.seq_lens.astype(np.int64).sum())
+
+
+@dataclasses.dataclass
+class ScanCase:
+    name: str
+    q16: np.ndarray   # uint16 [B,64,128] BF16 bit patterns
+    w: np.ndarray     # float32 [B,64]
+    k16: np.ndarray   # uint16 [B,N,128] BF16 bit patterns
+    lens: np.ndarray  # int32 [B]
+    K: int = 2048
+
+    @property
+    def B(self) -> int:
+        return int(self.k16.shape[0])
+
+    @property
+    def N(self) -> int:
+        return int(self.k16.shape[1])
+
+    @property
+    def pairs(self) -> int:
+        return int(self.lens.astype(np.int64).sum())
 
 
 def _gen(seed: int) -> torch.Generator:
@@ -280,3 +306,37 @@ WORKLOADS = {
     "long_prefill": long_prefill,
     "adversarial": adversarial,
 }
+
+
+def _bf16_bits(x: torch.Tensor) -> np.ndarray:
+    return x.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16).copy()
+
+
+def scan_stream(seed: int, b: int, N: int):
+    """Stream b of a BF16 scan case: (q16 [64,128], w [64], k16 [N,128])."""
+    g = _gen(seed * 1000003 + b)
+    q16 = _bf16_bits(torch.randn(H, D, generator=g))
+    w = (torch.randn(H, generator=g) / 8.0).numpy().astype(np.float32)
+    k16 = np.empty((N, D), dtype=np.uint16)
+    for i0 in range(0, N, 65536):  # bounded temporaries for long streams
+        n = min(65536, N - i0)
+        k16[i0:i0 + n] = _bf16_bits(torch.randn(n, D, generator=g))
+    return q16, w, k16
+
+
+def scan_case(name: str, B: int, N: int, seed: int, lens=None, K: int = 2048) -> ScanCase:
+    q16 = np.empty((B, H, D), dtype=np.uint16)
+    w = np.empty((B, H), dtype=np.float32)
+    k16 = np.empty((B, N, D), dtype=np.uint16)
+    for b in range(B):
+        q16[b], w[b], k16[b] = scan_stream(seed, b, N)
+    lens = np.full(B, N, dtype=np.int32) if lens is None else np.asarray(lens, dtype=np.int32)
+    return ScanCase(name, q16, w, k16, lens, K)
+
+
+def bf16_scan(seed: int = 0) -> ScanCase:
+    """32 streams x 262144 BF16 keys each (the page's M = 32 operating point), K = 2048."""
+    return scan_case("bf16_scan_b32_n262144", 32, 262144, seed)
+
+
+WORKLOADS["bf16_scan"] = bf16_scan

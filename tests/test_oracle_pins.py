@@ -359,3 +359,97 @@ def test_decode_matches_prefill_on_gathered_keys():
         kk = min(L, case.K)
         assert np.array_equal(phys[t2[0][:kk]], topk[b][:kk])
         assert th2[0] == theta[b]
+
+
+# ------------------------------------------------------------- BF16 stream scan
+
+def _to_bf16_bits(x) -> np.ndarray:
+    return torch.as_tensor(np.asarray(x, dtype=np.float32)).to(torch.bfloat16).view(torch.int16) \
+        .numpy().view(np.uint16).copy()
+
+
+def test_bf16_decode_exhaustive_vs_torch():
+    """Every 16-bit pattern decodes to torch's bfloat16 -> float32 value (NaNs
+    to NaN): BF16 is the upper half of an IEEE binary32."""
+    bits = np.arange(65536, dtype=np.uint16)
+    want = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).float().numpy().astype(np.float64)
+    got = np.array([oracle.bf16_value(int(b)) for b in bits])
+    nan = np.isnan(want)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], want[~nan])
+    assert oracle.bf16_value(0x3F80) == 1.0 and oracle.bf16_value(0xC040) == -3.0
+    assert oracle.bf16_value(0x0001) == 2.0 ** -133          # smallest subnormal
+
+
+def test_scan_one_hot_gives_relu_of_key_column():
+    """Query head j0 = e_d0, all other heads zero, w = e_j0: every score is
+    ReLU(k[i, d0]); the top-K follows that column (ties to lower positions)."""
+    rng = np.random.default_rng(3)
+    N, K, j0, d0 = 700, 50, 17, 93
+    q = np.zeros((1, 64, 128), dtype=np.float32)
+    q[0, j0, d0] = 1.0
+    w = np.zeros((1, 64), dtype=np.float32)
+    w[0, j0] = 1.0
+    kf = rng.standard_normal((1, N, 128)).astype(np.float32)
+    k16 = _to_bf16_bits(kf)
+    col = torch.from_numpy(k16[0, :, d0].view(np.int16)).view(torch.bfloat16).double().numpy()
+    topk, theta, sc = oracle.scan_bf16(_to_bf16_bits(q), w, k16, np.array([N], np.int32), K)
+    assert np.array_equal(sc[0], np.maximum(col, 0.0))
+    order = sorted(range(N), key=lambda i: (-max(col[i], 0.0), i))
+    assert topk[0].tolist() == order[:K]
+
+
+def test_scan_linear_regime_matches_matvec():
+    """Nonnegative queries, keys and weights: ReLU is the identity, so every
+    score is one float64 matrix-vector product (sum_j w_j q_j) . k."""
+    rng = np.random.default_rng(4)
+    B, N = 2, 300
+    q16 = _to_bf16_bits(np.abs(rng.standard_normal((B, 64, 128))))
+    k16 = _to_bf16_bits(np.abs(rng.standard_normal((B, N, 128))))
+    w = np.abs(rng.standard_normal((B, 64))).astype(np.float32)
+    dec = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).double().numpy()
+    _, _, sc = oracle.scan_bf16(q16, w, k16, np.array([N, N - 7], np.int32), 10)
+    for b in range(B):
+        u = (w[b].astype(np.float64)[:, None] * dec(q16[b])).sum(axis=0)
+        want = dec(k16[b]) @ u
+        L = N if b == 0 else N - 7
+        np.testing.assert_allclose(sc[b, :L], want[:L], rtol=1e-12, atol=0)
+        assert np.isnan(sc[b, L:]).all()
+
+
+def test_scan_equals_fp8_oracle_on_common_values():
+    """Values exactly representable in both e4m3 and BF16 (every e4m3 value
+    is): with unit scales the FP8 prefill oracle and the BF16 scan oracle are
+    two independent decodes of the same numbers, and must agree bit for bit
+    on every score and on the selection."""
+    rng = np.random.default_rng(5)
+    N, K = 900, 64
+    e4 = oracle.e4m3_table()
+    codes_q = rng.integers(0, 256, (1, 64, 128)).astype(np.uint8)
+    codes_k = rng.integers(0, 256, (N, 128)).astype(np.uint8)
+    for c in (codes_q, codes_k):
+        c[(c & 0x7F) == 0x7F] = 0x38                          # no NaN codes
+    w = rng.standard_normal((1, 64)).astype(np.float32)
+    pc = synth.PrefillCase("common", codes_q, np.ones((1, 64), np.float32), codes_k,
+                           np.ones(N, np.float32), w, np.array([0], np.int32), np.array([N], np.int32), K)
+    tk8, th8, sc8 = oracle.prefill_case(pc)
+    q16 = _to_bf16_bits(e4[codes_q])
+    k16 = _to_bf16_bits(e4[codes_k])[None]
+    assert np.array_equal(torch.from_numpy(k16.view(np.int16)).view(torch.bfloat16).double().numpy()[0],
+                          e4[codes_k])                        # the BF16 copies are exact
+    tk16, th16, sc16 = oracle.scan_bf16(q16, w, k16, np.array([N], np.int32), K)
+    assert np.array_equal(sc8[0], sc16[0]) and np.array_equal(tk8[0], tk16[0]) and th8[0] == th16[0]
+
+
+def test_scan_ties_and_short_streams():
+    """Identical keys tie: the K lowest positions; a stream with lens <= K
+    returns all its positions then -1."""
+    rng = np.random.default_rng(6)
+    N, K = 500, 100
+    q16 = _to_bf16_bits(rng.standard_normal((2, 64, 128)))
+    w = rng.standard_normal((2, 64)).astype(np.float32)
+    one = _to_bf16_bits(rng.standard_normal((1, 1, 128)))
+    k16 = np.repeat(np.repeat(one, N, axis=1), 2, axis=0)
+    topk, _, _ = oracle.scan_bf16(q16, w, k16, np.array([N, 60], np.int32), K)
+    assert topk[0].tolist() == list(range(K))
+    assert topk[1].tolist() == list(range(60)) + [-1] * (K - 60)
