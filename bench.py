@@ -43,6 +43,8 @@ HBM_PEAK_GBS = 8000.0           # MI355X HBM3E
 METRIC = "fused score+top-2048 Gqk-pairs/s and % FP8 MFMA peak at 128K ctx, 1 MI355X"
 PREFILL = ["long_prefill", "prefill_chunk", "prefill_smoke", "adversarial"]
 DECODE = ["paged_decode"]
+SCAN = ["bf16_scan"]
+SCAN_METRIC = "BF16 stream scan + exact top-2048, GB/s of keys, 32 streams x 262144 keys, 1 MI355X"
 
 
 def log(*a):
@@ -282,6 +284,87 @@ def bench_unfused(args, lib):
     return res
 
 
+def scan_score_bytes(case) -> int:
+    """Algorithmic bytes of k_scan_bf16: every scored stream (K < L <= N)
+    reads its keys (256 B each), its query (64x128 BF16) and weights (64 x
+    4 B), and writes one FP32 score per key; shorter streams take the remap
+    path of the selection kernel and are not read."""
+    n = 0
+    for L in case.lens.astype(np.int64):
+        if case.K < L <= case.N:
+            n += L * 256 + 64 * 128 * 2 + 64 * 4 + L * 4
+    return int(n)
+
+
+def cpu_baseline_scan(case, seconds: float):
+    """The oracle on whole streams of the workload, one after another until
+    `seconds`; the rate is in key bytes per second like the GPU's."""
+    import oracle
+    threads = oracle_threads()
+    done, dt, b = 0, 0.0, 0
+    while b == 0 or dt < seconds:
+        s = b % case.B
+        t0 = time.perf_counter()
+        oracle.scan_bf16(case.q16[s:s + 1], case.w[s:s + 1], case.k16[s:s + 1], case.lens[s:s + 1], case.K,
+                         want_scores=False, nthreads=threads)
+        dt += time.perf_counter() - t0
+        done += int(case.lens[s])
+        b += 1
+    return {"value": done * 256 / dt / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": "%d whole streams of %s (%d keys), fp64 exact scoring + full sort per stream, "
+                      "%.1f s" % (b, case.name, done, dt)}
+
+
+def bench_scan(args, lib):
+    case = synth.WORKLOADS[args.workload](0)
+    q16 = torch.from_numpy(case.q16.view(np.int16)).cuda()
+    k16 = torch.from_numpy(case.k16.view(np.int16)).cuda()
+    w = tensor(case.w)
+    lens = tensor(case.lens)
+    out = torch.empty((case.B, case.K), dtype=torch.int32, device="cuda")
+    ws = lib.alloc_workspace(lib.scan_bf16_workspace_bytes(case.B, case.N, case.K), "cuda")
+
+    def step(step_evs, reps):
+        lib.scan_bf16(q16, w, k16, lens, case.K, out=out, workspace=ws,
+                      main_events=None if step_evs is None else step_evs[0], main_reps=reps)
+
+    ms_per_step, main_avg, main_min = timed(step, 1, args.steps, args.warmup)
+    # the streaming floor over the same key records (one float out per key)
+    floor_out = torch.empty(case.B * case.N, dtype=torch.float32, device="cuda")
+    for _ in range(args.warmup):
+        lib.stream_floor(k16, out=floor_out)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(args.steps):
+        lib.stream_floor(k16, out=floor_out)
+    e1.record()
+    torch.cuda.synchronize()
+    floor_ms = e0.elapsed_time(e1) / args.steps
+    key_bytes = int(case.lens.clip(0, case.N).astype(np.int64).sum()) * 256
+    log("workload", args.workload, "ms/step %.4f" % ms_per_step,
+        "scan kernel ms/launch %.4f (min %.4f)" % (main_avg, main_min), "floor ms %.4f" % floor_ms)
+    log("  ", case.name, lib.read_stats(ws))
+    nbytes = scan_score_bytes(case)
+    achieved = nbytes / (main_avg * 1e-3) / 1e9
+    config = {"workload": case.name, "streams": case.B, "keys_per_stream": case.N, "heads": 64, "dim": 128,
+              "K": case.K, "key_bytes": key_bytes, "calls_per_step": 1}
+    roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS,
+                "traffic": stored_traffic("k_scan_bf16", args.workload),
+                "kernel": "k_scan_bf16", "ms_per_launch": main_avg, "algorithmic_bytes": nbytes}
+    res = result(args, key_bytes / (ms_per_step * 1e-3) / 1e9, ms_per_step, config, roofline,
+                 "bf16 x bf16 -> f32")
+    res.update(metric=SCAN_METRIC, unit="GB/s", data="synthetic (seeded Gaussian, BF16 keys and queries)")
+    res["compare"] = {"stream_floor_ms": floor_ms,
+                      "stream_floor_GBs": (case.B * case.N * (256 + 4)) / (floor_ms * 1e-3) / 1e9,
+                      "scan_kernel_ms": main_avg, "scan_over_floor": main_avg / floor_ms,
+                      "step_over_floor": ms_per_step / floor_ms}
+    if args.cpu_seconds > 0:
+        res["cpu_baseline"] = cpu_baseline_scan(case, args.cpu_seconds)
+    return res
+
+
 def decode_score_bytes(case) -> int:
     """Algorithmic bytes of k_decode_score: every scored sequence (L > K)
     reads its keys (128 B codes + 4 B scale each), its page-table entries,
@@ -336,7 +419,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="long_prefill", choices=PREFILL + DECODE)
+    ap.add_argument("--workload", default="long_prefill", choices=PREFILL + DECODE + SCAN)
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="oracle sample budget in seconds (0: skip the CPU baseline)")
     ap.add_argument("--unfused", action="store_true",
@@ -355,12 +438,13 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     import scoring_exact_top_amd as lib
     if args.unfused:
-        if args.workload in DECODE:
+        if args.workload not in PREFILL:
             print("--unfused applies to prefill workloads", file=sys.stderr)
             sys.exit(2)
         res = bench_unfused(args, lib)
     else:
-        res = (bench_decode if args.workload in DECODE else bench_prefill)(args, lib)
+        res = (bench_decode if args.workload in DECODE else
+               bench_scan if args.workload in SCAN else bench_prefill)(args, lib)
     print(json.dumps(res), flush=True)
 
 

@@ -182,6 +182,47 @@ int idx_topk_rows(const float *scores, int64_t ld, const int32_t *row_start,
                   const int32_t *row_end, int32_t K, int32_t *out_idx, int32_t Q, int32_t N,
                   void *stream);
 
+/* Bytes of workspace idx_topk_scan_bf16 needs: the [B][N] FP32 score rows plus
+ * the gather regions (about B*N*4 + B*48 KiB). */
+size_t idx_topk_scan_bf16_workspace(int32_t B, int32_t N, int32_t K);
+
+/*
+ * BF16 stream scan (the page "Deleting the key transpose puts the DSA indexer scan on its
+ * streaming floor"): B independent streams, each with its own unquantised keys; stream b scores
+ * every key i in [0, lens[b]) against its 64-head query,
+ *   I[b,i] = sum_{j<64} w[b,j] * ReLU( q[b,j] . k[b,i] )   (FP32 accumulation),
+ * and keeps the K largest.
+ *   q        [B][64][128] BF16 bit patterns (uint16), 16-byte aligned
+ *   w        [B][64] float
+ *   k        [B][N][128] BF16 bit patterns, 16-byte aligned; stream b's keys at
+ *            k + b*N*128; (N + 320)*256 must fit in 31 bits (IDX_EUNSUPPORTED)
+ *   lens     [B] int32 device, 0 <= lens[b] <= N (a stream outside gets all -1)
+ *   K        1..2048
+ *   out_idx  [B][K] int32: key positions, unsorted, ties at the K-th score to the
+ *            lowest positions, -1 padded (streams with lens[b] <= K get all
+ *            their positions)
+ *   opts     NULL or timing only (ev_main_* and main_reps for the scoring kernel)
+ * Inputs must be finite (BF16 infinities and NaNs are not scored meaningfully).
+ * Asynchronous on `stream`; returns IDX_OK or a negative IDX_E* code.
+ */
+int idx_topk_scan_bf16(const uint16_t *q, const float *w, const uint16_t *k, const int32_t *lens,
+                       int32_t B, int32_t N, int32_t K, int32_t *out_idx, void *workspace,
+                       size_t workspace_bytes, void *stream, const idx_topk_opts *opts);
+
+/* Tests and diagnosis: the device address, inside a workspace used by the last
+ * idx_topk_scan_bf16 call with these B and N, of its [B][N] FP32 score rows
+ * (stream b's scores of positions [0, lens[b]) at row b; other entries
+ * unspecified).  NULL for a NULL workspace or negative sizes. */
+const float *idx_topk_scan_bf16_scores(const void *workspace, int32_t B, int32_t N);
+
+/*
+ * The scan's streaming floor (same page, "stream only: read keys, write one score, no math"):
+ * reads n_records records of 256 bytes from src (16-byte aligned) and writes one
+ * float per record to dst[n_records].  A measurement reference, not part of the
+ * method.  Asynchronous on `stream`.
+ */
+int idx_topk_stream_floor(const void *src, int64_t n_records, float *dst, void *stream);
+
 /* Bytes of workspace idx_topk_decode_paged needs. */
 size_t idx_topk_decode_workspace(int32_t B, int32_t max_pages, int32_t page_size, int32_t K);
 

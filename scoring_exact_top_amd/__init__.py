@@ -62,6 +62,15 @@ _lib.idx_topk_prefill_unfused.restype = ctypes.c_int
 _lib.idx_topk_prefill_unfused.argtypes = _lib.idx_topk_prefill.argtypes + [ctypes.POINTER(Opts)]
 _lib.idx_topk_rows.restype = ctypes.c_int
 _lib.idx_topk_rows.argtypes = [_vp, ctypes.c_int64, _vp, _vp, _i32, _vp, _i32, _i32, _vp]
+_lib.idx_topk_scan_bf16_workspace.restype = _sz
+_lib.idx_topk_scan_bf16_workspace.argtypes = [_i32, _i32, _i32]
+_lib.idx_topk_scan_bf16.restype = ctypes.c_int
+_lib.idx_topk_scan_bf16.argtypes = [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _sz, _vp,
+                                    ctypes.POINTER(Opts)]
+_lib.idx_topk_scan_bf16_scores.restype = ctypes.c_void_p
+_lib.idx_topk_scan_bf16_scores.argtypes = [_vp, _i32, _i32]
+_lib.idx_topk_stream_floor.restype = ctypes.c_int
+_lib.idx_topk_stream_floor.argtypes = [_vp, ctypes.c_int64, _vp, _vp]
 _lib.idx_topk_decode_workspace.restype = _sz
 _lib.idx_topk_decode_workspace.argtypes = [_i32, _i32, _i32, _i32]
 _lib.idx_topk_decode_paged.restype = ctypes.c_int
@@ -110,6 +119,10 @@ def prefill_workspace_bytes(Q: int, N: int, K: int) -> int:
 
 def prefill_unfused_workspace_bytes(Q: int, N: int, K: int) -> int:
     return int(_lib.idx_topk_prefill_unfused_workspace(Q, N, K))
+
+
+def scan_bf16_workspace_bytes(B: int, N: int, K: int) -> int:
+    return int(_lib.idx_topk_scan_bf16_workspace(B, N, K))
 
 
 def decode_workspace_bytes(B: int, max_pages: int, page_size: int, K: int) -> int:
@@ -220,6 +233,51 @@ def topk_rows(scores, row_start, row_end, K: int, out=None, stream=None):
     _check(_lib.idx_topk_rows(_ptr(scores, torch.float32), N, _ptr(row_start, torch.int32),
                               _ptr(row_end, torch.int32), int(K), _ptr(out, torch.int32), Q, N,
                               _stream(stream)))
+    return out
+
+
+def scan_bf16(q16, w, k16, lens, K: int, out=None, workspace=None, stream=None, main_events=None,
+              main_reps: int = 1):
+    """idx_topk_scan_bf16: q16 [B,64,128] and k16 [B,N,128] as torch.bfloat16 or
+    uint16/int16 bit patterns, w [B,64] f32, lens [B] int32 (device).  Returns
+    out [B,K] int32 key positions.  main_events / main_reps: timing of the
+    scoring kernel."""
+    if q16.dtype == torch.bfloat16:
+        q16 = q16.view(torch.int16)
+    if k16.dtype == torch.bfloat16:
+        k16 = k16.view(torch.int16)
+    B, N = int(k16.shape[0]), int(k16.shape[1])
+    if q16.shape != (B, HEADS, DIM) or k16.shape[2:] != (DIM,):
+        raise ValueError("q16 must be [B,64,128] and k16 [B,N,128]")
+    dev = q16.device
+    if out is None:
+        out = torch.empty((B, K), dtype=torch.int32, device=dev)
+    if workspace is None:
+        workspace = alloc_workspace(scan_bf16_workspace_bytes(B, N, K), dev)
+    ev0 = ev1 = None
+    if main_events is not None:
+        ev0, ev1 = (ctypes.c_void_p(e.cuda_event) for e in main_events)
+    opts = Opts(0, 0.0, 0, 0, ev0, ev1, int(main_reps))
+    _check(_lib.idx_topk_scan_bf16(_ptr(q16), _ptr(w, torch.float32), _ptr(k16), _ptr(lens, torch.int32),
+                                   B, N, int(K), _ptr(out, torch.int32), _ptr(workspace),
+                                   int(workspace.numel()), _stream(stream), ctypes.byref(opts)))
+    return out
+
+
+def scan_bf16_scores(workspace: torch.Tensor, B: int, N: int) -> torch.Tensor:
+    """The [B,N] FP32 score rows inside a scan workspace (a copy; tests only)."""
+    addr = _lib.idx_topk_scan_bf16_scores(_ptr(workspace), int(B), int(N))
+    off = int(addr) - workspace.data_ptr()
+    return workspace[off: off + 4 * B * N].view(torch.float32).view(B, N).clone()
+
+
+def stream_floor(src: torch.Tensor, out=None, stream=None):
+    """idx_topk_stream_floor over src viewed as 256-byte records."""
+    nbytes = src.numel() * src.element_size()
+    n = nbytes // 256
+    if out is None:
+        out = torch.empty(n, dtype=torch.float32, device=src.device)
+    _check(_lib.idx_topk_stream_floor(_ptr(src), int(n), _ptr(out, torch.float32), _stream(stream)))
     return out
 
 

@@ -7,7 +7,7 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SOURCES = ["csrc/idx_api.hip", "csrc/idx_prefill.hip", "csrc/idx_decode.hip", "csrc/idx_rows.hip"]
+SOURCES = ["csrc/idx_api.hip", "csrc/idx_prefill.hip", "csrc/idx_decode.hip", "csrc/idx_rows.hip", "csrc/idx_scan.hip"]
 LIB = os.path.join(HERE, "libidxtopk.so")
 
 HIPCC_FLAGS = [

@@ -5,6 +5,7 @@
 #include "idx_internal.hpp"
 #include "idx_decode.hpp"
 #include "idx_rows.hpp"
+#include "idx_scan.hpp"
 
 namespace idxk {
 
@@ -162,6 +163,25 @@ extern "C" int idx_topk_rows(const float* scores, int64_t ld, const int32_t* row
   if ((int64_t)N * 4 > 0x7fffffffLL) return IDX_EUNSUPPORTED;
   RowsArgs R{scores, ld, row_start, row_end, Q, N, K, out_idx, nullptr};
   return launch_topk_rows(R, static_cast<hipStream_t>(stream));
+}
+
+extern "C" size_t idx_topk_scan_bf16_workspace(int32_t B, int32_t N, int32_t K) {
+  return scan_bf16_workspace_bytes(B, N, K);
+}
+
+extern "C" int idx_topk_scan_bf16(const uint16_t* q, const float* w, const uint16_t* k, const int32_t* lens,
+                                  int32_t B, int32_t N, int32_t K, int32_t* out_idx, void* workspace,
+                                  size_t workspace_bytes, void* stream, const idx_topk_opts* opts) {
+  return scan_bf16(q, w, k, lens, B, N, K, out_idx, workspace, workspace_bytes, static_cast<hipStream_t>(stream),
+                   opts);
+}
+
+extern "C" const float* idx_topk_scan_bf16_scores(const void* workspace, int32_t B, int32_t N) {
+  return scan_bf16_scores(workspace, B, N);
+}
+
+extern "C" int idx_topk_stream_floor(const void* src, int64_t n_records, float* dst, void* stream) {
+  return stream_floor(src, n_records, dst, static_cast<hipStream_t>(stream));
 }
 
 extern "C" size_t idx_topk_decode_workspace(int32_t B, int32_t max_pages, int32_t page_size, int32_t K) {

@@ -164,17 +164,30 @@ struct RowsShared {
 // Step 0: the sampled cut of a row of length L > K (key 0 keeps every key):
 // the r-th largest of kSampleKeys sampled keys, r chosen so that about 2K
 // of the row's keys are expected at or above it.  All threads call this.
-__device__ __forceinline__ uint32_t sample_cut(const float* row, int L, int K, SelShared& sh, int tid) {
-  if (L < kSampleMinLen) return 0u;
-  uint32_t sk[kSampleBlocks];
-  const int step = (L - kWG) / (kSampleBlocks - 1);  // block j starts at j*step
+// Split in two so that a caller can issue other loads between them: the
+// sample's loads (L >= 1; indexes clamped, so a short row reads valid
+// elements whose keys then go unused) and its select.
+__device__ __forceinline__ void sample_load(const float* row, int L, uint32_t (&sk)[kSampleBlocks], int tid) {
+  const int step = max(0, (L - kWG) / (kSampleBlocks - 1));  // block j starts at j*step
 #pragma unroll
-  for (int j = 0; j < kSampleBlocks; ++j) sk[j] = f2key(row[j * step + tid]);
+  for (int j = 0; j < kSampleBlocks; ++j) sk[j] = f2key(row[min(j * step + tid, L - 1)]);
+}
+
+__device__ __forceinline__ uint32_t sample_select(const uint32_t (&sk)[kSampleBlocks], int L, int K, SelShared& sh,
+                                                  int tid) {
+  if (L < kSampleMinLen) return 0u;
   // rank r in the sample <=> about r * L / kSampleKeys keys of the row
   const int r = (int)(((int64_t)2 * K * kSampleKeys + L - 1) / L);
   if (r >= kSampleKeys) return 0u;
   const RegLayout lay{(uint32_t)tid, (uint32_t)kWG, (uint32_t)kSampleKeys, (uint32_t)kSampleBlocks};
   return range_select_regs<kSampleBlocks>([&](int j) { return sk[j]; }, lay, r, sh, tid).lo;
+}
+
+__device__ __forceinline__ uint32_t sample_cut(const float* row, int L, int K, SelShared& sh, int tid) {
+  if (L < kSampleMinLen) return 0u;
+  uint32_t sk[kSampleBlocks];
+  sample_load(row, L, sk, tid);
+  return sample_select(sk, L, K, sh, tid);
 }
 
 // Exact selection of the rem largest of the gathered keys (ties to the
@@ -211,13 +224,13 @@ __device__ __forceinline__ void select_gathered(RowsShared& S, const uint32_t (&
 }
 
 // Rows of a dense matrix: row t is scores + t*ld, range [row_start[t],
-// row_end[t]), ids are positions.
+// row_end[t]) (row_start null: [0, row_end[t])), ids are positions.
 struct DenseRows {
   static constexpr int kUnroll = 4;  // many rows: workgroups enough to cover the latency
   static constexpr int kMinBlocks = 3;
   RowsArgs A;
   __device__ __forceinline__ bool range(int t, int& s0, int& s1, int) const {
-    s0 = A.row_start[t];
+    s0 = A.row_start ? A.row_start[t] : 0;
     s1 = A.row_end[t];
     return s0 >= 0 && s0 <= s1 && s1 <= A.N;
   }
@@ -399,13 +412,13 @@ __global__ __launch_bounds__(kWG, Rows::kMinBlocks) void k_topk_rows(RowsArgs A)
   }
 }
 
-// Pre-gather of paged rows: workgroup (g, t) computes row t's sampled cut
-// (as the per-row kernel would) and stores the keys >= cut of slice g of
-// the row into its own region of the workspace: per step each thread
-// counts its keys and a workgroup scan gives the slots, with no atomics
-// (same-address device atomics from every workgroup of a row would queue
-// at one L2 line).  Spreads over many CUs the pass that one workgroup per
-// row would make alone.
+// Pre-gather of long rows (paged decode sequences, scan streams): workgroup
+// (g, t) computes row t's sampled cut (as the per-row kernel would) and
+// stores the keys >= cut of slice g of the row into its own region of the
+// workspace; each thread counts its keys, one workgroup scan gives the
+// slots, with no atomics (same-address device atomics from every
+// workgroup of a row would queue at one L2 line).  Spreads over many CUs
+// the pass that one workgroup per row would make alone.
 template <class Rows>
 __global__ __launch_bounds__(kWG) void k_rows_gather(RowsArgs A) {
   __shared__ SelShared sh;
@@ -418,49 +431,99 @@ __global__ __launch_bounds__(kWG) void k_rows_gather(RowsArgs A) {
   const int L = s1 - s0, K = A.K;
   if (L <= K) return;
   const float* row = R.row(t) + s0;
-  const uint32_t cut = sample_cut(row, L, K, sh, tid);
   const int64_t lo = (int64_t)L * g / A.gsplit, hi = (int64_t)L * (g + 1) / A.gsplit;
   const int64_t region = ((int64_t)t * A.gsplit + g) * A.gcap;
   uint32_t* gk = A.gkey + region;
   int32_t* gi = A.gid + region;
-  constexpr int U = 4;
+  constexpr int U = 16;
   constexpr int kStep = kWG * U;
-  uint32_t count = 0u;  // keys found so far in the slice (uniform)
+  constexpr int kRounds = 4;  // slices up to kRounds * kStep keys stay in registers
+  if (hi - lo <= (int64_t)kRounds * kStep) {
+    // the sample's loads first, then the whole slice's (clamped, no branch),
+    // so that the slice arrives while the cut is being selected
+    uint32_t sk[kSampleBlocks];
+    sample_load(row, L, sk, tid);
+    uint32_t k[kRounds][U];
+#pragma unroll
+    for (int r = 0; r < kRounds; ++r)
+#pragma unroll
+      for (int u = 0; u < U; ++u) k[r][u] = f2key(row[min(lo + r * kStep + u * kWG + tid, hi - 1)]);
+    const uint32_t cut = sample_select(sk, L, K, sh, tid);
+    uint32_t cnt = 0u;
+#pragma unroll
+    for (int r = 0; r < kRounds; ++r)
+#pragma unroll
+      for (int u = 0; u < U; ++u) cnt += (lo + r * kStep + u * kWG + tid < hi) & (k[r][u] >= cut) ? 1u : 0u;
+    uint32_t total;
+    uint32_t slot = block_exclusive_scan(cnt, sh, tid, total);
+#pragma unroll
+    for (int r = 0; r < kRounds; ++r)
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int64_t i = lo + r * kStep + u * kWG + tid;
+        if ((i < hi) & (k[r][u] >= cut)) {
+          if (slot < (uint32_t)A.gcap) {
+            gk[slot] = k[r][u];
+            gi[slot] = (int32_t)i + s0;
+          }
+          ++slot;
+        }
+      }
+    if (tid == 0) A.gcnt[(int64_t)t * A.gsplit + g] = total;
+    return;
+  }
+  const uint32_t cut = sample_cut(row, L, K, sh, tid);
+  // longer slices, pass 1: per-thread counts, U loads in flight and no barrier; one
+  // workgroup scan gives each thread its first slot; pass 2 re-reads the
+  // slice (from L2) in threads that found keys and writes them.  A scan per
+  // round of loads would wait out a memory latency per round.  Loads past
+  // the slice read its last element (clamped index, not a branch: a load
+  // behind a branch is waited for at once) and are not counted.
+  uint32_t cnt = 0u;
 #pragma unroll 1
   for (int64_t base = lo; base < hi; base += kStep) {
     uint32_t k[U];
-    bool take[U];
-    uint32_t cnt = 0u;
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t i = base + u * kWG + tid;
-      const bool v = i < hi;
-      k[u] = v ? f2key(row[v ? i : 0]) : 0u;
-      take[u] = v && k[u] >= cut;
-      cnt += take[u] ? 1u : 0u;
-    }
-    uint32_t total;
-    uint32_t slot = count + block_exclusive_scan(cnt, sh, tid, total);
+    for (int u = 0; u < U; ++u) k[u] = f2key(row[min(base + u * kWG + tid, hi - 1)]);
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      if (take[u] && slot < (uint32_t)A.gcap) {
-        gk[slot] = k[u];
-        gi[slot] = (int32_t)(base + u * kWG + tid) + s0;
-      }
-      slot += take[u] ? 1u : 0u;
-    }
-    count += total;
+    for (int u = 0; u < U; ++u) cnt += (base + u * kWG + tid < hi) & (k[u] >= cut) ? 1u : 0u;
   }
-  if (tid == 0) A.gcnt[(int64_t)t * A.gsplit + g] = count;
+  uint32_t total;
+  uint32_t slot = block_exclusive_scan(cnt, sh, tid, total);
+  if (cnt != 0u && slot < (uint32_t)A.gcap) {
+#pragma unroll 1
+    for (int64_t base = lo; base < hi; base += kStep) {
+      uint32_t k[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) k[u] = f2key(row[min(base + u * kWG + tid, hi - 1)]);
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int64_t i = base + u * kWG + tid;
+        if ((i < hi) & (k[u] >= cut)) {
+          if (slot < (uint32_t)A.gcap) {
+            gk[slot] = k[u];
+            gi[slot] = (int32_t)i + s0;
+          }
+          ++slot;
+        }
+      }
+    }
+  }
+  if (tid == 0) A.gcnt[(int64_t)t * A.gsplit + g] = total;
 }
 
 int launch_topk_rows_gathered(const RowsArgs& A, hipStream_t stream) {
   if (A.Q == 0) return IDX_OK;
-  if (!A.table || !A.gkey || A.gsplit < 1 || A.gsplit > kMaxGatherSplit || (A.gsplit & (A.gsplit - 1)) ||
+  if (!A.gkey || A.gsplit < 1 || A.gsplit > kMaxGatherSplit || (A.gsplit & (A.gsplit - 1)) ||
       A.gcap * A.gsplit > kRowsCap)
     return IDX_EINVAL;
-  hipLaunchKernelGGL(k_rows_gather<PagedRows>, dim3(A.gsplit, A.Q), dim3(kWG), 0, stream, A);
-  hipLaunchKernelGGL(k_topk_rows<PagedRows>, dim3(A.Q), dim3(kWG), 0, stream, A);
+  if (A.table) {
+    hipLaunchKernelGGL(k_rows_gather<PagedRows>, dim3(A.gsplit, A.Q), dim3(kWG), 0, stream, A);
+    hipLaunchKernelGGL(k_topk_rows<PagedRows>, dim3(A.Q), dim3(kWG), 0, stream, A);
+  } else {
+    hipLaunchKernelGGL(k_rows_gather<DenseRows>, dim3(A.gsplit, A.Q), dim3(kWG), 0, stream, A);
+    hipLaunchKernelGGL(k_topk_rows<DenseRows>, dim3(A.Q), dim3(kWG), 0, stream, A);
+  }
   return hipGetLastError() == hipSuccess ? IDX_OK : IDX_EHIP;
 }
 

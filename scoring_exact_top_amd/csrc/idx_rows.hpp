@@ -34,7 +34,8 @@ struct RowsArgs {
 
 constexpr int kMaxGatherSplit = 32;
 
-// Launch the pre-gather (paged rows with gkey set) and the per-row select.
+// Launch the pre-gather and the per-row select (paged rows when table is
+// set, dense rows otherwise; gkey must be set).
 int launch_topk_rows_gathered(const RowsArgs& A, hipStream_t stream);
 
 int launch_topk_rows(const RowsArgs& A, hipStream_t stream);

@@ -1,0 +1,109 @@
+"""BF16 stream scan on MI355X against the CPU oracle: element-wise scores, the
+selection tolerance, bit-exact selection on the GPU's own scores (lowest-id
+tie rule), ragged stream lengths, ties, invalid lengths, and sampled streams
+of the full 32 x 262144 workload."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from oracle import check
+
+pytestmark = pytest.mark.gpu
+
+from gpu_util import log  # noqa: E402
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a GPU")
+    import scoring_exact_top_amd  # noqa: F401  (fails loudly if the library is missing)
+
+
+def _dec(a16):
+    return torch.from_numpy(np.ascontiguousarray(a16).view(np.int16)).view(torch.bfloat16).double().numpy()
+
+
+def _bound(case, b):
+    """B[i] = sum_j |w_j| sum_d |q_jd k_id|: the magnitude that bounds FP32
+    rounding of one score (as for the FP8 path)."""
+    q = np.abs(_dec(case.q16[b]))
+    k = np.abs(_dec(case.k16[b, :case.lens[b]]))
+    return np.abs(case.w[b].astype(np.float64)) @ (q @ k.T)
+
+
+def _run(case, scores=False):
+    import scoring_exact_top_amd as lib
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    ws = lib.alloc_workspace(lib.scan_bf16_workspace_bytes(case.B, case.N, case.K), "cuda")
+    out = lib.scan_bf16(t(case.q16.view(np.int16)), t(case.w), t(case.k16.view(np.int16)), t(case.lens),
+                        case.K, workspace=ws)
+    torch.cuda.synchronize()
+    S = lib.scan_bf16_scores(ws, case.B, case.N).cpu().numpy() if scores else None
+    return out.cpu().numpy(), S, lib.read_stats(ws)
+
+
+def _check(case, out, S, streams):
+    valid = [b for b in streams if 0 <= case.lens[b] <= case.N]
+    for b in streams:
+        if b not in valid:
+            assert (out[b] == -1).all(), "%s stream %d: invalid length must give -1" % (case.name, b)
+    if not valid:
+        return
+    topk, theta, sc = oracle.scan_bf16(case.q16[valid], case.w[valid], case.k16[valid], case.lens[valid], case.K)
+    for j, b in enumerate(valid):
+        L = int(case.lens[b])
+        where = "%s stream %d" % (case.name, b)
+        check.check_selection(out[b], sc[j], 0, L, case.K, theta[j], where=where)
+        if S is not None and L > case.K:
+            check.check_scores(S[b, :L], sc[j, :L], bound=_bound(case, b), where=where)
+            check.check_debug_bitexact(out[b], S[b], 0, L, case.K, where=where)
+            check.check_debug_canonical(out[b], S[b], 0, L, case.K, where=where)
+
+
+@pytest.mark.parametrize("K", [1, 100, 2048])
+def test_scan_ragged_streams(K):
+    lens = [0, 1, K, K + 1, 5000, 9001, 9001, 2049]
+    case = synth.scan_case("scan_ragged", len(lens), 9001, seed=10 + K, lens=lens, K=K)
+    log("case", case.name, lens, "K", K)
+    out, S, st = _run(case, scores=True)
+    log("stats", st)
+    _check(case, out, S, list(range(case.B)))
+    assert st["rows"] == case.B
+
+
+def test_scan_ties_and_invalid_lengths():
+    """Identical keys (the lowest positions win), and lengths outside [0, N]."""
+    case = synth.scan_case("scan_ties", 4, 6000, seed=7, lens=[6000, 6000, -1, 6001], K=2048)
+    case.k16[1] = case.k16[1, 123]                       # every key of stream 1 equal
+    out, S, st = _run(case, scores=True)
+    _check(case, out, S, [0, 1, 2, 3])
+    assert sorted(out[1].tolist()) == list(range(2048))
+    assert st["bad_rows"] == 2
+
+
+def test_scan_full_workload_sampled_streams():
+    """The 32 x 262144 workload: every stream's structure, two streams against
+    the oracle element by element."""
+    case = synth.bf16_scan(0)
+    log("case", case.name)
+    out, S, st = _run(case, scores=True)
+    log("stats", st)
+    for b in range(case.B):
+        check.check_structure(out[b], 0, int(case.lens[b]), case.K, where="stream %d" % b)
+    _check(case, out, S, [0, case.B - 1])
+    assert st["fast_ok"] == case.B
+
+
+def test_stream_floor_values():
+    """The floor kernel reads every record and writes the sum of words 0 and 3
+    of its 16 quads (small integers, so the sum is exact in any order)."""
+    import scoring_exact_top_amd as lib
+    n = 3 * 1024 + 5
+    rng = np.random.default_rng(3)
+    src = rng.integers(-50, 50, size=(n, 64)).astype(np.float32)
+    want = src.reshape(n, 16, 4)[:, :, [0, 3]].sum(axis=(1, 2))
+    got = lib.stream_floor(torch.from_numpy(src).cuda()).cpu().numpy()
+    assert np.array_equal(got, want)
