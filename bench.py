@@ -97,12 +97,19 @@ def cpu_baseline_decode(case, seconds: float):
                       "sort per sequence, %.1f s" % (case.name, case.B, case.pairs, reps, dt)}
 
 
-def source_digest() -> str:
-    """sha256 over the HIP sources, the public header and the build flags."""
+KERNEL_SOURCE = {"k_prefill_pair": "idx_prefill.hip", "k_decode_score": "idx_decode.hip",
+                 "k_scan_bf16": "idx_scan.hip"}
+
+
+def source_digest(kernel: str) -> str:
+    """sha256 over the source file that defines `kernel`, every header of the
+    library, the public header and the build flags: the stored counters stay
+    valid while none of these change."""
     h = hashlib.sha256()
     pkg = os.path.join(ROOT, "scoring_exact_top_amd")
-    files = sorted(glob.glob(os.path.join(pkg, "csrc", "*"))) + [
-        os.path.join(ROOT, "include", "idx_topk.h"), os.path.join(pkg, "build.py")]
+    files = ([os.path.join(pkg, "csrc", KERNEL_SOURCE[kernel])] +
+             sorted(glob.glob(os.path.join(pkg, "csrc", "*.hpp"))) +
+             [os.path.join(ROOT, "include", "idx_topk.h"), os.path.join(pkg, "build.py")])
     for f in files:
         h.update(os.path.relpath(f, ROOT).encode())
         with open(f, "rb") as fh:
@@ -119,7 +126,7 @@ def stored_traffic(kernel: str, workload: str):
     text = open(path).read()
     m_b = re.search(r"^traffic_bytes_per_launch\s*=\s*(\d+)", text, re.M)
     m_h = re.search(r"^source_sha256\s*=\s*([0-9a-f]{64})", text, re.M)
-    if not (m_b and m_h) or m_h.group(1) != source_digest():
+    if not (m_b and m_h) or m_h.group(1) != source_digest(kernel):
         return None
     return int(m_b.group(1))
 
