@@ -175,6 +175,25 @@ def timed(step, n_calls: int, steps: int, warmup: int):
     return ms_per_step, float(np.mean(per_step)) / n_calls, min(per_step) / n_calls
 
 
+def with_graph(args, lib, step):
+    """With --graph: the plain step, step(None, 1), recorded once into a HIP
+    graph (idx_topk_graph_*) and replayed; the event-timed steps stay eager
+    (their events are recorded by the launches themselves)."""
+    if not args.graph:
+        return step
+    step(None, 1)
+    torch.cuda.synchronize()
+    g = lib.capture(lambda: step(None, 1))
+
+    def gstep(step_evs, reps):
+        if step_evs is None and reps == 1:
+            g.launch()
+        else:
+            step(step_evs, reps)
+    gstep.graph = g
+    return gstep
+
+
 def result(args, value, ms_per_step, config, roofline, dtype):
     return {"metric": METRIC, "value": value, "unit": "Gqk-pairs/s", "n_gpus": 1,
             "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
@@ -199,7 +218,7 @@ def bench_prefill(args, lib):
                               d["row_end"], c.K, out=outs[j], workspace=wss[j],
                               main_events=None if step_evs is None else step_evs[j], main_reps=reps)
 
-    ms_per_step, main_avg, main_min = timed(step, n_calls, args.steps, args.warmup)
+    ms_per_step, main_avg, main_min = timed(with_graph(args, lib, step), n_calls, args.steps, args.warmup)
     log("workload", args.workload, "pairs", pairs, "ms/step %.4f" % ms_per_step,
         "main kernel ms/launch %.4f (min %.4f)" % (main_avg, main_min))
     for c, ws in zip(cases, wss):
@@ -207,7 +226,8 @@ def bench_prefill(args, lib):
     achieved = FLOP_PER_PAIR * (pairs / n_calls) / (main_avg * 1e-3) / 1e12
     config = {"workload": cases[0].name if n_calls == 1 else args.workload,
               "rows": sum(c.Q for c in cases), "keys": max(c.N for c in cases), "heads": 64,
-              "dim": 128, "K": cases[0].K, "pairs": pairs, "calls_per_step": n_calls}
+              "dim": 128, "K": cases[0].K, "pairs": pairs, "calls_per_step": n_calls,
+              "launch": "graph" if args.graph else "eager"}
     roofline = {"bound": "mfma", "achieved": achieved, "peak": FP8_DENSE_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": achieved / FP8_DENSE_PEAK_TFLOPS,
                 "traffic": stored_traffic("k_prefill_pair", args.workload) if n_calls == 1 else None,
@@ -335,7 +355,7 @@ def bench_scan(args, lib):
         lib.scan_bf16(q16, w, k16, lens, case.K, out=out, workspace=ws,
                       main_events=None if step_evs is None else step_evs[0], main_reps=reps)
 
-    ms_per_step, main_avg, main_min = timed(step, 1, args.steps, args.warmup)
+    ms_per_step, main_avg, main_min = timed(with_graph(args, lib, step), 1, args.steps, args.warmup)
     # the streaming floor over the same key records (one float out per key)
     floor_out = torch.empty(case.B * case.N, dtype=torch.float32, device="cuda")
     for _ in range(args.warmup):
@@ -355,7 +375,8 @@ def bench_scan(args, lib):
     nbytes = scan_score_bytes(case)
     achieved = nbytes / (main_avg * 1e-3) / 1e9
     config = {"workload": case.name, "streams": case.B, "keys_per_stream": case.N, "heads": 64, "dim": 128,
-              "K": case.K, "key_bytes": key_bytes, "calls_per_step": 1}
+              "K": case.K, "key_bytes": key_bytes, "calls_per_step": 1,
+              "launch": "graph" if args.graph else "eager"}
     roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": achieved / HBM_PEAK_GBS,
                 "traffic": stored_traffic("k_scan_bf16", args.workload),
@@ -400,7 +421,7 @@ def bench_decode(args, lib):
                          d["seq_lens"], case.K, out=out, workspace=ws,
                          main_events=None if step_evs is None else step_evs[0], main_reps=reps)
 
-    ms_per_step, main_avg, main_min = timed(step, 1, args.steps, args.warmup)
+    ms_per_step, main_avg, main_min = timed(with_graph(args, lib, step), 1, args.steps, args.warmup)
     log("workload", args.workload, "keys", case.pairs, "ms/step %.4f" % ms_per_step,
         "scoring kernel ms/launch %.4f (min %.4f)" % (main_avg, main_min))
     log("  ", case.name, lib.read_stats(ws))
@@ -408,7 +429,8 @@ def bench_decode(args, lib):
     achieved = nbytes / (main_avg * 1e-3) / 1e9
     config = {"workload": case.name, "batch": case.B, "keys": case.pairs,
               "max_seq_len": int(case.seq_lens.max()), "page_size": case.page_size, "heads": 64,
-              "dim": 128, "K": case.K, "pairs": case.pairs, "calls_per_step": 1}
+              "dim": 128, "K": case.K, "pairs": case.pairs, "calls_per_step": 1,
+              "launch": "graph" if args.graph else "eager"}
     roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": achieved / HBM_PEAK_GBS,
                 "traffic": stored_traffic("k_decode_score", args.workload),
@@ -432,6 +454,9 @@ def main():
     ap.add_argument("--unfused", action="store_true",
                     help="time the unfused comparator (score matrix, then top-K) on a prefill "
                          "workload, beside the fused path and the standalone top-K")
+    ap.add_argument("--graph", action="store_true",
+                    help="replay each step's library calls from a HIP graph recorded once "
+                         "(idx_topk_graph_*) instead of launching them one by one")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain copy of MIB MiB (counter calibration) and exit")
     args = ap.parse_args()

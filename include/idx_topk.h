@@ -273,6 +273,44 @@ int idx_topk_read_stats(const void *workspace, idx_topk_stats *out, void *stream
 /* Static description of an error code. */
 const char *idx_topk_strerror(int code);
 
+/*
+ * Graph capture of the multi-kernel calls.  A call of this library is a
+ * short chain of kernels (up to nine for prefill); at small shapes their
+ * launches, not their work, set the time of a call.  Recording the chain
+ * once into a HIP graph and replaying it costs one launch per replay.
+ *
+ *   idx_topk_graph_begin(stream)   starts recording on `stream` (thread-local
+ *                                  capture mode; the legacy NULL stream cannot
+ *                                  be captured: IDX_EINVAL)
+ *   ... any of idx_topk_prefill, _prefill_debug (no timing events),
+ *       _prefill_unfused, _rows, _decode_paged, _scan_bf16, _stream_floor
+ *       on `stream`, in any number and order ...
+ *   idx_topk_graph_end(stream, &g) stops recording and instantiates the graph;
+ *                                  on failure (a capture that was invalidated,
+ *                                  a call that failed) returns IDX_EHIP, *g =
+ *                                  NULL, and the stream is no longer capturing
+ *   idx_topk_graph_launch(g, s)    replays every recorded kernel on stream s
+ *                                  (any stream, also the NULL stream), in order
+ *   idx_topk_graph_destroy(g)      frees the graph (NULL is ignored)
+ *
+ * Every pointer and size is recorded by value: each replay reads the same
+ * input buffers (so new data goes into them before a replay), writes the
+ * same outputs and uses the same workspace.  Replays on one workspace must
+ * not overlap.  While a capture is open the recorded calls must not allocate
+ * (callers pass their output and workspace buffers), must not carry timing
+ * events (opts->ev_main_*: the capture then fails at
+ * idx_topk_graph_end), and idx_topk_read_stats (which synchronises) must not
+ * be called.  The graph object is host memory owned by the caller until
+ * idx_topk_graph_destroy; nothing recorded clears memory with a memset node
+ * (the chains clear their counters with kernels).
+ */
+typedef struct idx_topk_graph_s *idx_topk_graph;
+
+int idx_topk_graph_begin(void *stream);
+int idx_topk_graph_end(void *stream, idx_topk_graph *graph);
+int idx_topk_graph_launch(idx_topk_graph graph, void *stream);
+int idx_topk_graph_destroy(idx_topk_graph graph);
+
 #ifdef __cplusplus
 }
 #endif

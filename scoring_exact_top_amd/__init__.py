@@ -271,6 +271,60 @@ def scan_bf16_scores(workspace: torch.Tensor, B: int, N: int) -> torch.Tensor:
     return workspace[off: off + 4 * B * N].view(torch.float32).view(B, N).clone()
 
 
+_lib.idx_topk_graph_begin.restype = ctypes.c_int
+_lib.idx_topk_graph_begin.argtypes = [_vp]
+_lib.idx_topk_graph_end.restype = ctypes.c_int
+_lib.idx_topk_graph_end.argtypes = [_vp, ctypes.POINTER(_vp)]
+_lib.idx_topk_graph_launch.restype = ctypes.c_int
+_lib.idx_topk_graph_launch.argtypes = [_vp, _vp]
+_lib.idx_topk_graph_destroy.restype = ctypes.c_int
+_lib.idx_topk_graph_destroy.argtypes = [_vp]
+
+
+class Graph:
+    """A recorded chain of library calls (idx_topk_graph_*); launch() replays it."""
+
+    def __init__(self, handle):
+        self._h = handle
+
+    def launch(self, stream=None):
+        if not self._h:
+            raise ValueError("graph is destroyed")
+        _check(_lib.idx_topk_graph_launch(self._h, _stream(stream)))
+
+    def destroy(self):
+        if self._h:
+            h, self._h = self._h, None
+            _check(_lib.idx_topk_graph_destroy(h))
+
+    def __del__(self):
+        try:
+            self.destroy()
+        except Exception:
+            pass
+
+
+def capture(fn, stream=None) -> Graph:
+    """Record the library calls that fn() makes into a graph.  fn runs with a
+    side stream (or `stream`) current; it must pass its own output and
+    workspace buffers (nothing may allocate during the capture) and no
+    timing events."""
+    s = stream if stream is not None else torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        _check(_lib.idx_topk_graph_begin(_stream(s)))
+        h = _vp()
+        try:
+            fn()
+        except BaseException:
+            _lib.idx_topk_graph_end(_stream(s), ctypes.byref(h))
+            if h:
+                _lib.idx_topk_graph_destroy(h)
+            raise
+        _check(_lib.idx_topk_graph_end(_stream(s), ctypes.byref(h)))
+    return Graph(h)
+
+
 def stream_floor(src: torch.Tensor, out=None, stream=None):
     """idx_topk_stream_floor over src viewed as 256-byte records."""
     nbytes = src.numel() * src.element_size()

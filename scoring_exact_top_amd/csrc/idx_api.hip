@@ -103,6 +103,10 @@ static int prefill_common(const uint8_t* q, const float* q_scale, const uint8_t*
     A.tau_value = INFINITY;
     return launch_prefill_unfused(A, s);
   }
+  // N <= kCandCap with the default capacities: every valid row has L <=
+  // kCandCap, so its threshold is -inf, no segment overflows and the
+  // certificate cannot fail (no sampling, no repair to launch)
+  A.keep_all = (!A.force_tau && A.N > 0 && A.N <= kCandCap && A.cap_total >= kCandCap) ? 1 : 0;
   int rc = launch_prefill(A, s);
   if (rc == IDX_OK && tau_out) {
     if (hipMemcpyAsync(tau_out, A.tau, sizeof(float) * (size_t)Q, hipMemcpyDeviceToDevice, s) != hipSuccess)
@@ -231,4 +235,52 @@ extern "C" const char* idx_topk_strerror(int code) {
     case IDX_EHIP: return "HIP launch or copy failed";
     default: return "unknown error";
   }
+}
+
+// ---------------------------------------------------------------- graphs
+
+struct idx_topk_graph_s {
+  hipGraph_t graph;
+  hipGraphExec_t exec;
+};
+
+extern "C" int idx_topk_graph_begin(void* stream) {
+  if (!stream) return IDX_EINVAL;  // the legacy NULL stream cannot be captured
+  return hipStreamBeginCapture(static_cast<hipStream_t>(stream), hipStreamCaptureModeThreadLocal) == hipSuccess
+             ? IDX_OK
+             : IDX_EHIP;
+}
+
+extern "C" int idx_topk_graph_end(void* stream, idx_topk_graph* out) {
+  if (out) *out = nullptr;
+  if (!stream) return IDX_EINVAL;
+  hipGraph_t g = nullptr;
+  // ends the capture in every case, so that the stream is usable again
+  if (hipStreamEndCapture(static_cast<hipStream_t>(stream), &g) != hipSuccess || !g) {
+    (void)hipGetLastError();
+    return IDX_EHIP;
+  }
+  if (!out) {
+    hipGraphDestroy(g);
+    return IDX_EINVAL;
+  }
+  hipGraphExec_t e = nullptr;
+  if (hipGraphInstantiate(&e, g, nullptr, nullptr, 0) != hipSuccess) {
+    hipGraphDestroy(g);
+    return IDX_EHIP;
+  }
+  *out = new idx_topk_graph_s{g, e};
+  return IDX_OK;
+}
+
+extern "C" int idx_topk_graph_launch(idx_topk_graph graph, void* stream) {
+  if (!graph) return IDX_EINVAL;
+  return hipGraphLaunch(graph->exec, static_cast<hipStream_t>(stream)) == hipSuccess ? IDX_OK : IDX_EHIP;
+}
+
+extern "C" int idx_topk_graph_destroy(idx_topk_graph graph) {
+  if (!graph) return IDX_OK;
+  const bool ok = hipGraphExecDestroy(graph->exec) == hipSuccess && hipGraphDestroy(graph->graph) == hipSuccess;
+  delete graph;
+  return ok ? IDX_OK : IDX_EHIP;
 }

@@ -132,6 +132,7 @@ struct PrefillArgs {
   int64_t rstride;
   float* dbg_scores;    // [Q][N] or null
   int32_t force_tau;
+  int32_t keep_all;  // every valid row keeps all its keys (N <= kCandCap): no sampler, no repair
   float tau_value;
   hipEvent_t ev_main_start, ev_main_stop;  // host-side only: timing hooks
   int32_t main_reps;                       // host-side only: launches of the main kernel

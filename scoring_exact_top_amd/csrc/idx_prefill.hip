@@ -27,6 +27,13 @@ __global__ __launch_bounds__(kWG) void k_relayout_keys(PrefillArgs A) {
   uint4 v = make_uint4(0u, 0u, 0u, 0u);
   if (key < A.N) v = *reinterpret_cast<const uint4*>(A.k + relaid_src_offset(tile, blk, l));
   reinterpret_cast<uint4*>(A.kt)[chunk] = v;
+  if (A.keep_all) {  // the sampler is not launched: its other duties here
+    if (blockIdx.x == 0) clear_ctrl(A.ctrl, threadIdx.x);
+    for (int64_t t = chunk; t < A.Q; t += (int64_t)gridDim.x * kWG) {
+      const int s = A.row_start[t], e = A.row_end[t];
+      A.tau[t] = (s >= 0 && s <= e && e <= A.N) ? -INFINITY : INFINITY;
+    }
+  }
 }
 
 // ------------------------------------------------------------------ sampler
@@ -661,7 +668,7 @@ int launch_prefill(const PrefillArgs& A, hipStream_t stream) {
   if (A.Q == 0) return IDX_OK;
   const int64_t nchunks = (int64_t)((A.N + 63) >> 6) * 512;
   if (nchunks > 0) hipLaunchKernelGGL(k_relayout_keys, dim3((unsigned)(nchunks / kWG)), dim3(kWG), 0, stream, A);
-  hipLaunchKernelGGL(k_prefill_tau, dim3((A.Q + kWaves - 1) / kWaves), dim3(kWG), 0, stream, A);
+  if (!A.keep_all) hipLaunchKernelGGL(k_prefill_tau, dim3((A.Q + kWaves - 1) / kWaves), dim3(kWG), 0, stream, A);
   // the timing events, when given, are recorded by the launches themselves
   // (the first launch's start, the last launch's end; main_reps > 1 repeats
   // the idempotent kernel for timing)
@@ -675,6 +682,7 @@ int launch_prefill(const PrefillArgs& A, hipStream_t stream) {
       hipExtLaunchKernelGGL(k_prefill_pair<kPairFused>, dim3(grid), dim3(kWG), 0, stream, e0, e1, 0, A);
   }
   hipLaunchKernelGGL(k_prefill_select, dim3(A.Q), dim3(kWG), 0, stream, A);
+  if (A.keep_all) return hipGetLastError() == hipSuccess ? IDX_OK : IDX_EHIP;  // nothing can need repair
   hipLaunchKernelGGL(k_prefill_repair_score, dim3(kRepairGrid), dim3(kWG), 0, stream, A);
   hipLaunchKernelGGL(k_prefill_repair_pass<1>, dim3(kRepairGrid), dim3(kWG), 0, stream, A);
   hipLaunchKernelGGL(k_prefill_repair_pass<2>, dim3(kRepairGrid), dim3(kWG), 0, stream, A);
