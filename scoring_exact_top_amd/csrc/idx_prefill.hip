@@ -219,10 +219,16 @@ __global__ __launch_bounds__(kWG, 2) void k_prefill_pair(PrefillArgs A) {
   // past the end return 0.  (Carrying this pipeline across tiles measured
   // faster in isolation but does not fit the register budget of two
   // workgroups per CU.)
+  //
+  // Wave priority: raised over the sub-tiles (MFMAs with the epilogues
+  // interleaved), normal for the tail, so that of the two waves on a SIMD
+  // the one with MFMAs to issue goes first while the other finishes its
+  // tail (3-4% faster than equal priorities).
   v8i kb[4];
   float ks_cur = 0.f;
   auto tile_body = [&](int T) {
     const int ntoff = (T + nseg) * (kTile * kD);
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       v4f aA[4];
@@ -252,6 +258,7 @@ __global__ __launch_bounds__(kWG, 2) void k_prefill_pair(PrefillArgs A) {
       __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
+    __builtin_amdgcn_s_setprio(0);
     q1[3] = epi(qo.wh[1], qo.sh[1], aB, auB[2], auB[3]);
     tail(T, ks_cur);
     // The next tile's key scale is loaded only now, into the register the
