@@ -163,17 +163,36 @@ __device__ __forceinline__ const float* row_qscale(const float* q_scale, int64_t
 // a code within [-448, 448] is within 16 units of its value (half the
 // largest e4m3 spacing, 32), so |r_{m+1}| <= 16 sigma_m = (16*27/448)
 // sigma_{m+1} <= 448 sigma_{m+1}, and the next quotient needs no clamp.
-__device__ __forceinline__ void split_u(const uint8_t* q, const float* q_scale, const float* w, int64_t t,
-                                        uint32_t lane, uint8_t* codes, float (&sig)[kUTerms]) {
-  const uint8_t* base = q + t * (kH * kD) + 16 * (lane & 7u);
-  const float* qs = row_qscale(q_scale, t);
-  const uint32_t h0 = lane >> 3;
+// The loads of split_u: lane l's eight 16-byte code slices (heads
+// (l>>3) + 8i) and those heads' weights w_j q_scale_j.
+struct URaw {
   uint4 x[8];
   float wj[8];
+};
+
+__device__ __forceinline__ void split_u_codes(URaw& r, const uint8_t* q, int64_t t, uint32_t lane) {
+  const uint8_t* base = q + t * (kH * kD) + 16 * (lane & 7u);
+  const uint32_t h0 = lane >> 3;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) x[i] = *reinterpret_cast<const uint4*>(base + (h0 + 8 * i) * kD);
+  for (int i = 0; i < 8; ++i) r.x[i] = *reinterpret_cast<const uint4*>(base + (h0 + 8 * i) * kD);
+}
+
+__device__ __forceinline__ void split_u_core(const URaw& r, uint32_t lane, uint8_t* codes, float (&sig)[kUTerms]);
+
+__device__ __forceinline__ void split_u(const uint8_t* q, const float* q_scale, const float* w, int64_t t,
+                                        uint32_t lane, uint8_t* codes, float (&sig)[kUTerms]) {
+  const float* qs = row_qscale(q_scale, t);
+  const uint32_t h0 = lane >> 3;
+  URaw r;
+  split_u_codes(r, q, t, lane);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) wj[i] = w[t * kH + h0 + 8 * i] * qs[h0 + 8 * i];
+  for (int i = 0; i < 8; ++i) r.wj[i] = w[t * kH + h0 + 8 * i] * qs[h0 + 8 * i];
+  split_u_core(r, lane, codes, sig);
+}
+
+__device__ __forceinline__ void split_u_core(const URaw& r, uint32_t lane, uint8_t* codes, float (&sig)[kUTerms]) {
+  const uint4 (&x)[8] = r.x;
+  const float (&wj)[8] = r.wj;
   float acc[16];
 #pragma unroll
   for (int d = 0; d < 16; ++d) acc[d] = 0.f;
@@ -274,11 +293,56 @@ __device__ __forceinline__ void prepare_q2(QOp2& o, const uint8_t* q, const floa
 // the same nonzero partial sums in the same lanes and order as in its pair
 // and gets bit-identical scores (the other slot's rows are zero codes with
 // zero scales, and adding 0*0 leaves a sum unchanged).
+__device__ __forceinline__ void prepare_q_tail(QOp& o, const float (&sig)[kUTerms], uint32_t lane, uint8_t* scratch,
+                                               int slot);
+
 __device__ __forceinline__ void prepare_q(QOp& o, const uint8_t* q, const float* q_scale, const float* w,
                                           int64_t t, uint32_t lane, uint8_t* scratch, int slot) {
   head_ops(o.a, o.wh, q, q_scale, w, t, lane);
   float sig[kUTerms];
   split_u(q, q_scale, w, t, lane, scratch, sig);
+  prepare_q_tail(o, sig, lane, scratch, slot);
+}
+
+// prepare_q in two steps, for a caller that issues other loads between
+// them: prepare_q_load issues every load (the operand codes of head_ops,
+// the code slices of split_u, one weight w_j q_scale_j per lane), and
+// prepare_q_finish does the arithmetic with no memory access besides LDS.
+// The weights reach other lanes by shuffles; every value is computed as in
+// prepare_q, so the two give bit-identical operands.
+struct QRaw {
+  v8i a[4];
+  URaw u;
+  float wq;  // lane j: w_j * q_scale_j
+};
+
+__device__ __forceinline__ void prepare_q_load(QRaw& r, const uint8_t* q, const float* q_scale, const float* w,
+                                               int64_t t, uint32_t lane) {
+  const uint8_t* base = q + t * (kH * kD);
+  const uint32_t g = lane >> 4, i = lane & 15;
+#pragma unroll
+  for (int b = 0; b < 4; ++b) r.a[b] = ld32(base + (16 * b + i) * kD + 32 * g);
+  split_u_codes(r.u, q, t, lane);
+  r.wq = w[t * kH + lane] * row_qscale(q_scale, t)[lane];
+}
+
+__device__ __forceinline__ void prepare_q_finish(QOp& o, QRaw& r, uint32_t lane, uint8_t* scratch, int slot) {
+  const uint32_t g = lane >> 4;
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    o.a[b] = r.a[b];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) o.wh[4 * b + k] = 0.5f * __shfl(r.wq, 16 * b + 4 * (int)g + k, 64);
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r.u.wj[i] = __shfl(r.wq, (int)(lane >> 3) + 8 * i, 64);
+  float sig[kUTerms];
+  split_u_core(r.u, lane, scratch, sig);
+  prepare_q_tail(o, sig, lane, scratch, slot);
+}
+
+__device__ __forceinline__ void prepare_q_tail(QOp& o, const float (&sig)[kUTerms], uint32_t lane, uint8_t* scratch,
+                                               int slot) {
   wave_sync();
   const uint32_t g = lane >> 4, i = lane & 15;
   if (((i & 3u) >> 1) == (uint32_t)slot) {  // A row i carries term 2 (i >> 2) + (i & 1) of slot (i & 3) >> 1

@@ -42,12 +42,24 @@ struct DecodeArgs {
   float* scores;         // [B][max_pages*64] scores at logical positions
 };
 
-// Workgroup (g, b) takes chunk g of sequence b (a whole number of pages),
-// checks the chunk's page ids (and the length) and records the verdict in
-// its flag.  Wave w then scores the chunk's tiles w, w+4, ...: page ids are
-// loaded once per 64 tiles (lane i holds the page of the wave's i-th
-// tile) and key tiles two ahead.  Lane l writes the score of key l of each
-// tile (one coalesced 256-byte store per tile).
+// A key index past the end of any cache of fewer than 2^24 keys (2 GiB of
+// codes): the bounds check drops its loads.  Its byte offsets stay below
+// 2^31.  In a larger cache they read valid keys, which go unused.
+constexpr int kPastKeys = 0x00FFFFC0;
+
+// Workgroup (g, b) takes chunk g of sequence b (a whole number of pages)
+// and records in its flag whether the chunk holds a page id out of range
+// (or the length is).  Wave w scores the chunk's tiles w, w+4, ...: page
+// ids are loaded once per 64 tiles (lane i holds the page of the wave's
+// i-th tile, which is also where they are checked) and key tiles two
+// ahead.  Lane l writes the score of key l of each tile (one coalesced
+// 256-byte store per tile).  The prologue overlaps its round trips: the
+// query's loads and the first page ids go out together, then the first two
+// key tiles, and the query arithmetic runs while those are in flight (a
+// page check or query preparation ahead of the first key load idled the
+// memory system for about 4.5 us).  A bad page id is harmless to the loads
+// (the key buffer resource bounds them) and the sequence's scores are then
+// discarded by the selection.
 __global__ __launch_bounds__(kWG, 2) void k_decode_score(DecodeArgs A) {
   __shared__ uint8_t s_qprep[kWaves][kUTerms * kD];
   const int tid = threadIdx.x;
@@ -61,53 +73,69 @@ __global__ __launch_bounds__(kWG, 2) void k_decode_score(DecodeArgs A) {
   const int chunk = bad ? 0 : (((L + A.G - 1) / A.G) + 63) & ~63;
   const int k0 = g * chunk, k1 = min(L, k0 + chunk);
   const int p0 = k0 >> 6, p1 = (k1 + 63) >> 6;  // the chunk's pages (none when k0 >= k1)
-  for (int p = p0 + tid; p < p1; p += kWG) {
-    const int pg = pt[p];
-    bad |= pg < 0 || pg >= A.num_pages;
-  }
-  bad = __syncthreads_or(bad);
-  if (tid == 0) A.flags[(int64_t)b * A.G + g] = bad ? 1u : 0u;
-  if (bad || L <= A.K || p0 >= p1) return;
-
   const int tile0 = p0 + wave;
-  const int nt = tile0 < p1 ? (p1 - tile0 + kWaves - 1) / kWaves : 0;
-  if (nt == 0) return;
-  const KeyBuf kbuf = make_keybuf(A.k, A.k_scale, (int64_t)A.num_pages * 64);
-  QOp qo;
-  prepare_q(qo, A.q, A.q_scale, A.w, b, lane, s_qprep[wave], 0);
-  // scores through a buffer resource bounded by the chunk's end: a store
-  // past k1 (or of a padding step) is dropped by the bounds check, so no
-  // store sits behind a branch
-  const rsrc_t srow = __builtin_amdgcn_make_buffer_rsrc((void*)(A.scores + (int64_t)b * A.max_pages * 64),
-                                                        (short)0, k1 * 4, 0x00020000);
-  // Groups of up to 64 of the wave's tiles: lane i holds the page of the
-  // group's i-th tile, loaded before the group's loop so that the loop
-  // itself issues only tile loads and stores (a load behind a branch
-  // would make every later wait a full drain).  Three tile buffers in
-  // rotation give two tiles of lead; the roles rotate by unrolling rather
-  // than by register copies, which would wait for the loads just issued
-  // (the memory counter retires in order).
-#pragma unroll 1
-  for (int g0 = 0; g0 < nt; g0 += 64) {
-    const int ng = min(64, nt - g0);
-    const int pg_lane = pt[tile0 + kWaves * (g0 + min((int)lane, ng - 1))];
-    const auto base_of = [&](int i) { return __builtin_amdgcn_readlane(pg_lane, min(i, ng - 1)) << 6; };
+  const bool scoring = !bad && L > A.K && p0 < p1;
+  const int nt = scoring && tile0 < p1 ? (p1 - tile0 + kWaves - 1) / kWaves : 0;
+  if (!scoring) {
+    // nothing to score (a remapped or invalid sequence): only the page check
+    for (int p = p0 + tid; p < p1; p += kWG) {
+      const int pg = pt[p];
+      bad |= pg < 0 || pg >= A.num_pages;
+    }
+  } else if (nt > 0) {
+    const KeyBuf kbuf = make_keybuf(A.k, A.k_scale, (int64_t)A.num_pages * 64);
+    // scores through a buffer resource bounded by the chunk's end: a store
+    // past k1 (or of a padding step) is dropped by the bounds check, so no
+    // store sits behind a branch
+    const rsrc_t srow = __builtin_amdgcn_make_buffer_rsrc((void*)(A.scores + (int64_t)b * A.max_pages * 64),
+                                                          (short)0, k1 * 4, 0x00020000);
+    QRaw qr;
+    prepare_q_load(qr, A.q, A.q_scale, A.w, b, lane);
+    int ng = min(64, nt);
+    int pg_lane = pt[tile0 + kWaves * min((int)lane, ng - 1)];
+    // key index of the group's i-th tile; past the group, an index whose
+    // loads fall outside the key buffer (they return zeros without a memory
+    // access, so the loop's last steps and the final barrier do not wait
+    // out a round trip for tiles that are never used)
+    const auto base_of = [&](int i) {
+      return i < ng ? __builtin_amdgcn_readlane(pg_lane, min(i, ng - 1)) << 6 : kPastKeys;
+    };
     KeyTile ta, tb, tc;
     load_tile(ta, kbuf, base_of(0), lane);
     load_tile(tb, kbuf, base_of(1), lane);
-    const auto step = [&](KeyTile& use, KeyTile& refill, int i) {  // score tile i, load tile i + 2
-      load_tile(refill, kbuf, base_of(i + 2), lane);
-      const float sc = tile_score(qo, use);
-      const int my = ((tile0 + kWaves * (g0 + i)) << 6) + (int)lane;
-      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sc), srow, i < ng ? my * 4 : 0x7FFFFFF0, 0, 0);
-    };
+    QOp qo;
+    prepare_q_finish(qo, qr, lane, s_qprep[wave], 0);
+    // Groups of up to 64 of the wave's tiles.  Three tile buffers in
+    // rotation give two tiles of lead; the roles rotate by unrolling rather
+    // than by register copies, which would wait for the loads just issued
+    // (the memory counter retires in order).  Within a group the loop
+    // issues only tile loads and stores: a load behind a branch would make
+    // every later wait a full drain.
 #pragma unroll 1
-    for (int i = 0; i < ng; i += 3) {
-      step(ta, tc, i);
-      step(tb, ta, i + 1);
-      step(tc, tb, i + 2);
+    for (int g0 = 0; g0 < nt; g0 += 64) {
+      if (g0 > 0) {  // the next group's page ids and first tiles (sequences of more than 16384 keys per chunk)
+        ng = min(64, nt - g0);
+        pg_lane = pt[tile0 + kWaves * (g0 + min((int)lane, ng - 1))];
+        load_tile(ta, kbuf, base_of(0), lane);
+        load_tile(tb, kbuf, base_of(1), lane);
+      }
+      bad |= pg_lane < 0 || pg_lane >= A.num_pages;
+      const auto step = [&](KeyTile& use, KeyTile& refill, int i) {  // score tile i, load tile i + 2
+        load_tile(refill, kbuf, base_of(i + 2), lane);
+        const float sc = tile_score(qo, use);
+        const int my = ((tile0 + kWaves * (g0 + i)) << 6) + (int)lane;
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sc), srow, i < ng ? my * 4 : 0x7FFFFFF0, 0, 0);
+      };
+#pragma unroll 1
+      for (int i = 0; i < ng; i += 3) {
+        step(ta, tc, i);
+        step(tb, ta, i + 1);
+        step(tc, tb, i + 2);
+      }
     }
   }
+  bad = __syncthreads_or(bad);
+  if (tid == 0) A.flags[(int64_t)b * A.G + g] = bad ? 1u : 0u;
 }
 
 // ------------------------------------------------------------------ host

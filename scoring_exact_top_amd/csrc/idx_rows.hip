@@ -22,7 +22,10 @@
 // gathers bin b, which the range select finishes.  A bin too large for LDS
 // (massive ties) goes to the generic four-digit radix select over the row
 // in memory, with the same tie rule.
+#include <type_traits>
+
 #include "idx_internal.hpp"
+
 #include "idx_rows.hpp"
 
 namespace idxk {
@@ -438,26 +441,28 @@ __global__ __launch_bounds__(kWG) void k_rows_gather(RowsArgs A) {
   constexpr int U = 16;
   constexpr int kStep = kWG * U;
   constexpr int kRounds = 4;  // slices up to kRounds * kStep keys stay in registers
-  if (hi - lo <= (int64_t)kRounds * kStep) {
-    // the sample's loads first, then the whole slice's (clamped, no branch),
-    // so that the slice arrives while the cut is being selected
+  // the sample's loads first, then the whole slice's (clamped, no branch),
+  // so that the slice arrives while the cut is being selected; R rounds of
+  // U loads per thread, R the fewest that cover the slice
+  const auto in_regs = [&](auto RC) {
+    constexpr int R = decltype(RC)::value;
     uint32_t sk[kSampleBlocks];
     sample_load(row, L, sk, tid);
-    uint32_t k[kRounds][U];
+    uint32_t k[R][U];
 #pragma unroll
-    for (int r = 0; r < kRounds; ++r)
+    for (int r = 0; r < R; ++r)
 #pragma unroll
       for (int u = 0; u < U; ++u) k[r][u] = f2key(row[min(lo + r * kStep + u * kWG + tid, hi - 1)]);
     const uint32_t cut = sample_select(sk, L, K, sh, tid);
     uint32_t cnt = 0u;
 #pragma unroll
-    for (int r = 0; r < kRounds; ++r)
+    for (int r = 0; r < R; ++r)
 #pragma unroll
       for (int u = 0; u < U; ++u) cnt += (lo + r * kStep + u * kWG + tid < hi) & (k[r][u] >= cut) ? 1u : 0u;
     uint32_t total;
     uint32_t slot = block_exclusive_scan(cnt, sh, tid, total);
 #pragma unroll
-    for (int r = 0; r < kRounds; ++r)
+    for (int r = 0; r < R; ++r)
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int64_t i = lo + r * kStep + u * kWG + tid;
@@ -470,8 +475,11 @@ __global__ __launch_bounds__(kWG) void k_rows_gather(RowsArgs A) {
         }
       }
     if (tid == 0) A.gcnt[(int64_t)t * A.gsplit + g] = total;
-    return;
-  }
+  };
+  const int64_t n = hi - lo;
+  if (n <= kStep) return in_regs(std::integral_constant<int, 1>{});
+  if (n <= 2 * kStep) return in_regs(std::integral_constant<int, 2>{});
+  if (n <= kRounds * kStep) return in_regs(std::integral_constant<int, kRounds>{});
   const uint32_t cut = sample_cut(row, L, K, sh, tid);
   // longer slices, pass 1: per-thread counts, U loads in flight and no barrier; one
   // workgroup scan gives each thread its first slot; pass 2 re-reads the
