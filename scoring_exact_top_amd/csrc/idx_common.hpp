@@ -887,6 +887,13 @@ __device__ __forceinline__ void emit_range_regs(const uint32_t (&key)[M], const 
   const uint32_t lane = tid & 63;
   const int wave = tid >> 6;
   const uint32_t width = sel.last - sel.lo;
+  // every slot's output id first, all loads of a map that reads memory (one
+  // page-table entry per slot for paged rows) issued together and waited
+  // for after the counting below; translated inside the stores' branches,
+  // each load was waited for alone
+  int32_t mid[M];
+#pragma unroll
+  for (int j = 0; j < M; ++j) mid[j] = idmap(id[j]);
   const auto gt = [&](int j) { return key[j] > sel.last; };
   const auto eq = [&](int j) {  // recomputed at every use, as in tie_bound_regs
     uint32_t x = (uint32_t)id[j];
@@ -925,9 +932,9 @@ __device__ __forceinline__ void emit_range_regs(const uint32_t (&key)[M], const 
       const uint32_t bj = (uint32_t)__builtin_amdgcn_readlane((int)base, j);
       const bool g = gt(j), e = eq(j);
       const uint64_t bg = __ballot(g), be = __ballot(e);
-      if (g) out[(bj & 0xFFFFu) + rank_in(bg)] = idmap(id[j]);
+      if (g) out[(bj & 0xFFFFu) + rank_in(bg)] = mid[j];
       const uint32_t pe = (bj >> 16) + rank_in(be);
-      if (e && pe < (uint32_t)sel.rem) out[eq_base + pe] = idmap(id[j]);
+      if (e && pe < (uint32_t)sel.rem) out[eq_base + pe] = mid[j];
     }
   }
   for (int i = kr + tid; i < K; i += kWG) out[i] = -1;

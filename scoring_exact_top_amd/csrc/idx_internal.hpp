@@ -186,7 +186,8 @@ struct IdIdentity {
 };
 struct IdPaged {
   const int32_t* table;
-  __device__ int32_t operator()(int i) const { return table[i >> 6] * 64 + (i & 63); }
+  int32_t npages;  // the page index is clamped to [0, npages): an unused register slot (any id) reads a real entry
+  __device__ int32_t operator()(int i) const { return table[min(max(i >> 6, 0), npages - 1)] * 64 + (i & 63); }
 };
 
 // Key index of logical position i under a tile map.

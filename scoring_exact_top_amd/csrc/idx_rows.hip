@@ -258,7 +258,7 @@ struct PagedRows {
     return !__syncthreads_or(bad);
   }
   __device__ __forceinline__ const float* row(int b) const { return A.scores + (int64_t)b * A.ld; }
-  __device__ __forceinline__ IdPaged ids(int b) const { return IdPaged{A.table + (int64_t)b * A.max_pages}; }
+  __device__ __forceinline__ IdPaged ids(int b) const { return IdPaged{A.table + (int64_t)b * A.max_pages, A.max_pages}; }
 };
 
 // Dense rows come by the thousand: three workgroups per CU (LDS allows
