@@ -107,3 +107,43 @@ def test_stream_floor_values():
     want = src.reshape(n, 16, 4)[:, :, [0, 3]].sum(axis=(1, 2))
     got = lib.stream_floor(torch.from_numpy(src).cuda()).cpu().numpy()
     assert np.array_equal(got, want)
+
+
+def _sample_positions(L, blocks=16, width=256):
+    """Positions the selection's sampled cut reads in a row of L scores
+    (16 blocks of 256 consecutive keys, evenly spaced): used only to build
+    inputs that push the cut off, the check stays the oracle's."""
+    step = (L - width) // (blocks - 1)
+    return np.concatenate([np.arange(j * step, j * step + width) for j in range(blocks)])
+
+
+def _boost(k16_row, idx, factor):
+    """Multiply the BF16 keys at idx by a power of two (exact in BF16)."""
+    x = torch.from_numpy(k16_row[idx].view(np.int16)).view(torch.bfloat16) * factor
+    k16_row[idx] = x.view(torch.int16).numpy().view(np.uint16)
+
+
+def test_scan_biased_samples_take_the_fallbacks():
+    """Nonnegative head weights make a key's score scale with the key.
+    Stream 0: only the sampled keys boosted, so the cut lands above nearly
+    every key and the gathered keys number fewer than K (underflow).  Stream
+    1: every key but the sampled ones boosted, so the cut lands below almost
+    the whole row and the gather overflows its capacity.  Both go through
+    the in-kernel fallbacks and must still equal the oracle."""
+    L = 30000
+    case = synth.scan_case("scan_biased", 3, L, seed=21, K=2048)
+    case.w[:] = np.abs(case.w)
+    samp = _sample_positions(L)
+    _boost(case.k16[0], samp, 8.0)
+    rest = np.setdiff1d(np.arange(L), samp)
+    _boost(case.k16[1], rest, 8.0)
+    # the inputs do push the cut (r-th largest sample, r for about 2K keys
+    # above it) as intended, on the oracle's scores
+    _, _, sc = oracle.scan_bf16(case.q16[:2], case.w[:2], case.k16[:2], case.lens[:2], case.K)
+    r = -(-2 * case.K * samp.size // L)
+    above = [int((sc[b, :L] >= np.sort(sc[b, samp])[::-1][r - 1]).sum()) for b in range(2)]
+    log("keys at or above the sampled cut", above)
+    assert above[0] < case.K and above[1] > 6144
+    out, S, st = _run(case, scores=True)
+    log("stats", st)
+    _check(case, out, S, [0, 1, 2])
