@@ -197,6 +197,7 @@ size_t idx_topk_scan_bf16_workspace(int32_t B, int32_t N, int32_t K);
  *   k        [B][N][128] BF16 bit patterns, 16-byte aligned; stream b's keys at
  *            k + b*N*128; (N + 320)*256 must fit in 31 bits (IDX_EUNSUPPORTED)
  *   lens     [B] int32 device, 0 <= lens[b] <= N (a stream outside gets all -1)
+ *   B        at most 65535 (IDX_EUNSUPPORTED)
  *   K        1..2048
  *   out_idx  [B][K] int32: key positions, unsorted, ties at the K-th score to the
  *            lowest positions, -1 padded (streams with lens[b] <= K get all
@@ -237,6 +238,7 @@ size_t idx_topk_decode_workspace(int32_t B, int32_t max_pages, int32_t page_size
  *   w          [B][64] float
  *   page_table [B][max_pages] int32 physical page ids
  *   seq_lens   [B] int32 (device), 0 <= seq_len <= max_pages * page_size
+ *   B          at most 65535 (IDX_EUNSUPPORTED)
  *   page_size  must be 64
  *   out_idx    [B][K] int32: physical cache slots page*page_size + slot of the
  *              selected keys, unsorted, -1 padded; ties at the K-th score go

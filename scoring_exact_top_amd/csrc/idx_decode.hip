@@ -191,7 +191,7 @@ int decode_paged(const uint8_t* q, const float* q_scale, const uint8_t* k_cache,
                  int32_t max_pages, int32_t page_size, int32_t num_pages, int32_t K, int32_t* out_idx,
                  void* workspace, size_t workspace_bytes, hipStream_t stream, const idx_topk_opts* opts) {
   if (B < 0 || max_pages < 0 || num_pages < 0 || K < 1 || K > kKmax) return IDX_EINVAL;
-  if (page_size != 64) return IDX_EUNSUPPORTED;
+  if (page_size != 64 || B > kMaxGridY) return IDX_EUNSUPPORTED;
   if ((int64_t)max_pages * 64 * 4 > 0x7fffffffLL || (int64_t)num_pages * 64 > 0x7fffffffLL) return IDX_EINVAL;
   if (opts && (opts->force_tau || opts->lds_cap || opts->spill_cap)) return IDX_EINVAL;
   if (opts && (opts->main_reps < 0 || opts->main_reps > 1000)) return IDX_EINVAL;

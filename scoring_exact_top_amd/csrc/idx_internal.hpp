@@ -25,6 +25,10 @@ constexpr int kMaxSamples = 2048;  // longer rows widen the stride instead
 // a segment is sized so that a row short enough to keep all its keys
 // (L <= kCandCap, threshold -inf) never overflows it, and a row also fails
 // the certificate when one segment alone overflows.
+// Largest y (and z) dimension of a launch grid: bounds the sequences of
+// paged decode and the streams of the BF16 scan, which index it.
+constexpr int kMaxGridY = 65535;
+
 constexpr int kLdsCap = 4096;
 constexpr int kSpillCap = 4096;
 constexpr int kCandCap = kLdsCap + kSpillCap;

@@ -525,6 +525,7 @@ int launch_topk_rows_gathered(const RowsArgs& A, hipStream_t stream) {
   if (!A.gkey || A.gsplit < 1 || A.gsplit > kMaxGatherSplit || (A.gsplit & (A.gsplit - 1)) ||
       A.gcap * A.gsplit > kRowsCap)
     return IDX_EINVAL;
+  if (A.Q > kMaxGridY) return IDX_EUNSUPPORTED;  // rows index the gather grid's y dimension
   if (A.table) {
     hipLaunchKernelGGL(k_rows_gather<PagedRows>, dim3(A.gsplit, A.Q), dim3(kWG), 0, stream, A);
     hipLaunchKernelGGL(k_topk_rows<PagedRows>, dim3(A.Q), dim3(kWG), 0, stream, A);

@@ -197,6 +197,7 @@ int scan_bf16(const uint16_t* q, const float* w, const uint16_t* k, const int32_
               int32_t K, int32_t* out_idx, void* workspace, size_t workspace_bytes, hipStream_t stream,
               const idx_topk_opts* opts) {
   if (B < 0 || N < 0 || K < 1 || K > kKmax) return IDX_EINVAL;
+  if (B > kMaxGridY) return IDX_EUNSUPPORTED;  // streams index the grid's y dimension
   // one stream's keys per buffer resource, lookahead tiles included
   if (((int64_t)N + (kWaves + 1) * kTile) * kD * 2 > 0x7fffffffLL) return IDX_EUNSUPPORTED;
   if (opts && (opts->force_tau || opts->lds_cap || opts->spill_cap || opts->main_reps < 0 || opts->main_reps > 1000))

@@ -89,6 +89,7 @@ def test_host_argument_errors(lib):
     assert d(*dargs(ps=32)) == -2
     assert d(*dargs(K=0)) == -1
     assert d(*dargs(B=0)) == 0
+    assert d(*dargs(B=65536)) == -2                   # sequences index a grid dimension of 65535
     lib.idx_topk_strerror.restype = ctypes.c_char_p
     assert lib.idx_topk_strerror(-3) == b"workspace missing or too small"
 
@@ -113,3 +114,37 @@ def test_unfused_and_rows_argument_errors(lib):
     assert r(*rargs(s=None)) == -1
     assert r(*rargs(N=1 << 30, ld=1 << 30)) == -2     # rows longer than a buffer resource reaches
     assert r(*rargs(Q=0)) == 0
+
+
+def test_scan_argument_errors(lib):
+    """Argument checks of the BF16 scan and the floor kernel, all answered
+    before any device work."""
+    vp = ctypes.c_void_p
+    f = lib.idx_topk_scan_bf16
+    f.restype = ctypes.c_int
+    f.argtypes = [vp, vp, vp, vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, vp, vp, ctypes.c_size_t, vp, vp]
+    lib.idx_topk_scan_bf16_workspace.restype = ctypes.c_size_t
+    lib.idx_topk_scan_bf16_workspace.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]
+    good, ws = vp(1 << 20), vp(1 << 30)
+    need = lib.idx_topk_scan_bf16_workspace(32, 262144, 2048)
+    assert need >= 32 * 262144 * 4                    # the score rows
+    assert lib.idx_topk_scan_bf16_workspace(4, 100, 0) == 0
+    args = lambda **kw: [kw.get("q", good), good, kw.get("k", good), good, kw.get("B", 32),
+                         kw.get("N", 262144), kw.get("K", 2048), good, kw.get("ws", ws),
+                         kw.get("wsb", need), None, None]
+    assert f(*args(K=0)) == -1
+    assert f(*args(K=2049)) == -1
+    assert f(*args(B=-1)) == -1
+    assert f(*args(B=65536)) == -2                    # streams index a grid dimension of 65535
+    assert f(*args(N=1 << 23)) == -2                  # a stream's keys past a buffer resource's reach
+    assert f(*args(q=vp((1 << 20) + 8))) == -1        # q not 16-byte aligned
+    assert f(*args(k=None)) == -1
+    assert f(*args(ws=None)) == -3
+    assert f(*args(wsb=need - 1)) == -3
+    assert f(*args(B=0)) == 0
+    g = lib.idx_topk_stream_floor
+    g.restype = ctypes.c_int
+    g.argtypes = [vp, ctypes.c_int64, vp, vp]
+    assert g(good, -1, good, None) == -1
+    assert g(vp((1 << 20) + 4), 10, good, None) == -1
+    assert g(good, 0, good, None) == 0
