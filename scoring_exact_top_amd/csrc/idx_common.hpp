@@ -365,38 +365,6 @@ __device__ __forceinline__ void prepare_q_tail(QOp& o, const float (&sig)[kUTerm
   wave_sync();
 }
 
-// A prepared query row in device memory: kQOpWords dwords per lane, stored
-// field-major ([word][lane]) so that a wave's stores and loads are coalesced.
-constexpr int kQOpWords = 4 * 8 + 8 + 16 + 4;
-
-__device__ __forceinline__ void store_qop(const QOp& o, uint32_t* dst, uint32_t lane) {
-  int f = 0;
-#pragma unroll
-  for (int b = 0; b < 4; ++b)
-#pragma unroll
-    for (int k = 0; k < 8; ++k) dst[(f++) * 64 + lane] = (uint32_t)o.a[b][k];
-#pragma unroll
-  for (int k = 0; k < 8; ++k) dst[(f++) * 64 + lane] = (uint32_t)o.au[k];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) dst[(f++) * 64 + lane] = __float_as_uint(o.wh[i]);
-#pragma unroll
-  for (int r = 0; r < 4; ++r) dst[(f++) * 64 + lane] = __float_as_uint(o.sh[r]);
-}
-
-__device__ __forceinline__ void load_qop(QOp& o, const uint32_t* src, uint32_t lane) {
-  int f = 0;
-#pragma unroll
-  for (int b = 0; b < 4; ++b)
-#pragma unroll
-    for (int k = 0; k < 8; ++k) o.a[b][k] = (int)src[(f++) * 64 + lane];
-#pragma unroll
-  for (int k = 0; k < 8; ++k) o.au[k] = (int)src[(f++) * 64 + lane];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) o.wh[i] = __uint_as_float(src[(f++) * 64 + lane]);
-#pragma unroll
-  for (int r = 0; r < 4; ++r) o.sh[r] = __uint_as_float(src[(f++) * 64 + lane]);
-}
-
 // Keys of one 64-key tile as B operands plus the scale of this lane's key.
 struct KeyTile {
   v8i kb[4];

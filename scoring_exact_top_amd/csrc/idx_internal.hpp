@@ -194,10 +194,6 @@ struct IdPaged {
   __device__ int32_t operator()(int i) const { return table[min(max(i >> 6, 0), npages - 1)] * 64 + (i & 63); }
 };
 
-// Key index of logical position i under a tile map.
-template <class TM>
-__device__ __forceinline__ int key_index(const TM& tm, int i) { return tm(i >> 6) + (i & 63); }
-
 // Candidate source over a repair scratch row: element i is position s0 + i.
 template <class IdMap>
 struct SrcScratchT {
