@@ -217,9 +217,13 @@ int decode_paged(const uint8_t* q, const float* q_scale, const uint8_t* k_cache,
   // the timing events, when given, are recorded by the launches themselves
   // (main_reps > 1 repeats the idempotent scoring kernel for timing)
   const int reps = opts && opts->main_reps > 1 ? opts->main_reps : 1;
-  for (int r = 0; r < reps; ++r)
-    hipExtLaunchKernelGGL(k_decode_score, dim3(A.G, B), dim3(kWG), 0, stream, r == 0 ? ev0 : nullptr,
-                          r == reps - 1 ? ev1 : nullptr, 0, A);
+  for (int r = 0; r < reps; ++r) {
+    hipEvent_t e0 = r == 0 ? ev0 : nullptr, e1 = r == reps - 1 ? ev1 : nullptr;
+    if (e0 || e1)
+      hipExtLaunchKernelGGL(k_decode_score, dim3(A.G, B), dim3(kWG), 0, stream, e0, e1, 0, A);
+    else
+      hipLaunchKernelGGL(k_decode_score, dim3(A.G, B), dim3(kWG), 0, stream, A);
+  }
   if (hipGetLastError() != hipSuccess) return IDX_EHIP;
   RowsArgs R{A.scores, (int64_t)max_pages * 64, nullptr, seq_lens, B, max_pages * 64, K, out_idx, A.ctrl,
              page_table, max_pages, A.flags, A.G,

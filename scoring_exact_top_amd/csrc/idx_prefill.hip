@@ -678,15 +678,23 @@ int launch_prefill(const PrefillArgs& A, hipStream_t stream) {
   if (!A.keep_all) hipLaunchKernelGGL(k_prefill_tau, dim3((A.Q + kWaves - 1) / kWaves), dim3(kWG), 0, stream, A);
   // the timing events, when given, are recorded by the launches themselves
   // (the first launch's start, the last launch's end; main_reps > 1 repeats
-  // the idempotent kernel for timing)
+  // the idempotent kernel for timing); without events a plain launch (the
+  // extended one measured up to 1% slower per call)
   const unsigned grid = (unsigned)((A.Q + 1) / 2 * A.S);
   const int reps = A.main_reps > 1 ? A.main_reps : 1;
   for (int r = 0; r < reps; ++r) {
     hipEvent_t e0 = r == 0 ? A.ev_main_start : nullptr, e1 = r == reps - 1 ? A.ev_main_stop : nullptr;
-    if (A.dbg_scores)
-      hipExtLaunchKernelGGL(k_prefill_pair<kPairDebug>, dim3(grid), dim3(kWG), 0, stream, e0, e1, 0, A);
-    else
-      hipExtLaunchKernelGGL(k_prefill_pair<kPairFused>, dim3(grid), dim3(kWG), 0, stream, e0, e1, 0, A);
+    if (A.dbg_scores) {
+      if (e0 || e1)
+        hipExtLaunchKernelGGL(k_prefill_pair<kPairDebug>, dim3(grid), dim3(kWG), 0, stream, e0, e1, 0, A);
+      else
+        hipLaunchKernelGGL(k_prefill_pair<kPairDebug>, dim3(grid), dim3(kWG), 0, stream, A);
+    } else {
+      if (e0 || e1)
+        hipExtLaunchKernelGGL(k_prefill_pair<kPairFused>, dim3(grid), dim3(kWG), 0, stream, e0, e1, 0, A);
+      else
+        hipLaunchKernelGGL(k_prefill_pair<kPairFused>, dim3(grid), dim3(kWG), 0, stream, A);
+    }
   }
   hipLaunchKernelGGL(k_prefill_select, dim3(A.Q), dim3(kWG), 0, stream, A);
   if (A.keep_all) return hipGetLastError() == hipSuccess ? IDX_OK : IDX_EHIP;  // nothing can need repair
@@ -711,9 +719,13 @@ int launch_prefill_unfused(const PrefillArgs& A, hipStream_t stream) {
   hipLaunchKernelGGL(k_prefill_tau, dim3((A.Q + kWaves - 1) / kWaves), dim3(kWG), 0, stream, A);
   const unsigned grid = (unsigned)((A.Q + 1) / 2 * A.S);
   const int reps = A.main_reps > 1 ? A.main_reps : 1;
-  for (int r = 0; r < reps; ++r)
-    hipExtLaunchKernelGGL(k_prefill_pair<kPairDense>, dim3(grid), dim3(kWG), 0, stream,
-                          r == 0 ? A.ev_main_start : nullptr, r == reps - 1 ? A.ev_main_stop : nullptr, 0, A);
+  for (int r = 0; r < reps; ++r) {
+    hipEvent_t e0 = r == 0 ? A.ev_main_start : nullptr, e1 = r == reps - 1 ? A.ev_main_stop : nullptr;
+    if (e0 || e1)
+      hipExtLaunchKernelGGL(k_prefill_pair<kPairDense>, dim3(grid), dim3(kWG), 0, stream, e0, e1, 0, A);
+    else
+      hipLaunchKernelGGL(k_prefill_pair<kPairDense>, dim3(grid), dim3(kWG), 0, stream, A);
+  }
   if (hipGetLastError() != hipSuccess) return IDX_EHIP;
   RowsArgs R{A.dbg_scores, (int64_t)A.N, A.row_start, A.row_end, A.Q, A.N, A.K, A.out, A.ctrl};
   return launch_topk_rows(R, stream);

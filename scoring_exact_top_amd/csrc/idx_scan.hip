@@ -216,9 +216,13 @@ int scan_bf16(const uint16_t* q, const float* w, const uint16_t* k, const int32_
   // the timing events, when given, are recorded by the launches themselves
   // (main_reps > 1 repeats the idempotent scan for timing)
   const int reps = opts && opts->main_reps > 1 ? opts->main_reps : 1;
-  for (int r = 0; r < reps; ++r)
-    hipExtLaunchKernelGGL(k_scan_bf16, dim3(A.G, B), dim3(kWG), 0, stream, r == 0 ? ev0 : nullptr,
-                          r == reps - 1 ? ev1 : nullptr, 0, A);
+  for (int r = 0; r < reps; ++r) {
+    hipEvent_t e0 = r == 0 ? ev0 : nullptr, e1 = r == reps - 1 ? ev1 : nullptr;
+    if (e0 || e1)
+      hipExtLaunchKernelGGL(k_scan_bf16, dim3(A.G, B), dim3(kWG), 0, stream, e0, e1, 0, A);
+    else
+      hipLaunchKernelGGL(k_scan_bf16, dim3(A.G, B), dim3(kWG), 0, stream, A);
+  }
   if (hipGetLastError() != hipSuccess) return IDX_EHIP;
   const int gs = scan_gather_split(B);
   RowsArgs R{A.scores, (int64_t)N, nullptr, lens, B, N, K, out_idx, A.ctrl, nullptr, 0, nullptr, 0,
