@@ -195,7 +195,7 @@ size_t idx_topk_scan_bf16_workspace(int32_t B, int32_t N, int32_t K);
  *   q        [B][64][128] BF16 bit patterns (uint16), 16-byte aligned
  *   w        [B][64] float
  *   k        [B][N][128] BF16 bit patterns, 16-byte aligned; stream b's keys at
- *            k + b*N*128; (N + 320)*256 must fit in 31 bits (IDX_EUNSUPPORTED)
+ *            k + b*N*128; (N + 64)*256 must fit in 31 bits (IDX_EUNSUPPORTED)
  *   lens     [B] int32 device, 0 <= lens[b] <= N (a stream outside gets all -1)
  *   B        at most 65535 (IDX_EUNSUPPORTED)
  *   K        1..2048

@@ -92,8 +92,11 @@ __global__ __launch_bounds__(kWG, 2) void k_scan_bf16(ScanArgs A) {
                                                       L * 4, 0x00020000);
   const int voff = (int)li * (kD * 2) + 16 * (int)gi;
   v8bf kb[4][4];  // sub-tile c, K-step s: the current tile, refilled in place with the next one
+  // a refill runs up to tstep tiles past the stream's end: such tiles take
+  // an offset past any key buffer (2^31 bytes; the bounds check drops their
+  // loads), so no offset is computed beyond the stream
   const auto load_sub = [&](int tile, int c) {
-    const int soff = (tile * kTile + sub_off(c)) * (kD * 2);
+    const int soff = tile < tile_end ? (tile * kTile + sub_off(c)) * (kD * 2) : (int)0x80000000u;
 #pragma unroll
     for (int s = 0; s < 4; ++s)
       kb[c][s] = as_bf(__builtin_amdgcn_raw_buffer_load_b128(kr, voff, soff + 64 * s, 0));
@@ -198,8 +201,8 @@ int scan_bf16(const uint16_t* q, const float* w, const uint16_t* k, const int32_
               const idx_topk_opts* opts) {
   if (B < 0 || N < 0 || K < 1 || K > kKmax) return IDX_EINVAL;
   if (B > kMaxGridY) return IDX_EUNSUPPORTED;  // streams index the grid's y dimension
-  // one stream's keys per buffer resource, lookahead tiles included
-  if (((int64_t)N + (kWaves + 1) * kTile) * kD * 2 > 0x7fffffffLL) return IDX_EUNSUPPORTED;
+  // one stream's keys per buffer resource (the last tile's rows included)
+  if (((int64_t)N + kTile) * kD * 2 > 0x7fffffffLL) return IDX_EUNSUPPORTED;
   if (opts && (opts->force_tau || opts->lds_cap || opts->spill_cap || opts->main_reps < 0 || opts->main_reps > 1000))
     return IDX_EINVAL;
   if (B == 0) return IDX_OK;

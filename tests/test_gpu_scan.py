@@ -147,3 +147,25 @@ def test_scan_biased_samples_take_the_fallbacks():
     out, S, st = _run(case, scores=True)
     log("stats", st)
     _check(case, out, S, [0, 1, 2])
+
+
+def test_scan_longest_stream():
+    """One stream of the most keys the ABI accepts ((N + 64) * 256 < 2^31):
+    with a single stream, 1024 workgroups sweep it and each refill runs up
+    to 4096 tiles past the current one, so the sweep's last refills fall far
+    past the stream's end.  Full length and a ragged one, against the
+    oracle."""
+    import scoring_exact_top_amd as lib
+    N = 0x7FFFFFFF // 256 - 64
+    case = synth.scan_case("scan_longest", 1, N, seed=31, K=2048)
+    log("case", case.name, N)
+    dq, dw, dk = (torch.from_numpy(np.ascontiguousarray(a)).cuda()
+                  for a in (case.q16.view(np.int16), case.w, case.k16.view(np.int16)))
+    ws = lib.alloc_workspace(lib.scan_bf16_workspace_bytes(1, N, case.K), "cuda")
+    for L in (N, N - 12345):
+        lens = np.array([L], dtype=np.int32)
+        out = lib.scan_bf16(dq, dw, dk, torch.from_numpy(lens).cuda(), case.K, workspace=ws)
+        torch.cuda.synchronize()
+        topk, theta, sc = oracle.scan_bf16(case.q16, case.w, case.k16, lens, case.K)
+        check.check_selection(out.cpu().numpy()[0], sc[0], 0, L, case.K, theta[0],
+                              where="longest stream, L=%d" % L)
