@@ -113,7 +113,8 @@ size_t idx_topk_prefill_workspace(int32_t Q, int32_t N, int32_t K);
  * definition").
  *   q         [Q][64][128] uint8 e4m3fn codes, 16-byte aligned
  *   q_scale   [Q][64] float > 0, or NULL for all-ones
- *   k         [N][128] uint8 e4m3fn codes, 16-byte aligned
+ *   k         [N][128] uint8 e4m3fn codes, 16-byte aligned; (N + 64)*128 must
+ *             fit in 31 bits (IDX_EUNSUPPORTED otherwise)
  *   k_scale   [N] float > 0
  *   w         [Q][64] float head weights
  *   row_start [Q] int32, row_end [Q] int32: valid range [start, end), 0 <= start <= end <= N

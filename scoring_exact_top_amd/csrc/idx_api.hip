@@ -49,6 +49,8 @@ static int prefill_common(const uint8_t* q, const float* q_scale, const uint8_t*
   if (N > 0 && (!k || !k_scale)) return IDX_EINVAL;
   if (!aligned16(q) || (k && !aligned16(k))) return IDX_EINVAL;
   if (unfused && (int64_t)N * 4 > 0x7fffffffLL) return IDX_EUNSUPPORTED;
+  // the relaid key tiles (and the key codes) are addressed with 31-bit offsets
+  if (((int64_t)N + 64) * kD > 0x7fffffffLL) return IDX_EUNSUPPORTED;
   const PrefillLayout L = prefill_layout(Q, N, unfused);
   if (!workspace || workspace_bytes < L.total) return IDX_EWORKSPACE;
   if (((uintptr_t)workspace & 255u) != 0) return IDX_EINVAL;

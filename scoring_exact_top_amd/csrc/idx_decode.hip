@@ -42,10 +42,26 @@ struct DecodeArgs {
   float* scores;         // [B][max_pages*64] scores at logical positions
 };
 
-// A key index past the end of any cache of fewer than 2^24 keys (2 GiB of
-// codes): the bounds check drops its loads.  Its byte offsets stay below
-// 2^31.  In a larger cache they read valid keys, which go unused.
-constexpr int kPastKeys = 0x00FFFFC0;
+// One page of 64 keys (codes and scales) through buffer resources of its
+// own, with a 64-bit base: a cache of any size is addressed, and a page id
+// out of [0, num_pages) (or -1, a tile past a wave's share) gets empty
+// resources, whose loads return zeros without a memory access.
+__device__ __forceinline__ void load_page(KeyTile& t, const uint8_t* k, const float* k_scale, int num_pages, int pg,
+                                          uint32_t lane) {
+  const bool ok = pg >= 0 && pg < num_pages;
+  const int64_t key0 = ok ? (int64_t)pg * 64 : 0;
+  const rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)(k + key0 * kD), (short)0, ok ? 64 * kD : 0, 0x00020000);
+  const rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)(k_scale + key0), (short)0, ok ? 64 * 4 : 0, 0x00020000);
+  const int voff = (int)(lane & 15) * kD + 32 * (int)(lane >> 4);
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int soff = sub_off(c) * kD;
+    const v4i x = __builtin_amdgcn_raw_buffer_load_b128(rk, voff, soff, 0);
+    const v4i y = __builtin_amdgcn_raw_buffer_load_b128(rk, voff + 16, soff, 0);
+    t.kb[c] = cat8(x, y);
+  }
+  t.ks = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, (int)lane * 4, 0, 0));
+}
 
 // Workgroup (g, b) takes chunk g of sequence b (a whole number of pages)
 // and records in its flag whether the chunk holds a page id out of range
@@ -58,7 +74,7 @@ constexpr int kPastKeys = 0x00FFFFC0;
 // key tiles, and the query arithmetic runs while those are in flight (a
 // page check or query preparation ahead of the first key load idled the
 // memory system for about 4.5 us).  A bad page id is harmless to the loads
-// (the key buffer resource bounds them) and the sequence's scores are then
+// (its page gets empty resources) and the sequence's scores are then
 // discarded by the selection.
 __global__ __launch_bounds__(kWG, 2) void k_decode_score(DecodeArgs A) {
   __shared__ uint8_t s_qprep[kWaves][kUTerms * kD];
@@ -83,7 +99,6 @@ __global__ __launch_bounds__(kWG, 2) void k_decode_score(DecodeArgs A) {
       bad |= pg < 0 || pg >= A.num_pages;
     }
   } else if (nt > 0) {
-    const KeyBuf kbuf = make_keybuf(A.k, A.k_scale, (int64_t)A.num_pages * 64);
     // scores through a buffer resource bounded by the chunk's end: a store
     // past k1 (or of a padding step) is dropped by the bounds check, so no
     // store sits behind a branch
@@ -93,16 +108,14 @@ __global__ __launch_bounds__(kWG, 2) void k_decode_score(DecodeArgs A) {
     prepare_q_load(qr, A.q, A.q_scale, A.w, b, lane);
     int ng = min(64, nt);
     int pg_lane = pt[tile0 + kWaves * min((int)lane, ng - 1)];
-    // key index of the group's i-th tile; past the group, an index whose
-    // loads fall outside the key buffer (they return zeros without a memory
-    // access, so the loop's last steps and the final barrier do not wait
-    // out a round trip for tiles that are never used)
-    const auto base_of = [&](int i) {
-      return i < ng ? __builtin_amdgcn_readlane(pg_lane, min(i, ng - 1)) << 6 : kPastKeys;
-    };
+    // page of the group's i-th tile; past the group, -1: its loads return
+    // zeros without a memory access, so the loop's last steps and the final
+    // barrier do not wait out a round trip for tiles that are never used
+    const auto page_of = [&](int i) { return i < ng ? __builtin_amdgcn_readlane(pg_lane, min(i, ng - 1)) : -1; };
+    const auto load = [&](KeyTile& t, int i) { load_page(t, A.k, A.k_scale, A.num_pages, page_of(i), lane); };
     KeyTile ta, tb, tc;
-    load_tile(ta, kbuf, base_of(0), lane);
-    load_tile(tb, kbuf, base_of(1), lane);
+    load(ta, 0);
+    load(tb, 1);
     QOp qo;
     prepare_q_finish(qo, qr, lane, s_qprep[wave], 0);
     // Groups of up to 64 of the wave's tiles.  Three tile buffers in
@@ -116,12 +129,12 @@ __global__ __launch_bounds__(kWG, 2) void k_decode_score(DecodeArgs A) {
       if (g0 > 0) {  // the next group's page ids and first tiles (sequences of more than 16384 keys per chunk)
         ng = min(64, nt - g0);
         pg_lane = pt[tile0 + kWaves * (g0 + min((int)lane, ng - 1))];
-        load_tile(ta, kbuf, base_of(0), lane);
-        load_tile(tb, kbuf, base_of(1), lane);
+        load(ta, 0);
+        load(tb, 1);
       }
       bad |= pg_lane < 0 || pg_lane >= A.num_pages;
       const auto step = [&](KeyTile& use, KeyTile& refill, int i) {  // score tile i, load tile i + 2
-        load_tile(refill, kbuf, base_of(i + 2), lane);
+        load(refill, i + 2);
         const float sc = tile_score(qo, use);
         const int my = ((tile0 + kWaves * (g0 + i)) << 6) + (int)lane;
         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sc), srow, i < ng ? my * 4 : 0x7FFFFFF0, 0, 0);
@@ -192,6 +205,7 @@ int decode_paged(const uint8_t* q, const float* q_scale, const uint8_t* k_cache,
                  void* workspace, size_t workspace_bytes, hipStream_t stream, const idx_topk_opts* opts) {
   if (B < 0 || max_pages < 0 || num_pages < 0 || K < 1 || K > kKmax) return IDX_EINVAL;
   if (page_size != 64 || B > kMaxGridY) return IDX_EUNSUPPORTED;
+  // slots and logical positions are int32; the cache itself may be of any size
   if ((int64_t)max_pages * 64 * 4 > 0x7fffffffLL || (int64_t)num_pages * 64 > 0x7fffffffLL) return IDX_EINVAL;
   if (opts && (opts->force_tau || opts->lds_cap || opts->spill_cap)) return IDX_EINVAL;
   if (opts && (opts->main_reps < 0 || opts->main_reps > 1000)) return IDX_EINVAL;

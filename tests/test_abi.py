@@ -82,6 +82,7 @@ def test_host_argument_errors(lib):
     assert f(*args(wsb=16)) == -3
     assert f(*args(ws=vp((1 << 30) + 64))) == -1     # workspace not 256-byte aligned
     assert f(*args(Q=0)) == 0                         # empty batch: nothing to do
+    assert f(*args(N=(1 << 24) - 63)) == -2           # relaid keys past 31-bit offsets
     d = lib.idx_topk_decode_paged
     d.restype = ctypes.c_int
     d.argtypes = [vp] * 7 + [ctypes.c_int32] * 5 + [vp, vp, ctypes.c_size_t, vp]

@@ -126,3 +126,30 @@ def test_decode_main_events_time_the_scoring_kernel():
     out, st = _run(case, main_events=ev)
     assert ev[0].elapsed_time(ev[1]) > 0.0
     _check(case, out)
+
+
+def test_decode_cache_beyond_2gib():
+    """A page pool of more than 2 GiB of key codes (300000 pages of 64 keys):
+    the sequences' pages sit above the 2 GiB mark, so every key read crosses
+    it.  The same keys in a small pool give the oracle's reference."""
+    import scoring_exact_top_amd as lib
+    small = synth.decode_case("beyond_2gib", [5000, 3000, 70], seed=41, max_pages=100)
+    P, base = 300000, 270000                    # 300000 * 64 * 128 B = 2.46 GB of codes
+    assert (base * 64 * 128) > (1 << 31)
+    log("case", small.name, "pool pages", P, "first used page", base)
+    k_cache = torch.zeros((P, 64, 128), dtype=torch.uint8, device="cuda")
+    k_scale = torch.ones((P, 64), dtype=torch.float32, device="cuda")
+    n_small = small.k_cache.shape[0]                 # pages of the small pool
+    k_cache[base: base + n_small] = torch.from_numpy(small.k_cache).cuda()
+    k_scale[base: base + n_small] = torch.from_numpy(small.k_scale).cuda()
+    table = np.where(small.page_table >= 0, small.page_table + base, -1).astype(np.int32)
+    t = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    ws = lib.alloc_workspace(lib.decode_workspace_bytes(small.B, small.max_pages, 64, small.K), "cuda")
+    out = lib.decode_paged(t(small.q8), t(small.q_scale), k_cache, k_scale, t(small.w), t(table),
+                           t(small.seq_lens), small.K, workspace=ws)
+    torch.cuda.synchronize()
+    out = out.cpu().numpy()
+    shift = base * 64
+    out = np.where(out >= 0, out - shift, -1)    # physical slots of the small pool
+    _check(small, out)
+    assert lib.read_stats(ws)["bad_rows"] == 0
