@@ -137,6 +137,7 @@ struct PrefillArgs {
   float* dbg_scores;    // [Q][N] or null
   int32_t force_tau;
   int32_t keep_all;  // every valid row keeps all its keys (N <= kCandCap): no sampler, no repair
+  int32_t fuse_tau;  // one split: the main kernel takes its rows' thresholds itself
   float tau_value;
   hipEvent_t ev_main_start, ev_main_stop;  // host-side only: timing hooks
   int32_t main_reps;                       // host-side only: launches of the main kernel

@@ -27,11 +27,17 @@ __global__ __launch_bounds__(kWG) void k_relayout_keys(PrefillArgs A) {
   uint4 v = make_uint4(0u, 0u, 0u, 0u);
   if (key < A.N) v = *reinterpret_cast<const uint4*>(A.k + relaid_src_offset(tile, blk, l));
   reinterpret_cast<uint4*>(A.kt)[chunk] = v;
-  if (A.keep_all) {  // the sampler is not launched: its other duties here
+  if (A.keep_all || A.fuse_tau) {  // the sampler kernel is not launched: its other duties here
     if (blockIdx.x == 0) clear_ctrl(A.ctrl, threadIdx.x);
-    for (int64_t t = chunk; t < A.Q; t += (int64_t)gridDim.x * kWG) {
-      const int s = A.row_start[t], e = A.row_end[t];
-      A.tau[t] = (s >= 0 && s <= e && e <= A.N) ? -INFINITY : INFINITY;
+    const int64_t stride = (int64_t)gridDim.x * kWG;
+    if (A.keep_all) {
+      for (int64_t t = chunk; t < A.Q; t += stride) {
+        const int s = A.row_start[t], e = A.row_end[t];
+        A.tau[t] = (s >= 0 && s <= e && e <= A.N) ? -INFINITY : INFINITY;
+      }
+    } else {  // the main kernel writes the thresholds; the repair state starts at zero
+      for (int64_t i = chunk; i < (int64_t)A.rslots * 1024; i += stride) A.rhist[i] = 0u;
+      for (int64_t i = chunk; i < (int64_t)A.rslots * 2; i += stride) A.rcnt[i] = 0u;
     }
   }
 }
@@ -110,6 +116,43 @@ __global__ __launch_bounds__(kWG) void k_prefill_tau(PrefillArgs A) {
 // score to dbg_scores [Q][N]; kPairDense only writes the scores (no filter,
 // no candidates): the scoring stage of the unfused comparator.
 constexpr int kPairFused = 0, kPairDebug = 1, kPairDense = 2;
+
+// Head-weighted sum of one row's 16 heads held by this lane plus its two
+// u-block rows (ua, ub), in a fixed order (18 FMAs).
+__device__ __forceinline__ float pair_epi(const float (&wh)[16], const float (&shr)[2], const v4f (&a)[4], float ua,
+                                          float ub) {
+  float x = 0.f;
+#pragma unroll
+  for (int b = 0; b < 4; ++b)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) x = fmaf(wh[4 * b + r], fabsf(a[b][r]), x);
+  x = fmaf(shr[0], ua, x);
+  return fmaf(shr[1], ub, x);
+}
+
+// Both rows' scores of one tile (lane l: key l, key scale applied) with the
+// walk's arithmetic, unpipelined: the fused sampler's scores equal the
+// walk's bit for bit.
+__device__ __forceinline__ void pair_scores(const QOp2& qo, const KeyTile& kt, float& s0, float& s1) {
+  const v4f z = {0.f, 0.f, 0.f, 0.f};
+  float q0[4], q1[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    v4f aA[4], aB[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+      aA[b] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qo.a[0][b], kt.kb[c], z, 0, 0, 0, 0, 0, 0);
+    const v4f au = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qo.au, kt.kb[c], z, 0, 0, 0, 0, 0, 0);
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+      aB[b] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qo.a[1][b], kt.kb[c], z, 0, 0, 0, 0, 0, 0);
+    q0[c] = pair_epi(qo.wh[0], qo.sh[0], aA, au[0], au[1]);
+    q1[c] = pair_epi(qo.wh[1], qo.sh[1], aB, au[2], au[3]);
+  }
+  s0 = reduce_scatter4(q0[0], q0[1], q0[2], q0[3]) * kt.ks;
+  s1 = reduce_scatter4(q1[0], q1[1], q1[2], q1[3]) * kt.ks;
+}
+
 template <int MODE>
 __global__ __launch_bounds__(kWG, 2) void k_prefill_pair(PrefillArgs A) {
   __shared__ uint8_t s_qprep[kWaves][2 * kUTerms * kD];
@@ -131,7 +174,7 @@ __global__ __launch_bounds__(kWG, 2) void k_prefill_pair(PrefillArgs A) {
     if (t < A.Q) {
       const int s = A.row_start[t], e = A.row_end[t];
       if (s >= 0 && s <= e && e <= A.N) {
-        rs[r] = s; re[r] = e; tr[r] = A.tau[t];
+        rs[r] = s; re[r] = e; tr[r] = A.fuse_tau ? -INFINITY : A.tau[t];
         if (e > s) { lo = min(lo, s); hi = max(hi, e); }
       }
     }
@@ -139,6 +182,58 @@ __global__ __launch_bounds__(kWG, 2) void k_prefill_pair(PrefillArgs A) {
   QOp2 qo;
   prepare_q2(qo, A.q, A.q_scale, A.w, min(t0, A.Q - 1), min(t0 + 1, A.Q - 1), lane, s_qprep[wave]);
   __syncthreads();
+
+  // Fused sampler ("3.2 Sampled threshold"), when this workgroup owns both
+  // rows (one split, no forced threshold): the rows' thresholds are taken
+  // here, before the walk, instead of in a kernel of their own.  The waves
+  // score the sampled keys' tiles (once for both rows when they share the
+  // sample positions, as causal rows do) with the walk's arithmetic, so a
+  // threshold is one of the walk's scores; wave r then selects row r's.
+  if constexpr (MODE != kPairDense) {
+    if (A.fuse_tau) {
+      __shared__ uint32_t s_samp[2][kMaxSamples];
+      __shared__ uint32_t s_hist[2][256];
+      __shared__ float s_tau[2];
+      SampleGeom sg[2];
+#pragma unroll
+      for (int r = 0; r < 2; ++r)
+        sg[r] = re[r] > rs[r] ? sample_geom(re[r] - rs[r], A.cap_total) : SampleGeom{0, kSampleStride, 0};
+      const KeyBuf kbuf = make_keybuf(A.k, A.k_scale, A.N);
+      const auto pass = [&](int src, int n, bool st0, bool st1) {  // samples of row src's positions
+#pragma unroll 1
+        for (int i0 = kTile * wave; i0 < n; i0 += kTile * kWaves) {
+          KeyTile kt;
+          load_tile_gather(kt, kbuf, [&](int i) { return rs[src] + kSampleOffset + sg[src].stride * min(i0 + i, n - 1); },
+                           lane);
+          float s0, s1;
+          pair_scores(qo, kt, s0, s1);
+          const int i = i0 + (int)lane;
+          if (st0 && i < sg[0].n) s_samp[0][i] = f2key(s0);
+          if (st1 && i < sg[1].n) s_samp[1][i] = f2key(s1);
+        }
+      };
+      if (sg[0].n > 0 && sg[1].n > 0 && rs[0] == rs[1] && sg[0].stride == sg[1].stride) {
+        pass(0, max(sg[0].n, sg[1].n), true, true);
+      } else {
+        if (sg[0].n > 0) pass(0, sg[0].n, true, false);
+        if (sg[1].n > 0) pass(1, sg[1].n, false, true);
+      }
+      __syncthreads();
+      if (wave < 2) {
+        const SampleGeom g = wave == 0 ? sg[0] : sg[1];
+        if (g.n > 0) {
+          const SelResult sel = wave_radix_select(SrcLds{s_samp[wave]}, g.n, g.r, s_hist[wave], lane, false);
+          if (lane == 0) s_tau[wave] = key2f(sel.prefix);
+        }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        if (sg[r].n > 0) tr[r] = s_tau[r];  // else: -inf for a valid row (keeps all), +inf for an invalid one
+        if (tid == r && t0 + r < A.Q) A.tau[t0 + r] = tr[r];
+      }
+    }
+  }
 
   const KeyBuf kbuf = make_keybuf(A.k, A.k_scale, A.N);
   const int ntiles = (A.N + 63) >> 6;
@@ -163,13 +258,7 @@ __global__ __launch_bounds__(kWG, 2) void k_prefill_pair(PrefillArgs A) {
   // u-block rows (registers u0, u0+1 of the u accumulator), in a fixed order
   // (18 FMAs).
   const auto epi = [](const float (&wh)[16], const float (&shr)[2], const v4f (&a)[4], float ua, float ub) {
-    float x = 0.f;
-#pragma unroll
-    for (int b = 0; b < 4; ++b)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) x = fmaf(wh[4 * b + r], fabsf(a[b][r]), x);
-    x = fmaf(shr[0], ua, x);
-    return fmaf(shr[1], ub, x);
+    return pair_epi(wh, shr, a, ua, ub);
   };
   // Per-tile state: row B's accumulators of the last sub-tile (its epilogue
   // runs under the next sub-tile's MFMAs) and the tile's partial sums.
@@ -675,7 +764,8 @@ int launch_prefill(const PrefillArgs& A, hipStream_t stream) {
   if (A.Q == 0) return IDX_OK;
   const int64_t nchunks = (int64_t)((A.N + 63) >> 6) * 512;
   if (nchunks > 0) hipLaunchKernelGGL(k_relayout_keys, dim3((unsigned)(nchunks / kWG)), dim3(kWG), 0, stream, A);
-  if (!A.keep_all) hipLaunchKernelGGL(k_prefill_tau, dim3((A.Q + kWaves - 1) / kWaves), dim3(kWG), 0, stream, A);
+  if (!A.keep_all && !A.fuse_tau)
+    hipLaunchKernelGGL(k_prefill_tau, dim3((A.Q + kWaves - 1) / kWaves), dim3(kWG), 0, stream, A);
   // the timing events, when given, are recorded by the launches themselves
   // (the first launch's start, the last launch's end; main_reps > 1 repeats
   // the idempotent kernel for timing); without events a plain launch (the
