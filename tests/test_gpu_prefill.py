@@ -116,6 +116,27 @@ def test_sampler_matches_main_scores_bit_for_bit(e4m3):
     check_prefill_rows(case, r["out"], np.arange(case.Q), gpu_scores=r["scores"], e4m3=e4m3)
 
 
+def test_fused_sampler_bit_for_bit_with_ragged_ranges(e4m3):
+    """1024 rows: one workgroup per row pair, so the main kernel samples its
+    own rows.  Ragged ranges give the two rows of a pair different sample
+    positions (a pass per row) or, for equal starts, shared ones; every
+    threshold must be the r-th largest of the walk's own scores at the
+    sampled positions, and sampled rows must match the oracle."""
+    case = synth.random_case("fused_sampler", 1024, 20000, seed=29, K=2048, min_len=0, max_len=20000)
+    case.row_start[1::4] = case.row_start[0::4]        # some pairs share their start
+    case.row_end[1::4] = np.maximum(case.row_end[1::4], case.row_start[1::4])
+    log("case", case.name)
+    r = run_prefill(case, scores=True)
+    for t in range(case.Q):
+        s0, s1 = int(case.row_start[t]), int(case.row_end[t])
+        if s1 - s0 <= 8192:
+            assert r["tau"][t] == -np.inf, t
+            continue
+        want = np.float32(_sample_tau(r["scores"][t], s0, s1))
+        assert r["tau"][t].view(np.uint32) == want.view(np.uint32), (t, r["tau"][t], want)
+    check_prefill_rows(case, r["out"], np.arange(0, case.Q, 37), gpu_scores=r["scores"], e4m3=e4m3)
+
+
 def test_massive_ties_take_the_fast_path(e4m3):
     """Rows over 16 distinct keys: the threshold is the top score, held by
     about 10K keys, far more than the segments hold (capacity cut to 4096).
