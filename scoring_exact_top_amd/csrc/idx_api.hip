@@ -109,8 +109,9 @@ static int prefill_common(const uint8_t* q, const float* q_scale, const uint8_t*
   // kCandCap, so its threshold is -inf, no segment overflows and the
   // certificate cannot fail (no sampling, no repair to launch)
   A.keep_all = (!A.force_tau && A.N > 0 && A.N <= kCandCap && A.cap_total >= kCandCap) ? 1 : 0;
-  // one split per row pair: each workgroup owns its rows and samples them itself
-  A.fuse_tau = (!A.force_tau && !A.keep_all && A.N > 0 && A.S == 1) ? 1 : 0;
+  // the main kernel samples its rows itself (with S > 1 splits per row pair,
+  // each split samples the pair: the same values, S times, in parallel)
+  A.fuse_tau = (!A.force_tau && !A.keep_all && A.N > 0) ? 1 : 0;
   int rc = launch_prefill(A, s);
   if (rc == IDX_OK && tau_out) {
     if (hipMemcpyAsync(tau_out, A.tau, sizeof(float) * (size_t)Q, hipMemcpyDeviceToDevice, s) != hipSuccess)

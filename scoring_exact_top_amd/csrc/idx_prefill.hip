@@ -42,58 +42,22 @@ __global__ __launch_bounds__(kWG) void k_relayout_keys(PrefillArgs A) {
   }
 }
 
-// ------------------------------------------------------------------ sampler
+// ------------------------------------------------------------ thresholds
 
-// One workgroup per row: score the sampled keys exactly as the main pass
-// does, then take the r-th largest as tau.
+// Calls whose thresholds are not sampled by the main kernel (a forced
+// threshold, which the unfused comparator and the test knobs use; or no
+// keys at all): one thread per row sets tau (the forced value, +inf for an
+// invalid range, -inf for an empty one); workgroup 0 clears the counters,
+// and the repair state starts at zero.
 __global__ __launch_bounds__(kWG) void k_prefill_tau(PrefillArgs A) {
-  __shared__ uint32_t s_samp[kWaves][kMaxSamples];
-  __shared__ uint32_t s_hist[kWaves][256];
-  __shared__ uint8_t s_qprep[kWaves][kUTerms * kD];
-  const int tid = threadIdx.x;
-  const uint32_t lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  if (blockIdx.x == 0) clear_ctrl(A.ctrl, tid);
-  const int t = kWaves * blockIdx.x + wave;  // one row per wave
-  if (t >= A.Q) return;
-  if (t < A.rslots) {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) A.rhist[(int64_t)t * 1024 + 64 * i + lane] = 0u;
-    if (lane < 2) A.rcnt[2 * t + lane] = 0u;
+  const int64_t i0 = (int64_t)blockIdx.x * kWG + threadIdx.x, stride = (int64_t)gridDim.x * kWG;
+  if (blockIdx.x == 0) clear_ctrl(A.ctrl, threadIdx.x);
+  for (int64_t i = i0; i < (int64_t)A.rslots * 1024; i += stride) A.rhist[i] = 0u;
+  for (int64_t i = i0; i < (int64_t)A.rslots * 2; i += stride) A.rcnt[i] = 0u;
+  for (int64_t t = i0; t < A.Q; t += stride) {
+    const int s = A.row_start[t], e = A.row_end[t];
+    A.tau[t] = !(s >= 0 && s <= e && e <= A.N) ? INFINITY : A.force_tau ? A.tau_value : -INFINITY;
   }
-  const int s0 = A.row_start[t], s1 = A.row_end[t];
-  if (s0 < 0 || s0 > s1 || s1 > A.N) {
-    if (lane == 0) A.tau[t] = INFINITY;
-    return;
-  }
-  const int L = s1 - s0;
-  if (A.force_tau) {
-    if (lane == 0) A.tau[t] = A.tau_value;
-    return;
-  }
-  const SampleGeom sg = sample_geom(L, A.cap_total);
-  if (sg.n == 0) {
-    if (lane == 0) A.tau[t] = -INFINITY;
-    return;
-  }
-  QOp qo;
-  prepare_q(qo, A.q, A.q_scale, A.w, t, lane, s_qprep[wave], t & 1);
-  const KeyBuf kbuf = make_keybuf(A.k, A.k_scale, A.N);
-  // Score the samples 64 at a time, the next tile's gather in flight.
-  const auto key_of = [&](int i) { return s0 + kSampleOffset + sg.stride * min(i, sg.n - 1); };
-  KeyTile cur;
-  load_tile_gather(cur, kbuf, [&](int i) { return key_of(i); }, lane);
-#pragma unroll 1
-  for (int i0 = 0; i0 < sg.n; i0 += kTile) {
-    KeyTile nxt;
-    load_tile_gather(nxt, kbuf, [&](int i) { return key_of(i0 + kTile + i); }, lane);
-    const float sc = tile_score(qo, cur);
-    if (i0 + (int)lane < sg.n) s_samp[wave][i0 + lane] = f2key(sc);
-    cur = nxt;
-  }
-  wave_sync();
-  const SelResult sel = wave_radix_select(SrcLds{s_samp[wave]}, sg.n, sg.r, s_hist[wave], lane, false);
-  if (lane == 0) A.tau[t] = key2f(sel.prefix);
 }
 
 // ------------------------------------------------------ paired-row main
@@ -183,9 +147,10 @@ __global__ __launch_bounds__(kWG, 2) void k_prefill_pair(PrefillArgs A) {
   prepare_q2(qo, A.q, A.q_scale, A.w, min(t0, A.Q - 1), min(t0 + 1, A.Q - 1), lane, s_qprep[wave]);
   __syncthreads();
 
-  // Fused sampler ("3.2 Sampled threshold"), when this workgroup owns both
-  // rows (one split, no forced threshold): the rows' thresholds are taken
-  // here, before the walk, instead of in a kernel of their own.  The waves
+  // Fused sampler ("3.2 Sampled threshold"), unless a threshold is forced:
+  // the rows' thresholds are taken here, before the walk, instead of in a
+  // kernel of their own (with S splits per row pair each split samples the
+  // pair: the same values, in parallel; split 0 records them).  The waves
   // score the sampled keys' tiles (once for both rows when they share the
   // sample positions, as causal rows do) with the walk's arithmetic, so a
   // threshold is one of the walk's scores; wave r then selects row r's.
@@ -230,7 +195,7 @@ __global__ __launch_bounds__(kWG, 2) void k_prefill_pair(PrefillArgs A) {
 #pragma unroll
       for (int r = 0; r < 2; ++r) {
         if (sg[r].n > 0) tr[r] = s_tau[r];  // else: -inf for a valid row (keeps all), +inf for an invalid one
-        if (tid == r && t0 + r < A.Q) A.tau[t0 + r] = tr[r];
+        if (split == 0 && tid == r && t0 + r < A.Q) A.tau[t0 + r] = tr[r];
       }
     }
   }
@@ -764,8 +729,7 @@ int launch_prefill(const PrefillArgs& A, hipStream_t stream) {
   if (A.Q == 0) return IDX_OK;
   const int64_t nchunks = (int64_t)((A.N + 63) >> 6) * 512;
   if (nchunks > 0) hipLaunchKernelGGL(k_relayout_keys, dim3((unsigned)(nchunks / kWG)), dim3(kWG), 0, stream, A);
-  if (!A.keep_all && !A.fuse_tau)
-    hipLaunchKernelGGL(k_prefill_tau, dim3((A.Q + kWaves - 1) / kWaves), dim3(kWG), 0, stream, A);
+  if (!A.keep_all && !A.fuse_tau) hipLaunchKernelGGL(k_prefill_tau, dim3(kRepairGrid), dim3(kWG), 0, stream, A);
   // the timing events, when given, are recorded by the launches themselves
   // (the first launch's start, the last launch's end; main_reps > 1 repeats
   // the idempotent kernel for timing); without events a plain launch (the
@@ -806,7 +770,7 @@ int launch_prefill_unfused(const PrefillArgs& A, hipStream_t stream) {
   if (A.Q == 0) return IDX_OK;
   const int64_t nchunks = (int64_t)((A.N + 63) >> 6) * 512;
   if (nchunks > 0) hipLaunchKernelGGL(k_relayout_keys, dim3((unsigned)(nchunks / kWG)), dim3(kWG), 0, stream, A);
-  hipLaunchKernelGGL(k_prefill_tau, dim3((A.Q + kWaves - 1) / kWaves), dim3(kWG), 0, stream, A);
+  hipLaunchKernelGGL(k_prefill_tau, dim3(kRepairGrid), dim3(kWG), 0, stream, A);
   const unsigned grid = (unsigned)((A.Q + 1) / 2 * A.S);
   const int reps = A.main_reps > 1 ? A.main_reps : 1;
   for (int r = 0; r < reps; ++r) {
