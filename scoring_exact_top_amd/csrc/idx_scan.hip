@@ -15,9 +15,10 @@
 //                    (v_mfma_f32_16x16x32_bf16: 4 head blocks x 4 K-steps of
 //                    32 dims), keys as the B operand read straight from their
 //                    [N][128] rows (each load a 64-byte piece of each of 16
-//                    keys, nothing transposed, the page's operand-role
-//                    point), one tile of lead refilled sub-tile by sub-tile
-//                    in place;
+//                    keys): both MFMA operands take K-contiguous rows, so
+//                    the transpose that the page removes by swapping the
+//                    operands' roles never arises; one tile of lead refilled
+//                    sub-tile by sub-tile in place;
 //                    ReLU and head weights in registers, the same 4-group
 //                    reduce-scatter as the FP8 path; one FP32 score per key
 //                    written to the stream's score row.
