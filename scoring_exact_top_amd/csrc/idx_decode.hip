@@ -36,9 +36,11 @@ struct DecodeArgs {
   const float* w;
   const int32_t* table;  // [B][max_pages]
   const int32_t* seq_lens;
-  int32_t B, max_pages, num_pages, K, G;
+  int32_t B, max_pages, num_pages, K;
+  int32_t G;             // fixed assignment: workgroups per sequence
+  int32_t W;             // workgroups of the launch
+  int32_t balanced;      // 1: workgroups assigned to sequences in proportion to their tiles
   uint32_t* ctrl;
-  uint32_t* flags;       // [B][G]: 1 where workgroup g found the sequence invalid
   float* scores;         // [B][max_pages*64] scores at logical positions
 };
 
@@ -63,43 +65,80 @@ __device__ __forceinline__ void load_page(KeyTile& t, const uint8_t* k, const fl
   t.ks = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, (int)lane * 4, 0, 0));
 }
 
-// Workgroup (g, b) takes chunk g of sequence b (a whole number of pages)
-// and records in its flag whether the chunk holds a page id out of range
-// (or the length is).  Wave w scores the chunk's tiles w, w+4, ...: page
-// ids are loaded once per 64 tiles (lane i holds the page of the wave's
-// i-th tile, which is also where they are checked) and key tiles two
-// ahead.  Lane l writes the score of key l of each tile (one coalesced
-// 256-byte store per tile).  The prologue overlaps its round trips: the
-// query's loads and the first page ids go out together, then the first two
-// key tiles, and the query arithmetic runs while those are in flight (a
-// page check or query preparation ahead of the first key load idled the
-// memory system for about 4.5 us).  A bad page id is harmless to the loads
-// (its page gets empty resources) and the sequence's scores are then
-// discarded by the selection.
+// Each workgroup scores one piece of one sequence: a run of its 64-key
+// tiles (pages).  Balanced assignment (batches of at most 256 sequences):
+// every workgroup computes the same plan from the lengths, a sequence with
+// T tiles to score getting 1 + floor((W - B) T / sum T) workgroups (sum at
+// most W), which split its tiles evenly, so that a long sequence no longer
+// sets the kernel's time alone (equal lengths measured 16.6 us against
+// 19.8 us for the same keys spread unevenly); larger batches take a fixed
+// number of workgroups per sequence.  Sequences with nothing to score
+// (L <= K: remapped; invalid lengths) get no workgroup; page ids are checked
+// by the selection, and a bad one is harmless here (its page gets empty
+// resources) and the sequence's scores are then discarded.  Wave w scores
+// the piece's tiles w, w+4, ...: page ids are loaded once per 64 tiles
+// (lane i holds the page of the wave's i-th tile) and key tiles two ahead.
+// Lane l writes the score of key l of each tile (one coalesced 256-byte
+// store per tile).  The prologue overlaps its round trips: the query's
+// loads and the first page ids go out together, then the first two key
+// tiles, and the query arithmetic runs while those are in flight (a page
+// check or query preparation ahead of the first key load idled the memory
+// system for about 4.5 us).
 __global__ __launch_bounds__(kWG, 2) void k_decode_score(DecodeArgs A) {
   __shared__ uint8_t s_qprep[kWaves][kUTerms * kD];
+  __shared__ SelShared sh;
   const int tid = threadIdx.x;
   const uint32_t lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int g = blockIdx.x, b = blockIdx.y;
-  if (g == 0 && b == 0) clear_ctrl(A.ctrl, tid);  // first kernel of the call
-  const int L = A.seq_lens[b];
-  const int32_t* pt = A.table + (int64_t)b * A.max_pages;
-  bool bad = L < 0 || L > A.max_pages * 64;
-  const int chunk = bad ? 0 : (((L + A.G - 1) / A.G) + 63) & ~63;
-  const int k0 = g * chunk, k1 = min(L, k0 + chunk);
-  const int p0 = k0 >> 6, p1 = (k1 + 63) >> 6;  // the chunk's pages (none when k0 >= k1)
-  const int tile0 = p0 + wave;
-  const bool scoring = !bad && L > A.K && p0 < p1;
-  const int nt = scoring && tile0 < p1 ? (p1 - tile0 + kWaves - 1) / kWaves : 0;
-  if (!scoring) {
-    // nothing to score (a remapped or invalid sequence): only the page check
-    for (int p = p0 + tid; p < p1; p += kWG) {
-      const int pg = pt[p];
-      bad |= pg < 0 || pg >= A.num_pages;
+  const int wg = blockIdx.x;
+  if (wg == 0) clear_ctrl(A.ctrl, tid);  // first kernel of the call
+  int b = 0, p0 = 0, p1 = 0;              // this workgroup's piece: tiles [p0, p1) of sequence b
+  if (A.balanced) {
+    int T = 0;
+    if (tid < A.B) {
+      const int L = A.seq_lens[tid];
+      T = (L > A.K && L <= A.max_pages * 64) ? (L + 63) >> 6 : 0;
     }
-  } else if (nt > 0) {
-    // scores through a buffer resource bounded by the chunk's end: a store
+    uint32_t Tsum, Gsum;
+    block_exclusive_scan((uint32_t)T, sh, tid, Tsum);
+    const int G = T > 0 ? 1 + (int)((int64_t)(A.W - A.B) * T / (int64_t)(Tsum > 0u ? Tsum : 1u)) : 0;
+    const uint32_t first = block_exclusive_scan((uint32_t)G, sh, tid, Gsum);
+    if (tid == 0) sh.bucket = 0xFFFFFFFFu;
+    __syncthreads();
+    if (G > 0 && (uint32_t)wg >= first && (uint32_t)wg < first + (uint32_t)G) {
+      sh.bucket = (uint32_t)tid;
+      sh.above = (uint32_t)wg - first;
+      sh.inbucket = (uint32_t)G;
+      sh.pad0 = (uint32_t)T;
+    }
+    __syncthreads();
+    if (sh.bucket != 0xFFFFFFFFu) {
+      b = (int)sh.bucket;
+      const int64_t g = sh.above, Gb = sh.inbucket, Tb = sh.pad0;
+      p0 = (int)(Tb * g / Gb);
+      p1 = (int)(Tb * (g + 1) / Gb);
+    }
+  } else {
+    b = wg / A.G;
+    const int g = wg % A.G;
+    const int L = A.seq_lens[b];
+    if (L > A.K && L <= A.max_pages * 64) {
+      const int chunk = (((L + A.G - 1) / A.G) + 63) & ~63;
+      const int k0 = g * chunk;
+      if (k0 < L) {
+        p0 = k0 >> 6;
+        p1 = (min(L, k0 + chunk) + 63) >> 6;
+      }
+    }
+  }
+  if (p0 >= p1) return;
+  const int k1 = min(A.seq_lens[b], p1 << 6);  // the piece's last key + 1
+  const int32_t* pt = A.table + (int64_t)b * A.max_pages;
+  const int tile0 = p0 + wave;
+  const int nt = tile0 < p1 ? (p1 - tile0 + kWaves - 1) / kWaves : 0;
+  if (nt == 0) return;
+  {
+    // scores through a buffer resource bounded by the piece's end: a store
     // past k1 (or of a padding step) is dropped by the bounds check, so no
     // store sits behind a branch
     const rsrc_t srow = __builtin_amdgcn_make_buffer_rsrc((void*)(A.scores + (int64_t)b * A.max_pages * 64),
@@ -126,13 +165,12 @@ __global__ __launch_bounds__(kWG, 2) void k_decode_score(DecodeArgs A) {
     // every later wait a full drain.
 #pragma unroll 1
     for (int g0 = 0; g0 < nt; g0 += 64) {
-      if (g0 > 0) {  // the next group's page ids and first tiles (sequences of more than 16384 keys per chunk)
+      if (g0 > 0) {  // the next group's page ids and first tiles (pieces of more than 16384 keys)
         ng = min(64, nt - g0);
         pg_lane = pt[tile0 + kWaves * (g0 + min((int)lane, ng - 1))];
         load(ta, 0);
         load(tb, 1);
       }
-      bad |= pg_lane < 0 || pg_lane >= A.num_pages;
       const auto step = [&](KeyTile& use, KeyTile& refill, int i) {  // score tile i, load tile i + 2
         load(refill, i + 2);
         const float sc = tile_score(qo, use);
@@ -147,8 +185,6 @@ __global__ __launch_bounds__(kWG, 2) void k_decode_score(DecodeArgs A) {
       }
     }
   }
-  bad = __syncthreads_or(bad);
-  if (tid == 0) A.flags[(int64_t)b * A.G + g] = bad ? 1u : 0u;
 }
 
 // ------------------------------------------------------------------ host
@@ -159,6 +195,9 @@ static inline size_t a256(size_t x) { return (x + 255) & ~(size_t)255; }
 // sequence (a power of two, about 512 in all); each one's region holds
 // what its threads of the selection kernel hold in registers, 6144 / split.
 constexpr int kDecGatherKeys = 6144;
+
+// Scoring workgroups of a balanced launch: two per CU, all resident at once.
+constexpr int kDecodeWGs = 512;
 static inline int decode_gather_split(int32_t B) {
   int g = 1;  // a power of two
   while (2 * g <= kMaxGatherSplit && 2 * g * B <= 512) g *= 2;
@@ -166,7 +205,7 @@ static inline int decode_gather_split(int32_t B) {
 }
 
 struct DecodeLayout {
-  size_t ctrl, flags, scores, gcnt, gkey, gid, total;
+  size_t ctrl, scores, gcnt, gkey, gid, total;
 };
 
 static int decode_split_count(int32_t B, int32_t max_pages) {
@@ -184,7 +223,6 @@ static DecodeLayout decode_layout(int32_t B, int32_t max_pages) {
   size_t o = 0;
   const size_t b = (size_t)(B > 0 ? B : 0);
   L.ctrl = o; o = a256(o + 4 * kCtrlWords);
-  L.flags = o; o = a256(o + 4 * b * (size_t)decode_split_count(B, max_pages));
   L.scores = o; o = a256(o + 4 * b * (size_t)max_pages * 64);
   const size_t gs = (size_t)decode_gather_split(B);
   L.gcnt = o; o = a256(o + 4 * b * gs);
@@ -223,8 +261,9 @@ int decode_paged(const uint8_t* q, const float* q_scale, const uint8_t* k_cache,
   A.table = page_table; A.seq_lens = seq_lens;
   A.B = B; A.max_pages = max_pages; A.num_pages = num_pages; A.K = K;
   A.G = decode_split_count(B, max_pages);
+  A.balanced = B <= kWG ? 1 : 0;  // the plan's scan covers one length per thread
+  A.W = A.balanced ? kDecodeWGs : A.G * B;
   A.ctrl = reinterpret_cast<uint32_t*>(ws + L.ctrl);
-  A.flags = reinterpret_cast<uint32_t*>(ws + L.flags);
   A.scores = reinterpret_cast<float*>(ws + L.scores);
   hipEvent_t ev0 = opts ? static_cast<hipEvent_t>(opts->ev_main_start) : nullptr;
   hipEvent_t ev1 = opts ? static_cast<hipEvent_t>(opts->ev_main_stop) : nullptr;
@@ -234,13 +273,13 @@ int decode_paged(const uint8_t* q, const float* q_scale, const uint8_t* k_cache,
   for (int r = 0; r < reps; ++r) {
     hipEvent_t e0 = r == 0 ? ev0 : nullptr, e1 = r == reps - 1 ? ev1 : nullptr;
     if (e0 || e1)
-      hipExtLaunchKernelGGL(k_decode_score, dim3(A.G, B), dim3(kWG), 0, stream, e0, e1, 0, A);
+      hipExtLaunchKernelGGL(k_decode_score, dim3(A.W), dim3(kWG), 0, stream, e0, e1, 0, A);
     else
-      hipLaunchKernelGGL(k_decode_score, dim3(A.G, B), dim3(kWG), 0, stream, A);
+      hipLaunchKernelGGL(k_decode_score, dim3(A.W), dim3(kWG), 0, stream, A);
   }
   if (hipGetLastError() != hipSuccess) return IDX_EHIP;
   RowsArgs R{A.scores, (int64_t)max_pages * 64, nullptr, seq_lens, B, max_pages * 64, K, out_idx, A.ctrl,
-             page_table, max_pages, A.flags, A.G,
+             page_table, max_pages, num_pages,
              reinterpret_cast<uint32_t*>(ws + L.gkey), reinterpret_cast<int32_t*>(ws + L.gid),
              reinterpret_cast<uint32_t*>(ws + L.gcnt), kDecGatherKeys / decode_gather_split(B),
              decode_gather_split(B)};

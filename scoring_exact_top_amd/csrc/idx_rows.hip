@@ -249,12 +249,22 @@ struct PagedRows {
   static constexpr int kUnroll = 16;  // few long rows: one workgroup must cover the latency alone
   static constexpr int kMinBlocks = 1;
   RowsArgs A;
-  // all threads call this (one flag per thread, then a workgroup OR)
+  // all threads call this: the length and every page id the sequence uses,
+  // four loads per thread in flight per round of 1024 pages (clamped
+  // indexes, no branch per load), then a workgroup OR
   __device__ __forceinline__ bool range(int b, int& s0, int& s1, int tid) const {
     s0 = 0;
     s1 = A.row_end[b];
     bool bad = s1 < 0 || s1 > A.N;
-    for (int g = tid; g < A.nflags; g += kWG) bad |= A.flags[(int64_t)b * A.nflags + g] != 0u;
+    const int np = bad ? 0 : (s1 + 63) >> 6;
+    const int32_t* pt = A.table + (int64_t)b * A.max_pages;
+    for (int p0 = 0; p0 < np; p0 += 4 * kWG) {
+      int pg[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) pg[u] = pt[min(p0 + u * kWG + tid, np - 1)];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) bad |= (p0 + u * kWG + tid < np) & ((pg[u] < 0) | (pg[u] >= A.num_pages));
+    }
     return !__syncthreads_or(bad);
   }
   __device__ __forceinline__ const float* row(int b) const { return A.scores + (int64_t)b * A.ld; }

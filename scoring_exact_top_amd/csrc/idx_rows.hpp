@@ -8,8 +8,8 @@ namespace idxk {
 // Dense rows: row t's scores at scores + t*ld, position s at [s], range
 // [row_start[t], row_end[t]).  Paged decode rows (table != null): row b
 // covers logical positions [0, row_end[b]) (the sequence lengths, row_start
-// unused), is invalid when any of its nflags flags is set, and emits
-// physical slots table[b*max_pages + i/64]*64 + i%64.
+// unused), is invalid when one of the page ids it uses lies outside
+// [0, num_pages), and emits physical slots table[b*max_pages + i/64]*64 + i%64.
 struct RowsArgs {
   const float* scores;
   int64_t ld;
@@ -20,8 +20,7 @@ struct RowsArgs {
   uint32_t* ctrl;  // control words with the stats copies, or null
   const int32_t* table;
   int32_t max_pages;
-  const uint32_t* flags;  // [Q][nflags]
-  int32_t nflags;
+  int32_t num_pages;
   // Optional pre-gathered lists (paged rows): workgroup g of k_rows_gather
   // (gsplit a power of two <= kMaxGatherSplit per row) stores the keys at or above the
   // row's sampled cut found in slice g of the row into its own region

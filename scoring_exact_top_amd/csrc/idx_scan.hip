@@ -229,7 +229,7 @@ int scan_bf16(const uint16_t* q, const float* w, const uint16_t* k, const int32_
   }
   if (hipGetLastError() != hipSuccess) return IDX_EHIP;
   const int gs = scan_gather_split(B);
-  RowsArgs R{A.scores, (int64_t)N, nullptr, lens, B, N, K, out_idx, A.ctrl, nullptr, 0, nullptr, 0,
+  RowsArgs R{A.scores, (int64_t)N, nullptr, lens, B, N, K, out_idx, A.ctrl, nullptr, 0, 0,
              reinterpret_cast<uint32_t*>(ws + L.gkey), reinterpret_cast<int32_t*>(ws + L.gid),
              reinterpret_cast<uint32_t*>(ws + L.gcnt), 6144 / gs, gs};
   return launch_topk_rows_gathered(R, stream);

@@ -153,3 +153,27 @@ def test_decode_cache_beyond_2gib():
     out = np.where(out >= 0, out - shift, -1)    # physical slots of the small pool
     _check(small, out)
     assert lib.read_stats(ws)["bad_rows"] == 0
+
+
+def test_decode_large_batch_fixed_assignment():
+    """300 sequences (beyond the 256 the balanced assignment plans for: a
+    fixed number of scoring workgroups per sequence), ragged lengths around
+    K, two of them with a bad page id."""
+    g = np.random.default_rng(47)
+    lens = g.integers(1, 5000, size=300).astype(np.int32)
+    lens[:4] = [2048, 2049, 1, 4999]
+    case = synth.decode_case("large_batch", lens, seed=47, max_pages=80)
+    case.page_table[10, 0] = -5
+    case.page_table[11, (int(case.seq_lens[11]) - 1) // 64] = 10 ** 7
+    log("case", case.name, "B", case.B)
+    out, st = _run(case)
+    log("stats", st)
+    assert (out[10] == -1).all() and (out[11] == -1).all()
+    good = case.page_table.copy()
+    keep = np.ones(case.B, dtype=bool)
+    keep[[10, 11]] = False
+    sub = synth.DecodeCase(case.name, case.q8[keep], None if case.q_scale is None else case.q_scale[keep],
+                           case.k_cache, case.k_scale, case.w[keep], good[keep], case.seq_lens[keep],
+                           case.page_size, case.K)
+    _check(sub, out[keep])
+    assert st["bad_rows"] == 2
