@@ -237,6 +237,8 @@ struct DenseRows {
     s1 = A.row_end[t];
     return s0 >= 0 && s0 <= s1 && s1 <= A.N;
   }
+  // the pre-gather's check (the same)
+  __device__ __forceinline__ bool gather_range(int t, int& s0, int& s1, int tid) const { return range(t, s0, s1, tid); }
   __device__ __forceinline__ const float* row(int t) const { return A.scores + (int64_t)t * A.ld; }
   __device__ __forceinline__ IdIdentity ids(int) const { return IdIdentity{}; }
 };
@@ -266,6 +268,13 @@ struct PagedRows {
       for (int u = 0; u < 4; ++u) bad |= (p0 + u * kWG + tid < np) & ((pg[u] < 0) | (pg[u] >= A.num_pages));
     }
     return !__syncthreads_or(bad);
+  }
+  // the pre-gather checks the length only: the page ids decide the output,
+  // which the select kernel writes (-1 for a bad sequence), not what is gathered
+  __device__ __forceinline__ bool gather_range(int b, int& s0, int& s1, int) const {
+    s0 = 0;
+    s1 = A.row_end[b];
+    return s1 >= 0 && s1 <= A.N;
   }
   __device__ __forceinline__ const float* row(int b) const { return A.scores + (int64_t)b * A.ld; }
   __device__ __forceinline__ IdPaged ids(int b) const { return IdPaged{A.table + (int64_t)b * A.max_pages, A.max_pages}; }
@@ -440,7 +449,7 @@ __global__ __launch_bounds__(kWG) void k_rows_gather(RowsArgs A) {
   const uint32_t lane = tid & 63;
   const int g = blockIdx.x, t = blockIdx.y;
   int s0, s1;
-  if (!R.range(t, s0, s1, tid)) return;
+  if (!R.gather_range(t, s0, s1, tid)) return;
   const int L = s1 - s0, K = A.K;
   if (L <= K) return;
   const float* row = R.row(t) + s0;
