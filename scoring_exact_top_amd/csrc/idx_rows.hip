@@ -293,6 +293,28 @@ __global__ __launch_bounds__(kWG, Rows::kMinBlocks) void k_topk_rows(RowsArgs A)
   int32_t* out = A.out + (int64_t)t * A.K;
   uint32_t* stats = A.ctrl ? stat_copy(A.ctrl, blockIdx.x) : nullptr;
   if (stats && tid == 0) atomicAdd(&stats[kStRows], 1u);
+  // pre-gathered regions: every slot this thread may hold and the region's
+  // count, loaded first (their addresses depend on neither the count nor
+  // the row's checks), so that they arrive with the range check's loads
+  // instead of two round trips after it.  Region g is read by the 256/G
+  // threads g*256/G .. ; thread slot j holds region element
+  // (tid mod 256/G) + j*256/G.
+  uint32_t graw[kRowsRegs];
+  int32_t iraw[kRowsRegs];
+  uint32_t gc = 0u;
+  if (A.gcnt) {
+    const int G = A.gsplit;  // a power of two <= kMaxGatherSplit
+    const uint32_t tpr = (uint32_t)(kWG / G);
+    const int g = tid / (int)tpr;
+    const int64_t region = ((int64_t)t * G + g) * A.gcap;
+#pragma unroll
+    for (int j = 0; j < kRowsRegs; ++j) {
+      const int64_t e = region + min((uint32_t)tid % tpr + (uint32_t)j * tpr, (uint32_t)A.gcap - 1u);
+      graw[j] = A.gkey[e];
+      iraw[j] = A.gid[e];
+    }
+    gc = A.gcnt[(int64_t)t * G + g];
+  }
   int s0, s1;
   if (!R.range(t, s0, s1, tid)) {
     for (int i = tid; i < A.K; i += kWG) out[i] = -1;
@@ -310,14 +332,10 @@ __global__ __launch_bounds__(kWG, Rows::kMinBlocks) void k_topk_rows(RowsArgs A)
   const float* row = R.row(t) + s0;
 
   // pre-gathered regions that hold K to kRowsCap keys in all and each fit
-  // its threads' registers: select from them.  Region g is read by the
-  // 256/G threads g*256/G .. ; thread slot j holds region element
-  // (tid mod 256/G) + j*256/G.
+  // its threads' registers: select from them
   if (A.gcnt) {
-    const int G = A.gsplit;  // a power of two <= kMaxGatherSplit
+    const int G = A.gsplit;
     const uint32_t tpr = (uint32_t)(kWG / G);
-    const int g = tid / (int)tpr;
-    const uint32_t gc = A.gcnt[(int64_t)t * G + g];
     uint32_t n = 0u;
     block_exclusive_scan(tid % (int)tpr == 0 ? gc : 0u, S.sh, tid, n);
     const bool fits = !__syncthreads_or(gc > tpr * (uint32_t)kRowsRegs);
@@ -325,12 +343,11 @@ __global__ __launch_bounds__(kWG, Rows::kMinBlocks) void k_topk_rows(RowsArgs A)
       const RegLayout lay{(uint32_t)tid % tpr, tpr, gc, (uint32_t)kRowsRegs};
       uint32_t key[kRowsRegs];
       int32_t id[kRowsRegs];
-      const int64_t region = ((int64_t)t * G + g) * A.gcap;
 #pragma unroll
       for (int j = 0; j < kRowsRegs; ++j) {
         const bool v = lay.valid(j);
-        key[j] = v ? A.gkey[region + lay.at(j)] : 0u;
-        id[j] = v ? A.gid[region + lay.at(j)] : 0;
+        key[j] = v ? graw[j] : 0u;
+        id[j] = v ? iraw[j] : 0;
       }
       const auto kf = [&](int j) { return key[j]; };
       const RangeSel sel = (n > (uint32_t)K) ? range_select_regs<kRowsRegs>(kf, lay, K, S.sh, tid)
