@@ -266,12 +266,12 @@ extern "C" int idx_topk_graph_end(void* stream, idx_topk_graph* out) {
     return IDX_EHIP;
   }
   if (!out) {
-    hipGraphDestroy(g);
+    (void)hipGraphDestroy(g);
     return IDX_EINVAL;
   }
   hipGraphExec_t e = nullptr;
   if (hipGraphInstantiate(&e, g, nullptr, nullptr, 0) != hipSuccess) {
-    hipGraphDestroy(g);
+    (void)hipGraphDestroy(g);
     return IDX_EHIP;
   }
   *out = new idx_topk_graph_s{g, e};

@@ -494,7 +494,7 @@ __global__ __launch_bounds__(kWG) void k_rows_gather(RowsArgs A) {
 #pragma unroll
     for (int r = 0; r < R; ++r)
 #pragma unroll
-      for (int u = 0; u < U; ++u) cnt += (lo + r * kStep + u * kWG + tid < hi) & (k[r][u] >= cut) ? 1u : 0u;
+      for (int u = 0; u < U; ++u) cnt += ((lo + r * kStep + u * kWG + tid < hi) & (k[r][u] >= cut)) ? 1u : 0u;
     uint32_t total;
     uint32_t slot = block_exclusive_scan(cnt, sh, tid, total);
 #pragma unroll
@@ -530,7 +530,7 @@ __global__ __launch_bounds__(kWG) void k_rows_gather(RowsArgs A) {
 #pragma unroll
     for (int u = 0; u < U; ++u) k[u] = f2key(row[min(base + u * kWG + tid, hi - 1)]);
 #pragma unroll
-    for (int u = 0; u < U; ++u) cnt += (base + u * kWG + tid < hi) & (k[u] >= cut) ? 1u : 0u;
+    for (int u = 0; u < U; ++u) cnt += ((base + u * kWG + tid < hi) & (k[u] >= cut)) ? 1u : 0u;
   }
   uint32_t total;
   uint32_t slot = block_exclusive_scan(cnt, sh, tid, total);
@@ -558,7 +558,7 @@ __global__ __launch_bounds__(kWG) void k_rows_gather(RowsArgs A) {
 
 int launch_topk_rows_gathered(const RowsArgs& A, hipStream_t stream) {
   if (A.Q == 0) return IDX_OK;
-  if (!A.gkey || A.gsplit < 1 || A.gsplit > kMaxGatherSplit || (A.gsplit & (A.gsplit - 1)) ||
+  if (!A.gkey || A.gsplit < 1 || A.gsplit > kMaxGatherSplit || (A.gsplit & (A.gsplit - 1)) || A.gcap < 1 ||
       A.gcap * A.gsplit > kRowsCap)
     return IDX_EINVAL;
   if (A.Q > kMaxGridY) return IDX_EUNSUPPORTED;  // rows index the gather grid's y dimension
