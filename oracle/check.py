@@ -1,21 +1,23 @@
 """Exactness checks against the oracle -- TEST INFRASTRUCTURE ONLY.
 
-The criterion is the one of the Fusing Indexer Scoring and Exact Top-k page, "2.3 Problem
-definition": indices lie in the valid range and are distinct, the K selected
-scores sorted equal the true top-K scores, and ties may resolve to any valid
-index.  Because the GPU computes scores in FP32 while the oracle is fp64, the
-selection is judged with a relative tolerance REL_TOL around the oracle's K-th
-score theta, in both directions:
+Criterion (Fusing Indexer Scoring and Exact Top-k page, "2.3 Problem definition"): every
+returned id belongs to the row's half-open range, no id repeats, and the
+multiset of scores of the returned ids is the multiset of the K largest
+scores of the row; which of several equal-scoring ids is returned is free.
+The GPU scores in FP32 and the oracle in fp64, so the selection is judged
+with a relative tolerance REL_TOL around the oracle's K-th score theta, in
+both directions:
 
   * every selected index s has I[s] >= theta - REL_TOL*|theta|
   * every index s with I[s] > theta + REL_TOL*|theta| is selected.
 
-Scores emitted by the debug path are judged element-wise:
+Scores emitted by the debug paths are judged element-wise:
   |S - I| <= REL_TOL*|I|   or   |S - I| <= GAMMA*B[s]
 where B[s] = k_scale[s] * sum_j |w_j q_scale_j| * sum_d |dec(q)_jd dec(k)_sd| is the
 magnitude that bounds FP32 rounding of the ~194-operation dot/ReLU/head sum
 (standard forward error bound gamma_n = n*u/(1-n*u), n = 194, u = 2^-24).  The
-second clause only matters where I itself cancels to near zero.
+second clause only matters where I itself cancels to near zero.  B is
+computed by bound_from_values (both the FP8 and the BF16 paths use it).
 """
 from __future__ import annotations
 
@@ -158,11 +160,23 @@ def check_debug_canonical(out_row, S_row, start, end, K, where=""):
               % (where, int(np.setxor1d(got, want).size)))
 
 
+def bound_from_values(qd, kd, wq, ks=None):
+    """B[s] = ks[s] * sum_j |wq_j| * sum_d |qd[j,d]| * |kd[s,d]|  (numpy, fp64).
+
+    qd [64, D] decoded query codes (no scale), kd [n, D] decoded key codes,
+    wq [64] the head weights times the query scales, ks [n] key scales (None:
+    all ones).  Every term is nonnegative, so B bounds |I| and the magnitude
+    of every partial sum of the FP32 score computation."""
+    qa = np.abs(np.asarray(qd, dtype=np.float64))           # [64, D]
+    ka = np.abs(np.asarray(kd, dtype=np.float64))           # [n, D]
+    per_head = ka @ qa.T                                     # [n, 64]: sum over d
+    b = per_head @ np.abs(np.asarray(wq, dtype=np.float64))  # [n]: sum over heads
+    return b if ks is None else np.asarray(ks, dtype=np.float64) * b
+
+
 def score_bound(q8, q_scale, k8, k_scale, w, t, ids, e4m3_table):
-    """B[t,s] for the cancellation clause (numpy, fp64)."""
-    qd = np.abs(e4m3_table[q8[t]])                       # [64,128]
-    kd = np.abs(e4m3_table[k8[np.asarray(ids)]])         # [n,128]
+    """B[t,s] of the FP8 path for row t and key ids `ids`."""
+    ids = np.asarray(ids)
     qs = np.ones(64) if q_scale is None else q_scale[t].astype(np.float64)
-    wq = np.abs(w[t].astype(np.float64) * qs)            # [64]
-    per_head = kd @ qd.T                                  # [n,64]
-    return k_scale[np.asarray(ids)].astype(np.float64) * (per_head @ wq)
+    return bound_from_values(e4m3_table[q8[t]], e4m3_table[k8[ids]], w[t].astype(np.float64) * qs,
+                             k_scale[ids].astype(np.float64))

@@ -27,11 +27,8 @@ def _dec(a16):
 
 
 def _bound(case, b):
-    """B[i] = sum_j |w_j| sum_d |q_jd k_id|: the magnitude that bounds FP32
-    rounding of one score (as for the FP8 path)."""
-    q = np.abs(_dec(case.q16[b]))
-    k = np.abs(_dec(case.k16[b, :case.lens[b]]))
-    return np.abs(case.w[b].astype(np.float64)) @ (q @ k.T)
+    """B[i] of stream b (the pinned check.bound_from_values, unit scales)."""
+    return check.bound_from_values(_dec(case.q16[b]), _dec(case.k16[b, :case.lens[b]]), case.w[b].astype(np.float64))
 
 
 def _run(case, scores=False):

@@ -453,3 +453,153 @@ def test_scan_ties_and_short_streams():
     topk, _, _ = oracle.scan_bf16(q16, w, k16, np.array([N, 60], np.int32), K)
     assert topk[0].tolist() == list(range(K))
     assert topk[1].tolist() == list(range(60)) + [-1] * (K - 60)
+
+
+# ------------------------------------------------- cancellation-clause bound
+#
+# B[s] = k_scale[s] * sum_j |w_j q_scale_j| * sum_d |dec(q)_jd| |dec(k)_sd| is the
+# magnitude behind the cancellation clause of check_scores.  The pins below tie
+# check.bound_from_values (and the FP8 wrapper score_bound) to facts outside
+# it; the mutants are plausible slips, and each must fail at least one pin.
+
+def _bound_ok(q8, qs, k8, ks, w, t, ids, table, bound_fn):
+    return bound_fn(table[q8[t]], table[k8[ids]], w[t].astype(np.float64) * qs[t].astype(np.float64),
+                    ks[ids].astype(np.float64))
+
+
+def _pin_linear_regime(bound_fn, table):
+    """Nonnegative codes, w >= 0: no ReLU is active and no term cancels, so B
+    equals the oracle's own score I (to fp64 rounding of the head sum)."""
+    rng = np.random.default_rng(40)
+    Q, N = 2, 300
+    q8 = _finite_codes(rng, (Q, 64, 128), nonneg=True)
+    k8 = _finite_codes(rng, (N, 128), nonneg=True)
+    qs = rng.uniform(0.01, 1.0, (Q, 64)).astype(np.float32)
+    ks = rng.uniform(0.01, 4.0, N).astype(np.float32)
+    w = np.abs(rng.normal(0, 0.125, (Q, 64))).astype(np.float32)
+    case = _case(q8, qs, k8, ks, w, [0] * Q, [N] * Q, 32)
+    _, _, sc = oracle.prefill_case(case)
+    ids = np.arange(N)
+    return all(np.allclose(_bound_ok(q8, qs, k8, ks, w, t, ids, table, bound_fn), sc[t], rtol=1e-13, atol=0)
+               for t in range(Q))
+
+
+def _pin_head_pair(bound_fn, table):
+    """Heads 0 and 1 hold q and -q (sign bit flipped), weights a > 0 and -b < 0,
+    all other weights 0.  Closed form, summed term by term in exact rational
+    arithmetic from torch's e4m3 decode:
+        B[s] = ks[s] * (a qs0 + b qs1) * sum_d |q_d| |k_sd|
+    which differs from |I[s]| = ks[s] |a qs0 relu(c) - b qs1 relu(-c)| whenever
+    the products q_d k_sd have mixed signs."""
+    rng = np.random.default_rng(41)
+    N = 40
+    q8 = np.zeros((1, 64, 128), np.uint8)
+    qrow = _finite_codes(rng, 128)
+    q8[0, 0] = qrow
+    q8[0, 1] = qrow ^ 0x80
+    k8 = _finite_codes(rng, (N, 128))
+    qs = np.ones((1, 64), np.float32)
+    qs[0, 0], qs[0, 1] = 0.75, 1.25
+    ks = rng.uniform(0.5, 2.0, N).astype(np.float32)
+    w = np.zeros((1, 64), np.float32)
+    w[0, 0], w[0, 1] = 0.375, -0.625
+    qd = _torch_e4m3(qrow)
+    kd = _torch_e4m3(k8)
+    hw = Fraction(float(w[0, 0])) * Fraction(float(qs[0, 0])) - Fraction(float(w[0, 1])) * Fraction(float(qs[0, 1]))
+    want = np.array([float(Fraction(float(ks[s])) * hw *
+                           sum(abs(Fraction(float(qd[d]))) * abs(Fraction(float(kd[s, d]))) for d in range(128)))
+                     for s in range(N)])
+    got = _bound_ok(q8, qs, k8, ks, w, 0, np.arange(N), table, bound_fn)
+    return np.allclose(got, want, rtol=1e-14, atol=0)
+
+
+def _pin_dominates(bound_fn, table):
+    """|I| <= B on random signed data (triangle inequality), and B is not
+    off by a factor of heads or dims: with unit-variance q and k and w of
+    standard deviation sigma, B ~ 64 * 0.8 sigma * 128 * (2/pi) ~ 4200 sigma
+    while a typical |I| ~ sqrt(64) * sigma * sqrt(E relu(c)^2) * 0.8 ~ 50 sigma,
+    so the median ratio B/|I| sits near 100; it must stay in [30, 400]."""
+    case = synth.random_case("pin_bound", 3, 1500, seed=42, K=64, min_len=1500)
+    _, _, sc = oracle.prefill_case(case)
+    ok = True
+    for t in range(case.Q):
+        ids = np.arange(case.N)
+        B = _bound_ok(case.q8, case.q_scale, case.k8, case.k_scale, case.w, t, ids, table, bound_fn)
+        I = sc[t]
+        ok &= bool(np.all(np.abs(I) <= B * (1 + 1e-12)))
+        ratio = np.median(B / np.maximum(np.abs(I), 1e-300))
+        ok &= bool(30.0 < ratio < 400.0)
+    return ok
+
+
+_BOUND_PINS = [_pin_linear_regime, _pin_head_pair, _pin_dominates]
+
+
+def _mut_no_kscale(qd, kd, wq, ks=None):
+    return check.bound_from_values(qd, kd, wq, None)
+
+
+def _mut_no_abs_codes(qd, kd, wq, ks=None):
+    b = (np.asarray(kd, np.float64) @ np.asarray(qd, np.float64).T) @ np.abs(wq)
+    return b * ks
+
+
+def _mut_no_abs_weights(qd, kd, wq, ks=None):
+    b = (np.abs(kd) @ np.abs(qd).T) @ np.asarray(wq, np.float64)
+    return b * ks
+
+
+def _mut_heads_summed_first(qd, kd, wq, ks=None):
+    # sums the weighted query over heads before taking magnitudes (the wrong axis order)
+    u = np.abs(np.asarray(wq, np.float64) @ np.asarray(qd, np.float64))
+    return (np.abs(kd) @ u) * ks
+
+
+def _mut_abs_after_dot(qd, kd, wq, ks=None):
+    # |sum_d q k| instead of sum_d |q k|
+    b = np.abs(np.asarray(kd, np.float64) @ np.asarray(qd, np.float64).T) @ np.abs(wq)
+    return b * ks
+
+
+def test_score_bound_pins(e4m3_table):
+    for pin in _BOUND_PINS:
+        assert pin(check.bound_from_values, e4m3_table), pin.__name__
+
+
+def test_score_bound_wrapper_matches_its_definition(e4m3_table):
+    """score_bound(row t, ids) is bound_from_values on row t's decoded codes,
+    with w*q_scale and the keys' scales (and all-ones q_scale when None)."""
+    case = synth.random_case("pin_bound_wrap", 2, 700, seed=43, K=64, min_len=700)
+    ids = np.array([0, 5, 699, 350])
+    for qs in (case.q_scale, None):
+        B = check.score_bound(case.q8, qs, case.k8, case.k_scale, case.w, 1, ids, e4m3_table)
+        qsr = np.ones(64) if qs is None else qs[1].astype(np.float64)
+        want = [float(case.k_scale[s]) * sum(abs(float(case.w[1, j]) * qsr[j]) *
+                                             sum(abs(e4m3_table[case.q8[1, j, d]] * e4m3_table[case.k8[s, d]])
+                                                 for d in range(128)) for j in range(64)) for s in ids]
+        assert np.allclose(B, want, rtol=1e-12, atol=0)
+
+
+@pytest.mark.parametrize("mutant", [_mut_no_kscale, _mut_no_abs_codes, _mut_no_abs_weights,
+                                    _mut_heads_summed_first, _mut_abs_after_dot])
+def test_score_bound_mutants_fail_a_pin(mutant, e4m3_table):
+    assert not all(pin(mutant, e4m3_table) for pin in _BOUND_PINS), mutant.__name__
+
+
+def test_check_scores_cancellation_clause():
+    """Where I cancels to zero the relative clause cannot hold, so the bound
+    decides: an error of GAMMA*B/2 passes, 2*GAMMA*B fails; without a bound
+    both fail.  Where |I| is large the relative clause decides alone."""
+    g = check.GAMMA
+    I = np.array([0.0, 0.0, 1e-9])
+    B = np.array([10.0, 3.0, 7.0])
+    assert check.check_scores(I + 0.5 * g * B, I, bound=B) == 3
+    assert check.check_scores(I - 0.5 * g * B, I, bound=B) == 3
+    with pytest.raises(check.CheckError):
+        check.check_scores(I + 2.0 * g * B, I, bound=B)
+    with pytest.raises(check.CheckError):
+        check.check_scores(I + 0.5 * g * B, I)
+    big = np.array([100.0])
+    assert check.check_scores(big * (1 + 0.9 * check.REL_TOL), big, bound=np.array([1.0])) == 0
+    with pytest.raises(check.CheckError):
+        check.check_scores(big * (1 + 1.1 * check.REL_TOL), big, bound=np.array([1.0]))
