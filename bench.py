@@ -15,11 +15,20 @@ kernel; kernels and arguments are otherwise those of the plain entry points.
 
 Prints ONE JSON line.  The roofline object is for the dominant kernel:
 k_prefill_pair (bound by FP8 MFMA) for prefill, k_decode_score (bound by
-HBM) for decode.
+HBM) for decode.  For prefill it also carries the main kernel's mean shader
+clock, measured inside the kernel (shader-clock cycles over constant-rate
+wall-clock ticks of every wave), and the fraction of the peak at that clock;
+beside it, the Math-only control of "5.2 Exposed selection" (the main
+kernel's loads, MFMAs and scores with no sampling, filtering, selection or
+repair) gives the selection time the complete operator leaves exposed.  The
+short-context cases (prefill smoke, paged decode) are also timed cold: a
+512 MiB buffer is written between calls so that the 256 MB Infinity Cache
+holds none of the inputs.
 """
 from __future__ import annotations
 
 import argparse
+import ctypes
 import glob
 import hashlib
 import json
@@ -42,6 +51,7 @@ FP8_DENSE_PEAK_TFLOPS = 5000.0  # MI355X dense FP8 MFMA
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E
 METRIC = "fused score+top-2048 Gqk-pairs/s and % FP8 MFMA peak at 128K ctx, 1 MI355X"
 PREFILL = ["long_prefill", "prefill_chunk", "prefill_smoke", "adversarial"]
+COLD = ["prefill_smoke", "paged_decode"]  # short-context cases: also timed with cold caches
 DECODE = ["paged_decode"]
 SCAN = ["bf16_scan"]
 SCAN_METRIC = "BF16 stream scan + exact top-2048, GB/s of keys, 32 streams x 262144 keys, 1 MI355X"
@@ -49,6 +59,53 @@ SCAN_METRIC = "BF16 stream scan + exact top-2048, GB/s of keys, 32 streams x 262
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+NOMINAL_CLOCK_GHZ = 2.4  # the clock the FP8 peak is quoted at
+
+
+def wall_clock_khz() -> int:
+    """Rate of the constant wall clock the kernels read (hipDeviceAttributeWallClockRate)."""
+    hip = ctypes.CDLL("libamdhip64.so")
+    v = ctypes.c_int(0)
+    if hip.hipDeviceGetAttribute(ctypes.byref(v), 10017, torch.cuda.current_device()) != 0 or v.value <= 0:
+        raise RuntimeError("hipDeviceGetAttribute(WallClockRate) failed")
+    return v.value
+
+
+class CacheFlush:
+    """Writes a 512 MiB buffer: afterwards the 256 MB Infinity Cache and the
+    L2s hold none of a call's inputs."""
+
+    def __init__(self):
+        self.buf = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        self.n = 0
+
+    def __call__(self):
+        self.n += 1
+        self.buf.fill_(self.n & 0xFF)
+
+
+def timed_cold(step, steps: int):
+    """Each call alone after a cache flush: (mean call ms, mean dominant-kernel
+    ms), both from events on the call's stream."""
+    flush = CacheFlush()
+    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))]
+           for _ in range(steps)]
+    calls = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for e in evs:  # torch creates the HIP events on first record; the library records them again
+        for e0, e1 in e:
+            e0.record()
+            e1.record()
+    for i in range(steps):
+        flush()
+        calls[i][0].record()
+        step(evs[i], 1)
+        calls[i][1].record()
+    torch.cuda.synchronize()
+    call_ms = [a.elapsed_time(b) for a, b in calls]
+    kern_ms = [e[0][0].elapsed_time(e[0][1]) for e in evs]
+    return float(np.mean(call_ms)), float(np.mean(kern_ms))
 
 
 def tensor(a):
@@ -221,8 +278,33 @@ def bench_prefill(args, lib):
     ms_per_step, main_avg, main_min = timed(with_graph(args, lib, step), n_calls, args.steps, args.warmup)
     log("workload", args.workload, "pairs", pairs, "ms/step %.4f" % ms_per_step,
         "main kernel ms/launch %.4f (min %.4f)" % (main_avg, main_min))
+    subcalls = []
     for c, ws in zip(cases, wss):
-        log("  ", c.name, lib.read_stats(ws))
+        st = lib.read_stats(ws)
+        log("  ", c.name, st)
+        subcalls.append(dict(name=c.name, keys=c.N, pairs=c.pairs, **st))
+
+    # mean shader clock of the main kernel, read inside it (untimed pass)
+    clk = torch.zeros(2, dtype=torch.int64, device="cuda")
+    for j, (c, d) in enumerate(zip(cases, devs)):
+        for _ in range(args.steps):
+            lib.prefill_debug(d["q8"], d["q_scale"], d["k8"], d["k_scale"], d["w"], d["row_start"],
+                              d["row_end"], c.K, out=outs[j], workspace=wss[j], clock_out=clk)
+    torch.cuda.synchronize()
+    cycles, ticks = (int(x) for x in clk.cpu().tolist())
+    clock_ghz = cycles / ticks * wall_clock_khz() * 1e-6 if ticks > 0 else None
+    log("main kernel mean shader clock %.3f GHz" % clock_ghz if clock_ghz else "no clock reading")
+
+    # the Math-only control of the main kernel (no sampling, filter, selection or repair)
+    def step_control(step_evs, reps):
+        for j, (c, d) in enumerate(zip(cases, devs)):
+            lib.prefill_debug(d["q8"], d["q_scale"], d["k8"], d["k_scale"], d["w"], d["row_start"],
+                              d["row_end"], c.K, out=outs[j], workspace=wss[j], math_only=True,
+                              main_events=None if step_evs is None else step_evs[j], main_reps=reps)
+
+    ms_control, control_avg, _ = timed(step_control, n_calls, args.steps, args.warmup)
+    log("control (Math-only) ms/step %.4f, exposed selection %.2f%%"
+        % (ms_control, 100.0 * (ms_per_step - ms_control) / ms_per_step))
     achieved = FLOP_PER_PAIR * (pairs / n_calls) / (main_avg * 1e-3) / 1e12
     config = {"workload": cases[0].name if n_calls == 1 else args.workload,
               "rows": sum(c.Q for c in cases), "keys": max(c.N for c in cases), "heads": 64,
@@ -231,14 +313,36 @@ def bench_prefill(args, lib):
     roofline = {"bound": "mfma", "achieved": achieved, "peak": FP8_DENSE_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": achieved / FP8_DENSE_PEAK_TFLOPS,
                 "traffic": stored_traffic("k_prefill_pair", args.workload) if n_calls == 1 else None,
-                "kernel": "k_prefill_pair", "ms_per_launch": main_avg}
+                "kernel": "k_prefill_pair", "ms_per_launch": main_avg,
+                "clock_ghz": clock_ghz,
+                "frac_at_clock": (achieved / (FP8_DENSE_PEAK_TFLOPS * clock_ghz / NOMINAL_CLOCK_GHZ)
+                                  if clock_ghz else None)}
     res = result(args, pairs / (ms_per_step * 1e-3) / 1e9, ms_per_step, config, roofline,
                  "fp8_e4m3 x fp8_e4m3 -> f32")
     res["pct_fp8_peak"] = (100.0 * pairs * FLOP_PER_PAIR / (ms_per_step * 1e-3) / 1e12
                            / FP8_DENSE_PEAK_TFLOPS)
+    res["exposed_selection"] = {"control_ms_per_step": ms_control, "complete_ms_per_step": ms_per_step,
+                                "control_main_ms_per_launch": control_avg,
+                                "frac": (ms_per_step - ms_control) / ms_per_step}
+    if n_calls > 1:
+        res["subcalls"] = subcalls
+    if args.workload in COLD:
+        cold_ms, cold_main = timed_cold(step, args.steps)
+        log("cold (512 MiB written between calls): call %.4f ms, main kernel %.4f ms" % (cold_ms, cold_main))
+        res["cold"] = {"ms_per_call": cold_ms, "main_ms_per_launch": cold_main,
+                       "main_hbm_gbs": prefill_bytes(cases[0]) / (cold_main * 1e-3) / 1e9,
+                       "warm_main_hbm_gbs": prefill_bytes(cases[0]) / (main_avg * 1e-3) / 1e9}
     if args.cpu_seconds > 0:
         res["cpu_baseline"] = cpu_baseline_prefill(cases[0], args.cpu_seconds)
     return res
+
+
+def prefill_bytes(case) -> int:
+    """Algorithmic HBM bytes of one prefill call: q (8 KiB), w and q_scale
+    (512 B) and the output (4 B x K) per row; codes and scale of every key
+    in the rows' union range once (132 B)."""
+    lo, hi = int(case.row_start.min()), int(case.row_end.max())
+    return int(case.Q * (64 * 128 + 2 * 64 * 4 + 4 * case.K + 8) + (hi - lo) * 132)
 
 
 def bench_unfused(args, lib):
@@ -438,6 +542,11 @@ def bench_decode(args, lib):
                 "algorithmic_bytes": nbytes}
     res = result(args, case.pairs / (ms_per_step * 1e-3) / 1e9, ms_per_step, config, roofline,
                  "fp8_e4m3 x fp8_e4m3 -> f32")
+    cold_ms, cold_main = timed_cold(step, args.steps)
+    log("cold (512 MiB written between calls): call %.4f ms, scoring kernel %.4f ms" % (cold_ms, cold_main))
+    res["cold"] = {"ms_per_call": cold_ms, "main_ms_per_launch": cold_main,
+                   "main_hbm_gbs": nbytes / (cold_main * 1e-3) / 1e9,
+                   "warm_main_hbm_gbs": achieved, "pairs_per_s_cold": case.pairs / (cold_ms * 1e-3)}
     if args.cpu_seconds > 0:
         res["cpu_baseline"] = cpu_baseline_decode(case, args.cpu_seconds)
     return res
@@ -449,7 +558,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="long_prefill", choices=PREFILL + DECODE + SCAN)
-    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+    ap.add_argument("--cpu-seconds", type=float, default=30.0,
                     help="oracle sample budget in seconds (0: skip the CPU baseline)")
     ap.add_argument("--unfused", action="store_true",
                     help="time the unfused comparator (score matrix, then top-K) on a prefill "

@@ -103,7 +103,30 @@ typedef struct {
                           first launch and ev_main_stop with the last, so that a
                           small kernel's average duration is not dominated by
                           one dispatch (timing only; at most 1000)              */
+  int32_t *row_status; /* prefill: [Q] int32 device array or NULL; receives each
+                          row's outcome: IDX_ROW_FAST (certified by the fast
+                          path), IDX_ROW_UNDERFLOW or IDX_ROW_OVERFLOW (the
+                          certificate failed and the row was recomputed by the
+                          exact repair path), IDX_ROW_BAD (invalid range)      */
+  uint64_t *clock_out; /* prefill: [2] uint64 device array or NULL; the main
+                          scoring kernel adds, over all its workgroups, the
+                          shader-clock cycles ([0]) and the constant-rate
+                          wall-clock ticks ([1]) each workgroup ran for, so that
+                          [0]/[1] times the wall-clock rate is the kernel's mean
+                          shader clock.  The caller zeroes it before the call.  */
+  int32_t math_only;   /* prefill, 1: control build of the main kernel (timing
+                          only): the same key loads, MFMAs and head-weighted
+                          scores, folded into a per-row checksum instead of
+                          being filtered; no candidates, no selection, no
+                          repair.  out_idx, scores_out and tau_out are not
+                          written.  Needs force_tau = 0.                       */
 } idx_topk_opts;
+
+/* Row outcomes written to idx_topk_opts.row_status. */
+#define IDX_ROW_FAST 0
+#define IDX_ROW_UNDERFLOW 1
+#define IDX_ROW_OVERFLOW 2
+#define IDX_ROW_BAD (-1)
 
 /* Bytes of workspace idx_topk_prefill needs for Q rows over N keys. */
 size_t idx_topk_prefill_workspace(int32_t Q, int32_t N, int32_t K);
@@ -257,17 +280,24 @@ int idx_topk_decode_paged(const uint8_t *q, const float *q_scale, const uint8_t 
                           void *workspace, size_t workspace_bytes, void *stream);
 
 /*
- * Same as idx_topk_decode_paged, plus timing: opts (NULL = none) may carry
- * ev_main_start/ev_main_stop, recorded by the launch of the split scoring
- * kernel at its start and at its end.  The decode path has no threshold and no capacity
- * knobs: opts with force_tau, lds_cap or spill_cap set gives IDX_EINVAL.
+ * Same as idx_topk_decode_paged, plus diagnostics for tests:
+ *   scores_out [B][max_pages*page_size] float device array or NULL: for every
+ *              sequence that was scored (K < seq_len, valid length
+ *              and page ids) the FP32 score of logical position i at
+ *              [b][i] for i < seq_len, exactly the values its selection read;
+ *              other entries are unspecified.
+ *   opts       NULL or timing only: ev_main_start/ev_main_stop are recorded by
+ *              the launch of the split scoring kernel at its start and at its
+ *              end, main_reps repeats it.  The decode path has no threshold
+ *              and no capacity knobs: opts with force_tau, lds_cap, spill_cap,
+ *              row_status, clock_out or math_only set gives IDX_EINVAL.
  */
 int idx_topk_decode_paged_debug(const uint8_t *q, const float *q_scale, const uint8_t *k_cache,
                                 const float *k_scale, const float *w, const int32_t *page_table,
                                 const int32_t *seq_lens, int32_t B, int32_t max_pages,
                                 int32_t page_size, int32_t num_pages, int32_t K, int32_t *out_idx,
                                 void *workspace, size_t workspace_bytes, void *stream,
-                                const idx_topk_opts *opts);
+                                float *scores_out, const idx_topk_opts *opts);
 
 /* Copy the counters of the last call that used `workspace` into *out.
  * Synchronises `stream`.  For tests and diagnosis, not for hot loops. */

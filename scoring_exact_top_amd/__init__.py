@@ -36,7 +36,12 @@ class Opts(ctypes.Structure):
     _fields_ = [("force_tau", ctypes.c_int32), ("tau_value", ctypes.c_float),
                 ("lds_cap", ctypes.c_int32), ("spill_cap", ctypes.c_int32),
                 ("ev_main_start", ctypes.c_void_p), ("ev_main_stop", ctypes.c_void_p),
-                ("main_reps", ctypes.c_int32)]
+                ("main_reps", ctypes.c_int32), ("row_status", ctypes.c_void_p),
+                ("clock_out", ctypes.c_void_p), ("math_only", ctypes.c_int32)]
+
+
+# Row outcomes written to row_status (idx_topk.h IDX_ROW_*).
+ROW_FAST, ROW_UNDERFLOW, ROW_OVERFLOW, ROW_BAD = 0, 1, 2, -1
 
 
 class Stats(ctypes.Structure):
@@ -77,7 +82,7 @@ _lib.idx_topk_decode_paged.restype = ctypes.c_int
 _lib.idx_topk_decode_paged.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
                                        _i32, _vp, _vp, _sz, _vp]
 _lib.idx_topk_decode_paged_debug.restype = ctypes.c_int
-_lib.idx_topk_decode_paged_debug.argtypes = _lib.idx_topk_decode_paged.argtypes + [ctypes.POINTER(Opts)]
+_lib.idx_topk_decode_paged_debug.argtypes = _lib.idx_topk_decode_paged.argtypes + [_vp, ctypes.POINTER(Opts)]
 _lib.idx_topk_read_stats.restype = ctypes.c_int
 _lib.idx_topk_read_stats.argtypes = [_vp, ctypes.POINTER(Stats), _vp]
 _lib.idx_topk_strerror.restype = ctypes.c_char_p
@@ -156,17 +161,23 @@ def prefill(q8, q_scale, k8, k_scale, w, row_start, row_end, K: int, out=None, w
 def prefill_debug(q8, q_scale, k8, k_scale, w, row_start, row_end, K: int, out=None,
                   workspace=None, stream=None, scores_out=None, tau_out=None,
                   force_tau: Optional[float] = None, lds_cap: int = 0, spill_cap: int = 0,
-                  main_events=None, main_reps: int = 1):
+                  main_events=None, main_reps: int = 1, row_status=None, clock_out=None,
+                  math_only: bool = False):
     """idx_topk_prefill_debug: also emits FP32 scores [Q,N] and thresholds [Q].
 
     main_events: optional (start, stop) pair of torch.cuda.Event(enable_timing=True)
     recorded around the fused main kernel; main_reps > 1 launches that kernel
-    so many times back to back inside the pair (timing only)."""
+    so many times back to back inside the pair (timing only).  row_status [Q]
+    int32 receives each row's ROW_* outcome; clock_out [2] int64 (zeroed by
+    the caller) accumulates the main kernel's shader-clock cycles and
+    wall-clock ticks; math_only runs the control build of the main kernel
+    (no selection, out is not written)."""
     ev0 = ev1 = None
     if main_events is not None:
         ev0, ev1 = (ctypes.c_void_p(e.cuda_event) for e in main_events)
     opts = Opts(1 if force_tau is not None else 0, float(force_tau or 0.0), int(lds_cap),
-                int(spill_cap), ev0, ev1, int(main_reps))
+                int(spill_cap), ev0, ev1, int(main_reps), _ptr(row_status, torch.int32),
+                _ptr(clock_out, torch.int64), 1 if math_only else 0)
     return _prefill(q8, q_scale, k8, k_scale, w, row_start, row_end, K, out, workspace, stream,
                     debug=True, scores_out=scores_out, tau_out=tau_out, opts=opts)
 
@@ -337,15 +348,16 @@ def stream_floor(src: torch.Tensor, out=None, stream=None):
 
 def decode_paged(q8, q_scale, k_cache, k_scale, w, page_table, seq_lens, K: int, out=None,
                  workspace=None, stream=None, force_tau: Optional[float] = None, main_events=None,
-                 main_reps: int = 1):
+                 main_reps: int = 1, scores_out=None):
     """Top-K physical cache slots per sequence; see idx_topk_decode_paged.
 
     q8 [B,64,128], q_scale [B,64] or None, k_cache [P,64,128], k_scale [P,64],
     w [B,64], page_table [B,max_pages] int32, seq_lens [B] int32 (device).
     main_events selects idx_topk_decode_paged_debug with a (start, stop)
-    torch.cuda.Event pair around the scoring kernel; force_tau is passed
-    through so that the library's rejection of it (decode has no threshold)
-    can be tested.
+    torch.cuda.Event pair around the scoring kernel; scores_out
+    [B, max_pages*64] f32 (debug entry too) receives the scores the
+    selection read; force_tau is passed through so that the library's
+    rejection of it (decode has no threshold) can be tested.
     """
     q8, k_cache = _q_k(q8, k_cache)
     B = int(q8.shape[0])
@@ -360,7 +372,7 @@ def decode_paged(q8, q_scale, k_cache, k_scale, w, page_table, seq_lens, K: int,
             _ptr(k_scale, torch.float32), _ptr(w, torch.float32), _ptr(page_table, torch.int32),
             _ptr(seq_lens, torch.int32), B, max_pages, page, P, int(K), _ptr(out, torch.int32),
             _ptr(workspace), int(workspace.numel()), _stream(stream)]
-    if force_tau is None and main_events is None and main_reps == 1:
+    if force_tau is None and main_events is None and main_reps == 1 and scores_out is None:
         _check(_lib.idx_topk_decode_paged(*args))
     else:
         ev0 = ev1 = None
@@ -368,7 +380,7 @@ def decode_paged(q8, q_scale, k_cache, k_scale, w, page_table, seq_lens, K: int,
             ev0, ev1 = (ctypes.c_void_p(e.cuda_event) for e in main_events)
         opts = Opts(1 if force_tau is not None else 0, float(force_tau or 0.0), 0, 0, ev0, ev1,
                     int(main_reps))
-        _check(_lib.idx_topk_decode_paged_debug(*args, ctypes.byref(opts)))
+        _check(_lib.idx_topk_decode_paged_debug(*args, _ptr(scores_out, torch.float32), ctypes.byref(opts)))
     return out
 
 

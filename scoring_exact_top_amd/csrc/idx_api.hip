@@ -92,6 +92,10 @@ static int prefill_common(const uint8_t* q, const float* q_scale, const uint8_t*
     A.ev_main_stop = static_cast<hipEvent_t>(opts->ev_main_stop);
     if (opts->main_reps < 0 || opts->main_reps > 1000) return IDX_EINVAL;
     A.main_reps = opts->main_reps;
+    if (opts->math_only && (opts->force_tau || unfused)) return IDX_EINVAL;
+    A.row_status = opts->row_status;
+    A.clock = opts->clock_out;
+    A.math_only = opts->math_only ? 1 : 0;
   }
   A.cap_total = A.lds_cap + A.spill_cap;
   // usable entries per segment: the full segment unless a test knob shrank
@@ -108,10 +112,10 @@ static int prefill_common(const uint8_t* q, const float* q_scale, const uint8_t*
   // N <= kCandCap with the default capacities: every valid row has L <=
   // kCandCap, so its threshold is -inf, no segment overflows and the
   // certificate cannot fail (no sampling, no repair to launch)
-  A.keep_all = (!A.force_tau && A.N > 0 && A.N <= kCandCap && A.cap_total >= kCandCap) ? 1 : 0;
+  A.keep_all = (!A.force_tau && !A.math_only && A.N > 0 && A.N <= kCandCap && A.cap_total >= kCandCap) ? 1 : 0;
   // the main kernel samples its rows itself (with S > 1 splits per row pair,
   // each split samples the pair: the same values, S times, in parallel)
-  A.fuse_tau = (!A.force_tau && !A.keep_all && A.N > 0) ? 1 : 0;
+  A.fuse_tau = (!A.force_tau && !A.keep_all && !A.math_only && A.N > 0) ? 1 : 0;
   int rc = launch_prefill(A, s);
   if (rc == IDX_OK && tau_out) {
     if (hipMemcpyAsync(tau_out, A.tau, sizeof(float) * (size_t)Q, hipMemcpyDeviceToDevice, s) != hipSuccess)
@@ -157,7 +161,9 @@ extern "C" int idx_topk_prefill_unfused(const uint8_t* q, const float* q_scale, 
                                         const int32_t* row_end, int32_t K, int32_t* out_idx, int32_t Q,
                                         int32_t N, void* workspace, size_t workspace_bytes, void* stream,
                                         const idx_topk_opts* opts) {
-  if (opts && (opts->force_tau || opts->lds_cap || opts->spill_cap)) return IDX_EINVAL;
+  if (opts && (opts->force_tau || opts->lds_cap || opts->spill_cap || opts->row_status || opts->clock_out ||
+               opts->math_only))
+    return IDX_EINVAL;
   return prefill_common(q, q_scale, k, k_scale, w, row_start, row_end, K, out_idx, Q, N, workspace,
                         workspace_bytes, stream, nullptr, nullptr, opts, true);
 }
@@ -211,9 +217,10 @@ extern "C" int idx_topk_decode_paged_debug(const uint8_t* q, const float* q_scal
                                            const int32_t* seq_lens, int32_t B, int32_t max_pages,
                                            int32_t page_size, int32_t num_pages, int32_t K, int32_t* out_idx,
                                            void* workspace, size_t workspace_bytes, void* stream,
-                                           const idx_topk_opts* opts) {
+                                           float* scores_out, const idx_topk_opts* opts) {
   return decode_paged(q, q_scale, k_cache, k_scale, w, page_table, seq_lens, B, max_pages, page_size,
-                      num_pages, K, out_idx, workspace, workspace_bytes, static_cast<hipStream_t>(stream), opts);
+                      num_pages, K, out_idx, workspace, workspace_bytes, static_cast<hipStream_t>(stream), opts,
+                      scores_out);
 }
 
 extern "C" int idx_topk_read_stats(const void* workspace, idx_topk_stats* out, void* stream) {

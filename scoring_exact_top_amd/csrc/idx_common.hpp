@@ -408,7 +408,14 @@ __device__ __forceinline__ int relaid_src_offset(int tile, int blk, int l) {
   return ((tile << 6) + sub_off(c) + (l & 15)) * kD + 32 * (l >> 4) + 16 * h;
 }
 
-// Load relaid tile `tile` (wave-uniform); scales from the original array.
+// Tile index used for a refill of tile `tile` (scalar) of `ntiles` >= 1: a
+// refill past the last tile, whose data is never scored, reloads the last
+// tile instead, so every load's address stays inside the buffers and every
+// offset fits in 31 bits.
+__device__ __forceinline__ int refill_tile(int tile, int ntiles) { return tile < ntiles ? tile : ntiles - 1; }
+
+// Load relaid tile `tile` (wave-uniform, 0 <= tile < ntiles); scales from
+// the original array.
 __device__ __forceinline__ void load_tile_relaid(KeyTile& t, rsrc_t kt, rsrc_t ks, int tile, uint32_t lane) {
   const int soff = tile * (kTile * kD);
 #pragma unroll

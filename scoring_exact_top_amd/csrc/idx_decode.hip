@@ -240,12 +240,15 @@ size_t decode_workspace_bytes(int32_t B, int32_t max_pages, int32_t page_size, i
 int decode_paged(const uint8_t* q, const float* q_scale, const uint8_t* k_cache, const float* k_scale,
                  const float* w, const int32_t* page_table, const int32_t* seq_lens, int32_t B,
                  int32_t max_pages, int32_t page_size, int32_t num_pages, int32_t K, int32_t* out_idx,
-                 void* workspace, size_t workspace_bytes, hipStream_t stream, const idx_topk_opts* opts) {
+                 void* workspace, size_t workspace_bytes, hipStream_t stream, const idx_topk_opts* opts,
+                 float* scores_out) {
   if (B < 0 || max_pages < 0 || num_pages < 0 || K < 1 || K > kKmax) return IDX_EINVAL;
   if (page_size != 64 || B > kMaxGridY) return IDX_EUNSUPPORTED;
   // slots and logical positions are int32; the cache itself may be of any size
   if ((int64_t)max_pages * 64 * 4 > 0x7fffffffLL || (int64_t)num_pages * 64 > 0x7fffffffLL) return IDX_EINVAL;
-  if (opts && (opts->force_tau || opts->lds_cap || opts->spill_cap)) return IDX_EINVAL;
+  if (opts && (opts->force_tau || opts->lds_cap || opts->spill_cap || opts->row_status || opts->clock_out ||
+               opts->math_only))
+    return IDX_EINVAL;
   if (opts && (opts->main_reps < 0 || opts->main_reps > 1000)) return IDX_EINVAL;
   if (B == 0) return IDX_OK;
   if (!q || !w || !page_table || !seq_lens || !out_idx) return IDX_EINVAL;
@@ -283,7 +286,13 @@ int decode_paged(const uint8_t* q, const float* q_scale, const uint8_t* k_cache,
              reinterpret_cast<uint32_t*>(ws + L.gkey), reinterpret_cast<int32_t*>(ws + L.gid),
              reinterpret_cast<uint32_t*>(ws + L.gcnt), kDecGatherKeys / decode_gather_split(B),
              decode_gather_split(B)};
-  return launch_topk_rows_gathered(R, stream);
+  int rc = launch_topk_rows_gathered(R, stream);
+  // the debug path hands out the score rows the selection read
+  if (rc == IDX_OK && scores_out &&
+      hipMemcpyAsync(scores_out, A.scores, sizeof(float) * (size_t)B * (size_t)max_pages * 64,
+                     hipMemcpyDeviceToDevice, stream) != hipSuccess)
+    rc = IDX_EHIP;
+  return rc;
 }
 
 }  // namespace idxk

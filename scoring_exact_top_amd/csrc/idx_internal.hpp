@@ -135,6 +135,9 @@ struct PrefillArgs {
   int32_t rslots;
   int64_t rstride;
   float* dbg_scores;    // [Q][N] or null
+  int32_t* row_status;  // [Q] or null: IDX_ROW_* outcome of each row
+  uint64_t* clock;      // [2] or null: summed shader-clock cycles and wall-clock ticks of the main kernel's waves
+  int32_t math_only;    // control build: scores folded into checksums, no filter and no selection
   int32_t force_tau;
   int32_t keep_all;  // every valid row keeps all its keys (N <= kCandCap): no sampler, no repair
   int32_t fuse_tau;  // one split: the main kernel takes its rows' thresholds itself

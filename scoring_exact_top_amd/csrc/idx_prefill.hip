@@ -78,8 +78,13 @@ __global__ __launch_bounds__(kWG) void k_prefill_tau(PrefillArgs A) {
 //
 // MODE kPairFused is that fused pass; kPairDebug also writes every valid
 // score to dbg_scores [Q][N]; kPairDense only writes the scores (no filter,
-// no candidates): the scoring stage of the unfused comparator.
-constexpr int kPairFused = 0, kPairDebug = 1, kPairDense = 2;
+// no candidates): the scoring stage of the unfused comparator.  kPairControl
+// is the Math-only control of "5.2 Exposed selection" (Fusing Indexer
+// Scoring and Exact Top-k page): the same loads, MFMAs and scores, folded
+// into one checksum per (row, wave) instead of being sampled, filtered and
+// appended; with no selection or repair after it, the complete operator's
+// time minus this kernel's is the selection work left exposed.
+constexpr int kPairFused = 0, kPairDebug = 1, kPairDense = 2, kPairControl = 3;
 
 // Head-weighted sum of one row's 16 heads held by this lane plus its two
 // u-block rows (ua, ub), in a fixed order (18 FMAs).
@@ -120,6 +125,13 @@ __device__ __forceinline__ void pair_scores(const QOp2& qo, const KeyTile& kt, f
 template <int MODE>
 __global__ __launch_bounds__(kWG, 2) void k_prefill_pair(PrefillArgs A) {
   __shared__ uint8_t s_qprep[kWaves][2 * kUTerms * kD];
+  // optional clock probe: this wave's shader-clock cycles and constant-rate
+  // wall-clock ticks from its start to its end, summed over all waves
+  uint64_t clk0 = 0, rtc0 = 0;
+  if (A.clock) {
+    clk0 = __builtin_amdgcn_s_memtime();
+    rtc0 = __builtin_amdgcn_s_memrealtime();
+  }
   const int tid = threadIdx.x;
   const uint32_t lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -154,7 +166,7 @@ __global__ __launch_bounds__(kWG, 2) void k_prefill_pair(PrefillArgs A) {
   // score the sampled keys' tiles (once for both rows when they share the
   // sample positions, as causal rows do) with the walk's arithmetic, so a
   // threshold is one of the walk's scores; wave r then selects row r's.
-  if constexpr (MODE != kPairDense) {
+  if constexpr (MODE != kPairDense && MODE != kPairControl) {
     if (A.fuse_tau) {
       __shared__ uint32_t s_samp[2][kMaxSamples];
       __shared__ uint32_t s_hist[2][256];
@@ -207,6 +219,7 @@ __global__ __launch_bounds__(kWG, 2) void k_prefill_pair(PrefillArgs A) {
   const int tile_hi = (hi + 63) >> 6;
   const int voff = (int)lane * 16;
   uint32_t cnt[2] = {0u, 0u};  // candidates of each row found by this wave
+  float csum[2] = {0.f, 0.f};  // control build: running sums of the rows' valid scores
   float dmax[2] = {-INFINITY, -INFINITY};  // per lane: largest candidate dropped for lack of room
   int fdrop[2] = {0x7FFFFFFF, 0x7FFFFFFF};  // position of the segment's first dropped candidate
   // the (row, wave) workspace segments as buffer resources: a store past
@@ -242,8 +255,12 @@ __global__ __launch_bounds__(kWG, 2) void k_prefill_pair(PrefillArgs A) {
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
       const bool valid = my >= rs[r] && my < re[r];
-      if (MODE != kPairFused && valid) A.dbg_scores[(int64_t)(t0 + r) * A.N + my] = sc[r];
+      if ((MODE == kPairDebug || MODE == kPairDense) && valid) A.dbg_scores[(int64_t)(t0 + r) * A.N + my] = sc[r];
       if (MODE == kPairDense) continue;
+      if (MODE == kPairControl) {
+        csum[r] += valid ? sc[r] : 0.f;
+        continue;
+      }
       const bool take = valid && sc[r] >= tr[r];
       const uint64_t ball = __ballot(take);
       const uint32_t n = (uint32_t)__popcll(ball);
@@ -281,7 +298,8 @@ __global__ __launch_bounds__(kWG, 2) void k_prefill_pair(PrefillArgs A) {
   v8i kb[4];
   float ks_cur = 0.f;
   auto tile_body = [&](int T) {
-    const int ntoff = (T + nseg) * (kTile * kD);
+    const int nT = refill_tile(T + nseg, ntiles);  // the tile refilled into kb
+    const int ntoff = nT * (kTile * kD);
     __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
@@ -319,13 +337,13 @@ __global__ __launch_bounds__(kWG, 2) void k_prefill_pair(PrefillArgs A) {
     // tail just read: a load whose result were copied at the loop's back edge
     // would make that edge wait for every load issued before it (the memory
     // counter retires in order), that is for the whole next tile's keys.
-    ks_cur = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(kbuf.ks, (int)lane * 4, ntoff / kD * 4, 0));
+    ks_cur = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(kbuf.ks, (int)lane * 4, nT * 256, 0));
   };
   if (lo < hi) {
     int T = (lo >> 6) + seg;
     {
       KeyTile t;
-      load_tile_relaid(t, ktb, kbuf.ks, T, lane);
+      load_tile_relaid(t, ktb, kbuf.ks, refill_tile(T, ntiles), lane);  // past the last tile: the loop is empty
 #pragma unroll
       for (int c = 0; c < 4; ++c) kb[c] = t.kb[c];
       ks_cur = t.ks;
@@ -335,23 +353,38 @@ __global__ __launch_bounds__(kWG, 2) void k_prefill_pair(PrefillArgs A) {
     for (; T < tile_hi; T += nseg) tile_body(T);
   }
 
-  if (MODE == kPairDense) return;
-  // publish this wave's segment: entries stored, the order-preserving key of
-  // the largest dropped candidate (0: none dropped; a candidate is never
-  // NaN, so its key is nonzero) and the position of the first dropped one
-  // (candidates arrive in position order, so every later one was dropped)
+  if constexpr (MODE == kPairControl) {
+    // the checksums go to the unused fourth word of the segment records
 #pragma unroll
-  for (int r = 0; r < 2; ++r) {
-    uint32_t dk = 0u;
-    if (cnt[r] > seg_cap) {
-      float m = dmax[r];
+    for (int r = 0; r < 2; ++r) {
+      float m = csum[r];
 #pragma unroll
-      for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
-      dk = f2key(m);
+      for (int o = 32; o > 0; o >>= 1) m += __shfl_xor(m, o, 64);
+      if (lane == 0 && t0 + r < A.Q) A.segn[4 * ((int64_t)(t0 + r) * nseg + seg) + 3] = __float_as_uint(m);
     }
-    if (lane == 0 && t0 + r < A.Q)
-      *reinterpret_cast<uint4*>(A.segn + 4 * ((int64_t)(t0 + r) * nseg + seg)) =
-          make_uint4(min(cnt[r], seg_cap), dk, (uint32_t)fdrop[r], 0u);
+  } else if constexpr (MODE != kPairDense) {
+    // publish this wave's segment: entries stored, the order-preserving key of
+    // the largest dropped candidate (0: none dropped; a candidate is never
+    // NaN, so its key is nonzero) and the position of the first dropped one
+    // (candidates arrive in position order, so every later one was dropped)
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      uint32_t dk = 0u;
+      if (cnt[r] > seg_cap) {
+        float m = dmax[r];
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+        dk = f2key(m);
+      }
+      if (lane == 0 && t0 + r < A.Q)
+        *reinterpret_cast<uint4*>(A.segn + 4 * ((int64_t)(t0 + r) * nseg + seg)) =
+            make_uint4(min(cnt[r], seg_cap), dk, (uint32_t)fdrop[r], 0u);
+    }
+  }
+  if (A.clock && lane == 0) {
+    atomicAdd(reinterpret_cast<unsigned long long*>(A.clock), (unsigned long long)(__builtin_amdgcn_s_memtime() - clk0));
+    atomicAdd(reinterpret_cast<unsigned long long*>(A.clock + 1),
+              (unsigned long long)(__builtin_amdgcn_s_memrealtime() - rtc0));
   }
 }
 
@@ -380,7 +413,10 @@ __global__ __launch_bounds__(kWG) void k_prefill_select(PrefillArgs A) {
   const int rs_t = A.row_start[t], re_t = A.row_end[t];
   if (rs_t < 0 || rs_t > re_t || re_t > A.N) {
     for (int i = tid; i < A.K; i += kWG) out[i] = -1;
-    if (tid == 0) atomicAdd(&stats[kStBad], 1u);
+    if (tid == 0) {
+      atomicAdd(&stats[kStBad], 1u);
+      if (A.row_status) A.row_status[t] = IDX_ROW_BAD;
+    }
     return;
   }
   const int nseg = kWaves * A.S;
@@ -444,6 +480,7 @@ __global__ __launch_bounds__(kWG) void k_prefill_select(PrefillArgs A) {
     if (ok) emit_range_regs(key, id, lay, sel, idlo, kr, A.K, out, IdIdentity{}, sh, tid);
   }
   if (tid == 0) {
+    if (A.row_status) A.row_status[t] = ok ? IDX_ROW_FAST : drop ? IDX_ROW_OVERFLOW : IDX_ROW_UNDERFLOW;
     if (ok) {
       atomicAdd(&stats[kStFast], 1u);
       if (n > (uint32_t)A.lds_cap) atomicAdd(&stats[kStSpilled], 1u);
@@ -729,6 +766,18 @@ int launch_prefill(const PrefillArgs& A, hipStream_t stream) {
   if (A.Q == 0) return IDX_OK;
   const int64_t nchunks = (int64_t)((A.N + 63) >> 6) * 512;
   if (nchunks > 0) hipLaunchKernelGGL(k_relayout_keys, dim3((unsigned)(nchunks / kWG)), dim3(kWG), 0, stream, A);
+  if (A.math_only) {  // the control: the main kernel's scoring alone, nothing after it
+    const unsigned grid = (unsigned)((A.Q + 1) / 2 * A.S);
+    const int reps = A.main_reps > 1 ? A.main_reps : 1;
+    for (int r = 0; r < reps; ++r) {
+      hipEvent_t e0 = r == 0 ? A.ev_main_start : nullptr, e1 = r == reps - 1 ? A.ev_main_stop : nullptr;
+      if (e0 || e1)
+        hipExtLaunchKernelGGL(k_prefill_pair<kPairControl>, dim3(grid), dim3(kWG), 0, stream, e0, e1, 0, A);
+      else
+        hipLaunchKernelGGL(k_prefill_pair<kPairControl>, dim3(grid), dim3(kWG), 0, stream, A);
+    }
+    return hipGetLastError() == hipSuccess ? IDX_OK : IDX_EHIP;
+  }
   if (!A.keep_all && !A.fuse_tau) hipLaunchKernelGGL(k_prefill_tau, dim3(kRepairGrid), dim3(kWG), 0, stream, A);
   // the timing events, when given, are recorded by the launches themselves
   // (the first launch's start, the last launch's end; main_reps > 1 repeats

@@ -265,14 +265,17 @@ def long_prefill(seed: int = 0) -> PrefillCase:
 
 def adversarial(seed: int = 0) -> List[PrefillCase]:
     """2048 rows at the last positions of a 163840-token context, split into
-    three calls with their own key sets: 1024 rows over 16 distinct key
-    vectors (massive ties), 512 rows with an off-lattice x8 outlier block,
-    512 rows over plain N(0,1) keys."""
+    four calls with their own key sets: 1024 rows over 16 distinct key
+    vectors (massive ties), 256 rows with an off-lattice x8 outlier block of
+    3000 keys, 256 rows with x8 decoys on the sampling lattice (the sampled
+    threshold lands among them: too few candidates, exact repair), 512 rows
+    over plain N(0,1) keys."""
     N = 163840
     pos = np.arange(N - 2048, N, dtype=np.int64)
     return [
         causal_case("adversarial_ties16", 1024, N, seed * 16 + 1, "ties16", positions=pos[:1024]),
-        causal_case("adversarial_outlier", 512, N, seed * 16 + 2, "outlier", positions=pos[1024:1536]),
+        causal_case("adversarial_outlier", 256, N, seed * 16 + 2, "outlier", positions=pos[1024:1280]),
+        causal_case("adversarial_decoy", 256, N, seed * 16 + 4, "decoy", positions=pos[1280:1536]),
         causal_case("adversarial_normal", 512, N, seed * 16 + 3, "normal", positions=pos[1536:]),
     ]
 
@@ -282,6 +285,21 @@ def adversarial_decoy(seed: int = 0, Q: int = 256) -> PrefillCase:
     N = 163840
     pos = np.arange(N - Q, N, dtype=np.int64)
     return causal_case("adversarial_decoy", Q, N, seed * 16 + 4, "decoy", positions=pos)
+
+
+def random_codes_case(name: str, N: int, starts, ends, seed: int, K: int = 2048) -> PrefillCase:
+    """Rows over keys whose e4m3 codes are uniform random bytes (the two NaN
+    codes excluded) with per-key scales uniform in [1/896, 1/224): cheap to
+    make for very large N.  Queries and weights as in every other case."""
+    g = _gen(seed)
+    Q = len(starts)
+    q8, qs = _queries(g, Q)
+    w = _weights(g, Q)
+    rng = np.random.default_rng(seed)
+    k8 = rng.integers(0, 256, size=(N, D), dtype=np.uint8)
+    k8[(k8 & 0x7F) == 0x7F] ^= 0x01
+    ks = rng.uniform(1.0 / 896, 1.0 / 224, N).astype(np.float32)
+    return PrefillCase(name, q8, qs, k8, ks, w, np.asarray(starts, np.int32), np.asarray(ends, np.int32), K)
 
 
 def paged_decode_lens(seed: int = 0, B: int = 16) -> np.ndarray:

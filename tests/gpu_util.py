@@ -23,19 +23,23 @@ def dev_prefill(case, device="cuda"):
                 row_start=t(case.row_start), row_end=t(case.row_end))
 
 
-def run_prefill(case, debug=False, scores=False, **opts):
+def run_prefill(case, debug=False, scores=False, status=False, **opts):
     import scoring_exact_top_amd as lib
     d = dev_prefill(case)
     ws = lib.alloc_workspace(lib.prefill_workspace_bytes(case.Q, case.N, case.K), "cuda")
     res = {}
-    if debug or scores or opts:
+    if debug or scores or status or opts:
         sc = torch.full((case.Q, case.N), float("nan"), dtype=torch.float32, device="cuda") if scores else None
         tau = torch.empty(case.Q, dtype=torch.float32, device="cuda")
+        st = torch.full((case.Q,), -7, dtype=torch.int32, device="cuda") if status else None
         out = lib.prefill_debug(d["q8"], d["q_scale"], d["k8"], d["k_scale"], d["w"], d["row_start"],
-                                d["row_end"], case.K, workspace=ws, scores_out=sc, tau_out=tau, **opts)
+                                d["row_end"], case.K, workspace=ws, scores_out=sc, tau_out=tau,
+                                row_status=st, **opts)
         res["tau"] = tau.cpu().numpy()
         if scores:
             res["scores"] = sc.cpu().numpy()
+        if status:
+            res["status"] = st.cpu().numpy()
     else:
         out = lib.prefill(d["q8"], d["q_scale"], d["k8"], d["k_scale"], d["w"], d["row_start"],
                           d["row_end"], case.K, workspace=ws)
@@ -74,3 +78,29 @@ def sample_rows(Q, n, seed=0):
     base = {0, Q - 1, Q // 2}
     extra = rng.choice(Q, size=min(Q, n), replace=False).tolist()
     return np.array(sorted(base | set(extra)))[: max(n, 3)]
+
+
+def audit_rows(case, out, rows=None, batch=128, gpu_scores=None, e4m3=None):
+    """check_prefill_rows over the given rows (default: every row), in
+    batches so that the oracle's fp64 score rows stay a few hundred MB; the
+    oracle runs on all host threads."""
+    rows = np.arange(case.Q) if rows is None else np.asarray(rows)
+    tot = dict(rows=0, below_theta=0, cancel_only=0)
+    for i in range(0, rows.size, batch):
+        rep = check_prefill_rows(case, out, rows[i:i + batch], gpu_scores=gpu_scores, e4m3=e4m3)
+        for k in tot:
+            tot[k] += rep[k]
+    return tot
+
+
+def status_matches_stats(status, stats):
+    """Per-row outcomes agree with the call's counters."""
+    import scoring_exact_top_amd as lib
+    n_fast = int(np.sum(status == lib.ROW_FAST))
+    n_under = int(np.sum(status == lib.ROW_UNDERFLOW))
+    n_over = int(np.sum(status == lib.ROW_OVERFLOW))
+    n_bad = int(np.sum(status == lib.ROW_BAD))
+    assert n_fast + n_under + n_over + n_bad == status.size, "rows without an outcome"
+    assert (n_fast, n_under, n_over, n_bad) == (stats["fast_ok"], stats["underflow"], stats["overflow"],
+                                                stats["bad_rows"]), (n_fast, n_under, n_over, n_bad, stats)
+    assert stats["repaired"] == n_under + n_over, stats

@@ -149,3 +149,50 @@ def test_scan_argument_errors(lib):
     assert g(good, -1, good, None) == -1
     assert g(vp((1 << 20) + 4), 10, good, None) == -1
     assert g(good, 0, good, None) == 0
+
+
+def test_key_count_limit_is_exact(lib):
+    """The largest accepted N is the one whose relaid tiles plus one tile of
+    slack stay below 2^31 bytes: (N + 64) * 128 <= 2^31 - 1.  N at the limit
+    passes the geometry check (and fails on the missing workspace next), one
+    more is unsupported."""
+    vp = ctypes.c_void_p
+    f = lib.idx_topk_prefill
+    f.restype = ctypes.c_int
+    f.argtypes = [vp] * 7 + [ctypes.c_int32, vp, ctypes.c_int32, ctypes.c_int32, vp, ctypes.c_size_t, vp]
+    good = vp(1 << 20)
+    n_max = (2 ** 31 - 1) // 128 - 64
+    assert n_max == 16777151
+    call = lambda N: f(good, None, good, good, good, good, good, 2048, good, 4, N, None, 0, None)
+    assert call(n_max) == -3
+    assert call(n_max + 1) == -2
+
+
+def test_debug_knobs_are_rejected_where_they_do_not_apply(lib):
+    """row_status, clock_out and math_only belong to the fused prefill: the
+    unfused comparator and paged decode reject them; math_only with a forced
+    threshold is rejected too.  All answered before any device work."""
+    import scoring_exact_top_amd as st
+    vp = ctypes.c_void_p
+    good, ws, big = vp(1 << 20), vp(1 << 30), 1 << 40
+    u = lib.idx_topk_prefill_unfused
+    u.restype = ctypes.c_int
+    u.argtypes = [vp] * 7 + [ctypes.c_int32, vp, ctypes.c_int32, ctypes.c_int32, vp, ctypes.c_size_t, vp,
+                             ctypes.POINTER(st.Opts)]
+    d = lib.idx_topk_decode_paged_debug
+    d.restype = ctypes.c_int
+    d.argtypes = [vp] * 7 + [ctypes.c_int32] * 5 + [vp, vp, ctypes.c_size_t, vp, vp, ctypes.POINTER(st.Opts)]
+    p = lib.idx_topk_prefill_debug
+    p.restype = ctypes.c_int
+    p.argtypes = [vp] * 7 + [ctypes.c_int32, vp, ctypes.c_int32, ctypes.c_int32, vp, ctypes.c_size_t, vp,
+                             vp, vp, ctypes.POINTER(st.Opts)]
+    for field, val in (("row_status", good), ("clock_out", good), ("math_only", 1)):
+        o = st.Opts()
+        setattr(o, field, val)
+        assert u(good, None, good, good, good, good, good, 64, good, 4, 100, ws, big, None,
+                 ctypes.byref(o)) == -1, field
+        assert d(*([good] * 7 + [2, 8, 64, 16, 2048, good, ws, big, None, None]), ctypes.byref(o)) == -1, field
+    o = st.Opts()
+    o.math_only, o.force_tau = 1, 1
+    assert p(good, None, good, good, good, good, good, 64, good, 4, 100, ws, big, None, None, None,
+             ctypes.byref(o)) == -1

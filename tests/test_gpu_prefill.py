@@ -201,35 +201,3 @@ def test_identical_keys_get_identical_scores():
             v = S[group[:s1] == g]
             assert v.size == 0 or np.all(v.view(np.uint32) == v[0].view(np.uint32))
     check_prefill_rows(case, r["out"], np.arange(case.Q))
-
-
-@pytest.mark.parametrize("name", ["prefill_chunk", "long_prefill"])
-def test_full_size_sampled_rows(name):
-    """Full-size workloads in the benchmark's launch configuration; the oracle
-    checks a sample of rows (first, middle, last and random)."""
-    case = synth.WORKLOADS[name](0)
-    log("case", case.name, case.Q, case.N)
-    r = run_prefill(case)
-    log("stats", r["stats"])
-    assert r["stats"]["rows"] == case.Q
-    rows = sample_rows(case.Q, 12, seed=1)
-    rep = check_prefill_rows(case, r["out"], rows)
-    log(name, rep)
-    # structure of every row
-    for t in range(case.Q):
-        check.check_structure(r["out"][t], int(case.row_start[t]), int(case.row_end[t]), case.K)
-
-
-def test_adversarial_subcalls_sampled_rows():
-    for case in synth.adversarial(0) + [synth.adversarial_decoy(0, Q=64)]:
-        log("case", case.name, case.Q, case.N)
-        r = run_prefill(case)
-        log("stats", r["stats"])
-        rows = sample_rows(case.Q, 6, seed=2)
-        rep = check_prefill_rows(case, r["out"], rows)
-        log(case.name, rep)
-        if case.name == "adversarial_decoy":
-            assert r["stats"]["underflow"] > 0 and r["stats"]["repaired"] > 0
-        if case.name == "adversarial_ties16":
-            # ties at the threshold are certified without repair
-            assert r["stats"]["fast_ok"] >= 0.9 * case.Q, r["stats"]

@@ -81,16 +81,17 @@ def test_scan_ties_and_invalid_lengths():
     assert st["bad_rows"] == 2
 
 
-def test_scan_full_workload_sampled_streams():
-    """The 32 x 262144 workload: every stream's structure, two streams against
-    the oracle element by element."""
+def test_scan_full_workload_every_stream():
+    """The 32 x 262144 workload in the benchmark's launch configuration: every
+    stream against the oracle (selection tolerance, element-wise scores,
+    bit-exact and canonical selection on the GPU's own scores)."""
     case = synth.bf16_scan(0)
     log("case", case.name)
     out, S, st = _run(case, scores=True)
     log("stats", st)
-    for b in range(case.B):
-        check.check_structure(out[b], 0, int(case.lens[b]), case.K, where="stream %d" % b)
-    _check(case, out, S, [0, case.B - 1])
+    for b0 in range(0, case.B, 8):
+        _check(case, out, S, list(range(b0, min(case.B, b0 + 8))))
+        log("streams", b0, "..", min(case.B, b0 + 8) - 1, "match the oracle")
     assert st["fast_ok"] == case.B
 
 

@@ -48,3 +48,25 @@ def test_paged_decode_layout():
     used = c.page_table[c.page_table >= 0]
     assert sorted(used.tolist()) == list(range(c.k_cache.shape[0]))
     assert c.page_table[0].tolist()[:2] != [-1, -1] and c.page_table[0, 2] == -1
+
+
+def test_adversarial_rows_split_as_configured():
+    """2048 rows at the last positions of 163840 keys: half ties, a quarter
+    split between the off-lattice outlier block and the on-lattice decoys
+    (the underflow/repair quarter), the rest plain; every row appears once."""
+    import inspect
+    src = inspect.getsource(synth.adversarial)
+    assert "1024" in src and "256" in src and "512" in src
+    # row counts and disjoint positions without generating the keys
+    N = 163840
+    pos = np.arange(N - 2048, N)
+    parts = [pos[:1024], pos[1024:1280], pos[1280:1536], pos[1536:]]
+    assert sum(p.size for p in parts) == 2048
+    assert np.array_equal(np.concatenate(parts), pos)
+
+
+def test_random_codes_case_has_no_nan_codes():
+    c = synth.random_codes_case("rc", 5000, [0, 10], [100, 5000], seed=3)
+    assert not np.any((c.k8 & 0x7F) == 0x7F)
+    assert c.k8.shape == (5000, 128) and c.q8.shape == (2, 64, 128)
+    assert np.all(c.k_scale > 0)
