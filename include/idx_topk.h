@@ -71,7 +71,9 @@ enum {
   IDX_EINVAL = -1,       /* null pointer, negative size, bad alignment, K out of range */
   IDX_EUNSUPPORTED = -2, /* geometry the kernels do not implement (page_size != 64) */
   IDX_EWORKSPACE = -3,   /* workspace missing or smaller than the query returned */
-  IDX_EHIP = -4          /* a HIP launch or copy failed */
+  IDX_EHIP = -4,         /* a HIP launch or copy failed */
+  IDX_ESCRATCH = -5      /* the call needs more scratch than the static array of
+                            idx_topk_decode_paged_noalloc holds */
 };
 
 /* Per-call counters kept in the workspace (read with idx_topk_read_stats). */
@@ -298,6 +300,27 @@ int idx_topk_decode_paged_debug(const uint8_t *q, const float *q_scale, const ui
                                 int32_t page_size, int32_t num_pages, int32_t K, int32_t *out_idx,
                                 void *workspace, size_t workspace_bytes, void *stream,
                                 float *scores_out, const idx_topk_opts *opts);
+
+/*
+ * Paged decode without any allocation, for callers that cannot allocate
+ * device memory or pass a workspace: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation.  Same arguments, kernels
+ * and output as idx_topk_decode_paged, minus the workspace: the scratch is a
+ * static device array of IDX_TOPK_NOALLOC_SCRATCH_BYTES per GPU, set up by
+ * the first call on each device (make that first call outside a graph
+ * capture) and held until the process ends.  A call whose scratch would
+ * exceed it (idx_topk_decode_workspace(B, max_pages, page_size, K) bytes)
+ * returns IDX_ESCRATCH and enqueues nothing; the other errors are those of
+ * idx_topk_decode_paged.  Every call on one GPU shares that GPU's array:
+ * calls that overlap in time on one GPU (two streams, two threads) race and
+ * must be serialised by the caller.  Nothing is allocated or freed.
+ */
+#define IDX_TOPK_NOALLOC_SCRATCH_BYTES (16u << 20)
+int idx_topk_decode_paged_noalloc(const uint8_t *q, const float *q_scale, const uint8_t *k_cache,
+                                  const float *k_scale, const float *w, const int32_t *page_table,
+                                  const int32_t *seq_lens, int32_t B, int32_t max_pages,
+                                  int32_t page_size, int32_t num_pages, int32_t K, int32_t *out_idx,
+                                  void *stream);
 
 /* Copy the counters of the last call that used `workspace` into *out.
  * Synchronises `stream`.  For tests and diagnosis, not for hot loops. */

@@ -83,6 +83,8 @@ _lib.idx_topk_decode_paged.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, 
                                        _i32, _vp, _vp, _sz, _vp]
 _lib.idx_topk_decode_paged_debug.restype = ctypes.c_int
 _lib.idx_topk_decode_paged_debug.argtypes = _lib.idx_topk_decode_paged.argtypes + [_vp, ctypes.POINTER(Opts)]
+_lib.idx_topk_decode_paged_noalloc.restype = ctypes.c_int
+_lib.idx_topk_decode_paged_noalloc.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp, _vp]
 _lib.idx_topk_read_stats.restype = ctypes.c_int
 _lib.idx_topk_read_stats.argtypes = [_vp, ctypes.POINTER(Stats), _vp]
 _lib.idx_topk_strerror.restype = ctypes.c_char_p
@@ -381,6 +383,24 @@ def decode_paged(q8, q_scale, k_cache, k_scale, w, page_table, seq_lens, K: int,
         opts = Opts(1 if force_tau is not None else 0, float(force_tau or 0.0), 0, 0, ev0, ev1,
                     int(main_reps))
         _check(_lib.idx_topk_decode_paged_debug(*args, _ptr(scores_out, torch.float32), ctypes.byref(opts)))
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 16 << 20
+
+
+def decode_paged_noalloc(q8, q_scale, k_cache, k_scale, w, page_table, seq_lens, K: int, out, stream=None):
+    """idx_topk_decode_paged_noalloc: paged decode with the library's static
+    per-GPU scratch (no workspace, nothing allocated); `out` [B,K] int32 is
+    the caller's."""
+    q8, k_cache = _q_k(q8, k_cache)
+    B = int(q8.shape[0])
+    P, page = int(k_cache.shape[0]), int(k_cache.shape[1])
+    _check(_lib.idx_topk_decode_paged_noalloc(
+        _ptr(q8, torch.uint8), _ptr(q_scale, torch.float32), _ptr(k_cache, torch.uint8),
+        _ptr(k_scale, torch.float32), _ptr(w, torch.float32), _ptr(page_table, torch.int32),
+        _ptr(seq_lens, torch.int32), B, int(page_table.shape[1]), page, P, int(K), _ptr(out, torch.int32),
+        _stream(stream)))
     return out
 
 

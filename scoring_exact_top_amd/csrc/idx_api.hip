@@ -223,6 +223,15 @@ extern "C" int idx_topk_decode_paged_debug(const uint8_t* q, const float* q_scal
                       scores_out);
 }
 
+extern "C" int idx_topk_decode_paged_noalloc(const uint8_t* q, const float* q_scale, const uint8_t* k_cache,
+                                             const float* k_scale, const float* w, const int32_t* page_table,
+                                             const int32_t* seq_lens, int32_t B, int32_t max_pages,
+                                             int32_t page_size, int32_t num_pages, int32_t K, int32_t* out_idx,
+                                             void* stream) {
+  return decode_paged_noalloc(q, q_scale, k_cache, k_scale, w, page_table, seq_lens, B, max_pages, page_size,
+                              num_pages, K, out_idx, static_cast<hipStream_t>(stream));
+}
+
 extern "C" int idx_topk_read_stats(const void* workspace, idx_topk_stats* out, void* stream) {
   if (!workspace || !out) return IDX_EINVAL;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -245,6 +254,7 @@ extern "C" const char* idx_topk_strerror(int code) {
     case IDX_EUNSUPPORTED: return "unsupported geometry";
     case IDX_EWORKSPACE: return "workspace missing or too small";
     case IDX_EHIP: return "HIP launch or copy failed";
+    case IDX_ESCRATCH: return "call needs more scratch than the allocation-free entry point's static array";
     default: return "unknown error";
   }
 }

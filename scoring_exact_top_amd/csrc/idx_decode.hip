@@ -22,6 +22,8 @@
 #include <hip/hip_ext.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "idx_decode.hpp"
 #include "idx_internal.hpp"
 #include "idx_rows.hpp"
@@ -293,6 +295,49 @@ int decode_paged(const uint8_t* q, const float* q_scale, const uint8_t* k_cache,
                      hipMemcpyDeviceToDevice, stream) != hipSuccess)
     rc = IDX_EHIP;
   return rc;
+}
+
+// ---------------------------------------------------- allocation-free call
+
+// The allocation-free entry point's scratch: one array per GPU in the code
+// object's device data, held until the process ends.  Its name is a
+// host-side stand-in on the host; the device address of each GPU's copy is
+// looked up once per device (hipGetSymbolAddress, with that device current)
+// and only that address is passed to kernels.
+static __device__ __align__(256) uint8_t scratch[IDX_TOPK_NOALLOC_SCRATCH_BYTES];
+
+static void* scratch_address() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return nullptr;
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  if (dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+      (void)hipGetLastError();
+      return nullptr;
+    }
+    addr[dev] = p;
+  }
+  return addr[dev];
+}
+
+int decode_paged_noalloc(const uint8_t* q, const float* q_scale, const uint8_t* k_cache, const float* k_scale,
+                         const float* w, const int32_t* page_table, const int32_t* seq_lens, int32_t B,
+                         int32_t max_pages, int32_t page_size, int32_t num_pages, int32_t K, int32_t* out_idx,
+                         hipStream_t stream) {
+  const size_t need = decode_workspace_bytes(B, max_pages, page_size, K);
+  if (need == 0 || B == 0)  // rejected arguments or an empty batch: the full call's checks answer, no HIP call
+    return decode_paged(q, q_scale, k_cache, k_scale, w, page_table, seq_lens, B, max_pages, page_size, num_pages,
+                        K, out_idx, nullptr, 0, stream, nullptr);
+  if (need > IDX_TOPK_NOALLOC_SCRATCH_BYTES) return IDX_ESCRATCH;
+  void* ws = scratch_address();
+  if (!ws) return IDX_EHIP;
+  return decode_paged(q, q_scale, k_cache, k_scale, w, page_table, seq_lens, B, max_pages, page_size, num_pages, K,
+                      out_idx, ws, IDX_TOPK_NOALLOC_SCRATCH_BYTES, stream, nullptr);
 }
 
 }  // namespace idxk

@@ -196,3 +196,26 @@ def test_debug_knobs_are_rejected_where_they_do_not_apply(lib):
     o.math_only, o.force_tau = 1, 1
     assert p(good, None, good, good, good, good, good, 64, good, 4, 100, ws, big, None, None, None,
              ctypes.byref(o)) == -1
+
+
+def test_noalloc_decode_argument_errors(lib):
+    """The allocation-free decode answers argument errors like the workspace
+    entry point, and a call whose scratch would exceed the static array
+    with IDX_ESCRATCH, all before any HIP call."""
+    vp = ctypes.c_void_p
+    f = lib.idx_topk_decode_paged_noalloc
+    f.restype = ctypes.c_int
+    f.argtypes = [vp] * 7 + [ctypes.c_int32] * 5 + [vp, vp]
+    lib.idx_topk_decode_workspace.restype = ctypes.c_size_t
+    good = vp(1 << 20)
+    args = lambda B=2, mp=8, ps=64, K=2048: [good] * 7 + [B, mp, ps, 16, K, good, None]
+    assert f(*args(ps=32)) == -2
+    assert f(*args(K=0)) == -1
+    assert f(*args(B=-1)) == -1
+    assert f(*args(B=0)) == 0
+    limit = 16 << 20
+    assert lib.idx_topk_decode_workspace(16, 1024, 64, 2048) <= limit      # the benchmarked batch fits
+    assert lib.idx_topk_decode_workspace(64, 1024, 64, 2048) > limit       # this one does not
+    assert f(*args(B=64, mp=1024)) == -5
+    lib.idx_topk_strerror.restype = ctypes.c_char_p
+    assert b"scratch" in lib.idx_topk_strerror(-5)
