@@ -84,9 +84,8 @@ typedef struct {
   uint32_t overflow;   /* fast path failed: a candidate dropped for lack of
                           capacity scores above the selection (or ties with
                           it below a selected tied id)                          */
-  uint32_t spilled;    /* fast-path rows with more candidates than the on-chip
-                          share lds_cap (informational: the prefill main kernel
-                          writes candidates straight to the workspace)          */
+  uint32_t many_cands; /* fast-path rows that kept more than 4096 candidates
+                          (twice K at the default sampling target; informational) */
   uint32_t repaired;   /* rows recomputed by the exact repair path              */
   uint32_t trivial;    /* rows (sequences) with L <= K: no scoring needed       */
   uint32_t bad_rows;   /* rows with an invalid range or page id (output all -1) */
@@ -96,8 +95,9 @@ typedef struct {
 typedef struct {
   int32_t force_tau;   /* 1: use tau_value as every row's threshold             */
   float tau_value;
-  int32_t lds_cap;     /* >0: on-chip candidate capacity per row (<= default)   */
-  int32_t spill_cap;   /* >0: spill capacity per row (<= default); -1: none     */
+  int32_t cand_cap;    /* >0: candidates the fast path stores per row (<= the
+                          default 8192); a row with more fails its certificate
+                          and is repaired (0: the default)                       */
   void *ev_main_start; /* hipEvent_t or NULL: recorded by the launch of the main  */
   void *ev_main_stop;  /*   scoring kernel at its start and at its end (timing only) */
   int32_t main_reps;   /* >1: the main scoring kernel is launched this many times
@@ -291,7 +291,7 @@ int idx_topk_decode_paged(const uint8_t *q, const float *q_scale, const uint8_t 
  *   opts       NULL or timing only: ev_main_start/ev_main_stop are recorded by
  *              the launch of the split scoring kernel at its start and at its
  *              end, main_reps repeats it.  The decode path has no threshold
- *              and no capacity knobs: opts with force_tau, lds_cap, spill_cap,
+ *              and no capacity knobs: opts with force_tau, cand_cap,
  *              row_status, clock_out or math_only set gives IDX_EINVAL.
  */
 int idx_topk_decode_paged_debug(const uint8_t *q, const float *q_scale, const uint8_t *k_cache,

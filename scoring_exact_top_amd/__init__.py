@@ -34,7 +34,7 @@ _sz = ctypes.c_size_t
 
 class Opts(ctypes.Structure):
     _fields_ = [("force_tau", ctypes.c_int32), ("tau_value", ctypes.c_float),
-                ("lds_cap", ctypes.c_int32), ("spill_cap", ctypes.c_int32),
+                ("cand_cap", ctypes.c_int32),
                 ("ev_main_start", ctypes.c_void_p), ("ev_main_stop", ctypes.c_void_p),
                 ("main_reps", ctypes.c_int32), ("row_status", ctypes.c_void_p),
                 ("clock_out", ctypes.c_void_p), ("math_only", ctypes.c_int32)]
@@ -46,7 +46,7 @@ ROW_FAST, ROW_UNDERFLOW, ROW_OVERFLOW, ROW_BAD = 0, 1, 2, -1
 
 class Stats(ctypes.Structure):
     _fields_ = [(n, ctypes.c_uint32) for n in
-                ("rows", "fast_ok", "underflow", "overflow", "spilled", "repaired", "trivial",
+                ("rows", "fast_ok", "underflow", "overflow", "many_cands", "repaired", "trivial",
                  "bad_rows")]
 
     def asdict(self):
@@ -162,7 +162,7 @@ def prefill(q8, q_scale, k8, k_scale, w, row_start, row_end, K: int, out=None, w
 
 def prefill_debug(q8, q_scale, k8, k_scale, w, row_start, row_end, K: int, out=None,
                   workspace=None, stream=None, scores_out=None, tau_out=None,
-                  force_tau: Optional[float] = None, lds_cap: int = 0, spill_cap: int = 0,
+                  force_tau: Optional[float] = None, cand_cap: int = 0,
                   main_events=None, main_reps: int = 1, row_status=None, clock_out=None,
                   math_only: bool = False):
     """idx_topk_prefill_debug: also emits FP32 scores [Q,N] and thresholds [Q].
@@ -177,8 +177,8 @@ def prefill_debug(q8, q_scale, k8, k_scale, w, row_start, row_end, K: int, out=N
     ev0 = ev1 = None
     if main_events is not None:
         ev0, ev1 = (ctypes.c_void_p(e.cuda_event) for e in main_events)
-    opts = Opts(1 if force_tau is not None else 0, float(force_tau or 0.0), int(lds_cap),
-                int(spill_cap), ev0, ev1, int(main_reps), _ptr(row_status, torch.int32),
+    opts = Opts(1 if force_tau is not None else 0, float(force_tau or 0.0), int(cand_cap),
+                ev0, ev1, int(main_reps), _ptr(row_status, torch.int32),
                 _ptr(clock_out, torch.int64), 1 if math_only else 0)
     return _prefill(q8, q_scale, k8, k_scale, w, row_start, row_end, K, out, workspace, stream,
                     debug=True, scores_out=scores_out, tau_out=tau_out, opts=opts)
@@ -225,7 +225,7 @@ def prefill_unfused(q8, q_scale, k8, k_scale, w, row_start, row_end, K: int, out
     ev0 = ev1 = None
     if main_events is not None:
         ev0, ev1 = (ctypes.c_void_p(e.cuda_event) for e in main_events)
-    opts = Opts(0, 0.0, 0, 0, ev0, ev1, int(main_reps))
+    opts = Opts(0, 0.0, 0, ev0, ev1, int(main_reps))
     _check(_lib.idx_topk_prefill_unfused(
         _ptr(q8, torch.uint8), _ptr(q_scale, torch.float32), _ptr(k8, torch.uint8),
         _ptr(k_scale, torch.float32), _ptr(w, torch.float32), _ptr(row_start, torch.int32),
@@ -270,7 +270,7 @@ def scan_bf16(q16, w, k16, lens, K: int, out=None, workspace=None, stream=None, 
     ev0 = ev1 = None
     if main_events is not None:
         ev0, ev1 = (ctypes.c_void_p(e.cuda_event) for e in main_events)
-    opts = Opts(0, 0.0, 0, 0, ev0, ev1, int(main_reps))
+    opts = Opts(0, 0.0, 0, ev0, ev1, int(main_reps))
     _check(_lib.idx_topk_scan_bf16(_ptr(q16), _ptr(w, torch.float32), _ptr(k16), _ptr(lens, torch.int32),
                                    B, N, int(K), _ptr(out, torch.int32), _ptr(workspace),
                                    int(workspace.numel()), _stream(stream), ctypes.byref(opts)))
@@ -380,7 +380,7 @@ def decode_paged(q8, q_scale, k_cache, k_scale, w, page_table, seq_lens, K: int,
         ev0 = ev1 = None
         if main_events is not None:
             ev0, ev1 = (ctypes.c_void_p(e.cuda_event) for e in main_events)
-        opts = Opts(1 if force_tau is not None else 0, float(force_tau or 0.0), 0, 0, ev0, ev1,
+        opts = Opts(1 if force_tau is not None else 0, float(force_tau or 0.0), 0, ev0, ev1,
                     int(main_reps))
         _check(_lib.idx_topk_decode_paged_debug(*args, _ptr(scores_out, torch.float32), ctypes.byref(opts)))
     return out

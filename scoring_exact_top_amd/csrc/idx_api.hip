@@ -78,14 +78,10 @@ static int prefill_common(const uint8_t* q, const float* q_scale, const uint8_t*
   A.kt = reinterpret_cast<uint8_t*>(ws + L.kt);
   A.out = out_idx;
   A.dbg_scores = scores_out;
-  A.lds_cap = kLdsCap;
-  A.spill_cap = kSpillCap;
+  A.cand_cap = kCandCap;
   if (opts) {
-    if (opts->lds_cap < 0 || opts->lds_cap > kLdsCap || opts->spill_cap < -1 || opts->spill_cap > kSpillCap)
-      return IDX_EINVAL;
-    if (opts->lds_cap > 0) A.lds_cap = opts->lds_cap;
-    if (opts->spill_cap > 0) A.spill_cap = opts->spill_cap;
-    if (opts->spill_cap == -1) A.spill_cap = 0;
+    if (opts->cand_cap < 0 || opts->cand_cap > kCandCap) return IDX_EINVAL;
+    if (opts->cand_cap > 0) A.cand_cap = opts->cand_cap;
     A.force_tau = opts->force_tau ? 1 : 0;
     A.tau_value = opts->tau_value;
     A.ev_main_start = static_cast<hipEvent_t>(opts->ev_main_start);
@@ -97,11 +93,10 @@ static int prefill_common(const uint8_t* q, const float* q_scale, const uint8_t*
     A.clock = opts->clock_out;
     A.math_only = opts->math_only ? 1 : 0;
   }
-  A.cap_total = A.lds_cap + A.spill_cap;
   // usable entries per segment: the full segment unless a test knob shrank
   // the capacity, then an even share of it
-  const int share = A.cap_total / (kWaves * A.S);
-  A.seg_eff = (A.cap_total >= kCandCap || share > A.seg_cap) ? A.seg_cap : share;
+  const int share = A.cand_cap / (kWaves * A.S);
+  A.seg_eff = (A.cand_cap >= kCandCap || share > A.seg_cap) ? A.seg_cap : share;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (unfused) {
     A.dbg_scores = reinterpret_cast<float*>(ws + L.dense);
@@ -112,7 +107,7 @@ static int prefill_common(const uint8_t* q, const float* q_scale, const uint8_t*
   // N <= kCandCap with the default capacities: every valid row has L <=
   // kCandCap, so its threshold is -inf, no segment overflows and the
   // certificate cannot fail (no sampling, no repair to launch)
-  A.keep_all = (!A.force_tau && !A.math_only && A.N > 0 && A.N <= kCandCap && A.cap_total >= kCandCap) ? 1 : 0;
+  A.keep_all = (!A.force_tau && !A.math_only && A.N > 0 && A.N <= kCandCap && A.cand_cap >= kCandCap) ? 1 : 0;
   // the main kernel samples its rows itself (with S > 1 splits per row pair,
   // each split samples the pair: the same values, S times, in parallel)
   A.fuse_tau = (!A.force_tau && !A.keep_all && !A.math_only && A.N > 0) ? 1 : 0;
@@ -161,7 +156,7 @@ extern "C" int idx_topk_prefill_unfused(const uint8_t* q, const float* q_scale, 
                                         const int32_t* row_end, int32_t K, int32_t* out_idx, int32_t Q,
                                         int32_t N, void* workspace, size_t workspace_bytes, void* stream,
                                         const idx_topk_opts* opts) {
-  if (opts && (opts->force_tau || opts->lds_cap || opts->spill_cap || opts->row_status || opts->clock_out ||
+  if (opts && (opts->force_tau || opts->cand_cap || opts->row_status || opts->clock_out ||
                opts->math_only))
     return IDX_EINVAL;
   return prefill_common(q, q_scale, k, k_scale, w, row_start, row_end, K, out_idx, Q, N, workspace,

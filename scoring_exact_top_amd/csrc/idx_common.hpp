@@ -704,8 +704,10 @@ __device__ __forceinline__ RegLayout block_list_layout(uint32_t n, uint32_t tid)
 
 // Loads of one list into registers, key[j] and id[j] = element lay.at(j):
 // buffer loads whose out-of-range reads return 0, so all of them are issued
-// back to back without a branch per element; invalid slots get key 0.
-// `extent` (uniform) bounds the buffers; lay.valid masks the entries.
+// back to back without a branch per element; invalid slots get key 0 and
+// read nothing (their offset lies past every buffer, so the bounds check
+// answers them without a memory access).  `extent` (uniform) bounds the
+// buffers; lay.valid masks the entries.
 template <int M, class Dec>
 __device__ __forceinline__ void load_list_regs(uint32_t (&key)[M], int32_t (&id)[M], const uint32_t* keys,
                                                const int32_t* ids, uint32_t extent, const RegLayout& lay,
@@ -715,8 +717,9 @@ __device__ __forceinline__ void load_list_regs(uint32_t (&key)[M], int32_t (&id)
   uint32_t raw[M];
 #pragma unroll
   for (int j = 0; j < M; ++j) {
-    raw[j] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rk, (int)(lay.at(j) * 4u), 0, 0);
-    id[j] = __builtin_amdgcn_raw_buffer_load_b32(ri, (int)(lay.at(j) * 4u), 0, 0);
+    const int off = lay.valid(j) ? (int)(lay.at(j) * 4u) : 0x7FFFFFF0;
+    raw[j] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rk, off, 0, 0);
+    id[j] = __builtin_amdgcn_raw_buffer_load_b32(ri, off, 0, 0);
   }
 #pragma unroll
   for (int j = 0; j < M; ++j) key[j] = lay.valid(j) ? dec(raw[j]) : 0u;

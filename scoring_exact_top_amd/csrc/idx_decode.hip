@@ -248,7 +248,7 @@ int decode_paged(const uint8_t* q, const float* q_scale, const uint8_t* k_cache,
   if (page_size != 64 || B > kMaxGridY) return IDX_EUNSUPPORTED;
   // slots and logical positions are int32; the cache itself may be of any size
   if ((int64_t)max_pages * 64 * 4 > 0x7fffffffLL || (int64_t)num_pages * 64 > 0x7fffffffLL) return IDX_EINVAL;
-  if (opts && (opts->force_tau || opts->lds_cap || opts->spill_cap || opts->row_status || opts->clock_out ||
+  if (opts && (opts->force_tau || opts->cand_cap || opts->row_status || opts->clock_out ||
                opts->math_only))
     return IDX_EINVAL;
   if (opts && (opts->main_reps < 0 || opts->main_reps > 1000)) return IDX_EINVAL;

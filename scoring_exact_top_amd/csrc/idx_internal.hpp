@@ -20,18 +20,18 @@ constexpr int kMaxSamples = 2048;  // longer rows widen the stride instead
 // over S workgroups (S = 1 when there are rows enough to fill the chip, up
 // to kMaxSplit for few rows: parallelism along the keys, "10. The
 // optimization target after fusion"), and each (split, wave) stores its
-// candidates into a private workspace segment.  The certificate's capacity
-// per row is kCandCap (kLdsCap + kSpillCap, the default of the test knobs);
-// a segment is sized so that a row short enough to keep all its keys
-// (L <= kCandCap, threshold -inf) never overflows it, and a row also fails
-// the certificate when one segment alone overflows.
+// candidates straight into a private workspace segment (the pages' on-chip
+// store and spill area become one area in device memory).  The
+// certificate's capacity per row is kCandCap (the default of the cand_cap
+// test knob); a segment is sized so that a row short enough to keep all its
+// keys (L <= kCandCap, threshold -inf) never overflows it, and a row also
+// fails the certificate when one segment alone overflows.
 // Largest y (and z) dimension of a launch grid: bounds the sequences of
 // paged decode and the streams of the BF16 scan, which index it.
 constexpr int kMaxGridY = 65535;
 
-constexpr int kLdsCap = 4096;
-constexpr int kSpillCap = 4096;
-constexpr int kCandCap = kLdsCap + kSpillCap;
+constexpr int kCandCap = 8192;
+constexpr int kManyCands = 4096;  // rows keeping more are counted (idx_topk_stats.many_cands)
 constexpr int kMaxSplit = 8;
 constexpr int kSelRegs = 40;  // keys per thread of the select kernel, all S <= kMaxSplit
 
@@ -74,7 +74,7 @@ constexpr int kStatLanes = 32;
 constexpr int kStatStride = 32;  // words between copies
 constexpr int kStatCount = 8;    // counters per copy, idx_topk_stats order
 constexpr int kCtrlWords = kStatsOff + kStatLanes * kStatStride;
-constexpr int kStRows = 0, kStFast = 1, kStUnder = 2, kStOver = 3, kStSpilled = 4,
+constexpr int kStRows = 0, kStFast = 1, kStUnder = 2, kStOver = 3, kStMany = 4,
               kStRepaired = 5, kStTrivial = 6, kStBad = 7;
 
 __device__ __forceinline__ uint32_t* stat_copy(uint32_t* ctrl, int block) {
@@ -125,7 +125,7 @@ struct PrefillArgs {
   uint32_t* segn;       // [Q][kWaves*S][4]: entries stored, key of the largest dropped candidate
                         // (0: none), position of the first dropped one, unused
   int32_t S, seg_cap, seg_eff;  // splits, segment stride, usable entries per segment
-  int32_t lds_cap, spill_cap, cap_total;
+  int32_t cand_cap;  // candidates stored per row (the certificate's capacity)
   int32_t* fail_list;   // [Q]
   uint32_t* ctrl;       // kCtrlWords
   uint32_t* scratch;    // [repair_rows][repair_stride(N)] repair scores (order-preserving keys)
@@ -152,9 +152,9 @@ struct SampleGeom {
 
 // Sample lattice of a row of length L: positions OFFSET + stride*i < L.  Rows
 // that fit the candidate capacity need no threshold (n = 0: tau = -inf).
-__device__ inline SampleGeom sample_geom(int L, int cap_total) {
+__device__ inline SampleGeom sample_geom(int L, int cand_cap) {
   SampleGeom g{0, kSampleStride, 0};
-  if (L <= cap_total || L <= kSampleOffset) return g;
+  if (L <= cand_cap || L <= kSampleOffset) return g;
   const int64_t span = (int64_t)L - kSampleOffset;
   int64_t stride = kSampleStride;
   if ((span + stride - 1) / stride > kMaxSamples) stride = (span + kMaxSamples - 1) / kMaxSamples;

@@ -84,7 +84,15 @@ __global__ __launch_bounds__(kWG) void k_prefill_tau(PrefillArgs A) {
 // into one checksum per (row, wave) instead of being sampled, filtered and
 // appended; with no selection or repair after it, the complete operator's
 // time minus this kernel's is the selection work left exposed.
-constexpr int kPairFused = 0, kPairDebug = 1, kPairDense = 2, kPairControl = 3;
+// kPairRepair rescores the rows the certificate rejected (exact repair,
+// "3.2 Sampled threshold"): workgroups take the failure list's slotted
+// rows two at a time, split each pair's tiles over the whole grid (the
+// split count follows from the failure count, read on the device), write
+// every score as an order-preserving key into the row's scratch slot and
+// add the top-byte histogram of the row into its first digit histogram.  A
+// row's score does not depend on its partner or its slot in the pair, so
+// these are the walk's scores bit for bit.
+constexpr int kPairFused = 0, kPairDebug = 1, kPairDense = 2, kPairControl = 3, kPairRepair = 4;
 
 // Head-weighted sum of one row's 16 heads held by this lane plus its two
 // u-block rows (ua, ub), in a fixed order (18 FMAs).
@@ -128,17 +136,36 @@ __global__ __launch_bounds__(kWG, 2) void k_prefill_pair(PrefillArgs A) {
   // optional clock probe: this wave's shader-clock cycles and constant-rate
   // wall-clock ticks from its start to its end, summed over all waves
   uint64_t clk0 = 0, rtc0 = 0;
-  if (A.clock) {
+  if (MODE != kPairRepair && A.clock) {
     clk0 = __builtin_amdgcn_s_memtime();
     rtc0 = __builtin_amdgcn_s_memrealtime();
   }
   const int tid = threadIdx.x;
   const uint32_t lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int split = blockIdx.x % A.S;           // which share of the pair's tiles
-  const int t0 = 2 * (blockIdx.x / A.S);
+  // the pair's rows (t_of: -1 for none) and, in repair mode, their scratch slots
+  int split, nsplit, t_of[2], slot[2] = {0, 0};
+  if constexpr (MODE == kPairRepair) {
+    const int n_slot = (int)min(__atomic_load_n(&A.ctrl[kCtrlFail], __ATOMIC_RELAXED), (uint32_t)A.rslots);
+    const int pairs = (n_slot + 1) / 2;
+    if (pairs == 0) return;  // nothing failed (the whole workgroup leaves together)
+    nsplit = max(1, (int)gridDim.x / pairs);
+    const int pr = blockIdx.x / nsplit;
+    if (pr >= pairs) return;
+    split = blockIdx.x % nsplit;
+    slot[0] = 2 * pr;
+    slot[1] = 2 * pr + 1;
+    t_of[0] = A.fail_list[slot[0]];
+    t_of[1] = slot[1] < n_slot ? A.fail_list[slot[1]] : -1;
+  } else {
+    nsplit = A.S;
+    split = blockIdx.x % A.S;  // which share of the pair's tiles
+    t_of[0] = 2 * (blockIdx.x / A.S);
+    t_of[1] = t_of[0] + 1 < A.Q ? t_of[0] + 1 : -1;
+  }
+  const int t0 = t_of[0];
   const int seg = split * kWaves + wave;        // this wave's segment of each row
-  const int nseg = kWaves * A.S;
+  const int nseg = kWaves * nsplit;
 
   int rs[2], re[2];
   float tr[2];
@@ -146,8 +173,8 @@ __global__ __launch_bounds__(kWG, 2) void k_prefill_pair(PrefillArgs A) {
 #pragma unroll
   for (int r = 0; r < 2; ++r) {
     rs[r] = 0; re[r] = 0; tr[r] = INFINITY;
-    const int t = t0 + r;
-    if (t < A.Q) {
+    const int t = t_of[r];
+    if (t >= 0 && t < A.Q) {
       const int s = A.row_start[t], e = A.row_end[t];
       if (s >= 0 && s <= e && e <= A.N) {
         rs[r] = s; re[r] = e; tr[r] = A.fuse_tau ? -INFINITY : A.tau[t];
@@ -155,8 +182,14 @@ __global__ __launch_bounds__(kWG, 2) void k_prefill_pair(PrefillArgs A) {
       }
     }
   }
+  __shared__ uint32_t s_rhist[2][256];  // repair: the pair's top-byte histograms
+  if constexpr (MODE == kPairRepair) {
+    s_rhist[0][tid] = 0u;
+    s_rhist[1][tid] = 0u;
+  }
   QOp2 qo;
-  prepare_q2(qo, A.q, A.q_scale, A.w, min(t0, A.Q - 1), min(t0 + 1, A.Q - 1), lane, s_qprep[wave]);
+  prepare_q2(qo, A.q, A.q_scale, A.w, min(t_of[0], A.Q - 1), t_of[1] >= 0 ? t_of[1] : min(t_of[0], A.Q - 1), lane,
+             s_qprep[wave]);
   __syncthreads();
 
   // Fused sampler ("3.2 Sampled threshold"), unless a threshold is forced:
@@ -166,7 +199,7 @@ __global__ __launch_bounds__(kWG, 2) void k_prefill_pair(PrefillArgs A) {
   // score the sampled keys' tiles (once for both rows when they share the
   // sample positions, as causal rows do) with the walk's arithmetic, so a
   // threshold is one of the walk's scores; wave r then selects row r's.
-  if constexpr (MODE != kPairDense && MODE != kPairControl) {
+  if constexpr (MODE == kPairFused || MODE == kPairDebug) {
     if (A.fuse_tau) {
       __shared__ uint32_t s_samp[2][kMaxSamples];
       __shared__ uint32_t s_hist[2][256];
@@ -174,7 +207,7 @@ __global__ __launch_bounds__(kWG, 2) void k_prefill_pair(PrefillArgs A) {
       SampleGeom sg[2];
 #pragma unroll
       for (int r = 0; r < 2; ++r)
-        sg[r] = re[r] > rs[r] ? sample_geom(re[r] - rs[r], A.cap_total) : SampleGeom{0, kSampleStride, 0};
+        sg[r] = re[r] > rs[r] ? sample_geom(re[r] - rs[r], A.cand_cap) : SampleGeom{0, kSampleStride, 0};
       const KeyBuf kbuf = make_keybuf(A.k, A.k_scale, A.N);
       const auto pass = [&](int src, int n, bool st0, bool st1) {  // samples of row src's positions
 #pragma unroll 1
@@ -227,7 +260,7 @@ __global__ __launch_bounds__(kWG, 2) void k_prefill_pair(PrefillArgs A) {
   rsrc_t segk[2], segi[2];
 #pragma unroll
   for (int r = 0; r < 2; ++r) {
-    const int64_t o = ((int64_t)min(t0 + r, A.Q - 1) * nseg + seg) * A.seg_cap;
+    const int64_t o = MODE == kPairRepair ? 0 : ((int64_t)min(t0 + r, A.Q - 1) * nseg + seg) * A.seg_cap;
     segk[r] = __builtin_amdgcn_make_buffer_rsrc((void*)(A.cand_key + o), (short)0, (int)(seg_cap * 4u), 0x00020000);
     segi[r] = __builtin_amdgcn_make_buffer_rsrc((void*)(A.cand_idx + o), (short)0, (int)(seg_cap * 4u), 0x00020000);
   }
@@ -259,6 +292,12 @@ __global__ __launch_bounds__(kWG, 2) void k_prefill_pair(PrefillArgs A) {
       if (MODE == kPairDense) continue;
       if (MODE == kPairControl) {
         csum[r] += valid ? sc[r] : 0.f;
+        continue;
+      }
+      if (MODE == kPairRepair) {
+        const uint32_t key = f2key(sc[r]);
+        if (valid) A.scratch[(int64_t)slot[r] * A.rstride + (my - rs[r])] = key;
+        hist_add(s_rhist[r], key >> 24, valid);
         continue;
       }
       const bool take = valid && sc[r] >= tr[r];
@@ -362,6 +401,14 @@ __global__ __launch_bounds__(kWG, 2) void k_prefill_pair(PrefillArgs A) {
       for (int o = 32; o > 0; o >>= 1) m += __shfl_xor(m, o, 64);
       if (lane == 0 && t0 + r < A.Q) A.segn[4 * ((int64_t)(t0 + r) * nseg + seg) + 3] = __float_as_uint(m);
     }
+  } else if constexpr (MODE == kPairRepair) {
+    // the pair's histograms into the rows' first digit histograms
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const uint32_t h = s_rhist[r][tid];
+      if (h && t_of[r] >= 0) atomicAdd(&A.rhist[(int64_t)slot[r] * 4 * 256 + tid], h);
+    }
   } else if constexpr (MODE != kPairDense) {
     // publish this wave's segment: entries stored, the order-preserving key of
     // the largest dropped candidate (0: none dropped; a candidate is never
@@ -381,7 +428,7 @@ __global__ __launch_bounds__(kWG, 2) void k_prefill_pair(PrefillArgs A) {
             make_uint4(min(cnt[r], seg_cap), dk, (uint32_t)fdrop[r], 0u);
     }
   }
-  if (A.clock && lane == 0) {
+  if (MODE != kPairRepair && A.clock && lane == 0) {
     atomicAdd(reinterpret_cast<unsigned long long*>(A.clock), (unsigned long long)(__builtin_amdgcn_s_memtime() - clk0));
     atomicAdd(reinterpret_cast<unsigned long long*>(A.clock + 1),
               (unsigned long long)(__builtin_amdgcn_s_memrealtime() - rtc0));
@@ -483,7 +530,7 @@ __global__ __launch_bounds__(kWG) void k_prefill_select(PrefillArgs A) {
     if (A.row_status) A.row_status[t] = ok ? IDX_ROW_FAST : drop ? IDX_ROW_OVERFLOW : IDX_ROW_UNDERFLOW;
     if (ok) {
       atomicAdd(&stats[kStFast], 1u);
-      if (n > (uint32_t)A.lds_cap) atomicAdd(&stats[kStSpilled], 1u);
+      if (n > (uint32_t)kManyCands) atomicAdd(&stats[kStMany], 1u);
       if (L <= A.K) atomicAdd(&stats[kStTrivial], 1u);
     } else {
       const uint32_t f = atomicAdd(&A.ctrl[kCtrlFail], 1u);
@@ -530,51 +577,16 @@ __device__ RepairSel repair_replay(const uint32_t* rh, int L, int kr, int npass,
   return r;
 }
 
-// Rescore chunk c of slotted failed row f into its scratch row and add the
-// chunk's top-byte histogram to the row's first histogram.  Failures beyond
-// the slots are then repaired whole, one per fallback workgroup.
-__global__ __launch_bounds__(kWG) void k_prefill_repair_score(PrefillArgs A) {
+// Failures beyond the repair slots (the slotted ones are rescored by the
+// main kernel's repair mode) are repaired whole, one per fallback
+// workgroup.
+__global__ __launch_bounds__(kWG) void k_prefill_repair_fallback(PrefillArgs A) {
   __shared__ SelShared sh;
   __shared__ uint8_t s_qprep[kWaves][kUTerms * kD];
   const int tid = threadIdx.x;
   const uint32_t lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const uint32_t n_fail = __atomic_load_n(&A.ctrl[kCtrlFail], __ATOMIC_RELAXED);
-  const uint32_t n_slot = min(n_fail, (uint32_t)A.rslots);
-  const int ntiles = (A.N + 63) >> 6;
-  const int cmax = (ntiles + kRepairChunkTiles - 1) / kRepairChunkTiles;
-  const KeyBuf kbuf = make_keybuf(A.k, A.k_scale, A.N);
-  const rsrc_t ktb = __builtin_amdgcn_make_buffer_rsrc((void*)A.kt, (short)0, ntiles * kTile * kD, 0x00020000);
-  const int64_t items = (int64_t)n_slot * cmax;
-#pragma unroll 1
-  for (int64_t i = blockIdx.x; i < items; i += gridDim.x) {
-    const int f = (int)(i / cmax), c = (int)(i % cmax);
-    const int t = A.fail_list[f];
-    const int s0 = A.row_start[t], s1 = A.row_end[t];
-    const int tile_lo = (s0 >> 6) + c * kRepairChunkTiles;
-    const int tile_hi = min((s1 + 63) >> 6, tile_lo + kRepairChunkTiles);
-    if (tile_lo >= tile_hi) continue;
-    sh.hist[tid] = 0u;
-    QOp qo;
-    prepare_q(qo, A.q, A.q_scale, A.w, t, lane, s_qprep[wave], t & 1);
-    __syncthreads();
-    uint32_t* scratch = A.scratch + (int64_t)f * A.rstride;
-#pragma unroll 1
-    for (int tile = tile_lo + wave; tile < tile_hi; tile += kWaves) {
-      KeyTile kt;
-      load_tile_relaid(kt, ktb, kbuf.ks, tile, lane);
-      const float sc = tile_score(qo, kt);
-      const int my = (tile << 6) + (int)lane;
-      const bool valid = my >= s0 && my < s1;
-      const uint32_t key = f2key(sc);
-      if (valid) scratch[my - s0] = key;
-      hist_add(sh.hist, key >> 24, valid);
-    }
-    __syncthreads();
-    const uint32_t h = sh.hist[tid];
-    if (h) atomicAdd(&A.rhist[(int64_t)f * 4 * 256 + tid], h);
-    __syncthreads();
-  }
   if (blockIdx.x >= kRepairFallback) return;
   uint32_t* own = A.scratch + ((int64_t)A.rslots + blockIdx.x) * A.rstride;
   uint32_t* stats = stat_copy(A.ctrl, blockIdx.x);
@@ -801,7 +813,11 @@ int launch_prefill(const PrefillArgs& A, hipStream_t stream) {
   }
   hipLaunchKernelGGL(k_prefill_select, dim3(A.Q), dim3(kWG), 0, stream, A);
   if (A.keep_all) return hipGetLastError() == hipSuccess ? IDX_OK : IDX_EHIP;  // nothing can need repair
-  hipLaunchKernelGGL(k_prefill_repair_score, dim3(kRepairGrid), dim3(kWG), 0, stream, A);
+  // the slotted failures rescored two per workgroup: enough workgroups for
+  // every slot pair, at least two per CU for few failures
+  const unsigned rgrid = (unsigned)max(512, (A.rslots + 1) / 2);
+  hipLaunchKernelGGL(k_prefill_pair<kPairRepair>, dim3(rgrid), dim3(kWG), 0, stream, A);
+  if (A.rslots < A.Q) hipLaunchKernelGGL(k_prefill_repair_fallback, dim3(kRepairFallback), dim3(kWG), 0, stream, A);
   hipLaunchKernelGGL(k_prefill_repair_pass<1>, dim3(kRepairGrid), dim3(kWG), 0, stream, A);
   hipLaunchKernelGGL(k_prefill_repair_pass<2>, dim3(kRepairGrid), dim3(kWG), 0, stream, A);
   hipLaunchKernelGGL(k_prefill_repair_pass<3>, dim3(kRepairGrid), dim3(kWG), 0, stream, A);

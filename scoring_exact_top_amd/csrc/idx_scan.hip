@@ -204,7 +204,8 @@ int scan_bf16(const uint16_t* q, const float* w, const uint16_t* k, const int32_
   if (B > kMaxGridY) return IDX_EUNSUPPORTED;  // streams index the grid's y dimension
   // one stream's keys per buffer resource (the last tile's rows included)
   if (((int64_t)N + kTile) * kD * 2 > 0x7fffffffLL) return IDX_EUNSUPPORTED;
-  if (opts && (opts->force_tau || opts->lds_cap || opts->spill_cap || opts->main_reps < 0 || opts->main_reps > 1000))
+  if (opts && (opts->force_tau || opts->cand_cap || opts->row_status || opts->clock_out || opts->math_only ||
+               opts->main_reps < 0 || opts->main_reps > 1000))
     return IDX_EINVAL;
   if (B == 0) return IDX_OK;
   if (!q || !w || !k || !lens || !out_idx) return IDX_EINVAL;

@@ -67,24 +67,24 @@ def test_forced_underflow_goes_to_repair():
 def test_forced_overflow_goes_to_repair():
     case = synth.random_case("over", 12, 9000, seed=24, K=512, min_len=3000)
     log("case", case.name)
-    r = run_prefill(case, force_tau=float("-inf"), lds_cap=1024, spill_cap=-1)
+    r = run_prefill(case, force_tau=float("-inf"), cand_cap=1024)
     assert r["stats"]["overflow"] == case.Q and r["stats"]["repaired"] == case.Q
     check_prefill_rows(case, r["out"], np.arange(case.Q))
 
 
-def test_spill_area_is_merged():
+def test_rows_keeping_every_key_merge_all_segments():
     """Rows that keep every key (threshold -inf, L <= 8192, the default
-    capacity) hold more candidates than the on-chip share (4096): the
-    certificate still holds for every row and the selection merges all of
-    the row's segments.  Row 0 spans 8192 keys from an unaligned start, the
-    most tiles one row can put on a segment."""
-    case = synth.random_case("spill", 10, 9000, seed=25, K=700, min_len=4200, max_len=8192)
+    capacity) hold more than 4096 candidates, spread over all their
+    segments: the certificate holds for every row and the selection merges
+    every segment.  Row 0 spans 8192 keys from an unaligned start, the most
+    tiles one row can put on a segment."""
+    case = synth.random_case("keep_all", 10, 9000, seed=25, K=700, min_len=4200, max_len=8192)
     case.row_start[0], case.row_end[0] = 1, 8193
     log("case", case.name)
     r = run_prefill(case, force_tau=float("-inf"), scores=True)
     st = r["stats"]
     log("stats", st)
-    assert st["spilled"] == case.Q and st["fast_ok"] == case.Q and st["repaired"] == 0, st
+    assert st["many_cands"] == case.Q and st["fast_ok"] == case.Q and st["repaired"] == 0, st
     check_prefill_rows(case, r["out"], np.arange(case.Q))
 
 
@@ -145,7 +145,7 @@ def test_massive_ties_take_the_fast_path(e4m3):
     pos = np.arange(163840 - 8, 163840, dtype=np.int64)
     case = synth.causal_case("ties_fast", 8, 163840, seed=29, key_mode="ties16", positions=pos)
     log("case", case.name)
-    r = run_prefill(case, scores=True, lds_cap=2048, spill_cap=2048)
+    r = run_prefill(case, scores=True, cand_cap=4096)
     st = r["stats"]
     log("stats", st)
     assert st["fast_ok"] == case.Q and st["repaired"] == 0, st
