@@ -61,6 +61,15 @@ __host__ __device__ inline int prefill_seg_cap(int S) {
 constexpr int kRepairChunk = 4096;
 constexpr int kRepairChunkTiles = kRepairChunk / 64;
 constexpr int kRepairGrid = 256;  // one workgroup per CU; items are strided over the grid
+constexpr int kRepairPassGrid = 1024;  // digit passes, tie count and emit: four workgroups per CU
+
+// Words kept per slotted repair row (PrefillArgs::rrow): the emit's output
+// counters, then two groups of four holding the row's selection state
+// after an odd and after an even number of digits (prefix, mask, rem,
+// done: every key with (key & mask) > prefix is taken, and rem more among
+// those equal to it; done: the boundary group is taken whole).
+constexpr int kRowGt = 0, kRowEq = 1, kRowState = 4;
+constexpr int kRowWords = 12;
 constexpr int kRepairFallback = 256;
 constexpr int64_t kRepairScratchKeys = (int64_t)1 << 28;  // 1 GiB of scores
 
@@ -130,7 +139,7 @@ struct PrefillArgs {
   uint32_t* ctrl;       // kCtrlWords
   uint32_t* scratch;    // [repair_rows][repair_stride(N)] repair scores (order-preserving keys)
   uint32_t* rhist;      // [rslots][4][256] digit histograms of each slotted repair row
-  uint32_t* rcnt;       // [rslots][2] output counters of each slotted repair row
+  uint32_t* rrow;       // [rslots][kRowWords] counters and selection state of each slotted repair row
   uint32_t* reqc;       // [rslots][ceil(N/kRepairChunk)] keys tied at the K-th score per chunk
   int32_t rslots;
   int64_t rstride;

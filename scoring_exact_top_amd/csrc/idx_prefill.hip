@@ -37,7 +37,7 @@ __global__ __launch_bounds__(kWG) void k_relayout_keys(PrefillArgs A) {
       }
     } else {  // the main kernel writes the thresholds; the repair state starts at zero
       for (int64_t i = chunk; i < (int64_t)A.rslots * 1024; i += stride) A.rhist[i] = 0u;
-      for (int64_t i = chunk; i < (int64_t)A.rslots * 2; i += stride) A.rcnt[i] = 0u;
+      for (int64_t i = chunk; i < (int64_t)A.rslots * kRowWords; i += stride) A.rrow[i] = 0u;
     }
   }
 }
@@ -53,7 +53,7 @@ __global__ __launch_bounds__(kWG) void k_prefill_tau(PrefillArgs A) {
   const int64_t i0 = (int64_t)blockIdx.x * kWG + threadIdx.x, stride = (int64_t)gridDim.x * kWG;
   if (blockIdx.x == 0) clear_ctrl(A.ctrl, threadIdx.x);
   for (int64_t i = i0; i < (int64_t)A.rslots * 1024; i += stride) A.rhist[i] = 0u;
-  for (int64_t i = i0; i < (int64_t)A.rslots * 2; i += stride) A.rcnt[i] = 0u;
+  for (int64_t i = i0; i < (int64_t)A.rslots * kRowWords; i += stride) A.rrow[i] = 0u;
   for (int64_t t = i0; t < A.Q; t += stride) {
     const int s = A.row_start[t], e = A.row_end[t];
     A.tau[t] = !(s >= 0 && s <= e && e <= A.N) ? INFINITY : A.force_tau ? A.tau_value : -INFINITY;
@@ -543,38 +543,74 @@ __global__ __launch_bounds__(kWG) void k_prefill_select(PrefillArgs A) {
 // ------------------------------------------------------------------ repair
 //
 // Exact repair of rows the certificate rejected, split over the whole chip:
-// the first rslots failed rows each get a scratch slot, and every kernel
-// below walks work items (f, c) = (failed row, chunk of kRepairChunk
-// positions).  The radix select runs one 8-bit digit per launch: the digit
-// histogram of a row is summed in device memory over its chunks, and each
-// work item replays the finished digits (find_bucket over the stored
-// histograms) to know the prefix it filters by.
+// the first rslots failed rows each get a scratch slot, and the kernels
+// below walk work items (f, c) = (failed row, chunk of kRepairChunk
+// positions), each workgroup a contiguous run of them, so that its items
+// mostly share a row.  The radix select runs one 8-bit digit per launch:
+// the digit histogram of a row is summed in device memory over its chunks;
+// the next launch advances the row's selection state by that digit (once
+// per row and workgroup, from the state the launch before stored) and its
+// chunk-0 item stores the result for the launch after.  The stored states
+// alternate between two word groups, so a launch never overwrites the one
+// it reads.
 
-// Selection state after the first `npass` digits of slot f.  done: the
-// boundary bucket is taken whole, or the row has no more than kr keys.
 struct RepairSel {
   uint32_t prefix, mask;
   int rem;
   bool done;
 };
 
-__device__ RepairSel repair_replay(const uint32_t* rh, int L, int kr, int npass, SelShared& sh, int tid) {
-  RepairSel r{0u, 0u, kr, L <= kr};
-#pragma unroll 1
-  for (int p = 0; p < npass && !r.done; ++p) {
-    sh.hist[tid] = rh[p * 256 + tid];
+__device__ __forceinline__ RepairSel load_state(const uint32_t* rw, int buf) {
+  const uint32_t* w = rw + kRowState + 4 * buf;
+  return RepairSel{w[0], w[1], (int)w[2], w[3] != 0u};
+}
+
+__device__ __forceinline__ void store_state(uint32_t* rw, int buf, const RepairSel& s) {
+  *reinterpret_cast<uint4*>(rw + kRowState + 4 * buf) = make_uint4(s.prefix, s.mask, (uint32_t)s.rem, s.done ? 1u : 0u);
+}
+
+// A chunk kernel's current row: its id, range, keys kept and selection state.
+struct RepairRow {
+  int f, t, s0, L, kr;
+  RepairSel sel;
+};
+
+// Load slot f's row and its selection state after `digits` digits (1..4):
+// the state after digits-1 (the initial one for digits == 1, else as the
+// previous launch stored it) advanced by that digit's complete histogram.
+// Whole workgroup calls.
+__device__ __forceinline__ void repair_row_ids(RepairRow& row, const PrefillArgs& A, int f) {
+  row.f = f;
+  row.t = A.fail_list[f];
+  row.s0 = A.row_start[row.t];
+  row.L = A.row_end[row.t] - row.s0;
+  row.kr = min(A.K, row.L);
+}
+
+__device__ void repair_row_at(RepairRow& row, const PrefillArgs& A, int f, int digits, SelShared& sh, int tid) {
+  repair_row_ids(row, A, f);
+  const uint32_t* rw = A.rrow + (int64_t)f * kRowWords;
+  RepairSel s = digits == 1 ? RepairSel{0u, 0u, row.kr, row.L <= row.kr} : load_state(rw, (digits - 1) & 1);
+  if (!s.done) {
+    __syncthreads();  // the previous item's reads of sh are done
+    sh.hist[tid] = A.rhist[((int64_t)f * 4 + digits - 1) * 256 + tid];
     __syncthreads();
-    find_bucket(sh, r.rem, tid);
+    find_bucket(sh, s.rem, tid);
     __syncthreads();
-    const uint32_t b = sh.bucket, above = sh.above, inb = sh.inbucket;
-    __syncthreads();
-    const int shift = 24 - 8 * p;
-    r.prefix |= b << shift;
-    r.mask |= 0xFFu << shift;
-    r.rem -= (int)above;
-    r.done = (int)inb == r.rem;
+    const int shift = 32 - 8 * digits;
+    s.prefix |= sh.bucket << shift;
+    s.mask |= 0xFFu << shift;
+    s.rem -= (int)sh.above;
+    s.done = (int)sh.inbucket == s.rem;
   }
-  return r;
+  row.sel = s;
+}
+
+// Contiguous run of the n items for this workgroup.
+__device__ __forceinline__ void item_run(int64_t n, int64_t& i0, int64_t& i1) {
+  const int64_t per = (n + gridDim.x - 1) / gridDim.x;
+  i0 = min(n, per * (int64_t)blockIdx.x);
+  i1 = min(n, i0 + per);
 }
 
 // Failures beyond the repair slots (the slotted ones are rescored by the
@@ -623,37 +659,39 @@ __device__ __forceinline__ void load_chunk(ChunkKeys& ck, const uint32_t* row, i
 
 __device__ __forceinline__ int chunk_pos(const ChunkKeys& ck, int j) { return ck.base + (j >> 2) * 4 * kWG + (j & 3); }
 
-// Digit pass P (1..3) over the slotted failed rows that are still open.
+// Digit pass P (1..3) over the slotted failed rows that are still open:
+// the histogram of digit P among the keys that share the boundary prefix
+// of the first P digits.
 template <int P>
 __global__ __launch_bounds__(kWG) void k_prefill_repair_pass(PrefillArgs A) {
   __shared__ SelShared sh;
   const int tid = threadIdx.x;
   const uint32_t n_slot = min(__atomic_load_n(&A.ctrl[kCtrlFail], __ATOMIC_RELAXED), (uint32_t)A.rslots);
   const int cmax = (A.N + kRepairChunk - 1) / kRepairChunk;
-  const int64_t items = (int64_t)n_slot * cmax;
+  int64_t i0, i1;
+  item_run((int64_t)n_slot * cmax, i0, i1);
+  RepairRow row;
+  row.f = -1;
 #pragma unroll 1
-  for (int64_t i = blockIdx.x; i < items; i += gridDim.x) {
+  for (int64_t i = i0; i < i1; ++i) {
     const int f = (int)(i / cmax), c = (int)(i % cmax);
-    const int t = A.fail_list[f];
-    const int L = A.row_end[t] - A.row_start[t];
-    if (c * kRepairChunk >= L) continue;
-    const uint32_t* rh = A.rhist + (int64_t)f * 4 * 256;
-    const RepairSel rs = repair_replay(rh, L, min(A.K, L), P, sh, tid);
-    if (rs.done) continue;
+    if (f != row.f) repair_row_at(row, A, f, P, sh, tid);
+    if (c == 0 && tid == 0) store_state(A.rrow + (int64_t)f * kRowWords, P & 1, row.sel);
+    if (row.sel.done || c * kRepairChunk >= row.L) continue;
     ChunkKeys ck;
-    load_chunk(ck, A.scratch + (int64_t)f * A.rstride, c, L, tid);
+    load_chunk(ck, A.scratch + (int64_t)f * A.rstride, c, row.L, tid);
+    __syncthreads();  // the previous item's reads of sh are done
     sh.hist[tid] = 0u;
     __syncthreads();
     constexpr int shift = 24 - 8 * P;
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
-      const bool v = chunk_pos(ck, j) < L && (ck.v[j] & rs.mask) == rs.prefix;
+      const bool v = chunk_pos(ck, j) < row.L && (ck.v[j] & row.sel.mask) == row.sel.prefix;
       hist_add(sh.hist, (ck.v[j] >> shift) & 255u, v);
     }
     __syncthreads();
     const uint32_t h = sh.hist[tid];
     if (h) atomicAdd(&A.rhist[((int64_t)f * 4 + P) * 256 + tid], h);
-    __syncthreads();
   }
 }
 
@@ -665,20 +703,21 @@ __global__ __launch_bounds__(kWG) void k_prefill_repair_ties(PrefillArgs A) {
   const int tid = threadIdx.x;
   const uint32_t n_slot = min(__atomic_load_n(&A.ctrl[kCtrlFail], __ATOMIC_RELAXED), (uint32_t)A.rslots);
   const int cmax = (A.N + kRepairChunk - 1) / kRepairChunk;
-  const int64_t items = (int64_t)n_slot * cmax;
+  int64_t i0, i1;
+  item_run((int64_t)n_slot * cmax, i0, i1);
+  RepairRow row;
+  row.f = -1;
 #pragma unroll 1
-  for (int64_t i = blockIdx.x; i < items; i += gridDim.x) {
+  for (int64_t i = i0; i < i1; ++i) {
     const int f = (int)(i / cmax), c = (int)(i % cmax);
-    const int t = A.fail_list[f];
-    const int L = A.row_end[t] - A.row_start[t];
-    if (c * kRepairChunk >= L) continue;
-    const RepairSel rs = repair_replay(A.rhist + (int64_t)f * 4 * 256, L, min(A.K, L), 4, sh, tid);
-    if (rs.done) continue;
+    if (f != row.f) repair_row_at(row, A, f, 4, sh, tid);
+    if (c == 0 && tid == 0) store_state(A.rrow + (int64_t)f * kRowWords, 0, row.sel);
+    if (row.sel.done || c * kRepairChunk >= row.L) continue;
     ChunkKeys ck;
-    load_chunk(ck, A.scratch + (int64_t)f * A.rstride, c, L, tid);
+    load_chunk(ck, A.scratch + (int64_t)f * A.rstride, c, row.L, tid);
     uint32_t m = 0u;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) m += (chunk_pos(ck, j) < L && ck.v[j] == rs.prefix) ? 1u : 0u;
+    for (int j = 0; j < 16; ++j) m += (chunk_pos(ck, j) < row.L && ck.v[j] == row.sel.prefix) ? 1u : 0u;
     uint32_t tot;
     block_exclusive_scan(m, sh, tid, tot);
     if (tid == 0) A.reqc[(int64_t)f * cmax + c] = tot;
@@ -693,22 +732,27 @@ __global__ __launch_bounds__(kWG) void k_prefill_repair_emit(PrefillArgs A) {
   const int tid = threadIdx.x;
   const uint32_t n_slot = min(__atomic_load_n(&A.ctrl[kCtrlFail], __ATOMIC_RELAXED), (uint32_t)A.rslots);
   const int cmax = (A.N + kRepairChunk - 1) / kRepairChunk;
-  const int64_t items = (int64_t)n_slot * cmax;
+  int64_t i0, i1;
+  item_run((int64_t)n_slot * cmax, i0, i1);
   uint32_t* stats = stat_copy(A.ctrl, blockIdx.x);
+  RepairRow row;
+  row.f = -1;
 #pragma unroll 1
-  for (int64_t i = blockIdx.x; i < items; i += gridDim.x) {
+  for (int64_t i = i0; i < i1; ++i) {
     const int f = (int)(i / cmax), c = (int)(i % cmax);
-    const int t = A.fail_list[f];
-    const int s0 = A.row_start[t];
-    const int L = A.row_end[t] - s0;
-    const int kr = min(A.K, L);
-    int32_t* out = A.out + (int64_t)t * A.K;
+    uint32_t* rw = A.rrow + (int64_t)f * kRowWords;
+    if (f != row.f) {
+      repair_row_ids(row, A, f);
+      row.sel = load_state(rw, 0);  // after all four digits
+    }
+    const int s0 = row.s0, L = row.L, kr = row.kr;
+    const RepairSel& rs = row.sel;
+    int32_t* out = A.out + (int64_t)row.t * A.K;
     if (c == 0) {
       for (int j = kr + tid; j < A.K; j += kWG) out[j] = -1;
       if (tid == 0) atomicAdd(&stats[kStRepaired], 1u);
     }
     if (c * kRepairChunk >= L) continue;
-    const RepairSel rs = repair_replay(A.rhist + (int64_t)f * 4 * 256, L, kr, 4, sh, tid);
     ChunkKeys ck;
     load_chunk(ck, A.scratch + (int64_t)f * A.rstride, c, L, tid);
     // count this chunk's winners in LDS, then reserve their output range
@@ -729,8 +773,8 @@ __global__ __launch_bounds__(kWG) void k_prefill_repair_emit(PrefillArgs A) {
     if (ne) pe = atomicAdd(&sh.eq_count, ne);
     __syncthreads();
     if (tid == 0) {
-      sh.pad0 = sh.gt_count ? atomicAdd(&A.rcnt[2 * f + 0], sh.gt_count) : 0u;
-      sh.pad1 = sh.eq_count ? atomicAdd(&A.rcnt[2 * f + 1], sh.eq_count) : 0u;
+      sh.pad0 = sh.gt_count ? atomicAdd(&rw[kRowGt], sh.gt_count) : 0u;
+      sh.pad1 = sh.eq_count ? atomicAdd(&rw[kRowEq], sh.eq_count) : 0u;
     }
     __syncthreads();
     pg += sh.pad0;
@@ -818,11 +862,11 @@ int launch_prefill(const PrefillArgs& A, hipStream_t stream) {
   const unsigned rgrid = (unsigned)max(512, (A.rslots + 1) / 2);
   hipLaunchKernelGGL(k_prefill_pair<kPairRepair>, dim3(rgrid), dim3(kWG), 0, stream, A);
   if (A.rslots < A.Q) hipLaunchKernelGGL(k_prefill_repair_fallback, dim3(kRepairFallback), dim3(kWG), 0, stream, A);
-  hipLaunchKernelGGL(k_prefill_repair_pass<1>, dim3(kRepairGrid), dim3(kWG), 0, stream, A);
-  hipLaunchKernelGGL(k_prefill_repair_pass<2>, dim3(kRepairGrid), dim3(kWG), 0, stream, A);
-  hipLaunchKernelGGL(k_prefill_repair_pass<3>, dim3(kRepairGrid), dim3(kWG), 0, stream, A);
-  hipLaunchKernelGGL(k_prefill_repair_ties, dim3(kRepairGrid), dim3(kWG), 0, stream, A);
-  hipLaunchKernelGGL(k_prefill_repair_emit, dim3(kRepairGrid), dim3(kWG), 0, stream, A);
+  hipLaunchKernelGGL(k_prefill_repair_pass<1>, dim3(kRepairPassGrid), dim3(kWG), 0, stream, A);
+  hipLaunchKernelGGL(k_prefill_repair_pass<2>, dim3(kRepairPassGrid), dim3(kWG), 0, stream, A);
+  hipLaunchKernelGGL(k_prefill_repair_pass<3>, dim3(kRepairPassGrid), dim3(kWG), 0, stream, A);
+  hipLaunchKernelGGL(k_prefill_repair_ties, dim3(kRepairPassGrid), dim3(kWG), 0, stream, A);
+  hipLaunchKernelGGL(k_prefill_repair_emit, dim3(kRepairPassGrid), dim3(kWG), 0, stream, A);
   return hipGetLastError() == hipSuccess ? IDX_OK : IDX_EHIP;
 }
 
