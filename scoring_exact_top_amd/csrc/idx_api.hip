@@ -23,8 +23,9 @@ static PrefillLayout prefill_layout(int32_t Q, int32_t N, bool unfused = false) 
   L.ctrl = o; o = align256(o + sizeof(uint32_t) * kCtrlWords);
   L.tau = o; o = align256(o + sizeof(float) * (size_t)Q);
   L.fail = o; o = align256(o + sizeof(int32_t) * (size_t)Q);
-  const size_t nseg = (size_t)kWaves * prefill_split(Q);
-  const size_t cand = (size_t)Q * nseg * (size_t)prefill_seg_cap(prefill_split(Q));
+  const WalkGeom g = prefill_geom(Q);
+  const size_t nseg = (size_t)g.nseg;
+  const size_t cand = (size_t)Q * nseg * (size_t)prefill_seg_cap(g.nseg);
   L.skey = o; o = align256(o + sizeof(uint32_t) * cand);
   L.cidx = o; o = align256(o + sizeof(int32_t) * cand);
   L.segn = o; o = align256(o + 4 * sizeof(uint32_t) * (size_t)Q * nseg);
@@ -67,8 +68,11 @@ static int prefill_common(const uint8_t* q, const float* q_scale, const uint8_t*
   A.cand_key = reinterpret_cast<uint32_t*>(ws + L.skey);
   A.cand_idx = reinterpret_cast<int32_t*>(ws + L.cidx);
   A.segn = reinterpret_cast<uint32_t*>(ws + L.segn);
-  A.S = prefill_split(Q);
-  A.seg_cap = prefill_seg_cap(A.S);
+  const WalkGeom g = prefill_geom(Q);
+  A.S = g.S;
+  A.nseg = g.nseg;
+  A.shared = g.shared;
+  A.seg_cap = prefill_seg_cap(g.nseg);
   A.scratch = reinterpret_cast<uint32_t*>(ws + L.scratch);
   A.rhist = reinterpret_cast<uint32_t*>(ws + L.rhist);
   A.rrow = reinterpret_cast<uint32_t*>(ws + L.rrow);
@@ -95,7 +99,7 @@ static int prefill_common(const uint8_t* q, const float* q_scale, const uint8_t*
   }
   // usable entries per segment: the full segment unless a test knob shrank
   // the capacity, then an even share of it
-  const int share = A.cand_cap / (kWaves * A.S);
+  const int share = A.cand_cap / A.nseg;
   A.seg_eff = (A.cand_cap >= kCandCap || share > A.seg_cap) ? A.seg_cap : share;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (unfused) {

@@ -35,6 +35,8 @@ constexpr int kManyCands = 4096;  // rows keeping more are counted (idx_topk_sta
 constexpr int kMaxSplit = 8;
 constexpr int kSelRegs = 40;  // keys per thread of the select kernel, all S <= kMaxSplit
 
+constexpr int kMaxSeg = kWaves * kMaxSplit;  // candidate segments per row, at most
+
 // Splits of the main kernel for Q rows: at least 512 workgroups (two per
 // CU) when possible.
 __host__ __device__ inline int prefill_split(int rows) {
@@ -44,11 +46,37 @@ __host__ __device__ inline int prefill_split(int rows) {
   return s;
 }
 
-// Entries of one (split, wave) segment for S splits: the larger of an even
-// share of kCandCap and the tiles an unaligned kCandCap-key row puts on one
-// segment (such a row spans kCandCap/64 + 1 tiles).
-__host__ __device__ inline int prefill_seg_cap(int S) {
-  const int nseg = kWaves * S;
+// Geometry of the main kernel's walk.  With kSharedMinRows rows or more the
+// walk is shared: a workgroup takes kSharedRows rows (a pair per wave), each
+// tile is staged once in LDS for all four waves, and a row's candidates of
+// one split go to one segment (nseg = S).  Fewer rows keep one pair per
+// workgroup with the tiles split over its waves (nseg = kWaves * S), which
+// needs four times fewer splits for the same number of workgroups: every
+// split samples its rows' thresholds again, and at four or more splits that
+// repeated sampling cost more than the shared tiles saved (1024 rows of
+// 163840 keys: 0.534 against 0.531 ms; 4096 rows: 3.26 against 3.46 ms).
+constexpr int kSharedRows = 2 * kWaves;
+constexpr int kSharedMinRows = 2048;
+
+struct WalkGeom {
+  int shared, S, nseg;
+};
+
+__host__ __device__ inline WalkGeom prefill_geom(int rows) {
+  if (rows >= kSharedMinRows) {
+    const int groups = (rows + kSharedRows - 1) / kSharedRows;
+    int s = 1;
+    while (s < kMaxSeg && groups * s < 512) s *= 2;
+    return WalkGeom{1, s, s};
+  }
+  const int s = prefill_split(rows);
+  return WalkGeom{0, s, kWaves * s};
+}
+
+// Entries of one candidate segment for nseg segments per row: the larger of
+// an even share of kCandCap and the tiles an unaligned kCandCap-key row
+// puts on one segment (such a row spans kCandCap/64 + 1 tiles).
+__host__ __device__ inline int prefill_seg_cap(int nseg) {
   const int share = kCandCap / nseg;
   const int tiles = (kCandCap / 64 + 1 + nseg - 1) / nseg;
   return share > tiles * 64 ? share : tiles * 64;
@@ -134,6 +162,7 @@ struct PrefillArgs {
   uint32_t* segn;       // [Q][kWaves*S][4]: entries stored, key of the largest dropped candidate
                         // (0: none), position of the first dropped one, unused
   int32_t S, seg_cap, seg_eff;  // splits, segment stride, usable entries per segment
+  int32_t shared, nseg;         // shared walk (kSharedRows rows per workgroup); segments per row
   int32_t cand_cap;  // candidates stored per row (the certificate's capacity)
   int32_t* fail_list;   // [Q]
   uint32_t* ctrl;       // kCtrlWords

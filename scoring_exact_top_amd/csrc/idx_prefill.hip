@@ -130,8 +130,9 @@ __device__ __forceinline__ void pair_scores(const QOp2& qo, const KeyTile& kt, f
   s1 = reduce_scatter4(q1[0], q1[1], q1[2], q1[3]) * kt.ks;
 }
 
-template <int MODE>
+template <int MODE, bool SH = false>
 __global__ __launch_bounds__(kWG, 2) void k_prefill_pair(PrefillArgs A) {
+  static_assert(!SH || MODE != kPairRepair, "repair mode walks one pair per workgroup");
   __shared__ uint8_t s_qprep[kWaves][2 * kUTerms * kD];
   // optional clock probe: this wave's shader-clock cycles and constant-rate
   // wall-clock ticks from its start to its end, summed over all waves
@@ -159,13 +160,16 @@ __global__ __launch_bounds__(kWG, 2) void k_prefill_pair(PrefillArgs A) {
     t_of[1] = slot[1] < n_slot ? A.fail_list[slot[1]] : -1;
   } else {
     nsplit = A.S;
-    split = blockIdx.x % A.S;  // which share of the pair's tiles
-    t_of[0] = 2 * (blockIdx.x / A.S);
-    t_of[1] = t_of[0] + 1 < A.Q ? t_of[0] + 1 : -1;
+    split = blockIdx.x % A.S;  // which share of the rows' tiles
+    const int tb = SH ? kWaves * 2 * (blockIdx.x / A.S) + 2 * wave : 2 * (blockIdx.x / A.S);
+    t_of[0] = tb < A.Q ? tb : -1;
+    t_of[1] = tb + 1 < A.Q ? tb + 1 : -1;
   }
-  const int t0 = t_of[0];
-  const int seg = split * kWaves + wave;        // this wave's segment of each row
-  const int nseg = kWaves * nsplit;
+  const int tq = t_of[0] >= 0 ? t_of[0] : A.Q - 1;  // a real row for loads of an absent pair
+  // this wave's segment of each row: one per split when the waves share
+  // tiles (each walks all of them for its own pair), else one per wave
+  const int seg = SH ? split : split * kWaves + wave;
+  const int nseg = SH ? nsplit : kWaves * nsplit;
 
   int rs[2], re[2];
   float tr[2];
@@ -187,10 +191,23 @@ __global__ __launch_bounds__(kWG, 2) void k_prefill_pair(PrefillArgs A) {
     s_rhist[0][tid] = 0u;
     s_rhist[1][tid] = 0u;
   }
+  __shared__ int s_lohi[kWaves][2];
+  if (SH && lane == 0) {
+    s_lohi[wave][0] = lo;
+    s_lohi[wave][1] = hi;
+  }
   QOp2 qo;
-  prepare_q2(qo, A.q, A.q_scale, A.w, min(t_of[0], A.Q - 1), t_of[1] >= 0 ? t_of[1] : min(t_of[0], A.Q - 1), lane,
-             s_qprep[wave]);
+  prepare_q2(qo, A.q, A.q_scale, A.w, tq, t_of[1] >= 0 ? t_of[1] : tq, lane, s_qprep[wave]);
   __syncthreads();
+  if constexpr (SH) {  // the workgroup walks the union of its rows' ranges
+    lo = min(min(s_lohi[0][0], s_lohi[1][0]), min(s_lohi[2][0], s_lohi[3][0]));
+    hi = max(max(s_lohi[0][1], s_lohi[1][1]), max(s_lohi[2][1], s_lohi[3][1]));
+  }
+  // LDS shared by the sampler's scores and, after it, the staged key tiles
+  // of the shared walk (two 8 KiB buffers)
+  constexpr int kSampWords = (MODE == kPairFused || MODE == kPairDebug) ? (SH ? kWaves : 1) * 2 * kMaxSamples : 0;
+  constexpr int kStageWords = SH ? 2 * kTile * kD / 4 : 0;
+  __shared__ __attribute__((aligned(16))) uint32_t s_lds[kSampWords > kStageWords ? kSampWords : (kStageWords > 0 ? kStageWords : 1)];
 
   // Fused sampler ("3.2 Sampled threshold"), unless a threshold is forced:
   // the rows' thresholds are taken here, before the walk, instead of in a
@@ -199,10 +216,12 @@ __global__ __launch_bounds__(kWG, 2) void k_prefill_pair(PrefillArgs A) {
   // score the sampled keys' tiles (once for both rows when they share the
   // sample positions, as causal rows do) with the walk's arithmetic, so a
   // threshold is one of the walk's scores; wave r then selects row r's.
+  // When the waves share tiles, each wave samples its own pair alone.
   if constexpr (MODE == kPairFused || MODE == kPairDebug) {
     if (A.fuse_tau) {
-      __shared__ uint32_t s_samp[2][kMaxSamples];
-      __shared__ uint32_t s_hist[2][256];
+      uint32_t* const ss0 = s_lds + (SH ? wave : 0) * 2 * kMaxSamples;  // the rows' sampled scores
+      uint32_t* const ss1 = ss0 + kMaxSamples;
+      __shared__ uint32_t s_hist[SH ? kWaves : 2][256];
       __shared__ float s_tau[2];
       SampleGeom sg[2];
 #pragma unroll
@@ -211,15 +230,15 @@ __global__ __launch_bounds__(kWG, 2) void k_prefill_pair(PrefillArgs A) {
       const KeyBuf kbuf = make_keybuf(A.k, A.k_scale, A.N);
       const auto pass = [&](int src, int n, bool st0, bool st1) {  // samples of row src's positions
 #pragma unroll 1
-        for (int i0 = kTile * wave; i0 < n; i0 += kTile * kWaves) {
+        for (int i0 = SH ? 0 : kTile * wave; i0 < n; i0 += SH ? kTile : kTile * kWaves) {
           KeyTile kt;
           load_tile_gather(kt, kbuf, [&](int i) { return rs[src] + kSampleOffset + sg[src].stride * min(i0 + i, n - 1); },
                            lane);
           float s0, s1;
           pair_scores(qo, kt, s0, s1);
           const int i = i0 + (int)lane;
-          if (st0 && i < sg[0].n) s_samp[0][i] = f2key(s0);
-          if (st1 && i < sg[1].n) s_samp[1][i] = f2key(s1);
+          if (st0 && i < sg[0].n) ss0[i] = f2key(s0);
+          if (st1 && i < sg[1].n) ss1[i] = f2key(s1);
         }
       };
       if (sg[0].n > 0 && sg[1].n > 0 && rs[0] == rs[1] && sg[0].stride == sg[1].stride) {
@@ -228,20 +247,33 @@ __global__ __launch_bounds__(kWG, 2) void k_prefill_pair(PrefillArgs A) {
         if (sg[0].n > 0) pass(0, sg[0].n, true, false);
         if (sg[1].n > 0) pass(1, sg[1].n, false, true);
       }
-      __syncthreads();
-      if (wave < 2) {
-        const SampleGeom g = wave == 0 ? sg[0] : sg[1];
-        if (g.n > 0) {
-          const SelResult sel = wave_radix_select(SrcLds{s_samp[wave]}, g.n, g.r, s_hist[wave], lane, false);
-          if (lane == 0) s_tau[wave] = key2f(sel.prefix);
-        }
-      }
-      __syncthreads();
+      if constexpr (SH) {
+        wave_sync();
 #pragma unroll
-      for (int r = 0; r < 2; ++r) {
-        if (sg[r].n > 0) tr[r] = s_tau[r];  // else: -inf for a valid row (keeps all), +inf for an invalid one
-        if (split == 0 && tid == r && t0 + r < A.Q) A.tau[t0 + r] = tr[r];
+        for (int r = 0; r < 2; ++r) {
+          if (sg[r].n > 0) {
+            const SelResult sel = wave_radix_select(SrcLds{r == 0 ? ss0 : ss1}, sg[r].n, sg[r].r, s_hist[wave], lane, false);
+            tr[r] = key2f(sel.prefix);
+          }
+        }
+        __syncthreads();  // every wave is done with the sampler's LDS before tiles are staged there
+      } else {
+        __syncthreads();
+        if (wave < 2) {
+          const SampleGeom g = wave == 0 ? sg[0] : sg[1];
+          if (g.n > 0) {
+            const SelResult sel = wave_radix_select(SrcLds{wave == 0 ? ss0 : ss1}, g.n, g.r, s_hist[wave], lane, false);
+            if (lane == 0) s_tau[wave] = key2f(sel.prefix);
+          }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int r = 0; r < 2; ++r)
+          if (sg[r].n > 0) tr[r] = s_tau[r];  // else: -inf for a valid row (keeps all), +inf for an invalid one
       }
+#pragma unroll
+      for (int r = 0; r < 2; ++r)
+        if (split == 0 && (SH ? lane : tid) == r && t_of[r] >= 0) A.tau[t_of[r]] = tr[r];
     }
   }
 
@@ -260,7 +292,7 @@ __global__ __launch_bounds__(kWG, 2) void k_prefill_pair(PrefillArgs A) {
   rsrc_t segk[2], segi[2];
 #pragma unroll
   for (int r = 0; r < 2; ++r) {
-    const int64_t o = MODE == kPairRepair ? 0 : ((int64_t)min(t0 + r, A.Q - 1) * nseg + seg) * A.seg_cap;
+    const int64_t o = MODE == kPairRepair ? 0 : ((int64_t)(t_of[r] >= 0 ? t_of[r] : tq) * nseg + seg) * A.seg_cap;
     segk[r] = __builtin_amdgcn_make_buffer_rsrc((void*)(A.cand_key + o), (short)0, (int)(seg_cap * 4u), 0x00020000);
     segi[r] = __builtin_amdgcn_make_buffer_rsrc((void*)(A.cand_idx + o), (short)0, (int)(seg_cap * 4u), 0x00020000);
   }
@@ -288,7 +320,7 @@ __global__ __launch_bounds__(kWG, 2) void k_prefill_pair(PrefillArgs A) {
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
       const bool valid = my >= rs[r] && my < re[r];
-      if ((MODE == kPairDebug || MODE == kPairDense) && valid) A.dbg_scores[(int64_t)(t0 + r) * A.N + my] = sc[r];
+      if ((MODE == kPairDebug || MODE == kPairDense) && valid) A.dbg_scores[(int64_t)t_of[r] * A.N + my] = sc[r];
       if (MODE == kPairDense) continue;
       if (MODE == kPairControl) {
         csum[r] += valid ? sc[r] : 0.f;
@@ -378,7 +410,82 @@ __global__ __launch_bounds__(kWG, 2) void k_prefill_pair(PrefillArgs A) {
     // counter retires in order), that is for the whole next tile's keys.
     ks_cur = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(kbuf.ks, (int)lane * 4, nT * 256, 0));
   };
-  if (lo < hi) {
+  // The shared walk: the four waves score every tile of the split for
+  // their own pairs, so each tile is read from memory once per workgroup.
+  // Wave w stages blocks 2w and 2w+1 of the next tile into the free LDS
+  // buffer: its loads go out at the start of the tile and land under the
+  // tile's MFMAs; after the MFMAs it writes them, and one barrier, which
+  // waits for LDS traffic only, hands the buffer over.  The next tile's B
+  // operands are then read from LDS while the tail runs.
+  const auto tile_body_shared = [&](int T, uint8_t* nxt) {
+    const int nT = refill_tile(T + nseg, ntiles);
+    const int ntoff = nT * (kTile * kD);
+    const v4i g0 = __builtin_amdgcn_raw_buffer_load_b128(ktb, voff, ntoff + (2 * wave) * 1024, 0);
+    const v4i g1 = __builtin_amdgcn_raw_buffer_load_b128(ktb, voff, ntoff + (2 * wave + 1) * 1024, 0);
+    __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      v4f aA[4];
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+        aA[b] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qo.a[0][b], kb[c], z, 0, 0, 0, 0, 0, 0);
+      const v4f au = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qo.au, kb[c], z, 0, 0, 0, 0, 0, 0);
+      if (c > 0) q1[c - 1] = epi(qo.wh[1], qo.sh[1], aB, auB[2], auB[3]);
+#pragma unroll
+      for (int i = 0; i < 5; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+        aB[b] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qo.a[1][b], kb[c], z, 0, 0, 0, 0, 0, 0);
+      q0[c] = epi(qo.wh[0], qo.sh[0], aA, au[0], au[1]);
+      auB = au;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    __builtin_amdgcn_s_setprio(0);
+    q1[3] = epi(qo.wh[1], qo.sh[1], aB, auB[2], auB[3]);
+    *reinterpret_cast<v4i*>(nxt + (2 * wave) * 1024 + voff) = g0;
+    *reinterpret_cast<v4i*>(nxt + (2 * wave + 1) * 1024 + voff) = g1;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      kb[c] = cat8(*reinterpret_cast<const v4i*>(nxt + (2 * c) * 1024 + voff),
+                   *reinterpret_cast<const v4i*>(nxt + (2 * c + 1) * 1024 + voff));
+    tail(T, ks_cur);
+    ks_cur = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(kbuf.ks, (int)lane * 4, nT * 256, 0));
+  };
+  if constexpr (SH) {
+    if (lo < hi) {  // uniform over the workgroup
+      int T = (lo >> 6) + seg;
+      uint8_t* const buf0 = reinterpret_cast<uint8_t*>(s_lds);
+      {
+        const int t1 = refill_tile(T, ntiles);  // past the last tile: the loop is empty
+        const int toff = t1 * (kTile * kD);
+        *reinterpret_cast<v4i*>(buf0 + (2 * wave) * 1024 + voff) =
+            __builtin_amdgcn_raw_buffer_load_b128(ktb, voff, toff + (2 * wave) * 1024, 0);
+        *reinterpret_cast<v4i*>(buf0 + (2 * wave + 1) * 1024 + voff) =
+            __builtin_amdgcn_raw_buffer_load_b128(ktb, voff, toff + (2 * wave + 1) * 1024, 0);
+        ks_cur = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(kbuf.ks, (int)lane * 4, t1 * 256, 0));
+      }
+      __syncthreads();
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        kb[c] = cat8(*reinterpret_cast<const v4i*>(buf0 + (2 * c) * 1024 + voff),
+                     *reinterpret_cast<const v4i*>(buf0 + (2 * c + 1) * 1024 + voff));
+      int b = kTile * kD;  // offset of the buffer the next tile is staged in
+#pragma unroll 1
+      for (; T < tile_hi; T += nseg, b ^= kTile * kD) tile_body_shared(T, buf0 + b);
+    }
+  } else if (lo < hi) {
     int T = (lo >> 6) + seg;
     {
       KeyTile t;
@@ -399,7 +506,7 @@ __global__ __launch_bounds__(kWG, 2) void k_prefill_pair(PrefillArgs A) {
       float m = csum[r];
 #pragma unroll
       for (int o = 32; o > 0; o >>= 1) m += __shfl_xor(m, o, 64);
-      if (lane == 0 && t0 + r < A.Q) A.segn[4 * ((int64_t)(t0 + r) * nseg + seg) + 3] = __float_as_uint(m);
+      if (lane == 0 && t_of[r] >= 0) A.segn[4 * ((int64_t)t_of[r] * nseg + seg) + 3] = __float_as_uint(m);
     }
   } else if constexpr (MODE == kPairRepair) {
     // the pair's histograms into the rows' first digit histograms
@@ -423,8 +530,8 @@ __global__ __launch_bounds__(kWG, 2) void k_prefill_pair(PrefillArgs A) {
         for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
         dk = f2key(m);
       }
-      if (lane == 0 && t0 + r < A.Q)
-        *reinterpret_cast<uint4*>(A.segn + 4 * ((int64_t)(t0 + r) * nseg + seg)) =
+      if (lane == 0 && t_of[r] >= 0)
+        *reinterpret_cast<uint4*>(A.segn + 4 * ((int64_t)t_of[r] * nseg + seg)) =
             make_uint4(min(cnt[r], seg_cap), dk, (uint32_t)fdrop[r], 0u);
     }
   }
@@ -466,7 +573,7 @@ __global__ __launch_bounds__(kWG) void k_prefill_select(PrefillArgs A) {
     }
     return;
   }
-  const int nseg = kWaves * A.S;
+  const int nseg = A.nseg;
   uint32_t dk = 0u, fd = 0xFFFFFFFFu;
   if (tid < nseg) {
     const uint4 e = *reinterpret_cast<const uint4*>(A.segn + 4 * ((int64_t)t * nseg + tid));
@@ -818,20 +925,28 @@ __global__ __launch_bounds__(kWG) void k_prefill_repair_emit(PrefillArgs A) {
 
 // ------------------------------------------------------------------ launch
 
+// One launch of the main kernel in mode MODE with the call's walk geometry;
+// the events, when given, are recorded by the launch itself.
+template <int MODE>
+static void launch_main(const PrefillArgs& A, hipStream_t stream, hipEvent_t e0, hipEvent_t e1) {
+  const int rows = A.shared ? kSharedRows : 2;
+  const unsigned grid = (unsigned)((A.Q + rows - 1) / rows * A.S);
+  void (*const kern)(PrefillArgs) = A.shared ? k_prefill_pair<MODE, true> : k_prefill_pair<MODE, false>;
+  if (e0 || e1)
+    hipExtLaunchKernelGGL(kern, dim3(grid), dim3(kWG), 0, stream, e0, e1, 0, A);
+  else
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(kWG), 0, stream, A);
+}
+
 int launch_prefill(const PrefillArgs& A, hipStream_t stream) {
   if (A.Q == 0) return IDX_OK;
   const int64_t nchunks = (int64_t)((A.N + 63) >> 6) * 512;
   if (nchunks > 0) hipLaunchKernelGGL(k_relayout_keys, dim3((unsigned)(nchunks / kWG)), dim3(kWG), 0, stream, A);
   if (A.math_only) {  // the control: the main kernel's scoring alone, nothing after it
-    const unsigned grid = (unsigned)((A.Q + 1) / 2 * A.S);
     const int reps = A.main_reps > 1 ? A.main_reps : 1;
-    for (int r = 0; r < reps; ++r) {
-      hipEvent_t e0 = r == 0 ? A.ev_main_start : nullptr, e1 = r == reps - 1 ? A.ev_main_stop : nullptr;
-      if (e0 || e1)
-        hipExtLaunchKernelGGL(k_prefill_pair<kPairControl>, dim3(grid), dim3(kWG), 0, stream, e0, e1, 0, A);
-      else
-        hipLaunchKernelGGL(k_prefill_pair<kPairControl>, dim3(grid), dim3(kWG), 0, stream, A);
-    }
+    for (int r = 0; r < reps; ++r)
+      launch_main<kPairControl>(A, stream, r == 0 ? A.ev_main_start : nullptr,
+                                r == reps - 1 ? A.ev_main_stop : nullptr);
     return hipGetLastError() == hipSuccess ? IDX_OK : IDX_EHIP;
   }
   if (!A.keep_all && !A.fuse_tau) hipLaunchKernelGGL(k_prefill_tau, dim3(kRepairGrid), dim3(kWG), 0, stream, A);
@@ -839,21 +954,13 @@ int launch_prefill(const PrefillArgs& A, hipStream_t stream) {
   // (the first launch's start, the last launch's end; main_reps > 1 repeats
   // the idempotent kernel for timing); without events a plain launch (the
   // extended one measured up to 1% slower per call)
-  const unsigned grid = (unsigned)((A.Q + 1) / 2 * A.S);
   const int reps = A.main_reps > 1 ? A.main_reps : 1;
   for (int r = 0; r < reps; ++r) {
     hipEvent_t e0 = r == 0 ? A.ev_main_start : nullptr, e1 = r == reps - 1 ? A.ev_main_stop : nullptr;
-    if (A.dbg_scores) {
-      if (e0 || e1)
-        hipExtLaunchKernelGGL(k_prefill_pair<kPairDebug>, dim3(grid), dim3(kWG), 0, stream, e0, e1, 0, A);
-      else
-        hipLaunchKernelGGL(k_prefill_pair<kPairDebug>, dim3(grid), dim3(kWG), 0, stream, A);
-    } else {
-      if (e0 || e1)
-        hipExtLaunchKernelGGL(k_prefill_pair<kPairFused>, dim3(grid), dim3(kWG), 0, stream, e0, e1, 0, A);
-      else
-        hipLaunchKernelGGL(k_prefill_pair<kPairFused>, dim3(grid), dim3(kWG), 0, stream, A);
-    }
+    if (A.dbg_scores)
+      launch_main<kPairDebug>(A, stream, e0, e1);
+    else
+      launch_main<kPairFused>(A, stream, e0, e1);
   }
   hipLaunchKernelGGL(k_prefill_select, dim3(A.Q), dim3(kWG), 0, stream, A);
   if (A.keep_all) return hipGetLastError() == hipSuccess ? IDX_OK : IDX_EHIP;  // nothing can need repair
@@ -880,15 +987,9 @@ int launch_prefill_unfused(const PrefillArgs& A, hipStream_t stream) {
   const int64_t nchunks = (int64_t)((A.N + 63) >> 6) * 512;
   if (nchunks > 0) hipLaunchKernelGGL(k_relayout_keys, dim3((unsigned)(nchunks / kWG)), dim3(kWG), 0, stream, A);
   hipLaunchKernelGGL(k_prefill_tau, dim3(kRepairGrid), dim3(kWG), 0, stream, A);
-  const unsigned grid = (unsigned)((A.Q + 1) / 2 * A.S);
   const int reps = A.main_reps > 1 ? A.main_reps : 1;
-  for (int r = 0; r < reps; ++r) {
-    hipEvent_t e0 = r == 0 ? A.ev_main_start : nullptr, e1 = r == reps - 1 ? A.ev_main_stop : nullptr;
-    if (e0 || e1)
-      hipExtLaunchKernelGGL(k_prefill_pair<kPairDense>, dim3(grid), dim3(kWG), 0, stream, e0, e1, 0, A);
-    else
-      hipLaunchKernelGGL(k_prefill_pair<kPairDense>, dim3(grid), dim3(kWG), 0, stream, A);
-  }
+  for (int r = 0; r < reps; ++r)
+    launch_main<kPairDense>(A, stream, r == 0 ? A.ev_main_start : nullptr, r == reps - 1 ? A.ev_main_stop : nullptr);
   if (hipGetLastError() != hipSuccess) return IDX_EHIP;
   RowsArgs R{A.dbg_scores, (int64_t)A.N, A.row_start, A.row_end, A.Q, A.N, A.K, A.out, A.ctrl};
   return launch_topk_rows(R, stream);

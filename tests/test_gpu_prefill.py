@@ -137,6 +137,39 @@ def test_fused_sampler_bit_for_bit_with_ragged_ranges(e4m3):
     check_prefill_rows(case, r["out"], np.arange(0, case.Q, 37), gpu_scores=r["scores"], e4m3=e4m3)
 
 
+def test_shared_walk_bit_for_bit_with_the_pair_walk(e4m3):
+    """2051 rows with ragged ranges take the shared walk (eight rows per
+    workgroup, a pair per wave, each key tile staged once in LDS; 2051 is
+    not a multiple of eight, so the last workgroup has absent pairs).  The
+    first 64 rows alone take the one-pair walk.  Every row's scores must be
+    the same bits on both walks, every threshold must be the walk's own
+    sampled score, and sampled rows (the last ones among them) must match
+    the oracle."""
+    import dataclasses
+    case = synth.random_case("shared_walk", 2051, 20000, seed=31, K=2048, min_len=0, max_len=20000)
+    case.row_start[1::8] = case.row_start[0::8]        # some pairs share their start
+    case.row_end[1::8] = np.maximum(case.row_end[1::8], case.row_start[1::8])
+    log("case", case.name, case.Q, case.N)
+    r = run_prefill(case, scores=True)
+    n = 64
+    sub = dataclasses.replace(case, name="shared_walk_head", q8=case.q8[:n], q_scale=case.q_scale[:n], w=case.w[:n],
+                              row_start=case.row_start[:n], row_end=case.row_end[:n])
+    r2 = run_prefill(sub, scores=True)
+    assert np.array_equal(r["scores"][:n].view(np.uint32), r2["scores"].view(np.uint32))
+    assert np.array_equal(r["tau"][:n].view(np.uint32), r2["tau"].view(np.uint32))
+    for t in range(case.Q):
+        s0, s1 = int(case.row_start[t]), int(case.row_end[t])
+        if s1 - s0 <= 8192:
+            assert r["tau"][t] == -np.inf, t
+            continue
+        want = np.float32(_sample_tau(r["scores"][t], s0, s1))
+        assert r["tau"][t].view(np.uint32) == want.view(np.uint32), (t, r["tau"][t], want)
+    rows = np.unique(np.concatenate([np.arange(8), np.arange(case.Q - 11, case.Q), np.arange(0, case.Q, 97)]))
+    rep = check_prefill_rows(case, r["out"], rows, gpu_scores=r["scores"], e4m3=e4m3)
+    log("shared walk", rep, r["stats"])
+    assert r["stats"]["rows"] == case.Q
+
+
 def test_massive_ties_take_the_fast_path(e4m3):
     """Rows over 16 distinct keys: the threshold is the top score, held by
     about 10K keys, far more than the segments hold (capacity cut to 4096).
