@@ -90,6 +90,7 @@ constexpr int kRepairChunk = 4096;
 constexpr int kRepairChunkTiles = kRepairChunk / 64;
 constexpr int kRepairGrid = 256;  // one workgroup per CU; items are strided over the grid
 constexpr int kRepairPassGrid = 1024;  // digit passes, tie count and emit: four workgroups per CU
+constexpr int kRepairWalkWGs = 512;    // rescoring walk: the workgroups of one round, two per CU
 
 // Words kept per slotted repair row (PrefillArgs::rrow): the emit's output
 // counters, then two groups of four holding the row's selection state

@@ -150,7 +150,10 @@ __global__ __launch_bounds__(kWG, 2) void k_prefill_pair(PrefillArgs A) {
     const int n_slot = (int)min(__atomic_load_n(&A.ctrl[kCtrlFail], __ATOMIC_RELAXED), (uint32_t)A.rslots);
     const int pairs = (n_slot + 1) / 2;
     if (pairs == 0) return;  // nothing failed (the whole workgroup leaves together)
-    nsplit = max(1, (int)gridDim.x / pairs);
+    // splits per pair: the pairs fill one round of kRepairWalkWGs resident
+    // workgroups (two per CU); the launch has a workgroup for every slot
+    // pair, and those beyond the pairs' splits leave at once
+    nsplit = max(1, kRepairWalkWGs / pairs);
     const int pr = blockIdx.x / nsplit;
     if (pr >= pairs) return;
     split = blockIdx.x % nsplit;
@@ -966,7 +969,7 @@ int launch_prefill(const PrefillArgs& A, hipStream_t stream) {
   if (A.keep_all) return hipGetLastError() == hipSuccess ? IDX_OK : IDX_EHIP;  // nothing can need repair
   // the slotted failures rescored two per workgroup: enough workgroups for
   // every slot pair, at least two per CU for few failures
-  const unsigned rgrid = (unsigned)max(512, (A.rslots + 1) / 2);
+  const unsigned rgrid = (unsigned)max(kRepairWalkWGs, (A.rslots + 1) / 2);
   hipLaunchKernelGGL(k_prefill_pair<kPairRepair>, dim3(rgrid), dim3(kWG), 0, stream, A);
   if (A.rslots < A.Q) hipLaunchKernelGGL(k_prefill_repair_fallback, dim3(kRepairFallback), dim3(kWG), 0, stream, A);
   hipLaunchKernelGGL(k_prefill_repair_pass<1>, dim3(kRepairPassGrid), dim3(kWG), 0, stream, A);
