@@ -18,7 +18,7 @@ k_prefill_pair (bound by FP8 MFMA) for prefill, k_decode_score (bound by
 HBM) for decode.  For prefill it also carries the main kernel's mean shader
 clock, measured inside the kernel (shader-clock cycles over constant-rate
 wall-clock ticks of every wave), and the fraction of the peak at that clock;
-beside it, the Math-only control of "5.2 Exposed selection" (the main
+beside it, the control of "5.2 Math-only control" (the main
 kernel's loads, MFMAs and scores with no sampling, filtering, selection or
 repair) gives the selection time the complete operator leaves exposed.  The
 short-context cases (prefill smoke, paged decode) are also timed cold: a

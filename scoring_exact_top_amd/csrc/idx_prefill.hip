@@ -79,9 +79,9 @@ __global__ __launch_bounds__(kWG) void k_prefill_tau(PrefillArgs A) {
 // MODE kPairFused is that fused pass; kPairDebug also writes every valid
 // score to dbg_scores [Q][N]; kPairDense only writes the scores (no filter,
 // no candidates): the scoring stage of the unfused comparator.  kPairControl
-// is the Math-only control of "5.2 Exposed selection" (Fusing Indexer
+// is the control of "5.2 Math-only control" (Fusing Indexer
 // Scoring and Exact Top-k page): the same loads, MFMAs and scores, folded
-// into one checksum per (row, wave) instead of being sampled, filtered and
+// into one checksum per (row, segment) instead of being sampled, filtered and
 // appended; with no selection or repair after it, the complete operator's
 // time minus this kernel's is the selection work left exposed.
 // kPairRepair rescores the rows the certificate rejected (exact repair,

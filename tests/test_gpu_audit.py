@@ -1,7 +1,7 @@
 """Full-configuration audits on MI355X: every row of the benchmarked prefill
 workloads, in the benchmark's launch configuration, against the CPU oracle
 (the correctness audit of the Fusing Indexer Scoring and Exact Top-k page,
-"6.3 Correctness audit", extended from sampled rows to all of them).  Each
+"6.3 Correctness", extended from sampled rows to all of them).  Each
 call also returns its per-row outcome, so the rows that the exact repair
 rewrote are named and checked like every other.  Plus the paths that only
 large inputs reach: failed rows beyond the repair slots, and a key count at
