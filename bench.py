@@ -22,8 +22,8 @@ beside it, the control of "5.2 Math-only control" (the main
 kernel's loads, MFMAs and scores with no sampling, filtering, selection or
 repair) gives the selection time the complete operator leaves exposed.  The
 short-context cases (prefill smoke, paged decode) are also timed cold: a
-512 MiB buffer is written between calls so that the 256 MB Infinity Cache
-holds none of the inputs.
+512 MiB buffer is written and read back between calls, so that the 256 MB
+Infinity Cache holds none of the inputs and no dirty line of its own.
 """
 from __future__ import annotations
 
@@ -74,37 +74,47 @@ def wall_clock_khz() -> int:
 
 
 class CacheFlush:
-    """Writes a 512 MiB buffer: afterwards the 256 MB Infinity Cache and the
-    L2s hold none of a call's inputs."""
+    """Writes a 512 MiB buffer, then reads it back: afterwards the 256 MB
+    Infinity Cache and the L2s hold none of a call's inputs, and no dirty
+    line of the flush is left to be written back during the timed call."""
 
     def __init__(self):
         self.buf = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        self.acc = torch.zeros((), dtype=torch.int64, device="cuda")
         self.n = 0
 
     def __call__(self):
         self.n += 1
         self.buf.fill_(self.n & 0xFF)
+        self.acc += self.buf.view(torch.int64).sum()
 
 
 def timed_cold(step, steps: int):
-    """Each call alone after a cache flush: (mean call ms, mean dominant-kernel
-    ms), both from events on the call's stream."""
+    """Calls after a cache flush: (mean call ms, mean dominant-kernel ms).
+    Each call's time runs from an event recorded after its flush to one
+    recorded after the call, with no event inside the call (so it includes
+    the dispatch of the call's first kernel); the dominant kernel's time
+    comes from a second set of flushed calls whose launches record events."""
     flush = CacheFlush()
-    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))]
-           for _ in range(steps)]
-    calls = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    for e in evs:  # torch creates the HIP events on first record; the library records them again
-        for e0, e1 in e:
-            e0.record()
-            e1.record()
+
+    def pairs():
+        return [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+
+    calls, kern = pairs(), pairs()
+    for e0, e1 in kern:  # torch creates the HIP events on first record; the library records them again
+        e0.record()
+        e1.record()
     for i in range(steps):
         flush()
         calls[i][0].record()
-        step(evs[i], 1)
+        step(None, 1)
         calls[i][1].record()
+    for i in range(steps):
+        flush()
+        step([kern[i]], 1)
     torch.cuda.synchronize()
     call_ms = [a.elapsed_time(b) for a, b in calls]
-    kern_ms = [e[0][0].elapsed_time(e[0][1]) for e in evs]
+    kern_ms = [a.elapsed_time(b) for a, b in kern]
     return float(np.mean(call_ms)), float(np.mean(kern_ms))
 
 
@@ -328,7 +338,7 @@ def bench_prefill(args, lib):
         res["subcalls"] = subcalls
     if args.workload in COLD:
         cold_ms, cold_main = timed_cold(step, args.steps)
-        log("cold (512 MiB written between calls): call %.4f ms, main kernel %.4f ms" % (cold_ms, cold_main))
+        log("cold (512 MiB written and read back between calls): call %.4f ms, main kernel %.4f ms" % (cold_ms, cold_main))
         res["cold"] = {"ms_per_call": cold_ms, "main_ms_per_launch": cold_main,
                        "main_hbm_gbs": prefill_bytes(cases[0]) / (cold_main * 1e-3) / 1e9,
                        "warm_main_hbm_gbs": prefill_bytes(cases[0]) / (main_avg * 1e-3) / 1e9}
@@ -543,7 +553,7 @@ def bench_decode(args, lib):
     res = result(args, case.pairs / (ms_per_step * 1e-3) / 1e9, ms_per_step, config, roofline,
                  "fp8_e4m3 x fp8_e4m3 -> f32")
     cold_ms, cold_main = timed_cold(step, args.steps)
-    log("cold (512 MiB written between calls): call %.4f ms, scoring kernel %.4f ms" % (cold_ms, cold_main))
+    log("cold (512 MiB written and read back between calls): call %.4f ms, scoring kernel %.4f ms" % (cold_ms, cold_main))
     res["cold"] = {"ms_per_call": cold_ms, "main_ms_per_launch": cold_main,
                    "main_hbm_gbs": nbytes / (cold_main * 1e-3) / 1e9,
                    "warm_main_hbm_gbs": achieved, "pairs_per_s_cold": case.pairs / (cold_ms * 1e-3)}
