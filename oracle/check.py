@@ -82,6 +82,41 @@ def check_selection(out_row, scores_row, start, end, K, theta, where="", rel_tol
     return int(np.sum(sel_scores < theta))
 
 
+def check_selection_rounding(out_row, scores_row, start, end, K, theta, bound_row, where="", gamma=GAMMA):
+    """The selection judged at the scores' own rounding bound, for rows whose
+    K-th score theta is so small against that bound that the relative bar
+    of check_selection cannot be met in FP32 (theta near 0).  FP32 scoring
+    can order two keys a, b against their exact scores only when
+    |I[a] - I[b]| <= gamma*(B[a] + B[b]), the element-wise bound of
+    check_scores.  With B_theta the largest bound among the ids scoring
+    theta, every selected id s must have I[s] >= theta - gamma*(B[s] + B_theta)
+    and every id s left out I[s] <= theta + gamma*(B[s] + B_theta).
+
+    scores_row and bound_row are indexed by absolute id.  Returns the number
+    of selected ids scoring below theta."""
+    check_structure(out_row, start, end, K, where)
+    kk = min(K, end - start)
+    if kk == 0:
+        return 0
+    I = np.asarray(scores_row, dtype=np.float64)
+    B = np.asarray(bound_row, dtype=np.float64)
+    ids = np.arange(start, end)
+    b_theta = float(np.max(B[ids[I[start:end] == theta]]))
+    sel = np.asarray(out_row[:kk], dtype=np.int64)
+    low = I[sel] < theta - gamma * (B[sel] + b_theta)
+    if np.any(low):
+        _fail("%s: %d selected ids below theta beyond the rounding bound (theta=%r, worst=%r)"
+              % (where, int(low.sum()), theta, float(I[sel].min())))
+    mask = np.zeros(I.shape[0], dtype=bool)
+    mask[sel] = True
+    out = ids[~mask[start:end]]
+    high = I[out] > theta + gamma * (B[out] + b_theta)
+    if np.any(high):
+        _fail("%s: %d ids left out above theta beyond the rounding bound (theta=%r, e.g. id %d score %r)"
+              % (where, int(high.sum()), theta, int(out[high][0]), float(I[out[high][0]])))
+    return int(np.sum(I[sel] < theta))
+
+
 def check_exact_values(out_row, scores_row, start, end, K, where=""):
     """Strict form of the pages' criterion on the oracle's own scores: the
     sorted selected scores equal the sorted true top-K scores exactly."""

@@ -52,15 +52,19 @@ def run_prefill(case, debug=False, scores=False, status=False, **opts):
 def check_prefill_rows(case, out, rows, nthreads=0, gpu_scores=None, e4m3=None):
     """Oracle check of the given rows: structure + tolerance selection, and,
     when the GPU's scores are given, element-wise score tolerance and the
-    bit-exact selection on the GPU's own scores."""
+    bit-exact selection on the GPU's own scores.  A row whose K-th score is
+    too close to 0 for the relative selection bar (check_selection) is
+    judged at the scores' rounding bound (check_selection_rounding), which
+    needs the GPU's scores and the bound B; such rows are counted."""
     rows = np.asarray(rows, dtype=np.int32)
     topk, theta, sc = oracle.prefill_case(case, rows=rows, nthreads=nthreads)
     below = 0
     cancel = 0
+    rounding = 0
     for j, t in enumerate(rows):
         s0, s1 = int(case.row_start[t]), int(case.row_end[t])
         where = "%s row %d" % (case.name, t)
-        below += check.check_selection(out[t], sc[j], s0, s1, case.K, theta[j], where=where)
+        bound = None
         if gpu_scores is not None and s1 > s0:
             S = gpu_scores[t]
             ids = np.arange(s0, s1)
@@ -69,7 +73,17 @@ def check_prefill_rows(case, out, rows, nthreads=0, gpu_scores=None, e4m3=None):
             cancel += check.check_scores(S[s0:s1], sc[j][s0:s1], bound=bound, where=where)
             check.check_debug_bitexact(out[t], S, s0, s1, case.K, where=where)
             check.check_debug_canonical(out[t], S, s0, s1, case.K, where=where)
-    return dict(rows=len(rows), below_theta=below, cancel_only=cancel)
+        try:
+            below += check.check_selection(out[t], sc[j], s0, s1, case.K, theta[j], where=where)
+        except check.CheckError as e:
+            if bound is None:
+                raise
+            full = np.zeros(sc[j].shape[0])
+            full[s0:s1] = bound
+            below += check.check_selection_rounding(out[t], sc[j], s0, s1, case.K, theta[j], full, where=where)
+            log("%s: judged at the rounding bound (%s)" % (where, e))
+            rounding += 1
+    return dict(rows=len(rows), below_theta=below, cancel_only=cancel, rounding_only=rounding)
 
 
 def sample_rows(Q, n, seed=0):
@@ -85,7 +99,7 @@ def audit_rows(case, out, rows=None, batch=128, gpu_scores=None, e4m3=None):
     batches so that the oracle's fp64 score rows stay a few hundred MB; the
     oracle runs on all host threads."""
     rows = np.arange(case.Q) if rows is None else np.asarray(rows)
-    tot = dict(rows=0, below_theta=0, cancel_only=0)
+    tot = dict(rows=0, below_theta=0, cancel_only=0, rounding_only=0)
     for i in range(0, rows.size, batch):
         rep = check_prefill_rows(case, out, rows[i:i + batch], gpu_scores=gpu_scores, e4m3=e4m3)
         for k in tot:

@@ -10,7 +10,7 @@ from oracle import check
 
 pytestmark = pytest.mark.gpu
 
-from gpu_util import check_prefill_rows, log, run_prefill, sample_rows  # noqa: E402
+from gpu_util import check_prefill_rows, log, run_prefill, sample_rows, status_matches_stats  # noqa: E402
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -168,6 +168,36 @@ def test_shared_walk_bit_for_bit_with_the_pair_walk(e4m3):
     rep = check_prefill_rows(case, r["out"], rows, gpu_scores=r["scores"], e4m3=e4m3)
     log("shared walk", rep, r["stats"])
     assert r["stats"]["rows"] == case.Q
+
+
+@pytest.mark.parametrize("mode", ["keep_all", "overflow", "underflow"])
+def test_shared_walk_edge_modes(mode, e4m3):
+    """The shared walk (2048 rows, so two splits per group of eight rows)
+    where every row keeps all its keys (N <= 8192: no sampling, no
+    repair), where a shrunk capacity makes every row overflow, and where a
+    threshold of +inf makes every row underflow; the last two go through
+    the repair.  Every row against the oracle, with the GPU's scores (K =
+    1024 of ragged rows puts some K-th scores near 0, where the selection is
+    judged at the scores' rounding bound)."""
+    N = 6000 if mode == "keep_all" else 3000
+    case = synth.random_case("shared_" + mode, 2048, N, seed=33, K=1024, min_len=0)
+    opts = {}
+    if mode == "overflow":
+        opts = dict(force_tau=float("-inf"), cand_cap=512)
+    elif mode == "underflow":
+        opts = dict(force_tau=float("inf"))
+    r = run_prefill(case, status=True, scores=True, **opts)
+    st = r["stats"]
+    rep = check_prefill_rows(case, r["out"], np.arange(case.Q), gpu_scores=r["scores"], e4m3=e4m3)
+    log(mode, st, rep)
+    status_matches_stats(r["status"], st)
+    long_rows = int(np.sum(case.row_end - case.row_start > case.K))
+    if mode == "keep_all":
+        assert st["fast_ok"] == case.Q and st["repaired"] == 0
+    elif mode == "overflow":
+        assert st["overflow"] >= long_rows - 8 and st["repaired"] == st["overflow"] + st["underflow"]
+    else:
+        assert st["underflow"] >= long_rows
 
 
 def test_massive_ties_take_the_fast_path(e4m3):

@@ -603,3 +603,37 @@ def test_check_scores_cancellation_clause():
     assert check.check_scores(big * (1 + 0.9 * check.REL_TOL), big, bound=np.array([1.0])) == 0
     with pytest.raises(check.CheckError):
         check.check_scores(big * (1 + 1.1 * check.REL_TOL), big, bound=np.array([1.0]))
+
+
+def test_check_selection_rounding_bound():
+    """The rounding-bound selection check on a hand-made row (ids 0..5, K = 3,
+    exact top-3 = {0, 1, 2}, theta = I[2] = 0.004): a swap of the K-th key
+    with the next one (gap 0.003) passes exactly when the two keys' bounds
+    cover the gap, gamma*(B[3] + B[2]) >= 0.003, and fails otherwise; a key
+    far below theta never passes; the relative check rejects the swap, since
+    0.003 > 1e-3 * |theta|; a zero bound accepts only the exact top-K."""
+    g = check.GAMMA
+    I = np.array([5.0, 2.0, 0.004, 0.001, -1.0, -3.0])
+    theta = 0.004
+    exact = np.array([2, 0, 1])
+    swap = np.array([0, 1, 3])
+    far = np.array([0, 1, 4])
+    wide = np.full(6, 0.003 / (2 * g) * 1.01)     # bounds just cover the gap
+    narrow = np.full(6, 0.003 / (2 * g) * 0.99)   # just do not
+    zero = np.zeros(6)
+    assert check.check_selection_rounding(exact, I, 0, 6, 3, theta, zero) == 0
+    assert check.check_selection_rounding(exact, I, 0, 6, 3, theta, narrow) == 0
+    assert check.check_selection_rounding(swap, I, 0, 6, 3, theta, wide) == 1
+    for bad, B in ((swap, narrow), (swap, zero), (far, wide)):
+        with pytest.raises(check.CheckError):
+            check.check_selection_rounding(bad, I, 0, 6, 3, theta, B)
+    with pytest.raises(check.CheckError):
+        check.check_selection(swap, I, 0, 6, 3, theta)
+    # only the two keys' own bounds count: a large bound elsewhere changes nothing
+    lopsided = narrow.copy()
+    lopsided[5] = 1e9
+    with pytest.raises(check.CheckError):
+        check.check_selection_rounding(swap, I, 0, 6, 3, theta, lopsided)
+    # structure is still enforced
+    with pytest.raises(check.CheckError):
+        check.check_selection_rounding(np.array([0, 0, 1]), I, 0, 6, 3, theta, wide)
