@@ -62,19 +62,25 @@ __global__ __launch_bounds__(kWG) void k_prefill_tau(PrefillArgs A) {
 
 // ------------------------------------------------------ paired-row main
 
-// Two query rows per workgroup of four waves; two workgroups per CU.  With
-// few rows the pair's tiles are split over S workgroups (S*kWaves waves in
-// all), and each wave walks every (S*kWaves)-th 64-key tile of the rows'
-// union range.  Per 16-key
-// sub-tile it issues the 9 MFMAs of both rows (4 head blocks each plus the
-// shared u block), software-pipelined by row so that each row's epilogue
-// runs under the other row's MFMAs, and refills the sub-tile's registers
-// with the same sub-tile of its next tile (one tile of lead).  Keys >= tau
-// are stored, as raw score bits and key id, straight into the wave's
-// private segment of the row's workspace candidate area; the slot comes
-// from a scalar count plus the lane's rank in the ballot, so no atomics
-// are involved.  After the walk each wave publishes its segment counts;
-// certification and selection follow in their own kernel.
+// Every wave scores one pair of query rows; two workgroups of four waves per
+// CU.  Two walks (prefill_geom):
+//  - one-pair walk (SH = false): the four waves of a workgroup share one
+//    pair, whose tiles are split over S workgroups (S*kWaves waves in all);
+//    each wave walks every (S*kWaves)-th 64-key tile of the rows' union
+//    range and refills each sub-tile's B operand straight from memory with
+//    the same sub-tile of its next tile (one tile of lead);
+//  - shared walk (SH = true): the four waves own four pairs (eight rows),
+//    and all of them walk every S-th tile of the eight rows' union range;
+//    each tile is staged once into LDS for all four waves (see
+//    tile_body_shared).
+// Per 16-key sub-tile a wave issues the 9 MFMAs of its pair (4 head blocks
+// per row plus the shared u block), software-pipelined by row so that each
+// row's epilogue runs under the other row's MFMAs.  Keys >= tau are stored,
+// as raw score bits and key id, straight into the wave's private segment of
+// the row's workspace candidate area; the slot comes from a scalar count
+// plus the lane's rank in the ballot, so no atomics are involved.  After
+// the walk each wave publishes its segment records; certification and
+// selection follow in their own kernel.
 //
 // MODE kPairFused is that fused pass; kPairDebug also writes every valid
 // score to dbg_scores [Q][N]; kPairDense only writes the scores (no filter,
