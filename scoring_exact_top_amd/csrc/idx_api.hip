@@ -13,7 +13,7 @@ static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 static inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 struct PrefillLayout {
-  size_t ctrl, tau, fail, skey, cidx, segn, scratch, rhist, rrow, reqc, kt, dense, total;
+  size_t ctrl, tau, fail, cand, segn, scratch, rhist, rrow, reqc, kt, dense, total;
 };
 
 // unfused: also the [Q][N] FP32 score matrix of the unfused comparator.
@@ -26,8 +26,7 @@ static PrefillLayout prefill_layout(int32_t Q, int32_t N, bool unfused = false) 
   const WalkGeom g = prefill_geom(Q);
   const size_t nseg = (size_t)g.nseg;
   const size_t cand = (size_t)Q * nseg * (size_t)prefill_seg_cap(g.nseg);
-  L.skey = o; o = align256(o + sizeof(uint32_t) * cand);
-  L.cidx = o; o = align256(o + sizeof(int32_t) * cand);
+  L.cand = o; o = align256(o + sizeof(uint2) * cand);
   L.segn = o; o = align256(o + 4 * sizeof(uint32_t) * (size_t)Q * nseg);
   L.scratch = o; o = align256(o + sizeof(uint32_t) * (size_t)repair_rows(Q, N) * (size_t)repair_stride(N));
   L.rhist = o; o = align256(o + sizeof(uint32_t) * (size_t)repair_slots(Q, N) * 4 * 256);
@@ -65,8 +64,7 @@ static int prefill_common(const uint8_t* q, const float* q_scale, const uint8_t*
   A.ctrl = reinterpret_cast<uint32_t*>(ws + L.ctrl);
   A.tau = reinterpret_cast<float*>(ws + L.tau);
   A.fail_list = reinterpret_cast<int32_t*>(ws + L.fail);
-  A.cand_key = reinterpret_cast<uint32_t*>(ws + L.skey);
-  A.cand_idx = reinterpret_cast<int32_t*>(ws + L.cidx);
+  A.cand = reinterpret_cast<uint2*>(ws + L.cand);
   A.segn = reinterpret_cast<uint32_t*>(ws + L.segn);
   const WalkGeom g = prefill_geom(Q);
   A.S = g.S;

@@ -38,6 +38,7 @@ namespace idxk {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v2i __attribute__((ext_vector_type(2)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
@@ -702,27 +703,28 @@ __device__ __forceinline__ RegLayout block_list_layout(uint32_t n, uint32_t tid)
   return RegLayout{tid, (uint32_t)kWG, n, (n + kWG - 1u) / kWG};
 }
 
-// Loads of one list into registers, key[j] and id[j] = element lay.at(j):
-// buffer loads whose out-of-range reads return 0, so all of them are issued
-// back to back without a branch per element; invalid slots get key 0 and
-// read nothing (their offset lies past every buffer, so the bounds check
-// answers them without a memory access).  `extent` (uniform) bounds the
-// buffers; lay.valid masks the entries.
+// Loads of one list of (key bits, id) pairs into registers, key[j] and
+// id[j] = element lay.at(j): one 8-byte buffer load per element, whose
+// out-of-range reads return 0, so all of them are issued back to back
+// without a branch per element; invalid slots get key 0 and read nothing
+// (their offset lies past every buffer, so the bounds check answers them
+// without a memory access).  `extent` (uniform) bounds the list; lay.valid
+// masks the entries; dec maps the stored key bits to the key.
 template <int M, class Dec>
-__device__ __forceinline__ void load_list_regs(uint32_t (&key)[M], int32_t (&id)[M], const uint32_t* keys,
-                                               const int32_t* ids, uint32_t extent, const RegLayout& lay,
-                                               const Dec& dec) {
-  const rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)keys, (short)0, (int)(extent * 4u), 0x00020000);
-  const rsrc_t ri = __builtin_amdgcn_make_buffer_rsrc((void*)ids, (short)0, (int)(extent * 4u), 0x00020000);
-  uint32_t raw[M];
+__device__ __forceinline__ void load_list_regs(uint32_t (&key)[M], int32_t (&id)[M], const uint2* list,
+                                               uint32_t extent, const RegLayout& lay, const Dec& dec) {
+  const rsrc_t rl = __builtin_amdgcn_make_buffer_rsrc((void*)list, (short)0, (int)(extent * 8u), 0x00020000);
+  v2i raw[M];
 #pragma unroll
   for (int j = 0; j < M; ++j) {
-    const int off = lay.valid(j) ? (int)(lay.at(j) * 4u) : 0x7FFFFFF0;
-    raw[j] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rk, off, 0, 0);
-    id[j] = __builtin_amdgcn_raw_buffer_load_b32(ri, off, 0, 0);
+    const int off = lay.valid(j) ? (int)(lay.at(j) * 8u) : 0x7FFFFFF0;
+    raw[j] = __builtin_amdgcn_raw_buffer_load_b64(rl, off, 0, 0);
   }
 #pragma unroll
-  for (int j = 0; j < M; ++j) key[j] = lay.valid(j) ? dec(raw[j]) : 0u;
+  for (int j = 0; j < M; ++j) {
+    key[j] = lay.valid(j) ? dec((uint32_t)raw[j].x) : 0u;
+    id[j] = raw[j].y;
+  }
 }
 
 // Selection over keys held in registers: every key above `last` is in the

@@ -158,8 +158,7 @@ struct PrefillArgs {
   float* tau;           // [Q]
   int32_t* out;         // [Q][K]
   uint8_t* kt;          // [ntiles][8][64][16] keys relaid in MFMA lane order
-  uint32_t* cand_key;   // [Q][kWaves*S][seg_cap] candidate scores (FP32 bits)
-  int32_t* cand_idx;    // [Q][kWaves*S][seg_cap] candidate key ids
+  uint2* cand;          // [Q][nseg][seg_cap] candidates: (FP32 score bits, key id)
   uint32_t* segn;       // [Q][kWaves*S][4]: entries stored, key of the largest dropped candidate
                         // (0: none), position of the first dropped one, unused
   int32_t S, seg_cap, seg_eff;  // splits, segment stride, usable entries per segment

@@ -298,12 +298,11 @@ __global__ __launch_bounds__(kWG, 2) void k_prefill_pair(PrefillArgs A) {
   int fdrop[2] = {0x7FFFFFFF, 0x7FFFFFFF};  // position of the segment's first dropped candidate
   // the (row, wave) workspace segments as buffer resources: a store past
   // seg_cap is dropped by the bounds check
-  rsrc_t segk[2], segi[2];
+  rsrc_t segc[2];
 #pragma unroll
   for (int r = 0; r < 2; ++r) {
     const int64_t o = MODE == kPairRepair ? 0 : ((int64_t)(t_of[r] >= 0 ? t_of[r] : tq) * nseg + seg) * A.seg_cap;
-    segk[r] = __builtin_amdgcn_make_buffer_rsrc((void*)(A.cand_key + o), (short)0, (int)(seg_cap * 4u), 0x00020000);
-    segi[r] = __builtin_amdgcn_make_buffer_rsrc((void*)(A.cand_idx + o), (short)0, (int)(seg_cap * 4u), 0x00020000);
+    segc[r] = __builtin_amdgcn_make_buffer_rsrc((void*)(A.cand + o), (short)0, (int)(seg_cap * 8u), 0x00020000);
   }
   const v4f z = {0.f, 0.f, 0.f, 0.f};
   // Head-weighted sum of one row's 16 heads held by this lane plus its two
@@ -344,9 +343,9 @@ __global__ __launch_bounds__(kWG, 2) void k_prefill_pair(PrefillArgs A) {
       const bool take = valid && sc[r] >= tr[r];
       const uint64_t ball = __ballot(take);
       const uint32_t n = (uint32_t)__popcll(ball);
-      const int off = take ? (int)((cnt[r] + rank_in(ball)) * 4u) : 0x7FFFFFF0;
-      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sc[r]), segk[r], off, 0, 0);
-      __builtin_amdgcn_raw_buffer_store_b32((uint32_t)my, segi[r], off, 0, 0);
+      const int off = take ? (int)((cnt[r] + rank_in(ball)) * 8u) : 0x7FFFFFF0;
+      const v2i cand = {(int)__float_as_uint(sc[r]), my};
+      __builtin_amdgcn_raw_buffer_store_b64(cand, segc[r], off, 0, 0);
       if (cnt[r] + n > seg_cap) {
         const bool dropped = take && cnt[r] + rank_in(ball) >= seg_cap;
         dmax[r] = dropped ? fmaxf(dmax[r], sc[r]) : dmax[r];
@@ -613,7 +612,7 @@ __global__ __launch_bounds__(kWG) void k_prefill_select(PrefillArgs A) {
     const int64_t row = (int64_t)t * nseg * A.seg_cap;
     uint32_t key[kSelRegs];
     int32_t id[kSelRegs];
-    load_list_regs(key, id, A.cand_key + row, A.cand_idx + row, (uint32_t)(nseg * A.seg_cap), lay,
+    load_list_regs(key, id, A.cand + row, (uint32_t)(nseg * A.seg_cap), lay,
                    [](uint32_t x) { return f2key(__uint_as_float(x)); });
     const auto kf = [&](int j) { return key[j]; };
     const RangeSel sel = (n > (uint32_t)kr) ? range_select_regs<kSelRegs>(kf, lay, kr, sh, tid)
