@@ -130,6 +130,15 @@ extern "C" size_t idx_topk_prefill_workspace(int32_t Q, int32_t N, int32_t K) {
   return prefill_layout(Q, N).total;
 }
 
+extern "C" int idx_topk_prefill_geometry(int32_t Q, int32_t* shared, int32_t* splits, int32_t* segments) {
+  if (Q < 0) return IDX_EINVAL;
+  const WalkGeom g = prefill_geom(Q);
+  if (shared) *shared = g.shared;
+  if (splits) *splits = g.S;
+  if (segments) *segments = g.nseg;
+  return IDX_OK;
+}
+
 extern "C" int idx_topk_prefill(const uint8_t* q, const float* q_scale, const uint8_t* k,
                                 const float* k_scale, const float* w, const int32_t* row_start,
                                 const int32_t* row_end, int32_t K, int32_t* out_idx, int32_t Q,

@@ -46,31 +46,49 @@ __host__ __device__ inline int prefill_split(int rows) {
   return s;
 }
 
-// Geometry of the main kernel's walk.  With kSharedMinRows rows or more the
-// walk is shared: a workgroup takes kSharedRows rows (a pair per wave), each
-// tile is staged once in LDS for all four waves, and a row's candidates of
-// one split go to one segment (nseg = S).  Fewer rows keep one pair per
-// workgroup with the tiles split over its waves (nseg = kWaves * S), which
-// needs four times fewer splits for the same number of workgroups: every
-// split samples its rows' thresholds again, and at four or more splits that
-// repeated sampling cost more than the shared tiles saved (1024 rows of
-// 163840 keys: 0.534 against 0.531 ms; 4096 rows: 3.26 against 3.46 ms).
+// Geometry of the main kernel's walk.  Shared walk: a workgroup takes
+// kSharedRows rows (a pair per wave), each tile is staged once in LDS for
+// all four waves, and a row's candidates of one split go to one segment
+// (nseg = S).  One-pair walk: a workgroup takes one pair and splits its
+// tiles over its waves (nseg = kWaves * S), which needs four times fewer
+// splits for the same number of workgroups.  Two workgroups per CU are
+// resident (kRound in all), so a launch takes ceil(workgroups / kRound)
+// rounds, and its time goes as rounds x (rows per workgroup / S), the tiles
+// one workgroup walks.  The shared walk does that work about 5% faster
+// (its tiles come from LDS; 3.26 against 3.46 ms at 4096 x 131072), but its
+// workgroups are four times coarser, so a partly filled last round costs
+// more, and each split samples its rows again.  The walk of lower cost is
+// taken, the shared one only with S <= 2 and from kSharedMinRows rows.
+// Measured at 131072 keys, ms per call, shared against one-pair: 2048 rows
+// 1.72 against 1.80, 3072 rows 2.95 against 2.58 (the shared walk's 768
+// workgroups fill 1.5 rounds), 4096 rows 3.26 against 3.46.
 constexpr int kSharedRows = 2 * kWaves;
 constexpr int kSharedMinRows = 2048;
+constexpr int kRound = 512;
 
 struct WalkGeom {
   int shared, S, nseg;
 };
 
+__host__ __device__ inline int64_t walk_rounds(int64_t wgs) { return (wgs + kRound - 1) / kRound; }
+
 __host__ __device__ inline WalkGeom prefill_geom(int rows) {
-  if (rows >= kSharedMinRows) {
-    const int groups = (rows + kSharedRows - 1) / kSharedRows;
-    int s = 1;
-    while (s < kMaxSeg && groups * s < 512) s *= 2;
-    return WalkGeom{1, s, s};
+  const int s1 = prefill_split(rows);
+  const WalkGeom pair{0, s1, kWaves * s1};
+  if (rows < kSharedMinRows) return pair;
+  const int64_t pairs = (rows + 1) / 2, groups = (rows + kSharedRows - 1) / kSharedRows;
+  // cost = rounds x (rows per workgroup x 8 / S), x 20 for the one-pair walk
+  // and x 19 for the shared walk
+  int64_t best = 20 * walk_rounds(pairs * s1) * (2 * 8 / s1);
+  int best_s = 0;
+  for (int s = 1; s <= 2; s *= 2) {
+    const int64_t c = 19 * walk_rounds(groups * s) * (kSharedRows * 8 / s);
+    if (c < best) {
+      best = c;
+      best_s = s;
+    }
   }
-  const int s = prefill_split(rows);
-  return WalkGeom{0, s, kWaves * s};
+  return best_s ? WalkGeom{1, best_s, best_s} : pair;
 }
 
 // Entries of one candidate segment for nseg segments per row: the larger of

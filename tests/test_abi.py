@@ -219,3 +219,20 @@ def test_noalloc_decode_argument_errors(lib):
     assert f(*args(B=64, mp=1024)) == -5
     lib.idx_topk_strerror.restype = ctypes.c_char_p
     assert b"scratch" in lib.idx_topk_strerror(-5)
+
+
+def test_prefill_walk_geometry():
+    """The walk the main kernel takes for Q rows (host logic, no GPU): the
+    one-pair walk below 2048 rows, with splits until 512 workgroups; from
+    2048 rows the walk of lower cost in rounds of 512 resident workgroups,
+    so the shared walk at 2048 and 4096 rows but not at 3072 (whose 384 or
+    768 shared workgroups would leave a round part empty); segments per row
+    are the splits (shared) or four per split (one-pair)."""
+    import scoring_exact_top_amd as lib
+    want = {1: (0, 8, 32), 64: (0, 8, 32), 256: (0, 4, 16), 1024: (0, 1, 4), 2047: (0, 1, 4),
+            2048: (1, 2, 2), 3072: (0, 1, 4), 4093: (1, 1, 1), 4096: (1, 1, 1), 5120: (0, 1, 4),
+            8192: (1, 1, 1)}
+    for Q, g in want.items():
+        assert lib.prefill_geometry(Q) == g, (Q, lib.prefill_geometry(Q), g)
+    with pytest.raises(lib.IdxTopkError):
+        lib.prefill_geometry(-1)

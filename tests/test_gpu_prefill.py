@@ -138,15 +138,17 @@ def test_fused_sampler_bit_for_bit_with_ragged_ranges(e4m3):
 
 
 def test_shared_walk_bit_for_bit_with_the_pair_walk(e4m3):
-    """2051 rows with ragged ranges take the shared walk (eight rows per
-    workgroup, a pair per wave, each key tile staged once in LDS; 2051 is
-    not a multiple of eight, so the last workgroup has absent pairs).  The
-    first 64 rows alone take the one-pair walk.  Every row's scores must be
+    """4093 rows with ragged ranges take the shared walk (eight rows per
+    workgroup, a pair per wave, each key tile staged once in LDS; 4093 is
+    not a multiple of eight, so the last workgroup has a half pair and an
+    absent one).  The first 64 rows alone take the one-pair walk.  Every row's scores must be
     the same bits on both walks, every threshold must be the walk's own
     sampled score, and sampled rows (the last ones among them) must match
     the oracle."""
     import dataclasses
-    case = synth.random_case("shared_walk", 2051, 20000, seed=31, K=2048, min_len=0, max_len=20000)
+    import scoring_exact_top_amd as lib
+    assert lib.prefill_geometry(4093)[0] == 1 and lib.prefill_geometry(64)[0] == 0
+    case = synth.random_case("shared_walk", 4093, 20000, seed=31, K=2048, min_len=0, max_len=20000)
     case.row_start[1::8] = case.row_start[0::8]        # some pairs share their start
     case.row_end[1::8] = np.maximum(case.row_end[1::8], case.row_start[1::8])
     log("case", case.name, case.Q, case.N)
@@ -179,6 +181,8 @@ def test_shared_walk_edge_modes(mode, e4m3):
     the repair.  Every row against the oracle, with the GPU's scores (K =
     1024 of ragged rows puts some K-th scores near 0, where the selection is
     judged at the scores' rounding bound)."""
+    import scoring_exact_top_amd as lib
+    assert lib.prefill_geometry(2048) == (1, 2, 2)
     N = 6000 if mode == "keep_all" else 3000
     case = synth.random_case("shared_" + mode, 2048, N, seed=33, K=1024, min_len=0)
     opts = {}
