@@ -134,13 +134,13 @@ typedef struct {
 size_t idx_topk_prefill_workspace(int32_t Q, int32_t N, int32_t K);
 
 /*
- * How the main kernel walks Q rows (diagnostic, host only, no GPU call): *shared = 1 for the
- * shared walk (eight rows per workgroup, each key tile staged once in LDS for four row pairs),
- * 0 for the one-pair walk; *splits = workgroups each row's key tiles are split over;
+ * How the main kernel walks Q rows over N keys (diagnostic, host only, no GPU call): *shared = 1
+ * for the shared walk (eight rows per workgroup, each key tile staged once in LDS for four row
+ * pairs), 0 for the one-pair walk; *splits = workgroups each row's key tiles are split over;
  * *segments = candidate segments per row.  Any output pointer may be NULL.  Returns IDX_OK, or
- * IDX_EINVAL for Q < 0.
+ * IDX_EINVAL for Q < 0 or N < 0.
  */
-int idx_topk_prefill_geometry(int32_t Q, int32_t* shared, int32_t* splits, int32_t* segments);
+int idx_topk_prefill_geometry(int32_t Q, int32_t N, int32_t* shared, int32_t* splits, int32_t* segments);
 
 /*
  * Prefill: top-K ids per query row (Fusing Indexer Scoring and Exact Top-k page, "2.3 Problem

@@ -56,7 +56,7 @@ class Stats(ctypes.Structure):
 _lib.idx_topk_prefill_workspace.restype = _sz
 _lib.idx_topk_prefill_workspace.argtypes = [_i32, _i32, _i32]
 _lib.idx_topk_prefill_geometry.restype = _i32
-_lib.idx_topk_prefill_geometry.argtypes = [_i32, ctypes.POINTER(_i32), ctypes.POINTER(_i32), ctypes.POINTER(_i32)]
+_lib.idx_topk_prefill_geometry.argtypes = [_i32, _i32, ctypes.POINTER(_i32), ctypes.POINTER(_i32), ctypes.POINTER(_i32)]
 _lib.idx_topk_prefill.restype = ctypes.c_int
 _lib.idx_topk_prefill.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _vp, _sz,
                                   _vp]
@@ -126,11 +126,11 @@ def prefill_workspace_bytes(Q: int, N: int, K: int) -> int:
     return int(_lib.idx_topk_prefill_workspace(Q, N, K))
 
 
-def prefill_geometry(Q: int):
-    """(shared, splits, segments) of the main kernel's walk for Q rows; see
-    idx_topk_prefill_geometry in include/idx_topk.h."""
+def prefill_geometry(Q: int, N: int):
+    """(shared, splits, segments) of the main kernel's walk for Q rows over
+    N keys; see idx_topk_prefill_geometry in include/idx_topk.h."""
     sh, sp, sg = _i32(), _i32(), _i32()
-    _check(_lib.idx_topk_prefill_geometry(Q, ctypes.byref(sh), ctypes.byref(sp), ctypes.byref(sg)))
+    _check(_lib.idx_topk_prefill_geometry(Q, N, ctypes.byref(sh), ctypes.byref(sp), ctypes.byref(sg)))
     return int(sh.value), int(sp.value), int(sg.value)
 
 

@@ -23,7 +23,7 @@ static PrefillLayout prefill_layout(int32_t Q, int32_t N, bool unfused = false) 
   L.ctrl = o; o = align256(o + sizeof(uint32_t) * kCtrlWords);
   L.tau = o; o = align256(o + sizeof(float) * (size_t)Q);
   L.fail = o; o = align256(o + sizeof(int32_t) * (size_t)Q);
-  const WalkGeom g = prefill_geom(Q);
+  const WalkGeom g = prefill_geom(Q, N);
   const size_t nseg = (size_t)g.nseg;
   const size_t cand = (size_t)Q * nseg * (size_t)prefill_seg_cap(g.nseg);
   L.cand = o; o = align256(o + sizeof(uint2) * cand);
@@ -66,7 +66,7 @@ static int prefill_common(const uint8_t* q, const float* q_scale, const uint8_t*
   A.fail_list = reinterpret_cast<int32_t*>(ws + L.fail);
   A.cand = reinterpret_cast<uint2*>(ws + L.cand);
   A.segn = reinterpret_cast<uint32_t*>(ws + L.segn);
-  const WalkGeom g = prefill_geom(Q);
+  const WalkGeom g = prefill_geom(Q, N);
   A.S = g.S;
   A.nseg = g.nseg;
   A.shared = g.shared;
@@ -130,9 +130,10 @@ extern "C" size_t idx_topk_prefill_workspace(int32_t Q, int32_t N, int32_t K) {
   return prefill_layout(Q, N).total;
 }
 
-extern "C" int idx_topk_prefill_geometry(int32_t Q, int32_t* shared, int32_t* splits, int32_t* segments) {
-  if (Q < 0) return IDX_EINVAL;
-  const WalkGeom g = prefill_geom(Q);
+extern "C" int idx_topk_prefill_geometry(int32_t Q, int32_t N, int32_t* shared, int32_t* splits,
+                                         int32_t* segments) {
+  if (Q < 0 || N < 0) return IDX_EINVAL;
+  const WalkGeom g = prefill_geom(Q, N);
   if (shared) *shared = g.shared;
   if (splits) *splits = g.S;
   if (segments) *segments = g.nseg;

@@ -37,34 +37,28 @@ constexpr int kSelRegs = 40;  // keys per thread of the select kernel, all S <= 
 
 constexpr int kMaxSeg = kWaves * kMaxSplit;  // candidate segments per row, at most
 
-// Splits of the main kernel for Q rows: at least 512 workgroups (two per
-// CU) when possible.
-__host__ __device__ inline int prefill_split(int rows) {
-  const int pairs = (rows + 1) / 2;
-  int s = 1;
-  while (s < kMaxSplit && pairs * s < 512) s *= 2;
-  return s;
-}
-
-// Geometry of the main kernel's walk.  Shared walk: a workgroup takes
-// kSharedRows rows (a pair per wave), each tile is staged once in LDS for
-// all four waves, and a row's candidates of one split go to one segment
-// (nseg = S).  One-pair walk: a workgroup takes one pair and splits its
-// tiles over its waves (nseg = kWaves * S), which needs four times fewer
-// splits for the same number of workgroups.  Two workgroups per CU are
-// resident (kRound in all), so a launch takes ceil(workgroups / kRound)
-// rounds, and its time goes as rounds x (rows per workgroup / S), the tiles
-// one workgroup walks.  The shared walk does that work about 5% faster
-// (its tiles come from LDS; 3.26 against 3.46 ms at 4096 x 131072), but its
-// workgroups are four times coarser, so a partly filled last round costs
-// more, and each split samples its rows again.  The walk of lower cost is
-// taken, the shared one only with S <= 2 and from kSharedMinRows rows.
-// Measured at 131072 keys, ms per call, shared against one-pair: 2048 rows
-// 1.72 against 1.80, 3072 rows 2.95 against 2.58 (the shared walk's 768
-// workgroups fill 1.5 rounds), 4096 rows 3.26 against 3.46.
+// Geometry of the main kernel's walk.  One-pair walk: a workgroup takes
+// one pair of rows and splits its tiles over its four waves and over S
+// workgroups (S = 1, 2, 4, 8; nseg = kWaves * S segments per row).  Shared
+// walk: a workgroup takes kSharedRows rows (a pair per wave), each tile is
+// staged once in LDS for all four waves, and a row's candidates of one
+// split go to one segment (S = 1, 2; nseg = S).
+//
+// Two workgroups per CU are resident (kRound in all), so a launch takes
+// ceil(workgroups / kRound) rounds, and its time goes as rounds x (the
+// tiles one workgroup walks + its prologue, about kWgFixed tiles' worth).
+// Each split samples its rows again (about 2% per extra split), and the
+// shared walk does its work about 5% faster (its tiles come from LDS; 3.26
+// against 3.46 ms at 4096 x 131072) with four times coarser workgroups.  The
+// geometry of lowest cost is taken, the shared walk only from
+// kSharedMinRows rows.  Measured at 131072 keys, ms per call, shared against
+// one-pair: 2048 rows 1.72 against 1.80, 3072 rows 2.95 against 2.58 (the
+// shared walk's 768 workgroups fill 1.5 rounds), 4096 rows 3.26 against
+// 3.46; the cost picks the faster walk at 2560, 3584, 5120 and 6144 rows.
 constexpr int kSharedRows = 2 * kWaves;
 constexpr int kSharedMinRows = 2048;
 constexpr int kRound = 512;
+constexpr int kWgFixed = 8;
 
 struct WalkGeom {
   int shared, S, nseg;
@@ -72,23 +66,34 @@ struct WalkGeom {
 
 __host__ __device__ inline int64_t walk_rounds(int64_t wgs) { return (wgs + kRound - 1) / kRound; }
 
-__host__ __device__ inline WalkGeom prefill_geom(int rows) {
-  const int s1 = prefill_split(rows);
-  const WalkGeom pair{0, s1, kWaves * s1};
-  if (rows < kSharedMinRows) return pair;
+// rounds x (pair-tiles per workgroup + prologue) x (1 + 2% per extra split)
+// x (20 for the one-pair walk, 19 for the shared walk)
+__host__ __device__ inline int64_t walk_cost(int64_t wgs, int64_t pair_tiles, int s, int walk) {
+  return walk_rounds(wgs) * (pair_tiles + kWgFixed) * (50 + s - 1) * walk;
+}
+
+__host__ __device__ inline WalkGeom prefill_geom(int rows, int nkeys) {
+  const int64_t tiles = nkeys > 0 ? ((int64_t)nkeys + 63) / 64 : 1;
   const int64_t pairs = (rows + 1) / 2, groups = (rows + kSharedRows - 1) / kSharedRows;
-  // cost = rounds x (rows per workgroup x 8 / S), x 20 for the one-pair walk
-  // and x 19 for the shared walk
-  int64_t best = 20 * walk_rounds(pairs * s1) * (2 * 8 / s1);
-  int best_s = 0;
-  for (int s = 1; s <= 2; s *= 2) {
-    const int64_t c = 19 * walk_rounds(groups * s) * (kSharedRows * 8 / s);
-    if (c < best) {
-      best = c;
-      best_s = s;
+  WalkGeom best{0, 1, kWaves};
+  int64_t best_cost = walk_cost(pairs, tiles, 1, 20);
+  for (int s = 2; s <= kMaxSplit; s *= 2) {
+    const int64_t c = walk_cost(pairs * s, (tiles + s - 1) / s, s, 20);
+    if (c < best_cost) {
+      best_cost = c;
+      best = WalkGeom{0, s, kWaves * s};
     }
   }
-  return best_s ? WalkGeom{1, best_s, best_s} : pair;
+  if (rows >= kSharedMinRows) {
+    for (int s = 1; s <= 2; s *= 2) {
+      const int64_t c = walk_cost(groups * s, (4 * tiles + s - 1) / s, s, 19);
+      if (c < best_cost) {
+        best_cost = c;
+        best = WalkGeom{1, s, s};
+      }
+    }
+  }
+  return best;
 }
 
 // Entries of one candidate segment for nseg segments per row: the larger of

@@ -222,17 +222,21 @@ def test_noalloc_decode_argument_errors(lib):
 
 
 def test_prefill_walk_geometry():
-    """The walk the main kernel takes for Q rows (host logic, no GPU): the
-    one-pair walk below 2048 rows, with splits until 512 workgroups; from
-    2048 rows the walk of lower cost in rounds of 512 resident workgroups,
-    so the shared walk at 2048 and 4096 rows but not at 3072 (whose 384 or
-    768 shared workgroups would leave a round part empty); segments per row
-    are the splits (shared) or four per split (one-pair)."""
+    """The walk the main kernel takes for Q rows over N keys (host logic, no
+    GPU): the geometry of lowest cost in rounds of 512 resident workgroups.
+    Rows that fill whole rounds keep one split (1024 rows) or the shared
+    walk (4096); odd counts take more splits so that the last round is not
+    mostly empty (1200 rows: four splits, 2400 workgroups); 3072 rows avoid
+    the shared walk, whose 384 or 768 workgroups would leave a round part
+    empty; short rows spread over more splits (64 rows: eight)."""
     import scoring_exact_top_amd as lib
-    want = {1: (0, 8, 32), 64: (0, 8, 32), 256: (0, 4, 16), 1024: (0, 1, 4), 2047: (0, 1, 4),
-            2048: (1, 2, 2), 3072: (0, 1, 4), 4093: (1, 1, 1), 4096: (1, 1, 1), 5120: (0, 1, 4),
-            8192: (1, 1, 1)}
-    for Q, g in want.items():
-        assert lib.prefill_geometry(Q) == g, (Q, lib.prefill_geometry(Q), g)
-    with pytest.raises(lib.IdxTopkError):
-        lib.prefill_geometry(-1)
+    want = {(1, 8192): (0, 8, 32), (64, 8192): (0, 8, 32), (256, 163840): (0, 4, 16),
+            (512, 163840): (0, 2, 8), (1024, 163840): (0, 1, 4), (1200, 131072): (0, 4, 16),
+            (2048, 131072): (1, 2, 2), (2560, 131072): (0, 2, 8), (3072, 131072): (0, 1, 4),
+            (4093, 20000): (1, 1, 1), (4096, 131072): (1, 1, 1), (5120, 131072): (0, 1, 4),
+            (6144, 131072): (1, 2, 2), (8192, 131072): (1, 1, 1)}
+    for (Q, N), g in want.items():
+        assert lib.prefill_geometry(Q, N) == g, (Q, N, lib.prefill_geometry(Q, N), g)
+    for bad in ((-1, 8), (8, -1)):
+        with pytest.raises(lib.IdxTopkError):
+            lib.prefill_geometry(*bad)

@@ -147,7 +147,7 @@ def test_shared_walk_bit_for_bit_with_the_pair_walk(e4m3):
     the oracle."""
     import dataclasses
     import scoring_exact_top_amd as lib
-    assert lib.prefill_geometry(4093)[0] == 1 and lib.prefill_geometry(64)[0] == 0
+    assert lib.prefill_geometry(4093, 20000)[0] == 1 and lib.prefill_geometry(64, 20000)[0] == 0
     case = synth.random_case("shared_walk", 4093, 20000, seed=31, K=2048, min_len=0, max_len=20000)
     case.row_start[1::8] = case.row_start[0::8]        # some pairs share their start
     case.row_end[1::8] = np.maximum(case.row_end[1::8], case.row_start[1::8])
@@ -182,8 +182,8 @@ def test_shared_walk_edge_modes(mode, e4m3):
     1024 of ragged rows puts some K-th scores near 0, where the selection is
     judged at the scores' rounding bound)."""
     import scoring_exact_top_amd as lib
-    assert lib.prefill_geometry(2048) == (1, 2, 2)
     N = 6000 if mode == "keep_all" else 3000
+    assert lib.prefill_geometry(2048, N) == (1, 2, 2)
     case = synth.random_case("shared_" + mode, 2048, N, seed=33, K=1024, min_len=0)
     opts = {}
     if mode == "overflow":
