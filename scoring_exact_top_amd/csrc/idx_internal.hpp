@@ -33,7 +33,8 @@ constexpr int kMaxGridY = 65535;
 constexpr int kCandCap = 8192;
 constexpr int kManyCands = 4096;  // rows keeping more are counted (idx_topk_stats.many_cands)
 constexpr int kMaxSplit = 8;
-constexpr int kSelRegs = 40;  // keys per thread of the select kernel, all S <= kMaxSplit
+constexpr int kSelRegs = 40;        // keys per thread of the select kernel, any nseg <= kMaxSeg
+constexpr int kSelRegsShared = 33;  // ... for nseg <= 2 (seg_cap 8320 or 4160 over 256 or 128 threads)
 
 constexpr int kMaxSeg = kWaves * kMaxSplit;  // candidate segments per row, at most
 

@@ -563,6 +563,7 @@ __global__ __launch_bounds__(kWG, 2) void k_prefill_pair(PrefillArgs A) {
 // the first dropped position (segments drop only their latest candidates),
 // so that they are the lowest tied ids of the whole row.  Massive ties at
 // the boundary thus need no repair.  Rows that fail go to the failure list.
+template <int M>
 __global__ __launch_bounds__(kWG) void k_prefill_select(PrefillArgs A) {
   __shared__ SelShared sh;
   __shared__ uint32_t s_segn[kWaves * kMaxSplit];
@@ -608,18 +609,18 @@ __global__ __launch_bounds__(kWG) void k_prefill_select(PrefillArgs A) {
     const uint32_t tps = (uint32_t)(kWG / nseg);
     const uint32_t g = (uint32_t)tid / tps;
     const uint32_t first = g * (uint32_t)A.seg_cap;
-    const RegLayout lay{first + (uint32_t)tid % tps, tps, first + s_segn[g], kSelRegs};
+    const RegLayout lay{first + (uint32_t)tid % tps, tps, first + s_segn[g], (uint32_t)M};
     const int64_t row = (int64_t)t * nseg * A.seg_cap;
-    uint32_t key[kSelRegs];
-    int32_t id[kSelRegs];
+    uint32_t key[M];
+    int32_t id[M];
     load_list_regs(key, id, A.cand + row, (uint32_t)(nseg * A.seg_cap), lay,
                    [](uint32_t x) { return f2key(__uint_as_float(x)); });
     const auto kf = [&](int j) { return key[j]; };
-    const RangeSel sel = (n > (uint32_t)kr) ? range_select_regs<kSelRegs>(kf, lay, kr, sh, tid)
+    const RangeSel sel = (n > (uint32_t)kr) ? range_select_regs<M>(kf, lay, kr, sh, tid)
                                            : RangeSel{1u, 0xFFFFFFFFu, kr, (int)n};
     const uint32_t idlo = tie_bound_regs(key, id, lay, sel, sh, tid);
     if (drop >= sel.lo) {
-      const uint32_t theta = range_min_regs<kSelRegs>(kf, lay, sel, sh, tid);
+      const uint32_t theta = range_min_regs<M>(kf, lay, sel, sh, tid);
       ok = drop <= theta;
       if (drop == theta) {  // tied keys were dropped: the taken ones must precede them
         const auto tk = [&](int j) {  // recomputed per use (see tie_bound_regs)
@@ -629,7 +630,7 @@ __global__ __launch_bounds__(kWG) void k_prefill_select(PrefillArgs A) {
         };
         uint32_t mn = 0xFFFFFFFFu;  // smallest ~id taken at theta = ~(largest id)
 #pragma unroll
-        for (int j = 0; j < kSelRegs; ++j) mn = min(mn, tk(j));
+        for (int j = 0; j < M; ++j) mn = min(mn, tk(j));
 #pragma unroll
         for (int o = 32; o > 0; o >>= 1) mn = min(mn, (uint32_t)__shfl_xor((int)mn, o, 64));
         if (lane == 0) sh.wsum[0][tid >> 6] = mn;
@@ -970,7 +971,14 @@ int launch_prefill(const PrefillArgs& A, hipStream_t stream) {
     else
       launch_main<kPairFused>(A, stream, e0, e1);
   }
-  hipLaunchKernelGGL(k_prefill_select, dim3(A.Q), dim3(kWG), 0, stream, A);
+  // candidate slots per thread: a segment's capacity over its threads
+  // (256 / nseg of them), 33 for the shared walk's one or two segments per
+  // row, up to 40 for the one-pair walk's 4..32 (fewer registers let more
+  // rows run at once)
+  if (A.nseg <= 2)
+    hipLaunchKernelGGL(k_prefill_select<kSelRegsShared>, dim3(A.Q), dim3(kWG), 0, stream, A);
+  else
+    hipLaunchKernelGGL(k_prefill_select<kSelRegs>, dim3(A.Q), dim3(kWG), 0, stream, A);
   if (A.keep_all) return hipGetLastError() == hipSuccess ? IDX_OK : IDX_EHIP;  // nothing can need repair
   // the slotted failures rescored two per workgroup: enough workgroups for
   // every slot pair, at least two per CU for few failures
