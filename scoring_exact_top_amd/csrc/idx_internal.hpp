@@ -34,7 +34,7 @@ constexpr int kCandCap = 8192;
 constexpr int kManyCands = 4096;  // rows keeping more are counted (idx_topk_stats.many_cands)
 constexpr int kMaxSplit = 8;
 constexpr int kSelRegs = 40;        // keys per thread of the select kernel, any nseg <= kMaxSeg
-constexpr int kSelRegsShared = 33;  // ... for nseg <= 2 (seg_cap 8320 or 4160 over 256 or 128 threads)
+constexpr int kSelRegsFew = 33;     // ... for nseg <= 4 (seg_cap 8256, 4160, 2112 over 256, 128, 64 threads)
 
 constexpr int kMaxSeg = kWaves * kMaxSplit;  // candidate segments per row, at most
 

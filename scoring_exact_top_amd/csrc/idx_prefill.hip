@@ -972,11 +972,10 @@ int launch_prefill(const PrefillArgs& A, hipStream_t stream) {
       launch_main<kPairFused>(A, stream, e0, e1);
   }
   // candidate slots per thread: a segment's capacity over its threads
-  // (256 / nseg of them), 33 for the shared walk's one or two segments per
-  // row, up to 40 for the one-pair walk's 4..32 (fewer registers let more
-  // rows run at once)
-  if (A.nseg <= 2)
-    hipLaunchKernelGGL(k_prefill_select<kSelRegsShared>, dim3(A.Q), dim3(kWG), 0, stream, A);
+  // (256 / nseg of them), 33 for one, two or four segments per row, up to
+  // 40 for 8..32 (fewer registers let more rows run at once)
+  if (A.nseg <= 4)
+    hipLaunchKernelGGL(k_prefill_select<kSelRegsFew>, dim3(A.Q), dim3(kWG), 0, stream, A);
   else
     hipLaunchKernelGGL(k_prefill_select<kSelRegs>, dim3(A.Q), dim3(kWG), 0, stream, A);
   if (A.keep_all) return hipGetLastError() == hipSuccess ? IDX_OK : IDX_EHIP;  // nothing can need repair
