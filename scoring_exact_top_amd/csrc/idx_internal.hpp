@@ -16,11 +16,11 @@ constexpr int kSampleTarget = IDX_TOPK_SAMPLE_TARGET;
 constexpr int kMaxSamples = 2048;  // longer rows widen the stride instead
 
 // Candidates per row ("4.3 Candidate layout: warp-private segments" and "4.5
-// Overflow spill area"): the main kernel splits each row pair's key tiles
-// over S workgroups (S = 1 when there are rows enough to fill the chip, up
-// to kMaxSplit for few rows: parallelism along the keys, "10. The
-// optimization target after fusion"), and each (split, wave) stores its
-// candidates straight into a private workspace segment (the pages' on-chip
+// Overflow spill area"): the main kernel splits each row's key tiles over S
+// workgroups (parallelism along the keys for few rows, "10. The
+// optimization target after fusion"), and each wave that walks a share of
+// a row stores that share's candidates straight into a private workspace
+// segment: nseg segments per row (see prefill_geom; the pages' on-chip
 // store and spill area become one area in device memory).  The
 // certificate's capacity per row is kCandCap (the default of the cand_cap
 // test knob); a segment is sized so that a row short enough to keep all its
@@ -183,7 +183,7 @@ struct PrefillArgs {
   int32_t* out;         // [Q][K]
   uint8_t* kt;          // [ntiles][8][64][16] keys relaid in MFMA lane order
   uint2* cand;          // [Q][nseg][seg_cap] candidates: (FP32 score bits, key id)
-  uint32_t* segn;       // [Q][kWaves*S][4]: entries stored, key of the largest dropped candidate
+  uint32_t* segn;       // [Q][nseg][4]: entries stored, key of the largest dropped candidate
                         // (0: none), position of the first dropped one, unused
   int32_t S, seg_cap, seg_eff;  // splits, segment stride, usable entries per segment
   int32_t shared, nseg;         // shared walk (kSharedRows rows per workgroup); segments per row

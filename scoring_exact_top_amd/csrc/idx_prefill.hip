@@ -553,8 +553,8 @@ __global__ __launch_bounds__(kWG, 2) void k_prefill_pair(PrefillArgs A) {
 // ------------------------------------------------------------------ select
 
 // One workgroup per row, after the main kernel.  The row's candidates (its
-// kWaves*S segments: segment g in threads [g*tps, (g+1)*tps), tps =
-// 256/nseg, each thread every tps-th entry) are loaded into registers and
+// nseg segments: segment g in threads [g*tps, (g+1)*tps), tps = 256/nseg,
+// each thread every tps-th entry, M slots per thread) are loaded into registers and
 // the K largest selected, ties at the K-th score going to the lowest ids.
 // Certificate ("3.2 Sampled threshold", made exact for capacity drops):
 // this is the row's exact top-K iff there were at least K candidates and
