@@ -13,7 +13,7 @@ static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 static inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 struct PrefillLayout {
-  size_t ctrl, tau, fail, cand, segn, scratch, rhist, rrow, reqc, kt, dense, total;
+  size_t ctrl, tau, fail, cand, segn, scratch, rhist, rrow, kt, dense, total;
 };
 
 // unfused: also the [Q][N] FP32 score matrix of the unfused comparator.
@@ -29,9 +29,8 @@ static PrefillLayout prefill_layout(int32_t Q, int32_t N, bool unfused = false) 
   L.cand = o; o = align256(o + sizeof(uint2) * cand);
   L.segn = o; o = align256(o + 4 * sizeof(uint32_t) * (size_t)Q * nseg);
   L.scratch = o; o = align256(o + sizeof(uint32_t) * (size_t)repair_rows(Q, N) * (size_t)repair_stride(N));
-  L.rhist = o; o = align256(o + sizeof(uint32_t) * (size_t)repair_slots(Q, N) * 4 * 256);
+  L.rhist = o; o = align256(o + sizeof(uint32_t) * (size_t)repair_slots(Q, N) * kRepairDigits * 256);
   L.rrow = o; o = align256(o + sizeof(uint32_t) * (size_t)repair_slots(Q, N) * kRowWords);
-  L.reqc = o; o = align256(o + sizeof(uint32_t) * (size_t)repair_slots(Q, N) * (size_t)((N + kRepairChunk - 1) / kRepairChunk));
   L.kt = o; o = align256(o + (size_t)((N + 63) / 64) * 64 * 128);
   L.dense = o; if (unfused) o = align256(o + sizeof(float) * (size_t)Q * (size_t)N);
   L.total = o;
@@ -74,7 +73,6 @@ static int prefill_common(const uint8_t* q, const float* q_scale, const uint8_t*
   A.scratch = reinterpret_cast<uint32_t*>(ws + L.scratch);
   A.rhist = reinterpret_cast<uint32_t*>(ws + L.rhist);
   A.rrow = reinterpret_cast<uint32_t*>(ws + L.rrow);
-  A.reqc = reinterpret_cast<uint32_t*>(ws + L.reqc);
   A.rslots = repair_slots(Q, N);
   A.rstride = repair_stride(N);
   A.kt = reinterpret_cast<uint8_t*>(ws + L.kt);

@@ -113,14 +113,25 @@ __host__ __device__ inline int prefill_seg_cap(int nseg) {
 constexpr int kRepairChunk = 4096;
 constexpr int kRepairChunkTiles = kRepairChunk / 64;
 constexpr int kRepairGrid = 256;  // one workgroup per CU; items are strided over the grid
-constexpr int kRepairPassGrid = 1024;  // digit passes, tie count and emit: four workgroups per CU
+constexpr int kRepairPassGrid = 1024;  // digit pass and gather: four workgroups per CU
 constexpr int kRepairWalkWGs = 512;    // rescoring walk: the workgroups of one round, two per CU
+// The chip-wide passes resolve the top two 8-bit digits of the K-th key;
+// the keys that share them with it (the boundary group) are gathered into
+// the failed row's candidate area, which the fast path no longer needs, and
+// one workgroup per row selects among them in registers.  A larger group
+// (massive ties) is selected by that workgroup from the row's scratch.
+constexpr int kRepairDigits = 2;
+constexpr int kRepairGroupCap = kCandCap;  // gathered boundary keys per row (<= its candidate area)
+constexpr int kRepairGroupRegs = kRepairGroupCap / kWG;
+constexpr int kRepairFinalGrid = 1024;
 
-// Words kept per slotted repair row (PrefillArgs::rrow): the emit's output
-// counters, then two groups of four holding the row's selection state
-// after an odd and after an even number of digits (prefix, mask, rem,
-// done: every key with (key & mask) > prefix is taken, and rem more among
-// those equal to it; done: the boundary group is taken whole).
+// Words kept per slotted repair row (PrefillArgs::rrow): the gather's
+// output counters (keys above the boundary emitted; boundary keys emitted
+// or gathered), then two groups of four holding the row's selection state
+// after one and after two digits (prefix, mask, rem, and the size of the
+// boundary group or 0xFFFFFFFF once that group is taken whole: every key
+// with (key & mask) > prefix is taken, and rem more among those equal to
+// it).
 constexpr int kRowGt = 0, kRowEq = 1, kRowState = 4;
 constexpr int kRowWords = 12;
 constexpr int kRepairFallback = 256;
@@ -191,9 +202,8 @@ struct PrefillArgs {
   int32_t* fail_list;   // [Q]
   uint32_t* ctrl;       // kCtrlWords
   uint32_t* scratch;    // [repair_rows][repair_stride(N)] repair scores (order-preserving keys)
-  uint32_t* rhist;      // [rslots][4][256] digit histograms of each slotted repair row
+  uint32_t* rhist;      // [rslots][kRepairDigits][256] digit histograms of each slotted repair row
   uint32_t* rrow;       // [rslots][kRowWords] counters and selection state of each slotted repair row
-  uint32_t* reqc;       // [rslots][ceil(N/kRepairChunk)] keys tied at the K-th score per chunk
   int32_t rslots;
   int64_t rstride;
   float* dbg_scores;    // [Q][N] or null

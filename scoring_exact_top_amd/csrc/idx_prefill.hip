@@ -36,7 +36,7 @@ __global__ __launch_bounds__(kWG) void k_relayout_keys(PrefillArgs A) {
         A.tau[t] = (s >= 0 && s <= e && e <= A.N) ? -INFINITY : INFINITY;
       }
     } else {  // the main kernel writes the thresholds; the repair state starts at zero
-      for (int64_t i = chunk; i < (int64_t)A.rslots * 1024; i += stride) A.rhist[i] = 0u;
+      for (int64_t i = chunk; i < (int64_t)A.rslots * kRepairDigits * 256; i += stride) A.rhist[i] = 0u;
       for (int64_t i = chunk; i < (int64_t)A.rslots * kRowWords; i += stride) A.rrow[i] = 0u;
     }
   }
@@ -52,7 +52,7 @@ __global__ __launch_bounds__(kWG) void k_relayout_keys(PrefillArgs A) {
 __global__ __launch_bounds__(kWG) void k_prefill_tau(PrefillArgs A) {
   const int64_t i0 = (int64_t)blockIdx.x * kWG + threadIdx.x, stride = (int64_t)gridDim.x * kWG;
   if (blockIdx.x == 0) clear_ctrl(A.ctrl, threadIdx.x);
-  for (int64_t i = i0; i < (int64_t)A.rslots * 1024; i += stride) A.rhist[i] = 0u;
+  for (int64_t i = i0; i < (int64_t)A.rslots * kRepairDigits * 256; i += stride) A.rhist[i] = 0u;
   for (int64_t i = i0; i < (int64_t)A.rslots * kRowWords; i += stride) A.rrow[i] = 0u;
   for (int64_t t = i0; t < A.Q; t += stride) {
     const int s = A.row_start[t], e = A.row_end[t];
@@ -522,7 +522,7 @@ __global__ __launch_bounds__(kWG, 2) void k_prefill_pair(PrefillArgs A) {
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
       const uint32_t h = s_rhist[r][tid];
-      if (h && t_of[r] >= 0) atomicAdd(&A.rhist[(int64_t)slot[r] * 4 * 256 + tid], h);
+      if (h && t_of[r] >= 0) atomicAdd(&A.rhist[(int64_t)slot[r] * kRepairDigits * 256 + tid], h);
     }
   } else if constexpr (MODE != kPairDense) {
     // publish this wave's segment: entries stored, the order-preserving key of
@@ -573,6 +573,11 @@ __global__ __launch_bounds__(kWG) void k_prefill_select(PrefillArgs A) {
   uint32_t* stats = stat_copy(A.ctrl, blockIdx.x);
   int32_t* out = A.out + (int64_t)t * A.K;
   if (tid == 0) atomicAdd(&stats[kStRows], 1u);
+  // the segment records are loaded beside the row's range (one round trip
+  // for both; for an invalid row they are read and unused)
+  const int nseg = A.nseg;
+  uint4 e = make_uint4(0u, 0u, 0u, 0u);
+  if (tid < nseg) e = *reinterpret_cast<const uint4*>(A.segn + 4 * ((int64_t)t * nseg + tid));
   const int rs_t = A.row_start[t], re_t = A.row_end[t];
   if (rs_t < 0 || rs_t > re_t || re_t > A.N) {
     for (int i = tid; i < A.K; i += kWG) out[i] = -1;
@@ -582,10 +587,8 @@ __global__ __launch_bounds__(kWG) void k_prefill_select(PrefillArgs A) {
     }
     return;
   }
-  const int nseg = A.nseg;
   uint32_t dk = 0u, fd = 0xFFFFFFFFu;
   if (tid < nseg) {
-    const uint4 e = *reinterpret_cast<const uint4*>(A.segn + 4 * ((int64_t)t * nseg + tid));
     s_segn[tid] = e.x;
     dk = e.y;
     fd = e.y ? e.z : 0xFFFFFFFFu;
@@ -666,23 +669,28 @@ __global__ __launch_bounds__(kWG) void k_prefill_select(PrefillArgs A) {
 // the digit histogram of a row is summed in device memory over its chunks;
 // the next launch advances the row's selection state by that digit (once
 // per row and workgroup, from the state the launch before stored) and its
-// chunk-0 item stores the result for the launch after.  The stored states
-// alternate between two word groups, so a launch never overwrites the one
-// it reads.
+// chunk-0 item stores the result for the launch after.  The two digits'
+// states go to two word groups, so a launch never overwrites the one it
+// reads.  After two digits the gather writes out every key above the
+// boundary prefix and collects the boundary group; the final kernel, one
+// workgroup per row, selects the rest of the row's top-K among them.
 
 struct RepairSel {
   uint32_t prefix, mask;
   int rem;
-  bool done;
+  int group;  // keys with (key & mask) == prefix
+  bool done;  // the boundary group is taken whole (rem == group)
 };
 
 __device__ __forceinline__ RepairSel load_state(const uint32_t* rw, int buf) {
   const uint32_t* w = rw + kRowState + 4 * buf;
-  return RepairSel{w[0], w[1], (int)w[2], w[3] != 0u};
+  const bool done = w[3] == 0xFFFFFFFFu;
+  return RepairSel{w[0], w[1], (int)w[2], done ? (int)w[2] : (int)w[3], done};
 }
 
 __device__ __forceinline__ void store_state(uint32_t* rw, int buf, const RepairSel& s) {
-  *reinterpret_cast<uint4*>(rw + kRowState + 4 * buf) = make_uint4(s.prefix, s.mask, (uint32_t)s.rem, s.done ? 1u : 0u);
+  *reinterpret_cast<uint4*>(rw + kRowState + 4 * buf) =
+      make_uint4(s.prefix, s.mask, (uint32_t)s.rem, s.done ? 0xFFFFFFFFu : (uint32_t)s.group);
 }
 
 // A chunk kernel's current row: its id, range, keys kept and selection state.
@@ -691,10 +699,6 @@ struct RepairRow {
   RepairSel sel;
 };
 
-// Load slot f's row and its selection state after `digits` digits (1..4):
-// the state after digits-1 (the initial one for digits == 1, else as the
-// previous launch stored it) advanced by that digit's complete histogram.
-// Whole workgroup calls.
 __device__ __forceinline__ void repair_row_ids(RepairRow& row, const PrefillArgs& A, int f) {
   row.f = f;
   row.t = A.fail_list[f];
@@ -703,13 +707,17 @@ __device__ __forceinline__ void repair_row_ids(RepairRow& row, const PrefillArgs
   row.kr = min(A.K, row.L);
 }
 
+// Load slot f's row and its selection state after `digits` digits (1 or
+// 2): the state after digits-1 (the initial one for digits == 1, else as
+// the previous launch stored it) advanced by that digit's complete
+// histogram.  Whole workgroup calls.
 __device__ void repair_row_at(RepairRow& row, const PrefillArgs& A, int f, int digits, SelShared& sh, int tid) {
   repair_row_ids(row, A, f);
   const uint32_t* rw = A.rrow + (int64_t)f * kRowWords;
-  RepairSel s = digits == 1 ? RepairSel{0u, 0u, row.kr, row.L <= row.kr} : load_state(rw, (digits - 1) & 1);
+  RepairSel s = digits == 1 ? RepairSel{0u, 0u, row.kr, row.L, row.L <= row.kr} : load_state(rw, (digits - 1) & 1);
   if (!s.done) {
     __syncthreads();  // the previous item's reads of sh are done
-    sh.hist[tid] = A.rhist[((int64_t)f * 4 + digits - 1) * 256 + tid];
+    sh.hist[tid] = A.rhist[((int64_t)f * kRepairDigits + digits - 1) * 256 + tid];
     __syncthreads();
     find_bucket(sh, s.rem, tid);
     __syncthreads();
@@ -717,7 +725,8 @@ __device__ void repair_row_at(RepairRow& row, const PrefillArgs& A, int f, int d
     s.prefix |= sh.bucket << shift;
     s.mask |= 0xFFu << shift;
     s.rem -= (int)sh.above;
-    s.done = (int)sh.inbucket == s.rem;
+    s.group = (int)sh.inbucket;
+    s.done = s.group == s.rem;
   }
   row.sel = s;
 }
@@ -775,10 +784,9 @@ __device__ __forceinline__ void load_chunk(ChunkKeys& ck, const uint32_t* row, i
 
 __device__ __forceinline__ int chunk_pos(const ChunkKeys& ck, int j) { return ck.base + (j >> 2) * 4 * kWG + (j & 3); }
 
-// Digit pass P (1..3) over the slotted failed rows that are still open:
-// the histogram of digit P among the keys that share the boundary prefix
-// of the first P digits.
-template <int P>
+// Second digit over the slotted failed rows that are still open: the
+// histogram of bits 16..23 among the keys that share the K-th key's top
+// byte.
 __global__ __launch_bounds__(kWG) void k_prefill_repair_pass(PrefillArgs A) {
   __shared__ SelShared sh;
   const int tid = threadIdx.x;
@@ -791,59 +799,37 @@ __global__ __launch_bounds__(kWG) void k_prefill_repair_pass(PrefillArgs A) {
 #pragma unroll 1
   for (int64_t i = i0; i < i1; ++i) {
     const int f = (int)(i / cmax), c = (int)(i % cmax);
-    if (f != row.f) repair_row_at(row, A, f, P, sh, tid);
-    if (c == 0 && tid == 0) store_state(A.rrow + (int64_t)f * kRowWords, P & 1, row.sel);
+    if (f != row.f) repair_row_at(row, A, f, 1, sh, tid);
+    if (c == 0 && tid == 0) store_state(A.rrow + (int64_t)f * kRowWords, 1, row.sel);
     if (row.sel.done || c * kRepairChunk >= row.L) continue;
     ChunkKeys ck;
     load_chunk(ck, A.scratch + (int64_t)f * A.rstride, c, row.L, tid);
     __syncthreads();  // the previous item's reads of sh are done
     sh.hist[tid] = 0u;
     __syncthreads();
-    constexpr int shift = 24 - 8 * P;
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       const bool v = chunk_pos(ck, j) < row.L && (ck.v[j] & row.sel.mask) == row.sel.prefix;
-      hist_add(sh.hist, (ck.v[j] >> shift) & 255u, v);
+      hist_add(sh.hist, (ck.v[j] >> 16) & 255u, v);
     }
     __syncthreads();
     const uint32_t h = sh.hist[tid];
-    if (h) atomicAdd(&A.rhist[((int64_t)f * 4 + P) * 256 + tid], h);
+    if (h) atomicAdd(&A.rhist[((int64_t)f * kRepairDigits + 1) * 256 + tid], h);
   }
 }
 
-// Rows whose selection ends in a tie (after all four digits, fewer keys
-// are still needed than share the K-th score): count each chunk's keys
-// equal to that score, so that the emit can take the lowest positions.
-__global__ __launch_bounds__(kWG) void k_prefill_repair_ties(PrefillArgs A) {
-  __shared__ SelShared sh;
-  const int tid = threadIdx.x;
-  const uint32_t n_slot = min(__atomic_load_n(&A.ctrl[kCtrlFail], __ATOMIC_RELAXED), (uint32_t)A.rslots);
-  const int cmax = (A.N + kRepairChunk - 1) / kRepairChunk;
-  int64_t i0, i1;
-  item_run((int64_t)n_slot * cmax, i0, i1);
-  RepairRow row;
-  row.f = -1;
-#pragma unroll 1
-  for (int64_t i = i0; i < i1; ++i) {
-    const int f = (int)(i / cmax), c = (int)(i % cmax);
-    if (f != row.f) repair_row_at(row, A, f, 4, sh, tid);
-    if (c == 0 && tid == 0) store_state(A.rrow + (int64_t)f * kRowWords, 0, row.sel);
-    if (row.sel.done || c * kRepairChunk >= row.L) continue;
-    ChunkKeys ck;
-    load_chunk(ck, A.scratch + (int64_t)f * A.rstride, c, row.L, tid);
-    uint32_t m = 0u;
-#pragma unroll
-    for (int j = 0; j < 16; ++j) m += (chunk_pos(ck, j) < row.L && ck.v[j] == row.sel.prefix) ? 1u : 0u;
-    uint32_t tot;
-    block_exclusive_scan(m, sh, tid, tot);
-    if (tid == 0) A.reqc[(int64_t)f * cmax + c] = tot;
-  }
+// The failed row's candidate area holds its gathered boundary group:
+// (key, id) pairs, at most kRepairGroupCap of them.
+__device__ __forceinline__ uint2* repair_group(const PrefillArgs& A, int t) {
+  return A.cand + (int64_t)t * A.nseg * A.seg_cap;
 }
 
-// Write each slotted failed row's selection: keys above the boundary prefix
-// and `rem` keys equal to it (the lowest positions where the boundary is a
-// tie), positions from the row's counters.
-__global__ __launch_bounds__(kWG) void k_prefill_repair_emit(PrefillArgs A) {
+// After two digits: every key above the boundary prefix is written out
+// (positions from the row's counter, in any order), and so is the boundary
+// group when it is taken whole; otherwise the group is gathered for the
+// final kernel, unless it exceeds kRepairGroupCap (massive ties), when the
+// final kernel reads it from scratch instead.
+__global__ __launch_bounds__(kWG) void k_prefill_repair_gather(PrefillArgs A) {
   __shared__ SelShared sh;
   const int tid = threadIdx.x;
   const uint32_t n_slot = min(__atomic_load_n(&A.ctrl[kCtrlFail], __ATOMIC_RELAXED), (uint32_t)A.rslots);
@@ -857,30 +843,32 @@ __global__ __launch_bounds__(kWG) void k_prefill_repair_emit(PrefillArgs A) {
   for (int64_t i = i0; i < i1; ++i) {
     const int f = (int)(i / cmax), c = (int)(i % cmax);
     uint32_t* rw = A.rrow + (int64_t)f * kRowWords;
-    if (f != row.f) {
-      repair_row_ids(row, A, f);
-      row.sel = load_state(rw, 0);  // after all four digits
-    }
+    if (f != row.f) repair_row_at(row, A, f, 2, sh, tid);
     const int s0 = row.s0, L = row.L, kr = row.kr;
     const RepairSel& rs = row.sel;
     int32_t* out = A.out + (int64_t)row.t * A.K;
     if (c == 0) {
+      if (tid == 0) {
+        store_state(rw, 0, rs);
+        atomicAdd(&stats[kStRepaired], 1u);
+      }
       for (int j = kr + tid; j < A.K; j += kWG) out[j] = -1;
-      if (tid == 0) atomicAdd(&stats[kStRepaired], 1u);
     }
     if (c * kRepairChunk >= L) continue;
     ChunkKeys ck;
     load_chunk(ck, A.scratch + (int64_t)f * A.rstride, c, L, tid);
-    // count this chunk's winners in LDS, then reserve their output range
-    // with one device-memory atomic per class
+    const bool gather = !rs.done && rs.group <= kRepairGroupCap;  // uniform
     uint32_t gmask = 0u, emask = 0u;
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       const bool v = chunk_pos(ck, j) < L;
       const uint32_t mk = ck.v[j] & rs.mask;
       gmask |= (uint32_t)(v && mk > rs.prefix) << j;
-      emask |= (uint32_t)(v && mk == rs.prefix) << j;
+      emask |= (uint32_t)(v && mk == rs.prefix && (rs.done || gather)) << j;
     }
+    // count this chunk's keys of each class in LDS, then reserve their
+    // output range with one device-memory atomic per class
+    __syncthreads();  // the previous item's reads of sh are done
     if (tid == 0) { sh.gt_count = 0u; sh.eq_count = 0u; }
     __syncthreads();
     const uint32_t ng = (uint32_t)__popc(gmask), ne = (uint32_t)__popc(emask);
@@ -896,39 +884,70 @@ __global__ __launch_bounds__(kWG) void k_prefill_repair_emit(PrefillArgs A) {
     pg += sh.pad0;
     pe += sh.pad1;
     const int eq_base = kr - rs.rem;
-    if (!rs.done) {
-      // a tie: rank the chunk's tied keys in position order (k, thread, e),
-      // after the tied keys of the chunks before it
-      uint32_t before = 0u, tot;
-      for (int cc = tid; cc < c; cc += kWG) before += A.reqc[(int64_t)f * cmax + cc];
-      block_exclusive_scan(before, sh, tid, tot);
-      pe = tot;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const uint32_t mk = (emask >> (4 * k)) & 15u;
-        const uint32_t r = block_exclusive_scan((uint32_t)__popc(mk), sh, tid, tot);
-        uint32_t p = pe + r;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          if (mk >> e & 1u) {
-            if ((int)p < rs.rem) out[eq_base + p] = s0 + chunk_pos(ck, 4 * k + e);
-            ++p;
-          }
-        }
-        pe += tot;
-      }
-      emask = 0u;
-    }
+    uint2* grp = repair_group(A, row.t);
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       const int pos = chunk_pos(ck, j);
       if (gmask >> j & 1u) out[pg++] = s0 + pos;
       if (emask >> j & 1u) {
-        if ((int)pe < rs.rem) out[eq_base + pe] = s0 + pos;
+        if (rs.done) {
+          if ((int)pe < rs.rem) out[eq_base + pe] = s0 + pos;
+        } else if ((int)pe < kRepairGroupCap) {
+          grp[pe] = make_uint2(ck.v[j], (uint32_t)(s0 + pos));
+        }
         ++pe;
       }
     }
-    __syncthreads();
+  }
+}
+
+// A row's scratch keys restricted to its boundary group (0 elsewhere: below
+// every key of the group, which are nonzero).
+struct SrcGroup {
+  const uint32_t* row;
+  uint32_t mask, prefix;
+  int s0;
+  __device__ uint32_t key(int i) const {
+    const uint32_t k = row[i];
+    return (k & mask) == prefix ? k : 0u;
+  }
+  __device__ int32_t id(int i) const { return s0 + i; }
+};
+
+// One workgroup per slotted failed row still open after two digits: the
+// rem largest of its boundary group, ties at the K-th score to the lowest
+// ids, into out[kr - rem, kr).  A gathered group is selected in registers
+// (range select, then the tie-break on the ids); a larger one by radix
+// passes over the row's scratch keys, restricted to the group, whose emit
+// takes tied keys in position order.
+__global__ __launch_bounds__(kWG) void k_prefill_repair_final(PrefillArgs A) {
+  __shared__ SelShared sh;
+  const int tid = threadIdx.x;
+  const uint32_t n_slot = min(__atomic_load_n(&A.ctrl[kCtrlFail], __ATOMIC_RELAXED), (uint32_t)A.rslots);
+#pragma unroll 1
+  for (uint32_t f = blockIdx.x; f < n_slot; f += gridDim.x) {
+    RepairRow row;
+    repair_row_ids(row, A, (int)f);
+    const RepairSel rs = load_state(A.rrow + (int64_t)f * kRowWords, 0);
+    if (rs.done) continue;  // written whole by the gather
+    int32_t* out = A.out + (int64_t)row.t * A.K + (row.kr - rs.rem);
+    if (rs.group <= kRepairGroupCap) {
+      constexpr int M = kRepairGroupRegs;
+      const uint32_t n = (uint32_t)rs.group;
+      const RegLayout lay = block_list_layout(n, (uint32_t)tid);
+      uint32_t key[M];
+      int32_t id[M];
+      load_list_regs(key, id, repair_group(A, row.t), n, lay, [](uint32_t x) { return x; });
+      const auto kf = [&](int j) { return key[j]; };
+      const RangeSel sel = range_select_regs<M>(kf, lay, rs.rem, sh, tid);  // rem < group
+      const uint32_t idlo = tie_bound_regs(key, id, lay, sel, sh, tid);
+      emit_range_regs(key, id, lay, sel, idlo, rs.rem, rs.rem, out, IdIdentity{}, sh, tid);
+    } else {
+      const SrcGroup src{A.scratch + (int64_t)f * A.rstride, rs.mask, rs.prefix, row.s0};
+      const SelResult sel = radix_select(src, row.L, rs.rem, sh, tid, false, true);
+      emit_selection(src, row.L, sel, rs.rem, rs.rem, out, sh, tid);
+      __syncthreads();
+    }
   }
 }
 
@@ -984,11 +1003,9 @@ int launch_prefill(const PrefillArgs& A, hipStream_t stream) {
   const unsigned rgrid = (unsigned)max(kRepairWalkWGs, (A.rslots + 1) / 2);
   hipLaunchKernelGGL(k_prefill_pair<kPairRepair>, dim3(rgrid), dim3(kWG), 0, stream, A);
   if (A.rslots < A.Q) hipLaunchKernelGGL(k_prefill_repair_fallback, dim3(kRepairFallback), dim3(kWG), 0, stream, A);
-  hipLaunchKernelGGL(k_prefill_repair_pass<1>, dim3(kRepairPassGrid), dim3(kWG), 0, stream, A);
-  hipLaunchKernelGGL(k_prefill_repair_pass<2>, dim3(kRepairPassGrid), dim3(kWG), 0, stream, A);
-  hipLaunchKernelGGL(k_prefill_repair_pass<3>, dim3(kRepairPassGrid), dim3(kWG), 0, stream, A);
-  hipLaunchKernelGGL(k_prefill_repair_ties, dim3(kRepairPassGrid), dim3(kWG), 0, stream, A);
-  hipLaunchKernelGGL(k_prefill_repair_emit, dim3(kRepairPassGrid), dim3(kWG), 0, stream, A);
+  hipLaunchKernelGGL(k_prefill_repair_pass, dim3(kRepairPassGrid), dim3(kWG), 0, stream, A);
+  hipLaunchKernelGGL(k_prefill_repair_gather, dim3(kRepairPassGrid), dim3(kWG), 0, stream, A);
+  hipLaunchKernelGGL(k_prefill_repair_final, dim3((unsigned)min(A.rslots, kRepairFinalGrid)), dim3(kWG), 0, stream, A);
   return hipGetLastError() == hipSuccess ? IDX_OK : IDX_EHIP;
 }
 

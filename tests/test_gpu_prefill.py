@@ -232,6 +232,25 @@ def test_ties_through_repair_take_the_lowest_ids(e4m3):
     check_prefill_rows(case, r["out"], np.arange(case.Q), gpu_scores=r["scores"], e4m3=e4m3)
 
 
+def test_tie_group_beyond_the_gather_through_repair(e4m3):
+    """Rows over 16 distinct keys at 163840 keys sent to the exact repair:
+    the K-th score is held by more keys than the repair gathers per row
+    (8192), so its last step selects among them from the row's scratch
+    keys; ties still resolve to the lowest ids."""
+    pos = np.arange(163840 - 8, 163840, dtype=np.int64)
+    case = synth.causal_case("ties_scratch", 8, 163840, seed=32, key_mode="ties16", positions=pos)
+    log("case", case.name)
+    r = run_prefill(case, scores=True, force_tau=float("inf"))
+    st = r["stats"]
+    log("stats", st)
+    assert st["repaired"] == case.Q, st
+    for t in range(case.Q):   # the case reaches that step: a tie group above the gather's capacity
+        row = r["scores"][t, case.row_start[t]:case.row_end[t]]
+        kth = np.partition(row, -case.K)[-case.K]
+        assert np.count_nonzero(row == kth) > 8192, t
+    check_prefill_rows(case, r["out"], np.arange(case.Q), gpu_scores=r["scores"], e4m3=e4m3)
+
+
 def test_output_is_deterministic():
     """Two calls on the same inputs select the same ids (ties included)."""
     case = synth.causal_case("determinism", 16, 12000, seed=31, key_mode="ties16", K=512)
