@@ -551,6 +551,7 @@ struct SelShared {
   uint32_t bucket, above, inbucket, pad0;
   uint32_t gt_count, eq_count, pad1, pad2;
   uint32_t wsum[2][kWaves];  // per-wave minima and maxima of range_select_regs
+  uint32_t ring[2][256];     // range_select_regs: with hist, one histogram per pass in rotation
 };
 
 // Result of the digit passes: every key with (key & mask) > prefix is in the
@@ -590,6 +591,34 @@ __device__ __forceinline__ void find_bucket(SelShared& sh, int rem, int tid) {
       sh.inbucket = hb;
     }
   }
+}
+
+// The same search run by one wave on its own over a complete 256-bin
+// histogram in LDS (no barrier, no broadcast): the bucket, the count above
+// it and the count in it, wave-uniform.
+__device__ __forceinline__ void wave_find_bucket(const uint32_t* hist, int rem, uint32_t lane, uint32_t& bucket,
+                                                 uint32_t& above, uint32_t& inbucket) {
+  const uint32_t h0 = hist[4 * lane + 0], h1 = hist[4 * lane + 1];
+  const uint32_t h2 = hist[4 * lane + 2], h3 = hist[4 * lane + 3];
+  const uint32_t s = h0 + h1 + h2 + h3;
+  uint32_t suf = s;  // inclusive suffix sum over lanes >= lane
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t o = __shfl_down(suf, off, 64);
+    if (lane + off < 64) suf += o;
+  }
+  const uint32_t above_lane = suf - s;
+  const uint32_t r = (uint32_t)rem;
+  const bool owner = above_lane < r && r <= suf;
+  uint32_t acc = above_lane, b = 4 * lane, hb = h0;
+  if (acc + h3 >= r) { b = 4 * lane + 3; hb = h3; }
+  else if ((acc += h3) + h2 >= r) { b = 4 * lane + 2; hb = h2; }
+  else if ((acc += h2) + h1 >= r) { b = 4 * lane + 1; hb = h1; }
+  else { acc += h1; }
+  const int ol = __ffsll((unsigned long long)__ballot(owner)) - 1;
+  bucket = (uint32_t)__builtin_amdgcn_readlane((int)b, ol);
+  above = (uint32_t)__builtin_amdgcn_readlane((int)acc, ol);
+  inbucket = (uint32_t)__builtin_amdgcn_readlane((int)hb, ol);
 }
 
 // Exact K-th-largest search by four 8-bit radix passes from the high byte
@@ -750,10 +779,18 @@ struct RangeSel {
 // Each further pass splits the chosen bin 256 ways; a bin of width one ends
 // the search.  Requires 1 <= rem < number of keys.  All threads of the
 // workgroup call this.
+// One barrier per pass: the passes take three histograms in rotation
+// (sh.ring[0], sh.ring[1], sh.hist, ...), every wave finds the bucket
+// itself, and each pass clears the histogram of the pass after it, which
+// was last read two passes before (so behind this pass's barrier for every
+// wave).  sh.hist is first written in the second pass, behind two
+// barriers, so that a caller's earlier use of it has ended.
 template <int M, class KF>
 __device__ __forceinline__ RangeSel range_select_regs(const KF& kf, const RegLayout& lay, int rem, SelShared& sh, int tid) {
   const uint32_t lane = tid & 63;
   const int wave = tid >> 6;
+  const auto ring = [&](int i) { return i == 2 ? sh.hist : sh.ring[i]; };
+  sh.ring[0][tid] = 0u;  // kWG == 256 bins
   uint32_t mn = 0xFFFFFFFFu, mx = 0u;
 #pragma unroll
   for (int j = 0; j < M; ++j) {
@@ -780,22 +817,22 @@ __device__ __forceinline__ RangeSel range_select_regs(const KF& kf, const RegLay
   int s = bits > 8 ? bits - 8 : 0;
   uint32_t lo = mn, width = span;  // the range is [lo, lo + width]
   int group;
+  int cur = 0;
 #pragma unroll 1
   while (true) {
-    sh.hist[tid] = 0u;  // kWG == 256 bins
-    __syncthreads();
+    const int nxt = cur == 2 ? 0 : cur + 1;
+    uint32_t* const h = ring(cur);
+    ring(nxt)[tid] = 0u;
 #pragma unroll
     for (int j = 0; j < M; ++j) {
       if ((uint32_t)j < lay.jmax) {  // wave-uniform guard; keeps the keys in registers
         const uint32_t d = kf(j) - lo;  // key 0 wraps above any width (lo >= 1)
-        if (d <= width) atomicAdd(&sh.hist[d >> s], 1u);
+        if (d <= width) atomicAdd(&h[d >> s], 1u);
       }
     }
     __syncthreads();
-    find_bucket(sh, rem, tid);
-    __syncthreads();
-    const uint32_t b = sh.bucket, above = sh.above, inb = sh.inbucket;
-    __syncthreads();
+    uint32_t b, above, inb;
+    wave_find_bucket(h, rem, lane, b, above, inb);
     rem -= (int)above;
     group = (int)inb;
     const uint32_t off = b << s;
@@ -803,7 +840,9 @@ __device__ __forceinline__ RangeSel range_select_regs(const KF& kf, const RegLay
     width = min(width - off, (1u << s) - 1u);  // s <= 24
     if ((int)inb == rem || s == 0) break;
     s = s > 8 ? s - 8 : 0;
+    cur = nxt;
   }
+  __syncthreads();  // every wave has read the histograms before sh is used again
   return RangeSel{lo, lo + width, rem, group};
 }
 
@@ -853,19 +892,16 @@ __device__ __forceinline__ uint32_t tie_bound_regs(const uint32_t (&key)[M], con
 }
 
 // Emit for range_select_regs: keys above `last` fill out[0, kr - rem), the
-// boundary keys taken (those in [lo, last] with ~id >= idlo) fill
-// out[kr - rem, kr), -1 up to K; idmap(id[j]) is written.  Positions run
-// over (slot j, wave, lane) in that order, so a wave's winners in one slot
-// are stored to consecutive addresses and the result does not depend on
-// timing.  At most 64 slots per thread and 65535 keys per list (two 16-bit
-// counts share a word).
+// boundary keys taken (those in [lo, last] with ~id >= idlo: exactly rem of
+// them) fill out[kr - rem, kr), -1 up to K; idmap(id[j]) is written.  Each
+// thread counts its winners of both kinds, one workgroup scan turns the
+// counts into the thread's first output slots, and the thread writes its
+// winners there in slot order, so the result does not depend on timing.
+// At most 65535 keys per list (two 16-bit counts share a word).
 template <int M, class IdMap>
 __device__ __forceinline__ void emit_range_regs(const uint32_t (&key)[M], const int32_t (&id)[M], const RegLayout& lay,
                                 const RangeSel& sel, uint32_t idlo, int kr, int K, int32_t* out,
                                 const IdMap& idmap, SelShared& sh, int tid) {
-  static_assert(M <= 64, "one lane per register slot");
-  const uint32_t lane = tid & 63;
-  const int wave = tid >> 6;
   const uint32_t width = sel.last - sel.lo;
   // every slot's output id first, all loads of a map that reads memory (one
   // page-table entry per slot for paged rows) issued together and waited
@@ -880,41 +916,22 @@ __device__ __forceinline__ void emit_range_regs(const uint32_t (&key)[M], const 
     asm volatile("" : "+v"(x));
     return key[j] - sel.lo <= width && ~x >= idlo;
   };
-  // lane j: this wave's winners in slot j (above | boundary << 16)
-  uint32_t mine = 0u;
+  uint32_t mine = 0u;  // this thread's winners: above | boundary << 16
+#pragma unroll
+  for (int j = 0; j < M; ++j)
+    if ((uint32_t)j < lay.jmax) mine += (gt(j) ? 1u : 0u) + (eq(j) ? 0x10000u : 0u);
+  uint32_t total;
+  const uint32_t first = block_exclusive_scan(mine, sh, tid, total);
+  uint32_t pg = first & 0xFFFFu;
+  uint32_t pe = (uint32_t)(kr - sel.rem) + (first >> 16);
 #pragma unroll
   for (int j = 0; j < M; ++j) {
     if ((uint32_t)j < lay.jmax) {
-      const uint32_t c = (uint32_t)__popcll(__ballot(gt(j))) | (uint32_t)__popcll(__ballot(eq(j))) << 16;
-      mine = lane == (uint32_t)j ? c : mine;
-    }
-  }
-  sh.hist[wave * 64 + lane] = mine;
-  __syncthreads();
-  uint32_t col = 0u, before = 0u;  // slot `lane` over all waves, over the waves before this one
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w) {
-    const uint32_t c = sh.hist[w * 64 + lane];
-    col += c;
-    before += w < wave ? c : 0u;
-  }
-  uint32_t inc = col;  // inclusive scan over the slots
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint32_t x = (uint32_t)__shfl_up((int)inc, off, 64);
-    if (lane >= (uint32_t)off) inc += x;
-  }
-  const uint32_t base = inc - col + before;
-  const uint32_t eq_base = (uint32_t)(kr - sel.rem);
-#pragma unroll
-  for (int j = 0; j < M; ++j) {
-    if ((uint32_t)j < lay.jmax) {
-      const uint32_t bj = (uint32_t)__builtin_amdgcn_readlane((int)base, j);
-      const bool g = gt(j), e = eq(j);
-      const uint64_t bg = __ballot(g), be = __ballot(e);
-      if (g) out[(bj & 0xFFFFu) + rank_in(bg)] = mid[j];
-      const uint32_t pe = (bj >> 16) + rank_in(be);
-      if (e && pe < (uint32_t)sel.rem) out[eq_base + pe] = mid[j];
+      if (gt(j)) out[pg++] = mid[j];
+      if (eq(j)) {
+        if (pe < (uint32_t)kr) out[pe] = mid[j];
+        ++pe;
+      }
     }
   }
   for (int i = kr + tid; i < K; i += kWG) out[i] = -1;
@@ -944,27 +961,8 @@ __device__ SelResult wave_radix_select(const Src& src, int n, int rem, uint32_t*
       hist_add(hist, (key >> shift) & 255u, v && ((key & mask) == prefix));
     }
     wave_sync();
-    const uint32_t h0 = hist[4 * lane + 0], h1 = hist[4 * lane + 1];
-    const uint32_t h2 = hist[4 * lane + 2], h3 = hist[4 * lane + 3];
-    const uint32_t s = h0 + h1 + h2 + h3;
-    uint32_t suf = s;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const uint32_t o = __shfl_down(suf, off, 64);
-      if (lane + off < 64) suf += o;
-    }
-    const uint32_t above_lane = suf - s;
-    const uint32_t r = (uint32_t)rem;
-    const bool owner = above_lane < r && r <= suf;
-    uint32_t acc = above_lane, b = 4 * lane, hb = h0;
-    if (acc + h3 >= r) { b = 4 * lane + 3; hb = h3; }
-    else if ((acc += h3) + h2 >= r) { b = 4 * lane + 2; hb = h2; }
-    else if ((acc += h2) + h1 >= r) { b = 4 * lane + 1; hb = h1; }
-    else { acc += h1; }
-    const int ol = __ffsll((unsigned long long)__ballot(owner)) - 1;
-    const uint32_t bb = (uint32_t)__builtin_amdgcn_readlane((int)b, ol);
-    const uint32_t above = (uint32_t)__builtin_amdgcn_readlane((int)acc, ol);
-    const uint32_t inb = (uint32_t)__builtin_amdgcn_readlane((int)hb, ol);
+    uint32_t bb, above, inb;
+    wave_find_bucket(hist, rem, lane, bb, above, inb);
     prefix |= bb << shift;
     mask |= 0xFFu << shift;
     rem -= (int)above;
