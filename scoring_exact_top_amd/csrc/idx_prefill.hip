@@ -603,8 +603,11 @@ __global__ __launch_bounds__(kWG) void k_prefill_select(PrefillArgs A) {
   if (tid == 0) { sh.pad0 = dk; sh.pad1 = fd; }
   __syncthreads();
   const uint32_t drop = sh.pad0, first_drop = sh.pad1;
-  uint32_t n = 0u;
-  for (int g = 0; g < nseg; ++g) n += s_segn[g];
+  uint32_t n = 0u, most = 0u;  // candidates in all, in the fullest segment
+  for (int g = 0; g < nseg; ++g) {
+    n += s_segn[g];
+    most = max(most, s_segn[g]);
+  }
   const int L = re_t - rs_t;
   const int kr = min(A.K, L);
   bool ok = n >= (uint32_t)kr;
@@ -612,7 +615,10 @@ __global__ __launch_bounds__(kWG) void k_prefill_select(PrefillArgs A) {
     const uint32_t tps = (uint32_t)(kWG / nseg);
     const uint32_t g = (uint32_t)tid / tps;
     const uint32_t first = g * (uint32_t)A.seg_cap;
-    const RegLayout lay{first + (uint32_t)tid % tps, tps, first + s_segn[g], (uint32_t)M};
+    // slots past the fullest segment's entries are empty in every thread:
+    // the select's loops stop there
+    const uint32_t jmax = min((most + tps - 1u) / tps, (uint32_t)M);
+    const RegLayout lay{first + (uint32_t)tid % tps, tps, first + s_segn[g], jmax};
     const int64_t row = (int64_t)t * nseg * A.seg_cap;
     uint32_t key[M];
     int32_t id[M];

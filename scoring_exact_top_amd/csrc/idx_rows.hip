@@ -340,7 +340,11 @@ __global__ __launch_bounds__(kWG, Rows::kMinBlocks) void k_topk_rows(RowsArgs A)
     block_exclusive_scan(tid % (int)tpr == 0 ? gc : 0u, S.sh, tid, n);
     const bool fits = !__syncthreads_or(gc > tpr * (uint32_t)kRowsRegs);
     if (fits && n >= (uint32_t)K) {
-      const RegLayout lay{(uint32_t)tid % tpr, tpr, gc, (uint32_t)kRowsRegs};
+      // slots past the wave's fullest region are empty in all its threads
+      uint32_t jw = (gc + tpr - 1u) / tpr;
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) jw = max(jw, (uint32_t)__shfl_xor((int)jw, o, 64));
+      const RegLayout lay{(uint32_t)tid % tpr, tpr, gc, (uint32_t)__builtin_amdgcn_readfirstlane((int)jw)};
       uint32_t key[kRowsRegs];
       int32_t id[kRowsRegs];
 #pragma unroll
