@@ -111,9 +111,9 @@ typedef struct {
                           certificate failed and the row was recomputed by the
                           exact repair path), IDX_ROW_BAD (invalid range)      */
   uint64_t *clock_out; /* prefill: [2] uint64 device array or NULL; the main
-                          scoring kernel adds, over all its workgroups, the
+                          scoring kernel adds, over all its waves, the
                           shader-clock cycles ([0]) and the constant-rate
-                          wall-clock ticks ([1]) each workgroup ran for, so that
+                          wall-clock ticks ([1]) each wave ran for, so that
                           [0]/[1] times the wall-clock rate is the kernel's mean
                           shader clock.  The caller zeroes it before the call.  */
   int32_t math_only;   /* prefill, 1: control build of the main kernel (timing
