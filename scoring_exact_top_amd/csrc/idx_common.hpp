@@ -552,6 +552,7 @@ struct SelShared {
   uint32_t gt_count, eq_count, pad1, pad2;
   uint32_t wsum[2][kWaves];  // per-wave minima and maxima of range_select_regs
   uint32_t ring[2][256];     // range_select_regs: with hist, one histogram per pass in rotation
+  uint32_t trash[64];        // range_select_regs: where the keys outside a pass's range are counted
 };
 
 // Result of the digit passes: every key with (key & mask) > prefix is in the
@@ -791,15 +792,22 @@ __device__ __forceinline__ RangeSel range_select_regs(const KF& kf, const RegLay
   const int wave = tid >> 6;
   const auto ring = [&](int i) { return i == 2 ? sh.hist : sh.ring[i]; };
   sh.ring[0][tid] = 0u;  // kWG == 256 bins
-  uint32_t mn = 0xFFFFFFFFu, mx = 0u;
+  uint32_t mn = 0xFFFFFFFFu, mx = 0u, mn2 = 0xFFFFFFFFu, mx2 = 0u;  // two chains
 #pragma unroll
   for (int j = 0; j < M; ++j) {
     if ((uint32_t)j < lay.jmax) {
       const uint32_t k = kf(j);
-      mn = min(mn, k ? k : 0xFFFFFFFFu);
-      mx = max(mx, k);
+      if (j & 1) {
+        mn2 = min(mn2, k ? k : 0xFFFFFFFFu);
+        mx2 = max(mx2, k);
+      } else {
+        mn = min(mn, k ? k : 0xFFFFFFFFu);
+        mx = max(mx, k);
+      }
     }
   }
+  mn = min(mn, mn2);
+  mx = max(mx, mx2);
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) {
     mn = min(mn, (uint32_t)__shfl_xor((int)mn, off, 64));
@@ -823,11 +831,13 @@ __device__ __forceinline__ RangeSel range_select_regs(const KF& kf, const RegLay
     const int nxt = cur == 2 ? 0 : cur + 1;
     uint32_t* const h = ring(cur);
     ring(nxt)[tid] = 0u;
+    // branch-free: a key outside the range is counted in this lane's trash
+    // bin (no exec-mask change per slot, no conflicts among those lanes)
 #pragma unroll
     for (int j = 0; j < M; ++j) {
       if ((uint32_t)j < lay.jmax) {  // wave-uniform guard; keeps the keys in registers
         const uint32_t d = kf(j) - lo;  // key 0 wraps above any width (lo >= 1)
-        if (d <= width) atomicAdd(&h[d >> s], 1u);
+        atomicAdd(d <= width ? &h[d >> s] : &sh.trash[lane], 1u);
       }
     }
     __syncthreads();
@@ -916,22 +926,32 @@ __device__ __forceinline__ void emit_range_regs(const uint32_t (&key)[M], const 
     asm volatile("" : "+v"(x));
     return key[j] - sel.lo <= width && ~x >= idlo;
   };
-  uint32_t mine = 0u;  // this thread's winners: above | boundary << 16
+  uint32_t mine = 0u, mine2 = 0u;  // this thread's winners: above | boundary << 16 (two chains)
 #pragma unroll
-  for (int j = 0; j < M; ++j)
-    if ((uint32_t)j < lay.jmax) mine += (gt(j) ? 1u : 0u) + (eq(j) ? 0x10000u : 0u);
+  for (int j = 0; j < M; ++j) {
+    if ((uint32_t)j < lay.jmax) {
+      const uint32_t c = (gt(j) ? 1u : 0u) + (eq(j) ? 0x10000u : 0u);
+      if (j & 1) mine2 += c; else mine += c;
+    }
+  }
+  mine += mine2;
   uint32_t total;
   const uint32_t first = block_exclusive_scan(mine, sh, tid, total);
   uint32_t pg = first & 0xFFFFu;
   uint32_t pe = (uint32_t)(kr - sel.rem) + (first >> 16);
+  // branch-free stores through a resource bounded at out[kr]: a lane that
+  // stores nothing in a slot gets an offset past every buffer, and a
+  // boundary key past kr (none where the tie-break ran) is dropped the same
+  // way
+  const rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc((void*)out, (short)0, kr * 4, 0x00020000);
 #pragma unroll
   for (int j = 0; j < M; ++j) {
     if ((uint32_t)j < lay.jmax) {
-      if (gt(j)) out[pg++] = mid[j];
-      if (eq(j)) {
-        if (pe < (uint32_t)kr) out[pe] = mid[j];
-        ++pe;
-      }
+      const bool g = gt(j), e = eq(j);
+      __builtin_amdgcn_raw_buffer_store_b32(mid[j], ro, g ? (int)(pg * 4u) : 0x7FFFFFF0, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b32(mid[j], ro, e ? (int)(pe * 4u) : 0x7FFFFFF0, 0, 0);
+      pg += g ? 1u : 0u;
+      pe += e ? 1u : 0u;
     }
   }
   for (int i = kr + tid; i < K; i += kWG) out[i] = -1;
