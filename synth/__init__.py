@@ -38,6 +38,9 @@ E4M3_MAX = 448.0
 # include/idx_topk.h).  Only used here to place adversarial keys on or off it.
 SAMPLE_STRIDE = 200
 SAMPLE_OFFSET = 100
+# x8 keys of the off-lattice outlier block: with the plain keys' ~4096
+# candidates, more than a row's 8192+ candidate slots
+OUTLIER_KEYS = 6000
 
 
 @dataclasses.dataclass
@@ -161,7 +164,11 @@ def causal_case(name: str, Q: int, N: int, seed: int, key_mode: str = "normal",
       normal      k ~ N(0,1)
       heavy_tail  1% of key rows scaled x8 before quantisation
       ties16      every key is one of 16 distinct (code vector, scale) pairs
-      outlier     a 3000-key block of x8 keys placed off the sampling lattice
+      outlier     a 6000-key block of x8 keys off the sampling lattice, ending
+                  at the first row's last position: no sample sees them, so
+                  the threshold is taken from the plain keys and the rows
+                  keep about 6000 + 4096 candidates, more than the segments
+                  hold, and the last ones dropped are outliers (overflow)
       decoy       x8 keys placed exactly on the sampling lattice (every other
                   lattice point), so the sampled threshold lands among them
     """
@@ -177,13 +184,13 @@ def causal_case(name: str, Q: int, N: int, seed: int, key_mode: str = "normal",
     elif key_mode in ("normal", "outlier", "decoy"):
         k = torch.randn(N, D, generator=g)
         if key_mode == "outlier":
-            start = int(torch.randint(0, N // 2, (1,), generator=g).item())
+            last = int(positions[0]) if positions is not None else N - Q
             pos = []
-            p = start
-            while len(pos) < 3000:
+            p = last
+            while len(pos) < OUTLIER_KEYS and p >= 0:
                 if (p - SAMPLE_OFFSET) % SAMPLE_STRIDE != 0:
                     pos.append(p)
-                p += 1
+                p -= 1
             k[torch.tensor(pos)] *= 8.0
         elif key_mode == "decoy":
             lattice = torch.arange(SAMPLE_OFFSET, N, SAMPLE_STRIDE)
@@ -267,9 +274,10 @@ def adversarial(seed: int = 0) -> List[PrefillCase]:
     """2048 rows at the last positions of a 163840-token context, split into
     four calls with their own key sets: 1024 rows over 16 distinct key
     vectors (massive ties), 256 rows with an off-lattice x8 outlier block of
-    3000 keys, 256 rows with x8 decoys on the sampling lattice (the sampled
-    threshold lands among them: too few candidates, exact repair), 512 rows
-    over plain N(0,1) keys."""
+    6000 keys at the end of their ranges (more candidates than a row holds:
+    overflow, exact repair), 256 rows with x8 decoys on the sampling lattice
+    (the sampled threshold lands among them: too few candidates, exact
+    repair), 512 rows over plain N(0,1) keys."""
     N = 163840
     pos = np.arange(N - 2048, N, dtype=np.int64)
     return [

@@ -53,11 +53,14 @@ def test_audit_long_prefill_every_row():
 
 
 def test_audit_adversarial_every_row():
-    """All four sub-calls: ties, the off-lattice outlier block, the on-lattice
-    decoys (whose rows underflow and go through the exact repair) and plain
-    rows."""
+    """All four sub-calls: ties, the off-lattice outlier block (rows whose
+    segments overflow with outliers scoring above the selection go through
+    the exact repair), the on-lattice decoys (whose rows underflow and go
+    through it too) and plain rows."""
     for case in synth.adversarial(0):
         st, repaired = _audit(case)
+        if case.name == "adversarial_outlier":
+            assert st["overflow"] > 0 and repaired.size == st["repaired"] > 0, st
         if case.name == "adversarial_decoy":
             assert st["underflow"] > 0 and repaired.size == st["repaired"] > 0, st
         if case.name == "adversarial_ties16":

@@ -36,8 +36,11 @@ def test_adversarial_structure():
     assert np.median(dec.k_scale[lattice[::2]]) > 5 * np.median(dec.k_scale)
     out = synth.causal_case("o", 2, 20000, seed=1, key_mode="outlier")
     heavy = np.nonzero(out.k_scale > 5 * np.median(out.k_scale))[0]
-    assert 2900 <= heavy.size <= 3000
+    assert synth.OUTLIER_KEYS - 100 <= heavy.size <= synth.OUTLIER_KEYS
     assert not np.any((heavy - synth.SAMPLE_OFFSET) % synth.SAMPLE_STRIDE == 0)
+    # one block ending at the first row's last position, inside every row
+    assert heavy.max() <= out.row_end.min() - 1
+    assert heavy.max() - heavy.min() < synth.OUTLIER_KEYS * 1.01 + 10
 
 
 def test_paged_decode_layout():
