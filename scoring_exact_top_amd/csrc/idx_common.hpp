@@ -47,6 +47,7 @@ constexpr int kD = 128;
 constexpr int kKmax = 2048;
 constexpr int kWG = 256;     // threads per workgroup of the 4-wave kernels
 constexpr int kWaves = 4;
+constexpr int kMaxWaves = 16;  // the register select's largest workgroup (1024 threads)
 constexpr int kTile = 64;    // keys per tile (4 MFMA sub-tiles of 16)
 constexpr int kUTerms = 8;   // e4m3 terms of the linear vector u
 constexpr int kBlocks = 5;   // A blocks per tile: 4 head blocks + the u block
@@ -550,7 +551,7 @@ struct SelShared {
   uint32_t hist[256];
   uint32_t bucket, above, inbucket, pad0;
   uint32_t gt_count, eq_count, pad1, pad2;
-  uint32_t wsum[2][kWaves];  // per-wave minima and maxima of range_select_regs
+  uint32_t wsum[3][kMaxWaves];  // per-wave minima, maxima and key counts of range_select_regs
   uint32_t ring[2][256];     // range_select_regs: with hist, one histogram per pass in rotation
   uint32_t trash[64];        // range_select_regs: where the keys outside a pass's range are counted
 };
@@ -659,8 +660,9 @@ __device__ SelResult radix_select(const Src& src, int n, int rem, SelShared& sh,
   return SelResult{prefix, mask, rem, group};
 }
 
-// Exclusive prefix sum over the workgroup of one per-thread count, in
-// thread order; also returns the total.  All threads call this.
+// Exclusive prefix sum over the workgroup (NW waves) of one per-thread
+// count, in thread order; also returns the total.  All threads call this.
+template <int NW = kWaves>
 __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t a, SelShared& sh, int tid, uint32_t& total) {
   const uint32_t lane = tid & 63;
   const int wave = tid >> 6;
@@ -675,7 +677,7 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t a, SelShared& 
   uint32_t before = 0u;
   total = 0u;
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w) {
+  for (int w = 0; w < NW; ++w) {
     const uint32_t c = sh.wsum[0][w];
     before += w < wave ? c : 0u;
     total += c;
@@ -728,9 +730,12 @@ struct RegLayout {
   __device__ bool valid(int j) const { return at(j) < n; }
 };
 
-// The workgroup holds one list of n elements, element j*256 + tid in key[j].
+// The workgroup (NW waves) holds one list of n elements, element
+// j*64*NW + tid in key[j].
+template <int NW = kWaves>
 __device__ __forceinline__ RegLayout block_list_layout(uint32_t n, uint32_t tid) {
-  return RegLayout{tid, (uint32_t)kWG, n, (n + kWG - 1u) / kWG};
+  constexpr uint32_t nt = 64u * NW;
+  return RegLayout{tid, nt, n, (n + nt - 1u) / nt};
 }
 
 // Loads of one list of (key bits, id) pairs into registers, key[j] and
@@ -785,18 +790,24 @@ struct RangeSel {
 // itself, and each pass clears the histogram of the pass after it, which
 // was last read two passes before (so behind this pass's barrier for every
 // wave).  sh.hist is first written in the second pass, behind two
-// barriers, so that a caller's earlier use of it has ended.
-template <int M, class KF>
+// barriers, so that a caller's earlier use of it has ended.  NW waves (4 to
+// 16) per workgroup; the first 256 threads clear the 256 bins.  A list of
+// one value (massive ties) needs no pass.
+template <int M, int NW = kWaves, class KF>
 __device__ __forceinline__ RangeSel range_select_regs(const KF& kf, const RegLayout& lay, int rem, SelShared& sh, int tid) {
+  static_assert(NW >= 4 && NW <= kMaxWaves, "256 bins cleared by the first 256 threads");
   const uint32_t lane = tid & 63;
   const int wave = tid >> 6;
+  const bool clears = NW == 4 || tid < 256;
   const auto ring = [&](int i) { return i == 2 ? sh.hist : sh.ring[i]; };
-  sh.ring[0][tid] = 0u;  // kWG == 256 bins
+  if (clears) sh.ring[0][tid] = 0u;
   uint32_t mn = 0xFFFFFFFFu, mx = 0u, mn2 = 0xFFFFFFFFu, mx2 = 0u;  // two chains
+  uint32_t cnt = 0u;  // keys held (nonzero)
 #pragma unroll
   for (int j = 0; j < M; ++j) {
     if ((uint32_t)j < lay.jmax) {
       const uint32_t k = kf(j);
+      cnt += k ? 1u : 0u;
       if (j & 1) {
         mn2 = min(mn2, k ? k : 0xFFFFFFFFu);
         mx2 = max(mx2, k);
@@ -812,13 +823,20 @@ __device__ __forceinline__ RangeSel range_select_regs(const KF& kf, const RegLay
   for (int off = 32; off > 0; off >>= 1) {
     mn = min(mn, (uint32_t)__shfl_xor((int)mn, off, 64));
     mx = max(mx, (uint32_t)__shfl_xor((int)mx, off, 64));
+    cnt += (uint32_t)__shfl_xor((int)cnt, off, 64);
   }
-  if (lane == 0) { sh.wsum[0][wave] = mn; sh.wsum[1][wave] = mx; }
+  if (lane == 0) { sh.wsum[0][wave] = mn; sh.wsum[1][wave] = mx; sh.wsum[2][wave] = cnt; }
   __syncthreads();
+  cnt = 0u;
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w) {
+  for (int w = 0; w < NW; ++w) {
     mn = min(mn, sh.wsum[0][w]);
     mx = max(mx, sh.wsum[1][w]);
+    cnt += sh.wsum[2][w];
+  }
+  if (mx == mn) {  // every key is one value (massive ties): no pass to run
+    __syncthreads();  // the minima are read before sh is used again
+    return RangeSel{mn, mn, rem, (int)cnt};
   }
   const uint32_t span = mx - mn;
   const int bits = span ? 32 - __clz((int)span) : 0;
@@ -830,7 +848,7 @@ __device__ __forceinline__ RangeSel range_select_regs(const KF& kf, const RegLay
   while (true) {
     const int nxt = cur == 2 ? 0 : cur + 1;
     uint32_t* const h = ring(cur);
-    ring(nxt)[tid] = 0u;
+    if (clears) ring(nxt)[tid] = 0u;
     // branch-free: a key outside the range is counted in this lane's trash
     // bin (no exec-mask change per slot, no conflicts among those lanes)
 #pragma unroll
@@ -859,7 +877,7 @@ __device__ __forceinline__ RangeSel range_select_regs(const KF& kf, const RegLay
 // Smallest key in [sel.lo, sel.last]: the smallest key selected by `sel`
 // when the boundary range is taken whole or holds one value.  All threads
 // of the workgroup call this.
-template <int M, class KF>
+template <int M, int NW = kWaves, class KF>
 __device__ __forceinline__ uint32_t range_min_regs(const KF& kf, const RegLayout& lay, const RangeSel& sel, SelShared& sh,
                                    int tid) {
   const uint32_t lane = tid & 63;
@@ -874,7 +892,7 @@ __device__ __forceinline__ uint32_t range_min_regs(const KF& kf, const RegLayout
   if (lane == 0) sh.wsum[0][wave] = mn;
   __syncthreads();
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w) mn = min(mn, sh.wsum[0][w]);
+  for (int w = 0; w < NW; ++w) mn = min(mn, sh.wsum[0][w]);
   __syncthreads();
   return mn;
 }
@@ -884,7 +902,7 @@ __device__ __forceinline__ uint32_t range_min_regs(const KF& kf, const RegLayout
 // range select over ~id of the tied keys (ids are >= 0 and distinct, so
 // ~id is nonzero and the select ends with the rem largest ~id taken whole).
 // Returns the smallest ~id taken (0: no tie-break, every boundary key).
-template <int M>
+template <int NW = kWaves, int M>
 __device__ __forceinline__ uint32_t tie_bound_regs(const uint32_t (&key)[M], const int32_t (&id)[M], const RegLayout& lay,
                                    const RangeSel& sel, SelShared& sh, int tid) {
   if (sel.rem >= sel.group) return 0u;
@@ -898,7 +916,7 @@ __device__ __forceinline__ uint32_t tie_bound_regs(const uint32_t (&key)[M], con
     asm volatile("" : "+v"(x));
     return key[j] == v ? ~x : 0u;
   };
-  return range_select_regs<M>(tk, lay, sel.rem, sh, tid).lo;
+  return range_select_regs<M, NW>(tk, lay, sel.rem, sh, tid).lo;
 }
 
 // Emit for range_select_regs: keys above `last` fill out[0, kr - rem), the
@@ -907,8 +925,8 @@ __device__ __forceinline__ uint32_t tie_bound_regs(const uint32_t (&key)[M], con
 // thread counts its winners of both kinds, one workgroup scan turns the
 // counts into the thread's first output slots, and the thread writes its
 // winners there in slot order, so the result does not depend on timing.
-// At most 65535 keys per list (two 16-bit counts share a word).
-template <int M, class IdMap>
+// At most 65535 keys per list (two 16-bit counts share a word).  NW waves.
+template <int NW = kWaves, int M, class IdMap>
 __device__ __forceinline__ void emit_range_regs(const uint32_t (&key)[M], const int32_t (&id)[M], const RegLayout& lay,
                                 const RangeSel& sel, uint32_t idlo, int kr, int K, int32_t* out,
                                 const IdMap& idmap, SelShared& sh, int tid) {
@@ -936,7 +954,7 @@ __device__ __forceinline__ void emit_range_regs(const uint32_t (&key)[M], const 
   }
   mine += mine2;
   uint32_t total;
-  const uint32_t first = block_exclusive_scan(mine, sh, tid, total);
+  const uint32_t first = block_exclusive_scan<NW>(mine, sh, tid, total);
   uint32_t pg = first & 0xFFFFu;
   uint32_t pe = (uint32_t)(kr - sel.rem) + (first >> 16);
   // branch-free stores through a resource bounded at out[kr]: a lane that
@@ -954,7 +972,7 @@ __device__ __forceinline__ void emit_range_regs(const uint32_t (&key)[M], const 
       pe += e ? 1u : 0u;
     }
   }
-  for (int i = kr + tid; i < K; i += kWG) out[i] = -1;
+  for (int i = kr + tid; i < K; i += 64 * NW) out[i] = -1;
   __syncthreads();
 }
 

@@ -35,6 +35,12 @@ constexpr int kManyCands = 4096;  // rows keeping more are counted (idx_topk_sta
 constexpr int kMaxSplit = 8;
 constexpr int kSelRegs = 40;        // keys per thread of the select kernel, any nseg <= kMaxSeg
 constexpr int kSelRegsFew = 33;     // ... for nseg <= 4 (seg_cap 8256, 4160, 2112 over 256, 128, 64 threads)
+// Calls with at most kSelWideRows rows (one per CU) select each row with
+// 1024 threads (a row's latency, not the CU's throughput, sets the time;
+// at 512 rows the 256-thread select was faster), kSelRegsWide slots per
+// thread for any nseg (seg_cap over 1024/nseg threads: at most 10).
+constexpr int kSelWideRows = 256;
+constexpr int kSelRegsWide = 10;
 
 constexpr int kMaxSeg = kWaves * kMaxSplit;  // candidate segments per row, at most
 

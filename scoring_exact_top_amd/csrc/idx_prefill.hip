@@ -553,7 +553,7 @@ __global__ __launch_bounds__(kWG, 2) void k_prefill_pair(PrefillArgs A) {
 // ------------------------------------------------------------------ select
 
 // One workgroup per row, after the main kernel.  The row's candidates (its
-// nseg segments: segment g in threads [g*tps, (g+1)*tps), tps = 256/nseg,
+// nseg segments: segment g in threads [g*tps, (g+1)*tps), tps = 64*NW/nseg,
 // each thread every tps-th entry, M slots per thread) are loaded into registers and
 // the K largest selected, ties at the K-th score going to the lowest ids.
 // Certificate ("3.2 Sampled threshold", made exact for capacity drops):
@@ -563,8 +563,11 @@ __global__ __launch_bounds__(kWG, 2) void k_prefill_pair(PrefillArgs A) {
 // the first dropped position (segments drop only their latest candidates),
 // so that they are the lowest tied ids of the whole row.  Massive ties at
 // the boundary thus need no repair.  Rows that fail go to the failure list.
-template <int M>
-__global__ __launch_bounds__(kWG) void k_prefill_select(PrefillArgs A) {
+// NW waves per workgroup: 4 where many rows share each CU, 16 (four times
+// fewer slots per thread, so shorter chains) for calls with few rows.
+template <int M, int NW>
+__global__ __launch_bounds__(64 * NW) void k_prefill_select(PrefillArgs A) {
+  constexpr int NT = 64 * NW;
   __shared__ SelShared sh;
   __shared__ uint32_t s_segn[kWaves * kMaxSplit];
   const int tid = threadIdx.x;
@@ -580,7 +583,7 @@ __global__ __launch_bounds__(kWG) void k_prefill_select(PrefillArgs A) {
   if (tid < nseg) e = *reinterpret_cast<const uint4*>(A.segn + 4 * ((int64_t)t * nseg + tid));
   const int rs_t = A.row_start[t], re_t = A.row_end[t];
   if (rs_t < 0 || rs_t > re_t || re_t > A.N) {
-    for (int i = tid; i < A.K; i += kWG) out[i] = -1;
+    for (int i = tid; i < A.K; i += NT) out[i] = -1;
     if (tid == 0) {
       atomicAdd(&stats[kStBad], 1u);
       if (A.row_status) A.row_status[t] = IDX_ROW_BAD;
@@ -612,7 +615,7 @@ __global__ __launch_bounds__(kWG) void k_prefill_select(PrefillArgs A) {
   const int kr = min(A.K, L);
   bool ok = n >= (uint32_t)kr;
   if (ok) {
-    const uint32_t tps = (uint32_t)(kWG / nseg);
+    const uint32_t tps = (uint32_t)(NT / nseg);
     const uint32_t g = (uint32_t)tid / tps;
     const uint32_t first = g * (uint32_t)A.seg_cap;
     // slots past the fullest segment's entries are empty in every thread:
@@ -625,11 +628,11 @@ __global__ __launch_bounds__(kWG) void k_prefill_select(PrefillArgs A) {
     load_list_regs(key, id, A.cand + row, (uint32_t)(nseg * A.seg_cap), lay,
                    [](uint32_t x) { return f2key(__uint_as_float(x)); });
     const auto kf = [&](int j) { return key[j]; };
-    const RangeSel sel = (n > (uint32_t)kr) ? range_select_regs<M>(kf, lay, kr, sh, tid)
+    const RangeSel sel = (n > (uint32_t)kr) ? range_select_regs<M, NW>(kf, lay, kr, sh, tid)
                                            : RangeSel{1u, 0xFFFFFFFFu, kr, (int)n};
-    const uint32_t idlo = tie_bound_regs(key, id, lay, sel, sh, tid);
+    const uint32_t idlo = tie_bound_regs<NW>(key, id, lay, sel, sh, tid);
     if (drop >= sel.lo) {
-      const uint32_t theta = range_min_regs<M>(kf, lay, sel, sh, tid);
+      const uint32_t theta = range_min_regs<M, NW>(kf, lay, sel, sh, tid);
       ok = drop <= theta;
       if (drop == theta) {  // tied keys were dropped: the taken ones must precede them
         const auto tk = [&](int j) {  // recomputed per use (see tie_bound_regs)
@@ -644,12 +647,13 @@ __global__ __launch_bounds__(kWG) void k_prefill_select(PrefillArgs A) {
         for (int o = 32; o > 0; o >>= 1) mn = min(mn, (uint32_t)__shfl_xor((int)mn, o, 64));
         if (lane == 0) sh.wsum[0][tid >> 6] = mn;
         __syncthreads();
-        mn = min(min(sh.wsum[0][0], sh.wsum[0][1]), min(sh.wsum[0][2], sh.wsum[0][3]));
+#pragma unroll
+        for (int w = 0; w < NW; ++w) mn = min(mn, sh.wsum[0][w]);
         __syncthreads();
         ok = ok && ~mn < first_drop;
       }
     }
-    if (ok) emit_range_regs(key, id, lay, sel, idlo, kr, A.K, out, IdIdentity{}, sh, tid);
+    if (ok) emit_range_regs<NW>(key, id, lay, sel, idlo, kr, A.K, out, IdIdentity{}, sh, tid);
   }
   if (tid == 0) {
     if (A.row_status) A.row_status[t] = ok ? IDX_ROW_FAST : drop ? IDX_ROW_OVERFLOW : IDX_ROW_UNDERFLOW;
@@ -996,13 +1000,16 @@ int launch_prefill(const PrefillArgs& A, hipStream_t stream) {
     else
       launch_main<kPairFused>(A, stream, e0, e1);
   }
-  // candidate slots per thread: a segment's capacity over its threads
-  // (256 / nseg of them), 33 for one, two or four segments per row, up to
-  // 40 for 8..32 (fewer registers let more rows run at once)
-  if (A.nseg <= 4)
-    hipLaunchKernelGGL(k_prefill_select<kSelRegsFew>, dim3(A.Q), dim3(kWG), 0, stream, A);
+  // calls with few rows: 1024 threads per row; otherwise 256, and candidate
+  // slots per thread a segment's capacity over its threads (256 / nseg of
+  // them): 33 for one, two or four segments per row, up to 40 for 8..32
+  // (fewer registers let more rows run at once)
+  if (A.Q <= kSelWideRows)
+    hipLaunchKernelGGL((k_prefill_select<kSelRegsWide, kMaxWaves>), dim3(A.Q), dim3(64 * kMaxWaves), 0, stream, A);
+  else if (A.nseg <= 4)
+    hipLaunchKernelGGL((k_prefill_select<kSelRegsFew, kWaves>), dim3(A.Q), dim3(kWG), 0, stream, A);
   else
-    hipLaunchKernelGGL(k_prefill_select<kSelRegs>, dim3(A.Q), dim3(kWG), 0, stream, A);
+    hipLaunchKernelGGL((k_prefill_select<kSelRegs, kWaves>), dim3(A.Q), dim3(kWG), 0, stream, A);
   if (A.keep_all) return hipGetLastError() == hipSuccess ? IDX_OK : IDX_EHIP;  // nothing can need repair
   // the slotted failures rescored two per workgroup: enough workgroups for
   // every slot pair, at least two per CU for few failures
