@@ -628,18 +628,19 @@ __device__ __forceinline__ void wave_find_bucket(const uint32_t* hist, int rem, 
 // i's order-preserving key.  If first_hist_ready, sh.hist already holds the
 // top-byte histogram of all n elements (built during scoring).  Stops early
 // once the chosen bucket is taken whole (allow_early).  Requires 1 <= rem <= n.
-// All threads of the workgroup call this.
-template <typename Src>
+// All threads of the workgroup (NW waves) call this.
+template <int NW = kWaves, typename Src>
 __device__ SelResult radix_select(const Src& src, int n, int rem, SelShared& sh, int tid,
                                   bool first_hist_ready, bool allow_early) {
+  constexpr int NT = 64 * NW;
   uint32_t prefix = 0, mask = 0;
   int group = n;
 #pragma unroll 1
   for (int shift = 24; shift >= 0; shift -= 8) {
     if (!(shift == 24 && first_hist_ready)) {
-      for (int i = tid; i < 256; i += kWG) sh.hist[i] = 0;
+      for (int i = tid; i < 256; i += NT) sh.hist[i] = 0;
       __syncthreads();
-      for (int base = 0; base < n; base += kWG) {
+      for (int base = 0; base < n; base += NT) {
         const int i = base + tid;
         const bool v = i < n;
         const uint32_t key = v ? src.key(i) : 0u;
@@ -688,16 +689,17 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t a, SelShared& 
 
 // Write the selection into out[0..kr): ids of keys above the boundary first,
 // then `rem` ids from the boundary group (the lowest positions first where
-// the group is a tie larger than rem), then -1 up to K.
-template <typename Src>
+// the group is a tie larger than rem), then -1 up to K.  NW waves.
+template <int NW = kWaves, typename Src>
 __device__ void emit_selection(const Src& src, int n, const SelResult& sel, int kr, int K,
                                int32_t* out, SelShared& sh, int tid) {
+  constexpr int NT = 64 * NW;
   if (tid == 0) { sh.gt_count = 0; sh.eq_count = 0; }
   __syncthreads();
   const int eq_base = kr - sel.rem;
   const bool ordered = sel.rem < sel.group;  // a tie: take its lowest positions
   uint32_t eq_done = 0u;                     // group members before this pass (ordered)
-  for (int base = 0; base < n; base += kWG) {
+  for (int base = 0; base < n; base += NT) {
     const int i = base + tid;
     const bool v = i < n;
     const uint32_t key = v ? src.key(i) : 0u;
@@ -711,12 +713,12 @@ __device__ void emit_selection(const Src& src, int n, const SelResult& sel, int 
       if (eq && (int)pe < sel.rem) out[eq_base + pe] = src.id(i);
     } else if (eq_done < (uint32_t)sel.rem) {  // workgroup-uniform
       uint32_t tot;
-      const uint32_t pe = eq_done + block_exclusive_scan(eq ? 1u : 0u, sh, tid, tot);
+      const uint32_t pe = eq_done + block_exclusive_scan<NW>(eq ? 1u : 0u, sh, tid, tot);
       if (eq && pe < (uint32_t)sel.rem) out[eq_base + pe] = src.id(i);
       eq_done += tot;
     }
   }
-  for (int i = kr + tid; i < K; i += kWG) out[i] = -1;
+  for (int i = kr + tid; i < K; i += NT) out[i] = -1;
 }
 
 // ------------------------------------------ register-resident selection

@@ -6,10 +6,11 @@
 // selection stage of the paged decode, and as a library routine of its own.
 //
 // Per row of length L > K:
-//   0. a cut c from a sample of the row: kSampleBlocks contiguous blocks of
-//      256 scores spread over it, c = a sample key with about 2K of the
-//      row's keys expected at or above it (the page's sampled threshold,
-//      "3.2 Sampled threshold", applied to an explicit score row);
+//   0. a cut c from a sample of the row: kSampleKeys scores in contiguous
+//      blocks of one score per thread spread over it, c = a sample key with
+//      about 2K of the row's keys expected at or above it (the page's
+//      sampled threshold, "3.2 Sampled threshold", applied to an explicit
+//      score row);
 //   1. one streaming pass gathers every key >= c into LDS (a row shorter
 //      than the sample, c = key 0: all of it), each wave into a private
 //      segment with a scalar count; with K to kRowsCap of them, the
@@ -33,11 +34,19 @@ namespace idxk {
 constexpr int kRowsBins = 2048;
 constexpr int kRowsShift = 21;  // 32 - 11 bits
 constexpr int kRowsCap = 6144;  // gathered keys held in LDS
-constexpr int kRowsRegs = kRowsCap / kWG;
-constexpr int kSegCap = kRowsCap / kWaves;  // one-pass gather: a private segment per wave
-constexpr int kSampleBlocks = 16;  // sample: 16 blocks of kWG scores
-constexpr int kSampleKeys = kSampleBlocks * kWG;
+constexpr int kSampleKeys = 4096;  // sample: kSampleKeys / NT blocks of NT scores
 constexpr int kSampleMinLen = kSampleKeys;  // shorter rows (< kRowsCap keys) are gathered whole
+// Per workgroup size (NW waves, NT threads): register slots of the
+// gathered list, each wave's private gather segment, sample blocks.
+template <int NW>
+struct RowsGeom {
+  static constexpr int NT = 64 * NW;
+  static constexpr int Regs = kRowsCap / NT;
+  static constexpr int SegCap = kRowsCap / NW;
+  static constexpr int SampleBlocks = kSampleKeys / NT;
+};
+constexpr int kRowsRegs = RowsGeom<kWaves>::Regs;  // the 256-thread kernels'
+constexpr int kSampleBlocks = RowsGeom<kWaves>::SampleBlocks;
 
 // Dense row in memory: element i is position s0 + i, emitted as ids(s0 + i).
 template <class IdMap>
@@ -54,23 +63,24 @@ struct SrcDense {
 // loads from the 16-byte-aligned address at or below the row's start (reads
 // past the end return 0), U loads per thread per step; the next step's
 // loads are issued before this step's keys are processed.
-template <int U, class F>
+template <int U, int NW = kWaves, class F>
 __device__ __forceinline__ void for_each_key(const float* row, int L, int tid, const F& f) {
   constexpr int kRowsUnroll = U;
+  constexpr int NT = 64 * NW;
   const int shift = (int)(((uintptr_t)row & 15u) >> 2);  // elements before the row in its first 16 bytes
   const float* abase = row - shift;
   const int span = L + shift;
   const rsrc_t rr = __builtin_amdgcn_make_buffer_rsrc((void*)abase, (short)0, span * 4, 0x00020000);
-  constexpr int kStep = kWG * 4 * kRowsUnroll;
+  constexpr int kStep = NT * 4 * kRowsUnroll;
   const auto load = [&](v4i (&v)[kRowsUnroll], int base) {
 #pragma unroll
     for (int u = 0; u < kRowsUnroll; ++u)
-      v[u] = __builtin_amdgcn_raw_buffer_load_b128(rr, (base + (u * kWG + tid) * 4) * 4, 0, 0);
+      v[u] = __builtin_amdgcn_raw_buffer_load_b128(rr, (base + (u * NT + tid) * 4) * 4, 0, 0);
   };
   const auto process = [&](const v4i (&v)[kRowsUnroll], int base) {
 #pragma unroll
     for (int u = 0; u < kRowsUnroll; ++u) {
-      const int i0 = base + (u * kWG + tid) * 4 - shift;
+      const int i0 = base + (u * NT + tid) * 4 - shift;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int i = i0 + e;
@@ -91,24 +101,26 @@ __device__ __forceinline__ void for_each_key(const float* row, int L, int tid, c
 }
 
 // Gathers the keys >= cut of the row into this wave's segment (lkey/lid
-// point at it, kSegCap entries) and returns how many there were (more than
-// kSegCap: the excess was not stored).  Same loads as for_each_key; per
+// point at it, SegCap entries) and returns how many there were (more than
+// SegCap: the excess was not stored).  Same loads as for_each_key; per
 // step each thread counts its qualifying keys, a wave scan turns the counts
 // into slots after the wave's running total, and each thread stores its
 // keys there: vector instructions only, no branch or atomic per key.
-template <int U>
+template <int U, int NW = kWaves>
 __device__ __forceinline__ uint32_t gather_ge(const float* row, int L, int tid, uint32_t cut, uint32_t* lkey,
                                               int32_t* lid, int32_t s0) {
+  constexpr int NT = 64 * NW;
+  constexpr uint32_t kSegCap = (uint32_t)RowsGeom<NW>::SegCap;
   const uint32_t lane = tid & 63;
   const int shift = (int)(((uintptr_t)row & 15u) >> 2);
   const float* abase = row - shift;
   const int span = L + shift;
   const rsrc_t rr = __builtin_amdgcn_make_buffer_rsrc((void*)abase, (short)0, span * 4, 0x00020000);
-  constexpr int kStep = kWG * 4 * U;
+  constexpr int kStep = NT * 4 * U;
   const auto load = [&](v4i (&v)[U], int base) {
 #pragma unroll
     for (int u = 0; u < U; ++u)
-      v[u] = __builtin_amdgcn_raw_buffer_load_b128(rr, (base + (u * kWG + tid) * 4) * 4, 0, 0);
+      v[u] = __builtin_amdgcn_raw_buffer_load_b128(rr, (base + (u * NT + tid) * 4) * 4, 0, 0);
   };
   const auto take = [&](int i, int v) { return i >= 0 && i < L && f2key(__int_as_float(v)) >= cut; };
   uint32_t wcnt = 0u;
@@ -116,7 +128,7 @@ __device__ __forceinline__ uint32_t gather_ge(const float* row, int L, int tid, 
     uint32_t cnt = 0u;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int i0 = base + (u * kWG + tid) * 4 - shift;
+      const int i0 = base + (u * NT + tid) * 4 - shift;
 #pragma unroll
       for (int e = 0; e < 4; ++e) cnt += take(i0 + e, cur[u][e]) ? 1u : 0u;
     }
@@ -129,11 +141,11 @@ __device__ __forceinline__ uint32_t gather_ge(const float* row, int L, int tid, 
     uint32_t slot = wcnt + inc - cnt;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int i0 = base + (u * kWG + tid) * 4 - shift;
+      const int i0 = base + (u * NT + tid) * 4 - shift;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const bool g = take(i0 + e, cur[u][e]);
-        if (g && slot < (uint32_t)kSegCap) {
+        if (g && slot < kSegCap) {
           lkey[slot] = f2key(__int_as_float(cur[u][e]));
           lid[slot] = s0 + i0 + e;
         }
@@ -160,7 +172,7 @@ struct RowsShared {
   };
   int32_t lid[kRowsCap];
   uint32_t n_gt, n_eq, bin, above, inbin, pad[3];
-  uint32_t segc[kWaves];  // keys each wave's gather segment received
+  uint32_t segc[kMaxWaves];  // keys each wave's gather segment received
   SelShared sh;
 };
 
@@ -170,47 +182,56 @@ struct RowsShared {
 // Split in two so that a caller can issue other loads between them: the
 // sample's loads (L >= 1; indexes clamped, so a short row reads valid
 // elements whose keys then go unused) and its select.
-__device__ __forceinline__ void sample_load(const float* row, int L, uint32_t (&sk)[kSampleBlocks], int tid) {
-  const int step = max(0, (L - kWG) / (kSampleBlocks - 1));  // block j starts at j*step
+template <int NW = kWaves>
+__device__ __forceinline__ void sample_load(const float* row, int L, uint32_t (&sk)[RowsGeom<NW>::SampleBlocks],
+                                            int tid) {
+  constexpr int SB = RowsGeom<NW>::SampleBlocks, NT = 64 * NW;
+  const int step = max(0, (L - NT) / (SB - 1));  // block j starts at j*step
 #pragma unroll
-  for (int j = 0; j < kSampleBlocks; ++j) sk[j] = f2key(row[min(j * step + tid, L - 1)]);
+  for (int j = 0; j < SB; ++j) sk[j] = f2key(row[min(j * step + tid, L - 1)]);
 }
 
-__device__ __forceinline__ uint32_t sample_select(const uint32_t (&sk)[kSampleBlocks], int L, int K, SelShared& sh,
-                                                  int tid) {
+template <int NW = kWaves>
+__device__ __forceinline__ uint32_t sample_select(const uint32_t (&sk)[RowsGeom<NW>::SampleBlocks], int L, int K,
+                                                  SelShared& sh, int tid) {
+  constexpr int SB = RowsGeom<NW>::SampleBlocks;
   if (L < kSampleMinLen) return 0u;
   // rank r in the sample <=> about r * L / kSampleKeys keys of the row
   const int r = (int)(((int64_t)2 * K * kSampleKeys + L - 1) / L);
   if (r >= kSampleKeys) return 0u;
-  const RegLayout lay{(uint32_t)tid, (uint32_t)kWG, (uint32_t)kSampleKeys, (uint32_t)kSampleBlocks};
-  return range_select_regs<kSampleBlocks>([&](int j) { return sk[j]; }, lay, r, sh, tid).lo;
+  const RegLayout lay{(uint32_t)tid, (uint32_t)(64 * NW), (uint32_t)kSampleKeys, (uint32_t)SB};
+  return range_select_regs<SB, NW>([&](int j) { return sk[j]; }, lay, r, sh, tid).lo;
 }
 
+template <int NW = kWaves>
 __device__ __forceinline__ uint32_t sample_cut(const float* row, int L, int K, SelShared& sh, int tid) {
   if (L < kSampleMinLen) return 0u;
-  uint32_t sk[kSampleBlocks];
-  sample_load(row, L, sk, tid);
-  return sample_select(sk, L, K, sh, tid);
+  uint32_t sk[RowsGeom<NW>::SampleBlocks];
+  sample_load<NW>(row, L, sk, tid);
+  return sample_select<NW>(sk, L, K, sh, tid);
 }
 
 // Exact selection of the rem largest of the gathered keys (ties to the
 // lowest positions), ids(position) written to out[0, rem).  The keys sit in
-// kWaves segments of lkey/lid: segment w holds c[w] keys from w*stride (the
+// NW segments of lkey/lid: segment w holds c[w] keys from w*stride (the
 // histogram path passes one segment).  1 <= rem <= n = sum of c[w] <=
 // kRowsCap.  All threads call this.
-template <class IdMap>
-__device__ __forceinline__ void select_gathered(RowsShared& S, const uint32_t (&c)[kWaves], uint32_t stride,
+template <int NW, class IdMap>
+__device__ __forceinline__ void select_gathered(RowsShared& S, const uint32_t (&c)[NW], uint32_t stride,
                                                 int rem, int32_t* out, const IdMap& ids, int tid) {
-  const uint32_t n = c[0] + c[1] + c[2] + c[3];
-  const RegLayout lay = block_list_layout(n, (uint32_t)tid);
-  uint32_t key[kRowsRegs];
-  int32_t id[kRowsRegs];
+  constexpr int Regs = RowsGeom<NW>::Regs;
+  uint32_t n = 0u;
 #pragma unroll
-  for (int j = 0; j < kRowsRegs; ++j) {
+  for (int w = 0; w < NW; ++w) n += c[w];
+  const RegLayout lay = block_list_layout<NW>(n, (uint32_t)tid);
+  uint32_t key[Regs];
+  int32_t id[Regs];
+#pragma unroll
+  for (int j = 0; j < Regs; ++j) {
     uint32_t x = lay.at(j), at = x;  // list element x -> its segment slot
     bool later = true;               // x lies beyond the segments seen so far
 #pragma unroll
-    for (int w = 0; w < kWaves - 1; ++w) {
+    for (int w = 0; w < NW - 1; ++w) {
       later = later && x >= c[w];
       x = later ? x - c[w] : x;
       at = later ? x + (uint32_t)(w + 1) * stride : at;
@@ -220,25 +241,29 @@ __device__ __forceinline__ void select_gathered(RowsShared& S, const uint32_t (&
     id[j] = v ? S.lid[at] : 0;
   }
   const auto kf = [&](int j) { return key[j]; };
-  const RangeSel sel = (n > (uint32_t)rem) ? range_select_regs<kRowsRegs>(kf, lay, rem, S.sh, tid)
+  const RangeSel sel = (n > (uint32_t)rem) ? range_select_regs<Regs, NW>(kf, lay, rem, S.sh, tid)
                                             : RangeSel{1u, 0xFFFFFFFFu, rem, (int)n};
-  const uint32_t idlo = tie_bound_regs(key, id, lay, sel, S.sh, tid);
-  emit_range_regs(key, id, lay, sel, idlo, rem, rem, out, ids, S.sh, tid);
+  const uint32_t idlo = tie_bound_regs<NW>(key, id, lay, sel, S.sh, tid);
+  emit_range_regs<NW>(key, id, lay, sel, idlo, rem, rem, out, ids, S.sh, tid);
 }
 
 // Rows of a dense matrix: row t is scores + t*ld, range [row_start[t],
 // row_end[t]) (row_start null: [0, row_end[t])), ids are positions.
 struct DenseRows {
-  static constexpr int kUnroll = 4;  // many rows: workgroups enough to cover the latency
+  template <int NW>
+  static constexpr int unroll() { return 4; }  // many rows: workgroups enough to cover the latency
   static constexpr int kMinBlocks = 3;
   RowsArgs A;
+  template <int NW>
   __device__ __forceinline__ bool range(int t, int& s0, int& s1, int) const {
     s0 = A.row_start ? A.row_start[t] : 0;
     s1 = A.row_end[t];
     return s0 >= 0 && s0 <= s1 && s1 <= A.N;
   }
   // the pre-gather's check (the same)
-  __device__ __forceinline__ bool gather_range(int t, int& s0, int& s1, int tid) const { return range(t, s0, s1, tid); }
+  __device__ __forceinline__ bool gather_range(int t, int& s0, int& s1, int tid) const {
+    return range<kWaves>(t, s0, s1, tid);
+  }
   __device__ __forceinline__ const float* row(int t) const { return A.scores + (int64_t)t * A.ld; }
   __device__ __forceinline__ IdIdentity ids(int) const { return IdIdentity{}; }
 };
@@ -248,24 +273,29 @@ struct DenseRows {
 // range or a workgroup of the scoring kernel flagged a bad page id; ids are
 // physical cache slots.
 struct PagedRows {
-  static constexpr int kUnroll = 16;  // few long rows: one workgroup must cover the latency alone
+  // few long rows: one workgroup must cover the latency alone (four times
+  // fewer loads per step with four times the threads)
+  template <int NW>
+  static constexpr int unroll() { return NW >= 16 ? 4 : 16; }
   static constexpr int kMinBlocks = 1;
   RowsArgs A;
   // all threads call this: the length and every page id the sequence uses,
-  // four loads per thread in flight per round of 1024 pages (clamped
+  // four loads per thread in flight per round of 4*NT pages (clamped
   // indexes, no branch per load), then a workgroup OR
+  template <int NW>
   __device__ __forceinline__ bool range(int b, int& s0, int& s1, int tid) const {
+    constexpr int NT = 64 * NW;
     s0 = 0;
     s1 = A.row_end[b];
     bool bad = s1 < 0 || s1 > A.N;
     const int np = bad ? 0 : (s1 + 63) >> 6;
     const int32_t* pt = A.table + (int64_t)b * A.max_pages;
-    for (int p0 = 0; p0 < np; p0 += 4 * kWG) {
+    for (int p0 = 0; p0 < np; p0 += 4 * NT) {
       int pg[4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) pg[u] = pt[min(p0 + u * kWG + tid, np - 1)];
+      for (int u = 0; u < 4; ++u) pg[u] = pt[min(p0 + u * NT + tid, np - 1)];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) bad |= (p0 + u * kWG + tid < np) & ((pg[u] < 0) | (pg[u] >= A.num_pages));
+      for (int u = 0; u < 4; ++u) bad |= (p0 + u * NT + tid < np) & ((pg[u] < 0) | (pg[u] >= A.num_pages));
     }
     return !__syncthreads_or(bad);
   }
@@ -280,12 +310,19 @@ struct PagedRows {
   __device__ __forceinline__ IdPaged ids(int b) const { return IdPaged{A.table + (int64_t)b * A.max_pages, A.max_pages}; }
 };
 
-// Dense rows come by the thousand: three workgroups per CU (LDS allows
-// three) keep enough loads in flight.  Paged decode rows are few and long:
-// one workgroup per row with deeper loads and no occupancy bound, so that
-// the register select does not spill.
-template <class Rows>
-__global__ __launch_bounds__(kWG, Rows::kMinBlocks) void k_topk_rows(RowsArgs A) {
+// Dense rows come by the thousand: three 256-thread workgroups per CU (LDS
+// allows three) keep enough loads in flight.  Paged decode rows are few and
+// long: one workgroup per row with no occupancy bound, so that the register
+// select does not spill, and 1024 threads (NW = 16), whose shorter per-thread
+// chains select a sequence's pre-gathered keys faster (13 against 15 us for
+// 16 sequences); reading and selecting a whole sequence in that one
+// workgroup instead of pre-gathering it over 32 took 30 us.
+template <class Rows, int NW>
+__global__ __launch_bounds__(64 * NW, Rows::kMinBlocks) void k_topk_rows(RowsArgs A) {
+  constexpr int NT = 64 * NW;
+  constexpr int Regs = RowsGeom<NW>::Regs;
+  constexpr int SegCap = RowsGeom<NW>::SegCap;
+  constexpr int U = Rows::template unroll<NW>();
   __shared__ RowsShared S;
   const Rows R{A};
   const int tid = threadIdx.x;
@@ -296,19 +333,19 @@ __global__ __launch_bounds__(kWG, Rows::kMinBlocks) void k_topk_rows(RowsArgs A)
   // pre-gathered regions: every slot this thread may hold and the region's
   // count, loaded first (their addresses depend on neither the count nor
   // the row's checks), so that they arrive with the range check's loads
-  // instead of two round trips after it.  Region g is read by the 256/G
-  // threads g*256/G .. ; thread slot j holds region element
-  // (tid mod 256/G) + j*256/G.
-  uint32_t graw[kRowsRegs];
-  int32_t iraw[kRowsRegs];
+  // instead of two round trips after it.  Region g is read by the NT/G
+  // threads g*NT/G .. ; thread slot j holds region element
+  // (tid mod NT/G) + j*NT/G.
+  uint32_t graw[Regs];
+  int32_t iraw[Regs];
   uint32_t gc = 0u;
   if (A.gcnt) {
     const int G = A.gsplit;  // a power of two <= kMaxGatherSplit
-    const uint32_t tpr = (uint32_t)(kWG / G);
+    const uint32_t tpr = (uint32_t)(NT / G);
     const int g = tid / (int)tpr;
     const int64_t region = ((int64_t)t * G + g) * A.gcap;
 #pragma unroll
-    for (int j = 0; j < kRowsRegs; ++j) {
+    for (int j = 0; j < Regs; ++j) {
       const int64_t e = region + min((uint32_t)tid % tpr + (uint32_t)j * tpr, (uint32_t)A.gcap - 1u);
       graw[j] = A.gkey[e];
       iraw[j] = A.gid[e];
@@ -316,8 +353,8 @@ __global__ __launch_bounds__(kWG, Rows::kMinBlocks) void k_topk_rows(RowsArgs A)
     gc = A.gcnt[(int64_t)t * G + g];
   }
   int s0, s1;
-  if (!R.range(t, s0, s1, tid)) {
-    for (int i = tid; i < A.K; i += kWG) out[i] = -1;
+  if (!R.template range<NW>(t, s0, s1, tid)) {
+    for (int i = tid; i < A.K; i += NT) out[i] = -1;
     if (stats && tid == 0) atomicAdd(&stats[kStBad], 1u);
     return;
   }
@@ -325,7 +362,7 @@ __global__ __launch_bounds__(kWG, Rows::kMinBlocks) void k_topk_rows(RowsArgs A)
   const int K = A.K;
   const auto ids = R.ids(t);
   if (L <= K) {  // every key of the row, in position order
-    for (int i = tid; i < K; i += kWG) out[i] = i < L ? ids(s0 + i) : -1;
+    for (int i = tid; i < K; i += NT) out[i] = i < L ? ids(s0 + i) : -1;
     if (stats && tid == 0) atomicAdd(&stats[kStTrivial], 1u);
     return;
   }
@@ -335,58 +372,59 @@ __global__ __launch_bounds__(kWG, Rows::kMinBlocks) void k_topk_rows(RowsArgs A)
   // its threads' registers: select from them
   if (A.gcnt) {
     const int G = A.gsplit;
-    const uint32_t tpr = (uint32_t)(kWG / G);
+    const uint32_t tpr = (uint32_t)(NT / G);
     uint32_t n = 0u;
-    block_exclusive_scan(tid % (int)tpr == 0 ? gc : 0u, S.sh, tid, n);
-    const bool fits = !__syncthreads_or(gc > tpr * (uint32_t)kRowsRegs);
+    block_exclusive_scan<NW>(tid % (int)tpr == 0 ? gc : 0u, S.sh, tid, n);
+    const bool fits = !__syncthreads_or(gc > tpr * (uint32_t)Regs);
     if (fits && n >= (uint32_t)K) {
       // slots past the wave's fullest region are empty in all its threads
       uint32_t jw = (gc + tpr - 1u) / tpr;
 #pragma unroll
       for (int o = 32; o > 0; o >>= 1) jw = max(jw, (uint32_t)__shfl_xor((int)jw, o, 64));
       const RegLayout lay{(uint32_t)tid % tpr, tpr, gc, (uint32_t)__builtin_amdgcn_readfirstlane((int)jw)};
-      uint32_t key[kRowsRegs];
-      int32_t id[kRowsRegs];
+      uint32_t key[Regs];
+      int32_t id[Regs];
 #pragma unroll
-      for (int j = 0; j < kRowsRegs; ++j) {
+      for (int j = 0; j < Regs; ++j) {
         const bool v = lay.valid(j);
         key[j] = v ? graw[j] : 0u;
         id[j] = v ? iraw[j] : 0;
       }
       const auto kf = [&](int j) { return key[j]; };
-      const RangeSel sel = (n > (uint32_t)K) ? range_select_regs<kRowsRegs>(kf, lay, K, S.sh, tid)
+      const RangeSel sel = (n > (uint32_t)K) ? range_select_regs<Regs, NW>(kf, lay, K, S.sh, tid)
                                               : RangeSel{1u, 0xFFFFFFFFu, K, (int)n};
-      const uint32_t idlo = tie_bound_regs(key, id, lay, sel, S.sh, tid);
-      emit_range_regs(key, id, lay, sel, idlo, K, K, out, ids, S.sh, tid);
+      const uint32_t idlo = tie_bound_regs<NW>(key, id, lay, sel, S.sh, tid);
+      emit_range_regs<NW>(key, id, lay, sel, idlo, K, K, out, ids, S.sh, tid);
       if (stats && tid == 0) atomicAdd(&stats[kStFast], 1u);
       return;
     }
   }
 
   // step 0: the sampled cut (key 0 keeps every key)
-  uint32_t cut = sample_cut(row, L, K, S.sh, tid);
+  uint32_t cut = sample_cut<NW>(row, L, K, S.sh, tid);
 
   // step 1: one pass gathering the keys at or above the cut into the
   // waves' private segments (slot = the wave's scalar count + rank in the
   // ballot: no atomics)
-  uint32_t c[kWaves] = {0u, 0u, 0u, 0u};  // keys in each segment
-  uint32_t stride = (uint32_t)kSegCap;
+  uint32_t c[NW];  // keys in each segment
+#pragma unroll
+  for (int w = 0; w < NW; ++w) c[w] = 0u;
+  uint32_t stride = (uint32_t)SegCap;
   int rem = K;       // how many of them to take
   int32_t* dst = out;
   bool gathered = false;
   {
     const int wave = tid >> 6;
-    const uint32_t wcnt = gather_ge<Rows::kUnroll>(row, L, tid, cut, S.lkey + wave * kSegCap,
-                                                    S.lid + wave * kSegCap, s0);
+    const uint32_t wcnt = gather_ge<U, NW>(row, L, tid, cut, S.lkey + wave * SegCap, S.lid + wave * SegCap, s0);
     if ((tid & 63) == 0) S.segc[wave] = wcnt;
     __syncthreads();
     uint32_t n = 0u;
     bool full = false;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
+    for (int w = 0; w < NW; ++w) {
       c[w] = S.segc[w];
       n += c[w];
-      full |= c[w] > (uint32_t)kSegCap;
+      full |= c[w] > (uint32_t)SegCap;
     }
     gathered = n >= (uint32_t)K && !full;
     if (n < (uint32_t)K) cut = 0u;  // the cut kept too few keys: histogram the whole row
@@ -397,26 +435,27 @@ __global__ __launch_bounds__(kWG, Rows::kMinBlocks) void k_topk_rows(RowsArgs A)
   bool generic = false;  // the boundary bin does not fit in LDS
   if (!gathered) {
     // histogram path: the bin of the K-th largest key among keys >= cut
-    for (int i = tid; i < kRowsBins; i += kWG) S.hist[i] = 0u;
+    for (int i = tid; i < kRowsBins; i += NT) S.hist[i] = 0u;
     if (tid == 0) { S.n_gt = 0u; S.n_eq = 0u; }
     __syncthreads();
-    for_each_key<Rows::kUnroll>(row, L, tid, [&](int, bool v, uint32_t key) {
+    for_each_key<U, NW>(row, L, tid, [&](int, bool v, uint32_t key) {
       hist_add(S.hist, key >> kRowsShift, v && key >= cut);  // returns at once when no lane qualifies
     });
     __syncthreads();
     {
-      // thread u holds bins 8u .. 8u+7
-      uint32_t h[8], a = 0u;
+      // thread u holds bins BPT*u .. BPT*u + BPT-1
+      constexpr int BPT = kRowsBins / NT;
+      uint32_t h[BPT], a = 0u;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) { h[j] = S.hist[8 * tid + j]; a += h[j]; }
+      for (int j = 0; j < BPT; ++j) { h[j] = S.hist[BPT * tid + j]; a += h[j]; }
       uint32_t total;
-      const uint32_t before = block_exclusive_scan(a, S.sh, tid, total);
+      const uint32_t before = block_exclusive_scan<NW>(a, S.sh, tid, total);
       uint32_t ab = total - before - a;  // keys in bins above this thread's
       const uint32_t r = (uint32_t)K;
       if (ab < r && r <= ab + a) {
 #pragma unroll
-        for (int j = 7; j >= 0; --j) {
-          if (ab < r && r <= ab + h[j]) { S.bin = 8u * tid + j; S.above = ab; S.inbin = h[j]; }
+        for (int j = BPT - 1; j >= 0; --j) {
+          if (ab < r && r <= ab + h[j]) { S.bin = (uint32_t)(BPT * tid + j); S.above = ab; S.inbin = h[j]; }
           ab += h[j];
         }
       }
@@ -425,7 +464,7 @@ __global__ __launch_bounds__(kWG, Rows::kMinBlocks) void k_topk_rows(RowsArgs A)
     const uint32_t bin = S.bin, above = S.above, inbin = S.inbin;
 
     // keys above the bin go straight out; the bin's keys (>= cut) to LDS
-    for_each_key<Rows::kUnroll>(row, L, tid, [&](int i, bool v, uint32_t key) {
+    for_each_key<U, NW>(row, L, tid, [&](int i, bool v, uint32_t key) {
       const uint32_t d = key >> kRowsShift;
       const bool gt = v && d > bin, eq = v && d == bin && key >= cut;
       if (__ballot(gt || eq)) {
@@ -436,7 +475,9 @@ __global__ __launch_bounds__(kWG, Rows::kMinBlocks) void k_topk_rows(RowsArgs A)
       }
     });
     __syncthreads();
-    c[0] = inbin; c[1] = 0u; c[2] = 0u; c[3] = 0u;
+    c[0] = inbin;
+#pragma unroll
+    for (int w = 1; w < NW; ++w) c[w] = 0u;
     stride = 0u;
     rem = K - (int)above;  // 1 <= rem <= inbin
     dst = out + above;
@@ -444,13 +485,13 @@ __global__ __launch_bounds__(kWG, Rows::kMinBlocks) void k_topk_rows(RowsArgs A)
   }
 
   if (!generic) {
-    select_gathered(S, c, stride, rem, dst, ids, tid);
+    select_gathered<NW>(S, c, stride, rem, dst, ids, tid);
     if (stats && tid == 0) atomicAdd(&stats[kStFast], 1u);
   } else {
     // the bin does not fit: exact radix select over the row in memory
     const SrcDense<decltype(ids)> src{row, s0, ids};
-    const SelResult sel = radix_select(src, L, K, S.sh, tid, false, true);
-    emit_selection(src, L, sel, K, K, out, S.sh, tid);
+    const SelResult sel = radix_select<NW>(src, L, K, S.sh, tid, false, true);
+    emit_selection<NW>(src, L, sel, K, K, out, S.sh, tid);
     if (stats && tid == 0) atomicAdd(&stats[kStRepaired], 1u);
   }
 }
@@ -568,20 +609,18 @@ int launch_topk_rows_gathered(const RowsArgs& A, hipStream_t stream) {
   if (A.Q > kMaxGridY) return IDX_EUNSUPPORTED;  // rows index the gather grid's y dimension
   if (A.table) {
     hipLaunchKernelGGL(k_rows_gather<PagedRows>, dim3(A.gsplit, A.Q), dim3(kWG), 0, stream, A);
-    hipLaunchKernelGGL(k_topk_rows<PagedRows>, dim3(A.Q), dim3(kWG), 0, stream, A);
+    hipLaunchKernelGGL((k_topk_rows<PagedRows, kMaxWaves>), dim3(A.Q), dim3(64 * kMaxWaves), 0, stream, A);
   } else {
     hipLaunchKernelGGL(k_rows_gather<DenseRows>, dim3(A.gsplit, A.Q), dim3(kWG), 0, stream, A);
-    hipLaunchKernelGGL(k_topk_rows<DenseRows>, dim3(A.Q), dim3(kWG), 0, stream, A);
+    hipLaunchKernelGGL((k_topk_rows<DenseRows, kWaves>), dim3(A.Q), dim3(kWG), 0, stream, A);
   }
   return hipGetLastError() == hipSuccess ? IDX_OK : IDX_EHIP;
 }
 
 int launch_topk_rows(const RowsArgs& A, hipStream_t stream) {
   if (A.Q == 0) return IDX_OK;
-  if (A.table)
-    hipLaunchKernelGGL(k_topk_rows<PagedRows>, dim3(A.Q), dim3(kWG), 0, stream, A);
-  else
-    hipLaunchKernelGGL(k_topk_rows<DenseRows>, dim3(A.Q), dim3(kWG), 0, stream, A);
+  if (A.table) return IDX_EINVAL;  // paged rows go through the pre-gather
+  hipLaunchKernelGGL((k_topk_rows<DenseRows, kWaves>), dim3(A.Q), dim3(kWG), 0, stream, A);
   return hipGetLastError() == hipSuccess ? IDX_OK : IDX_EHIP;
 }
 

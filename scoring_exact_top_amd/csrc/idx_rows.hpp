@@ -37,6 +37,7 @@ constexpr int kMaxGatherSplit = 32;
 // set, dense rows otherwise; gkey must be set).
 int launch_topk_rows_gathered(const RowsArgs& A, hipStream_t stream);
 
+// The per-row select alone, for dense rows (table must be null).
 int launch_topk_rows(const RowsArgs& A, hipStream_t stream);
 
 }  // namespace idxk
