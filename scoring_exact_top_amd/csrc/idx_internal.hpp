@@ -128,8 +128,7 @@ constexpr int kRepairWalkWGs = 512;    // rescoring walk: the workgroups of one 
 // (massive ties) is selected by that workgroup from the row's scratch.
 constexpr int kRepairDigits = 2;
 constexpr int kRepairGroupCap = kCandCap;  // gathered boundary keys per row (<= its candidate area)
-constexpr int kRepairGroupRegs = kRepairGroupCap / kWG;
-constexpr int kRepairFinalGrid = 1024;
+constexpr int kRepairFinalGrid = 256;  // workgroups of 1024 threads, one row each at a time
 
 // Words kept per slotted repair row (PrefillArgs::rrow): the gather's
 // output counters (keys above the boundary emitted; boundary keys emitted

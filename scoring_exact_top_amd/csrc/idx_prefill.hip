@@ -930,7 +930,8 @@ struct SrcGroup {
 // (range select, then the tie-break on the ids); a larger one by radix
 // passes over the row's scratch keys, restricted to the group, whose emit
 // takes tied keys in position order.
-__global__ __launch_bounds__(kWG) void k_prefill_repair_final(PrefillArgs A) {
+__global__ __launch_bounds__(64 * kMaxWaves) void k_prefill_repair_final(PrefillArgs A) {
+  constexpr int NW = kMaxWaves;  // one row per workgroup: 1024 threads shorten its chains
   __shared__ SelShared sh;
   const int tid = threadIdx.x;
   const uint32_t n_slot = min(__atomic_load_n(&A.ctrl[kCtrlFail], __ATOMIC_RELAXED), (uint32_t)A.rslots);
@@ -942,20 +943,20 @@ __global__ __launch_bounds__(kWG) void k_prefill_repair_final(PrefillArgs A) {
     if (rs.done) continue;  // written whole by the gather
     int32_t* out = A.out + (int64_t)row.t * A.K + (row.kr - rs.rem);
     if (rs.group <= kRepairGroupCap) {
-      constexpr int M = kRepairGroupRegs;
+      constexpr int M = kRepairGroupCap / (64 * NW);
       const uint32_t n = (uint32_t)rs.group;
-      const RegLayout lay = block_list_layout(n, (uint32_t)tid);
+      const RegLayout lay = block_list_layout<NW>(n, (uint32_t)tid);
       uint32_t key[M];
       int32_t id[M];
       load_list_regs(key, id, repair_group(A, row.t), n, lay, [](uint32_t x) { return x; });
       const auto kf = [&](int j) { return key[j]; };
-      const RangeSel sel = range_select_regs<M>(kf, lay, rs.rem, sh, tid);  // rem < group
-      const uint32_t idlo = tie_bound_regs(key, id, lay, sel, sh, tid);
-      emit_range_regs(key, id, lay, sel, idlo, rs.rem, rs.rem, out, IdIdentity{}, sh, tid);
+      const RangeSel sel = range_select_regs<M, NW>(kf, lay, rs.rem, sh, tid);  // rem < group
+      const uint32_t idlo = tie_bound_regs<NW>(key, id, lay, sel, sh, tid);
+      emit_range_regs<NW>(key, id, lay, sel, idlo, rs.rem, rs.rem, out, IdIdentity{}, sh, tid);
     } else {
       const SrcGroup src{A.scratch + (int64_t)f * A.rstride, rs.mask, rs.prefix, row.s0};
-      const SelResult sel = radix_select(src, row.L, rs.rem, sh, tid, false, true);
-      emit_selection(src, row.L, sel, rs.rem, rs.rem, out, sh, tid);
+      const SelResult sel = radix_select<NW>(src, row.L, rs.rem, sh, tid, false, true);
+      emit_selection<NW>(src, row.L, sel, rs.rem, rs.rem, out, sh, tid);
       __syncthreads();
     }
   }
@@ -1018,7 +1019,8 @@ int launch_prefill(const PrefillArgs& A, hipStream_t stream) {
   if (A.rslots < A.Q) hipLaunchKernelGGL(k_prefill_repair_fallback, dim3(kRepairFallback), dim3(kWG), 0, stream, A);
   hipLaunchKernelGGL(k_prefill_repair_pass, dim3(kRepairPassGrid), dim3(kWG), 0, stream, A);
   hipLaunchKernelGGL(k_prefill_repair_gather, dim3(kRepairPassGrid), dim3(kWG), 0, stream, A);
-  hipLaunchKernelGGL(k_prefill_repair_final, dim3((unsigned)min(A.rslots, kRepairFinalGrid)), dim3(kWG), 0, stream, A);
+  hipLaunchKernelGGL(k_prefill_repair_final, dim3((unsigned)min(A.rslots, kRepairFinalGrid)), dim3(64 * kMaxWaves), 0,
+                     stream, A);
   return hipGetLastError() == hipSuccess ? IDX_OK : IDX_EHIP;
 }
 
