@@ -416,19 +416,6 @@ __device__ __forceinline__ int relaid_src_offset(int tile, int blk, int l) {
 // offset fits in 31 bits.
 __device__ __forceinline__ int refill_tile(int tile, int ntiles) { return tile < ntiles ? tile : ntiles - 1; }
 
-// Load relaid tile `tile` (wave-uniform, 0 <= tile < ntiles); scales from
-// the original array.
-__device__ __forceinline__ void load_tile_relaid(KeyTile& t, rsrc_t kt, rsrc_t ks, int tile, uint32_t lane) {
-  const int soff = tile * (kTile * kD);
-#pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    const v4i x = __builtin_amdgcn_raw_buffer_load_b128(kt, (int)lane * 16, soff + (2 * c) * 1024, 0);
-    const v4i y = __builtin_amdgcn_raw_buffer_load_b128(kt, (int)lane * 16, soff + (2 * c + 1) * 1024, 0);
-    t.kb[c] = cat8(x, y);
-  }
-  t.ks = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(ks, (int)lane * 4, tile * 256, 0));
-}
-
 // Tile of 64 arbitrary keys: key_of(i) gives the key index of tile slot i.
 template <class F>
 __device__ __forceinline__ void load_tile_gather(KeyTile& t, const KeyBuf& kbuf, const F& key_of, uint32_t lane) {

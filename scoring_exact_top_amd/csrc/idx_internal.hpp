@@ -218,6 +218,9 @@ struct PrefillArgs {
   int32_t force_tau;
   int32_t keep_all;  // every valid row keeps all its keys (N <= kCandCap): no sampler, no repair
   int32_t fuse_tau;  // one split: the main kernel takes its rows' thresholds itself
+  int32_t direct;    // no relaid copy: the one-pair walk (and the repair) read key tiles from k
+                     // itself, as the shared walk always does
+  int32_t clear_main;  // no kernel ran before the main one: it clears the counters and repair state
   float tau_value;
   hipEvent_t ev_main_start, ev_main_stop;  // host-side only: timing hooks
   int32_t main_reps;                       // host-side only: launches of the main kernel

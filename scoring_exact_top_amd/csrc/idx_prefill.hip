@@ -136,9 +136,13 @@ __device__ __forceinline__ void pair_scores(const QOp2& qo, const KeyTile& kt, f
   s1 = reduce_scatter4(q1[0], q1[1], q1[2], q1[3]) * kt.ks;
 }
 
-template <int MODE, bool SH = false>
+template <int MODE, bool SH = false, bool DIRECT = false>
 __global__ __launch_bounds__(kWG, 2) void k_prefill_pair(PrefillArgs A) {
   static_assert(!SH || MODE != kPairRepair, "repair mode walks one pair per workgroup");
+  // key tiles from k itself (the shared walk stages each tile once per
+  // workgroup, so the loads' extra address work is hidden; the one-pair
+  // walk only where no relaid copy was made) or from the relaid copy kt
+  constexpr bool kRaw = SH || DIRECT;
   __shared__ uint8_t s_qprep[kWaves][2 * kUTerms * kD];
   // optional clock probe: this wave's shader-clock cycles and constant-rate
   // wall-clock ticks from its start to its end, summed over all waves
@@ -150,6 +154,18 @@ __global__ __launch_bounds__(kWG, 2) void k_prefill_pair(PrefillArgs A) {
   const int tid = threadIdx.x;
   const uint32_t lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  if constexpr (MODE == kPairFused || MODE == kPairDebug) {
+    // the first kernel of the call: the counters and the repair state start
+    // at zero (read only by the kernels after this one)
+    if (A.clear_main) {
+      if (blockIdx.x == 0) clear_ctrl(A.ctrl, tid);
+      if (!A.keep_all) {
+        const int64_t i0 = (int64_t)blockIdx.x * kWG + tid, stride = (int64_t)gridDim.x * kWG;
+        for (int64_t i = i0; i < (int64_t)A.rslots * kRepairDigits * 256; i += stride) A.rhist[i] = 0u;
+        for (int64_t i = i0; i < (int64_t)A.rslots * kRowWords; i += stride) A.rrow[i] = 0u;
+      }
+    }
+  }
   // the pair's rows (t_of: -1 for none) and, in repair mode, their scratch slots
   int split, nsplit, t_of[2], slot[2] = {0, 0};
   if constexpr (MODE == kPairRepair) {
@@ -190,7 +206,7 @@ __global__ __launch_bounds__(kWG, 2) void k_prefill_pair(PrefillArgs A) {
     if (t >= 0 && t < A.Q) {
       const int s = A.row_start[t], e = A.row_end[t];
       if (s >= 0 && s <= e && e <= A.N) {
-        rs[r] = s; re[r] = e; tr[r] = A.fuse_tau ? -INFINITY : A.tau[t];
+        rs[r] = s; re[r] = e; tr[r] = (A.fuse_tau || A.keep_all) ? -INFINITY : A.tau[t];
         if (e > s) { lo = min(lo, s); hi = max(hi, e); }
       }
     }
@@ -286,12 +302,28 @@ __global__ __launch_bounds__(kWG, 2) void k_prefill_pair(PrefillArgs A) {
     }
   }
 
+  if constexpr (MODE == kPairFused || MODE == kPairDebug) {
+    // keeping every key, the rows' thresholds are -inf (+inf for an invalid
+    // range), recorded as the sampler records its thresholds
+    if (A.keep_all) {
+#pragma unroll
+      for (int r = 0; r < 2; ++r)
+        if (split == 0 && (SH ? lane : tid) == r && t_of[r] >= 0) A.tau[t_of[r]] = tr[r];
+    }
+  }
+
   const KeyBuf kbuf = make_keybuf(A.k, A.k_scale, A.N);
   const int ntiles = (A.N + 63) >> 6;
-  const rsrc_t ktb = __builtin_amdgcn_make_buffer_rsrc((void*)A.kt, (short)0, ntiles * kTile * kD, 0x00020000);
+  // tile T's keys start at byte T*8192 in both layouts; block 2c+h of a tile
+  // (bytes 32*(l/16) + 16h of key (sub-tile c, row l%16) for lane l) lies at
+  // lane l's voff + boff(c, h) in the relaid copy, at gvoff + boff(c, h) in k
+  const rsrc_t ktb = kRaw ? __builtin_amdgcn_make_buffer_rsrc((void*)A.k, (short)0, A.N * kD, 0x00020000)
+                          : __builtin_amdgcn_make_buffer_rsrc((void*)A.kt, (short)0, ntiles * kTile * kD, 0x00020000);
   const uint32_t seg_cap = (uint32_t)A.seg_eff;
   const int tile_hi = (hi + 63) >> 6;
-  const int voff = (int)lane * 16;
+  const int voff = (int)lane * 16;  // LDS staging and relaid loads
+  const int gvoff = kRaw ? (int)(lane & 15) * kD + 32 * (int)(lane >> 4) : voff;
+  const auto boff = [](int c, int h) { return kRaw ? sub_off(c) * kD + 16 * h : (2 * c + h) * 1024; };
   uint32_t cnt[2] = {0u, 0u};  // candidates of each row found by this wave
   float csum[2] = {0.f, 0.f};  // control build: running sums of the rows' valid scores
   float dmax[2] = {-INFINITY, -INFINITY};  // per lane: largest candidate dropped for lack of room
@@ -397,8 +429,8 @@ __global__ __launch_bounds__(kWG, 2) void k_prefill_pair(PrefillArgs A) {
 #pragma unroll
       for (int b = 0; b < 4; ++b)
         aB[b] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qo.a[1][b], kb[c], z, 0, 0, 0, 0, 0, 0);
-      kb[c] = cat8(__builtin_amdgcn_raw_buffer_load_b128(ktb, voff, ntoff + (2 * c) * 1024, 0),
-                   __builtin_amdgcn_raw_buffer_load_b128(ktb, voff, ntoff + (2 * c + 1) * 1024, 0));
+      kb[c] = cat8(__builtin_amdgcn_raw_buffer_load_b128(ktb, gvoff, ntoff + boff(c, 0), 0),
+                   __builtin_amdgcn_raw_buffer_load_b128(ktb, gvoff, ntoff + boff(c, 1), 0));
       q0[c] = epi(qo.wh[0], qo.sh[0], aA, au[0], au[1]);
       auB = au;
 #pragma unroll
@@ -428,8 +460,8 @@ __global__ __launch_bounds__(kWG, 2) void k_prefill_pair(PrefillArgs A) {
   const auto tile_body_shared = [&](int T, uint8_t* nxt) {
     const int nT = refill_tile(T + nseg, ntiles);
     const int ntoff = nT * (kTile * kD);
-    const v4i g0 = __builtin_amdgcn_raw_buffer_load_b128(ktb, voff, ntoff + (2 * wave) * 1024, 0);
-    const v4i g1 = __builtin_amdgcn_raw_buffer_load_b128(ktb, voff, ntoff + (2 * wave + 1) * 1024, 0);
+    const v4i g0 = __builtin_amdgcn_raw_buffer_load_b128(ktb, gvoff, ntoff + boff(wave, 0), 0);
+    const v4i g1 = __builtin_amdgcn_raw_buffer_load_b128(ktb, gvoff, ntoff + boff(wave, 1), 0);
     __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
@@ -479,9 +511,9 @@ __global__ __launch_bounds__(kWG, 2) void k_prefill_pair(PrefillArgs A) {
         const int t1 = refill_tile(T, ntiles);  // past the last tile: the loop is empty
         const int toff = t1 * (kTile * kD);
         *reinterpret_cast<v4i*>(buf0 + (2 * wave) * 1024 + voff) =
-            __builtin_amdgcn_raw_buffer_load_b128(ktb, voff, toff + (2 * wave) * 1024, 0);
+            __builtin_amdgcn_raw_buffer_load_b128(ktb, gvoff, toff + boff(wave, 0), 0);
         *reinterpret_cast<v4i*>(buf0 + (2 * wave + 1) * 1024 + voff) =
-            __builtin_amdgcn_raw_buffer_load_b128(ktb, voff, toff + (2 * wave + 1) * 1024, 0);
+            __builtin_amdgcn_raw_buffer_load_b128(ktb, gvoff, toff + boff(wave, 1), 0);
         ks_cur = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(kbuf.ks, (int)lane * 4, t1 * 256, 0));
       }
       __syncthreads();
@@ -496,11 +528,12 @@ __global__ __launch_bounds__(kWG, 2) void k_prefill_pair(PrefillArgs A) {
   } else if (lo < hi) {
     int T = (lo >> 6) + seg;
     {
-      KeyTile t;
-      load_tile_relaid(t, ktb, kbuf.ks, refill_tile(T, ntiles), lane);  // past the last tile: the loop is empty
+      const int t0 = refill_tile(T, ntiles);  // past the last tile: the loop is empty
 #pragma unroll
-      for (int c = 0; c < 4; ++c) kb[c] = t.kb[c];
-      ks_cur = t.ks;
+      for (int c = 0; c < 4; ++c)
+        kb[c] = cat8(__builtin_amdgcn_raw_buffer_load_b128(ktb, gvoff, t0 * (kTile * kD) + boff(c, 0), 0),
+                     __builtin_amdgcn_raw_buffer_load_b128(ktb, gvoff, t0 * (kTile * kD) + boff(c, 1), 0));
+      ks_cur = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(kbuf.ks, (int)lane * 4, t0 * 256, 0));
     }
     __builtin_amdgcn_s_waitcnt(0x0F70);  // drain once so the loop's waits stay exact
 #pragma unroll 1
@@ -964,23 +997,35 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_prefill_repair_final(Prefill
 
 // ------------------------------------------------------------------ launch
 
-// One launch of the main kernel in mode MODE with the call's walk geometry;
-// the events, when given, are recorded by the launch itself.
+// One launch of the main kernel in mode MODE with the call's walk geometry
+// and key source; the events, when given, are recorded by the launch itself.
 template <int MODE>
 static void launch_main(const PrefillArgs& A, hipStream_t stream, hipEvent_t e0, hipEvent_t e1) {
   const int rows = A.shared ? kSharedRows : 2;
   const unsigned grid = (unsigned)((A.Q + rows - 1) / rows * A.S);
-  void (*const kern)(PrefillArgs) = A.shared ? k_prefill_pair<MODE, true> : k_prefill_pair<MODE, false>;
+  void (*const kern)(PrefillArgs) = A.shared   ? k_prefill_pair<MODE, true>
+                                    : A.direct ? k_prefill_pair<MODE, false, true>
+                                               : k_prefill_pair<MODE, false, false>;
   if (e0 || e1)
     hipExtLaunchKernelGGL(kern, dim3(grid), dim3(kWG), 0, stream, e0, e1, 0, A);
   else
     hipLaunchKernelGGL(kern, dim3(grid), dim3(kWG), 0, stream, A);
 }
 
-int launch_prefill(const PrefillArgs& A, hipStream_t stream) {
-  if (A.Q == 0) return IDX_OK;
+// The relaid key copy is made only for the one-pair walk over rows too long
+// to keep every key (A.direct = 0): it needs it (reading k itself took it 20-25%
+// longer), while the shared walk stages each tile once per workgroup and
+// reads k at the same speed, and calls that keep every key are too short to
+// pay for the copy's launch.  Without the relayout kernel the main kernel
+// takes over its other duties.
+int launch_prefill(const PrefillArgs& args, hipStream_t stream) {
+  if (args.Q == 0) return IDX_OK;
+  PrefillArgs A = args;
   const int64_t nchunks = (int64_t)((A.N + 63) >> 6) * 512;
-  if (nchunks > 0) hipLaunchKernelGGL(k_relayout_keys, dim3((unsigned)(nchunks / kWG)), dim3(kWG), 0, stream, A);
+  if (!A.direct && nchunks > 0)
+    hipLaunchKernelGGL(k_relayout_keys, dim3((unsigned)(nchunks / kWG)), dim3(kWG), 0, stream, A);
+  else
+    A.clear_main = (A.keep_all || A.fuse_tau) ? 1 : 0;  // k_prefill_tau is not launched either
   if (A.math_only) {  // the control: the main kernel's scoring alone, nothing after it
     const int reps = A.main_reps > 1 ? A.main_reps : 1;
     for (int r = 0; r < reps; ++r)
@@ -1015,7 +1060,10 @@ int launch_prefill(const PrefillArgs& A, hipStream_t stream) {
   // the slotted failures rescored two per workgroup: enough workgroups for
   // every slot pair, at least two per CU for few failures
   const unsigned rgrid = (unsigned)max(kRepairWalkWGs, (A.rslots + 1) / 2);
-  hipLaunchKernelGGL(k_prefill_pair<kPairRepair>, dim3(rgrid), dim3(kWG), 0, stream, A);
+  if (A.direct)
+    hipLaunchKernelGGL((k_prefill_pair<kPairRepair, false, true>), dim3(rgrid), dim3(kWG), 0, stream, A);
+  else
+    hipLaunchKernelGGL((k_prefill_pair<kPairRepair, false, false>), dim3(rgrid), dim3(kWG), 0, stream, A);
   if (A.rslots < A.Q) hipLaunchKernelGGL(k_prefill_repair_fallback, dim3(kRepairFallback), dim3(kWG), 0, stream, A);
   hipLaunchKernelGGL(k_prefill_repair_pass, dim3(kRepairPassGrid), dim3(kWG), 0, stream, A);
   hipLaunchKernelGGL(k_prefill_repair_gather, dim3(kRepairPassGrid), dim3(kWG), 0, stream, A);
@@ -1032,7 +1080,8 @@ int launch_prefill(const PrefillArgs& A, hipStream_t stream) {
 int launch_prefill_unfused(const PrefillArgs& A, hipStream_t stream) {
   if (A.Q == 0) return IDX_OK;
   const int64_t nchunks = (int64_t)((A.N + 63) >> 6) * 512;
-  if (nchunks > 0) hipLaunchKernelGGL(k_relayout_keys, dim3((unsigned)(nchunks / kWG)), dim3(kWG), 0, stream, A);
+  if (!A.direct && nchunks > 0)
+    hipLaunchKernelGGL(k_relayout_keys, dim3((unsigned)(nchunks / kWG)), dim3(kWG), 0, stream, A);
   hipLaunchKernelGGL(k_prefill_tau, dim3(kRepairGrid), dim3(kWG), 0, stream, A);
   const int reps = A.main_reps > 1 ? A.main_reps : 1;
   for (int r = 0; r < reps; ++r)
