@@ -102,7 +102,6 @@ static int prefill_common(const uint8_t* q, const float* q_scale, const uint8_t*
     A.dbg_scores = reinterpret_cast<float*>(ws + L.dense);
     A.force_tau = 1;
     A.tau_value = INFINITY;
-    A.direct = A.shared;
     return launch_prefill_unfused(A, s);
   }
   // N <= kCandCap with the default capacities: every valid row has L <=
@@ -110,10 +109,9 @@ static int prefill_common(const uint8_t* q, const float* q_scale, const uint8_t*
   // certificate cannot fail (no sampling, no repair to launch)
   const bool small = !A.force_tau && A.N > 0 && A.N <= kCandCap && A.cand_cap >= kCandCap;
   A.keep_all = (small && !A.math_only) ? 1 : 0;
-  // key tiles from k itself in the shared walk and in calls this short (the
-  // control as the call it stands for); the one-pair walk over longer rows
-  // reads a relaid copy
-  A.direct = (A.shared || small) ? 1 : 0;
+  // the one-pair walk of calls this short reads key tiles from k itself (the
+  // control as the call it stands for); other calls read a relaid copy
+  A.direct = (small && !A.shared) ? 1 : 0;
   // the main kernel samples its rows itself (with S > 1 splits per row pair,
   // each split samples the pair: the same values, S times, in parallel)
   A.fuse_tau = (!A.force_tau && !A.keep_all && !A.math_only && A.N > 0) ? 1 : 0;

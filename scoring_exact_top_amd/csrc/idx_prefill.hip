@@ -139,10 +139,10 @@ __device__ __forceinline__ void pair_scores(const QOp2& qo, const KeyTile& kt, f
 template <int MODE, bool SH = false, bool DIRECT = false>
 __global__ __launch_bounds__(kWG, 2) void k_prefill_pair(PrefillArgs A) {
   static_assert(!SH || MODE != kPairRepair, "repair mode walks one pair per workgroup");
-  // key tiles from k itself (the shared walk stages each tile once per
-  // workgroup, so the loads' extra address work is hidden; the one-pair
-  // walk only where no relaid copy was made) or from the relaid copy kt
-  constexpr bool kRaw = SH || DIRECT;
+  static_assert(!SH || !DIRECT, "the shared walk reads the relaid copy");
+  // key tiles from the relaid copy kt, or (DIRECT: calls too short to pay
+  // for the copy) from k itself
+  constexpr bool kRaw = DIRECT;
   __shared__ uint8_t s_qprep[kWaves][2 * kUTerms * kD];
   // optional clock probe: this wave's shader-clock cycles and constant-rate
   // wall-clock ticks from its start to its end, summed over all waves
@@ -1012,12 +1012,11 @@ static void launch_main(const PrefillArgs& A, hipStream_t stream, hipEvent_t e0,
     hipLaunchKernelGGL(kern, dim3(grid), dim3(kWG), 0, stream, A);
 }
 
-// The relaid key copy is made only for the one-pair walk over rows too long
-// to keep every key (A.direct = 0): it needs it (reading k itself took it 20-25%
-// longer), while the shared walk stages each tile once per workgroup and
-// reads k at the same speed, and calls that keep every key are too short to
-// pay for the copy's launch.  Without the relayout kernel the main kernel
-// takes over its other duties.
+// The relaid key copy is made for every call but the one-pair walk over
+// calls that keep every key (A.direct): those are too short to pay for the
+// copy's launch, while elsewhere reading k itself cost the main kernel more
+// than the copy (the one-pair walk 20-25%, the shared walk 8% more cycles).
+// Without the relayout kernel the main kernel takes over its other duties.
 int launch_prefill(const PrefillArgs& args, hipStream_t stream) {
   if (args.Q == 0) return IDX_OK;
   PrefillArgs A = args;
