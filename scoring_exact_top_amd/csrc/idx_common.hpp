@@ -50,7 +50,6 @@ constexpr int kWaves = 4;
 constexpr int kMaxWaves = 16;  // the register select's largest workgroup (1024 threads)
 constexpr int kTile = 64;    // keys per tile (4 MFMA sub-tiles of 16)
 constexpr int kUTerms = 8;   // e4m3 terms of the linear vector u
-constexpr int kBlocks = 5;   // A blocks per tile: 4 head blocks + the u block
 
 // Sub-tile c of a 64-key tile covers keys [sub_off(c), +16).  This order makes
 // the reduce-scatter below land key l in lane l.

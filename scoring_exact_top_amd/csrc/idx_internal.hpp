@@ -117,7 +117,6 @@ __host__ __device__ inline int prefill_seg_cap(int nseg) {
 // repair_slots() failed rows at once, and kRepairFallback more slots serve
 // workgroups that repair whole rows alone once the slots run out.
 constexpr int kRepairChunk = 4096;
-constexpr int kRepairChunkTiles = kRepairChunk / 64;
 constexpr int kRepairGrid = 256;  // one workgroup per CU; items are strided over the grid
 constexpr int kRepairPassGrid = 1024;  // digit pass and gather: four workgroups per CU
 constexpr int kRepairWalkWGs = 512;    // rescoring walk: the workgroups of one round, two per CU
@@ -163,8 +162,6 @@ __device__ __forceinline__ uint32_t* stat_copy(uint32_t* ctrl, int block) {
 __device__ __forceinline__ void clear_ctrl(uint32_t* ctrl, int tid) {
   for (int i = tid; i < kCtrlWords; i += kWG) ctrl[i] = 0u;
 }
-
-__host__ __device__ inline int repair_grid(int rows) { return rows < 256 ? (rows > 0 ? rows : 1) : 256; }
 
 // Scratch row stride (keys): N rounded up to 64, so rows are 256-byte aligned.
 __host__ __device__ inline int64_t repair_stride(int nkeys) { return ((int64_t)nkeys + 63) & ~(int64_t)63; }

@@ -45,7 +45,6 @@ struct RowsGeom {
   static constexpr int SegCap = kRowsCap / NW;
   static constexpr int SampleBlocks = kSampleKeys / NT;
 };
-constexpr int kRowsRegs = RowsGeom<kWaves>::Regs;  // the 256-thread kernels'
 constexpr int kSampleBlocks = RowsGeom<kWaves>::SampleBlocks;
 
 // Dense row in memory: element i is position s0 + i, emitted as ids(s0 + i).
