@@ -45,6 +45,36 @@ def test_k_values(K):
     check_prefill_rows(case, r["out"], np.arange(case.Q))
 
 
+@pytest.mark.parametrize("name,Q,N,K,mode,opts", [
+    ("one_row_short", 1, 100, 2048, "normal", {}),                # keeps every key, L < K
+    ("keep_all_k17", 3, 8192, 17, "normal", {}),                  # keys read from k, 1024-thread select
+    ("fused_257", 257, 8193, 2048, "normal", {}),                 # sampled threshold, 256-thread select
+    ("fused_600", 600, 20000, 100, "normal", {}),
+    ("repair_all", 64, 70000, 2048, "normal", {"force_tau": float("inf")}),
+    ("repair_overflow", 40, 30000, 1000, "normal", {"force_tau": float("-inf"), "cand_cap": 600}),
+    ("repair_ties", 5, 40000, 2048, "ties16", {"force_tau": float("inf")}),
+])
+def test_shape_sweep(name, Q, N, K, mode, opts):
+    """Row counts on both sides of the select's workgroup-size switch (256
+    rows), key counts on both sides of the keep-every-key bound (8192), K
+    from 17 to 2048, and calls sent through the exact repair (underflow,
+    overflow, a tie group in the gathered boundary group): ragged ranges,
+    every row against the oracle."""
+    if mode == "ties16":
+        case = synth.causal_case(name, Q, N, seed=41, key_mode="ties16", K=K)
+    else:
+        case = synth.random_case(name, Q, N, seed=40 + Q, K=K, min_len=min(N, 50))
+    log("case", name, Q, N, K, opts)
+    r = run_prefill(case, **opts)
+    st = r["stats"]
+    log("stats", st)
+    check_prefill_rows(case, r["out"], np.arange(case.Q))
+    assert st["rows"] == case.Q and st["fast_ok"] + st["repaired"] == case.Q - st["bad_rows"], st
+    if opts.get("force_tau") == float("inf"):
+        long_rows = int(np.sum(case.row_end - case.row_start > K))
+        assert st["repaired"] >= long_rows, st
+
+
 def test_prefill_smoke_workload_full(e4m3):
     """64 rows at positions 8128..8191 of 8192 keys: every row, scores too."""
     case = synth.prefill_smoke(0)
