@@ -4,21 +4,26 @@
 //   k_decode_score  G workgroups per sequence split its keys (KV-dimension
 //                   parallelism, Fusing Indexer Scoring and Exact Top-k
 //                   page, "10. The optimization target after fusion");
-//                   each validates its pages, scores its chunk with the
-//                   prefill MFMA tile code and writes the FP32 scores at
-//                   the keys' logical positions into the workspace.
-//   k_topk_rows     one workgroup per sequence (idx_rows.hip): exact top-K
-//                   over the sequence's score row, ties at the K-th score to
-//                   the lowest logical positions, emitted as physical cache
-//                   slots.  Sequences with seq_len <= K take the remap path
-//                   there (every slot, no selection).
+//                   each scores its chunk with the prefill MFMA tile code
+//                   and writes the FP32 scores at the keys' logical
+//                   positions into the workspace.  For batches of up to 256
+//                   sequences it also takes the sequence's sampled threshold
+//                   from a few whole pages and stores the keys at or above
+//                   it as candidates, per wave.
+//   k_topk_rows     one workgroup per sequence (idx_rows.hip): checks the
+//                   sequence's page ids, then the exact top-K of those
+//                   candidates when there are at least K of them and none
+//                   was dropped (every other key scores below the
+//                   threshold), else of the score row itself; ties at the
+//                   K-th score go to the lowest logical positions, emitted
+//                   as physical cache slots.  Sequences with seq_len <= K
+//                   take the remap path there (every slot, no selection).
+//                   Larger batches pre-gather each score row above a cut
+//                   sampled from the row itself (k_rows_gather) instead.
 //
-// Unlike prefill, decode writes its scores out: a key costs 132 bytes of
-// HBM reads (codes and scale) and its score 4 bytes of writes, so the score
-// row adds 3% to the traffic, while a sampled threshold would need a
-// separate sampling pass before the scoring (one sequence's sample is a
-// chain of dependent gathers, about as long as the whole scoring kernel)
-// and a certificate with a repair path.  No host synchronisation anywhere.
+// The score row costs 4 bytes of writes per key against the 132 bytes of
+// reads (codes and scale) that scoring needs anyway; it serves the exact
+// fallback and the debug entry.  No host synchronisation anywhere.
 #include <hip/hip_ext.h>
 #include <string.h>
 
@@ -44,6 +49,16 @@ struct DecodeArgs {
   int32_t balanced;      // 1: workgroups assigned to sequences in proportion to their tiles
   uint32_t* ctrl;
   float* scores;         // [B][max_pages*64] scores at logical positions
+  // filtered candidates (balanced assignment only; null otherwise): wave v
+  // of workgroup g stores (order-preserving key, logical position) pairs of
+  // its keys at or above the sequence's sampled threshold into
+  // cand[(4g + v) * seg_cap ...] and their number (stored or not) into
+  // cnt[4g + v]; the first workgroup of sequence b records plan[b] = (its
+  // index, the sequence's workgroup count)
+  uint2* cand;
+  uint32_t* cnt;
+  uint2* plan;
+  int32_t seg_cap;
 };
 
 // One page of 64 keys (codes and scales) through buffer resources of its
@@ -67,6 +82,57 @@ __device__ __forceinline__ void load_page(KeyTile& t, const uint8_t* k, const fl
   t.ks = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, (int)lane * 4, 0, 0));
 }
 
+// Sampled threshold of a sequence ("3.2 Sampled threshold", Fusing Indexer
+// Scoring and Exact Top-k page, applied per decode sequence), at that
+// section's rate of about one key in 200 but taken as whole pages of the
+// cache (64 keys each, read like any other tile) at a fixed stride over the
+// sequence's full pages: P = ceil(ceil((L - 100) / 200) / 64) pages, at
+// most kDecodeSamplePages, page j being logical page floor((2j+1) F / (2P))
+// of the F = floor(L / 64) full ones.  tau is taken at the r-th largest of
+// the 64 P sampled scores, r = ceil(64 P * kSampleTarget / L), so that about
+// kSampleTarget keys are expected at or above it.  Sequences of at most
+// kDecodeKeepAll keys keep every key.
+constexpr int kDecodeSamplePages = 8;
+constexpr int kDecodeKeepAll = 4096;
+struct DecodeSample {
+  int pages, full, r;  // sampled pages (0: keep every key), full pages, rank
+};
+__device__ __forceinline__ DecodeSample decode_sample(int L) {
+  DecodeSample d{0, L >> 6, 0};
+  if (L <= kDecodeKeepAll) return d;
+  const int ns = (L - kSampleOffset + kSampleStride - 1) / kSampleStride;
+  d.pages = min(kDecodeSamplePages, max(1, (ns + 63) >> 6));
+  const int64_t n = 64 * (int64_t)d.pages;
+  const int64_t r = (n * kSampleTarget + L - 1) / L;
+  d.r = (int)(r < 1 ? 1 : (r > n ? n : r));
+  return d;
+}
+
+// The lower edge of the 16-bit bucket of the r-th largest of n <= 512
+// order-preserving keys (keys[0..n) in LDS), at or below that key, found
+// by one wave with no atomics: each lane holds eight keys, and the
+// bucket's bits are fixed from the top, each kept when at least r keys lie
+// at or above it (a ballot per key, counted on the scalar unit).
+// 1 <= r <= n.
+__device__ __forceinline__ uint32_t wave_cut16(const uint32_t* keys, int n, int r, uint32_t lane) {
+  uint32_t k[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int i = (int)lane + 64 * j;
+    k[j] = i < n ? keys[i] : 0u;
+  }
+  uint32_t t = 0u;
+#pragma unroll 1
+  for (int bit = 31; bit >= 16; --bit) {
+    const uint32_t c = t | (1u << bit);
+    int cnt = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) cnt += __popcll(__ballot(k[j] >= c));
+    t = cnt >= r ? c : t;
+  }
+  return t;
+}
+
 // Each workgroup scores one piece of one sequence: a run of its 64-key
 // tiles (pages).  Balanced assignment (batches of at most 256 sequences):
 // every workgroup computes the same plan from the lengths, a sequence with
@@ -86,9 +152,19 @@ __device__ __forceinline__ void load_page(KeyTile& t, const uint8_t* k, const fl
 // tiles, and the query arithmetic runs while those are in flight (a page
 // check or query preparation ahead of the first key load idled the memory
 // system for about 4.5 us).
+//
+// With the balanced assignment the workgroup also filters: before its walk
+// it takes the sequence's sampled threshold tau (every workgroup of the
+// sequence samples the same pages, so all get the same tau: the four
+// waves score the sampled pages into LDS, then each wave finds tau itself),
+// and each wave stores the keys of its tiles that score at least tau as
+// candidates into its own segment (slot = count + rank in the ballot; a
+// segment holds seg_cap of them and counts the rest), so that the selection
+// reads about 2K candidates per sequence instead of its whole score row.
 __global__ __launch_bounds__(kWG, 2) void k_decode_score(DecodeArgs A) {
   __shared__ uint8_t s_qprep[kWaves][kUTerms * kD];
   __shared__ SelShared sh;
+  __shared__ uint32_t s_samp[64 * kDecodeSamplePages];  // the sampled scores as order-preserving keys
   const int tid = threadIdx.x;
   const uint32_t lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -119,6 +195,7 @@ __global__ __launch_bounds__(kWG, 2) void k_decode_score(DecodeArgs A) {
       const int64_t g = sh.above, Gb = sh.inbucket, Tb = sh.pad0;
       p0 = (int)(Tb * g / Gb);
       p1 = (int)(Tb * (g + 1) / Gb);
+      if (g == 0 && tid == 0 && A.plan) A.plan[b] = make_uint2((uint32_t)wg, (uint32_t)Gb);
     }
   } else {
     b = wg / A.G;
@@ -133,32 +210,66 @@ __global__ __launch_bounds__(kWG, 2) void k_decode_score(DecodeArgs A) {
       }
     }
   }
-  if (p0 >= p1) return;
-  const int k1 = min(A.seq_lens[b], p1 << 6);  // the piece's last key + 1
-  const int32_t* pt = A.table + (int64_t)b * A.max_pages;
-  const int tile0 = p0 + wave;
-  const int nt = tile0 < p1 ? (p1 - tile0 + kWaves - 1) / kWaves : 0;
-  if (nt == 0) return;
-  {
+  const bool filter = A.cand != nullptr;
+  uint32_t ncand = 0u;  // this wave's candidates (wave-uniform)
+  if (p0 < p1) {
+    const int L = A.seq_lens[b];
+    const int k1 = min(L, p1 << 6);  // the piece's last key + 1
+    const int32_t* pt = A.table + (int64_t)b * A.max_pages;
+    const int tile0 = p0 + wave;
+    const int nt = tile0 < p1 ? (p1 - tile0 + kWaves - 1) / kWaves : 0;
     // scores through a buffer resource bounded by the piece's end: a store
     // past k1 (or of a padding step) is dropped by the bounds check, so no
-    // store sits behind a branch
+    // store sits behind a branch; candidates likewise through the wave's
+    // segment, bounded at seg_cap pairs
     const rsrc_t srow = __builtin_amdgcn_make_buffer_rsrc((void*)(A.scores + (int64_t)b * A.max_pages * 64),
                                                           (short)0, k1 * 4, 0x00020000);
+    const rsrc_t crow = __builtin_amdgcn_make_buffer_rsrc(
+        filter ? (void*)(A.cand + ((int64_t)wg * kWaves + wave) * A.seg_cap) : (void*)A.scores, (short)0,
+        filter ? A.seg_cap * 8 : 0, 0x00020000);
+    const DecodeSample ds = filter ? decode_sample(L) : DecodeSample{0, 0, 0};
     QRaw qr;
     prepare_q_load(qr, A.q, A.q_scale, A.w, b, lane);
+    // Loads are issued unconditionally, with clamped indexes: a load behind a
+    // branch makes every later wait a full drain (the memory counter retires
+    // in order and the compiler cannot count a load it may have skipped).
     int ng = min(64, nt);
-    int pg_lane = pt[tile0 + kWaves * min((int)lane, ng - 1)];
+    int pg_lane = pt[max(0, tile0 + kWaves * min((int)lane, ng - 1))];
+    // this wave's sample pages: j = wave and wave + 4 (a page id of -1, past
+    // the sampled pages, reads nothing)
+    int spg[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int sj = wave + 4 * j;
+      const int lp = (int)((2 * (int64_t)sj + 1) * ds.full / (2 * max(ds.pages, 1)));
+      const int id = pt[min(lp, max(ds.full - 1, 0))];
+      spg[j] = sj < ds.pages ? id : -1;
+    }
     // page of the group's i-th tile; past the group, -1: its loads return
     // zeros without a memory access, so the loop's last steps and the final
     // barrier do not wait out a round trip for tiles that are never used
     const auto page_of = [&](int i) { return i < ng ? __builtin_amdgcn_readlane(pg_lane, min(i, ng - 1)) : -1; };
     const auto load = [&](KeyTile& t, int i) { load_page(t, A.k, A.k_scale, A.num_pages, page_of(i), lane); };
-    KeyTile ta, tb, tc;
+    KeyTile ta, tb, tc, td;
     load(ta, 0);
     load(tb, 1);
+    // both sample pages go out with the first two tiles, before the query
+    // arithmetic
+    load_page(tc, A.k, A.k_scale, A.num_pages, spg[0], lane);
+    load_page(td, A.k, A.k_scale, A.num_pages, spg[1], lane);
     QOp qo;
     prepare_q_finish(qo, qr, lane, s_qprep[wave], 0);
+    float tau = -INFINITY;  // keeps every key
+    if (ds.pages > 0) {  // uniform over the workgroup
+      const float sc0 = tile_score(qo, tc), sc1 = tile_score(qo, td);
+      if (wave < ds.pages) s_samp[64 * wave + lane] = f2key(sc0);
+      if (wave + 4 < ds.pages) s_samp[64 * (wave + 4) + lane] = f2key(sc1);
+      __syncthreads();
+      // every wave selects the threshold itself (the same value), with no
+      // second barrier; two digits: tau is the lower edge of the r-th
+      // largest sample's 16-bit bucket, at or below that sample
+      tau = key2f(wave_cut16(s_samp, 64 * ds.pages, ds.r, lane));
+    }
     // Groups of up to 64 of the wave's tiles.  Three tile buffers in
     // rotation give two tiles of lead; the roles rotate by unrolling rather
     // than by register copies, which would wait for the loads just issued
@@ -178,6 +289,14 @@ __global__ __launch_bounds__(kWG, 2) void k_decode_score(DecodeArgs A) {
         const float sc = tile_score(qo, use);
         const int my = ((tile0 + kWaves * (g0 + i)) << 6) + (int)lane;
         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sc), srow, i < ng ? my * 4 : 0x7FFFFFF0, 0, 0);
+        if (filter) {
+          const bool take = i < ng && my < k1 && sc >= tau;
+          const uint64_t ball = __ballot(take);
+          const int off = take ? (int)((ncand + rank_in(ball)) * 8u) : 0x7FFFFFF0;
+          const v2i c = {(int)f2key(sc), my};
+          __builtin_amdgcn_raw_buffer_store_b64(c, crow, off, 0, 0);
+          ncand += (uint32_t)__popcll(ball);
+        }
       };
 #pragma unroll 1
       for (int i = 0; i < ng; i += 3) {
@@ -187,6 +306,9 @@ __global__ __launch_bounds__(kWG, 2) void k_decode_score(DecodeArgs A) {
       }
     }
   }
+  // every wave of every workgroup reports its count (zero without a piece),
+  // so that a selection never reads a count of an earlier call
+  if (filter && lane == 0) A.cnt[wg * kWaves + wave] = ncand;
 }
 
 // ------------------------------------------------------------------ host
@@ -207,7 +329,8 @@ static inline int decode_gather_split(int32_t B) {
 }
 
 struct DecodeLayout {
-  size_t ctrl, scores, gcnt, gkey, gid, total;
+  size_t ctrl, scores, gcnt, gkey, gid, cand, cnt, plan, total;
+  int32_t seg_cap;  // candidate pairs per scoring wave (balanced assignment)
 };
 
 static int decode_split_count(int32_t B, int32_t max_pages) {
@@ -220,16 +343,38 @@ static int decode_split_count(int32_t B, int32_t max_pages) {
   return g;
 }
 
+// Candidate segment of one scoring wave under the balanced assignment: a
+// piece has at most ceil(B * max_pages / (W - B)) tiles (a sequence with T
+// tiles gets more than (W - B) T / sum T workgroups), a wave a quarter of
+// them, so the segment holds every key of its tiles; capped at 2048 pairs
+// (a wave that finds more is counted and its sequence selected from the
+// score row instead).
+static int32_t decode_seg_cap(int32_t B, int32_t max_pages) {
+  const int64_t piece = ((int64_t)B * max_pages + (kDecodeWGs - B) - 1) / (kDecodeWGs - B) + 1;
+  const int64_t cap = 64 * ((piece + kWaves - 1) / kWaves);
+  return (int32_t)(cap < 2048 ? cap : 2048);
+}
+
 static DecodeLayout decode_layout(int32_t B, int32_t max_pages) {
   DecodeLayout L;
   size_t o = 0;
   const size_t b = (size_t)(B > 0 ? B : 0);
+  const bool balanced = B <= kWG;
   L.ctrl = o; o = a256(o + 4 * kCtrlWords);
   L.scores = o; o = a256(o + 4 * b * (size_t)max_pages * 64);
-  const size_t gs = (size_t)decode_gather_split(B);
-  L.gcnt = o; o = a256(o + 4 * b * gs);
-  L.gkey = o; o = a256(o + 4 * b * kDecGatherKeys);
-  L.gid = o; o = a256(o + 4 * b * kDecGatherKeys);
+  L.seg_cap = balanced ? decode_seg_cap(B, max_pages) : 0;
+  if (balanced) {  // filtered candidates
+    L.gcnt = L.gkey = L.gid = o;
+    L.cand = o; o = a256(o + 8 * (size_t)kDecodeWGs * kWaves * (size_t)L.seg_cap);
+    L.cnt = o; o = a256(o + 4 * (size_t)kDecodeWGs * kWaves);
+    L.plan = o; o = a256(o + 8 * b);
+  } else {  // pre-gather
+    const size_t gs = (size_t)decode_gather_split(B);
+    L.gcnt = o; o = a256(o + 4 * b * gs);
+    L.gkey = o; o = a256(o + 4 * b * kDecGatherKeys);
+    L.gid = o; o = a256(o + 4 * b * kDecGatherKeys);
+    L.cand = L.cnt = L.plan = o;
+  }
   L.total = o;
   return L;
 }
@@ -270,6 +415,12 @@ int decode_paged(const uint8_t* q, const float* q_scale, const uint8_t* k_cache,
   A.W = A.balanced ? kDecodeWGs : A.G * B;
   A.ctrl = reinterpret_cast<uint32_t*>(ws + L.ctrl);
   A.scores = reinterpret_cast<float*>(ws + L.scores);
+  if (A.balanced) {  // the scoring kernel filters; the selection reads its candidates
+    A.cand = reinterpret_cast<uint2*>(ws + L.cand);
+    A.cnt = reinterpret_cast<uint32_t*>(ws + L.cnt);
+    A.plan = reinterpret_cast<uint2*>(ws + L.plan);
+    A.seg_cap = L.seg_cap;
+  }
   hipEvent_t ev0 = opts ? static_cast<hipEvent_t>(opts->ev_main_start) : nullptr;
   hipEvent_t ev1 = opts ? static_cast<hipEvent_t>(opts->ev_main_stop) : nullptr;
   // the timing events, when given, are recorded by the launches themselves
@@ -285,10 +436,22 @@ int decode_paged(const uint8_t* q, const float* q_scale, const uint8_t* k_cache,
   if (hipGetLastError() != hipSuccess) return IDX_EHIP;
   RowsArgs R{A.scores, (int64_t)max_pages * 64, nullptr, seq_lens, B, max_pages * 64, K, out_idx, A.ctrl,
              page_table, max_pages, num_pages,
-             reinterpret_cast<uint32_t*>(ws + L.gkey), reinterpret_cast<int32_t*>(ws + L.gid),
-             reinterpret_cast<uint32_t*>(ws + L.gcnt), kDecGatherKeys / decode_gather_split(B),
-             decode_gather_split(B)};
-  int rc = launch_topk_rows_gathered(R, stream);
+             nullptr, nullptr, nullptr, 0, 0, nullptr, nullptr, nullptr, 0};
+  int rc;
+  if (A.balanced) {
+    R.dcand = A.cand;
+    R.dcnt = A.cnt;
+    R.dplan = A.plan;
+    R.dseg = A.seg_cap;
+    rc = launch_topk_rows_filtered(R, stream);
+  } else {
+    R.gkey = reinterpret_cast<uint32_t*>(ws + L.gkey);
+    R.gid = reinterpret_cast<int32_t*>(ws + L.gid);
+    R.gcnt = reinterpret_cast<uint32_t*>(ws + L.gcnt);
+    R.gsplit = decode_gather_split(B);
+    R.gcap = kDecGatherKeys / R.gsplit;
+    rc = launch_topk_rows_gathered(R, stream);
+  }
   // the debug path hands out the score rows the selection read
   if (rc == IDX_OK && scores_out &&
       hipMemcpyAsync(scores_out, A.scores, sizeof(float) * (size_t)B * (size_t)max_pages * 64,

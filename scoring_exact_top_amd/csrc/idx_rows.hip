@@ -36,6 +36,7 @@ constexpr int kRowsShift = 21;  // 32 - 11 bits
 constexpr int kRowsCap = 6144;  // gathered keys held in LDS
 constexpr int kSampleKeys = 4096;  // sample: kSampleKeys / NT blocks of NT scores
 constexpr int kSampleMinLen = kSampleKeys;  // shorter rows (< kRowsCap keys) are gathered whole
+constexpr int kDecodeRegs = 8;  // register slots per thread for a decode row's filtered candidates
 // Per workgroup size (NW waves, NT threads): register slots of the
 // gathered list, each wave's private gather segment, sample blocks.
 template <int NW>
@@ -351,6 +352,10 @@ __global__ __launch_bounds__(64 * NW, Rows::kMinBlocks) void k_topk_rows(RowsArg
     }
     gc = A.gcnt[(int64_t)t * G + g];
   }
+  // the scoring kernel's plan for this row (filtered decode candidates),
+  // loaded beside the range check; only used for a row it scored
+  uint2 dpl = make_uint2(0u, 0u);
+  if (A.dcnt) dpl = A.dplan[t];
   int s0, s1;
   if (!R.template range<NW>(t, s0, s1, tid)) {
     for (int i = tid; i < A.K; i += NT) out[i] = -1;
@@ -397,6 +402,70 @@ __global__ __launch_bounds__(64 * NW, Rows::kMinBlocks) void k_topk_rows(RowsArg
       if (stats && tid == 0) atomicAdd(&stats[kStFast], 1u);
       return;
     }
+  }
+
+  // candidates filtered by the scoring kernel: all of the row's keys at or
+  // above its threshold, in the four wave segments of each of the row's
+  // dpl.y workgroups.  The segments' counts are scanned into offsets of one
+  // list (in LDS), whose element x thread slot j of thread x mod NT holds
+  // (x = tid + j*NT); the segment of x is found by a binary search over the
+  // offsets.  Exact when every segment kept all its candidates, they fit the
+  // slots and there are at least K of them (every other key scores below
+  // the threshold); otherwise the row takes the passes below.
+  if (A.dcnt) {
+    constexpr int DR = kDecodeRegs;
+    const int nseg = 4 * (int)dpl.y;  // at most 2048 (512 workgroups)
+    const int64_t seg0 = (int64_t)dpl.x * kWaves;
+    uint32_t ca = 0u, cb = 0u;  // segments tid and tid + NT
+    if (tid < nseg) ca = A.dcnt[seg0 + tid];
+    if (tid + NT < nseg) cb = A.dcnt[seg0 + tid + NT];
+    const bool over = ca > (uint32_t)A.dseg || cb > (uint32_t)A.dseg;
+    uint32_t n = 0u;
+    const uint32_t pa = block_exclusive_scan<NW>(ca, S.sh, tid, n);  // offsets of the first NT segments
+    uint32_t nb = 0u;
+    const uint32_t pb = n + block_exclusive_scan<NW>(cb, S.sh, tid, nb);
+    n += nb;
+    uint32_t* const off = S.lkey;  // nseg + 1 offsets (the LDS list area is unused on this path)
+    if (tid < nseg) off[tid] = pa;
+    if (tid + NT < nseg) off[tid + NT] = pb;
+    if (tid == 0) off[nseg] = n;
+    const bool dropped = __syncthreads_or(over) || n > (uint32_t)(NT * DR);
+    if (nseg >= 1 && !dropped && n >= (uint32_t)K) {
+      const RegLayout lay = block_list_layout<NW>(n, (uint32_t)tid);
+      uint32_t sg[DR], lo[DR];  // per slot: search window [lo, lo + span)
+#pragma unroll
+      for (int j = 0; j < DR; ++j) lo[j] = 0u;
+      for (int span = nseg; span > 1;) {  // largest segment s with off[s] <= x
+        const int half = span >> 1;
+#pragma unroll
+        for (int j = 0; j < DR; ++j) {
+          const uint32_t mid = lo[j] + (uint32_t)half;
+          lo[j] = off[mid] <= lay.at(j) ? mid : lo[j];
+        }
+        span -= half;
+      }
+      uint32_t key[DR];
+      int32_t id[DR];
+#pragma unroll
+      for (int j = 0; j < DR; ++j) {
+        const bool ok = lay.valid(j);
+        sg[j] = lo[j];
+        const uint2 pr = ok ? A.dcand[(seg0 + sg[j]) * A.dseg + (lay.at(j) - off[sg[j]])] : make_uint2(0u, 0u);
+        key[j] = pr.x;
+        id[j] = (int32_t)pr.y;
+      }
+      const auto kf = [&](int j) { return key[j]; };
+      const RangeSel sel = (n > (uint32_t)K) ? range_select_regs<DR, NW>(kf, lay, K, S.sh, tid)
+                                              : RangeSel{1u, 0xFFFFFFFFu, K, (int)n};
+      const uint32_t idlo = tie_bound_regs<NW>(key, id, lay, sel, S.sh, tid);
+      emit_range_regs<NW>(key, id, lay, sel, idlo, K, K, out, ids, S.sh, tid);
+      if (stats && tid == 0) atomicAdd(&stats[kStFast], 1u);
+      return;
+    }
+    // the candidates do not settle the row: counted as an overflow (some
+    // were dropped) or an underflow (fewer than K), then the passes below
+    if (stats && tid == 0) atomicAdd(&stats[dropped ? kStOver : kStUnder], 1u);
+    __syncthreads();  // the offsets' LDS is the passes' list area
   }
 
   // step 0: the sampled cut (key 0 keeps every key)
@@ -613,6 +682,13 @@ int launch_topk_rows_gathered(const RowsArgs& A, hipStream_t stream) {
     hipLaunchKernelGGL(k_rows_gather<DenseRows>, dim3(A.gsplit, A.Q), dim3(kWG), 0, stream, A);
     hipLaunchKernelGGL((k_topk_rows<DenseRows, kWaves>), dim3(A.Q), dim3(kWG), 0, stream, A);
   }
+  return hipGetLastError() == hipSuccess ? IDX_OK : IDX_EHIP;
+}
+
+int launch_topk_rows_filtered(const RowsArgs& A, hipStream_t stream) {
+  if (A.Q == 0) return IDX_OK;
+  if (!A.table || !A.dcnt || !A.dcand || !A.dplan || A.dseg < 1 || A.gcnt) return IDX_EINVAL;
+  hipLaunchKernelGGL((k_topk_rows<PagedRows, kMaxWaves>), dim3(A.Q), dim3(64 * kMaxWaves), 0, stream, A);
   return hipGetLastError() == hipSuccess ? IDX_OK : IDX_EHIP;
 }
 

@@ -29,6 +29,16 @@ struct RowsArgs {
   int32_t* gid;    // [Q][gsplit][gcap] logical positions
   uint32_t* gcnt;  // [Q][gsplit]
   int32_t gcap, gsplit;
+  // Optional candidates filtered by the paged decode's scoring kernel
+  // (instead of the pre-gather): sequence t's workgroups are
+  // dplan[t].x .. dplan[t].x + dplan[t].y - 1; wave v of workgroup g stored
+  // dcnt[4g + v] (order-preserving key, logical position) pairs, the first
+  // dseg of them at dcand[(4g + v) * dseg]; they are the keys of the
+  // sequence at or above one threshold.
+  const uint2* dcand;
+  const uint32_t* dcnt;
+  const uint2* dplan;
+  int32_t dseg;
 };
 
 constexpr int kMaxGatherSplit = 32;
@@ -36,6 +46,10 @@ constexpr int kMaxGatherSplit = 32;
 // Launch the pre-gather and the per-row select (paged rows when table is
 // set, dense rows otherwise; gkey must be set).
 int launch_topk_rows_gathered(const RowsArgs& A, hipStream_t stream);
+
+// The per-sequence select of the paged decode over the candidates its
+// scoring kernel filtered (dcnt, dcand, dplan set; no pre-gather).
+int launch_topk_rows_filtered(const RowsArgs& A, hipStream_t stream);
 
 // The per-row select alone, for dense rows (table must be null).
 int launch_topk_rows(const RowsArgs& A, hipStream_t stream);

@@ -177,3 +177,43 @@ def test_decode_large_batch_fixed_assignment():
                            case.page_size, case.K)
     _check(sub, out[keep])
     assert st["bad_rows"] == 2
+
+
+def _sampled_pages(L):
+    """Logical pages whose keys give a scored sequence of L keys its
+    threshold (the sampling geometry documented with the decode scoring
+    kernel: about one key in 200, as whole pages at a fixed stride over the
+    full pages, at most 8; none up to 4096 keys).  Test construction only."""
+    if L <= 4096:
+        return []
+    ns = -(-(L - 100) // 200)
+    P = min(8, max(1, -(-ns // 64)))
+    F = L // 64
+    return [(2 * j + 1) * F // (2 * P) for j in range(P)]
+
+
+def test_decode_boosted_sample_pages_force_underflow():
+    """The keys of every sampled page scaled by 8: each sequence's threshold
+    lands above nearly all its other keys, so fewer than K candidates pass
+    it (underflow) and the selection falls back to the score row; exact."""
+    lens = [9000, 30000, 65536]
+    case = synth.decode_case("dec_decoy", lens, seed=38, max_pages=1024)
+    for b, L in enumerate(lens):
+        for lp in _sampled_pages(L):
+            case.k_scale[case.page_table[b, lp]] *= 8.0
+    log("case", case.name, lens, [len(_sampled_pages(L)) for L in lens], "sampled pages")
+    out, st = _run(case)
+    log("stats", st)
+    assert st["underflow"] == len(lens) and st["fast_ok"] + st["repaired"] == len(lens)
+    _check(case, out)
+
+
+def test_decode_filtered_candidates_on_the_workload():
+    """The benchmarked batch: every scored sequence is settled by the
+    candidates its scoring kernel filtered (no fallback), and exact."""
+    case = synth.paged_decode(0)
+    out, st = _run(case)
+    log("stats", st)
+    scored = int(np.sum(case.seq_lens > case.K))
+    assert st["fast_ok"] == scored and st["underflow"] == 0 and st["overflow"] == 0
+    _check(case, out)
