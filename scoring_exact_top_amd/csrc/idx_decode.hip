@@ -50,11 +50,11 @@ struct DecodeArgs {
   uint32_t* ctrl;
   float* scores;         // [B][max_pages*64] scores at logical positions
   // filtered candidates (balanced assignment only; null otherwise): wave v
-  // of workgroup g stores (order-preserving key, logical position) pairs of
-  // its keys at or above the sequence's sampled threshold into
-  // cand[(4g + v) * seg_cap ...] and their number (stored or not) into
-  // cnt[4g + v]; the first workgroup of sequence b records plan[b] = (its
-  // index, the sequence's workgroup count)
+  // of workgroup g, the i-th of sequence b's, stores (order-preserving key,
+  // logical position) pairs of its keys at or above the sequence's sampled
+  // threshold into cand[(4g + v) * seg_cap ...] and their number (stored or
+  // not) into cnt[b * kDecodeCntStride + 4i + v]; the first workgroup of
+  // sequence b records plan[b] = (g, the sequence's workgroup count)
   uint2* cand;
   uint32_t* cnt;
   uint2* plan;
@@ -171,6 +171,7 @@ __global__ __launch_bounds__(kWG, 2) void k_decode_score(DecodeArgs A) {
   const int wg = blockIdx.x;
   if (wg == 0) clear_ctrl(A.ctrl, tid);  // first kernel of the call
   int b = 0, p0 = 0, p1 = 0;              // this workgroup's piece: tiles [p0, p1) of sequence b
+  int gi = -1;                            // its index among the sequence's workgroups (balanced)
   if (A.balanced) {
     int T = 0;
     if (tid < A.B) {
@@ -195,6 +196,7 @@ __global__ __launch_bounds__(kWG, 2) void k_decode_score(DecodeArgs A) {
       const int64_t g = sh.above, Gb = sh.inbucket, Tb = sh.pad0;
       p0 = (int)(Tb * g / Gb);
       p1 = (int)(Tb * (g + 1) / Gb);
+      gi = (int)g;
       if (g == 0 && tid == 0 && A.plan) A.plan[b] = make_uint2((uint32_t)wg, (uint32_t)Gb);
     }
   } else {
@@ -306,9 +308,9 @@ __global__ __launch_bounds__(kWG, 2) void k_decode_score(DecodeArgs A) {
       }
     }
   }
-  // every wave of every workgroup reports its count (zero without a piece),
-  // so that a selection never reads a count of an earlier call
-  if (filter && lane == 0) A.cnt[wg * kWaves + wave] = ncand;
+  // every wave of a sequence's workgroups reports its count (zero for an
+  // empty piece), so that a selection never reads a count of an earlier call
+  if (filter && gi >= 0 && lane == 0) A.cnt[(int64_t)b * kDecodeCntStride + gi * kWaves + wave] = ncand;
 }
 
 // ------------------------------------------------------------------ host
@@ -366,7 +368,7 @@ static DecodeLayout decode_layout(int32_t B, int32_t max_pages) {
   if (balanced) {  // filtered candidates
     L.gcnt = L.gkey = L.gid = o;
     L.cand = o; o = a256(o + 8 * (size_t)kDecodeWGs * kWaves * (size_t)L.seg_cap);
-    L.cnt = o; o = a256(o + 4 * (size_t)kDecodeWGs * kWaves);
+    L.cnt = o; o = a256(o + 4 * b * (size_t)kDecodeCntStride);
     L.plan = o; o = a256(o + 8 * b);
   } else {  // pre-gather
     const size_t gs = (size_t)decode_gather_split(B);

@@ -355,7 +355,13 @@ __global__ __launch_bounds__(64 * NW, Rows::kMinBlocks) void k_topk_rows(RowsArg
   // the scoring kernel's plan for this row (filtered decode candidates),
   // loaded beside the range check; only used for a row it scored
   uint2 dpl = make_uint2(0u, 0u);
-  if (A.dcnt) dpl = A.dplan[t];
+  uint32_t dca = 0u, dcb = 0u;  // counts of segments tid and tid + NT (valid below 4 dpl.y)
+  if (A.dcnt) {
+    dpl = A.dplan[t];
+    const uint32_t* cn = A.dcnt + (int64_t)t * kDecodeCntStride;
+    dca = cn[tid];
+    dcb = cn[min(tid + NT, kDecodeCntStride - 1)];
+  }
   int s0, s1;
   if (!R.template range<NW>(t, s0, s1, tid)) {
     for (int i = tid; i < A.K; i += NT) out[i] = -1;
@@ -416,9 +422,7 @@ __global__ __launch_bounds__(64 * NW, Rows::kMinBlocks) void k_topk_rows(RowsArg
     constexpr int DR = kDecodeRegs;
     const int nseg = 4 * (int)dpl.y;  // at most 2048 (512 workgroups)
     const int64_t seg0 = (int64_t)dpl.x * kWaves;
-    uint32_t ca = 0u, cb = 0u;  // segments tid and tid + NT
-    if (tid < nseg) ca = A.dcnt[seg0 + tid];
-    if (tid + NT < nseg) cb = A.dcnt[seg0 + tid + NT];
+    const uint32_t ca = tid < nseg ? dca : 0u, cb = tid + NT < nseg ? dcb : 0u;
     const bool over = ca > (uint32_t)A.dseg || cb > (uint32_t)A.dseg;
     uint32_t n = 0u;
     const uint32_t pa = block_exclusive_scan<NW>(ca, S.sh, tid, n);  // offsets of the first NT segments

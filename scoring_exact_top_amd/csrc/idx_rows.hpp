@@ -31,10 +31,10 @@ struct RowsArgs {
   int32_t gcap, gsplit;
   // Optional candidates filtered by the paged decode's scoring kernel
   // (instead of the pre-gather): sequence t's workgroups are
-  // dplan[t].x .. dplan[t].x + dplan[t].y - 1; wave v of workgroup g stored
-  // dcnt[4g + v] (order-preserving key, logical position) pairs, the first
-  // dseg of them at dcand[(4g + v) * dseg]; they are the keys of the
-  // sequence at or above one threshold.
+  // g = dplan[t].x + i for i < dplan[t].y; wave v of workgroup g stored
+  // dcnt[t * kDecodeCntStride + 4i + v] (order-preserving key, logical
+  // position) pairs, the first dseg of them at dcand[(4g + v) * dseg]; they
+  // are the keys of the sequence at or above one threshold.
   const uint2* dcand;
   const uint32_t* dcnt;
   const uint2* dplan;
@@ -42,6 +42,9 @@ struct RowsArgs {
 };
 
 constexpr int kMaxGatherSplit = 32;
+// Count slots per decode sequence: four waves for each of at most 512
+// scoring workgroups.
+constexpr int kDecodeCntStride = 2048;
 
 // Launch the pre-gather and the per-row select (paged rows when table is
 // set, dense rows otherwise; gkey must be set).
