@@ -282,7 +282,15 @@ size_t idx_topk_decode_workspace(int32_t B, int32_t max_pages, int32_t page_size
  *              A sequence whose length is out of range or whose used page
  *              ids are outside [0, num_pages) gets all -1 (bad_rows count).
  * The keys are scored into a [B][max_pages*page_size] FP32 row per sequence in
- * the workspace, then each row is selected exactly (no threshold, no repair).
+ * the workspace.  For batches of up to 256 sequences the scoring kernel also
+ * takes each sequence's sampled threshold (sequences longer than 4096 keys:
+ * up to 8 whole pages at a fixed stride, "3.2 Sampled threshold" of the
+ * Fusing Indexer Scoring and Exact Top-k page) and keeps the keys at or
+ * above it as candidates; the selection is exact either way: from the
+ * candidates when there are at least K of them and none was dropped
+ * (counted as fast_ok), else from the score row (counted as underflow or
+ * overflow, then fast_ok or repaired).  Larger batches select from the score
+ * rows.  No host synchronisation; nothing is copied to the host.
  */
 int idx_topk_decode_paged(const uint8_t *q, const float *q_scale, const uint8_t *k_cache,
                           const float *k_scale, const float *w, const int32_t *page_table,
@@ -300,8 +308,9 @@ int idx_topk_decode_paged(const uint8_t *q, const float *q_scale, const uint8_t 
  *   opts       NULL or timing only: ev_main_start/ev_main_stop are recorded by
  *              the launch of the split scoring kernel at its start and at its
  *              end, main_reps repeats it.  The decode path has no threshold
- *              and no capacity knobs: opts with force_tau, cand_cap,
- *              row_status, clock_out or math_only set gives IDX_EINVAL.
+ *              or capacity knobs (its threshold is always sampled): opts
+ *              with force_tau, cand_cap, row_status, clock_out or math_only
+ *              set gives IDX_EINVAL.
  */
 int idx_topk_decode_paged_debug(const uint8_t *q, const float *q_scale, const uint8_t *k_cache,
                                 const float *k_scale, const float *w, const int32_t *page_table,

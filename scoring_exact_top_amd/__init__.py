@@ -369,7 +369,7 @@ def decode_paged(q8, q_scale, k_cache, k_scale, w, page_table, seq_lens, K: int,
     torch.cuda.Event pair around the scoring kernel; scores_out
     [B, max_pages*64] f32 (debug entry too) receives the scores the
     selection read; force_tau is passed through so that the library's
-    rejection of it (decode has no threshold) can be tested.
+    rejection of it (decode has no threshold knob) can be tested.
     """
     q8, k_cache = _q_k(q8, k_cache)
     B = int(q8.shape[0])

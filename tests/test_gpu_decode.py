@@ -79,7 +79,8 @@ def test_decode_row_paths():
 
 
 def test_decode_rejects_a_threshold():
-    """Decode has no threshold: the debug knob is refused, not ignored."""
+    """Decode samples its threshold itself: the debug knob that forces one
+    is refused, not ignored."""
     import scoring_exact_top_amd as lib
     case = synth.decode_case("dec_tau", [3000], seed=34, max_pages=100)
     with pytest.raises(lib.IdxTopkError):
