@@ -270,8 +270,8 @@ struct DenseRows {
 
 // Sequences of the paged decode: row b holds the scores of logical positions
 // [0, seq_lens[b]) at scores + b*ld; it is invalid when its length is out of
-// range or a workgroup of the scoring kernel flagged a bad page id; ids are
-// physical cache slots.
+// range or one of the page ids it uses is outside [0, num_pages) (checked
+// here, by the selection); ids are physical cache slots.
 struct PagedRows {
   // few long rows: one workgroup must cover the latency alone (four times
   // fewer loads per step with four times the threads)
@@ -314,9 +314,9 @@ struct PagedRows {
 // allows three) keep enough loads in flight.  Paged decode rows are few and
 // long: one workgroup per row with no occupancy bound, so that the register
 // select does not spill, and 1024 threads (NW = 16), whose shorter per-thread
-// chains select a sequence's pre-gathered keys faster (13 against 15 us for
-// 16 sequences); reading and selecting a whole sequence in that one
-// workgroup instead of pre-gathering it over 32 took 30 us.
+// chains select a sequence's candidates faster (13 against 15 us for 16
+// sequences' pre-gathered keys); reading and selecting a whole sequence in
+// that one workgroup took 30 us.
 template <class Rows, int NW>
 __global__ __launch_bounds__(64 * NW, Rows::kMinBlocks) void k_topk_rows(RowsArgs A) {
   constexpr int NT = 64 * NW;
@@ -568,7 +568,8 @@ __global__ __launch_bounds__(64 * NW, Rows::kMinBlocks) void k_topk_rows(RowsArg
   }
 }
 
-// Pre-gather of long rows (paged decode sequences, scan streams): workgroup
+// Pre-gather of long rows (scan streams; paged decode sequences of batches
+// beyond 256, whose scoring kernel does not filter): workgroup
 // (g, t) computes row t's sampled cut (as the per-row kernel would) and
 // stores the keys >= cut of slice g of the row into its own region of the
 // workspace; each thread counts its keys, one workgroup scan gives the
@@ -698,7 +699,7 @@ int launch_topk_rows_filtered(const RowsArgs& A, hipStream_t stream) {
 
 int launch_topk_rows(const RowsArgs& A, hipStream_t stream) {
   if (A.Q == 0) return IDX_OK;
-  if (A.table) return IDX_EINVAL;  // paged rows go through the pre-gather
+  if (A.table) return IDX_EINVAL;  // paged rows go through the filtered or pre-gathered launches
   hipLaunchKernelGGL((k_topk_rows<DenseRows, kWaves>), dim3(A.Q), dim3(kWG), 0, stream, A);
   return hipGetLastError() == hipSuccess ? IDX_OK : IDX_EHIP;
 }
