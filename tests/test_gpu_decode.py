@@ -218,3 +218,19 @@ def test_decode_filtered_candidates_on_the_workload():
     scored = int(np.sum(case.seq_lens > case.K))
     assert st["fast_ok"] == scored and st["underflow"] == 0 and st["overflow"] == 0
     _check(case, out)
+
+
+def test_decode_damped_sample_pages_force_overflow():
+    """The keys of every sampled page scaled by 1/8: each sequence's
+    threshold lands far below its K-th score, so about half its keys pass it,
+    more than the selection holds in registers (counted as overflow), and
+    the selection falls back to the score row; exact."""
+    lens = [30000, 65536]
+    case = synth.decode_case("dec_damped", lens, seed=39, max_pages=1024)
+    for b, L in enumerate(lens):
+        for lp in _sampled_pages(L):
+            case.k_scale[case.page_table[b, lp]] *= 0.125
+    out, st = _run(case)
+    log("stats", st)
+    assert st["overflow"] == len(lens) and st["fast_ok"] + st["repaired"] == len(lens)
+    _check(case, out)
