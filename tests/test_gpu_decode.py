@@ -234,3 +234,21 @@ def test_decode_damped_sample_pages_force_overflow():
     log("stats", st)
     assert st["overflow"] == len(lens) and st["fast_ok"] + st["repaired"] == len(lens)
     _check(case, out)
+
+
+def test_decode_largest_filtered_batch():
+    """256 sequences, the largest batch whose scoring kernel samples and
+    filters (one fewer would change nothing, one more takes the pre-gather):
+    ragged lengths around K, around the keep-every-key bound (4096) and up to
+    20000, with the balanced plan giving some sequences one or two scoring
+    workgroups; every sequence exact."""
+    g = np.random.default_rng(49)
+    lens = g.integers(1, 20000, size=256).astype(np.int32)
+    lens[:8] = [2048, 2049, 4095, 4096, 4097, 4160, 1, 0]
+    case = synth.decode_case("dec_b256", lens, seed=49, max_pages=320)
+    log("case", case.name, "B", case.B)
+    out, st = _run(case)
+    log("stats", st)
+    scored = int(np.sum(case.seq_lens > case.K))
+    assert st["rows"] == case.B and st["fast_ok"] + st["repaired"] == scored
+    _check(case, out)
