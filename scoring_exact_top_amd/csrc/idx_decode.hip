@@ -348,14 +348,19 @@ static int decode_split_count(int32_t B, int32_t max_pages) {
 // Candidate segment of one scoring wave under the balanced assignment: a
 // piece has at most ceil(B * max_pages / (W - B)) tiles (a sequence with T
 // tiles gets more than (W - B) T / sum T workgroups), a wave a quarter of
-// them, so the segment holds every key of its tiles, up to 512 pairs (a
-// wave expects about 2K / (4 G) candidates of a sequence with G workgroups;
-// one that finds more than its segment holds is counted, and its sequence
-// is selected from the score row instead).
+// them, so the segment holds every key of its tiles, up to 8 B pairs kept
+// within [512, 2048].  A wave expects about 2K / (4 G) candidates of a
+// sequence with G workgroups, G being W / B on average, so 2 B per wave,
+// and a sequence short enough to keep every key (4096) on one workgroup
+// brings at most 1024 per wave; a wave that finds more than its segment
+// holds is counted, and its sequence is selected from the score row
+// instead.
 static int32_t decode_seg_cap(int32_t B, int32_t max_pages) {
   const int64_t piece = ((int64_t)B * max_pages + (kDecodeWGs - B) - 1) / (kDecodeWGs - B) + 1;
   const int64_t cap = 64 * ((piece + kWaves - 1) / kWaves);
-  return (int32_t)(cap < 512 ? cap : 512);
+  const int64_t lim = 64 * ((8 * (int64_t)B + 63) / 64);
+  const int64_t top = lim < 512 ? 512 : (lim > 2048 ? 2048 : lim);
+  return (int32_t)(cap < top ? cap : top);
 }
 
 static DecodeLayout decode_layout(int32_t B, int32_t max_pages) {
