@@ -551,6 +551,61 @@ struct SelResult {
   int rem, group;
 };
 
+// ------------------------------------------------- wave-wide DPP primitives
+
+// Lane-to-lane moves inside the VALU (DPP) instead of LDS permutes: each
+// step of a wave scan or reduction costs one VALU operation rather than an
+// LDS round trip.  Every lane of the wave must be active.
+namespace dpp {
+constexpr int kRowShr1 = 0x111, kRowShr2 = 0x112, kRowShr4 = 0x114, kRowShr8 = 0x118;
+constexpr int kRowBcast15 = 0x142, kRowBcast31 = 0x143;  // GFX9 row broadcasts
+constexpr int kQuadXor1 = 0xB1, kQuadXor2 = 0x4E;      // quad_perm [1,0,3,2], [2,3,0,1]
+constexpr int kRowHalfMirror = 0x141, kRowMirror = 0x140;
+// lane value moved by `ctrl`; lanes whose source lies outside the row (or
+// whose row is masked off) get `fill`
+template <int ctrl, int row_mask = 0xf>
+__device__ __forceinline__ uint32_t mov(uint32_t fill, uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)fill, (int)v, ctrl, row_mask, 0xf, false);
+}
+}  // namespace dpp
+
+// Inclusive prefix sum over the wave's 64 lanes in lane order: a scan
+// within each row of 16 lanes by shifts of 1, 2, 4 and 8, then the row
+// totals carried by broadcasting lane 15 into rows 1 and 3 and lane 31
+// into rows 2 and 3.
+__device__ __forceinline__ uint32_t wave_inclusive_sum(uint32_t x) {
+  x += dpp::mov<dpp::kRowShr1>(0u, x);
+  x += dpp::mov<dpp::kRowShr2>(0u, x);
+  x += dpp::mov<dpp::kRowShr4>(0u, x);
+  x += dpp::mov<dpp::kRowShr8>(0u, x);
+  x += dpp::mov<dpp::kRowBcast15, 0xa>(0u, x);
+  x += dpp::mov<dpp::kRowBcast31, 0xc>(0u, x);
+  return x;
+}
+
+// Reduction over the wave's 64 lanes, returned wave-uniform: within each
+// row of 16 by two quad exchanges and the half-row and row mirrors, then
+// the four row results read on the scalar unit.
+template <class Op>
+__device__ __forceinline__ uint32_t wave_reduce(uint32_t x, const Op& op) {
+  x = op(x, dpp::mov<dpp::kQuadXor1>(x, x));
+  x = op(x, dpp::mov<dpp::kQuadXor2>(x, x));
+  x = op(x, dpp::mov<dpp::kRowHalfMirror>(x, x));
+  x = op(x, dpp::mov<dpp::kRowMirror>(x, x));
+  const uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)x, 0), b = (uint32_t)__builtin_amdgcn_readlane((int)x, 16);
+  const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)x, 32), d = (uint32_t)__builtin_amdgcn_readlane((int)x, 48);
+  return op(op(a, b), op(c, d));
+}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t x) {
+  return wave_reduce(x, [](uint32_t p, uint32_t q) { return p < q ? p : q; });
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
+  return wave_reduce(x, [](uint32_t p, uint32_t q) { return p > q ? p : q; });
+}
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t x) {
+  return wave_reduce(x, [](uint32_t p, uint32_t q) { return p + q; });
+}
+
 // From a complete 256-bin histogram in sh.hist, find the bucket that holds
 // the rem-th largest element (wave 0 scans, result broadcast through LDS).
 __device__ __forceinline__ void find_bucket(SelShared& sh, int rem, int tid) {
@@ -559,13 +614,9 @@ __device__ __forceinline__ void find_bucket(SelShared& sh, int rem, int tid) {
     const uint32_t h0 = sh.hist[4 * lane + 0], h1 = sh.hist[4 * lane + 1];
     const uint32_t h2 = sh.hist[4 * lane + 2], h3 = sh.hist[4 * lane + 3];
     const uint32_t s = h0 + h1 + h2 + h3;
-    uint32_t suf = s;  // inclusive suffix sum over lanes >= lane
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const uint32_t o = __shfl_down(suf, off, 64);
-      if (lane + off < 64) suf += o;
-    }
-    const uint32_t above_lane = suf - s;
+    const uint32_t inc = wave_inclusive_sum(s);
+    const uint32_t above_lane = (uint32_t)__builtin_amdgcn_readlane((int)inc, 63) - inc;  // lanes above this one
+    const uint32_t suf = above_lane + s;
     const uint32_t r = (uint32_t)rem;
     if (above_lane < r && r <= suf) {
       uint32_t acc = above_lane;
@@ -589,13 +640,9 @@ __device__ __forceinline__ void wave_find_bucket(const uint32_t* hist, int rem, 
   const uint32_t h0 = hist[4 * lane + 0], h1 = hist[4 * lane + 1];
   const uint32_t h2 = hist[4 * lane + 2], h3 = hist[4 * lane + 3];
   const uint32_t s = h0 + h1 + h2 + h3;
-  uint32_t suf = s;  // inclusive suffix sum over lanes >= lane
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint32_t o = __shfl_down(suf, off, 64);
-    if (lane + off < 64) suf += o;
-  }
-  const uint32_t above_lane = suf - s;
+  const uint32_t inc = wave_inclusive_sum(s);
+  const uint32_t above_lane = (uint32_t)__builtin_amdgcn_readlane((int)inc, 63) - inc;  // lanes above this one
+  const uint32_t suf = above_lane + s;
   const uint32_t r = (uint32_t)rem;
   const bool owner = above_lane < r && r <= suf;
   uint32_t acc = above_lane, b = 4 * lane, hb = h0;
@@ -653,12 +700,7 @@ template <int NW = kWaves>
 __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t a, SelShared& sh, int tid, uint32_t& total) {
   const uint32_t lane = tid & 63;
   const int wave = tid >> 6;
-  uint32_t inc = a;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint32_t x = (uint32_t)__shfl_up((int)inc, off, 64);
-    if (lane >= (uint32_t)off) inc += x;
-  }
+  const uint32_t inc = wave_inclusive_sum(a);
   if (lane == 63) sh.wsum[0][wave] = inc;
   __syncthreads();
   uint32_t before = 0u;
@@ -805,14 +847,9 @@ __device__ __forceinline__ RangeSel range_select_regs(const KF& kf, const RegLay
       }
     }
   }
-  mn = min(mn, mn2);
-  mx = max(mx, mx2);
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    mn = min(mn, (uint32_t)__shfl_xor((int)mn, off, 64));
-    mx = max(mx, (uint32_t)__shfl_xor((int)mx, off, 64));
-    cnt += (uint32_t)__shfl_xor((int)cnt, off, 64);
-  }
+  mn = wave_min_u32(min(mn, mn2));
+  mx = wave_max_u32(max(mx, mx2));
+  cnt = wave_sum_u32(cnt);
   if (lane == 0) { sh.wsum[0][wave] = mn; sh.wsum[1][wave] = mx; sh.wsum[2][wave] = cnt; }
   __syncthreads();
   cnt = 0u;
@@ -875,8 +912,7 @@ __device__ __forceinline__ uint32_t range_min_regs(const KF& kf, const RegLayout
 #pragma unroll
   for (int j = 0; j < M; ++j)
     if ((uint32_t)j < lay.jmax && kf(j) - sel.lo <= width) mn = min(mn, kf(j));
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) mn = min(mn, (uint32_t)__shfl_xor((int)mn, off, 64));
+  mn = wave_min_u32(mn);
   if (lane == 0) sh.wsum[0][wave] = mn;
   __syncthreads();
 #pragma unroll

@@ -631,11 +631,8 @@ __global__ __launch_bounds__(64 * NW) void k_prefill_select(PrefillArgs A) {
   }
   // largest dropped key and first dropped position over the segments (all
   // in wave 0: nseg <= 32)
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    dk = max(dk, (uint32_t)__shfl_xor((int)dk, o, 64));
-    fd = min(fd, (uint32_t)__shfl_xor((int)fd, o, 64));
-  }
+  dk = wave_max_u32(dk);
+  fd = wave_min_u32(fd);
   if (tid == 0) { sh.pad0 = dk; sh.pad1 = fd; }
   __syncthreads();
   const uint32_t drop = sh.pad0, first_drop = sh.pad1;
@@ -676,8 +673,7 @@ __global__ __launch_bounds__(64 * NW) void k_prefill_select(PrefillArgs A) {
         uint32_t mn = 0xFFFFFFFFu;  // smallest ~id taken at theta = ~(largest id)
 #pragma unroll
         for (int j = 0; j < M; ++j) mn = min(mn, tk(j));
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) mn = min(mn, (uint32_t)__shfl_xor((int)mn, o, 64));
+        mn = wave_min_u32(mn);
         if (lane == 0) sh.wsum[0][tid >> 6] = mn;
         __syncthreads();
 #pragma unroll

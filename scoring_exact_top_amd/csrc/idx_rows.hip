@@ -132,12 +132,7 @@ __device__ __forceinline__ uint32_t gather_ge(const float* row, int L, int tid, 
 #pragma unroll
       for (int e = 0; e < 4; ++e) cnt += take(i0 + e, cur[u][e]) ? 1u : 0u;
     }
-    uint32_t inc = cnt;  // inclusive scan over the wave's lanes
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const uint32_t x = (uint32_t)__shfl_up((int)inc, off, 64);
-      if (lane >= (uint32_t)off) inc += x;
-    }
+    const uint32_t inc = wave_inclusive_sum(cnt);  // inclusive scan over the wave's lanes
     uint32_t slot = wcnt + inc - cnt;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -389,9 +384,8 @@ __global__ __launch_bounds__(64 * NW, Rows::kMinBlocks) void k_topk_rows(RowsArg
     if (fits && n >= (uint32_t)K) {
       // slots past the wave's fullest region are empty in all its threads
       uint32_t jw = (gc + tpr - 1u) / tpr;
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) jw = max(jw, (uint32_t)__shfl_xor((int)jw, o, 64));
-      const RegLayout lay{(uint32_t)tid % tpr, tpr, gc, (uint32_t)__builtin_amdgcn_readfirstlane((int)jw)};
+      jw = wave_max_u32(jw);
+      const RegLayout lay{(uint32_t)tid % tpr, tpr, gc, jw};
       uint32_t key[Regs];
       int32_t id[Regs];
 #pragma unroll
