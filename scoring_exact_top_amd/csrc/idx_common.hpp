@@ -823,7 +823,14 @@ struct RangeSel {
 // barriers, so that a caller's earlier use of it has ended.  NW waves (4 to
 // 16) per workgroup; the first 256 threads clear the 256 bins.  A list of
 // one value (massive ties) needs no pass.
-template <int M, int NW = kWaves, class KF>
+// kScores: the keys are f2key images of scores.  Where they lie on both
+// sides of zero, equal key bins would hold nearly all of them in one or two
+// bins (the key range between two scores of opposite sign is mostly taken
+// by tiny magnitudes), and the atomics of that pass would queue on those
+// bins; the first pass then cuts the score range [min, max] itself into 256
+// equal bins (monotone in the key, so each bin is a key range), and one
+// reduction finds the key range of the chosen bin for the passes after it.
+template <int M, int NW = kWaves, bool kScores = true, class KF>
 __device__ __forceinline__ RangeSel range_select_regs(const KF& kf, const RegLayout& lay, int rem, SelShared& sh, int tid) {
   static_assert(NW >= 4 && NW <= kMaxWaves, "256 bins cleared by the first 256 threads");
   const uint32_t lane = tid & 63;
@@ -867,10 +874,59 @@ __device__ __forceinline__ RangeSel range_select_regs(const KF& kf, const RegLay
   const int bits = span ? 32 - __clz((int)span) : 0;
   int s = bits > 8 ? bits - 8 : 0;
   uint32_t lo = mn, width = span;  // the range is [lo, lo + width]
-  int group;
+  int group = (int)cnt;
   int cur = 0;
+  bool done = false;
+  if (kScores && mn < 0x80000000u && mx >= 0x80000000u && bits > 24) {  // scores of both signs
+    const float vlo = key2f(mn);
+    const float scale = 256.0f / (key2f(mx) - vlo);
+    // bin of a key: 0..255, nondecreasing in the key (a NaN product, which
+    // finite scores do not make, would land in the top bin)
+    const auto vbin = [&](uint32_t k) { return (uint32_t)fminf((key2f(k) - vlo) * scale, 255.0f); };
+    uint32_t* const h = ring(0);
+    if (clears) ring(1)[tid] = 0u;
+#pragma unroll
+    for (int j = 0; j < M; ++j) {
+      if ((uint32_t)j < lay.jmax) {
+        const uint32_t k = kf(j);
+        atomicAdd(k ? &h[vbin(k)] : &sh.trash[lane], 1u);
+      }
+    }
+    __syncthreads();
+    uint32_t b, above, inb;
+    wave_find_bucket(h, rem, lane, b, above, inb);
+    rem -= (int)above;
+    group = (int)inb;
+    // the chosen bin's smallest and largest keys (the minima above were read
+    // before this pass's barrier, so sh.wsum is free)
+    uint32_t bmn = 0xFFFFFFFFu, bmx = 0u;
+#pragma unroll
+    for (int j = 0; j < M; ++j) {
+      if ((uint32_t)j < lay.jmax) {
+        const uint32_t k = kf(j);
+        const bool in = k != 0u && vbin(k) == b;
+        bmn = in ? min(bmn, k) : bmn;
+        bmx = in ? max(bmx, k) : bmx;
+      }
+    }
+    bmn = wave_min_u32(bmn);
+    bmx = wave_max_u32(bmx);
+    if (lane == 0) { sh.wsum[0][wave] = bmn; sh.wsum[1][wave] = bmx; }
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      bmn = min(bmn, sh.wsum[0][w]);
+      bmx = max(bmx, sh.wsum[1][w]);
+    }
+    lo = bmn;
+    width = bmx - bmn;
+    const int wb = width ? 32 - __clz((int)width) : 0;
+    s = wb > 8 ? wb - 8 : 0;
+    cur = 1;  // ring(1) was cleared by this pass
+    done = (int)inb == rem || width == 0u;  // taken whole, or one value (a tie)
+  }
 #pragma unroll 1
-  while (true) {
+  while (!done) {
     const int nxt = cur == 2 ? 0 : cur + 1;
     uint32_t* const h = ring(cur);
     if (clears) ring(nxt)[tid] = 0u;
@@ -940,7 +996,7 @@ __device__ __forceinline__ uint32_t tie_bound_regs(const uint32_t (&key)[M], con
     asm volatile("" : "+v"(x));
     return key[j] == v ? ~x : 0u;
   };
-  return range_select_regs<M, NW>(tk, lay, sel.rem, sh, tid).lo;
+  return range_select_regs<M, NW, false>(tk, lay, sel.rem, sh, tid).lo;
 }
 
 // Emit for range_select_regs: keys above `last` fill out[0, kr - rem), the
