@@ -108,29 +108,41 @@ __device__ __forceinline__ DecodeSample decode_sample(int L) {
   return d;
 }
 
-// The lower edge of the 16-bit bucket of the r-th largest of n <= 512
-// order-preserving keys (keys[0..n) in LDS), at or below that key, found
-// by one wave with no atomics: each lane holds eight keys, and the
-// bucket's bits are fixed from the top, each kept when at least r keys lie
-// at or above it (a ballot per key, counted on the scalar unit).
-// 1 <= r <= n.
-__device__ __forceinline__ uint32_t wave_cut16(const uint32_t* keys, int n, int r, uint32_t lane) {
+// A threshold at or below the r-th largest of n <= 512 order-preserving
+// score keys (keys[0..n) in LDS, all nonzero), found by one wave on its own
+// with no barrier: the samples' score range [min, max] cut into 256 equal
+// bins (monotone in the key), one histogram in the wave's own 256 LDS
+// words, the bin holding the r-th largest found from the top, and the
+// smallest sample in that bin returned.  1 <= r <= n.
+__device__ __forceinline__ uint32_t wave_cut_bins(const uint32_t* keys, int n, int r, uint32_t lane, uint32_t* hist) {
   uint32_t k[8];
+  uint32_t mn = 0xFFFFFFFFu, mx = 0u;
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const int i = (int)lane + 64 * j;
-    k[j] = i < n ? keys[i] : 0u;
+    k[j] = i < n ? keys[i] : 0u;  // 0: no sample
+    mn = min(mn, k[j] ? k[j] : 0xFFFFFFFFu);
+    mx = max(mx, k[j]);
   }
-  uint32_t t = 0u;
-#pragma unroll 1
-  for (int bit = 31; bit >= 16; --bit) {
-    const uint32_t c = t | (1u << bit);
-    int cnt = 0;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) cnt += __popcll(__ballot(k[j] >= c));
-    t = cnt >= r ? c : t;
-  }
-  return t;
+  for (int q = 0; q < 4; ++q) hist[lane + 64 * q] = 0u;
+  mn = wave_min_u32(mn);
+  mx = wave_max_u32(mx);
+  if (mn == mx) return mn;  // every sample one value
+  const float vlo = key2f(mn);
+  const float scale = 256.0f / (key2f(mx) - vlo);
+  const auto vbin = [&](uint32_t x) { return (uint32_t)fminf((key2f(x) - vlo) * scale, 255.0f); };
+  wave_sync();
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    if (k[j]) atomicAdd(&hist[vbin(k[j])], 1u);
+  wave_sync();
+  uint32_t b, above, inb;
+  wave_find_bucket(hist, r, lane, b, above, inb);
+  uint32_t lo = 0xFFFFFFFFu;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) lo = (k[j] && vbin(k[j]) == b) ? min(lo, k[j]) : lo;
+  return wave_min_u32(lo);
 }
 
 // Each workgroup scores one piece of one sequence: a run of its 64-key
@@ -165,6 +177,7 @@ __global__ __launch_bounds__(kWG, 2) void k_decode_score(DecodeArgs A) {
   __shared__ uint8_t s_qprep[kWaves][kUTerms * kD];
   __shared__ SelShared sh;
   __shared__ uint32_t s_samp[64 * kDecodeSamplePages];  // the sampled scores as order-preserving keys
+  __shared__ uint32_t s_cut[kWaves][256];              // each wave's threshold histogram
   const int tid = threadIdx.x;
   const uint32_t lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -268,9 +281,8 @@ __global__ __launch_bounds__(kWG, 2) void k_decode_score(DecodeArgs A) {
       if (wave + 4 < ds.pages) s_samp[64 * (wave + 4) + lane] = f2key(sc1);
       __syncthreads();
       // every wave selects the threshold itself (the same value), with no
-      // second barrier; two digits: tau is the lower edge of the r-th
-      // largest sample's 16-bit bucket, at or below that sample
-      tau = key2f(wave_cut16(s_samp, 64 * ds.pages, ds.r, lane));
+      // second barrier: the smallest sample in the bin of the r-th largest
+      tau = key2f(wave_cut_bins(s_samp, 64 * ds.pages, ds.r, lane, s_cut[wave]));
     }
     // Groups of up to 64 of the wave's tiles.  Three tile buffers in
     // rotation give two tiles of lead; the roles rotate by unrolling rather
