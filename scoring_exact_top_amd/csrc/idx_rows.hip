@@ -350,12 +350,10 @@ __global__ __launch_bounds__(64 * NW, Rows::kMinBlocks) void k_topk_rows(RowsArg
   // the scoring kernel's plan for this row (filtered decode candidates),
   // loaded beside the range check; only used for a row it scored
   uint2 dpl = make_uint2(0u, 0u);
-  uint32_t dca = 0u, dcb = 0u;  // counts of segments tid and tid + NT (valid below 4 dpl.y)
+  uint2 dc2 = make_uint2(0u, 0u);  // counts of segments 2 tid and 2 tid + 1 (valid below 4 dpl.y)
   if (A.dcnt) {
     dpl = A.dplan[t];
-    const uint32_t* cn = A.dcnt + (int64_t)t * kDecodeCntStride;
-    dca = cn[tid];
-    dcb = cn[min(tid + NT, kDecodeCntStride - 1)];
+    dc2 = reinterpret_cast<const uint2*>(A.dcnt + (int64_t)t * kDecodeCntStride)[min(tid, kDecodeCntStride / 2 - 1)];
   }
   int s0, s1;
   if (!R.template range<NW>(t, s0, s1, tid)) {
@@ -406,28 +404,28 @@ __global__ __launch_bounds__(64 * NW, Rows::kMinBlocks) void k_topk_rows(RowsArg
 
   // candidates filtered by the scoring kernel: all of the row's keys at or
   // above its threshold, in the four wave segments of each of the row's
-  // dpl.y workgroups.  The segments' counts are scanned into offsets of one
-  // list (in LDS), whose element x thread slot j of thread x mod NT holds
-  // (x = tid + j*NT); the segment of x is found by a binary search over the
-  // offsets.  Exact when every segment kept all its candidates, they fit the
-  // slots and there are at least K of them (every other key scores below
-  // the threshold); otherwise the row takes the passes below.
-  if (A.dcnt) {
+  // dpl.y workgroups.  The segments' counts (two per thread) are scanned
+  // into offsets of one list (in LDS), whose element x thread slot j of
+  // thread x mod NT holds (x = tid + j*NT); the segment of x is found by a
+  // binary search over the offsets.  A segment that dropped candidates
+  // enters the scan as more than the slots hold, so one total tells both.
+  // Exact when every segment kept all its candidates, they fit the slots
+  // and there are at least K of them (every other key scores below the
+  // threshold); otherwise the row takes the passes below.
+  if (2 * NT >= kDecodeCntStride && A.dcnt) {  // two counts per thread cover the row's (paged rows)
     constexpr int DR = kDecodeRegs;
     const int nseg = 4 * (int)dpl.y;  // at most 2048 (512 workgroups)
     const int64_t seg0 = (int64_t)dpl.x * kWaves;
-    const uint32_t ca = tid < nseg ? dca : 0u, cb = tid + NT < nseg ? dcb : 0u;
+    const uint32_t ca = 2 * tid < nseg ? dc2.x : 0u, cb = 2 * tid + 1 < nseg ? dc2.y : 0u;
     const bool over = ca > (uint32_t)A.dseg || cb > (uint32_t)A.dseg;
     uint32_t n = 0u;
-    const uint32_t pa = block_exclusive_scan<NW>(ca, S.sh, tid, n);  // offsets of the first NT segments
-    uint32_t nb = 0u;
-    const uint32_t pb = n + block_exclusive_scan<NW>(cb, S.sh, tid, nb);
-    n += nb;
+    const uint32_t pa = block_exclusive_scan<NW>(over ? (uint32_t)(NT * DR + 1) : ca + cb, S.sh, tid, n);
     uint32_t* const off = S.lkey;  // nseg + 1 offsets (the LDS list area is unused on this path)
-    if (tid < nseg) off[tid] = pa;
-    if (tid + NT < nseg) off[tid + NT] = pb;
+    if (2 * tid < nseg) off[2 * tid] = pa;
+    if (2 * tid + 1 < nseg) off[2 * tid + 1] = pa + ca;
     if (tid == 0) off[nseg] = n;
-    const bool dropped = __syncthreads_or(over) || n > (uint32_t)(NT * DR);
+    __syncthreads();
+    const bool dropped = n > (uint32_t)(NT * DR);
     if (nseg >= 1 && !dropped && n >= (uint32_t)K) {
       const RegLayout lay = block_list_layout<NW>(n, (uint32_t)tid);
       uint32_t sg[DR], lo[DR];  // per slot: search window [lo, lo + span)
